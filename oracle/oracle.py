@@ -1,0 +1,170 @@
+"""ctypes binding of the fp64 C oracle (``oracle/sdv_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg
+may import this module.  It builds ``liboracle.so`` with gcc on first use if it is missing.
+
+Semantics (each documented where the C source defines it):
+  * Rule 1 (greedy) and Rule 2 (speculative sampling) of "Speculative Decoding Coordination
+    Protocol (SDCP)", section "Acceptance Rules"; the accept test r <= p/q of "SOTA-227", section
+    "What to do".
+  * ragged batches: request i owns draft rows cu[i]..cu[i+1]-1 and target rows cu[i]+i..cu[i+1]+i
+    ("M7.8 - Speculative Serving", section 0x01: one extra target row per request beyond its K_i).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "sdv_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+BF16, FP32 = 0, 1
+TERM_GREEDY, TERM_BONUS, TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, TERM_BAD = 0, 1, 2, 3, -1
+
+
+def build(out: str = LIBRARY, extra_flags: tuple[str, ...] = ()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, fp64, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", *extra_flags, SOURCE, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+class _Diag(ctypes.Structure):
+    _fields_ = [
+        ("target_lse", ctypes.c_void_p),
+        ("draft_lse", ctypes.c_void_p),
+        ("target_argmax", ctypes.c_void_p),
+        ("ratio", ctypes.c_void_p),
+        ("accept_margin", ctypes.c_void_p),
+        ("cdf_margin", ctypes.c_void_p),
+        ("resid_mass", ctypes.c_void_p),
+        ("terminal_kind", ctypes.c_void_p),
+    ]
+
+
+_LIBS: dict[str, ctypes.CDLL] = {}
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    if path in _LIBS:
+        return _LIBS[path]
+    if not os.path.exists(path) or (path == LIBRARY and os.path.getmtime(path) < os.path.getmtime(SOURCE)):
+        build(path)
+    lib = ctypes.CDLL(path)
+    lib.oracle_verify.restype = ctypes.c_int
+    lib.oracle_verify.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
+    ]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_philox_block.restype = None
+    lib.oracle_philox_block.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    lib.oracle_philox_grid.restype = None
+    lib.oracle_philox_grid.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.oracle_row_lse.restype = ctypes.c_double
+    lib.oracle_row_lse.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
+    lib.oracle_row_argmax.restype = ctypes.c_int32
+    lib.oracle_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    _LIBS[path] = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None) -> int | None:
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_code(logits: np.ndarray) -> int:
+    if logits.dtype == np.uint16:
+        return BF16  # bf16 stored as its 16 raw bits
+    if logits.dtype == np.float32:
+        return FP32
+    raise TypeError(f"logits must be uint16 (bf16 bits) or float32, got {logits.dtype}")
+
+
+def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, cu: np.ndarray,
+           temperature: float, seed: int, diag: bool = False, lib_path: str = LIBRARY) -> dict:
+    """Run the oracle on one ragged batch.
+
+    target: (n_draft_rows + B, V); draft: (n_draft_rows, V) or None when temperature == 0;
+    draft_tokens: (n_draft_rows,) int32; cu: (B + 1,) int32 exclusive prefix sums of K_i.
+    Returns accepted_len (B,), out_tokens (n_draft_rows + B,), and with ``diag`` the per-row LSEs,
+    argmaxes, ratios, margins, residual masses and terminal kinds.
+    """
+    lib = load(lib_path)
+    target = np.ascontiguousarray(target)
+    dt = _dtype_code(target)
+    if draft is not None:
+        draft = np.ascontiguousarray(draft)
+        if _dtype_code(draft) != dt:
+            raise TypeError("target and draft must share a dtype")
+    draft_tokens = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    B = cu.shape[0] - 1
+    n_d = draft_tokens.shape[0]
+    V = target.shape[1]
+    if target.shape[0] != n_d + B:
+        raise ValueError("target must have n_draft_rows + B rows")
+    acc = np.full(B, -7, dtype=np.int32)
+    out = np.full(n_d + B, -7, dtype=np.int32)
+    res: dict = {"accepted_len": acc, "out_tokens": out}
+    dg_p = None
+    if diag:
+        n_t = n_d + B
+        res.update(
+            target_lse=np.full(n_t, np.nan), draft_lse=np.full(n_d, np.nan),
+            target_argmax=np.full(n_t, -1, dtype=np.int32), ratio=np.full(n_d, np.nan),
+            accept_margin=np.full(n_d, np.nan), cdf_margin=np.full(B, np.nan),
+            resid_mass=np.full(B, np.nan), terminal_kind=np.full(B, -9, dtype=np.int32),
+        )
+        dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
+        dg_p = ctypes.pointer(dg)
+    rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
+                           float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(acc), _ptr(out), dg_p)
+    if rc != 0:
+        raise ValueError(f"oracle_verify rejected its arguments (status {rc})")
+    return res
+
+
+def philox4x32_10(counter, key) -> np.ndarray:
+    lib = load()
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox_block(seed: int, request: int, position: int) -> np.ndarray:
+    lib = load()
+    out = np.zeros(4, dtype=np.uint32)
+    lib.oracle_philox_block(int(seed) & 0xFFFFFFFFFFFFFFFF, request, position, _ptr(out))
+    return out
+
+
+def philox_grid(seed: int, n_requests: int, n_positions: int) -> np.ndarray:
+    """Blocks for every (request, position) pair, shape (n_requests, n_positions, 4)."""
+    out = np.zeros((n_requests, n_positions, 4), dtype=np.uint32)
+    load().oracle_philox_grid(int(seed) & 0xFFFFFFFFFFFFFFFF, n_requests, n_positions, _ptr(out))
+    return out
+
+
+def row_lse(row: np.ndarray, temperature: float) -> float:
+    row = np.ascontiguousarray(row)
+    return load().oracle_row_lse(_ptr(row), _dtype_code(row), 0, row.shape[-1], float(temperature))
+
+
+def row_argmax(row: np.ndarray) -> int:
+    row = np.ascontiguousarray(row)
+    return load().oracle_row_argmax(_ptr(row), _dtype_code(row), 0, row.shape[-1])
+
+
+def num_threads() -> int:
+    return load().oracle_num_threads()

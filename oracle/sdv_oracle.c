@@ -1,0 +1,355 @@
+/*
+ * oracle/sdv_oracle.c -- fp64 CPU oracle for batched speculative-sampling verification.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU
+ * baseline load this library.  The product path (the HIP library) never calls it, shares no
+ * source with it, and must fail loudly rather than fall back to it.
+ *
+ * What it computes, and where the pages define it:
+ *
+ *  - Rule 1, greedy ("Speculative Decoding Coordination Protocol (SDCP)", section "Acceptance
+ *    Rules", Rule 1; the temperature-zero tie rule is in section "Session Contract"): a draft
+ *    token is accepted iff it equals the argmax of the target row, ties going to the smallest
+ *    token id; evaluation stops at the first miss, and the extra token is the argmax of the row
+ *    after the accepted prefix.
+ *
+ *  - Rule 2, speculative sampling (SDCP section "Acceptance Rules", Rule 2; "SOTA-227: Decode
+ *    with a draft model and an accept-reject rule, which is exactly lossless", section "What to
+ *    do", steps 3 and 4): walking the draft left to right, position j is accepted when
+ *    r_j <= p_j(x_j) / q_j(x_j); at the first rejection the extra token is drawn from
+ *    normalize(max(p_j - q_j, 0)); when every draft is accepted it is drawn from p at the
+ *    position after the last draft.  A request with no drafts (K = 0) therefore draws one
+ *    ordinary target token ("M7.8 - Speculative Serving", section 0x09, the K = 0 case).
+ *
+ *  - p and q are softmax(z / T) of the target and draft logit rows (SDCP "Session Contract":
+ *    temperature is the first step of the sampling profile; top-k / top-p are not applied).
+ *
+ *  - Precondition (SDCP section "Verification and Commit", step 5): a proposal whose draft
+ *    probability q_j(x_j) is zero at any position is rejected before any uniform is drawn.
+ *    Out-of-range draft tokens and depths beyond 64 (SDCP "Session Contract", m_max <= 64) are
+ *    rejected the same way.  A rejected request reports accepted_len = -1.
+ *
+ * Readings where the pages leave a step open (each one is listed in the design notes):
+ *  - uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+ *    1, 2, 3", SC'11) with key = (seed & 0xffffffff, seed >> 32) and counter =
+ *    (position, request, 0, 0).  Word 0 feeds the accept test, word 1 the extra-token draw, which
+ *    mirrors SDCP's two "purpose" values.  r = ((w0 >> 8) + 1) / 2^24 lies in (0, 1];
+ *    u = (w1 >> 8) / 2^24 lies in [0, 1).  Both are exact in fp32 and fp64.
+ *  - accept iff r <= ratio (the SOTA-227 form).  Since r > 0, a token with p(x) = 0 is never
+ *    accepted, and ratio >= 1 always accepts.
+ *  - the extra-token draw is the inverse CDF in ascending token id:
+ *    y = min{ v : C(v) > u * S }, with C the inclusive prefix sum of the weights w and S = C(V-1).
+ *    If rounding leaves no such v, y is the largest v with w_v > 0.
+ *  - a residual with S = 0 (p == q exactly, which a rejection makes mathematically impossible)
+ *    falls back to w = p.
+ *
+ * Everything is evaluated in fp64: bf16 and fp32 inputs convert to fp64 exactly, sums run in
+ * ascending token order, and the residual is formed as p_v - q_v directly.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MAX_DEPTH 64
+
+enum { ORACLE_BF16 = 0, ORACLE_FP32 = 1 };
+
+enum {
+  ORACLE_TERM_GREEDY = 0,
+  ORACLE_TERM_BONUS = 1,
+  ORACLE_TERM_RESIDUAL = 2,
+  ORACLE_TERM_RESIDUAL_EMPTY = 3,
+  ORACLE_TERM_BAD = -1
+};
+
+/* Optional per-row / per-position / per-request outputs.  Any pointer may be NULL. */
+typedef struct {
+  double* target_lse;     /* [n_target_rows]  LSE of z/T; written for every row of a valid request (T > 0) */
+  double* draft_lse;      /* [n_draft_rows]   LSE of z/T; written for every row of a valid request (T > 0) */
+  int32_t* target_argmax; /* [n_target_rows]  argmax, lowest index on ties (T == 0) */
+  double* ratio;          /* [n_draft_rows]   p(x)/q(x) at every draft position of a valid request (T > 0) */
+  double* accept_margin;  /* [n_draft_rows]   |r - ratio| at the positions actually tested, else NaN */
+  double* cdf_margin;     /* [B]              margin of the extra-token draw, NaN when there was no draw */
+  double* resid_mass;     /* [B]              S, the total weight of the extra-token draw */
+  int32_t* terminal_kind; /* [B]              one of ORACLE_TERM_* */
+} oracle_diag;
+
+/* ---------------------------------------------------------------- Philox4x32-10 (SC'11) */
+
+/* One Philox4x32 round: two 32x32->64 products of the even counter words with the round
+ * multipliers; the high halves are mixed with the odd words and the key, the low halves are
+ * carried over, and the words are permuted. */
+static void philox4x32_round(uint32_t x[4], const uint32_t k[2]) {
+  const uint64_t prod_a = (uint64_t)0xD2511F53u * (uint64_t)x[0];
+  const uint64_t prod_b = (uint64_t)0xCD9E8D57u * (uint64_t)x[2];
+  const uint32_t y0 = (uint32_t)(prod_b >> 32) ^ x[1] ^ k[0];
+  const uint32_t y1 = (uint32_t)prod_b;
+  const uint32_t y2 = (uint32_t)(prod_a >> 32) ^ x[3] ^ k[1];
+  const uint32_t y3 = (uint32_t)prod_a;
+  x[0] = y0;
+  x[1] = y1;
+  x[2] = y2;
+  x[3] = y3;
+}
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+  uint32_t k[2] = {key[0], key[1]};
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) { /* the key schedule adds the Weyl constants before every round but the first */
+      k[0] += 0x9E3779B9u;
+      k[1] += 0xBB67AE85u;
+    }
+    philox4x32_round(x, k);
+  }
+  memcpy(out, x, sizeof x);
+}
+
+/* The verifier's block for (request, position): key from the seed, counter (position, request, 0, 0). */
+void oracle_philox_block(uint64_t seed, uint32_t request, uint32_t position, uint32_t out[4]) {
+  const uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+  const uint32_t ctr[4] = {position, request, 0u, 0u};
+  oracle_philox4x32_10(ctr, key, out);
+}
+
+/* Blocks for requests 0..n_req-1 and positions 0..n_pos-1, laid out [request][position][4]. */
+void oracle_philox_grid(uint64_t seed, int32_t n_req, int32_t n_pos, uint32_t* out) {
+  for (int32_t i = 0; i < n_req; ++i)
+    for (int32_t j = 0; j < n_pos; ++j)
+      oracle_philox_block(seed, (uint32_t)i, (uint32_t)j, out + 4 * ((int64_t)i * n_pos + j));
+}
+
+/* r in (0, 1] for the accept test, from word 0. */
+static double accept_uniform(const uint32_t w[4]) { return (double)((w[0] >> 8) + 1u) / 16777216.0; }
+/* u in [0, 1) for the extra-token draw, from word 1. */
+static double draw_uniform(const uint32_t w[4]) { return (double)(w[1] >> 8) / 16777216.0; }
+
+/* ---------------------------------------------------------------- logit access */
+
+static double logit_at(const void* base, int dtype, int64_t row, int32_t V, int32_t v) {
+  const int64_t idx = row * (int64_t)V + v;
+  if (dtype == ORACLE_BF16) {
+    const uint16_t bits = ((const uint16_t*)base)[idx];
+    uint32_t wide = (uint32_t)bits << 16; /* bf16 is the top half of an IEEE binary32 */
+    float f;
+    memcpy(&f, &wide, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)base)[idx];
+}
+
+/* Natural-log LSE of z/T over one row: m/T + ln(sum_v exp((z_v - m)/T)), ascending v. */
+double oracle_row_lse(const void* base, int dtype, int64_t row, int32_t V, double T) {
+  double m = -INFINITY;
+  for (int32_t v = 0; v < V; ++v) {
+    const double z = logit_at(base, dtype, row, V, v);
+    if (z > m) m = z;
+  }
+  if (m == -INFINITY) return -INFINITY;
+  double s = 0.0;
+  for (int32_t v = 0; v < V; ++v) s += exp((logit_at(base, dtype, row, V, v) - m) / T);
+  return m / T + log(s);
+}
+
+/* argmax over one row; the smallest index wins a tie (strict > while ascending). */
+int32_t oracle_row_argmax(const void* base, int dtype, int64_t row, int32_t V) {
+  int32_t best = 0;
+  double best_z = logit_at(base, dtype, row, V, 0);
+  for (int32_t v = 1; v < V; ++v) {
+    const double z = logit_at(base, dtype, row, V, v);
+    if (z > best_z) {
+      best_z = z;
+      best = v;
+    }
+  }
+  return best;
+}
+
+/* ---------------------------------------------------------------- inverse-CDF draw */
+
+/* y = min{v : C(v) > u*S}; returns y and its margin min(u - C(y-1)/S, C(y)/S - u). */
+static int32_t inverse_cdf(const double* w, int32_t V, double u, double* S_out, double* margin) {
+  double S = 0.0;
+  for (int32_t v = 0; v < V; ++v) S += w[v];
+  *S_out = S;
+  const double target = u * S;
+  double below = 0.0; /* C(v-1) */
+  for (int32_t v = 0; v < V; ++v) {
+    const double upto = below + w[v]; /* C(v) */
+    if (upto > target) {
+      const double lo = u - below / S, hi = upto / S - u;
+      *margin = lo < hi ? lo : hi;
+      return v;
+    }
+    below = upto;
+  }
+  /* rounding left u*S at or beyond C(V-1): the largest token with positive weight */
+  for (int32_t v = V - 1; v >= 0; --v) {
+    if (w[v] > 0.0) {
+      *margin = 0.0;
+      return v;
+    }
+  }
+  *margin = 0.0;
+  return V - 1;
+}
+
+/* ---------------------------------------------------------------- one request */
+
+static void set_nan(double* p) {
+  if (p) *p = NAN;
+}
+
+static void verify_request(const void* target, const void* draft, int dtype, const int32_t* tokens,
+                           const int32_t* cu, int32_t i, int64_t n_draft_rows, int32_t V, double T,
+                           uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* dg,
+                           double* w /* scratch [V] */) {
+  const int64_t lo = cu[i], hi = cu[i + 1];
+  const int64_t K = hi - lo;
+  if (dg && dg->cdf_margin) dg->cdf_margin[i] = NAN;
+  if (dg && dg->resid_mass) dg->resid_mass[i] = NAN;
+  if (lo < 0 || hi > n_draft_rows || K < 0 || K > ORACLE_MAX_DEPTH) {
+    /* offsets that do not describe a valid request: no slot can be named, none is written */
+    accepted_len[i] = -1;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_BAD;
+    return;
+  }
+  const int64_t trow0 = lo + i; /* target rows of request i: trow0 .. trow0 + K */
+  const int64_t drow0 = lo;     /* draft rows of request i:  drow0 .. drow0 + K - 1 */
+  int32_t* slots = out_tokens + trow0;
+
+  int bad = 0;
+  for (int64_t j = 0; j < K; ++j)
+    if (tokens[drow0 + j] < 0 || tokens[drow0 + j] >= V) bad = 1;
+  /* q_j(x_j) = 0 exactly when the draft logit at x_j is -inf; checked before any draw */
+  if (!bad && T > 0.0)
+    for (int64_t j = 0; j < K; ++j)
+      if (logit_at(draft, dtype, drow0 + j, V, tokens[drow0 + j]) == -INFINITY) bad = 1;
+  if (bad) {
+    accepted_len[i] = -1;
+    for (int64_t j = 0; j <= K; ++j) slots[j] = -1;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_BAD;
+    return;
+  }
+
+  if (T == 0.0) { /* ---- Rule 1 */
+    int64_t a = K;
+    for (int64_t j = 0; j < K; ++j) {
+      if (tokens[drow0 + j] != oracle_row_argmax(target, dtype, trow0 + j, V)) {
+        a = j;
+        break;
+      }
+    }
+    if (dg && dg->target_argmax)
+      for (int64_t j = 0; j <= K; ++j) dg->target_argmax[trow0 + j] = oracle_row_argmax(target, dtype, trow0 + j, V);
+    for (int64_t j = 0; j < a; ++j) slots[j] = tokens[drow0 + j];
+    slots[a] = oracle_row_argmax(target, dtype, trow0 + a, V);
+    for (int64_t j = a + 1; j <= K; ++j) slots[j] = -1;
+    accepted_len[i] = (int32_t)a;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_GREEDY;
+    return;
+  }
+
+  /* ---- Rule 2 */
+  double lse_t[ORACLE_MAX_DEPTH + 1], lse_d[ORACLE_MAX_DEPTH];
+  for (int64_t j = 0; j <= K; ++j) lse_t[j] = oracle_row_lse(target, dtype, trow0 + j, V, T);
+  for (int64_t j = 0; j < K; ++j) lse_d[j] = oracle_row_lse(draft, dtype, drow0 + j, V, T);
+  if (dg) {
+    for (int64_t j = 0; j <= K; ++j)
+      if (dg->target_lse) dg->target_lse[trow0 + j] = lse_t[j];
+    for (int64_t j = 0; j < K; ++j) {
+      if (dg->draft_lse) dg->draft_lse[drow0 + j] = lse_d[j];
+      set_nan(dg->accept_margin ? &dg->accept_margin[drow0 + j] : NULL);
+    }
+  }
+
+  int64_t a = K;
+  for (int64_t j = 0; j < K; ++j) {
+    const int32_t x = tokens[drow0 + j];
+    const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) / T -
+                             (lse_t[j] - lse_d[j]);
+    const double ratio = exp(log_ratio); /* p_j(x) / q_j(x) */
+    if (dg && dg->ratio) dg->ratio[drow0 + j] = ratio;
+    if (a < K) continue; /* positions after the first rejection are never tested */
+    uint32_t blk[4];
+    oracle_philox_block(seed, (uint32_t)i, (uint32_t)j, blk);
+    const double r = accept_uniform(blk);
+    if (dg && dg->accept_margin) dg->accept_margin[drow0 + j] = fabs(r - ratio);
+    if (!(r <= ratio)) a = j;
+  }
+
+  const int64_t t = a; /* the position whose extra token is drawn */
+  uint32_t blk[4];
+  oracle_philox_block(seed, (uint32_t)i, (uint32_t)t, blk);
+  const double u = draw_uniform(blk);
+  int kind;
+  if (t < K) {
+    kind = ORACLE_TERM_RESIDUAL;
+    double S = 0.0;
+    for (int32_t v = 0; v < V; ++v) {
+      const double p = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
+      const double q = exp(logit_at(draft, dtype, drow0 + t, V, v) / T - lse_d[t]);
+      w[v] = p > q ? p - q : 0.0;
+      S += w[v];
+    }
+    if (!(S > 0.0)) {
+      kind = ORACLE_TERM_RESIDUAL_EMPTY;
+      for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
+    }
+  } else {
+    kind = ORACLE_TERM_BONUS;
+    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
+  }
+  double S, margin;
+  const int32_t y = inverse_cdf(w, V, u, &S, &margin);
+
+  for (int64_t j = 0; j < t; ++j) slots[j] = tokens[drow0 + j];
+  slots[t] = y;
+  for (int64_t j = t + 1; j <= K; ++j) slots[j] = -1;
+  accepted_len[i] = (int32_t)a;
+  if (dg) {
+    if (dg->cdf_margin) dg->cdf_margin[i] = margin;
+    if (dg->resid_mass) dg->resid_mass[i] = S;
+    if (dg->terminal_kind) dg->terminal_kind[i] = kind;
+  }
+}
+
+/* ---------------------------------------------------------------- batch entry point */
+
+/*
+ * target        [n_draft_rows + B][V]  row-major, dtype (0 = bf16 bits as uint16, 1 = fp32)
+ * draft         [n_draft_rows][V]      may be NULL when T == 0
+ * draft_tokens  [n_draft_rows]
+ * cu            [B + 1] exclusive prefix sums of the per-request depths K_i
+ * accepted_len  [B]     out
+ * out_tokens    [n_draft_rows + B]  out: request i owns slots cu[i]+i .. cu[i]+i+K_i
+ * Returns 0, or -1 for arguments that describe no batch.
+ */
+int oracle_verify(const void* target, const void* draft, int dtype, const int32_t* draft_tokens, const int32_t* cu,
+                  int32_t B, int64_t n_draft_rows, int32_t V, double T, uint64_t seed, int32_t* accepted_len,
+                  int32_t* out_tokens, oracle_diag* diag) {
+  if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens) return -1;
+  if (B <= 0 || V <= 0 || n_draft_rows < 0 || !(T >= 0.0) || (T > 0.0 && !draft)) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* w = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!w) failed = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t i = 0; i < B; ++i)
+      if (w) verify_request(target, draft, dtype, draft_tokens, cu, i, n_draft_rows, V, T, seed, accepted_len, out_tokens, diag, w);
+    free(w);
+  }
+  return failed ? -2 : 0;
+}
+
+/* Number of OpenMP threads the oracle runs on (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

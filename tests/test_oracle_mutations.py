@@ -1,0 +1,134 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU only), builds it, and
+checks that at least one pin fails: the Monte Carlo against the exact enumeration, the
+closed-form LSE, the planted argmax tie, the K = 0 categorical draw, or the rocRAND Philox values.
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle import exact, oracle
+from workloads import offsets_from_depths
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTATIONS = {
+    "residual_without_clamp": ("w[v] = p > q ? p - q : 0.0;", "w[v] = p - q;"),
+    "residual_sign_flipped": ("w[v] = p > q ? p - q : 0.0;", "w[v] = q > p ? q - p : 0.0;"),
+    "ratio_inverted": ("const double ratio = exp(log_ratio);", "const double ratio = exp(-log_ratio);"),
+    "accept_comparison_reversed": ("if (!(r <= ratio)) a = j;", "if (!(r >= ratio)) a = j;"),
+    "lse_drops_max": ("return m / T + log(s);", "return log(s);"),
+    "residual_from_next_row": ("const double p = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);",
+                               "const double p = exp(logit_at(target, dtype, trow0 + t + 1, V, v) / T - lse_t[t + 1]);"),
+    "bonus_from_draft_side": ("kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);",
+                              "kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) * (v + 1);"),
+    "greedy_tie_to_largest": ("if (z > best_z) {", "if (z >= best_z) {"),
+    "philox_key_bumped_every_round": ("if (round > 0) {", "if (round >= 0) {"),
+    "temperature_ignored": ("const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) / T -",
+                            "const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) -"),
+}
+
+
+def _build_mutant(tmp_path, name):
+    src = open(oracle.SOURCE).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    src = src.replace(old, new, 1)
+    path = tmp_path / f"{name}.c"
+    path.write_text(src)
+    lib = str(tmp_path / f"lib{name}.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", str(path), "-o", lib, "-lm"], check=True)
+    return lib
+
+
+def _pin_monte_carlo(lib_path, T=1.0):
+    """Distinct rows per position, 60 calls x 4096 requests; fails if any chi-square p < 1e-6."""
+    rng = np.random.default_rng(321)
+    K, V, B = 3, 8, 4096
+    zt = (rng.standard_normal((K + 1, V)) * 1.5).astype(np.float32)
+    zd = (zt[:K] + rng.standard_normal((K, V)) * 1.0).astype(np.float32)
+    p = np.stack([exact.softmax(r, T) for r in zt])
+    q = np.stack([exact.softmax(r, T) for r in zd])
+    law = exact.round_distribution(p, q, grid=True)
+    cu = offsets_from_depths(np.full(B, K))
+    target, draft = np.tile(zt, (B, 1)), np.tile(zd, (B, 1))
+    pmf = np.zeros(K + 1)
+    reached = np.zeros((K + 1, V))
+    for c in range(60):
+        g = -np.log(-np.log(np.random.default_rng([5, c]).random((B * K, V))))
+        tokens = np.argmax(draft.astype(np.float64) / T + g, axis=1).astype(np.int32)
+        res = oracle.verify(target, draft, tokens, cu, T, 1000 + c, lib_path=lib_path)
+        a = res["accepted_len"]
+        if (a < 0).any():
+            return False
+        pmf += np.bincount(a, minlength=K + 1)
+        slots = res["out_tokens"].reshape(B, K + 1)
+        for j in range(K + 1):
+            reached[j] += np.bincount(np.clip(slots[a >= j, j], 0, V - 1), minlength=V)
+    pv = [stats.chisquare(pmf, law["pmf_accepted"] * pmf.sum()).pvalue]
+    for j in range(K + 1):
+        e = law["token_reached"][j] / law["token_reached"][j].sum() * reached[j].sum()
+        if (reached[j][e == 0] > 0).any():
+            return False
+        pv.append(stats.chisquare(reached[j][e > 0], e[e > 0]).pvalue)
+    return min(pv) > 1e-6
+
+
+def _pin_lse(lib_path):
+    lib = ctypes.CDLL(lib_path)
+    lib.oracle_row_lse.restype = ctypes.c_double
+    lib.oracle_row_lse.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
+    row = np.full(100, 3.0, dtype=np.float32)
+    return abs(lib.oracle_row_lse(row.ctypes.data, 1, 0, 100, 0.5) - (6.0 + np.log(100))) < 1e-12
+
+
+def _pin_greedy_tie(lib_path):
+    row = np.zeros((2, 10), dtype=np.float32)
+    row[0, [3, 6]] = 5.0
+    res = oracle.verify(row, None, np.array([6], dtype=np.int32), offsets_from_depths([1]), 0.0, 0, lib_path=lib_path)
+    return res["out_tokens"][0] == 3
+
+
+def _pin_philox(lib_path, tmp_path):
+    header = "/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"
+    if not os.path.exists(header) or shutil.which("g++") is None:
+        return True
+    exe = str(tmp_path / "probe")
+    subprocess.run(["g++", "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                    os.path.join(HERE, "rocrand_philox_probe.cpp"), "-o", exe], check=True)
+    ref = subprocess.run([exe, "12345", "0", "4", "4"], check=True, capture_output=True, text=True).stdout
+    lib = ctypes.CDLL(lib_path)
+    lib.oracle_philox_block.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    got = []
+    for i in range(4):
+        for j in range(4):
+            out = np.zeros(4, dtype=np.uint32)
+            lib.oracle_philox_block(12345, i, j, out.ctypes.data)
+            got.append(" ".join(f"{w:08x}" for w in out))
+    return ref.split("\n")[:16] == got
+
+
+def test_unmutated_oracle_passes_every_pin(tmp_path):
+    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie):
+        assert check(oracle.LIBRARY)
+    assert _pin_philox(oracle.LIBRARY, tmp_path)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(tmp_path, name):
+    oracle.load()  # make sure the reference build exists
+    lib = _build_mutant(tmp_path, name)
+    results = {
+        "monte_carlo": _pin_monte_carlo(lib),
+        "monte_carlo_T0.7": _pin_monte_carlo(lib, T=0.7),
+        "lse": _pin_lse(lib),
+        "greedy_tie": _pin_greedy_tie(lib),
+        "philox": _pin_philox(lib, tmp_path),
+    }
+    assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"

@@ -1,0 +1,202 @@
+"""Seeded synthetic workloads for the verification step.
+
+Shared by the oracle tests, the GPU parity tests, the smoke check and the benchmark.  It draws
+inputs only: logits, ragged depths and the drafter's tokens.  It holds none of the verifier's
+arithmetic: draft tokens are drawn with the Gumbel-max trick (x = argmax_v z_v/T + G_v), which the
+verification step never uses, and at temperature 0 the drafter proposes its own argmax.
+
+The pages measure on no public benchmark or dataset that could be loaded here.  Their serving
+workloads and trained models are replaced by Gaussian logits: target z ~ N(0, s_t^2), draft
+z + N(0, s_d^2), so that the draft/target agreement (the acceptance rate alpha) is set by s_d.
+
+Layout of a ragged batch ("M7.8 - Speculative Serving", section 0x01: N_query = sum_i (K_i + 1)):
+  cu[i]       exclusive prefix sum of the depths K_i, cu[0] = 0, cu[B] = n_draft_rows
+  draft rows  request i, position j < K_i  -> row cu[i] + j
+  target rows request i, position j <= K_i -> row cu[i] + i + j
+bf16 logits are kept as their raw 16 bits (uint16), rounded to nearest-even from fp32.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits, round to nearest even (finite inputs)."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((b + (((b >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Batch:
+    """One verification call's inputs, host side."""
+    name: str
+    V: int
+    dtype: str                    # "bf16" or "fp32"
+    temperature: float
+    seed: int                     # the verifier's seed
+    target: np.ndarray            # (n_draft_rows + B, V) uint16 bf16 bits or float32
+    draft: np.ndarray | None      # (n_draft_rows, V), None for greedy workloads
+    tokens: np.ndarray            # (n_draft_rows,) int32
+    cu: np.ndarray                # (B + 1,) int32
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.cu.shape[0] - 1)
+
+    @property
+    def n_draft_rows(self) -> int:
+        return int(self.tokens.shape[0])
+
+    @property
+    def depths(self) -> np.ndarray:
+        return np.diff(self.cu)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    def algorithmic_bytes(self) -> int:
+        """Every logit the method needs, read once: target rows, plus draft rows when T > 0."""
+        rows = self.target.shape[0] + (self.n_draft_rows if self.temperature > 0 else 0)
+        return rows * self.V * self.elem_bytes
+
+    def target_f32(self) -> np.ndarray:
+        return bf16_to_f32(self.target) if self.dtype == "bf16" else self.target
+
+    def draft_f32(self) -> np.ndarray | None:
+        if self.draft is None:
+            return None
+        return bf16_to_f32(self.draft) if self.dtype == "bf16" else self.draft
+
+
+def offsets_from_depths(depths) -> np.ndarray:
+    d = np.asarray(depths, dtype=np.int64)
+    return np.concatenate([[0], np.cumsum(d)]).astype(np.int32)
+
+
+def _store(x32: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, dtype=np.float32)
+
+
+def _gumbel_tokens(rng: np.random.Generator, stored_draft: np.ndarray, dtype: str, temperature: float,
+                   block_rows: int = 64) -> np.ndarray:
+    """Draft tokens x_j ~ softmax(stored draft row / T) via x = argmax(z/T + Gumbel)."""
+    n, V = stored_draft.shape
+    out = np.empty(n, dtype=np.int32)
+    for r0 in range(0, n, block_rows):
+        rows = stored_draft[r0:r0 + block_rows]
+        z = (bf16_to_f32(rows) if dtype == "bf16" else rows).astype(np.float64)
+        g = -np.log(-np.log(rng.random(z.shape)))
+        out[r0:r0 + block_rows] = np.argmax(z / temperature + g, axis=1)
+    return out
+
+
+def _argmax_tokens(stored_draft: np.ndarray, dtype: str) -> np.ndarray:
+    z = bf16_to_f32(stored_draft) if dtype == "bf16" else stored_draft
+    return np.argmax(z, axis=1).astype(np.int32)  # first occurrence on ties
+
+
+def make_random(name: str, depths, V: int, dtype: str, temperature: float, target_sigma: float,
+                draft_sigma, data_seed: int, verify_seed: int, greedy_drafts: bool | None = None,
+                keep_draft: bool | None = None) -> Batch:
+    """Gaussian-logit batch with the given per-request depths.
+
+    draft_sigma: scalar or one value per request (noise added to the target logits).
+    At temperature 0 the drafter proposes its argmax and the draft logits are not kept unless asked.
+    """
+    rng = np.random.Generator(np.random.Philox(data_seed))
+    depths = np.asarray(depths, dtype=np.int64)
+    B = depths.shape[0]
+    cu = offsets_from_depths(depths)
+    n_d = int(cu[-1])
+    sig = np.broadcast_to(np.asarray(draft_sigma, dtype=np.float64), (B,))
+    tgt = rng.standard_normal((n_d + B, V), dtype=np.float32)
+    tgt *= np.float32(target_sigma)
+    # draft row (i, j) perturbs target row (i, j)
+    t_of_d = np.concatenate([np.arange(cu[i], cu[i + 1]) + i for i in range(B)]).astype(np.int64)
+    req_of_d = np.repeat(np.arange(B), depths)
+    drf = rng.standard_normal((n_d, V), dtype=np.float32)
+    drf *= sig[req_of_d].astype(np.float32)[:, None]
+    drf += tgt[t_of_d]
+    target = _store(tgt, dtype)
+    del tgt
+    draft = _store(drf, dtype)
+    del drf
+    greedy = temperature == 0 if greedy_drafts is None else greedy_drafts
+    tokens = _argmax_tokens(draft, dtype) if greedy else _gumbel_tokens(rng, draft, dtype, temperature)
+    if keep_draft is None:
+        keep_draft = temperature > 0
+    return Batch(name=name, V=V, dtype=dtype, temperature=float(temperature), seed=int(verify_seed),
+                 target=target, draft=draft if keep_draft else None, tokens=tokens, cu=cu,
+                 meta={"data_seed": data_seed, "target_sigma": target_sigma,
+                       "draft_sigma": np.asarray(draft_sigma).tolist()})
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+DATA_SEED_BASE = 20261202
+
+
+def small_b1(round_index: int = 0) -> Batch:
+    """B=1, K=4, V=1000, fp32: target ~ N(0, 2^2), draft = target + N(0, 1), T = 1; one of 100 rounds."""
+    return make_random("b1_k4_v1000_fp32", [4], 1000, "fp32", 1.0, 2.0, 1.0,
+                       data_seed=DATA_SEED_BASE + 1000 + round_index, verify_seed=1000 + round_index)
+
+
+def exactness_case(case: int, B: int = 4096, K: int = 3, V: int = 8):
+    """One fixed (target, draft) row pair per case, reused at every position of every request.
+
+    target ~ N(0, 1.5^2), draft = target + N(0, 0.7^2), fp32, T = 1.  Returns the two rows; batches
+    with fresh draft tokens per trial come from ``exactness_batch``.
+    """
+    rng = np.random.Generator(np.random.Philox(DATA_SEED_BASE + 2000 + case))
+    zt = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    zd = (zt + rng.standard_normal(V) * 0.7).astype(np.float32)
+    return zt, zd
+
+
+def exactness_batch(case: int, trial_block: int, B: int = 4096, K: int = 3, V: int = 8,
+                    rows: tuple[np.ndarray, np.ndarray] | None = None) -> Batch:
+    """B requests of depth K sharing one row pair; the draft tokens are redrawn per trial block."""
+    zt, zd = exactness_case(case, B, K, V) if rows is None else rows
+    cu = offsets_from_depths(np.full(B, K))
+    target = np.ascontiguousarray(np.broadcast_to(zt, (B * (K + 1), V)), dtype=np.float32)
+    draft = np.ascontiguousarray(np.broadcast_to(zd, (B * K, V)), dtype=np.float32)
+    rng = np.random.Generator(np.random.Philox([DATA_SEED_BASE + 2000 + case, trial_block + 1]))
+    g = -np.log(-np.log(rng.random((B * K, V))))
+    tokens = np.argmax(zd.astype(np.float64)[None, :] + g, axis=1).astype(np.int32)
+    return Batch(name="exact_b4096_k3_v8_fp32", V=V, dtype="fp32", temperature=1.0,
+                 seed=(case << 32) | trial_block, target=target, draft=draft, tokens=tokens, cu=cu,
+                 meta={"case": case, "trial_block": trial_block})
+
+
+def uniform_b64(data_seed: int = DATA_SEED_BASE + 3, verify_seed: int = 3000) -> Batch:
+    """B=64, K=5, V=32000, bf16: target ~ N(0, 3^2), draft = target + N(0, 1.5^2), T = 0.8."""
+    return make_random("b64_k5_v32000_bf16", np.full(64, 5), 32000, "bf16", 0.8, 3.0, 1.5,
+                       data_seed=data_seed, verify_seed=verify_seed)
+
+
+def ragged_b256(data_seed: int = DATA_SEED_BASE + 4, verify_seed: int = 4000, B: int = 256,
+                V: int = 128256) -> Batch:
+    """B=256, K_i ~ U{0..8}, V=128256, bf16: target ~ N(0, 3^2), draft = target + N(0, s_i^2) with
+    s_i ~ U[0.5, 3] per request, T = 1."""
+    rng = np.random.Generator(np.random.Philox([data_seed, 7]))
+    depths = rng.integers(0, 9, size=B)
+    sig = rng.uniform(0.5, 3.0, size=B)
+    return make_random(f"b{B}_ragged_k0to8_v{V}_bf16", depths, V, "bf16", 1.0, 3.0, sig,
+                       data_seed=data_seed, verify_seed=verify_seed)
+
+
+def greedy_b512(data_seed: int = DATA_SEED_BASE + 5, verify_seed: int = 5000, B: int = 512,
+                V: int = 151936) -> Batch:
+    """B=512, K=4, V=151936, bf16, T=0: target ~ N(0, 4^2), draft = target + N(0, 1); the drafter
+    proposes its argmax; ties go to the lowest index."""
+    return make_random(f"greedy_b{B}_k4_v{V}_bf16", np.full(B, 4), V, "bf16", 0.0, 4.0, 1.0,
+                       data_seed=data_seed, verify_seed=verify_seed)
