@@ -1,0 +1,153 @@
+/*
+ * sdv.h -- C ABI of the MI355X (gfx950) speculative-decoding verification library (libsdv.so).
+ *
+ * The library verifies a batch of draft proposals against target logits in one call, on one GPU,
+ * with hand-written HIP kernels.  Every pointer argument of sdv_verify / sdv_verify_ex /
+ * sdv_philox4x32_10 is a DEVICE pointer owned by the caller; the library never allocates, frees,
+ * copies to the host or synchronizes.  All work is enqueued on the caller's HIP stream and the call
+ * returns as soon as it is enqueued.  Calls are stateless and may run concurrently on different
+ * streams as long as they use different workspaces and outputs.
+ *
+ * Definitions the entry points follow:
+ *  - Rule 1 (temperature 0) and Rule 2 (temperature > 0) of "Speculative Decoding Coordination
+ *    Protocol (SDCP)", section "Acceptance Rules"; the accept test r <= p(x)/q(x) of "SOTA-227:
+ *    Decode with a draft model and an accept-reject rule, which is exactly lossless", section
+ *    "What to do".  p and q are softmax(z/T) of the target and draft logit rows (SDCP section
+ *    "Session Contract": temperature, then top-k / top-p, which this library does not apply).
+ *  - Ragged batches ("M7.8 - Speculative Serving", section 0x01, N_query = sum_i (K_i + 1)):
+ *    request i has K_i = cu[i+1] - cu[i] draft tokens, 0 <= K_i <= 64 (SDCP m_max <= 64).
+ *    Draft row of (i, j), j < K_i:  row cu[i] + j        of draft_logits / draft_tokens.
+ *    Target row of (i, j), j <= K_i: row cu[i] + i + j   of target_logits.
+ *  - Uniforms: Philox4x32-10 (Salmon et al., SC'11), key = (seed low 32 bits, seed high 32 bits),
+ *    counter = (position j, request i, 0, 0).  Accept test r = ((w0 >> 8) + 1) * 2^-24 in (0, 1];
+ *    correction / bonus draw u = (w1 >> 8) * 2^-24 in [0, 1), from the block of the drawn position.
+ *  - The correction (first rejected position t) is drawn from normalize(max(p_t - q_t, 0)); if no
+ *    position is rejected the bonus is drawn from p at position K_i.  The draw is the inverse CDF
+ *    in ascending token id: y = min{v : C(v) > u * S}, S the total weight.
+ */
+#ifndef SDV_H
+#define SDV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDV_ABI_VERSION 1
+#define SDV_MAX_DEPTH 64 /* largest K_i a request may carry */
+#define SDV_MAX_EVENTS 4 /* timing hooks in sdv_diag */
+
+typedef enum { SDV_BF16 = 0, SDV_FP32 = 1 } sdv_dtype;
+
+typedef enum {
+  SDV_OK = 0,
+  SDV_ERR_INVALID_ARG = -1, /* a required pointer is NULL, or a size / temperature is out of range */
+  SDV_ERR_UNSUPPORTED = -2, /* dtype not one of sdv_dtype */
+  SDV_ERR_LIMIT = -3,       /* the batch exceeds an index or launch-size limit of this build */
+  SDV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than sdv_workspace_bytes() */
+  SDV_ERR_HIP = -5          /* a kernel launch failed; the stream state is as HIP reports it */
+} sdv_status;
+
+/* Terminal kinds reported through sdv_diag.terminal_kind. */
+typedef enum {
+  SDV_TERM_GREEDY = 0,         /* temperature 0: the extra token is the target argmax */
+  SDV_TERM_BONUS = 1,          /* every draft accepted (or K_i = 0): drawn from p at position K_i */
+  SDV_TERM_RESIDUAL = 2,       /* first rejection at t < K_i: drawn from max(p_t - q_t, 0) */
+  SDV_TERM_RESIDUAL_EMPTY = 3, /* the residual had no positive weight in floating point: drawn from p_t */
+  SDV_TERM_BAD = -1            /* the request was rejected (see sdv_verify) */
+} sdv_terminal_kind;
+
+/*
+ * Optional diagnostics for sdv_verify_ex.  Every member may be NULL; non-NULL arrays are device
+ * pointers the library writes for valid requests only (other entries are left untouched).
+ *   target_lse     [n_draft_rows + B]  ln sum_v exp(z_v / T) of each target row      (T > 0)
+ *   draft_lse      [n_draft_rows]      ln sum_v exp(z_v / T) of each draft row       (T > 0)
+ *   target_argmax  [n_draft_rows + B]  argmax of each target row, smallest id on ties (T == 0)
+ *   ratio          [n_draft_rows]      p_j(x_j) / q_j(x_j) at every draft position   (T > 0)
+ *   accept_uniform [n_draft_rows]      r_j at every draft position                   (T > 0)
+ *   draw_uniform   [B]                 u of the drawn position                        (T > 0)
+ *   terminal_kind  [B]                 one of sdv_terminal_kind
+ *   events         hipEvent_t handles (cast to void*) recorded on the stream: events[0] before the
+ *                  first kernel, events[k] after the k-th kernel.  The kernels run in the order
+ *                  row pass, accept scan, terminal draw (the last is skipped at T == 0).
+ */
+typedef struct sdv_diag {
+  double* target_lse;
+  double* draft_lse;
+  int32_t* target_argmax;
+  double* ratio;
+  float* accept_uniform;
+  float* draw_uniform;
+  int32_t* terminal_kind;
+  void* events[SDV_MAX_EVENTS];
+} sdv_diag;
+
+/*
+ * Bytes of device workspace sdv_verify needs for a batch of this shape (0 on invalid shapes).
+ * The workspace needs no initialisation and holds nothing between calls.
+ */
+size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype);
+
+/*
+ * Verify one ragged batch (SDCP "Verification and Commit", steps 5 to 7, for every request).
+ *
+ *   target_logits  [n_draft_rows + B][V] row-major, dtype elements (bf16 as raw 16-bit words)
+ *   draft_logits   [n_draft_rows][V]     same dtype; may be NULL when temperature == 0 (it is not
+ *                                        read then) or when n_draft_rows == 0
+ *   draft_tokens   [n_draft_rows] int32  the proposed token of each draft position
+ *   ragged_offsets [B + 1] int32         cu[0] = 0, non-decreasing, cu[B] = n_draft_rows
+ *   B, n_draft_rows, V                   host values: B >= 1, n_draft_rows >= 0, V >= 1
+ *   dtype                                SDV_BF16 or SDV_FP32
+ *   temperature                          0 selects Rule 1 (greedy); > 0 selects Rule 2 with
+ *                                        p = softmax(z_target / T), q = softmax(z_draft / T)
+ *   seed                                 key of the verifier's Philox stream (vary it per round)
+ *   accepted_len   [B] int32 out         a_i in [0, K_i] accepted drafts, or -1 for a rejected request
+ *   out_tokens     [n_draft_rows + B] int32 out: request i writes slots cu[i]+i .. cu[i]+i+K_i:
+ *                                        its a_i accepted drafts, then the correction / bonus
+ *                                        token, then -1 in the remaining K_i - a_i slots
+ *   workspace      device scratch of at least sdv_workspace_bytes(...) bytes, 256-byte aligned
+ *   stream         hipStream_t (as void*), NULL for the null stream
+ *
+ * Errors.  Argument errors are detected on the host and returned synchronously; nothing is
+ * launched then: NULL required pointers, B < 1, n_draft_rows < 0, V < 1, temperature negative,
+ * NaN or infinite (or so small that log2(e)/T overflows), T > 0 with NULL draft_logits while
+ * n_draft_rows > 0 -> SDV_ERR_INVALID_ARG; unknown dtype -> SDV_ERR_UNSUPPORTED; sizes beyond the
+ * 32-bit row / launch limits -> SDV_ERR_LIMIT; small workspace -> SDV_ERR_WORKSPACE.
+ * Per-request errors are decided on the device before any uniform is used (SDCP step 5 and
+ * problem types "sdcp-bad-proposal" / "sdcp-limit"): a request whose depth is outside [0, 64] or
+ * whose offsets fall outside [0, n_draft_rows] gets accepted_len = -1 and none of its slots are
+ * written; a request with a draft token outside [0, V), or (T > 0) with a draft logit of -inf at
+ * its token (q = 0), gets accepted_len = -1 and all of its K_i + 1 slots set to -1.  Other requests
+ * are unaffected.  Launch failures -> SDV_ERR_HIP.
+ */
+int sdv_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+               const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+               double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* sdv_verify plus optional diagnostics and timing events (diag may be NULL). */
+int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                  const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                  double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens,
+                  void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
+
+/*
+ * Raw Philox4x32-10 blocks on the device, for testing the verifier's uniforms: out[b] =
+ * Philox4x32-10(counter = counters[b][0..3], key = keys[b][0..1]) for b < n.  counters [n][4],
+ * keys [n][2], out [n][4] are uint32 device arrays.  n < 1 or NULL pointers -> SDV_ERR_INVALID_ARG.
+ */
+int sdv_philox4x32_10(const uint32_t* counters, const uint32_t* keys, int64_t n, uint32_t* out, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* sdv_status_string(int status);
+
+/* SDV_ABI_VERSION of the loaded library. */
+int sdv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDV_H */

@@ -1,0 +1,135 @@
+"""Lossless speculative-decoding verification on MI355X (gfx950).
+
+Python face of libsdv.so (C ABI in include/sdv.h).  Tensors are torch tensors on the GPU; this
+module only checks and marshals arguments, and every step of the verification runs in the HIP
+kernels behind ``sdv_verify``.  Work goes on torch's current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_RESIDUAL,
+                      TERM_RESIDUAL_EMPTY, SdvError)
+
+__all__ = ["verify", "verify_ex", "workspace_bytes", "philox4x32_10", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+           "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
+
+_DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
+_WORKSPACE: dict = {}
+
+
+def library_path() -> str:
+    return _native.lib()._name
+
+
+def abi_version() -> int:
+    return _native.lib().sdv_abi_version()
+
+
+def workspace_bytes(B: int, n_draft_rows: int, V: int, dtype: torch.dtype) -> int:
+    return int(_native.lib().sdv_workspace_bytes(B, n_draft_rows, V, _DTYPES[dtype]))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACE.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WORKSPACE[key] = ws
+    return ws
+
+
+def _check(target, draft, draft_tokens, offsets, temperature):
+    if not target.is_cuda:
+        raise ValueError("target logits must be on the GPU")
+    if target.dtype not in _DTYPES:
+        raise TypeError("logits must be bfloat16 or float32")
+    if target.dim() != 2 or not target.is_contiguous():
+        raise ValueError("target logits must be a contiguous [n_draft_rows + B, V] tensor")
+    for name, t in (("draft_tokens", draft_tokens), ("offsets", offsets)):
+        if t.dtype != torch.int32 or t.device != target.device or t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 vector on the logits' device")
+    if draft is not None:
+        if draft.dtype != target.dtype or draft.device != target.device or not draft.is_contiguous():
+            raise ValueError("draft logits must match the target's dtype and device and be contiguous")
+        if draft.dim() != 2 or draft.shape[1] != target.shape[1] or draft.shape[0] != draft_tokens.shape[0]:
+            raise ValueError("draft logits must be [n_draft_rows, V]")
+    B = offsets.shape[0] - 1
+    if target.shape[0] != draft_tokens.shape[0] + B:
+        raise ValueError("target logits must have n_draft_rows + B rows")
+    if temperature > 0 and draft is None and draft_tokens.shape[0] > 0:
+        raise ValueError("temperature > 0 needs draft logits")
+
+
+def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, offsets: torch.Tensor,
+              temperature: float, seed: int, *, out: tuple | None = None, workspace: torch.Tensor | None = None,
+              diag: tuple[str, ...] = (), events: list | None = None):
+    """Run sdv_verify_ex.  Returns (accepted_len, out_tokens, diag_dict).
+
+    ``diag`` names the diagnostic arrays to fill (fields of sdv_diag); ``events`` up to four
+    torch.cuda.Event objects recorded before the first kernel and after each kernel.
+    """
+    _check(target, draft, draft_tokens, offsets, temperature)
+    dev = target.device
+    B = offsets.shape[0] - 1
+    n_d = draft_tokens.shape[0]
+    V = target.shape[1]
+    dt = _DTYPES[target.dtype]
+    if out is None:
+        accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+        out_tokens = torch.empty(n_d + B, dtype=torch.int32, device=dev)
+    else:
+        accepted_len, out_tokens = out
+    need = int(_native.lib().sdv_workspace_bytes(B, n_d, V, dt))
+    ws = _workspace(need, dev) if workspace is None else workspace
+    shapes = {"target_lse": (n_d + B, torch.float64), "draft_lse": (n_d, torch.float64),
+              "target_argmax": (n_d + B, torch.int32), "ratio": (n_d, torch.float64),
+              "accept_uniform": (n_d, torch.float32), "draw_uniform": (B, torch.float32),
+              "terminal_kind": (B, torch.int32)}
+    dvals = {}
+    dg = None
+    if diag or events:
+        dg = _native.SdvDiag()
+        for name in diag:
+            n, t = shapes[name]
+            fill = -9 if t == torch.int32 else float("nan")
+            dvals[name] = torch.full((n,), fill, dtype=t, device=dev)
+            setattr(dg, name, dvals[name].data_ptr())
+        for k, ev in enumerate(events or []):
+            if ev is not None:
+                dg.events[k] = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _native.lib().sdv_verify_ex(
+            _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(offsets), B, n_d, V, dt, float(temperature),
+            int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(out_tokens), _ptr(ws),
+            ws.numel() * ws.element_size(), stream, ctypes.byref(dg) if dg is not None else None)
+    if rc != 0:
+        raise SdvError(rc, "sdv_verify_ex")
+    return accepted_len, out_tokens, dvals
+
+
+def verify(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, offsets: torch.Tensor,
+           temperature: float, seed: int, *, out: tuple | None = None, workspace: torch.Tensor | None = None):
+    """sdv_verify: (accepted_len [B] int32, out_tokens [n_draft_rows + B] int32), enqueued on the current stream."""
+    a, o, _ = verify_ex(target, draft, draft_tokens, offsets, temperature, seed, out=out, workspace=workspace)
+    return a, o
+
+
+def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor) -> torch.Tensor:
+    """Raw device Philox4x32-10 blocks: counters [n, 4] and keys [n, 2] (int32 views of uint32 words)."""
+    n = counters.shape[0]
+    out = torch.empty((n, 4), dtype=torch.int32, device=counters.device)
+    with torch.cuda.device(counters.device):
+        rc = _native.lib().sdv_philox4x32_10(_ptr(counters), _ptr(keys), n, _ptr(out),
+                                             torch.cuda.current_stream(counters.device).cuda_stream)
+    if rc != 0:
+        raise SdvError(rc, "sdv_philox4x32_10")
+    return out

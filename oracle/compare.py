@@ -1,0 +1,43 @@
+"""GPU-vs-oracle verdict comparison with first-divergence attribution.
+
+TEST INFRASTRUCTURE ONLY.  A request's verdict (accepted length and emitted tokens) must equal the
+oracle's exactly.  The only excuse is a first divergence at a decision the oracle itself took
+within ``eps`` of its threshold: an accept test with |r - p/q| < eps, or an extra-token draw whose
+CDF margin is below eps.  Greedy verdicts have no excuse.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def compare_verdicts(acc_gpu, out_gpu, ref: dict, cu, temperature: float, eps: float = 1e-6) -> dict:
+    """ref: oracle.verify(..., diag=True).  Returns counts and the list of hard mismatches."""
+    acc_gpu = np.asarray(acc_gpu)
+    out_gpu = np.asarray(out_gpu)
+    cu = np.asarray(cu)
+    acc_ref, out_ref = ref["accepted_len"], ref["out_tokens"]
+    B = acc_ref.shape[0]
+    hard, excused = [], []
+    for i in range(B):
+        K = int(cu[i + 1] - cu[i])
+        if acc_ref[i] == -1 and not (0 <= K <= 64 and cu[i] >= 0 and cu[i + 1] <= out_ref.shape[0] - B):
+            if acc_gpu[i] != -1:
+                hard.append((i, "invalid request not rejected"))
+            continue
+        s = slice(int(cu[i]) + i, int(cu[i]) + i + K + 1)
+        if acc_gpu[i] == acc_ref[i] and np.array_equal(out_gpu[s], out_ref[s]):
+            continue
+        if temperature == 0 or acc_ref[i] == -1 or acc_gpu[i] == -1:
+            hard.append((i, f"accepted {acc_gpu[i]} vs {acc_ref[i]}"))
+            continue
+        a_g, a_r = int(acc_gpu[i]), int(acc_ref[i])
+        if a_g != a_r:
+            j = min(a_g, a_r)  # the first position whose accept decision differs
+            margin = ref["accept_margin"][int(cu[i]) + j]
+            what = f"accept decision at position {j}, oracle margin {margin:.3g}"
+        else:
+            prefix_ok = np.array_equal(out_gpu[s][:a_r], out_ref[s][:a_r]) and (out_gpu[s][a_r + 1:] == -1).all()
+            margin = ref["cdf_margin"][i] if prefix_ok else np.inf
+            what = f"drawn token {out_gpu[s][a_r]} vs {out_ref[s][a_r]}, oracle CDF margin {margin:.3g}"
+        (excused if margin < eps else hard).append((i, what))
+    return {"requests": B, "hard": hard, "excused": excused, "n_hard": len(hard), "n_excused": len(excused)}

@@ -1,0 +1,54 @@
+"""Shared helpers for the GPU parity tests: upload a workload, run the HIP path through the C ABI
+(via the package's ctypes binding), run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import lossless_draft_verification_online_amd as sdv
+from oracle import oracle
+from oracle.compare import compare_verdicts
+
+DEV = torch.device("cuda:0")
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(a: np.ndarray | None, dtype: str):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def upload(b):
+    return (to_device(b.target, b.dtype), to_device(b.draft, b.dtype),
+            torch.from_numpy(b.tokens).to(DEV), torch.from_numpy(b.cu).to(DEV))
+
+
+def run_gpu(b, diag=(), seed=None, dev_inputs=None):
+    t, d, x, cu = upload(b) if dev_inputs is None else dev_inputs
+    acc, out, dg = sdv.verify_ex(t, d, x, cu, b.temperature, b.seed if seed is None else seed, diag=diag)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.cpu().numpy(), {k: v.cpu().numpy() for k, v in dg.items()}
+
+
+def run_oracle(b, seed=None):
+    return oracle.verify(b.target, b.draft, b.tokens, b.cu, b.temperature, b.seed if seed is None else seed,
+                         diag=True)
+
+
+def check_parity(b, seed=None, eps=1e-6, dev_inputs=None, diag=("terminal_kind",)):
+    """GPU verdicts equal the oracle's, except first divergences at oracle margins below eps."""
+    log(f"  parity {b.name}: B={b.B} n_draft_rows={b.n_draft_rows} V={b.V} {b.dtype} T={b.temperature}")
+    acc, out, dg = run_gpu(b, diag=diag, seed=seed, dev_inputs=dev_inputs)
+    ref = run_oracle(b, seed=seed)
+    cmp = compare_verdicts(acc, out, ref, b.cu, b.temperature, eps=eps)
+    assert cmp["n_hard"] == 0, f"{b.name}: hard mismatches {cmp['hard'][:10]}"
+    return acc, out, ref, cmp, dg

@@ -1,0 +1,93 @@
+"""The C ABI of libsdv.so: every function include/sdv.h declares is exported, and host-side
+argument checks reject bad calls before anything is launched (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from lossless_draft_verification_online_amd import _native
+from lossless_draft_verification_online_amd.build import LIBRARY, is_stale
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sdv_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if is_stale():
+        pytest.fail(f"{LIBRARY} is missing or older than its sources; run __graft_entry__.build()")
+    return _native.lib()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
+                          "sdv_status_string", "sdv_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.sdv_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.sdv_status_string(code) not in (None, b"", b"unknown status")
+    assert lib.sdv_status_string(17) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    # row-pass records (8 B per 16 KiB chunk of every row) + 32 B per request + 8 B per request-chunk
+    ws = lib.sdv_workspace_bytes(256, 1024, 128256, 0)
+    chunks = (128256 + 8191) // 8192
+    assert chunks == 16
+    assert ws >= (1280 + 1024) * chunks * 8 + 256 * 32 + 256 * chunks * 8
+    assert ws % 256 == 0
+    assert lib.sdv_workspace_bytes(0, 10, 10, 0) == 0
+    assert lib.sdv_workspace_bytes(1, -1, 10, 0) == 0
+    assert lib.sdv_workspace_bytes(1, 0, 10, 7) == 0
+    assert lib.sdv_workspace_bytes(1, 0, 1, 1) > 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its host-side checks
+
+
+def _call(lib, **kw):
+    args = dict(target=FAKE, draft=FAKE, tokens=FAKE, cu=FAKE, B=4, n_d=8, V=1000, dtype=0, T=1.0, seed=1,
+                acc=FAKE, out=FAKE, ws=FAKE * 16, ws_bytes=0, stream=None)
+    args.update(kw)
+    return lib.sdv_verify(args["target"], args["draft"], args["tokens"], args["cu"], args["B"], args["n_d"],
+                          args["V"], args["dtype"], args["T"], args["seed"], args["acc"], args["out"], args["ws"],
+                          args["ws_bytes"], args["stream"])
+
+
+def test_host_argument_errors(lib):
+    need = lib.sdv_workspace_bytes(4, 8, 1000, 0)
+    assert _call(lib, dtype=5) == -2
+    assert _call(lib, B=0) == -1
+    assert _call(lib, n_d=-1) == -1
+    assert _call(lib, V=0) == -1
+    assert _call(lib, target=None, ws_bytes=need) == -1
+    assert _call(lib, cu=None, ws_bytes=need) == -1
+    assert _call(lib, acc=None, ws_bytes=need) == -1
+    assert _call(lib, tokens=None, ws_bytes=need) == -1
+    assert _call(lib, T=-0.5, ws_bytes=need) == -1
+    assert _call(lib, T=float("nan"), ws_bytes=need) == -1
+    assert _call(lib, T=float("inf"), ws_bytes=need) == -1
+    assert _call(lib, T=1e-300, ws_bytes=need) == -1  # log2(e)/T overflows fp32
+    assert _call(lib, draft=None, ws_bytes=need) == -1  # sampling needs draft logits
+    assert _call(lib, ws_bytes=need - 1) == -4
+    assert _call(lib, ws=None, ws_bytes=need) == -4
+    assert _call(lib, ws=FAKE + 8, ws_bytes=need) == -4  # not 256-byte aligned
+    assert _call(lib, B=2**31 - 1, n_d=2**31 - 2, ws_bytes=2**62) == -3
+    assert lib.sdv_philox4x32_10(None, FAKE, 4, FAKE, None) == -1
+    assert lib.sdv_philox4x32_10(FAKE, FAKE, 0, FAKE, None) == -1
+
+
+def test_verify_ex_accepts_null_diag_checks_first(lib):
+    assert lib.sdv_verify_ex(FAKE, FAKE, FAKE, FAKE, 0, 8, 1000, 0, 1.0, 1, FAKE, FAKE, FAKE, 0, None, None) == -1

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded inputs.
+
+Verdicts (accepted lengths and every emitted token id) must match the oracle bit for bit; the only
+excuse is a first divergence at a decision the oracle took within 1e-6 of its threshold (|r - p/q|
+or the CDF margin of the draw), counted by the comparator.  Greedy verdicts allow no excuse.
+Intermediate values are checked too: log-normalisers and p/q ratios to 1e-5 relative on
+probabilities, argmaxes exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import DEV, check_parity, log, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+RTOL_PROB = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ----------------------------------------------------------------------------- Philox
+
+def test_device_philox_matches_oracle():
+    import lossless_draft_verification_online_amd as sdv
+    from oracle import oracle
+    rng = np.random.default_rng(0)
+    n = 4096
+    ctr = rng.integers(0, 2**32, size=(n, 4), dtype=np.uint64).astype(np.uint32)
+    key = rng.integers(0, 2**32, size=(n, 2), dtype=np.uint64).astype(np.uint32)
+    ctr[:64] = 0
+    key[:32] = 0
+    out = sdv.philox4x32_10(torch.from_numpy(ctr.view(np.int32)).to(DEV),
+                            torch.from_numpy(key.view(np.int32)).to(DEV)).cpu().numpy().view(np.uint32)
+    for b in range(n):
+        assert np.array_equal(out[b], oracle.philox4x32_10(ctr[b], key[b])), b
+
+
+def test_device_uniforms_match_oracle_blocks():
+    from oracle import oracle
+    b = W.make_random("philox_layout", np.full(16, 8), 64, "fp32", 1.0, 1.0, 1.0, 3, 0xFEEDFACECAFEBEEF)
+    _, _, dg = run_gpu(b, diag=("accept_uniform", "draw_uniform", "terminal_kind"))
+    grid = oracle.philox_grid(b.seed, 16, 9)
+    r = ((grid[:, :8, 0] >> 8) + 1).astype(np.float64) / 2**24
+    assert np.array_equal(dg["accept_uniform"].astype(np.float64), r.reshape(-1))
+
+
+# ----------------------------------------------------------------------------- row quantities
+
+@pytest.mark.parametrize("V,dtype", [(1000, "fp32"), (32000, "bf16"), (8192, "bf16"), (8193, "bf16"),
+                                     (20011, "bf16"), (13, "fp32"), (4099, "fp32")])
+def test_row_lse_and_ratio(V, dtype):
+    rng = np.random.default_rng(V)
+    depths = rng.integers(0, 9, size=12)
+    b = W.make_random(f"rows_v{V}", depths, V, dtype, 0.8, 3.0, rng.uniform(0.5, 3, 12), V, 77)
+    _, _, dg = run_gpu(b, diag=("target_lse", "draft_lse", "ratio"))
+    ref = run_oracle(b)
+    # an LSE error dL is a relative probability error of about dL
+    np.testing.assert_allclose(dg["target_lse"], ref["target_lse"], rtol=0, atol=RTOL_PROB)
+    np.testing.assert_allclose(dg["draft_lse"], ref["draft_lse"], rtol=0, atol=RTOL_PROB)
+    np.testing.assert_allclose(dg["ratio"], ref["ratio"], rtol=RTOL_PROB, atol=0)
+
+
+@pytest.mark.parametrize("V", [1, 7, 8192, 8193, 151936])
+def test_row_argmax_exact_with_ties(V):
+    rng = np.random.default_rng(V + 5)
+    depths = rng.integers(0, 5, size=16)
+    b = W.make_random(f"argmax_v{V}", depths, V, "bf16", 0.0, 4.0, 1.0, V + 1, 0)
+    # plant ties at the row maximum in half of the rows
+    tv = W.bf16_to_f32(b.target).copy()
+    for r in range(0, tv.shape[0], 2):
+        k = min(V, 4)
+        idx = rng.choice(V, size=k, replace=False)
+        tv[r, idx] = tv[r].max() + 1.0
+    b.target = W.bf16_bits(tv)
+    _, _, dg = run_gpu(b, diag=("target_argmax",))
+    np.testing.assert_array_equal(dg["target_argmax"], np.argmax(W.bf16_to_f32(b.target), axis=1))
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+def test_workload_b1_v1000_fp32_100_rounds():
+    n_exc = 0
+    for rnd in range(100):
+        _, _, _, cmp, _ = check_parity(W.small_b1(rnd))
+        n_exc += cmp["n_excused"]
+    log(f"  100 rounds: {n_exc} near-tie excuses")
+
+
+def test_workload_exactness_v8_subset():
+    for case in range(8):
+        for blk in range(2):
+            check_parity(W.exactness_batch(case, blk))
+
+
+def test_workload_b64_v32000_bf16():
+    for seed in range(4):
+        check_parity(W.uniform_b64(verify_seed=3000 + seed))
+
+
+def test_workload_b256_ragged_v128256_bf16_full():
+    b = W.ragged_b256()
+    dev_inputs = (to_device(b.target, b.dtype), to_device(b.draft, b.dtype), torch.from_numpy(b.tokens).to(DEV),
+                  torch.from_numpy(b.cu).to(DEV))
+    for seed in (4000, 4001):
+        acc, out, ref, cmp, dg = check_parity(b, seed=seed, dev_inputs=dev_inputs)
+        kinds = dg["terminal_kind"]
+        log(f"  seed {seed}: mean accepted {acc.mean():.3f}, residual draws {(kinds == 2).sum()}, "
+            f"bonus {(kinds == 1).sum()}, excused {cmp['n_excused']}")
+
+
+def test_workload_greedy_b512_v151936_bf16_full():
+    b = W.greedy_b512()
+    acc, out, ref, cmp, dg = check_parity(b)
+    assert cmp["n_excused"] == 0
+    log(f"  greedy mean accepted {acc.mean():.3f}")
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def test_all_requests_k0():
+    b = W.make_random("k0", np.zeros(37, int), 5000, "bf16", 1.0, 3.0, 1.0, 9, 10)
+    acc, out, *_ = check_parity(b)
+    assert (acc == 0).all()
+
+
+def test_depth_64_and_mixed():
+    b = W.make_random("k64", [64, 0, 63, 1, 64], 700, "fp32", 1.0, 1.0, 0.05, 10, 11)
+    check_parity(b)
+    g = W.make_random("k64g", [64, 0, 63, 1, 64], 700, "fp32", 0.0, 1.0, 0.0, 10, 11)
+    acc, out, ref, cmp, _ = check_parity(g)
+    assert acc[0] == 64 and acc[4] == 64  # the drafter proposes the target argmax itself
+
+
+@pytest.mark.parametrize("V,dtype", [(1, "fp32"), (1, "bf16"), (7, "bf16"), (13, "fp32"), (8192, "bf16"),
+                                     (8193, "bf16"), (65541, "bf16"), (4096, "fp32"), (4097, "fp32")])
+def test_vocab_sizes_and_ragged_tails(V, dtype):
+    rng = np.random.default_rng(V * 3 + len(dtype))
+    depths = rng.integers(0, 9, size=20)
+    for T in (1.0, 0.0):
+        b = W.make_random(f"v{V}", depths, V, dtype, T, 2.0, rng.uniform(0.3, 2.0, 20), V + 3, 7)
+        check_parity(b)
+
+
+def test_bad_requests_are_isolated():
+    rng = np.random.default_rng(21)
+    depths = [3, 2, 4, 0, 5]
+    b = W.make_random("bad", depths, 3000, "bf16", 1.0, 3.0, 1.0, 21, 22)
+    good_acc, good_out, *_ = run_gpu(b)
+    b.tokens = b.tokens.copy()
+    b.tokens[b.cu[1] + 1] = 3000                     # request 1: token out of range
+    d = W.bf16_to_f32(b.draft).copy()
+    d[b.cu[2] + 3, b.tokens[b.cu[2] + 3]] = -np.inf  # request 2: q(x) = 0 at its last position
+    b.draft = W.bf16_bits(d)
+    acc, out, ref, cmp, _ = check_parity(b)
+    assert acc[1] == -1 and acc[2] == -1
+    assert (out[b.cu[1] + 1: b.cu[3] + 3] == -1).all()
+    keep = [0, 3, 4]
+    assert np.array_equal(acc[keep], good_acc[keep])
+
+
+def test_depth_over_limit_writes_nothing():
+    b = W.make_random("limit", [65, 2], 64, "fp32", 1.0, 1.0, 1.0, 5, 6)
+    t, d, x, cu = (to_device(b.target, "fp32"), to_device(b.draft, "fp32"), torch.from_numpy(b.tokens).to(DEV),
+                   torch.from_numpy(b.cu).to(DEV))
+    import lossless_draft_verification_online_amd as sdv
+    out = torch.full((b.n_draft_rows + 2,), -7, dtype=torch.int32, device=DEV)
+    acc = torch.empty(2, dtype=torch.int32, device=DEV)
+    sdv.verify(t, d, x, cu, 1.0, 6, out=(acc, out))
+    torch.cuda.synchronize()
+    assert acc.cpu().tolist()[0] == -1 and acc.cpu().tolist()[1] >= 0
+    assert (out[:66].cpu().numpy() == -7).all()
+
+
+def test_draft_equal_to_target_accepts_all():
+    rng = np.random.default_rng(3)
+    depths = rng.integers(0, 9, size=32)
+    b = W.make_random("same", depths, 40000, "bf16", 1.0, 3.0, 0.0, 31, 32)
+    acc, out, ref, cmp, dg = check_parity(b, diag=("ratio", "terminal_kind"))
+    assert np.array_equal(acc, depths)
+    assert (dg["ratio"] == 1.0).all()
+
+
+def test_repeat_launches_are_deterministic():
+    b = W.uniform_b64()
+    ins = (to_device(b.target, b.dtype), to_device(b.draft, b.dtype), torch.from_numpy(b.tokens).to(DEV),
+           torch.from_numpy(b.cu).to(DEV))
+    first = run_gpu(b, dev_inputs=ins, diag=("target_lse", "ratio"))
+    for _ in range(20):
+        again = run_gpu(b, dev_inputs=ins, diag=("target_lse", "ratio"))
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
+        assert np.array_equal(first[2]["target_lse"], again[2]["target_lse"])
+        assert np.array_equal(first[2]["ratio"], again[2]["ratio"], equal_nan=True)
