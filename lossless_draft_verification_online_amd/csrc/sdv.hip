@@ -2,22 +2,25 @@
 //
 // The step verifies every request of a ragged batch at once (SDCP "Verification and Commit",
 // steps 5 to 7; Rule 1 and Rule 2 of its section "Acceptance Rules"; the r <= p/q test of
-// "SOTA-227", section "What to do").  It runs as three kernels on the caller's stream:
+// "SOTA-227", section "What to do").  Two kernels run on the caller's stream:
 //
-//   1. row pass      one wave64 per 16 KiB chunk of every logit row: a single coalesced read of
-//                    the chunk; at T > 0 it records the chunk's max-based exponent reference and
-//                    its sum of 2^(z k - ref) (k = log2(e)/T), at T = 0 the chunk's max and the
-//                    smallest index reaching it.  This kernel carries essentially all HBM traffic.
-//   2. accept scan   one wave64 per request: lane j folds the chunk records of its target and
-//                    draft rows into log-normalisers (fp64), gathers the two logits at the draft
-//                    token, forms p/q, draws r from Philox (seed; j, request) and the wave ballot
-//                    yields the first rejection.  Greedy requests finish here.
-//   3. terminal draw one workgroup per request (T > 0 only): chunk masses of the residual
-//                    max(p - q, 0) of the rejected position (re-reading that row pair), or of p
-//                    at the bonus position (from the row pass records, no re-read); the chunk
-//                    holding u * S is found by prefix sum and searched element by element.
+//  row_records   The stream.  One wave64 per 16 KiB chunk of every logit row reads the chunk once
+//                with 16-byte loads.  At T > 0 it records the chunk's exponent reference
+//                ref = fl(max z * k) and s = sum 2^(z k - ref), k = log2(e)/T; at T = 0 the chunk's
+//                maximum and the smallest index reaching it.  Waves never wait on each other, so
+//                nothing interrupts the stream.
+//  verdicts      One workgroup of 8 waves per request.  The waves fold the request's rows from
+//                their chunk records (fp64, lanes over chunks) into shared memory; wave 0 gathers the
+//                target and draft logits at each draft token, forms p/q, draws r from Philox
+//                (seed; position, request), and a ballot finds the first rejection.  Greedy
+//                terminals come from the folded argmax.  A bonus is drawn from p at position K
+//                using the bonus row's chunk records and one chunk re-read; a correction needs the
+//                chunk masses of max(p - q, 0) on the rejected row pair, which the 8 waves compute
+//                into shared memory before wave 0 draws.
 //
-// No matrix cores are involved: nothing here is a contraction.  The roofline is HBM bandwidth.
+// Nothing is handed between workgroups inside a kernel: the kernel boundary orders the stream
+// before the verdicts.  No matrix cores are involved: nothing here is a contraction, and the
+// roofline is HBM bandwidth.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -29,17 +32,7 @@
 
 namespace sdv {
 
-// Per-request hand-off from the accept scan to the terminal draw.
-struct ReqInfo {
-  int32_t kind;  // sdv_terminal_kind
-  int32_t t;     // drawn position
-  int32_t trow;  // target row of the drawn position
-  int32_t drow;  // draft row of the drawn position (residual draws), else -1
-  float u;       // draw uniform
-  float ref_t;   // weights are 2^(z_t k - ref_t): ref_t is the largest chunk reference of the target row
-  float e_hi;    // draft side: q-weights are 2^(z_d k - e), e = ref_t + log2-normaliser(draft) - (target),
-  float e_lo;    //   carried as e_hi + e_lo to keep fp64 accuracy
-};
+constexpr double kLn2 = 0.69314718055994530942;
 
 struct DiagPtrs {
   double* target_lse;
@@ -51,443 +44,538 @@ struct DiagPtrs {
   int32_t* terminal_kind;
 };
 
-constexpr double kLn2 = 0.69314718055994530942;
+struct Params {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* cu;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  float2* part;         // [row slots][C] chunk records; target row r is slot r, draft row d slot n_t + d
+  int32_t B, n_d, n_t, V, C;
+  int64_t n_units;
+  float k2;  // log2(e) / T, or 0 for the greedy rule
+  uint64_t seed;
+  DiagPtrs dg;
+};
 
-// ============================================================================ 1. row pass
+// ============================================================================ offsets
 
-template <class E, bool kGreedy>
-__device__ inline void finish_chunk_greedy(float best, int32_t idx, float2* out, int lane) {
-  wave_argmax(best, idx);
-  if (lane == 0) *out = make_float2(best, __int_as_float(idx));
+// cu[0] = 0, non-decreasing, cu[B] = n_d.  Anything else rejects the whole batch.
+__device__ __forceinline__ bool offsets_valid(const Params& P, int lane) {
+  bool bad = false;
+  for (int32_t j = lane; j < P.B; j += kWave) bad |= P.cu[j] > P.cu[j + 1];
+  if (lane == 0) bad |= P.cu[0] != 0 || P.cu[P.B] != P.n_d;
+  return __ballot(bad) == 0;
 }
 
-// 16-byte vector path: every row starts 16-byte aligned (row bytes and base pointers are multiples of 16).
-template <class E, bool kGreedy>
-__global__ __launch_bounds__(256) void row_pass_vec(const void* __restrict__ target, const void* __restrict__ draft,
-                                                    int32_t n_target_rows, int32_t V, int32_t n_chunks,
-                                                    int64_t n_units, float k2, float2* __restrict__ part) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t unit = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (unit >= n_units) return;
-  const int32_t row = (int32_t)(unit / n_chunks);
-  const int32_t chunk = (int32_t)(unit - (int64_t)row * n_chunks);
-  const char* rp = row < n_target_rows ? row_ptr<E>(target, row, V) : row_ptr<E>(draft, row - n_target_rows, V);
-  const int32_t c0 = chunk * E::kChunk;
-  const int32_t nvec = min(E::kChunk, V - c0) / E::kPerVec;
-  const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+// ============================================================================ 1. the stream
 
-  u32x4 buf[kVecPerLane];
-#pragma unroll
-  for (int k = 0; k < kVecPerLane; ++k) {
-    const int vi = lane + kWave * k;
-    buf[k] = vi < nvec ? vp[vi] : u32x4{E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord};
-  }
+template <class E>
+__device__ __forceinline__ u32x4 neg_inf_vec() {
+  return u32x4{E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord};
+}
 
-  if constexpr (kGreedy) {
-    float best = -INFINITY;
-    int32_t idx = INT32_MAX;
+// One 16 KiB chunk: (ref, sum 2^(z k - ref)) at T > 0, (max, first index of max) at T = 0.
+template <class E, bool kGreedy, bool kVec>
+__device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32_t n, float k2, int lane) {
+  if constexpr (kVec) {
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+    const int32_t nvec = n / E::kPerVec;
+    // the stream is read once: non-temporal loads keep it from displacing reused lines in L2
+    u32x4 buf[kVecPerLane];
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
-      float f[E::kPerVec];
-      E::unpack(buf[k], f);
-      const int32_t e0 = c0 + (lane + kWave * k) * E::kPerVec;
+      const int vi = lane + kWave * k;
+      buf[k] = vi < nvec ? __builtin_nontemporal_load(vp + vi) : neg_inf_vec<E>();
+    }
+    if constexpr (kGreedy) {
+      float best = -INFINITY;
+      int32_t idx = INT32_MAX;
 #pragma unroll
-      for (int e = 0; e < E::kPerVec; ++e) {
-        if (f[e] > best) {  // ascending within the lane: the first maximum is kept
-          best = f[e];
-          idx = e0 + e;
+      for (int k = 0; k < kVecPerLane; ++k) {
+        float f[E::kPerVec];
+        E::unpack(buf[k], f);
+        const int32_t e0 = c0 + (lane + kWave * k) * E::kPerVec;
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) {
+          if (f[e] > best) {  // ascending within the lane: the first maximum is kept
+            best = f[e];
+            idx = e0 + e;
+          }
         }
       }
-    }
-    finish_chunk_greedy<E, kGreedy>(best, idx, part + unit, lane);
-  } else {
-    float m = -INFINITY;
+      wave_argmax(best, idx);
+      return make_float2(best, __int_as_float(idx));
+    } else {
+      float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-      float f[E::kPerVec];
-      E::unpack(buf[k], f);
+      for (int k = 0; k < kVecPerLane; ++k) {
+        float f[E::kPerVec];
+        E::unpack(buf[k], f);
 #pragma unroll
-      for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
-    }
-    m = wave_max(m);
-    float ref = -INFINITY, s = 0.0f;
-    if (m != -INFINITY) {
-      ref = m * k2;
+        for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
+      }
+      m = wave_max(m);
+      if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+      const float ref = m * k2;
       float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < kVecPerLane; ++k) {
+        // re-unpack from the raw words rather than keep every unpacked element live across the max
+        asm volatile("" : "+v"(buf[k]));
         float f[E::kPerVec];
         E::unpack(buf[k], f);
 #pragma unroll
         for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
         acc[k & 3] += tree_sum(f);
       }
-      s = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+      return make_float2(ref, wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3])));
     }
-    if (lane == 0) part[unit] = make_float2(ref, s);
-  }
-}
-
-// Element-wise path for rows that are not 16-byte aligned: two passes over the chunk.
-template <class E, bool kGreedy>
-__global__ __launch_bounds__(256) void row_pass_scalar(const void* __restrict__ target,
-                                                       const void* __restrict__ draft, int32_t n_target_rows,
-                                                       int32_t V, int32_t n_chunks, int64_t n_units, float k2,
-                                                       float2* __restrict__ part) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t unit = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (unit >= n_units) return;
-  const int32_t row = (int32_t)(unit / n_chunks);
-  const int32_t chunk = (int32_t)(unit - (int64_t)row * n_chunks);
-  const char* rp = row < n_target_rows ? row_ptr<E>(target, row, V) : row_ptr<E>(draft, row - n_target_rows, V);
-  const int32_t c0 = chunk * E::kChunk;
-  const int32_t c1 = min(c0 + E::kChunk, V);
-  if constexpr (kGreedy) {
-    float best = -INFINITY;
-    int32_t idx = INT32_MAX;
-    for (int32_t v = c0 + lane; v < c1; v += kWave) {
-      const float z = E::at(rp, v);
-      if (z > best) {
-        best = z;
-        idx = v;
-      }
-    }
-    finish_chunk_greedy<E, kGreedy>(best, idx, part + unit, lane);
   } else {
-    float m = -INFINITY;
-    for (int32_t v = c0 + lane; v < c1; v += kWave) m = fmaxf(m, E::at(rp, v));
-    m = wave_max(m);
-    float ref = -INFINITY, s = 0.0f;
-    if (m != -INFINITY) {
-      ref = m * k2;
+    const int32_t c1 = c0 + n;
+    if constexpr (kGreedy) {
+      float best = -INFINITY;
+      int32_t idx = INT32_MAX;
+      for (int32_t v = c0 + lane; v < c1; v += kWave) {
+        const float z = E::at(rp, v);
+        if (z > best) {
+          best = z;
+          idx = v;
+        }
+      }
+      wave_argmax(best, idx);
+      return make_float2(best, __int_as_float(idx));
+    } else {
+      float m = -INFINITY;
+      for (int32_t v = c0 + lane; v < c1; v += kWave) m = fmaxf(m, E::at(rp, v));
+      m = wave_max(m);
+      if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+      const float ref = m * k2;
+      float s = 0.0f;
       for (int32_t v = c0 + lane; v < c1; v += kWave) s += fast_exp2(fmaf(E::at(rp, v), k2, -ref));
-      s = wave_sum(s);
-    }
-    if (lane == 0) part[unit] = make_float2(ref, s);
-  }
-}
-
-// ============================================================================ 2. accept scan
-
-struct Frame {
-  double l2;  // log2 sum_v 2^(z_v k)
-  float ref;  // largest chunk reference of the row
-};
-
-// Fold the chunk records of one row: l2 = R + log2(sum_c s_c 2^(ref_c - R)), R = max_c ref_c.
-__device__ inline Frame fold_row(const float2* __restrict__ p, int32_t n_chunks) {
-  float R = -INFINITY;
-  for (int32_t c = 0; c < n_chunks; ++c) R = fmaxf(R, p[c].x);
-  if (R == -INFINITY) return {-(double)INFINITY, R};
-  double s = 0.0;
-  for (int32_t c = 0; c < n_chunks; ++c) s += (double)p[c].y * exp2((double)p[c].x - (double)R);
-  return {(double)R + log2(s), R};
-}
-
-// Chunk maxima in ascending order with a strict comparison: the smallest index of the row maximum.
-__device__ inline int32_t fold_argmax(const float2* __restrict__ p, int32_t n_chunks) {
-  float best = p[0].x;
-  int32_t idx = __float_as_int(p[0].y);
-  for (int32_t c = 1; c < n_chunks; ++c) {
-    if (p[c].x > best) {
-      best = p[c].x;
-      idx = __float_as_int(p[c].y);
-    }
-  }
-  return idx == INT32_MAX ? 0 : idx;  // a row of -inf only: index 0
-}
-
-__device__ inline void reject_request(int32_t i, int32_t trow0, int K, int lane, int32_t* accepted_len,
-                                      int32_t* out_tokens, ReqInfo* info, const DiagPtrs& dg) {
-  for (int j = lane; j <= K; j += kWave) out_tokens[trow0 + j] = -1;
-  if (lane == 0) {
-    accepted_len[i] = -1;
-    info[i].kind = SDV_TERM_BAD;
-    if (dg.terminal_kind) dg.terminal_kind[i] = SDV_TERM_BAD;
-  }
-}
-
-template <class E, bool kGreedy>
-__global__ __launch_bounds__(64) void accept_scan(const void* __restrict__ target, const void* __restrict__ draft,
-                                                  const int32_t* __restrict__ tokens, const int32_t* __restrict__ cu,
-                                                  int32_t B, int32_t n_draft_rows, int32_t V, int32_t n_chunks,
-                                                  float k2, uint64_t seed, const float2* __restrict__ part,
-                                                  int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
-                                                  ReqInfo* __restrict__ info, DiagPtrs dg) {
-  const int32_t i = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int32_t lo = cu[i], hi = cu[i + 1];
-  const int64_t K64 = (int64_t)hi - (int64_t)lo;
-  if (lo < 0 || hi > n_draft_rows || K64 < 0 || K64 > SDV_MAX_DEPTH) {
-    // offsets that name no valid slot range: report the request and write no slot
-    if (lane == 0) {
-      accepted_len[i] = -1;
-      info[i].kind = SDV_TERM_BAD;
-      if (dg.terminal_kind) dg.terminal_kind[i] = SDV_TERM_BAD;
-    }
-    return;
-  }
-  const int K = (int)K64;
-  const int32_t n_target_rows = n_draft_rows + B;
-  const int32_t trow0 = lo + i, drow0 = lo;
-  const bool active = lane < K;
-  const int32_t x = active ? tokens[drow0 + lane] : 0;
-  if (__ballot(active && (x < 0 || x >= V)) != 0) {
-    reject_request(i, trow0, K, lane, accepted_len, out_tokens, info, dg);
-    return;
-  }
-
-  if constexpr (kGreedy) {
-    const int32_t g = lane <= K ? fold_argmax(part + (int64_t)(trow0 + lane) * n_chunks, n_chunks) : 0;
-    const uint64_t miss = __ballot(active && x != g);
-    const int a = miss ? __ffsll((unsigned long long)miss) - 1 : K;
-    int32_t g_a = __shfl(g, a & (kWave - 1), kWave);
-    int32_t g_last = 0;
-    if (K == kWave) {  // target row 64 has no lane of its own
-      g_last = fold_argmax(part + (int64_t)(trow0 + kWave) * n_chunks, n_chunks);
-      if (a == kWave) g_a = g_last;
-    }
-    for (int j = lane; j <= K; j += kWave) out_tokens[trow0 + j] = j < a ? x : (j == a ? g_a : -1);
-    if (dg.target_argmax) {
-      if (lane <= K) dg.target_argmax[trow0 + lane] = g;
-      if (K == kWave && lane == 0) dg.target_argmax[trow0 + kWave] = g_last;
-    }
-    if (lane == 0) {
-      accepted_len[i] = a;
-      info[i].kind = SDV_TERM_GREEDY;
-      if (dg.terminal_kind) dg.terminal_kind[i] = SDV_TERM_GREEDY;
-    }
-  } else {
-    // target rows j <= K (the row at j = 64 is folded separately), draft rows j < K
-    Frame ft{0.0, 0.0f}, fd{0.0, 0.0f};
-    if (lane <= K) ft = fold_row(part + (int64_t)(trow0 + lane) * n_chunks, n_chunks);
-    double ratio = 0.0;
-    float r = 1.0f;
-    bool qzero = false;
-    Philox4 blk{0u, 0u, 0u, 0u};
-    if (active) {
-      fd = fold_row(part + (int64_t)(n_target_rows + drow0 + lane) * n_chunks, n_chunks);
-      const float zt = E::at(row_ptr<E>(target, trow0 + lane, V), x);
-      const float zd = E::at(row_ptr<E>(draft, drow0 + lane, V), x);
-      qzero = zd == -INFINITY;
-      // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
-      const double lr2 = ((double)zt - (double)zd) * (double)k2 - (ft.l2 - fd.l2);
-      ratio = exp2(lr2);
-      blk = verifier_block(seed, (uint32_t)i, (uint32_t)lane);
-      r = accept_uniform(blk);
-    }
-    if (__ballot(qzero) != 0) {  // q(x) = 0 somewhere: rejected before any uniform is used
-      reject_request(i, trow0, K, lane, accepted_len, out_tokens, info, dg);
-      return;
-    }
-    const uint64_t rej = __ballot(active && !((double)r <= ratio));
-    const int a = rej ? __ffsll((unsigned long long)rej) - 1 : K;
-
-    Frame f_last{0.0, 0.0f};
-    if (K == kWave) f_last = fold_row(part + (int64_t)(trow0 + kWave) * n_chunks, n_chunks);
-    const float ref_bonus = K == kWave ? f_last.ref : __shfl(ft.ref, K & (kWave - 1), kWave);
-    if (a < K) {
-      if (lane == a) {
-        ReqInfo in;
-        in.kind = SDV_TERM_RESIDUAL;
-        in.t = a;
-        in.trow = trow0 + a;
-        in.drow = drow0 + a;
-        in.u = draw_uniform(blk);
-        in.ref_t = ft.ref;
-        const double e = (double)ft.ref + fd.l2 - ft.l2;
-        in.e_hi = (float)e;
-        in.e_lo = (float)(e - (double)in.e_hi);
-        info[i] = in;
-      }
-    } else if (lane == 0) {
-      ReqInfo in;
-      in.kind = SDV_TERM_BONUS;
-      in.t = K;
-      in.trow = trow0 + K;
-      in.drow = -1;
-      in.u = draw_uniform(verifier_block(seed, (uint32_t)i, (uint32_t)K));
-      in.ref_t = ref_bonus;
-      in.e_hi = 0.0f;
-      in.e_lo = 0.0f;
-      info[i] = in;
-    }
-    for (int j = lane; j <= K; j += kWave) out_tokens[trow0 + j] = j < a ? x : -1;
-    if (lane == 0) accepted_len[i] = a;
-
-    if (dg.target_lse && lane <= K) dg.target_lse[trow0 + lane] = ft.l2 * kLn2;
-    if (dg.target_lse && K == kWave && lane == 0) dg.target_lse[trow0 + kWave] = f_last.l2 * kLn2;
-    if (active) {
-      if (dg.draft_lse) dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
-      if (dg.ratio) dg.ratio[drow0 + lane] = ratio;
-      if (dg.accept_uniform) dg.accept_uniform[drow0 + lane] = r;
-    }
-    if (lane == 0) {
-      if (dg.terminal_kind) dg.terminal_kind[i] = a < K ? SDV_TERM_RESIDUAL : SDV_TERM_BONUS;
-    }
-    if (dg.draw_uniform) {
-      if (a < K && lane == a) dg.draw_uniform[i] = draw_uniform(blk);
-      if (a == K && lane == 0) dg.draw_uniform[i] = draw_uniform(verifier_block(seed, (uint32_t)i, (uint32_t)K));
+      return make_float2(ref, wave_sum(s));
     }
   }
 }
-
-// ============================================================================ 3. terminal draw
 
 // Residual weight max(p - q, 0), both sides scaled by the same factor 2^(l2_t - ref_t).
-__device__ inline float resid_weight(float zt, float zd, float k2, float ref_t, float e_hi, float e_lo) {
+__device__ __forceinline__ float resid_weight(float zt, float zd, float k2, float ref_t, float e_hi, float e_lo) {
   const float p = fast_exp2(fmaf(zt, k2, -ref_t));
   const float q = fast_exp2(fmaf(zd, k2, -e_hi) - e_lo);
   return fmaxf(p - q, 0.0f);
 }
 
-__device__ inline float target_weight(float zt, float k2, float ref_t) { return fast_exp2(fmaf(zt, k2, -ref_t)); }
+// Inverse CDF inside one chunk: the smallest v in [c0, c0 + n) whose running mass exceeds target.
+// Step 1: lane l sums the weights of its contiguous run [c0 + l*run, c0 + (l+1)*run) (16 vector
+// loads); a wave scan of the run totals (fp64) picks the run that crosses the target.  Step 2: the
+// wave re-reads that run, each lane taking run/64 consecutive elements, and a second scan picks the
+// element.  If rounding leaves the target unreached, the last element of positive weight is taken.
+template <class E, bool kVec, bool kResid>
+__device__ __forceinline__ int32_t search_chunk(const char* trow, const char* drow, int32_t c0, int32_t n, double target,
+                                float k2, float ref_t, float e_hi, float e_lo, int lane) {
+  constexpr int run = kVecPerLane * E::kPerVec;  // 128 bf16 or 64 fp32 elements
+  constexpr int per_lane = run / kWave;          // 2 or 1 elements per lane in step 2
+  auto weight = [&](float zt, float zd) -> float {
+    if constexpr (kResid) return resid_weight(zt, zd, k2, ref_t, e_hi, e_lo);
+    return fast_exp2(fmaf(zt, k2, -ref_t));
+  };
+  const int32_t end = c0 + n;
+  // step 1: run totals
+  const int32_t b = c0 + lane * run;
+  double tot = 0.0;
+  if constexpr (kVec) {
+    const u32x4* tp = reinterpret_cast<const u32x4*>(trow + (int64_t)b * E::kBytes);
+    const u32x4* dp = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)b * E::kBytes);
+    constexpr int kHalf = kVecPerLane / 2;  // two halves bound the registers held per lane
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      asm volatile("" ::: "memory");  // keep the second half's loads after the first half's use
+      u32x4 tb[kHalf], db[kHalf];
+#pragma unroll
+      for (int k = 0; k < kHalf; ++k) {
+        const bool ok = b + (h * kHalf + k) * E::kPerVec < end;
+        tb[k] = ok ? tp[h * kHalf + k] : neg_inf_vec<E>();
+        if constexpr (kResid) db[k] = ok ? dp[h * kHalf + k] : neg_inf_vec<E>();
+      }
+#pragma unroll
+      for (int k = 0; k < kHalf; ++k) {
+        float ft[E::kPerVec], fd[E::kPerVec];
+        E::unpack(tb[k], ft);
+        if constexpr (kResid) E::unpack(db[k], fd);
+#pragma unroll
+        for (int q = 0; q < E::kPerVec; ++q) ft[q] = weight(ft[q], kResid ? fd[q] : 0.0f);
+        tot += (double)tree_sum(ft);
+      }
+    }
+  } else {
+    for (int32_t v = b; v < min(b + run, end); ++v)
+      tot += (double)weight(E::at(trow, v), kResid ? E::at(drow, v) : 0.0f);
+  }
+  const double before = wave_exclusive_scan(tot, lane);
+  const uint64_t hit = __ballot(b < end && before + tot > target);
+  const uint64_t pos = __ballot(b < end && tot > 0.0);
+  if (!hit && !pos) return end - 1;
+  // the run to open: the crossing run, or else the last run with positive mass
+  const int f = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)pos);
+  const double rest = target - __shfl(before, f, kWave);
+  // step 2: per_lane consecutive elements per lane inside run f
+  const int32_t bf = c0 + f * run;
+  float w[per_lane];
+  double sub = 0.0;
+#pragma unroll
+  for (int q = 0; q < per_lane; ++q) {
+    const int32_t v = bf + lane * per_lane + q;
+    w[q] = v < end ? weight(E::at(trow, v), kResid ? E::at(drow, v) : 0.0f) : 0.0f;
+    sub += (double)w[q];
+  }
+  const double sub_before = wave_exclusive_scan(sub, lane);
+  const uint64_t hit2 = __ballot(hit && sub_before + sub > rest);
+  const uint64_t pos2 = __ballot(sub > 0.0);
+  int32_t y = end - 1;
+  if (hit2) {
+    const int g = __ffsll((unsigned long long)hit2) - 1;
+    // the first element of lane g whose running mass exceeds rest (its last element if rounding
+    // leaves every partial sum short)
+    int32_t yl = bf + lane * per_lane + per_lane - 1;
+    double upto = sub_before;
+    bool found = false;
+#pragma unroll
+    for (int q = 0; q < per_lane; ++q) {
+      upto += (double)w[q];
+      if (!found && upto > rest) {
+        yl = bf + lane * per_lane + q;
+        found = true;
+      }
+    }
+    y = __shfl(yl, g, kWave);
+  } else if (pos2) {
+    const int h = 63 - __clzll((long long)pos2);
+    int32_t yl = -1;
+#pragma unroll
+    for (int q = 0; q < per_lane; ++q)
+      if (w[q] > 0.0f) yl = bf + lane * per_lane + q;
+    y = __shfl(yl, h, kWave);
+  }
+  return y;
+}
 
-// Residual mass of one chunk, coalesced 16-byte loads; fp32 per vector, fp64 across vectors and lanes.
+// Masses m_c (fp64) of the chunks of one row; returns the chunk holding u * S and the target inside it.
+// mass(c) is evaluated by every lane for its chunks; chunks are visited in ascending order.
+template <class MassFn>
+__device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, double* target_in_chunk, int lane) {
+  double S = 0.0;
+  for (int32_t c0 = 0; c0 < C; c0 += kWave) S += wave_sum(c0 + lane < C ? mass(c0 + lane) : 0.0);
+  const double U = u * S;
+  double carry = 0.0;
+  int32_t last_pos = -1;
+  double last_before = 0.0;
+  for (int32_t c0 = 0; c0 < C; c0 += kWave) {
+    const double m = c0 + lane < C ? mass(c0 + lane) : 0.0;
+    const double excl = wave_exclusive_scan(m, lane);
+    const uint64_t hit = __ballot(c0 + lane < C && carry + excl + m > U);
+    if (hit) {
+      const int f = __ffsll((unsigned long long)hit) - 1;
+      *target_in_chunk = U - (carry + __shfl(excl, f, kWave));
+      return c0 + f;
+    }
+    const uint64_t pos = __ballot(c0 + lane < C && m > 0.0);
+    if (pos) {
+      const int h = 63 - __clzll((long long)pos);
+      last_pos = c0 + h;
+      last_before = carry + __shfl(excl, h, kWave);
+    }
+    carry += wave_sum(m);
+  }
+  // rounding left U at or beyond the total: the last chunk with positive mass, targeting its end
+  if (last_pos < 0) {
+    *target_in_chunk = 0.0;
+    return C - 1;
+  }
+  *target_in_chunk = U - last_before;
+  return last_pos;
+}
+
+// Residual mass of one chunk of the rejected row pair: coalesced 16-byte loads, fp32 per vector,
+// fp64 across vectors and lanes.
 template <class E, bool kVec>
-__device__ double resid_chunk_mass(const char* trow, const char* drow, int32_t c0, int32_t n, float k2,
-                                   const ReqInfo& in, int lane) {
+__device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* dp, int32_t c0, int32_t n, float k2, float ref_t,
+                                   float e_hi, float e_lo, int lane) {
   double acc = 0.0;
   if constexpr (kVec) {
-    const u32x4* tp = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
-    const u32x4* dp = reinterpret_cast<const u32x4*>(drow + (int64_t)c0 * E::kBytes);
+    const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
+    const u32x4* dv = reinterpret_cast<const u32x4*>(dp + (int64_t)c0 * E::kBytes);
     const int32_t nvec = n / E::kPerVec;
-#pragma unroll 4
-    for (int k = 0; k < kVecPerLane; ++k) {
-      const int vi = lane + kWave * k;
-      if (vi < nvec) {
-        float ft[E::kPerVec], fd[E::kPerVec];
-        E::unpack(tp[vi], ft);
-        E::unpack(dp[vi], fd);
+    constexpr int kHalf = kVecPerLane / 2;  // two halves keep the register footprint at one chunk
 #pragma unroll
-        for (int e = 0; e < E::kPerVec; ++e) ft[e] = resid_weight(ft[e], fd[e], k2, in.ref_t, in.e_hi, in.e_lo);
+    for (int h = 0; h < 2; ++h) {
+      asm volatile("" ::: "memory");  // keep the second half's loads after the first half's use
+      u32x4 tb[kHalf], db[kHalf];
+#pragma unroll
+      for (int k = 0; k < kHalf; ++k) {
+        const int vi = lane + kWave * (h * kHalf + k);
+        tb[k] = vi < nvec ? tv[vi] : neg_inf_vec<E>();
+        db[k] = vi < nvec ? dv[vi] : neg_inf_vec<E>();
+      }
+#pragma unroll
+      for (int k = 0; k < kHalf; ++k) {
+        float ft[E::kPerVec], fd[E::kPerVec];
+        E::unpack(tb[k], ft);
+        E::unpack(db[k], fd);
+#pragma unroll
+        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, e_lo);
         acc += (double)tree_sum(ft);
       }
     }
   } else {
     for (int32_t v = c0 + lane; v < c0 + n; v += kWave)
-      acc += (double)resid_weight(E::at(trow, v), E::at(drow, v), k2, in.ref_t, in.e_hi, in.e_lo);
+      acc += (double)resid_weight(E::at(tp, v), E::at(dp, v), k2, ref_t, e_hi, e_lo);
   }
   return wave_sum(acc);
 }
 
-// Inverse CDF inside one chunk: the smallest v with (mass of chunk elements up to v) > target.
-// Each lane owns a contiguous run of the chunk; a wave scan of the run totals finds the lane and
-// that lane walks its run.  If rounding leaves the target unreached, the last element of positive
-// weight is taken.
-template <class E>
-__device__ int32_t search_chunk(bool residual, const char* trow, const char* drow, int32_t c0, int32_t n,
-                                double target, float k2, const ReqInfo& in, int lane) {
-  const int32_t run = (n + kWave - 1) / kWave;
-  const int32_t b = min(c0 + lane * run, c0 + n);
-  const int32_t e = min(b + run, c0 + n);
-  auto weight = [&](int32_t v) -> float {
-    return residual ? resid_weight(E::at(trow, v), E::at(drow, v), k2, in.ref_t, in.e_hi, in.e_lo)
-                    : target_weight(E::at(trow, v), k2, in.ref_t);
-  };
-  double tot = 0.0;
-  int32_t last_pos = -1;
-  for (int32_t v = b; v < e; ++v) {
-    const float w = weight(v);
-    tot += (double)w;
-    if (w > 0.0f) last_pos = v;
+template <class E, bool kGreedy, bool kVec>
+__global__ __launch_bounds__(256) void row_records(Params P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (u >= P.n_units) return;
+  const int32_t slot = (int32_t)(u / P.C);
+  const int32_t c = (int32_t)(u - (int64_t)slot * P.C);
+  const char* rp = slot < P.n_t ? row_ptr<E>(P.target, slot, P.V) : row_ptr<E>(P.draft, slot - P.n_t, P.V);
+  const int32_t c0 = c * E::kChunk;
+  const float2 rec = chunk_record<E, kGreedy, kVec>(rp, c0, min(E::kChunk, P.V - c0), P.k2, lane);
+  if (lane == 0) P.part[u] = rec;
+}
+
+// ============================================================================ 2. verdicts
+
+// Row fold by one wave, lanes over chunks.  T > 0: l2 = R + log2(sum_c s_c 2^(ref_c - R)) with
+// R = max_c ref_c.  T = 0: the row argmax (chunk maxima with their first indices; ties to the
+// smaller index).
+struct RowFold {
+  double l2;
+  float ref;
+  int32_t argmax;
+};
+
+template <bool kGreedy>
+__device__ __forceinline__ RowFold fold_row(const float2* p, int32_t C, int lane) {
+  RowFold f{0.0, -INFINITY, 0};
+  if constexpr (kGreedy) {
+    float best = -INFINITY;
+    int32_t idx = INT32_MAX;
+    for (int32_t c = lane; c < C; c += kWave) {
+      const float2 r = p[c];
+      const int32_t ri = __float_as_int(r.y);
+      if (r.x > best || (r.x == best && ri < idx)) {
+        best = r.x;
+        idx = ri;
+      }
+    }
+    wave_argmax(best, idx);
+    f.argmax = idx == INT32_MAX ? 0 : idx;  // a row of -inf only: index 0
+  } else {
+    float R = -INFINITY;
+    for (int32_t c = lane; c < C; c += kWave) R = fmaxf(R, p[c].x);
+    R = wave_max(R);
+    f.ref = R;
+    if (R == -INFINITY) {
+      f.l2 = -(double)INFINITY;
+      return f;
+    }
+    double s = 0.0;
+    for (int32_t c = lane; c < C; c += kWave) {
+      const float2 r = p[c];
+      if (r.y > 0.0f) s += (double)r.y * exp2((double)r.x - (double)R);
+    }
+    f.l2 = (double)R + log2(wave_sum(s));
   }
-  const double before = wave_exclusive_scan(tot, lane);
-  const uint64_t hit = __ballot(b < e && before + tot > target);
-  int32_t y = -1;
-  if (hit) {
-    const int f = __ffsll((unsigned long long)hit) - 1;
-    if (lane == f) {
-      double acc = before;
-      y = last_pos;
-      for (int32_t v = b; v < e; ++v) {
-        acc += (double)weight(v);
-        if (acc > target) {
-          y = v;
-          break;
+  return f;
+}
+
+__device__ __forceinline__ void write_reject(const Params& P, int32_t i, int32_t trow0, int K, bool write_slots, int lane) {
+  if (write_slots)
+    for (int j = lane; j <= K; j += kWave) P.out_tokens[trow0 + j] = -1;
+  if (lane == 0) {
+    P.accepted_len[i] = -1;
+    if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_BAD;
+  }
+}
+
+// Decision of wave 0, shared with the other waves of the workgroup.
+struct Decision {
+  int32_t kind;  // sdv_terminal_kind, SDV_TERM_BAD when the request is rejected
+  int32_t a;
+  float ref_t, e_hi, e_lo, u;
+};
+
+template <class E, bool kVec>
+__device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, int32_t i, int32_t trow0,
+                                              int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
+                                              int wave, int n_waves);
+
+constexpr int kVerdictWaves = 8;
+constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
+
+// One workgroup of 8 waves per request.  Shared memory: the folded rows, the decision, and the
+// residual chunk masses (C doubles, dynamic).
+template <class E, bool kGreedy, bool kVec>
+__global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
+  extern __shared__ double lds_mass[];  // [C]
+  __shared__ RowFold rows[kMaxRows];
+  __shared__ Decision dec;
+  const int32_t i = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n_waves = blockDim.x / kWave;
+
+  // screening: every wave reaches the same answer from the same loads
+  const bool ok_offsets = offsets_valid(P, lane);
+  const int32_t lo = ok_offsets ? P.cu[i] : 0, hi = ok_offsets ? P.cu[i + 1] : 0;
+  const int K = hi - lo;
+  const int32_t trow0 = lo + i, drow0 = lo;
+  if (!ok_offsets || K > SDV_MAX_DEPTH) {  // malformed batch, or the depth limit: no slot written
+    if (wave == 0) write_reject(P, i, 0, 0, false, lane);
+    return;
+  }
+  const float2* rec_t = P.part + (int64_t)trow0 * P.C;
+  const float2* rec_d = P.part + (int64_t)(P.n_t + drow0) * P.C;
+
+  // 1. fold the request's rows: r <= K target row r, r > K draft row r - K - 1
+  const int n_rows = kGreedy ? K + 1 : 2 * K + 1;
+  for (int r = wave; r < n_rows; r += n_waves) {
+    const float2* p = r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C;
+    const RowFold f = fold_row<kGreedy>(p, P.C, lane);
+    if (lane == 0) rows[r] = f;
+  }
+  __syncthreads();
+
+  // 2. the verdict, by wave 0
+  if (wave == 0) {
+    const bool active = lane < K;
+    const int32_t x = active ? P.tokens[drow0 + lane] : 0;
+    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
+      write_reject(P, i, trow0, K, true, lane);
+    } else if constexpr (kGreedy) {
+      const int32_t g = lane <= K ? rows[lane].argmax : 0;
+      const uint64_t miss = __ballot(active && x != g);
+      const int a = miss ? __ffsll((unsigned long long)miss) - 1 : K;
+      const int32_t g_a = rows[a].argmax;
+      for (int j = lane; j <= K; j += kWave) P.out_tokens[trow0 + j] = j < a ? x : (j == a ? g_a : -1);
+      if (P.dg.target_argmax)
+        for (int j = lane; j <= K; j += kWave) P.dg.target_argmax[trow0 + j] = rows[j].argmax;
+      if (lane == 0) {
+        P.accepted_len[i] = a;
+        if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_GREEDY;
+      }
+      d.kind = SDV_TERM_GREEDY;
+    } else {
+      RowFold ft{0.0, 0.0f, 0}, fd{0.0, 0.0f, 0};
+      double ratio = 0.0;
+      float r = 1.0f;
+      bool qzero = false;
+      Philox4 blk{0u, 0u, 0u, 0u};
+      if (active) {
+        ft = rows[lane];
+        fd = rows[K + 1 + lane];
+        const float zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
+        const float zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+        qzero = zd == -INFINITY;
+        // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
+        ratio = exp2(((double)zt - (double)zd) * (double)P.k2 - (ft.l2 - fd.l2));
+        blk = verifier_block(P.seed, (uint32_t)i, (uint32_t)lane);
+        r = accept_uniform(blk);
+      }
+      if (__ballot(qzero) != 0) {  // q(x) = 0 somewhere: rejected before any uniform is used
+        write_reject(P, i, trow0, K, true, lane);
+      } else {
+        const uint64_t rej = __ballot(active && !((double)r <= ratio));
+        const int a = rej ? __ffsll((unsigned long long)rej) - 1 : K;
+        // slot a is written by the draw below
+        for (int j = lane; j <= K; j += kWave)
+          if (j != a) P.out_tokens[trow0 + j] = j < a ? x : -1;
+        if (lane == 0) P.accepted_len[i] = a;
+        if (P.dg.target_lse)
+          for (int j = lane; j <= K; j += kWave) P.dg.target_lse[trow0 + j] = rows[j].l2 * kLn2;
+        if (active) {
+          if (P.dg.draft_lse) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
+          if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
+          if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = r;
+        }
+        d.a = a;
+        if (a == K) {
+          d.kind = SDV_TERM_BONUS;
+          d.ref_t = rows[K].ref;
+          d.u = draw_uniform(verifier_block(P.seed, (uint32_t)i, (uint32_t)K));
+        } else {
+          // weights in the frame 2^(z_t k - ref_t) of the rejected target row; draft side
+          // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi + e_lo
+          d.kind = SDV_TERM_RESIDUAL;
+          d.ref_t = __shfl(ft.ref, a, kWave);
+          const double e = (double)d.ref_t + __shfl(fd.l2, a, kWave) - __shfl(ft.l2, a, kWave);
+          d.e_hi = (float)e;
+          d.e_lo = (float)(e - (double)d.e_hi);
+          d.u = __shfl(draw_uniform(blk), a, kWave);
         }
       }
     }
-    y = __shfl(y, f, kWave);
-  } else {
-    const uint64_t has = __ballot(last_pos >= 0);
-    if (has) {
-      const int h = 63 - __clzll((long long)has);
-      y = __shfl(last_pos, h, kWave);
-    }
-  }
-  return y < 0 ? c0 + n - 1 : y;
-}
-
-template <class E, bool kVec>
-__global__ __launch_bounds__(256) void terminal_draw(const void* __restrict__ target, const void* __restrict__ draft,
-                                                     int32_t V, int32_t n_chunks, float k2,
-                                                     const float2* __restrict__ part,
-                                                     const ReqInfo* __restrict__ info,
-                                                     int32_t* __restrict__ out_tokens, double* __restrict__ mass,
-                                                     int32_t* __restrict__ diag_kind) {
-  const int32_t i = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const ReqInfo in = info[i];
-  if (in.kind != SDV_TERM_BONUS && in.kind != SDV_TERM_RESIDUAL) return;  // uniform over the block
-  double* m = mass + (int64_t)i * n_chunks;
-  const char* trow = row_ptr<E>(target, in.trow, V);
-  const char* drow = in.kind == SDV_TERM_RESIDUAL ? row_ptr<E>(draft, in.drow, V) : nullptr;
-  if (in.kind == SDV_TERM_RESIDUAL) {
-    for (int32_t c = wave; c < n_chunks; c += blockDim.x / kWave) {
-      const int32_t c0 = c * E::kChunk;
-      const double cm = resid_chunk_mass<E, kVec>(trow, drow, c0, min(E::kChunk, V - c0), k2, in, lane);
-      if (lane == 0) m[c] = cm;
-    }
+    if (lane == 0) dec = d;
   }
   __syncthreads();
-  if (wave != 0) return;
+  if constexpr (!kGreedy) draw_terminal<E, kVec>(P, dec, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
+}
 
-  // lane 0 walks the chunk masses in ascending order
-  const float2* tp = part + (int64_t)in.trow * n_chunks;
-  bool residual = in.kind == SDV_TERM_RESIDUAL;
-  int32_t cstar = 0;
-  double target_in_chunk = 0.0;
-  if (lane == 0) {
-    double S = 0.0;
-    if (residual) {
-      for (int32_t c = 0; c < n_chunks; ++c) S += m[c];
-      if (!(S > 0.0)) residual = false;  // no positive residual weight: fall back to p
+// The correction or bonus draw of a request (T > 0), by the verdict workgroup.
+template <class E, bool kVec>
+__device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, int32_t i, int32_t trow0,
+                                              int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
+                                              int wave, int n_waves) {
+  if (d.kind != SDV_TERM_BONUS && d.kind != SDV_TERM_RESIDUAL) return;  // uniform over the workgroup
+  const int32_t trow = trow0 + d.a;
+  const char* tp = row_ptr<E>(P.target, trow, P.V);
+
+  // 3. the draw
+  bool residual = d.kind == SDV_TERM_RESIDUAL;
+  const char* dp = residual ? row_ptr<E>(P.draft, drow0 + d.a, P.V) : nullptr;
+  if (residual) {
+    for (int32_t c = wave; c < P.C; c += n_waves) {
+      const int32_t c0 = c * E::kChunk;
+      const double cm = resid_chunk_mass<E, kVec>(tp, dp, c0, min(E::kChunk, P.V - c0), P.k2, d.ref_t, d.e_hi,
+                                                   d.e_lo, lane);
+      if (lane == 0) lds_mass[c] = cm;
     }
-    if (!residual) {
-      S = 0.0;
-      for (int32_t c = 0; c < n_chunks; ++c) {
-        m[c] = (double)tp[c].y * exp2((double)tp[c].x - (double)in.ref_t);
-        S += m[c];
-      }
-    }
-    const double U = (double)in.u * S;
-    double below = 0.0;
-    cstar = -1;
-    for (int32_t c = 0; c < n_chunks; ++c) {
-      if (below + m[c] > U) {
-        cstar = c;
-        break;
-      }
-      below += m[c];
-    }
-    if (cstar < 0) {  // rounding: the last chunk with positive mass
-      below = 0.0;
-      for (int32_t c = 0; c < n_chunks; ++c)
-        if (m[c] > 0.0) cstar = c;
-      if (cstar < 0) cstar = n_chunks - 1;
-      for (int32_t c = 0; c < cstar; ++c) below += m[c];
-    }
-    target_in_chunk = U - below;
+    __syncthreads();
   }
-  residual = __shfl((int)residual, 0, kWave) != 0;
-  cstar = __shfl(cstar, 0, kWave);
-  target_in_chunk = __shfl(target_in_chunk, 0, kWave);
-  const int32_t c0 = cstar * E::kChunk;
-  const int32_t y = search_chunk<E>(residual, trow, drow, c0, min(E::kChunk, V - c0), target_in_chunk, k2, in, lane);
+  if (wave != 0) return;
+  double S = 0.0;
+  if (residual) {
+    for (int32_t c = lane; c < P.C; c += kWave) S += lds_mass[c];
+    S = wave_sum(S);
+  }
+  bool empty = false;
+  if (residual && !(S > 0.0)) {  // no positive residual weight in floating point: draw from p_t
+    residual = false;
+    empty = true;
+  }
+  const float2* rec = rec_t + (int64_t)d.a * P.C;
+  double tgt = 0.0;
+  int32_t cs;
+  if (residual) {
+    cs = pick_chunk(P.C, (double)d.u, [&](int32_t c) { return lds_mass[c]; }, &tgt, lane);
+  } else {
+    cs = pick_chunk(
+        P.C, (double)d.u, [&](int32_t c) { return (double)rec[c].y * exp2((double)rec[c].x - (double)d.ref_t); },
+        &tgt, lane);
+  }
+  const int32_t s0 = cs * E::kChunk;
+  const int32_t n = min(E::kChunk, P.V - s0);
+  const int32_t y = residual ? search_chunk<E, kVec, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.e_lo, lane)
+                             : search_chunk<E, kVec, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lane);
   if (lane == 0) {
-    out_tokens[in.trow] = y;
-    if (diag_kind && in.kind == SDV_TERM_RESIDUAL && !residual) diag_kind[i] = SDV_TERM_RESIDUAL_EMPTY;
+    P.out_tokens[trow] = y;
+    if (P.dg.draw_uniform) P.dg.draw_uniform[i] = d.u;
+    if (P.dg.terminal_kind)
+      P.dg.terminal_kind[i] = d.kind == SDV_TERM_BONUS ? SDV_TERM_BONUS : (empty ? SDV_TERM_RESIDUAL_EMPTY : SDV_TERM_RESIDUAL);
   }
 }
 
@@ -507,12 +595,13 @@ __global__ void philox_kernel(const uint32_t* __restrict__ ctr, const uint32_t* 
 // ============================================================================ host side
 
 struct Layout {
-  int32_t n_chunks;
-  int64_t n_target_rows;
-  size_t part_off, info_off, mass_off, total;
+  int32_t C;
+  int64_t n_t, slots;
+  size_t part, total;
 };
 
 constexpr size_t kAlign = 256;
+constexpr int32_t kMaxChunks = 4096;  // residual chunk masses live in 32 KiB of shared memory
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Returns SDV_OK and fills the layout, or the status the shape violates.
@@ -520,79 +609,46 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   if (dtype != SDV_BF16 && dtype != SDV_FP32) return SDV_ERR_UNSUPPORTED;
   if (B < 1 || n_draft_rows < 0 || V < 1) return SDV_ERR_INVALID_ARG;
   const int64_t n_t = n_draft_rows + B;
-  const int64_t rows = n_t + n_draft_rows;
-  if (rows > INT32_MAX) return SDV_ERR_LIMIT;
+  const int64_t slots = n_t + n_draft_rows;
+  if (slots > INT32_MAX) return SDV_ERR_LIMIT;
   const int32_t chunk = dtype == SDV_BF16 ? Bf16::kChunk : F32::kChunk;
-  const int32_t n_chunks = (int32_t)((V + (int64_t)chunk - 1) / chunk);
-  const int64_t units = rows * n_chunks;
-  if ((units + 3) / 4 > INT32_MAX) return SDV_ERR_LIMIT;
-  L->n_chunks = n_chunks;
-  L->n_target_rows = n_t;
-  L->part_off = 0;
-  L->info_off = align_up((size_t)units * sizeof(float2));
-  L->mass_off = L->info_off + align_up((size_t)B * sizeof(ReqInfo));
-  L->total = L->mass_off + align_up((size_t)B * n_chunks * sizeof(double));
+  const int32_t C = (int32_t)((V + (int64_t)chunk - 1) / chunk);
+  if ((slots * C + 3) / 4 > INT32_MAX || C > kMaxChunks) return SDV_ERR_LIMIT;
+  L->C = C;
+  L->n_t = n_t;
+  L->slots = slots;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  L->part = take((size_t)slots * C * sizeof(float2));
+  L->total = off;
+  return SDV_OK;
+}
+
+template <class E, bool kGreedy, bool kVec>
+int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
+  auto record = [&](int k) {
+    if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
+  };
+  P.n_units = (int64_t)(kGreedy ? P.n_t : P.n_t + P.n_d) * P.C;
+  record(0);
+  hipLaunchKernelGGL((row_records<E, kGreedy, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
+  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+  record(1);
+  hipLaunchKernelGGL((verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves),
+                     (size_t)P.C * sizeof(double), stream, P);
+  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+  record(2);
   return SDV_OK;
 }
 
 template <class E>
-int launch_all(const void* target, const void* draft, const int32_t* tokens, const int32_t* cu, int32_t B,
-               int64_t n_d, int32_t V, double T, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens,
-               char* ws, const Layout& L, hipStream_t stream, const sdv_diag* diag) {
-  const bool greedy = T == 0.0;
-  const float k2 = greedy ? 1.0f : (float)(1.4426950408889634074 / T);  // log2(e) / T
-  const bool vec = ((uintptr_t)target % 16 == 0) && (draft == nullptr || (uintptr_t)draft % 16 == 0) &&
-                   ((int64_t)V * E::kBytes) % 16 == 0;
-  float2* part = reinterpret_cast<float2*>(ws + L.part_off);
-  ReqInfo* info = reinterpret_cast<ReqInfo*>(ws + L.info_off);
-  double* mass = reinterpret_cast<double*>(ws + L.mass_off);
-  DiagPtrs dg{};
-  if (diag) {
-    dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
-                  diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};
-  }
-  auto record = [&](int k) {
-    if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
-  };
-  const int32_t n_t = (int32_t)L.n_target_rows;
-  const int64_t rows = greedy ? n_t : n_t + n_d;
-  const int64_t units = rows * L.n_chunks;
-  const dim3 blk1(256);
-  const dim3 grid1((unsigned)((units + 3) / 4));
-
-  record(0);
-  if (greedy) {
-    if (vec)
-      hipLaunchKernelGGL((row_pass_vec<E, true>), grid1, blk1, 0, stream, target, draft, n_t, V, L.n_chunks, units, k2, part);
-    else
-      hipLaunchKernelGGL((row_pass_scalar<E, true>), grid1, blk1, 0, stream, target, draft, n_t, V, L.n_chunks, units, k2, part);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((row_pass_vec<E, false>), grid1, blk1, 0, stream, target, draft, n_t, V, L.n_chunks, units, k2, part);
-    else
-      hipLaunchKernelGGL((row_pass_scalar<E, false>), grid1, blk1, 0, stream, target, draft, n_t, V, L.n_chunks, units, k2, part);
-  }
-  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
-  record(1);
-  if (greedy)
-    hipLaunchKernelGGL((accept_scan<E, true>), dim3(B), dim3(kWave), 0, stream, target, draft, tokens, cu, B,
-                       (int32_t)n_d, V, L.n_chunks, k2, seed, part, accepted_len, out_tokens, info, dg);
-  else
-    hipLaunchKernelGGL((accept_scan<E, false>), dim3(B), dim3(kWave), 0, stream, target, draft, tokens, cu, B,
-                       (int32_t)n_d, V, L.n_chunks, k2, seed, part, accepted_len, out_tokens, info, dg);
-  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
-  record(2);
-  if (!greedy) {
-    if (vec)
-      hipLaunchKernelGGL((terminal_draw<E, true>), dim3(B), dim3(256), 0, stream, target, draft, V, L.n_chunks, k2, part,
-                         info, out_tokens, mass, dg.terminal_kind);
-    else
-      hipLaunchKernelGGL((terminal_draw<E, false>), dim3(B), dim3(256), 0, stream, target, draft, V, L.n_chunks, k2, part,
-                         info, out_tokens, mass, dg.terminal_kind);
-    if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
-    record(3);
-  }
-  return SDV_OK;
+int launch_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
+  if (P.k2 == 0.0f) return vec ? launch<E, true, true>(P, stream, diag) : launch<E, true, false>(P, stream, diag);
+  return vec ? launch<E, false, true>(P, stream, diag) : launch<E, false, false>(P, stream, diag);
 }
 
 }  // namespace sdv
@@ -614,19 +670,40 @@ int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int
   if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
   if (n_draft_rows > 0 && !draft_tokens) return SDV_ERR_INVALID_ARG;
   if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;
+  float k2 = 0.0f;  // 0 selects the greedy rule
   if (temperature > 0.0) {
-    const double k2 = 1.4426950408889634074 / temperature;
-    if (!isfinite((float)k2)) return SDV_ERR_INVALID_ARG;
+    k2 = (float)(1.4426950408889634074 / temperature);  // log2(e) / T
+    if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
     if (n_draft_rows > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
   }
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % sdv::kAlign != 0) return SDV_ERR_WORKSPACE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int esize = dtype == SDV_BF16 ? 2 : 4;
+  const void* draft = k2 > 0.0f ? draft_logits : nullptr;
+  const bool vec = ((uintptr_t)target_logits % 16 == 0) && (draft == nullptr || (uintptr_t)draft % 16 == 0) &&
+                   ((int64_t)V * esize) % 16 == 0;
   char* ws = static_cast<char*>(workspace);
-  if (dtype == SDV_BF16)
-    return sdv::launch_all<sdv::Bf16>(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V,
-                                      temperature, seed, accepted_len, out_tokens, ws, L, s, diag);
-  return sdv::launch_all<sdv::F32>(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V,
-                                   temperature, seed, accepted_len, out_tokens, ws, L, s, diag);
+  sdv::Params P{};
+  P.target = target_logits;
+  P.draft = draft;
+  P.tokens = draft_tokens;
+  P.cu = ragged_offsets;
+  P.accepted_len = accepted_len;
+  P.out_tokens = out_tokens;
+  P.part = reinterpret_cast<float2*>(ws + L.part);
+  P.B = B;
+  P.n_d = (int32_t)n_draft_rows;
+  P.n_t = (int32_t)L.n_t;
+  P.V = V;
+  P.C = L.C;
+  P.k2 = k2;
+  P.seed = seed;
+  if (diag) {
+    P.dg = sdv::DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
+                         diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == SDV_BF16) return sdv::launch_any<sdv::Bf16>(P, vec, s, diag);
+  return sdv::launch_any<sdv::F32>(P, vec, s, diag);
 }
 
 int sdv_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,

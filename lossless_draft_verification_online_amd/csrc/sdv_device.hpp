@@ -21,7 +21,7 @@ struct Bf16 {
   static constexpr int kPerVec = 8;
   static constexpr int kChunk = kChunkBytes / kBytes;
   // bf16 is the upper half of a binary32: the even element sits in the low 16 bits of a word.
-  __device__ static inline void unpack(const u32x4 v, float (&f)[kPerVec]) {
+  __device__ static __forceinline__ void unpack(const u32x4 v, float (&f)[kPerVec]) {
     f[0] = __uint_as_float(v.x << 16);
     f[1] = __uint_as_float(v.x & 0xffff0000u);
     f[2] = __uint_as_float(v.y << 16);
@@ -31,7 +31,7 @@ struct Bf16 {
     f[6] = __uint_as_float(v.w << 16);
     f[7] = __uint_as_float(v.w & 0xffff0000u);
   }
-  __device__ static inline float at(const void* row, int64_t v) {
+  __device__ static __forceinline__ float at(const void* row, int64_t v) {
     return __uint_as_float((uint32_t)(static_cast<const uint16_t*>(row)[v]) << 16);
   }
   static constexpr uint32_t kNegInfWord = 0xff80ff80u;  // two bf16 -inf
@@ -41,18 +41,18 @@ struct F32 {
   static constexpr int kBytes = 4;
   static constexpr int kPerVec = 4;
   static constexpr int kChunk = kChunkBytes / kBytes;
-  __device__ static inline void unpack(const u32x4 v, float (&f)[kPerVec]) {
+  __device__ static __forceinline__ void unpack(const u32x4 v, float (&f)[kPerVec]) {
     f[0] = __uint_as_float(v.x);
     f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z);
     f[3] = __uint_as_float(v.w);
   }
-  __device__ static inline float at(const void* row, int64_t v) { return static_cast<const float*>(row)[v]; }
+  __device__ static __forceinline__ float at(const void* row, int64_t v) { return static_cast<const float*>(row)[v]; }
   static constexpr uint32_t kNegInfWord = 0xff800000u;
 };
 
 template <class E>
-__device__ inline const char* row_ptr(const void* base, int64_t row, int32_t V) {
+__device__ __forceinline__ const char* row_ptr(const void* base, int64_t row, int32_t V) {
   return static_cast<const char*>(base) + row * (int64_t)V * E::kBytes;
 }
 
@@ -60,26 +60,26 @@ __device__ inline const char* row_ptr(const void* base, int64_t row, int32_t V) 
 // xor butterflies: at every level both partners add the same two values, so every lane ends with
 // the bit-identical result.
 
-__device__ inline float wave_max(float v) {
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
 
-__device__ inline float wave_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
-__device__ inline double wave_sum(double v) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
 // Larger value wins; equal values go to the smaller index.
-__device__ inline void wave_argmax(float& v, int32_t& idx) {
+__device__ __forceinline__ void wave_argmax(float& v, int32_t& idx) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(v, o, kWave);
@@ -92,7 +92,7 @@ __device__ inline void wave_argmax(float& v, int32_t& idx) {
 }
 
 // Exclusive prefix sum over the wave (lane order), fp64.
-__device__ inline double wave_exclusive_scan(double v, int lane) {
+__device__ __forceinline__ double wave_exclusive_scan(double v, int lane) {
   double incl = v;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -104,7 +104,7 @@ __device__ inline double wave_exclusive_scan(double v, int lane) {
 
 // Sum of the eight (or four) elements of one vector as a balanced tree.
 template <int N>
-__device__ inline float tree_sum(const float (&f)[N]) {
+__device__ __forceinline__ float tree_sum(const float (&f)[N]) {
   if constexpr (N == 8) {
     return ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
   } else {
@@ -112,7 +112,7 @@ __device__ inline float tree_sum(const float (&f)[N]) {
   }
 }
 
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): ten
@@ -124,7 +124,7 @@ struct Philox4 {
   uint32_t w0, w1, w2, w3;
 };
 
-__device__ inline Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
                                         uint32_t k1) {
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
@@ -141,12 +141,12 @@ __device__ inline Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, u
 }
 
 // The verifier's block for (request, position): key = seed, counter = (position, request, 0, 0).
-__device__ inline Philox4 verifier_block(uint64_t seed, uint32_t request, uint32_t position) {
+__device__ __forceinline__ Philox4 verifier_block(uint64_t seed, uint32_t request, uint32_t position) {
   return philox4x32_10(position, request, 0u, 0u, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
 // Accept-test uniform in (0, 1] from word 0 and draw uniform in [0, 1) from word 1, both exact in fp32.
-__device__ inline float accept_uniform(const Philox4& b) { return (float)((b.w0 >> 8) + 1u) * 0x1.0p-24f; }
-__device__ inline float draw_uniform(const Philox4& b) { return (float)(b.w1 >> 8) * 0x1.0p-24f; }
+__device__ __forceinline__ float accept_uniform(const Philox4& b) { return (float)((b.w0 >> 8) + 1u) * 0x1.0p-24f; }
+__device__ __forceinline__ float draw_uniform(const Philox4& b) { return (float)(b.w1 >> 8) * 0x1.0p-24f; }
 
 }  // namespace sdv
