@@ -54,6 +54,7 @@ struct Params {
   float2* part;         // [row slots][C] chunk records; target row r is slot r, draft row d slot n_t + d
   int32_t B, n_d, n_t, V, C;
   int64_t n_units;
+  int64_t lds_records;  // chunk records the verdict kernel can stage in shared memory
   float k2;  // log2(e) / T, or 0 for the greedy rule
   uint64_t seed;
   DiagPtrs dg;
@@ -76,6 +77,16 @@ __device__ __forceinline__ u32x4 neg_inf_vec() {
   return u32x4{E::kNegInfWord, E::kNegInfWord, E::kNegInfWord, E::kNegInfWord};
 }
 
+// Vector vi of a chunk with nvec vectors, -inf past the chunk's end.
+template <class E>
+__device__ __forceinline__ u32x4 load_vec(const u32x4* v, int vi, int32_t nvec) {
+  return vi < nvec ? v[vi] : neg_inf_vec<E>();
+}
+template <class E>
+__device__ __forceinline__ u32x4 load_vec_nt(const u32x4* v, int vi, int32_t nvec) {
+  return vi < nvec ? __builtin_nontemporal_load(v + vi) : neg_inf_vec<E>();
+}
+
 // One 16 KiB chunk: (ref, sum 2^(z k - ref)) at T > 0, (max, first index of max) at T = 0.
 template <class E, bool kGreedy, bool kVec>
 __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32_t n, float k2, int lane) {
@@ -87,7 +98,7 @@ __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32
 #pragma unroll
     for (int k = 0; k < kVecPerLane; ++k) {
       const int vi = lane + kWave * k;
-      buf[k] = vi < nvec ? __builtin_nontemporal_load(vp + vi) : neg_inf_vec<E>();
+      buf[k] = load_vec_nt<E>(vp, vi, nvec);
     }
     if constexpr (kGreedy) {
       float best = -INFINITY;
@@ -194,9 +205,10 @@ __device__ __forceinline__ int32_t search_chunk(const char* trow, const char* dr
       u32x4 tb[kHalf], db[kHalf];
 #pragma unroll
       for (int k = 0; k < kHalf; ++k) {
-        const bool ok = b + (h * kHalf + k) * E::kPerVec < end;
-        tb[k] = ok ? tp[h * kHalf + k] : neg_inf_vec<E>();
-        if constexpr (kResid) db[k] = ok ? dp[h * kHalf + k] : neg_inf_vec<E>();
+        // vectors of this lane's run that lie inside the chunk: (end - b) / kPerVec of them
+        const int32_t nv = max((end - b) / E::kPerVec, 1);
+        tb[k] = (end - b) > 0 ? load_vec<E>(tp, h * kHalf + k, nv) : neg_inf_vec<E>();
+        if constexpr (kResid) db[k] = (end - b) > 0 ? load_vec<E>(dp, h * kHalf + k, nv) : neg_inf_vec<E>();
       }
 #pragma unroll
       for (int k = 0; k < kHalf; ++k) {
@@ -314,8 +326,8 @@ __device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* d
 #pragma unroll
       for (int k = 0; k < kHalf; ++k) {
         const int vi = lane + kWave * (h * kHalf + k);
-        tb[k] = vi < nvec ? tv[vi] : neg_inf_vec<E>();
-        db[k] = vi < nvec ? dv[vi] : neg_inf_vec<E>();
+        tb[k] = load_vec<E>(tv, vi, nvec);
+        db[k] = load_vec<E>(dv, vi, nvec);
       }
 #pragma unroll
       for (int k = 0; k < kHalf; ++k) {
@@ -345,6 +357,147 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
   const int32_t c0 = c * E::kChunk;
   const float2 rec = chunk_record<E, kGreedy, kVec>(rp, c0, min(E::kChunk, P.V - c0), P.k2, lane);
   if (lane == 0) P.part[u] = rec;
+}
+
+// Residual chunk masses of a row pair by the waves of one workgroup (16-byte aligned rows).  Wave w
+// takes chunks w, w + n_waves, ...; each full chunk is read in two halves, and the loads of the next
+// half are issued before the current half is reduced, so every wave keeps one half in flight.  The
+// loads of full chunks carry no bounds test (a predicated load would leave the hardware load counter
+// uncertain and force a wait for every outstanding load); a row's last, partial chunk goes through
+// the bounds-tested path.
+template <class E>
+__device__ __forceinline__ void resid_masses_pipelined(const char* tp, const char* dp, int32_t V, int32_t C, float k2,
+                                                       float ref_t, float e_hi, float e_lo, double* lds_mass,
+                                                       int lane, int wave, int n_waves) {
+  constexpr int kHalf = kVecPerLane / 2;
+  struct Half {
+    u32x4 t[kHalf], d[kHalf];
+  };
+  auto load = [&](int32_t c, int h, Half& b) {
+    const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c * E::kChunk * E::kBytes);
+    const u32x4* dv = reinterpret_cast<const u32x4*>(dp + (int64_t)c * E::kChunk * E::kBytes);
+#pragma unroll
+    for (int k = 0; k < kHalf; ++k) {
+      const int vi = lane + kWave * (h * kHalf + k);
+      b.t[k] = tv[vi];
+      b.d[k] = dv[vi];
+    }
+  };
+  auto reduce = [&](const Half& b) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kHalf; ++k) {
+      float ft[E::kPerVec], fd[E::kPerVec];
+      E::unpack(b.t[k], ft);
+      E::unpack(b.d[k], fd);
+#pragma unroll
+      for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, e_lo);
+      acc += (double)tree_sum(ft);
+    }
+    return acc;
+  };
+  const int32_t C_full = V / E::kChunk;  // chunks of kChunk elements
+  int32_t c = wave;
+  if (c < C_full) {
+    Half A, Bh;
+    load(c, 0, A);
+    asm volatile("" ::: "memory");
+    for (;;) {
+      load(c, 1, Bh);
+      asm volatile("" ::: "memory");  // the second half is in flight while the first is reduced
+      double acc = reduce(A);
+      asm volatile("" : "+v"(acc)::"memory");  // the first half is consumed before its registers reload
+      const int32_t cn = c + n_waves;
+      if (cn < C_full) load(cn, 0, A);
+      asm volatile("" ::: "memory");
+      acc += reduce(Bh);
+      asm volatile("" : "+v"(acc)::"memory");
+      acc = wave_sum(acc);
+      if (lane == 0) lds_mass[c] = acc;
+      c = cn;
+      if (c >= C_full) break;
+    }
+  }
+  if (c < C) {  // the partial last chunk, if this wave owns it
+    const int32_t c0 = c * E::kChunk;
+    const double cm = resid_chunk_mass<E, true>(tp, dp, c0, V - c0, k2, ref_t, e_hi, e_lo, lane);
+    if (lane == 0) lds_mass[c] = cm;
+  }
+}
+
+// Inverse CDF inside one chunk (16-byte aligned rows) by a whole workgroup: the chunk's vectors form
+// rows of 64 (vector k*64 + l for lane l), wave w sums rows w and w + n_waves, a scan of the row sums
+// picks the row, and the wave that owns it scans its 64 vector sums and walks the chosen vector.
+// Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
+template <class E, bool kResid>
+__device__ __forceinline__ int32_t search_chunk_block(const char* trow, const char* drow, int32_t c0, int32_t n,
+                                                      double target, float k2, float ref_t, float e_hi, float e_lo,
+                                                      double* scratch, int lane, int wave, int n_waves) {
+  constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
+  const int32_t nvec = n / E::kPerVec;
+  const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
+  const u32x4* dv = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)c0 * E::kBytes);
+  auto weights = [&](const u32x4& t, const u32x4& dd, float (&w)[E::kPerVec]) {
+    float ft[E::kPerVec], fd[E::kPerVec];
+    E::unpack(t, ft);
+    if constexpr (kResid) E::unpack(dd, fd);
+#pragma unroll
+    for (int q = 0; q < E::kPerVec; ++q)
+      w[q] = kResid ? resid_weight(ft[q], fd[q], k2, ref_t, e_hi, e_lo) : fast_exp2(fmaf(ft[q], k2, -ref_t));
+  };
+  // rows owned by this wave: wave and wave + n_waves (n_waves == 8 covers the 16 rows)
+  u32x4 t[2], dd[2];
+  float vs[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int vi = (wave + j * n_waves) * kWave + lane;
+    t[j] = wave + j * n_waves < kRows ? load_vec<E>(tv, vi, nvec) : neg_inf_vec<E>();
+    dd[j] = (kResid && wave + j * n_waves < kRows) ? load_vec<E>(dv, vi, nvec) : neg_inf_vec<E>();
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float w[E::kPerVec];
+    weights(t[j], dd[j], w);
+    vs[j] = tree_sum(w);
+    const double rs = wave_sum((double)vs[j]);
+    if (lane == 0 && wave + j * n_waves < kRows) scratch[wave + j * n_waves] = rs;
+  }
+  __syncthreads();
+  // every wave scans the 16 row sums the same way
+  const double rsum = lane < kRows ? scratch[lane] : 0.0;
+  const double rex = wave_exclusive_scan(rsum, lane);
+  const uint64_t rhit = __ballot(lane < kRows && rex + rsum > target);
+  const uint64_t rpos = __ballot(lane < kRows && rsum > 0.0);
+  if (!rhit && !rpos) return wave == 0 ? c0 + n - 1 : -1;
+  const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
+  const int owner = kr % n_waves;
+  if (wave != owner) return -1;
+  const int j = kr / n_waves;
+  const double rest = target - __shfl(rex, kr, kWave);
+  // the owning wave: scan its 64 vector sums of row kr, then walk the chosen vector
+  const float v = j == 0 ? vs[0] : vs[1];
+  const double vex = wave_exclusive_scan((double)v, lane);
+  const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
+  const uint64_t vpos = __ballot(v > 0.0f);
+  const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
+  float w[E::kPerVec];
+  weights(j == 0 ? t[0] : t[1], j == 0 ? dd[0] : dd[1], w);
+  const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+  int32_t yl = base + E::kPerVec - 1;
+  int32_t last_pos = -1;
+  double upto = vex;
+  bool found = false;
+#pragma unroll
+  for (int q = 0; q < E::kPerVec; ++q) {
+    upto += (double)w[q];
+    if (w[q] > 0.0f) last_pos = base + q;
+    if (!found && upto > rest) {
+      yl = base + q;
+      found = true;
+    }
+  }
+  if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
+  return __shfl(yl, l, kWave);
 }
 
 // ============================================================================ 2. verdicts
@@ -415,6 +568,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
                                               int wave, int n_waves);
 
 constexpr int kVerdictWaves = 8;
+static_assert(2 * kVerdictWaves >= kVecPerLane, "the in-chunk search gives each wave two rows of 64 vectors");
 constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
 // One workgroup of 8 waves per request.  Shared memory: the folded rows, the decision, and the
@@ -440,10 +594,36 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   const float2* rec_t = P.part + (int64_t)trow0 * P.C;
   const float2* rec_d = P.part + (int64_t)(P.n_t + drow0) * P.C;
 
-  // 1. fold the request's rows: r <= K target row r, r > K draft row r - K - 1
+  // 1. all chunk records of the request's rows (r <= K target row r, r > K draft row r - K - 1)
+  // are staged in shared memory in one pass when they fit, while wave 0 fetches the draft
+  // tokens and the logits at them
   const int n_rows = kGreedy ? K + 1 : 2 * K + 1;
+  const int64_t n_rec = (int64_t)n_rows * P.C;
+  float2* lds_rec = reinterpret_cast<float2*>(lds_mass + P.C);
+  const bool staged = n_rec <= P.lds_records;
+  if (staged) {
+    for (int64_t q = threadIdx.x; q < n_rec; q += blockDim.x) {
+      const int64_t r = q / P.C;
+      const int32_t c = (int32_t)(q - r * P.C);
+      lds_rec[q] = r <= K ? rec_t[r * P.C + c] : rec_d[(r - K - 1) * P.C + c];
+    }
+  }
+  const bool active = lane < K;
+  int32_t x = 0;
+  float zt = 0.0f, zd = 0.0f;
+  if (wave == 0 && active) {
+    x = P.tokens[drow0 + lane];
+    if constexpr (!kGreedy) {
+      if (x >= 0 && x < P.V) {
+        zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
+        zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+      }
+    }
+  }
+  __syncthreads();
   for (int r = wave; r < n_rows; r += n_waves) {
-    const float2* p = r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C;
+    const float2* p = staged ? lds_rec + (int64_t)r * P.C
+                             : (r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C);
     const RowFold f = fold_row<kGreedy>(p, P.C, lane);
     if (lane == 0) rows[r] = f;
   }
@@ -451,8 +631,6 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
 
   // 2. the verdict, by wave 0
   if (wave == 0) {
-    const bool active = lane < K;
-    const int32_t x = active ? P.tokens[drow0 + lane] : 0;
     Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0f};
     if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
       write_reject(P, i, trow0, K, true, lane);
@@ -478,8 +656,6 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
       if (active) {
         ft = rows[lane];
         fd = rows[K + 1 + lane];
-        const float zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
-        const float zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
         qzero = zd == -INFINITY;
         // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
         ratio = exp2(((double)zt - (double)zd) * (double)P.k2 - (ft.l2 - fd.l2));
@@ -533,20 +709,24 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   if (d.kind != SDV_TERM_BONUS && d.kind != SDV_TERM_RESIDUAL) return;  // uniform over the workgroup
   const int32_t trow = trow0 + d.a;
   const char* tp = row_ptr<E>(P.target, trow, P.V);
-
-  // 3. the draw
   bool residual = d.kind == SDV_TERM_RESIDUAL;
   const char* dp = residual ? row_ptr<E>(P.draft, drow0 + d.a, P.V) : nullptr;
+
+  // residual masses of every chunk, into shared memory
   if (residual) {
-    for (int32_t c = wave; c < P.C; c += n_waves) {
-      const int32_t c0 = c * E::kChunk;
-      const double cm = resid_chunk_mass<E, kVec>(tp, dp, c0, min(E::kChunk, P.V - c0), P.k2, d.ref_t, d.e_hi,
-                                                   d.e_lo, lane);
-      if (lane == 0) lds_mass[c] = cm;
+    if constexpr (kVec) {
+      resid_masses_pipelined<E>(tp, dp, P.V, P.C, P.k2, d.ref_t, d.e_hi, d.e_lo, lds_mass, lane, wave, n_waves);
+    } else {
+      for (int32_t c = wave; c < P.C; c += n_waves) {
+        const int32_t c0 = c * E::kChunk;
+        const double cm = resid_chunk_mass<E, false>(tp, dp, c0, min(E::kChunk, P.V - c0), P.k2, d.ref_t, d.e_hi,
+                                                     d.e_lo, lane);
+        if (lane == 0) lds_mass[c] = cm;
+      }
     }
     __syncthreads();
   }
-  if (wave != 0) return;
+  // every wave picks the same chunk from the same masses
   double S = 0.0;
   if (residual) {
     for (int32_t c = lane; c < P.C; c += kWave) S += lds_mass[c];
@@ -569,9 +749,18 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   }
   const int32_t s0 = cs * E::kChunk;
   const int32_t n = min(E::kChunk, P.V - s0);
-  const int32_t y = residual ? search_chunk<E, kVec, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.e_lo, lane)
-                             : search_chunk<E, kVec, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lane);
-  if (lane == 0) {
+  int32_t y = -1;
+  if constexpr (kVec) {
+    y = residual ? search_chunk_block<E, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.e_lo, lds_mass + P.C,
+                                               lane, wave, n_waves)
+                 : search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
+                                                lane, wave, n_waves);
+  } else {
+    if (wave != 0) return;
+    y = residual ? search_chunk<E, false, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.e_lo, lane)
+                 : search_chunk<E, false, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lane);
+  }
+  if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
     P.out_tokens[trow] = y;
     if (P.dg.draw_uniform) P.dg.draw_uniform[i] = d.u;
     if (P.dg.terminal_kind)
@@ -601,7 +790,8 @@ struct Layout {
 };
 
 constexpr size_t kAlign = 256;
-constexpr int32_t kMaxChunks = 4096;  // residual chunk masses live in 32 KiB of shared memory
+constexpr int32_t kMaxChunks = 4096;          // residual chunk masses live in 32 KiB of shared memory
+constexpr size_t kVerdictLdsBytes = 48 * 1024;  // dynamic shared memory of the verdict workgroup
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Returns SDV_OK and fills the layout, or the status the shape violates.
@@ -638,8 +828,13 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   hipLaunchKernelGGL((row_records<E, kGreedy, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(1);
-  hipLaunchKernelGGL((verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves),
-                     (size_t)P.C * sizeof(double), stream, P);
+  // shared memory: C residual masses, then as many chunk records as the deepest request can need,
+  // up to the budget; deeper requests fold straight from the workspace
+  const int64_t want = (int64_t)(2 * SDV_MAX_DEPTH + 1) * P.C;
+  const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
+  P.lds_records = want < room ? want : room;
+  const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
+  hipLaunchKernelGGL((verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves), lds, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(2);
   return SDV_OK;
