@@ -1,19 +1,28 @@
 """Benchmark of the verification step on one MI355X.
 
-One step = one sdv_verify call (row pass, accept scan, terminal draw) over one ragged batch whose
-inputs are already resident in HBM.  Default workload: B = 256 requests, K_i ~ U{0..8},
-V = 128256, bf16 logits, T = 1 (target ~ N(0, 3^2), draft = target + N(0, s_i^2), s_i ~ U[0.5, 3]).
-Two independently drawn input sets (about 1.2 GB together) alternate so that the memory-side
-cache cannot serve a call from the previous one.
+One step = one sdv_verify call (the row pass, then the per-request verdict kernel) over one ragged
+batch whose inputs are already resident in HBM.  Default workload: B = 256 requests,
+K_i ~ U{0..8}, V = 128256, bf16 logits, T = 1 (target ~ N(0, 3^2), draft = target + N(0, s_i^2),
+s_i ~ U[0.5, 3]).  Two independently drawn input sets (about 1.1 GB together) alternate so that
+the memory-side cache cannot serve a call from the previous one.
 
-Prints one JSON line: verified draft positions per second (sum K_i per call / time per call), the
-call's algorithmic HBM bandwidth, the row-pass kernel's roofline fraction (algorithmic bytes of
-one launch / its mean duration from HIP events recorded on the library's stream), and the CPU
-oracle's rate on the host.
+Prints one JSON line: verified draft positions per second (sum K_i per call / wall time per call),
+the call's algorithmic HBM bandwidth, the row-pass kernel's roofline fraction (algorithmic bytes of
+one launch / its mean duration from HIP events recorded on the library's stream), the bandwidth of
+a plain read of the same size with the row pass's loads, per-call percentiles, accepted-length
+statistics and the CPU oracle's rate on the host.
+
+  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64] [--steps K] [--warmup W]
+
+Profile summaries (rocprofv3 output -> text under profiles/):
+
+  python bench.py --summarize-trace KERNEL_STATS_CSV --bench-json OUT --command "..."
+  python bench.py --summarize-pmc FETCH_CSV WRITE_CSV --copy-mib 512 --command "..."
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -29,6 +38,8 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=256, V=128256"
 KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
                   "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
+KERNELS = ["row_records", "verdicts"]
+CHUNK_BYTES = 16384
 
 
 def log(msg):
@@ -53,16 +64,20 @@ def make_workload(name: str, set_index: int):
     raise SystemExit(f"unknown workload {name}")
 
 
+def pmc_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"row_records_{workload}_pmc.json")
+
+
 def traffic_from_profile(workload: str):
     """HBM bytes per row_records launch from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"row_records_{workload}_pmc.json")
+    path = pmc_path(workload)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec.get("row_records", {}).get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(batch, budget_s: float):
@@ -82,6 +97,35 @@ def cpu_baseline(batch, budget_s: float):
                       f"{t * 1e3:.1f} ms per call, fp64 C with OpenMP"}
 
 
+def reread_bytes(batch, acc: np.ndarray) -> int:
+    """Bytes the verdict kernel reads again beyond the algorithmic bytes: a correction re-reads its
+    target and draft rows for the residual chunk masses and then one chunk of each for the search;
+    a bonus re-reads one chunk of its target row; greedy terminals read nothing again."""
+    if batch.temperature == 0:
+        return 0
+    K = batch.depths
+    row = batch.V * batch.elem_bytes
+    chunk = min(CHUNK_BYTES, row)
+    resid = int(np.sum((acc >= 0) & (acc < K)))
+    bonus = int(np.sum(acc == K))
+    return resid * (2 * row + 2 * chunk) + bonus * chunk
+
+
+def acceptance_stats(batch, accs):
+    """Mean accepted length, committed tokens per call and the acceptance rate by depth
+    (accepts at j / requests that reached j with a draft there)."""
+    K = batch.depths
+    a = np.stack(accs)                      # calls x B
+    ok = a >= 0
+    committed = float(np.mean(np.sum(np.where(ok, a + 1, 0), axis=1)))
+    by_depth = []
+    for j in range(int(K.max()) if K.size else 0):
+        reach = ok & (K[None, :] > j) & (a >= j)
+        by_depth.append(float(np.sum(reach & (a > j)) / max(1, np.sum(reach))))
+    return {"mean_accepted_len": float(np.mean(a[ok])), "committed_tokens_per_call": committed,
+            "alpha_hat_by_depth": [round(x, 4) for x in by_depth], "calls": int(a.shape[0])}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +137,16 @@ def main():
     ap.add_argument("--no-check", action="store_true", help="skip the oracle comparison of one call")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--bench-json", help="bench output of the profiled run (for --summarize-trace)")
+    ap.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (--summarize-pmc)")
+    ap.add_argument("--command", default="", help="the command that produced the profile")
     args = ap.parse_args()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         raise SystemExit("bench.py measures one GPU: the verification step is built and measured on a single "
                          "MI355X; requests shard across GPUs with no exchange (see the design notes), and "
@@ -122,6 +175,7 @@ def main():
                          cu=torch.from_numpy(b.cu).to(dev), batch=b))
     B0 = batches[0]
     positions = [int(b.cu[-1]) for b in batches]
+    rows = [int(b.cu[-1]) + b.B for b in batches]
     alg_bytes = [b.algorithmic_bytes() for b in batches]
     ws = torch.empty(max(sdv.workspace_bytes(b.B, b.n_draft_rows, b.V, sets[0]["target"].dtype) for b in batches),
                      dtype=torch.uint8, device=dev)
@@ -169,10 +223,8 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # a second pass with HIP events that the library records on its stream before the first kernel
-    # and after each kernel: per-kernel durations for the roofline
-    greedy = B0.temperature == 0
-    n_kernels = 2
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_kernels + 1)] for _ in range(args.steps)]
+    # and after each kernel: per-kernel and per-call durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()  # instantiate the handles
@@ -181,9 +233,40 @@ def main():
         step(args.warmup + k, events=evs[k])
     torch.cuda.synchronize()
     per_kernel = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)]))
-                  for j in range(n_kernels)]
+                  for j in range(len(KERNELS))]
+    per_call = np.array([evs[k][0].elapsed_time(evs[k][-1]) for k in range(args.steps)])
+
+    # the bandwidth yardstick: the row pass's loads with no arithmetic over buffers of the call's size
+    n_chunks = int(np.mean(alg_bytes)) // CHUNK_BYTES
+    bufs = [torch.empty(n_chunks * CHUNK_BYTES, dtype=torch.uint8, device=dev) for _ in range(len(sets))]
+    for buf in bufs:
+        buf.fill_(1)
+    folded = torch.empty(n_chunks, dtype=torch.int32, device=dev)
+    for k in range(10):
+        sdv.read_ceiling(bufs[k % len(bufs)], folded)
+    reps = 100
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for k in range(reps):
+        sdv.read_ceiling(bufs[k % len(bufs)], folded)
+    r1.record()
+    torch.cuda.synchronize()
+    read_gbps = n_chunks * CHUNK_BYTES / (r0.elapsed_time(r1) / reps * 1e-3) / 1e9
+    del bufs
+
+    # verdict statistics over a few more calls (untimed)
+    accs, rereads = [], []
+    for k in range(16):
+        step(k)
+        acc = outs[k % len(sets)][0].cpu().numpy()
+        if k % len(sets) == 0:
+            accs.append(acc)
+        rereads.append(reread_bytes(batches[k % len(sets)], acc))
+    stats = acceptance_stats(B0, accs)
+
     ms_step = elapsed * 1e3 / args.steps
     mean_pos = float(np.mean([positions[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
+    mean_rows = float(np.mean([rows[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     mean_bytes = float(np.mean([alg_bytes[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     value = mean_pos / (ms_step * 1e-3)
     call_gbps = mean_bytes / (ms_step * 1e-3) / 1e9
@@ -207,10 +290,20 @@ def main():
                    "algorithmic_bytes_per_call": alg_bytes},
         "hbm_gbps": call_gbps,
         "hbm_frac_of_peak": call_gbps / PEAK_HBM_GBPS,
-        "kernel_ms": dict(zip(["row_records", "verdicts"], per_kernel)),
+        "read_ceiling_gbps": read_gbps,
+        "hbm_frac_of_read_ceiling": call_gbps / read_gbps,
+        "rows_per_s": mean_rows / (ms_step * 1e-3),
+        "committed_tokens_per_s": stats["committed_tokens_per_call"] / (ms_step * 1e-3),
+        "call_ms_events": {"median": float(np.median(per_call)), "p5": float(np.percentile(per_call, 5)),
+                           "p95": float(np.percentile(per_call, 95)), "n": int(per_call.size)},
+        "kernel_ms": dict(zip(KERNELS, per_kernel)),
+        "terminal_reread_bytes_per_call": float(np.mean(rereads)),
+        "terminal_reread_frac_of_algorithmic": float(np.mean(rereads)) / mean_bytes,
+        "acceptance": stats,
         "roofline": {"bound": "hbm", "achieved": rowpass_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": rowpass_gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(args.workload),
-                     "kernel": "row_records", "algorithmic_bytes_per_launch": mean_bytes},
+                     "kernel": "row_records", "algorithmic_bytes_per_launch": mean_bytes,
+                     "frac_of_read_ceiling": rowpass_gbps / read_gbps},
         "parity": parity,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -220,6 +313,92 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------------------------------- profile summaries
+
+def _short(name: str) -> str:
+    for k in KERNELS + ["read_kernel", "philox_kernel"]:
+        if f"sdv{len(k)}{k}" in name or f"::{k}" in name or name.startswith(k):
+            return k
+    return name.split("(")[0][:48]
+
+
+def summarize_trace(args):
+    """rocprofv3 --kernel-trace --stats kernel_stats.csv -> profiles/kernels_<workload>_trace.md."""
+    rows = list(csv.DictReader(open(args.summarize_trace)))
+    bench = None
+    if args.bench_json and os.path.exists(args.bench_json):
+        for line in open(args.bench_json):
+            if line.startswith("{"):
+                bench = json.loads(line)
+    workload = bench["config"]["workload"] if bench else "unknown"
+    lines = [f"# Kernel durations: {workload}", "", "Command ($REPO is the repository root):", "", "```",
+             args.command, "```", "",
+             "| kernel | calls | total ms | mean us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        n = int(r["Calls"])
+        lines.append(f"| {_short(r['Name'])} | {n} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    if bench:
+        lines += ["", "The same run's bench line (HIP events on the library's stream):", "",
+                  f"- kernel_ms: {json.dumps({k: round(v * 1e3, 2) for k, v in bench['kernel_ms'].items()})} (us)",
+                  f"- ms_per_step: {bench['ms_per_step'] * 1e3:.2f} us; roofline frac of row_records: "
+                  f"{bench['roofline']['frac']:.4f}; kernel_source_hash {bench['kernel_source_hash']}"]
+    out = os.path.join(ROOT, "profiles", f"kernels_{args.workload}_trace.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(args):
+    """Two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) -> HBM bytes per launch,
+    each counter scaled by what it reads for one plain device copy of --copy-mib MiB."""
+    copy_kib = args.copy_mib * 1024
+
+    def per_kernel(path, counter):
+        vals, copies = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            if "copyBuffer" in name:
+                copies.append(v)
+            else:
+                vals.setdefault(_short(name), []).append(v)
+        big = max(copies) if copies else 0.0
+        if not (0.25 * copy_kib <= big <= 2.0 * copy_kib):
+            raise SystemExit(f"{counter}: no calibration copy of about {copy_kib} KiB found (largest {big} KiB)")
+        return {k: float(np.mean(v)) for k, v in vals.items()}, copy_kib / big, big
+
+    fetch, f_fac, f_copy = per_kernel(args.summarize_pmc[0], "FETCH_SIZE")
+    write, w_fac, w_copy = per_kernel(args.summarize_pmc[1], "WRITE_SIZE")
+    batches = [make_workload(args.workload, s) for s in range(2)]
+    alg = float(np.mean([b.algorithmic_bytes() for b in batches]))
+    rec = {"kernel_source_hash": kernel_source_hash(), "workload": args.workload, "command": args.command,
+           "calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_read": f_copy, "write_kib_read": w_copy,
+                           "fetch_factor": f_fac, "write_factor": w_fac},
+           "algorithmic_bytes_per_row_records_launch": alg}
+    lines = [f"# HBM traffic per launch: {args.workload}", "", "Commands ($REPO is the repository root):", "",
+             "```", args.command, "```", "",
+             f"Calibration: a {args.copy_mib} MiB device copy reads FETCH_SIZE {f_copy:.0f} KiB "
+             f"(factor {f_fac:.3f}) and WRITE_SIZE {w_copy:.0f} KiB (factor {w_fac:.3f}).", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetched bytes (scaled) | written bytes (scaled) |",
+             "|---|---|---|---|---|"]
+    for k in sorted(set(fetch) | set(write)):
+        fb = fetch.get(k, 0.0) * 1024 * f_fac
+        wb = write.get(k, 0.0) * 1024 * w_fac
+        rec[k] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb}
+        lines.append(f"| {k} | {fetch.get(k, 0):.0f} | {write.get(k, 0):.0f} | {fb:.4g} | {wb:.4g} |")
+    if "row_records" in rec:
+        lines += ["", f"row_records: traffic {rec['row_records']['traffic_bytes_per_launch']:.4g} B against "
+                      f"{alg:.4g} algorithmic bytes per launch "
+                      f"(ratio {rec['row_records']['traffic_bytes_per_launch'] / alg:.4f})."]
+    json.dump(rec, open(pmc_path(args.workload), "w"), indent=1)
+    out = os.path.join(ROOT, "profiles", f"row_records_{args.workload}_pmc.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":

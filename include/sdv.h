@@ -14,7 +14,8 @@
  *    Decode with a draft model and an accept-reject rule, which is exactly lossless", section
  *    "What to do".  p and q are softmax(z/T) of the target and draft logit rows (SDCP section
  *    "Session Contract": temperature, then top-k / top-p, which this library does not apply).
- *  - Ragged batches ("M7.8 - Speculative Serving", section 0x01, N_query = sum_i (K_i + 1)):
+ *  - Ragged batches ("M7.8 - Speculative Serving", section 0x00, background on the serving unit,
+ *    N_query = sum_i (K_i + 1)):
  *    request i has K_i = cu[i+1] - cu[i] draft tokens, 0 <= K_i <= 64 (SDCP m_max <= 64).
  *    Draft row of (i, j), j < K_i:  row cu[i] + j        of draft_logits / draft_tokens.
  *    Target row of (i, j), j <= K_i: row cu[i] + i + j   of target_logits.
@@ -70,8 +71,9 @@ typedef enum {
  *   draw_uniform   [B]                 u of the drawn position                        (T > 0)
  *   terminal_kind  [B]                 one of sdv_terminal_kind
  *   events         hipEvent_t handles (cast to void*) recorded on the stream: events[0] before the
- *                  first kernel, events[k] after the k-th kernel.  The kernels run in the order
- *                  row pass, accept scan, terminal draw (the last is skipped at T == 0).
+ *                  first kernel, events[1] after the row pass (one record per 16 KiB chunk of
+ *                  every row read), events[2] after the verdict kernel (per request: fold, accept
+ *                  scan, terminal draw).  events[3] is not used.
  */
 typedef struct sdv_diag {
   double* target_lse;
@@ -139,6 +141,17 @@ int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int
  * keys [n][2], out [n][4] are uint32 device arrays.  n < 1 or NULL pointers -> SDV_ERR_INVALID_ARG.
  */
 int sdv_philox4x32_10(const uint32_t* counters, const uint32_t* keys, int64_t n, uint32_t* out, void* stream);
+
+/*
+ * Measurement hook: the bandwidth yardstick of the row pass.  Decoding is limited by memory
+ * bandwidth, not arithmetic (SDCP, section "Introduction", its background paragraph; "SOTA-227",
+ * section "Why it is free rather than a trade"); this kernel reads n_chunks consecutive 16 KiB
+ * chunks of src (device, 16-byte aligned, n_chunks * 16384 bytes) with exactly the row pass's loads
+ * and no arithmetic, and writes out[c] (device uint32 [n_chunks]) = the xor of the 4096 words of
+ * chunk c.  Its rate is the best a single read-once stream of this shape reaches.  n_chunks < 1,
+ * NULL or misaligned pointers -> SDV_ERR_INVALID_ARG.
+ */
+int sdv_read_ceiling(const void* src, int64_t n_chunks, uint32_t* out, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* sdv_status_string(int status);

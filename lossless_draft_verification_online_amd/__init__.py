@@ -14,7 +14,7 @@ from . import _native
 from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_RESIDUAL,
                       TERM_RESIDUAL_EMPTY, SdvError)
 
-__all__ = ["verify", "verify_ex", "workspace_bytes", "philox4x32_10", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+__all__ = ["verify", "verify_ex", "workspace_bytes", "philox4x32_10", "read_ceiling", "abi_version", "SdvError", "SDV_MAX_DEPTH",
            "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
 
 _DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
@@ -132,4 +132,23 @@ def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor) -> torch.Tensor:
                                              torch.cuda.current_stream(counters.device).cuda_stream)
     if rc != 0:
         raise SdvError(rc, "sdv_philox4x32_10")
+    return out
+
+
+READ_CHUNK_BYTES = 16384
+
+
+def read_ceiling(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The row pass's loads with no arithmetic over a contiguous device buffer of whole 16 KiB
+    chunks: returns the xor of each chunk's 32-bit words (int32 view), one per chunk."""
+    nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous() or nbytes % READ_CHUNK_BYTES:
+        raise ValueError("read_ceiling needs a contiguous buffer of whole 16 KiB chunks")
+    n = nbytes // READ_CHUNK_BYTES
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=src.device)
+    with torch.cuda.device(src.device):
+        rc = _native.lib().sdv_read_ceiling(_ptr(src), n, _ptr(out), torch.cuda.current_stream(src.device).cuda_stream)
+    if rc != 0:
+        raise SdvError(rc, "sdv_read_ceiling")
     return out

@@ -61,6 +61,8 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_philox4x32_10.restype = ctypes.c_int
     L.sdv_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.restype = ctypes.c_char_p
+    L.sdv_read_ceiling.restype = ctypes.c_int
+    L.sdv_read_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.argtypes = [ctypes.c_int]
     L.sdv_abi_version.restype = ctypes.c_int
     L.sdv_abi_version.argtypes = []

@@ -781,6 +781,28 @@ __global__ void philox_kernel(const uint32_t* __restrict__ ctr, const uint32_t* 
   out[4 * b + 3] = r.w3;
 }
 
+// ============================================================================ read ceiling
+// The row pass's access pattern with no arithmetic: one wave per 16 KiB chunk, sixteen 16-byte
+// non-temporal loads per lane, the words folded by xor so that no load is dead.  Its rate is the
+// bandwidth a one-pass stream can reach, the yardstick for the row pass.
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n_chunks,
+                                                    uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t c = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (c >= n_chunks) return;
+  const u32x4* v = src + c * (kChunkBytes / 16);
+  u32x4 buf[kVecPerLane];
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) buf[k] = __builtin_nontemporal_load(v + lane + kWave * k);
+  uint32_t x = 0;
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) x ^= buf[k].x ^ buf[k].y ^ buf[k].z ^ buf[k].w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, kWave);
+  if (lane == 0) out[c] = x;
+}
+
 // ============================================================================ host side
 
 struct Layout {
@@ -914,6 +936,14 @@ int sdv_philox4x32_10(const uint32_t* counters, const uint32_t* keys, int64_t n,
   if ((n + 255) / 256 > INT32_MAX) return SDV_ERR_LIMIT;
   hipLaunchKernelGGL(sdv::philox_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), counters, keys, n, out);
+  return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
+}
+
+int sdv_read_ceiling(const void* src, int64_t n_chunks, uint32_t* out, void* stream) {
+  if (!src || !out || n_chunks < 1 || (uintptr_t)src % 16 != 0) return SDV_ERR_INVALID_ARG;
+  if ((n_chunks + 3) / 4 > INT32_MAX) return SDV_ERR_LIMIT;
+  hipLaunchKernelGGL(sdv::read_kernel, dim3((unsigned)((n_chunks + 3) / 4)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const sdv::u32x4*>(src), n_chunks, out);
   return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
 }
 

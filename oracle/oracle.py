@@ -8,7 +8,8 @@ Semantics (each documented where the C source defines it):
     Protocol (SDCP)", section "Acceptance Rules"; the accept test r <= p/q of "SOTA-227", section
     "What to do".
   * ragged batches: request i owns draft rows cu[i]..cu[i+1]-1 and target rows cu[i]+i..cu[i+1]+i
-    ("M7.8 - Speculative Serving", section 0x01: one extra target row per request beyond its K_i).
+    ("M7.8 - Speculative Serving", section 0x00, its background on the serving unit: one extra
+    target row per request beyond its K_i).
 """
 from __future__ import annotations
 

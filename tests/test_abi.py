@@ -29,7 +29,7 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
-                          "sdv_status_string", "sdv_abi_version"}
+                          "sdv_read_ceiling", "sdv_status_string", "sdv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
@@ -42,11 +42,11 @@ def test_abi_version_and_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # row-pass records (8 B per 16 KiB chunk of every row) + 32 B per request + 8 B per request-chunk
+    # row-pass records: 8 B per 16 KiB chunk of every target and draft row, 256-byte aligned
     ws = lib.sdv_workspace_bytes(256, 1024, 128256, 0)
     chunks = (128256 + 8191) // 8192
     assert chunks == 16
-    assert ws >= (1280 + 1024) * chunks * 8 + 256 * 32 + 256 * chunks * 8
+    assert ws == -(-(1280 + 1024) * chunks * 8 // 256) * 256
     assert ws % 256 == 0
     assert lib.sdv_workspace_bytes(0, 10, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, -1, 10, 0) == 0
@@ -87,6 +87,10 @@ def test_host_argument_errors(lib):
     assert _call(lib, B=2**31 - 1, n_d=2**31 - 2, ws_bytes=2**62) == -3
     assert lib.sdv_philox4x32_10(None, FAKE, 4, FAKE, None) == -1
     assert lib.sdv_philox4x32_10(FAKE, FAKE, 0, FAKE, None) == -1
+    assert lib.sdv_read_ceiling(None, 4, FAKE, None) == -1
+    assert lib.sdv_read_ceiling(FAKE, 0, FAKE, None) == -1
+    assert lib.sdv_read_ceiling(FAKE + 8, 4, FAKE, None) == -1  # not 16-byte aligned
+    assert lib.sdv_read_ceiling(FAKE, 4, None, None) == -1
 
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):

@@ -196,3 +196,15 @@ def test_repeat_launches_are_deterministic():
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1])
         assert np.array_equal(first[2]["target_lse"], again[2]["target_lse"])
         assert np.array_equal(first[2]["ratio"], again[2]["ratio"], equal_nan=True)
+
+
+# ----------------------------------------------------------------------------- read yardstick
+
+def test_read_ceiling_folds_every_word():
+    import lossless_draft_verification_online_amd as sdv
+    rng = np.random.default_rng(11)
+    n_chunks = 1037
+    words = rng.integers(0, 2**32, size=n_chunks * 4096, dtype=np.uint64).astype(np.uint32)
+    got = sdv.read_ceiling(torch.from_numpy(words.view(np.int32)).to(DEV)).cpu().numpy().view(np.uint32)
+    want = np.bitwise_xor.reduce(words.reshape(n_chunks, 4096), axis=1)
+    assert np.array_equal(got, want)

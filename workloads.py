@@ -9,7 +9,7 @@ The pages measure on no public benchmark or dataset that could be loaded here.  
 workloads and trained models are replaced by Gaussian logits: target z ~ N(0, s_t^2), draft
 z + N(0, s_d^2), so that the draft/target agreement (the acceptance rate alpha) is set by s_d.
 
-Layout of a ragged batch ("M7.8 - Speculative Serving", section 0x01: N_query = sum_i (K_i + 1)):
+Layout of a ragged batch ("M7.8 - Speculative Serving", section 0x00, background on the serving unit: N_query = sum_i (K_i + 1)):
   cu[i]       exclusive prefix sum of the depths K_i, cu[0] = 0, cu[B] = n_draft_rows
   draft rows  request i, position j < K_i  -> row cu[i] + j
   target rows request i, position j <= K_i -> row cu[i] + i + j
