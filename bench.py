@@ -12,7 +12,7 @@ one launch / its mean duration from HIP events recorded on the library's stream)
 a plain read of the same size with the row pass's loads, per-call percentiles, accepted-length
 statistics and the CPU oracle's rate on the host.
 
-  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64] [--steps K] [--warmup W]
+  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1] [--steps K] [--warmup W]
 
 Profile summaries (rocprofv3 output -> text under profiles/):
 
@@ -61,6 +61,8 @@ def make_workload(name: str, set_index: int):
         return W.greedy_b512(data_seed=W.DATA_SEED_BASE + 5 + 1000 * set_index, verify_seed=5000)
     if name == "uniform_b64":
         return W.uniform_b64(data_seed=W.DATA_SEED_BASE + 3 + 1000 * set_index, verify_seed=3000)
+    if name == "small_b1":
+        return W.small_b1(set_index)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -131,7 +133,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64"])
+    ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1"])
     ap.add_argument("--sets", type=int, default=2, help="input sets rotated through the timed steps")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--no-check", action="store_true", help="skip the oracle comparison of one call")
