@@ -170,11 +170,13 @@ __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32
   }
 }
 
-// Residual weight max(p - q, 0), both sides scaled by the same factor 2^(l2_t - ref_t).
-__device__ __forceinline__ float resid_weight(float zt, float zd, float k2, float ref_t, float e_hi, float e_lo) {
+// Residual weight max(p - q, 0), both sides scaled by the same factor 2^(l2_t - ref_t).  The draft
+// side is 2^(z_d k - e); e is split into its fp32 rounding e_hi and a remainder that enters as the
+// factor q_scale = 2^(e_hi - e), applied by the final fused multiply-add.
+__device__ __forceinline__ float resid_weight(float zt, float zd, float k2, float ref_t, float e_hi, float q_scale) {
   const float p = fast_exp2(fmaf(zt, k2, -ref_t));
-  const float q = fast_exp2(fmaf(zd, k2, -e_hi) - e_lo);
-  return fmaxf(p - q, 0.0f);
+  const float q = fast_exp2(fmaf(zd, k2, -e_hi));
+  return fmaxf(fmaf(-q, q_scale, p), 0.0f);
 }
 
 // Inverse CDF inside one chunk: the smallest v in [c0, c0 + n) whose running mass exceeds target.
@@ -184,11 +186,11 @@ __device__ __forceinline__ float resid_weight(float zt, float zd, float k2, floa
 // element.  If rounding leaves the target unreached, the last element of positive weight is taken.
 template <class E, bool kVec, bool kResid>
 __device__ __forceinline__ int32_t search_chunk(const char* trow, const char* drow, int32_t c0, int32_t n, double target,
-                                float k2, float ref_t, float e_hi, float e_lo, int lane) {
+                                float k2, float ref_t, float e_hi, float q_scale, int lane) {
   constexpr int run = kVecPerLane * E::kPerVec;  // 128 bf16 or 64 fp32 elements
   constexpr int per_lane = run / kWave;          // 2 or 1 elements per lane in step 2
   auto weight = [&](float zt, float zd) -> float {
-    if constexpr (kResid) return resid_weight(zt, zd, k2, ref_t, e_hi, e_lo);
+    if constexpr (kResid) return resid_weight(zt, zd, k2, ref_t, e_hi, q_scale);
     return fast_exp2(fmaf(zt, k2, -ref_t));
   };
   const int32_t end = c0 + n;
@@ -312,7 +314,7 @@ __device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, 
 // fp64 across vectors and lanes.
 template <class E, bool kVec>
 __device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* dp, int32_t c0, int32_t n, float k2, float ref_t,
-                                   float e_hi, float e_lo, int lane) {
+                                   float e_hi, float q_scale, int lane) {
   double acc = 0.0;
   if constexpr (kVec) {
     const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
@@ -335,13 +337,13 @@ __device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* d
         E::unpack(tb[k], ft);
         E::unpack(db[k], fd);
 #pragma unroll
-        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, e_lo);
+        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, q_scale);
         acc += (double)tree_sum(ft);
       }
     }
   } else {
     for (int32_t v = c0 + lane; v < c0 + n; v += kWave)
-      acc += (double)resid_weight(E::at(tp, v), E::at(dp, v), k2, ref_t, e_hi, e_lo);
+      acc += (double)resid_weight(E::at(tp, v), E::at(dp, v), k2, ref_t, e_hi, q_scale);
   }
   return wave_sum(acc);
 }
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
 // the bounds-tested path.
 template <class E>
 __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const char* dp, int32_t V, int32_t C, float k2,
-                                                       float ref_t, float e_hi, float e_lo, double* lds_mass,
+                                                       float ref_t, float e_hi, float q_scale, double* lds_mass,
                                                        int lane, int wave, int n_waves) {
   constexpr int kHalf = kVecPerLane / 2;
   struct Half {
@@ -391,7 +393,7 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
       E::unpack(b.t[k], ft);
       E::unpack(b.d[k], fd);
 #pragma unroll
-      for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, e_lo);
+      for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, q_scale);
       acc += (double)tree_sum(ft);
     }
     return acc;
@@ -420,7 +422,7 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
   }
   if (c < C) {  // the partial last chunk, if this wave owns it
     const int32_t c0 = c * E::kChunk;
-    const double cm = resid_chunk_mass<E, true>(tp, dp, c0, V - c0, k2, ref_t, e_hi, e_lo, lane);
+    const double cm = resid_chunk_mass<E, true>(tp, dp, c0, V - c0, k2, ref_t, e_hi, q_scale, lane);
     if (lane == 0) lds_mass[c] = cm;
   }
 }
@@ -431,7 +433,7 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
 // Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
 template <class E, bool kResid>
 __device__ __forceinline__ int32_t search_chunk_block(const char* trow, const char* drow, int32_t c0, int32_t n,
-                                                      double target, float k2, float ref_t, float e_hi, float e_lo,
+                                                      double target, float k2, float ref_t, float e_hi, float q_scale,
                                                       double* scratch, int lane, int wave, int n_waves) {
   constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
   const int32_t nvec = n / E::kPerVec;
@@ -443,7 +445,7 @@ __device__ __forceinline__ int32_t search_chunk_block(const char* trow, const ch
     if constexpr (kResid) E::unpack(dd, fd);
 #pragma unroll
     for (int q = 0; q < E::kPerVec; ++q)
-      w[q] = kResid ? resid_weight(ft[q], fd[q], k2, ref_t, e_hi, e_lo) : fast_exp2(fmaf(ft[q], k2, -ref_t));
+      w[q] = kResid ? resid_weight(ft[q], fd[q], k2, ref_t, e_hi, q_scale) : fast_exp2(fmaf(ft[q], k2, -ref_t));
   };
   // rows owned by this wave: wave and wave + n_waves (n_waves == 8 covers the 16 rows)
   u32x4 t[2], dd[2];
@@ -559,7 +561,7 @@ __device__ __forceinline__ void write_reject(const Params& P, int32_t i, int32_t
 struct Decision {
   int32_t kind;  // sdv_terminal_kind, SDV_TERM_BAD when the request is rejected
   int32_t a;
-  float ref_t, e_hi, e_lo, u;
+  float ref_t, e_hi, q_scale, u;
 };
 
 template <class E, bool kVec>
@@ -685,12 +687,12 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
           d.u = draw_uniform(verifier_block(P.seed, (uint32_t)i, (uint32_t)K));
         } else {
           // weights in the frame 2^(z_t k - ref_t) of the rejected target row; draft side
-          // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi + e_lo
+          // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and the factor 2^-(e - e_hi)
           d.kind = SDV_TERM_RESIDUAL;
           d.ref_t = __shfl(ft.ref, a, kWave);
           const double e = (double)d.ref_t + __shfl(fd.l2, a, kWave) - __shfl(ft.l2, a, kWave);
           d.e_hi = (float)e;
-          d.e_lo = (float)(e - (double)d.e_hi);
+          d.q_scale = (float)exp2((double)d.e_hi - e);
           d.u = __shfl(draw_uniform(blk), a, kWave);
         }
       }
@@ -715,12 +717,12 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   // residual masses of every chunk, into shared memory
   if (residual) {
     if constexpr (kVec) {
-      resid_masses_pipelined<E>(tp, dp, P.V, P.C, P.k2, d.ref_t, d.e_hi, d.e_lo, lds_mass, lane, wave, n_waves);
+      resid_masses_pipelined<E>(tp, dp, P.V, P.C, P.k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
     } else {
       for (int32_t c = wave; c < P.C; c += n_waves) {
         const int32_t c0 = c * E::kChunk;
         const double cm = resid_chunk_mass<E, false>(tp, dp, c0, min(E::kChunk, P.V - c0), P.k2, d.ref_t, d.e_hi,
-                                                     d.e_lo, lane);
+                                                     d.q_scale, lane);
         if (lane == 0) lds_mass[c] = cm;
       }
     }
@@ -751,13 +753,13 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const int32_t n = min(E::kChunk, P.V - s0);
   int32_t y = -1;
   if constexpr (kVec) {
-    y = residual ? search_chunk_block<E, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.e_lo, lds_mass + P.C,
+    y = residual ? search_chunk_block<E, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C,
                                                lane, wave, n_waves)
                  : search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
                                                 lane, wave, n_waves);
   } else {
     if (wave != 0) return;
-    y = residual ? search_chunk<E, false, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.e_lo, lane)
+    y = residual ? search_chunk<E, false, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.q_scale, lane)
                  : search_chunk<E, false, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lane);
   }
   if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
