@@ -74,6 +74,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.oracle_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = None
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _LIBS[path] = lib
     return lib
 
@@ -169,3 +171,7 @@ def row_argmax(row: np.ndarray) -> int:
 
 def num_threads() -> int:
     return load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    load().oracle_set_num_threads(n)

@@ -346,10 +346,12 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
   return failed ? -2 : 0;
 }
 
-/* Number of OpenMP threads the oracle runs on (for reporting). */
+/* Number of OpenMP threads the oracle runs on (for reporting), and a way to change it (timing). */
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif
