@@ -62,6 +62,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
     ]
+    lib.oracle_verify_profiled.restype = ctypes.c_int
+    lib.oracle_verify_profiled.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
+    ]
     lib.oracle_philox4x32_10.restype = None
     lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.oracle_philox_block.restype = None
@@ -93,11 +99,12 @@ def _dtype_code(logits: np.ndarray) -> int:
 
 
 def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, cu: np.ndarray,
-           temperature: float, seed: int, diag: bool = False, lib_path: str = LIBRARY) -> dict:
+           temperature, seed, diag: bool = False, lib_path: str = LIBRARY) -> dict:
     """Run the oracle on one ragged batch.
 
     target: (n_draft_rows + B, V); draft: (n_draft_rows, V) or None when temperature == 0;
     draft_tokens: (n_draft_rows,) int32; cu: (B + 1,) int32 exclusive prefix sums of K_i.
+    temperature and seed are scalars, or arrays of B values (one sampling profile per request).
     Returns accepted_len (B,), out_tokens (n_draft_rows + B,), and with ``diag`` the per-row LSEs,
     argmaxes, ratios, margins, residual masses and terminal kinds.
     """
@@ -129,8 +136,16 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
         )
         dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
         dg_p = ctypes.pointer(dg)
-    rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
-                           float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(acc), _ptr(out), dg_p)
+    if np.ndim(temperature) == 0 and np.ndim(seed) == 0:
+        rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
+                               float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(acc), _ptr(out), dg_p)
+    else:
+        t_each = np.ascontiguousarray(np.broadcast_to(np.asarray(temperature, dtype=np.float64), (B,)))
+        s_each = np.ascontiguousarray(np.broadcast_to(
+            np.asarray([int(x) & 0xFFFFFFFFFFFFFFFF for x in np.ravel(seed)], dtype=np.uint64)
+            if np.ndim(seed) else np.uint64(int(seed) & 0xFFFFFFFFFFFFFFFF), (B,)))
+        rc = lib.oracle_verify_profiled(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
+                                        _ptr(t_each), _ptr(s_each), _ptr(acc), _ptr(out), dg_p)
     if rc != 0:
         raise ValueError(f"oracle_verify rejected its arguments (status {rc})")
     return res

@@ -220,8 +220,9 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   const int64_t drow0 = lo;     /* draft rows of request i:  drow0 .. drow0 + K - 1 */
   int32_t* slots = out_tokens + trow0;
 
-  int bad = 0;
-  for (int64_t j = 0; j < K; ++j)
+  /* a temperature that is negative, NaN or infinite describes no sampling profile */
+  int bad = !(T >= 0.0) || isinf(T);
+  for (int64_t j = 0; j < K && !bad; ++j)
     if (tokens[drow0 + j] < 0 || tokens[drow0 + j] >= V) bad = 1;
   /* q_j(x_j) = 0 exactly when the draft logit at x_j is -inf; checked before any draw */
   if (!bad && T > 0.0)
@@ -327,12 +328,10 @@ static void verify_request(const void* target, const void* draft, int dtype, con
  * out_tokens    [n_draft_rows + B]  out: request i owns slots cu[i]+i .. cu[i]+i+K_i
  * Returns 0, or -1 for arguments that describe no batch.
  */
-int oracle_verify(const void* target, const void* draft, int dtype, const int32_t* draft_tokens, const int32_t* cu,
-                  int32_t B, int64_t n_draft_rows, int32_t V, double T, uint64_t seed, int32_t* accepted_len,
-                  int32_t* out_tokens, oracle_diag* diag) {
-  if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens) return -1;
-  if (B <= 0 || V <= 0 || n_draft_rows < 0 || !(T >= 0.0) || (T > 0.0 && !draft)) return -1;
-  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
+static int verify_batch(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
+                        const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, double T, uint64_t seed,
+                        const double* T_each, const uint64_t* seed_each, int32_t* accepted_len,
+                        int32_t* out_tokens, oracle_diag* diag) {
   int failed = 0;
 #pragma omp parallel reduction(| : failed)
   {
@@ -340,10 +339,39 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
     if (!w) failed = 1;
 #pragma omp for schedule(dynamic, 1)
     for (int32_t i = 0; i < B; ++i)
-      if (w) verify_request(target, draft, dtype, draft_tokens, cu, i, n_draft_rows, V, T, seed, accepted_len, out_tokens, diag, w);
+      if (w)
+        verify_request(target, draft, dtype, draft_tokens, cu, i, n_draft_rows, V, T_each ? T_each[i] : T,
+                       seed_each ? seed_each[i] : seed, accepted_len, out_tokens, diag, w);
     free(w);
   }
   return failed ? -2 : 0;
+}
+
+int oracle_verify(const void* target, const void* draft, int dtype, const int32_t* draft_tokens, const int32_t* cu,
+                  int32_t B, int64_t n_draft_rows, int32_t V, double T, uint64_t seed, int32_t* accepted_len,
+                  int32_t* out_tokens, oracle_diag* diag) {
+  if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens) return -1;
+  if (B <= 0 || V <= 0 || n_draft_rows < 0 || !(T >= 0.0) || isinf(T) || (T > 0.0 && !draft)) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
+  return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, T, seed, NULL, NULL, accepted_len,
+                      out_tokens, diag);
+}
+
+/*
+ * The same with a sampling profile per request (SDCP "Session Contract": every session carries its
+ * own profile, and a verification batch gathers many sessions).  temperature[i] and seed[i] apply
+ * to request i: temperature 0 selects Rule 1 for that request, a positive one Rule 2; a negative,
+ * NaN or infinite temperature rejects the request (accepted_len -1, all of its slots -1).  draft
+ * may be NULL only when n_draft_rows == 0.
+ */
+int oracle_verify_profiled(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
+                           const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, const double* temperature,
+                           const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* diag) {
+  if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens || !temperature || !seed) return -1;
+  if (B <= 0 || V <= 0 || n_draft_rows < 0 || (n_draft_rows > 0 && !draft)) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
+  return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, 0.0, 0, temperature, seed,
+                      accepted_len, out_tokens, diag);
 }
 
 /* Number of OpenMP threads the oracle runs on (for reporting), and a way to change it (timing). */

@@ -2,7 +2,8 @@
 
 Each case plants one mistake in a copy of the oracle's C source (on the CPU only), builds it, and
 checks that at least one pin fails: the Monte Carlo against the exact enumeration, the
-closed-form LSE, the planted argmax tie, the K = 0 categorical draw, or the rocRAND Philox values.
+closed-form LSE, the planted argmax tie, the rocRAND Philox values, or the per-request profile
+check (each request of a profiled batch against the scalar run with its own profile).
 """
 import ctypes
 import os
@@ -30,6 +31,9 @@ MUTATIONS = {
                               "kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) * (v + 1);"),
     "greedy_tie_to_largest": ("if (z > best_z) {", "if (z >= best_z) {"),
     "philox_key_bumped_every_round": ("if (round > 0) {", "if (round >= 0) {"),
+    "profile_temperature_of_first_request": ("T_each ? T_each[i] : T", "T_each ? T_each[0] : T"),
+    "profile_seed_of_next_request": ("seed_each ? seed_each[i] : seed", "seed_each ? seed_each[(i + 1) % B] : seed"),
+    "profile_invalid_temperature_accepted": ("int bad = !(T >= 0.0) || isinf(T);", "int bad = 0;"),
     "temperature_ignored": ("const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) / T -",
                             "const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) -"),
 }
@@ -114,8 +118,37 @@ def _pin_philox(lib_path, tmp_path):
     return ref.split("\n")[:16] == got
 
 
+def _pin_profiles(lib_path):
+    """Request i of a batch with per-request (T_i, seed_i) equals request i of the scalar run with
+    (T_i, seed_i); a NaN temperature rejects its request alone."""
+    rng = np.random.default_rng(8)
+    depths = rng.integers(0, 5, size=12)
+    cu = offsets_from_depths(depths)
+    n_d, B, V = int(cu[-1]), 12, 64
+    target = (rng.standard_normal((n_d + B, V)) * 2).astype(np.float32)
+    draft = (target[:n_d] + rng.standard_normal((n_d, V))).astype(np.float32)
+    tokens = rng.integers(0, V, size=n_d).astype(np.int32)
+    profiles = [(0.0, 3), (0.8, 4), (1.3, 5)]
+    pick = np.arange(B) % 3
+    T = np.array([profiles[k][0] for k in pick])
+    T[7] = np.nan
+    seeds = np.array([profiles[k][1] for k in pick], dtype=np.uint64)
+    got = oracle.verify(target, draft, tokens, cu, T, seeds, lib_path=lib_path)
+    if got["accepted_len"][7] != -1:
+        return False
+    for k, (t, sd) in enumerate(profiles):
+        ref = oracle.verify(target, draft, tokens, cu, t, sd, lib_path=lib_path)
+        for i in np.nonzero((pick == k) & (np.arange(B) != 7))[0]:
+            lo, hi = cu[i] + i, cu[i + 1] + i + 1
+            if got["accepted_len"][i] != ref["accepted_len"][i]:
+                return False
+            if not np.array_equal(got["out_tokens"][lo:hi], ref["out_tokens"][lo:hi]):
+                return False
+    return True
+
+
 def test_unmutated_oracle_passes_every_pin(tmp_path):
-    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie):
+    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles):
         assert check(oracle.LIBRARY)
     assert _pin_philox(oracle.LIBRARY, tmp_path)
 
@@ -130,5 +163,6 @@ def test_planted_mistake_is_caught(tmp_path, name):
         "lse": _pin_lse(lib),
         "greedy_tie": _pin_greedy_tie(lib),
         "philox": _pin_philox(lib, tmp_path),
+        "profiles": _pin_profiles(lib),
     }
     assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"
