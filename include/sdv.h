@@ -136,6 +136,27 @@ int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int
                   void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
 
 /*
+ * sdv_verify_ex with a sampling profile per request.  SDCP ("Speculative Decoding Coordination
+ * Protocol (SDCP)") fixes a sampling profile per session (section "Session Contract"; section
+ * "Sampling Policy Updates" lets it change between rounds), and one verification batch gathers
+ * requests of many sessions, so temperature and seed come per request:
+ *
+ *   temperature  [B] float device array: T_i = 0 selects Rule 1 for request i, T_i > 0 Rule 2 with
+ *                p = softmax(z_target / T_i), q = softmax(z_draft / T_i)
+ *   seed         [B] uint64 device array: the Philox key of request i (counter as in sdv_verify)
+ *
+ * Everything else is as in sdv_verify_ex.  draft_logits must be non-NULL whenever
+ * n_draft_rows > 0 (draft rows of greedy requests are not read).  A temperature that is negative,
+ * NaN, infinite, or so small that log2(e)/T_i overflows binary32 describes no profile: that request
+ * gets accepted_len = -1 and all of its K_i + 1 slots set to -1, and the other requests are
+ * unaffected.  NULL temperature or seed -> SDV_ERR_INVALID_ARG.
+ */
+int sdv_verify_profiled(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                        const float* temperature, const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
+
+/*
  * Raw Philox4x32-10 blocks on the device, for testing the verifier's uniforms: out[b] =
  * Philox4x32-10(counter = counters[b][0..3], key = keys[b][0..1]) for b < n.  counters [n][4],
  * keys [n][2], out [n][4] are uint32 device arrays.  n < 1 or NULL pointers -> SDV_ERR_INVALID_ARG.

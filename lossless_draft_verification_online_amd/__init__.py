@@ -46,6 +46,22 @@ def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
     return ws
 
 
+def _profile_arrays(temperature, seed, B, dev):
+    """Per-request profile tensors (temperature float32 [B], seed int64/uint64 [B] on the logits'
+    device), or None for one scalar profile."""
+    if not isinstance(temperature, torch.Tensor) and not isinstance(seed, torch.Tensor):
+        return None
+    if not (isinstance(temperature, torch.Tensor) and isinstance(seed, torch.Tensor)):
+        raise ValueError("per-request profiles need both temperature and seed as [B] tensors")
+    if temperature.dtype != torch.float32 or temperature.shape != (B,) or temperature.device != dev \
+            or not temperature.is_contiguous():
+        raise ValueError("temperature must be a contiguous float32 [B] tensor on the logits' device")
+    if seed.dtype not in (torch.int64, torch.uint64) or seed.shape != (B,) or seed.device != dev \
+            or not seed.is_contiguous():
+        raise ValueError("seed must be a contiguous int64 or uint64 [B] tensor on the logits' device")
+    return temperature, seed
+
+
 def _check(target, draft, draft_tokens, offsets, temperature):
     if not target.is_cuda:
         raise ValueError("target logits must be on the GPU")
@@ -64,14 +80,16 @@ def _check(target, draft, draft_tokens, offsets, temperature):
     B = offsets.shape[0] - 1
     if target.shape[0] != draft_tokens.shape[0] + B:
         raise ValueError("target logits must have n_draft_rows + B rows")
-    if temperature > 0 and draft is None and draft_tokens.shape[0] > 0:
-        raise ValueError("temperature > 0 needs draft logits")
+    needs_draft = isinstance(temperature, torch.Tensor) or temperature > 0
+    if needs_draft and draft is None and draft_tokens.shape[0] > 0:
+        raise ValueError("sampling (any temperature > 0, or per-request profiles) needs draft logits")
 
 
 def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, offsets: torch.Tensor,
-              temperature: float, seed: int, *, out: tuple | None = None, workspace: torch.Tensor | None = None,
+              temperature, seed, *, out: tuple | None = None, workspace: torch.Tensor | None = None,
               diag: tuple[str, ...] = (), events: list | None = None):
-    """Run sdv_verify_ex.  Returns (accepted_len, out_tokens, diag_dict).
+    """Run sdv_verify_ex, or sdv_verify_profiled when temperature and seed are [B] device tensors
+    (one sampling profile per request).  Returns (accepted_len, out_tokens, diag_dict).
 
     ``diag`` names the diagnostic arrays to fill (fields of sdv_diag); ``events`` up to four
     torch.cuda.Event objects recorded before the first kernel and after each kernel.
@@ -79,6 +97,7 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
     _check(target, draft, draft_tokens, offsets, temperature)
     dev = target.device
     B = offsets.shape[0] - 1
+    profile = _profile_arrays(temperature, seed, B, dev)
     n_d = draft_tokens.shape[0]
     V = target.shape[1]
     dt = _DTYPES[target.dtype]
@@ -106,19 +125,27 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
             if ev is not None:
                 dg.events[k] = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
     stream = torch.cuda.current_stream(dev).cuda_stream
+    dg_ref = ctypes.byref(dg) if dg is not None else None
     with torch.cuda.device(dev):
-        rc = _native.lib().sdv_verify_ex(
-            _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(offsets), B, n_d, V, dt, float(temperature),
-            int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(out_tokens), _ptr(ws),
-            ws.numel() * ws.element_size(), stream, ctypes.byref(dg) if dg is not None else None)
+        if profile is None:
+            rc = _native.lib().sdv_verify_ex(
+                _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(offsets), B, n_d, V, dt, float(temperature),
+                int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(out_tokens), _ptr(ws),
+                ws.numel() * ws.element_size(), stream, dg_ref)
+        else:
+            rc = _native.lib().sdv_verify_profiled(
+                _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(offsets), B, n_d, V, dt, _ptr(profile[0]),
+                _ptr(profile[1]), _ptr(accepted_len), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+                stream, dg_ref)
     if rc != 0:
-        raise SdvError(rc, "sdv_verify_ex")
+        raise SdvError(rc, "sdv_verify_profiled" if profile is not None else "sdv_verify_ex")
     return accepted_len, out_tokens, dvals
 
 
 def verify(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, offsets: torch.Tensor,
-           temperature: float, seed: int, *, out: tuple | None = None, workspace: torch.Tensor | None = None):
-    """sdv_verify: (accepted_len [B] int32, out_tokens [n_draft_rows + B] int32), enqueued on the current stream."""
+           temperature, seed, *, out: tuple | None = None, workspace: torch.Tensor | None = None):
+    """sdv_verify (or sdv_verify_profiled for [B] tensors of temperatures and seeds): (accepted_len [B]
+    int32, out_tokens [n_draft_rows + B] int32), enqueued on the current stream."""
     a, o, _ = verify_ex(target, draft, draft_tokens, offsets, temperature, seed, out=out, workspace=workspace)
     return a, o
 

@@ -58,6 +58,9 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_verify.argtypes = list(_VERIFY_ARGS)
     L.sdv_verify_ex.restype = ctypes.c_int
     L.sdv_verify_ex.argtypes = list(_VERIFY_ARGS) + [ctypes.POINTER(SdvDiag)]
+    L.sdv_verify_profiled.restype = ctypes.c_int
+    L.sdv_verify_profiled.argtypes = (list(_VERIFY_ARGS[:8]) + [ctypes.c_void_p, ctypes.c_void_p]
+                                      + list(_VERIFY_ARGS[10:]) + [ctypes.POINTER(SdvDiag)])
     L.sdv_philox4x32_10.restype = ctypes.c_int
     L.sdv_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.restype = ctypes.c_char_p

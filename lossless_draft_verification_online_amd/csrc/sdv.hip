@@ -55,10 +55,40 @@ struct Params {
   int32_t B, n_d, n_t, V, C;
   int64_t n_units;
   int64_t lds_records;  // chunk records the verdict kernel can stage in shared memory
-  float k2;  // log2(e) / T, or 0 for the greedy rule
+  float k2;  // log2(e) / T, or 0 for the greedy rule (one profile for the whole batch)
   uint64_t seed;
+  const float* temp_each;     // [B] temperature of each request, or null: one profile for the batch
+  const uint64_t* seed_each;  // [B] seed of each request (with temp_each)
   DiagPtrs dg;
 };
+
+// ============================================================================ sampling profiles
+
+// k = log2(e) / T in fp32 for a temperature T: 0 selects the greedy rule; NaN marks a temperature
+// that describes no profile (negative, NaN, infinite, or so small that k overflows fp32).
+__device__ __forceinline__ float k2_of(float T) {
+  if (T == 0.0f) return 0.0f;
+  if (!(T > 0.0f) || isinf(T)) return __int_as_float(0x7fc00000);
+  const float k2 = (float)(1.4426950408889634074 / (double)T);
+  return isfinite(k2) && k2 > 0.0f ? k2 : __int_as_float(0x7fc00000);
+}
+
+// The request a logit row belongs to, by a wave-uniform binary search over the offsets read through
+// the scalar cache (these reads do not wait behind the stream's vector loads).  Target row r
+// belongs to the largest i < B with cu[i] + i <= r; draft row d to the largest i < B with
+// cu[i] <= d.  Offsets that are not non-decreasing still give an index in [0, B); such batches are
+// rejected by the verdict kernel.
+__device__ __forceinline__ int32_t request_of_row(const int32_t* cu, int32_t B, int32_t row, bool target) {
+  const __attribute__((address_space(4))) int32_t* c = (const __attribute__((address_space(4))) int32_t*)cu;
+  int32_t lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int32_t mid = lo + (hi - lo) / 2;
+    const int64_t key = (int64_t)c[mid] + (target ? mid : 0);
+    if (key <= row) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
 
 // ============================================================================ offsets
 
@@ -87,62 +117,71 @@ __device__ __forceinline__ u32x4 load_vec_nt(const u32x4* v, int vi, int32_t nve
   return vi < nvec ? __builtin_nontemporal_load(v + vi) : neg_inf_vec<E>();
 }
 
+// The 16 vectors per lane of one 16 KiB chunk (16-byte aligned rows), -inf past the row's end.
+// The stream is read once: non-temporal loads keep it from displacing reused lines in L2.
+template <class E>
+__device__ __forceinline__ void load_chunk(const char* rp, int32_t c0, int32_t n, int lane, u32x4 (&buf)[kVecPerLane]) {
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+  const int32_t nvec = n / E::kPerVec;
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) buf[k] = load_vec_nt<E>(vp, lane + kWave * k, nvec);
+}
+
+// The record of a loaded chunk: (ref, sum 2^(z k - ref)) at T > 0, (max, first index of max) at T = 0.
+template <class E, bool kGreedy>
+__device__ __forceinline__ float2 record_of(u32x4 (&buf)[kVecPerLane], int32_t c0, float k2, int lane) {
+  if constexpr (kGreedy) {
+    float best = -INFINITY;
+    int32_t idx = INT32_MAX;
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+      float f[E::kPerVec];
+      E::unpack(buf[k], f);
+      const int32_t e0 = c0 + (lane + kWave * k) * E::kPerVec;
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) {
+        if (f[e] > best) {  // ascending within the lane: the first maximum is kept
+          best = f[e];
+          idx = e0 + e;
+        }
+      }
+    }
+    wave_argmax(best, idx);
+    return make_float2(best, __int_as_float(idx));
+  } else {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+      float f[E::kPerVec];
+      E::unpack(buf[k], f);
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
+    }
+    m = wave_max(m);
+    if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+    const float ref = m * k2;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+      // re-unpack from the raw words rather than keep every unpacked element live across the max
+      asm volatile("" : "+v"(buf[k]));
+      float f[E::kPerVec];
+      E::unpack(buf[k], f);
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
+      acc[k & 3] += tree_sum(f);
+    }
+    return make_float2(ref, wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3])));
+  }
+}
+
 // One 16 KiB chunk: (ref, sum 2^(z k - ref)) at T > 0, (max, first index of max) at T = 0.
 template <class E, bool kGreedy, bool kVec>
 __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32_t n, float k2, int lane) {
   if constexpr (kVec) {
-    const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
-    const int32_t nvec = n / E::kPerVec;
-    // the stream is read once: non-temporal loads keep it from displacing reused lines in L2
     u32x4 buf[kVecPerLane];
-#pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-      const int vi = lane + kWave * k;
-      buf[k] = load_vec_nt<E>(vp, vi, nvec);
-    }
-    if constexpr (kGreedy) {
-      float best = -INFINITY;
-      int32_t idx = INT32_MAX;
-#pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) {
-        float f[E::kPerVec];
-        E::unpack(buf[k], f);
-        const int32_t e0 = c0 + (lane + kWave * k) * E::kPerVec;
-#pragma unroll
-        for (int e = 0; e < E::kPerVec; ++e) {
-          if (f[e] > best) {  // ascending within the lane: the first maximum is kept
-            best = f[e];
-            idx = e0 + e;
-          }
-        }
-      }
-      wave_argmax(best, idx);
-      return make_float2(best, __int_as_float(idx));
-    } else {
-      float m = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) {
-        float f[E::kPerVec];
-        E::unpack(buf[k], f);
-#pragma unroll
-        for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
-      }
-      m = wave_max(m);
-      if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
-      const float ref = m * k2;
-      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) {
-        // re-unpack from the raw words rather than keep every unpacked element live across the max
-        asm volatile("" : "+v"(buf[k]));
-        float f[E::kPerVec];
-        E::unpack(buf[k], f);
-#pragma unroll
-        for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
-        acc[k & 3] += tree_sum(f);
-      }
-      return make_float2(ref, wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3])));
-    }
+    load_chunk<E>(rp, c0, n, lane, buf);
+    return record_of<E, kGreedy>(buf, c0, k2, lane);
   } else {
     const int32_t c1 = c0 + n;
     if constexpr (kGreedy) {
@@ -348,16 +387,51 @@ __device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* d
   return wave_sum(acc);
 }
 
-template <class E, bool kGreedy, bool kVec>
+// How a launch chooses the rule: one greedy or one sampling profile for the batch, or a profile per
+// request (the rule of each row then follows its request's temperature).
+enum Mode : int { kModeGreedy = 0, kModeSampling = 1, kModeProfiled = 2 };
+
+// The temperature of request i, read through the scalar cache (the index is wave-uniform).
+__device__ __forceinline__ float temperature_of(const float* temp_each, int32_t i) {
+  return ((const __attribute__((address_space(4))) float*)temp_each)[i];
+}
+
+template <class E, int kMode, bool kVec>
 __global__ __launch_bounds__(256) void row_records(Params P) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  // the unit is wave-uniform; saying so lets the request lookup use scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
   if (u >= P.n_units) return;
   const int32_t slot = (int32_t)(u / P.C);
   const int32_t c = (int32_t)(u - (int64_t)slot * P.C);
-  const char* rp = slot < P.n_t ? row_ptr<E>(P.target, slot, P.V) : row_ptr<E>(P.draft, slot - P.n_t, P.V);
+  const bool target = slot < P.n_t;
+  const char* rp = target ? row_ptr<E>(P.target, slot, P.V) : row_ptr<E>(P.draft, slot - P.n_t, P.V);
   const int32_t c0 = c * E::kChunk;
-  const float2 rec = chunk_record<E, kGreedy, kVec>(rp, c0, min(E::kChunk, P.V - c0), P.k2, lane);
+  const int32_t n = min(E::kChunk, P.V - c0);
+  float2 rec;
+  if constexpr (kMode != kModeProfiled) {
+    rec = chunk_record<E, kMode == kModeGreedy, kVec>(rp, c0, n, P.k2, lane);
+  } else {
+    // a target row is always read, so its loads go out before the request lookup; a draft row is
+    // read only for a request that samples, so the lookup comes first
+    const int32_t row = target ? slot : slot - P.n_t;
+    if constexpr (kVec) {
+      u32x4 buf[kVecPerLane];
+      if (target) load_chunk<E>(rp, c0, n, lane, buf);
+      const float k2 = k2_of(temperature_of(P.temp_each, request_of_row(P.cu, P.B, row, target)));
+      if (!target) {
+        if (!(k2 > 0.0f)) return;  // draft row of a greedy or rejected request: never read
+        load_chunk<E>(rp, c0, n, lane, buf);
+      }
+      rec = k2 > 0.0f ? record_of<E, false>(buf, c0, k2, lane) : record_of<E, true>(buf, c0, 0.0f, lane);
+    } else {
+      const float k2 = k2_of(temperature_of(P.temp_each, request_of_row(P.cu, P.B, row, target)));
+      if (!target && !(k2 > 0.0f)) return;
+      rec = k2 > 0.0f ? chunk_record<E, false, false>(rp, c0, n, k2, lane)
+                      : chunk_record<E, true, false>(rp, c0, n, 0.0f, lane);
+    }
+  }
   if (lane == 0) P.part[u] = rec;
 }
 
@@ -565,7 +639,7 @@ struct Decision {
 };
 
 template <class E, bool kVec>
-__device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, int32_t i, int32_t trow0,
+__device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves);
 
@@ -573,14 +647,12 @@ constexpr int kVerdictWaves = 8;
 static_assert(2 * kVerdictWaves >= kVecPerLane, "the in-chunk search gives each wave two rows of 64 vectors");
 constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
-// One workgroup of 8 waves per request.  Shared memory: the folded rows, the decision, and the
-// residual chunk masses (C doubles, dynamic).
+// The verdict of request i under one rule (k2 = log2(e)/T and the Philox key seed), by one
+// workgroup of 8 waves.  Shared memory: the folded rows, the decision, and the residual chunk masses
+// (C doubles, dynamic).  bad_profile rejects the request once its offsets have been screened.
 template <class E, bool kGreedy, bool kVec>
-__global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
-  extern __shared__ double lds_mass[];  // [C]
-  __shared__ RowFold rows[kMaxRows];
-  __shared__ Decision dec;
-  const int32_t i = blockIdx.x;
+__device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k2, uint64_t seed, bool bad_profile,
+                                             double* lds_mass, RowFold* rows, Decision& dec) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n_waves = blockDim.x / kWave;
 
@@ -591,6 +663,10 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   const int32_t trow0 = lo + i, drow0 = lo;
   if (!ok_offsets || K > SDV_MAX_DEPTH) {  // malformed batch, or the depth limit: no slot written
     if (wave == 0) write_reject(P, i, 0, 0, false, lane);
+    return;
+  }
+  if (bad_profile) {  // a temperature that describes no profile: every slot of the request is -1
+    if (wave == 0) write_reject(P, i, trow0, K, true, lane);
     return;
   }
   const float2* rec_t = P.part + (int64_t)trow0 * P.C;
@@ -660,8 +736,8 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
         fd = rows[K + 1 + lane];
         qzero = zd == -INFINITY;
         // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
-        ratio = exp2(((double)zt - (double)zd) * (double)P.k2 - (ft.l2 - fd.l2));
-        blk = verifier_block(P.seed, (uint32_t)i, (uint32_t)lane);
+        ratio = exp2(((double)zt - (double)zd) * (double)k2 - (ft.l2 - fd.l2));
+        blk = verifier_block(seed, (uint32_t)i, (uint32_t)lane);
         r = accept_uniform(blk);
       }
       if (__ballot(qzero) != 0) {  // q(x) = 0 somewhere: rejected before any uniform is used
@@ -684,7 +760,7 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
         if (a == K) {
           d.kind = SDV_TERM_BONUS;
           d.ref_t = rows[K].ref;
-          d.u = draw_uniform(verifier_block(P.seed, (uint32_t)i, (uint32_t)K));
+          d.u = draw_uniform(verifier_block(seed, (uint32_t)i, (uint32_t)K));
         } else {
           // weights in the frame 2^(z_t k - ref_t) of the rejected target row; draft side
           // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and the factor 2^-(e - e_hi)
@@ -700,12 +776,30 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
     if (lane == 0) dec = d;
   }
   __syncthreads();
-  if constexpr (!kGreedy) draw_terminal<E, kVec>(P, dec, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
+  if constexpr (!kGreedy) draw_terminal<E, kVec>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
+}
+
+// One workgroup per request.  With a profile per request, the request's temperature selects the
+// rule at run time (uniformly over the workgroup).
+template <class E, int kMode, bool kVec>
+__global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
+  extern __shared__ double lds_mass[];  // [C]
+  __shared__ RowFold rows[kMaxRows];
+  __shared__ Decision dec;
+  const int32_t i = blockIdx.x;
+  if constexpr (kMode == kModeProfiled) {
+    const float k2 = k2_of(temperature_of(P.temp_each, i));
+    const uint64_t seed = P.seed_each[i];
+    if (k2 > 0.0f) verdict_body<E, false, kVec>(P, i, k2, seed, false, lds_mass, rows, dec);
+    else verdict_body<E, true, kVec>(P, i, 0.0f, seed, !(k2 == 0.0f), lds_mass, rows, dec);
+  } else {
+    verdict_body<E, kMode == kModeGreedy, kVec>(P, i, P.k2, P.seed, false, lds_mass, rows, dec);
+  }
 }
 
 // The correction or bonus draw of a request (T > 0), by the verdict workgroup.
 template <class E, bool kVec>
-__device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, int32_t i, int32_t trow0,
+__device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves) {
   if (d.kind != SDV_TERM_BONUS && d.kind != SDV_TERM_RESIDUAL) return;  // uniform over the workgroup
@@ -717,11 +811,11 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   // residual masses of every chunk, into shared memory
   if (residual) {
     if constexpr (kVec) {
-      resid_masses_pipelined<E>(tp, dp, P.V, P.C, P.k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
+      resid_masses_pipelined<E>(tp, dp, P.V, P.C, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
     } else {
       for (int32_t c = wave; c < P.C; c += n_waves) {
         const int32_t c0 = c * E::kChunk;
-        const double cm = resid_chunk_mass<E, false>(tp, dp, c0, min(E::kChunk, P.V - c0), P.k2, d.ref_t, d.e_hi,
+        const double cm = resid_chunk_mass<E, false>(tp, dp, c0, min(E::kChunk, P.V - c0), k2, d.ref_t, d.e_hi,
                                                      d.q_scale, lane);
         if (lane == 0) lds_mass[c] = cm;
       }
@@ -753,14 +847,14 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const int32_t n = min(E::kChunk, P.V - s0);
   int32_t y = -1;
   if constexpr (kVec) {
-    y = residual ? search_chunk_block<E, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C,
+    y = residual ? search_chunk_block<E, true>(tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C,
                                                lane, wave, n_waves)
-                 : search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
+                 : search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
                                                 lane, wave, n_waves);
   } else {
     if (wave != 0) return;
-    y = residual ? search_chunk<E, false, true>(tp, dp, s0, n, tgt, P.k2, d.ref_t, d.e_hi, d.q_scale, lane)
-                 : search_chunk<E, false, false>(tp, nullptr, s0, n, tgt, P.k2, d.ref_t, 0.0f, 0.0f, lane);
+    y = residual ? search_chunk<E, false, true>(tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lane)
+                 : search_chunk<E, false, false>(tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lane);
   }
   if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
     P.out_tokens[trow] = y;
@@ -842,14 +936,14 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   return SDV_OK;
 }
 
-template <class E, bool kGreedy, bool kVec>
+template <class E, int kMode, bool kVec>
 int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   auto record = [&](int k) {
     if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
   };
-  P.n_units = (int64_t)(kGreedy ? P.n_t : P.n_t + P.n_d) * P.C;
+  P.n_units = (int64_t)(kMode == kModeGreedy ? P.n_t : P.n_t + P.n_d) * P.C;
   record(0);
-  hipLaunchKernelGGL((row_records<E, kGreedy, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
+  hipLaunchKernelGGL((row_records<E, kMode, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(1);
   // shared memory: C residual masses, then as many chunk records as the deepest request can need,
@@ -858,16 +952,78 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
   P.lds_records = want < room ? want : room;
   const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
-  hipLaunchKernelGGL((verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves), lds, stream, P);
+  hipLaunchKernelGGL((verdicts<E, kMode, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves), lds, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(2);
   return SDV_OK;
 }
 
+template <class E, int kMode>
+int launch_vec(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
+  return vec ? launch<E, kMode, true>(P, stream, diag) : launch<E, kMode, false>(P, stream, diag);
+}
+
 template <class E>
 int launch_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
-  if (P.k2 == 0.0f) return vec ? launch<E, true, true>(P, stream, diag) : launch<E, true, false>(P, stream, diag);
-  return vec ? launch<E, false, true>(P, stream, diag) : launch<E, false, false>(P, stream, diag);
+  if (P.temp_each) return launch_vec<E, kModeProfiled>(P, vec, stream, diag);
+  if (P.k2 == 0.0f) return launch_vec<E, kModeGreedy>(P, vec, stream, diag);
+  return launch_vec<E, kModeSampling>(P, vec, stream, diag);
+}
+
+// Validation and launch shared by the entry points.  temp_each / seed_each are null for one profile
+// per batch (temperature, seed), else device arrays of B values.
+int verify_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                double temperature, uint64_t seed, const float* temp_each, const uint64_t* seed_each,
+                int32_t* accepted_len, int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                const sdv_diag* diag) {
+  Layout L;
+  const int shape = make_layout(B, n_draft_rows, V, dtype, &L);
+  if (shape != SDV_OK) return shape;
+  if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
+  if (n_draft_rows > 0 && !draft_tokens) return SDV_ERR_INVALID_ARG;
+  float k2 = 0.0f;  // 0 selects the greedy rule
+  const bool profiled = temp_each != nullptr || seed_each != nullptr;
+  if (profiled) {
+    if (!temp_each || !seed_each || (n_draft_rows > 0 && !draft_logits)) return SDV_ERR_INVALID_ARG;
+  } else {
+    if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;
+    if (temperature > 0.0) {
+      k2 = (float)(1.4426950408889634074 / temperature);  // log2(e) / T
+      if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
+      if (n_draft_rows > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
+    }
+  }
+  if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % kAlign != 0) return SDV_ERR_WORKSPACE;
+  const int esize = dtype == SDV_BF16 ? 2 : 4;
+  const void* draft = (profiled || k2 > 0.0f) ? draft_logits : nullptr;
+  const bool vec = ((uintptr_t)target_logits % 16 == 0) && (draft == nullptr || (uintptr_t)draft % 16 == 0) &&
+                   ((int64_t)V * esize) % 16 == 0;
+  char* ws = static_cast<char*>(workspace);
+  Params P{};
+  P.target = target_logits;
+  P.draft = draft;
+  P.tokens = draft_tokens;
+  P.cu = ragged_offsets;
+  P.accepted_len = accepted_len;
+  P.out_tokens = out_tokens;
+  P.part = reinterpret_cast<float2*>(ws + L.part);
+  P.B = B;
+  P.n_d = (int32_t)n_draft_rows;
+  P.n_t = (int32_t)L.n_t;
+  P.V = V;
+  P.C = L.C;
+  P.k2 = k2;
+  P.seed = seed;
+  P.temp_each = temp_each;
+  P.seed_each = seed_each;
+  if (diag) {
+    P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
+                    diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == SDV_BF16) return launch_any<Bf16>(P, vec, s, diag);
+  return launch_any<F32>(P, vec, s, diag);
 }
 
 }  // namespace sdv
@@ -883,46 +1039,18 @@ int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int
                   const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
                   double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
                   size_t workspace_bytes, void* stream, const sdv_diag* diag) {
-  sdv::Layout L;
-  const int shape = sdv::make_layout(B, n_draft_rows, V, dtype, &L);
-  if (shape != SDV_OK) return shape;
-  if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
-  if (n_draft_rows > 0 && !draft_tokens) return SDV_ERR_INVALID_ARG;
-  if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;
-  float k2 = 0.0f;  // 0 selects the greedy rule
-  if (temperature > 0.0) {
-    k2 = (float)(1.4426950408889634074 / temperature);  // log2(e) / T
-    if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
-    if (n_draft_rows > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
-  }
-  if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % sdv::kAlign != 0) return SDV_ERR_WORKSPACE;
-  const int esize = dtype == SDV_BF16 ? 2 : 4;
-  const void* draft = k2 > 0.0f ? draft_logits : nullptr;
-  const bool vec = ((uintptr_t)target_logits % 16 == 0) && (draft == nullptr || (uintptr_t)draft % 16 == 0) &&
-                   ((int64_t)V * esize) % 16 == 0;
-  char* ws = static_cast<char*>(workspace);
-  sdv::Params P{};
-  P.target = target_logits;
-  P.draft = draft;
-  P.tokens = draft_tokens;
-  P.cu = ragged_offsets;
-  P.accepted_len = accepted_len;
-  P.out_tokens = out_tokens;
-  P.part = reinterpret_cast<float2*>(ws + L.part);
-  P.B = B;
-  P.n_d = (int32_t)n_draft_rows;
-  P.n_t = (int32_t)L.n_t;
-  P.V = V;
-  P.C = L.C;
-  P.k2 = k2;
-  P.seed = seed;
-  if (diag) {
-    P.dg = sdv::DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
-                         diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};
-  }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == SDV_BF16) return sdv::launch_any<sdv::Bf16>(P, vec, s, diag);
-  return sdv::launch_any<sdv::F32>(P, vec, s, diag);
+  return sdv::verify_impl(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V, dtype,
+                          temperature, seed, nullptr, nullptr, accepted_len, out_tokens, workspace, workspace_bytes,
+                          stream, diag);
+}
+
+int sdv_verify_profiled(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                        const float* temperature, const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens,
+                        void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+  if (!temperature || !seed) return SDV_ERR_INVALID_ARG;
+  return sdv::verify_impl(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V, dtype, 0.0,
+                          0, temperature, seed, accepted_len, out_tokens, workspace, workspace_bytes, stream, diag);
 }
 
 int sdv_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,

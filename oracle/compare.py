@@ -10,8 +10,9 @@ from __future__ import annotations
 import numpy as np
 
 
-def compare_verdicts(acc_gpu, out_gpu, ref: dict, cu, temperature: float, eps: float = 1e-6) -> dict:
-    """ref: oracle.verify(..., diag=True).  Returns counts and the list of hard mismatches."""
+def compare_verdicts(acc_gpu, out_gpu, ref: dict, cu, temperature, eps: float = 1e-6) -> dict:
+    """ref: oracle.verify(..., diag=True); temperature: the batch's, or one per request.  Returns
+    counts and the list of hard mismatches."""
     acc_gpu = np.asarray(acc_gpu)
     out_gpu = np.asarray(out_gpu)
     cu = np.asarray(cu)
@@ -27,7 +28,8 @@ def compare_verdicts(acc_gpu, out_gpu, ref: dict, cu, temperature: float, eps: f
         s = slice(int(cu[i]) + i, int(cu[i]) + i + K + 1)
         if acc_gpu[i] == acc_ref[i] and np.array_equal(out_gpu[s], out_ref[s]):
             continue
-        if temperature == 0 or acc_ref[i] == -1 or acc_gpu[i] == -1:
+        t_i = temperature[i] if np.ndim(temperature) else temperature
+        if t_i == 0 or acc_ref[i] == -1 or acc_gpu[i] == -1:
             hard.append((i, f"accepted {acc_gpu[i]} vs {acc_ref[i]}"))
             continue
         a_g, a_r = int(acc_gpu[i]), int(acc_ref[i])

@@ -32,14 +32,26 @@ def upload(b):
             torch.from_numpy(b.tokens).to(DEV), torch.from_numpy(b.cu).to(DEV))
 
 
+def profile_args(b, seed=None):
+    """(temperature, seed) for the GPU call: scalars, or [B] device tensors for a profiled batch."""
+    if b.temp_each is None:
+        return b.temperature, (b.seed if seed is None else seed)
+    return (torch.from_numpy(np.ascontiguousarray(b.temp_each, dtype=np.float32)).to(DEV),
+            torch.from_numpy(np.ascontiguousarray(b.seed_each, dtype=np.uint64).view(np.int64)).to(DEV))
+
+
 def run_gpu(b, diag=(), seed=None, dev_inputs=None):
     t, d, x, cu = upload(b) if dev_inputs is None else dev_inputs
-    acc, out, dg = sdv.verify_ex(t, d, x, cu, b.temperature, b.seed if seed is None else seed, diag=diag)
+    temperature, sd = profile_args(b, seed)
+    acc, out, dg = sdv.verify_ex(t, d, x, cu, temperature, sd, diag=diag)
     torch.cuda.synchronize()
     return acc.cpu().numpy(), out.cpu().numpy(), {k: v.cpu().numpy() for k, v in dg.items()}
 
 
 def run_oracle(b, seed=None):
+    if b.temp_each is not None:
+        return oracle.verify(b.target, b.draft, b.tokens, b.cu, b.temp_each.astype(np.float64), b.seed_each,
+                             diag=True)
     return oracle.verify(b.target, b.draft, b.tokens, b.cu, b.temperature, b.seed if seed is None else seed,
                          diag=True)
 
@@ -49,6 +61,7 @@ def check_parity(b, seed=None, eps=1e-6, dev_inputs=None, diag=("terminal_kind",
     log(f"  parity {b.name}: B={b.B} n_draft_rows={b.n_draft_rows} V={b.V} {b.dtype} T={b.temperature}")
     acc, out, dg = run_gpu(b, diag=diag, seed=seed, dev_inputs=dev_inputs)
     ref = run_oracle(b, seed=seed)
-    cmp = compare_verdicts(acc, out, ref, b.cu, b.temperature, eps=eps)
+    temperature = b.temp_each.astype(np.float64) if b.temp_each is not None else b.temperature
+    cmp = compare_verdicts(acc, out, ref, b.cu, temperature, eps=eps)
     assert cmp["n_hard"] == 0, f"{b.name}: hard mismatches {cmp['hard'][:10]}"
     return acc, out, ref, cmp, dg

@@ -29,7 +29,7 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
-                          "sdv_read_ceiling", "sdv_status_string", "sdv_abi_version"}
+                          "sdv_read_ceiling", "sdv_verify_profiled", "sdv_status_string", "sdv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
@@ -91,6 +91,24 @@ def test_host_argument_errors(lib):
     assert lib.sdv_read_ceiling(FAKE, 0, FAKE, None) == -1
     assert lib.sdv_read_ceiling(FAKE + 8, 4, FAKE, None) == -1  # not 16-byte aligned
     assert lib.sdv_read_ceiling(FAKE, 4, None, None) == -1
+
+
+def test_profiled_host_argument_checks(lib):
+    f = lib.sdv_verify_profiled
+    need = lib.sdv_workspace_bytes(2, 8, 1000, 0)
+    ok = dict(t=FAKE, d=FAKE, x=FAKE, cu=FAKE, B=2, n_d=8, V=1000, dt=0, temp=FAKE, seed=FAKE, a=FAKE, o=FAKE,
+              ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["t"], a["d"], a["x"], a["cu"], a["B"], a["n_d"], a["V"], a["dt"], a["temp"], a["seed"], a["a"],
+                 a["o"], a["ws"], a["wsb"], None, None)
+    assert call(temp=None) == -1
+    assert call(seed=None) == -1
+    assert call(d=None) == -1  # draft rows exist: the draft logits are needed whatever the profiles
+    assert call(dt=5) == -2
+    assert call(wsb=need - 1) == -4
+    assert call(B=0) == -1
 
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):

@@ -45,6 +45,8 @@ class Batch:
     tokens: np.ndarray            # (n_draft_rows,) int32
     cu: np.ndarray                # (B + 1,) int32
     meta: dict = field(default_factory=dict)
+    temp_each: np.ndarray | None = None  # (B,) float32: one temperature per request, else None
+    seed_each: np.ndarray | None = None  # (B,) uint64: one seed per request (with temp_each)
 
     @property
     def B(self) -> int:
@@ -63,9 +65,13 @@ class Batch:
         return 2 if self.dtype == "bf16" else 4
 
     def algorithmic_bytes(self) -> int:
-        """Every logit the method needs, read once: target rows, plus draft rows when T > 0."""
-        rows = self.target.shape[0] + (self.n_draft_rows if self.temperature > 0 else 0)
-        return rows * self.V * self.elem_bytes
+        """Every logit the method needs, read once: target rows, plus the draft rows of every request
+        that samples (T > 0)."""
+        if self.temp_each is not None:
+            draft_rows = int(np.sum(self.depths[self.temp_each > 0]))
+        else:
+            draft_rows = self.n_draft_rows if self.temperature > 0 else 0
+        return (self.target.shape[0] + draft_rows) * self.V * self.elem_bytes
 
     def target_f32(self) -> np.ndarray:
         return bf16_to_f32(self.target) if self.dtype == "bf16" else self.target
@@ -137,6 +143,34 @@ def make_random(name: str, depths, V: int, dtype: str, temperature: float, targe
                  target=target, draft=draft if keep_draft else None, tokens=tokens, cu=cu,
                  meta={"data_seed": data_seed, "target_sigma": target_sigma,
                        "draft_sigma": np.asarray(draft_sigma).tolist()})
+
+
+def with_profiles(b: Batch, temps, seeds, token_seed: int) -> Batch:
+    """The same logits under one sampling profile per request: each request's draft tokens are
+    redrawn from its own draft rows at its own temperature (the argmax where T_i = 0)."""
+    if b.draft is None:
+        raise ValueError("profiles need the draft logits")
+    temps = np.asarray(temps, dtype=np.float32).reshape(b.B)
+    seeds = np.asarray(seeds, dtype=np.uint64).reshape(b.B)
+    rng = np.random.Generator(np.random.Philox(token_seed))
+    req_of_d = np.repeat(np.arange(b.B), b.depths)
+    tokens = _argmax_tokens(b.draft, b.dtype)
+    sampled = np.nonzero(temps[req_of_d] > 0)[0]
+    for r0 in range(0, sampled.size, 64):
+        rows = sampled[r0:r0 + 64]
+        z = (bf16_to_f32(b.draft[rows]) if b.dtype == "bf16" else b.draft[rows]).astype(np.float64)
+        g = -np.log(-np.log(rng.random(z.shape)))
+        tokens[rows] = np.argmax(z / temps[req_of_d[rows]].astype(np.float64)[:, None] + g, axis=1)
+    return Batch(name=b.name + "_profiled", V=b.V, dtype=b.dtype, temperature=float("nan"), seed=0,
+                 target=b.target, draft=b.draft, tokens=tokens.astype(np.int32), cu=b.cu,
+                 meta=dict(b.meta, token_seed=token_seed), temp_each=temps, seed_each=seeds)
+
+
+def mixed_profiles(B: int, rng: np.random.Generator, temps=(0.0, 0.6, 1.0, 1.5)) -> tuple[np.ndarray, np.ndarray]:
+    """Temperatures drawn from ``temps`` and distinct 64-bit seeds, one per request."""
+    t = np.asarray(temps, dtype=np.float32)[rng.integers(0, len(temps), size=B)]
+    seeds = rng.integers(0, 2**63, size=B, dtype=np.int64).astype(np.uint64) * np.uint64(2) + np.uint64(1)
+    return t, seeds
 
 
 # ----------------------------------------------------------------------------- the five workloads
