@@ -13,7 +13,8 @@ one launch / its mean duration from HIP events recorded on the library's stream)
 a plain read of the same size with the row pass's loads, per-call percentiles, accepted-length
 statistics and the CPU oracle's rate on the host.
 
-  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1] [--steps K] [--warmup W]
+  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1|ragged_b256_profiled]
+                  [--steps K] [--warmup W]
 
 Profile summaries (rocprofv3 output -> text under profiles/):
 
@@ -64,6 +65,10 @@ def make_workload(name: str, set_index: int):
         return W.uniform_b64(data_seed=W.DATA_SEED_BASE + 3 + 1000 * set_index, verify_seed=3000)
     if name == "small_b1":
         return W.small_b1(set_index)
+    if name == "ragged_b256_profiled":  # one sampling profile per request: a quarter greedy
+        base = W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000)
+        t, s = W.mixed_profiles(base.B, np.random.default_rng(W.DATA_SEED_BASE + 6 + set_index))
+        return W.with_profiles(base, t, s, token_seed=W.DATA_SEED_BASE + 7 + set_index)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -83,6 +88,13 @@ def traffic_from_profile(workload: str):
     return rec.get("row_records", {}).get("traffic_bytes_per_launch")
 
 
+def oracle_profile(b):
+    """(temperature, seed) as the oracle takes them: scalars, or one value per request."""
+    if b.temp_each is not None:
+        return b.temp_each.astype(np.float64), b.seed_each
+    return b.temperature, b.seed
+
+
 def cpu_baseline(batch, budget_s: float):
     """The oracle on all host threads (median of up to 3 calls), then once on a single thread."""
     from oracle import oracle
@@ -92,7 +104,7 @@ def cpu_baseline(batch, budget_s: float):
         t_end = time.perf_counter() + budget
         while True:
             t0 = time.perf_counter()
-            oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, batch.temperature, batch.seed)
+            oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, *oracle_profile(batch))
             times.append(time.perf_counter() - t0)
             if len(times) >= 3 or time.perf_counter() > t_end:
                 return float(np.median(times)), len(times)
@@ -113,13 +125,12 @@ def reread_bytes(batch, acc: np.ndarray) -> int:
     """Bytes the verdict kernel reads again beyond the algorithmic bytes: a correction re-reads its
     target and draft rows for the residual chunk masses and then one chunk of each for the search;
     a bonus re-reads one chunk of its target row; greedy terminals read nothing again."""
-    if batch.temperature == 0:
-        return 0
+    sampling = batch.temp_each > 0 if batch.temp_each is not None else np.full(batch.B, batch.temperature > 0)
     K = batch.depths
     row = batch.V * batch.elem_bytes
     chunk = min(CHUNK_BYTES, row)
-    resid = int(np.sum((acc >= 0) & (acc < K)))
-    bonus = int(np.sum(acc == K))
+    resid = int(np.sum(sampling & (acc >= 0) & (acc < K)))
+    bonus = int(np.sum(sampling & (acc == K)))
     return resid * (2 * row + 2 * chunk) + bonus * chunk
 
 
@@ -143,7 +154,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1"])
+    ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1",
+                                                           "ragged_b256_profiled"])
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through the timed steps (0: enough for 1 GB, at least 2, at most 32)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing (0 = skip)")
@@ -190,6 +202,9 @@ def main():
     for b in batches:
         sets.append(dict(target=up(b.target), draft=up(b.draft), tokens=torch.from_numpy(b.tokens).to(dev),
                          cu=torch.from_numpy(b.cu).to(dev), batch=b))
+        if b.temp_each is not None:  # one sampling profile per request, as device arrays
+            sets[-1]["temp"] = torch.from_numpy(b.temp_each.astype(np.float32)).to(dev)
+            sets[-1]["seeds"] = torch.from_numpy(b.seed_each.astype(np.uint64).view(np.int64)).to(dev)
     B0 = batches[0]
     positions = [int(b.cu[-1]) for b in batches]
     rows = [int(b.cu[-1]) + b.B for b in batches]
@@ -202,7 +217,8 @@ def main():
     def step(k, events=None):
         s = sets[k % len(sets)]
         b = s["batch"]
-        sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], b.temperature, b.seed + k,
+        temperature, seed = (s["temp"], s["seeds"]) if "temp" in s else (b.temperature, b.seed + k)
+        sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], temperature, seed,
                       out=outs[k % len(sets)], workspace=ws, events=events)
 
     # correctness of the timed configuration, once, against the oracle
@@ -212,8 +228,8 @@ def main():
         log("[bench] checking one call against the oracle")
         step(0)
         torch.cuda.synchronize()
-        ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, B0.temperature, B0.seed, diag=True)
-        cmp = compare_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ref, B0.cu, B0.temperature)
+        ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, *oracle_profile(B0), diag=True)
+        cmp = compare_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ref, B0.cu, oracle_profile(B0)[0])
         parity = {"requests": cmp["requests"], "hard_mismatches": cmp["n_hard"], "near_tie_excused": cmp["n_excused"]}
         if cmp["n_hard"]:
             raise SystemExit(f"GPU verdicts differ from the oracle: {cmp['hard'][:5]}")
@@ -302,7 +318,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if B0.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": B0.name, "B": B0.B, "V": B0.V, "temperature": B0.temperature,
+        "config": {"workload": B0.name, "B": B0.B, "V": B0.V,
+                   "temperature": B0.temperature if B0.temp_each is None else
+                   {f"{t:g}": int(n) for t, n in zip(*np.unique(B0.temp_each, return_counts=True))},
                    "sum_K_per_call": positions, "input_sets": len(sets),
                    "algorithmic_bytes_per_call": alg_bytes},
         "hbm_gbps": call_gbps,
