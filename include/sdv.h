@@ -57,6 +57,8 @@ typedef enum {
   SDV_TERM_BONUS = 1,          /* every draft accepted (or K_i = 0): drawn from p at position K_i */
   SDV_TERM_RESIDUAL = 2,       /* first rejection at t < K_i: drawn from max(p_t - q_t, 0) */
   SDV_TERM_RESIDUAL_EMPTY = 3, /* the residual had no positive weight in floating point: drawn from p_t */
+  SDV_TERM_NONE = 4,           /* a stop token or the budget ended emission inside the accepted drafts:
+                                  no extra token is emitted or drawn (sdv_verify_opts) */
   SDV_TERM_BAD = -1            /* the request was rejected (see sdv_verify) */
 } sdv_terminal_kind;
 
@@ -155,6 +157,74 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
                         const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
                         const float* temperature, const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens,
                         void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
+
+/*
+ * Per-request options of sdv_verify_opts.  Every member may be NULL (n_stop_tokens 0), which keeps
+ * the behaviour of sdv_verify_ex; all arrays are DEVICE arrays owned by the caller.
+ *
+ *  temperature, seed  [B] float / uint64: one sampling profile per request, as in
+ *                     sdv_verify_profiled (both or neither; they replace the scalar T and seed).
+ *  accept_uniform     [n_draft_rows] double: the caller's r in [0, 1) for each draft position.
+ *  draw_uniform       [n_draft_rows + B] double: the caller's u in [0, 1) for each position, in the
+ *                     target-row layout (position j of request i at cu[i] + i + j).
+ *                     Both or neither.  With them the uniforms come from the caller instead of
+ *                     Philox (for instance SDCP's HMAC-SHA-256 values, sdv_sdcp_uniforms), and the
+ *                     accept test is SDCP Rule 2's strict one, r < p/q ("Speculative Decoding
+ *                     Coordination Protocol (SDCP)", section "Acceptance Rules").  Values outside
+ *                     [0, 1) give unspecified (memory-safe) verdicts.
+ *  stop_offsets       [B + 1] int32, stop_tokens [n_stop_tokens] int32: request i stops at any token
+ *                     of stop_tokens[stop_offsets[i] .. stop_offsets[i + 1]).  A list outside
+ *                     [0, n_stop_tokens] rejects that request (accepted_len -1, every slot -1).
+ *  budget             [B] int32: the remaining output budget of each request (<= 0 emits nothing).
+ *  emitted_len        [B] int32 out: the number of tokens request i emits.
+ *
+ * Emission (SDCP section "Verification and Commit", step 7; "M7.8 - Speculative Serving", section
+ * 0x09, "EOS and length-limit stopping"): of the a_i + 1 candidate tokens (the accepted drafts,
+ * then the extra token), no token after the first stop token and no more than budget[i] are
+ * emitted; out_tokens holds the emitted tokens first and -1 in every other slot of the request.
+ * accepted_len still reports a_i.  When emission ends inside the accepted drafts the extra token is
+ * neither emitted nor drawn (terminal kind SDV_TERM_NONE).  A rejected request emits 0 tokens.
+ */
+typedef struct sdv_options {
+  const float* temperature;
+  const uint64_t* seed;
+  const double* accept_uniform;
+  const double* draw_uniform;
+  const int32_t* stop_offsets;
+  const int32_t* stop_tokens;
+  int64_t n_stop_tokens;
+  const int32_t* budget;
+  int32_t* emitted_len;
+} sdv_options;
+
+/*
+ * sdv_verify_ex refined by per-request options (options may be NULL).  With options->temperature
+ * the scalar temperature and seed are ignored and draft_logits must be non-NULL when
+ * n_draft_rows > 0.  Errors as in sdv_verify_ex, plus SDV_ERR_INVALID_ARG for a uniform array
+ * without its partner, a temperature array without seeds (or the reverse), or stop_offsets with
+ * n_stop_tokens < 0 or (n_stop_tokens > 0 and stop_tokens NULL).
+ */
+int sdv_verify_opts(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                    const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                    double temperature, uint64_t seed, const sdv_options* options, int32_t* accepted_len,
+                    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                    const sdv_diag* diag);
+
+/*
+ * SDCP's verifier uniforms, computed on the HOST for sdv_options ("Speculative Decoding
+ * Coordination Protocol (SDCP)", section "Acceptance Rules", Rule 2).  For request i, with profile
+ * seed seeds[i], session id sessions[16 i .. 16 i + 15] and round rounds[i], each value is the first
+ * 53 bits of HMAC-SHA-256 keyed with the seed as eight octets in network byte order over
+ *   "SDCP-VERIFY-1" || 0x00 || session || uint32(round) || uint32(position) || uint8(purpose)
+ * (integers in network byte order; positions counted from 1 as SDCP numbers p[1..M+1]), divided by
+ * 2^53.  Purpose 0 feeds the acceptance test, purpose 1 the draw of the extra token.  Writes
+ *   accept_uniform[cu[i] + j]      purpose 0 at position j + 1, j < K_i   (HOST, cu[B] doubles)
+ *   draw_uniform[cu[i] + i + t]    purpose 1 at position t + 1, t <= K_i  (HOST, cu[B] + B doubles)
+ * cu is a HOST copy of the ragged offsets.  Invalid offsets (cu[0] != 0, decreasing, a depth above
+ * 64) or NULL pointers -> SDV_ERR_INVALID_ARG and nothing written.
+ */
+int sdv_sdcp_uniforms(int32_t B, const int32_t* cu, const uint64_t* seeds, const uint8_t* sessions,
+                      const uint32_t* rounds, double* accept_uniform, double* draw_uniform);
 
 /*
  * Raw Philox4x32-10 blocks on the device, for testing the verifier's uniforms: out[b] =

@@ -14,7 +14,7 @@ from . import _native
 from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_RESIDUAL,
                       TERM_RESIDUAL_EMPTY, SdvError)
 
-__all__ = ["verify", "verify_ex", "workspace_bytes", "philox4x32_10", "read_ceiling", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+__all__ = ["verify", "verify_ex", "workspace_bytes", "philox4x32_10", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
            "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
 
 _DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
@@ -85,19 +85,43 @@ def _check(target, draft, draft_tokens, offsets, temperature):
         raise ValueError("sampling (any temperature > 0, or per-request profiles) needs draft logits")
 
 
+def _device_vector(t, dtype, n, dev, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != dev or t.dim() != 1 \
+            or t.shape[0] != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} vector of {n} values on the logits' device")
+    return t
+
+
 def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, offsets: torch.Tensor,
               temperature, seed, *, out: tuple | None = None, workspace: torch.Tensor | None = None,
-              diag: tuple[str, ...] = (), events: list | None = None):
-    """Run sdv_verify_ex, or sdv_verify_profiled when temperature and seed are [B] device tensors
-    (one sampling profile per request).  Returns (accepted_len, out_tokens, diag_dict).
-
-    ``diag`` names the diagnostic arrays to fill (fields of sdv_diag); ``events`` up to four
-    torch.cuda.Event objects recorded before the first kernel and after each kernel.
+              diag: tuple[str, ...] = (), events: list | None = None, accept_uniform: torch.Tensor | None = None,
+              draw_uniform: torch.Tensor | None = None, stop_offsets: torch.Tensor | None = None,
+              stop_tokens: torch.Tensor | None = None, budget: torch.Tensor | None = None):
+    """Run sdv_verify_ex; sdv_verify_profiled when temperature and seed are [B] device tensors (one
+    sampling profile per request); sdv_verify_opts when the caller's uniforms (float64
+    accept_uniform [n_draft_rows], draw_uniform [n_draft_rows + B]), stop lists (int32 CSR
+    stop_offsets [B + 1], stop_tokens) or a budget (int32 [B]) are given.  Returns
+    (accepted_len, out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag)
+    and, with stop lists or a budget, "emitted_len".  ``events``: up to four torch.cuda.Event
+    objects recorded before the first kernel and after each kernel.
     """
     _check(target, draft, draft_tokens, offsets, temperature)
     dev = target.device
     B = offsets.shape[0] - 1
     profile = _profile_arrays(temperature, seed, B, dev)
+    n_d0 = draft_tokens.shape[0]
+    accept_uniform = _device_vector(accept_uniform, torch.float64, n_d0, dev, "accept_uniform")
+    draw_uniform = _device_vector(draw_uniform, torch.float64, n_d0 + B, dev, "draw_uniform")
+    if (accept_uniform is None) != (draw_uniform is None):
+        raise ValueError("accept_uniform and draw_uniform go together")
+    stop_offsets = _device_vector(stop_offsets, torch.int32, B + 1, dev, "stop_offsets")
+    if stop_offsets is not None:
+        stop_tokens = stop_tokens if stop_tokens is not None else torch.empty(0, dtype=torch.int32, device=dev)
+        stop_tokens = _device_vector(stop_tokens, torch.int32, stop_tokens.shape[0], dev, "stop_tokens")
+    budget = _device_vector(budget, torch.int32, B, dev, "budget")
+    use_opts = accept_uniform is not None or stop_offsets is not None or budget is not None
     n_d = draft_tokens.shape[0]
     V = target.shape[1]
     dt = _DTYPES[target.dtype]
@@ -127,7 +151,25 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
     stream = torch.cuda.current_stream(dev).cuda_stream
     dg_ref = ctypes.byref(dg) if dg is not None else None
     with torch.cuda.device(dev):
-        if profile is None:
+        if use_opts:
+            opt = _native.SdvOptions()
+            if profile is not None:
+                opt.temperature, opt.seed = _ptr(profile[0]), _ptr(profile[1])
+            opt.accept_uniform, opt.draw_uniform = _ptr(accept_uniform), _ptr(draw_uniform)
+            if stop_offsets is not None:
+                opt.stop_offsets, opt.stop_tokens = _ptr(stop_offsets), _ptr(stop_tokens)
+                opt.n_stop_tokens = stop_tokens.shape[0]
+            if stop_offsets is not None or budget is not None:
+                opt.budget = _ptr(budget)
+                dvals["emitted_len"] = torch.full((B,), -9, dtype=torch.int32, device=dev)
+                opt.emitted_len = dvals["emitted_len"].data_ptr()
+            scalar_t = 0.0 if profile is not None else float(temperature)
+            scalar_s = 0 if profile is not None else int(seed) & 0xFFFFFFFFFFFFFFFF
+            rc = _native.lib().sdv_verify_opts(
+                _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(offsets), B, n_d, V, dt, scalar_t, scalar_s,
+                ctypes.byref(opt), _ptr(accepted_len), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
+                stream, dg_ref)
+        elif profile is None:
             rc = _native.lib().sdv_verify_ex(
                 _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(offsets), B, n_d, V, dt, float(temperature),
                 int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(out_tokens), _ptr(ws),
@@ -138,8 +180,28 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
                 _ptr(profile[1]), _ptr(accepted_len), _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(),
                 stream, dg_ref)
     if rc != 0:
-        raise SdvError(rc, "sdv_verify_profiled" if profile is not None else "sdv_verify_ex")
+        raise SdvError(rc, "sdv_verify_opts" if use_opts else
+                       ("sdv_verify_profiled" if profile is not None else "sdv_verify_ex"))
     return accepted_len, out_tokens, dvals
+
+
+def sdcp_uniforms(offsets, seeds, sessions, rounds):
+    """SDCP's HMAC-SHA-256 uniforms on the host (sdv_sdcp_uniforms): offsets (B + 1,) int32, seeds
+    (B,) uint64, sessions (B, 16) uint8, rounds (B,) uint32.  Returns numpy float64 arrays
+    (accept_uniform [n_draft_rows], draw_uniform [n_draft_rows + B]) for verify_ex."""
+    import numpy as np
+    cu = np.ascontiguousarray(offsets, dtype=np.int32)
+    B = cu.shape[0] - 1
+    seeds = np.ascontiguousarray(seeds, dtype=np.uint64).reshape(B)
+    sessions = np.ascontiguousarray(sessions, dtype=np.uint8).reshape(B, 16)
+    rounds = np.ascontiguousarray(rounds, dtype=np.uint32).reshape(B)
+    r = np.zeros(int(cu[-1]), dtype=np.float64)
+    u = np.zeros(int(cu[-1]) + B, dtype=np.float64)
+    rc = _native.lib().sdv_sdcp_uniforms(B, cu.ctypes.data, seeds.ctypes.data, sessions.ctypes.data,
+                                         rounds.ctypes.data, r.ctypes.data if r.size else None, u.ctypes.data)
+    if rc != 0:
+        raise SdvError(rc, "sdv_sdcp_uniforms")
+    return r, u
 
 
 def verify(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, offsets: torch.Tensor,

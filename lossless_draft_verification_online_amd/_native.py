@@ -33,6 +33,20 @@ class SdvError(RuntimeError):
         self.status = status
 
 
+class SdvOptions(ctypes.Structure):
+    _fields_ = [
+        ("temperature", ctypes.c_void_p),
+        ("seed", ctypes.c_void_p),
+        ("accept_uniform", ctypes.c_void_p),
+        ("draw_uniform", ctypes.c_void_p),
+        ("stop_offsets", ctypes.c_void_p),
+        ("stop_tokens", ctypes.c_void_p),
+        ("n_stop_tokens", ctypes.c_int64),
+        ("budget", ctypes.c_void_p),
+        ("emitted_len", ctypes.c_void_p),
+    ]
+
+
 _LIB = None
 
 _VERIFY_ARGS = [
@@ -61,6 +75,11 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_verify_profiled.restype = ctypes.c_int
     L.sdv_verify_profiled.argtypes = (list(_VERIFY_ARGS[:8]) + [ctypes.c_void_p, ctypes.c_void_p]
                                       + list(_VERIFY_ARGS[10:]) + [ctypes.POINTER(SdvDiag)])
+    L.sdv_verify_opts.restype = ctypes.c_int
+    L.sdv_verify_opts.argtypes = (list(_VERIFY_ARGS[:10]) + [ctypes.POINTER(SdvOptions)] + list(_VERIFY_ARGS[10:])
+                                  + [ctypes.POINTER(SdvDiag)])
+    L.sdv_sdcp_uniforms.restype = ctypes.c_int
+    L.sdv_sdcp_uniforms.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 6
     L.sdv_philox4x32_10.restype = ctypes.c_int
     L.sdv_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.restype = ctypes.c_char_p

@@ -59,6 +59,13 @@ struct Params {
   uint64_t seed;
   const float* temp_each;     // [B] temperature of each request, or null: one profile for the batch
   const uint64_t* seed_each;  // [B] seed of each request (with temp_each)
+  const double* r_each;       // [n_d] caller's accept uniforms in [0, 1), or null: Philox
+  const double* u_each;       // [n_t] caller's draw uniforms in [0, 1) per position (with r_each)
+  const int32_t* stop_off;    // [B + 1] stop-token lists (CSR into stop_tok), or null
+  const int32_t* stop_tok;    // [n_stop]
+  int64_t n_stop;
+  const int32_t* budget;      // [B] remaining output tokens, or null: no limit
+  int32_t* emitted_len;       // [B] out: tokens emitted after truncation, or null
   DiagPtrs dg;
 };
 
@@ -627,15 +634,42 @@ __device__ __forceinline__ void write_reject(const Params& P, int32_t i, int32_t
     for (int j = lane; j <= K; j += kWave) P.out_tokens[trow0 + j] = -1;
   if (lane == 0) {
     P.accepted_len[i] = -1;
+    if (P.emitted_len) P.emitted_len[i] = 0;
     if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_BAD;
   }
+}
+
+// Request i's stop list [s0, s1) lies inside the stop-token array (or there is none).
+__device__ __forceinline__ bool stop_list_valid(const Params& P, int32_t i) {
+  if (!P.stop_off) return true;
+  const int64_t s0 = P.stop_off[i], s1 = P.stop_off[i + 1];
+  return s0 >= 0 && s1 >= s0 && s1 <= P.n_stop;
+}
+
+// How many of the a + 1 candidate tokens (the accepted drafts x_0 .. x_{a-1} in lanes 0 .. a-1,
+// then the extra token) are emitted: none after the first stop token and no more than the
+// remaining budget (SDCP "Verification and Commit", step 7; M7.8 section 0x09).  The extra token
+// is emitted only when the count reaches a + 1, so the answer is known before it is drawn.
+// Wave-uniform result.
+__device__ __forceinline__ int emitted_count(const Params& P, int32_t i, int32_t x, int a, int lane) {
+  int n = a + 1;
+  if (P.stop_off) {
+    bool hit = false;
+    const int32_t s0 = P.stop_off[i], s1 = P.stop_off[i + 1];
+    for (int32_t s = s0; s < s1; ++s) hit |= lane < a && x == P.stop_tok[s];
+    const uint64_t m = __ballot(hit);
+    if (m) n = __ffsll((unsigned long long)m);  // the first stop among the drafts, inclusive
+  }
+  if (P.budget) n = min(n, max(P.budget[i], 0));
+  return n;
 }
 
 // Decision of wave 0, shared with the other waves of the workgroup.
 struct Decision {
   int32_t kind;  // sdv_terminal_kind, SDV_TERM_BAD when the request is rejected
   int32_t a;
-  float ref_t, e_hi, q_scale, u;
+  float ref_t, e_hi, q_scale;
+  double u;
 };
 
 template <class E, bool kVec>
@@ -665,7 +699,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     if (wave == 0) write_reject(P, i, 0, 0, false, lane);
     return;
   }
-  if (bad_profile) {  // a temperature that describes no profile: every slot of the request is -1
+  if (bad_profile || !stop_list_valid(P, i)) {  // no profile, or no stop set: every slot is -1
     if (wave == 0) write_reject(P, i, trow0, K, true, lane);
     return;
   }
@@ -709,7 +743,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
 
   // 2. the verdict, by wave 0
   if (wave == 0) {
-    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0f};
+    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0};
     if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
       write_reject(P, i, trow0, K, true, lane);
     } else if constexpr (kGreedy) {
@@ -717,19 +751,22 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
       const uint64_t miss = __ballot(active && x != g);
       const int a = miss ? __ffsll((unsigned long long)miss) - 1 : K;
       const int32_t g_a = rows[a].argmax;
-      for (int j = lane; j <= K; j += kWave) P.out_tokens[trow0 + j] = j < a ? x : (j == a ? g_a : -1);
+      const int n_emit = emitted_count(P, i, x, a, lane);
+      for (int j = lane; j <= K; j += kWave) P.out_tokens[trow0 + j] = j >= n_emit ? -1 : (j < a ? x : g_a);
       if (P.dg.target_argmax)
         for (int j = lane; j <= K; j += kWave) P.dg.target_argmax[trow0 + j] = rows[j].argmax;
       if (lane == 0) {
         P.accepted_len[i] = a;
-        if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_GREEDY;
+        if (P.emitted_len) P.emitted_len[i] = n_emit;
+        if (P.dg.terminal_kind) P.dg.terminal_kind[i] = n_emit == a + 1 ? SDV_TERM_GREEDY : SDV_TERM_NONE;
       }
       d.kind = SDV_TERM_GREEDY;
     } else {
       RowFold ft{0.0, 0.0f, 0}, fd{0.0, 0.0f, 0};
       double ratio = 0.0;
-      float r = 1.0f;
+      double r = 1.0;
       bool qzero = false;
+      bool accept = true;
       Philox4 blk{0u, 0u, 0u, 0u};
       if (active) {
         ft = rows[lane];
@@ -737,30 +774,44 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
         qzero = zd == -INFINITY;
         // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
         ratio = exp2(((double)zt - (double)zd) * (double)k2 - (ft.l2 - fd.l2));
-        blk = verifier_block(seed, (uint32_t)i, (uint32_t)lane);
-        r = accept_uniform(blk);
+        if (P.r_each) {  // the caller's r in [0, 1): SDCP Rule 2, r < p/q
+          r = P.r_each[drow0 + lane];
+          accept = r < ratio;
+        } else {  // Philox r in (0, 1]: r <= p/q
+          blk = verifier_block(seed, (uint32_t)i, (uint32_t)lane);
+          r = (double)accept_uniform(blk);
+          accept = r <= ratio;
+        }
       }
       if (__ballot(qzero) != 0) {  // q(x) = 0 somewhere: rejected before any uniform is used
         write_reject(P, i, trow0, K, true, lane);
       } else {
-        const uint64_t rej = __ballot(active && !((double)r <= ratio));
+        const uint64_t rej = __ballot(active && !accept);
         const int a = rej ? __ffsll((unsigned long long)rej) - 1 : K;
-        // slot a is written by the draw below
+        const int n_emit = emitted_count(P, i, x, a, lane);
+        const bool frontier = n_emit == a + 1;
+        // slot a is written by the draw below when the extra token is emitted
         for (int j = lane; j <= K; j += kWave)
-          if (j != a) P.out_tokens[trow0 + j] = j < a ? x : -1;
-        if (lane == 0) P.accepted_len[i] = a;
+          if (j != a || !frontier) P.out_tokens[trow0 + j] = j < a && j < n_emit ? x : -1;
+        if (lane == 0) {
+          P.accepted_len[i] = a;
+          if (P.emitted_len) P.emitted_len[i] = n_emit;
+          if (!frontier && P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_NONE;
+        }
         if (P.dg.target_lse)
           for (int j = lane; j <= K; j += kWave) P.dg.target_lse[trow0 + j] = rows[j].l2 * kLn2;
         if (active) {
           if (P.dg.draft_lse) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
           if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
-          if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = r;
+          if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
         }
         d.a = a;
-        if (a == K) {
+        if (!frontier) {  // emission stops inside the accepted drafts: nothing is drawn
+          d.kind = SDV_TERM_NONE;
+        } else if (a == K) {
           d.kind = SDV_TERM_BONUS;
           d.ref_t = rows[K].ref;
-          d.u = draw_uniform(verifier_block(seed, (uint32_t)i, (uint32_t)K));
+          d.u = P.u_each ? P.u_each[trow0 + K] : (double)draw_uniform(verifier_block(seed, (uint32_t)i, (uint32_t)K));
         } else {
           // weights in the frame 2^(z_t k - ref_t) of the rejected target row; draft side
           // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and the factor 2^-(e - e_hi)
@@ -769,7 +820,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
           const double e = (double)d.ref_t + __shfl(fd.l2, a, kWave) - __shfl(ft.l2, a, kWave);
           d.e_hi = (float)e;
           d.q_scale = (float)exp2((double)d.e_hi - e);
-          d.u = __shfl(draw_uniform(blk), a, kWave);
+          d.u = P.u_each ? P.u_each[trow0 + a] : (double)__shfl(draw_uniform(blk), a, kWave);
         }
       }
     }
@@ -858,7 +909,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   }
   if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
     P.out_tokens[trow] = y;
-    if (P.dg.draw_uniform) P.dg.draw_uniform[i] = d.u;
+    if (P.dg.draw_uniform) P.dg.draw_uniform[i] = (float)d.u;
     if (P.dg.terminal_kind)
       P.dg.terminal_kind[i] = d.kind == SDV_TERM_BONUS ? SDV_TERM_BONUS : (empty ? SDV_TERM_RESIDUAL_EMPTY : SDV_TERM_RESIDUAL);
   }
@@ -974,9 +1025,15 @@ int launch_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
 // per batch (temperature, seed), else device arrays of B values.
 int verify_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                 const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
-                double temperature, uint64_t seed, const float* temp_each, const uint64_t* seed_each,
-                int32_t* accepted_len, int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream,
-                const sdv_diag* diag) {
+                double temperature, uint64_t seed, const sdv_options* opt, int32_t* accepted_len,
+                int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+  const sdv_options none{};
+  if (!opt) opt = &none;
+  const float* temp_each = opt->temperature;
+  const uint64_t* seed_each = opt->seed;
+  if ((opt->accept_uniform == nullptr) != (opt->draw_uniform == nullptr)) return SDV_ERR_INVALID_ARG;
+  if (opt->stop_offsets && (opt->n_stop_tokens < 0 || (opt->n_stop_tokens > 0 && !opt->stop_tokens)))
+    return SDV_ERR_INVALID_ARG;
   Layout L;
   const int shape = make_layout(B, n_draft_rows, V, dtype, &L);
   if (shape != SDV_OK) return shape;
@@ -1017,6 +1074,13 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.seed = seed;
   P.temp_each = temp_each;
   P.seed_each = seed_each;
+  P.r_each = opt->accept_uniform;
+  P.u_each = opt->draw_uniform;
+  P.stop_off = opt->stop_offsets;
+  P.stop_tok = opt->stop_tokens;
+  P.n_stop = opt->stop_offsets ? opt->n_stop_tokens : 0;
+  P.budget = opt->budget;
+  P.emitted_len = opt->emitted_len;
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};
@@ -1040,8 +1104,18 @@ int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int
                   double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
                   size_t workspace_bytes, void* stream, const sdv_diag* diag) {
   return sdv::verify_impl(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V, dtype,
-                          temperature, seed, nullptr, nullptr, accepted_len, out_tokens, workspace, workspace_bytes,
-                          stream, diag);
+                          temperature, seed, nullptr, accepted_len, out_tokens, workspace, workspace_bytes, stream,
+                          diag);
+}
+
+int sdv_verify_opts(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                    const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                    double temperature, uint64_t seed, const sdv_options* options, int32_t* accepted_len,
+                    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                    const sdv_diag* diag) {
+  return sdv::verify_impl(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V, dtype,
+                          temperature, seed, options, accepted_len, out_tokens, workspace, workspace_bytes, stream,
+                          diag);
 }
 
 int sdv_verify_profiled(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
@@ -1049,8 +1123,11 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
                         const float* temperature, const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens,
                         void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
   if (!temperature || !seed) return SDV_ERR_INVALID_ARG;
+  sdv_options opt{};
+  opt.temperature = temperature;
+  opt.seed = seed;
   return sdv::verify_impl(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V, dtype, 0.0,
-                          0, temperature, seed, accepted_len, out_tokens, workspace, workspace_bytes, stream, diag);
+                          0, &opt, accepted_len, out_tokens, workspace, workspace_bytes, stream, diag);
 }
 
 int sdv_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,

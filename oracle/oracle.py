@@ -24,7 +24,7 @@ SOURCE = os.path.join(_HERE, "sdv_oracle.c")
 LIBRARY = os.path.join(_HERE, "liboracle.so")
 
 BF16, FP32 = 0, 1
-TERM_GREEDY, TERM_BONUS, TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, TERM_BAD = 0, 1, 2, 3, -1
+TERM_GREEDY, TERM_BONUS, TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, TERM_NONE, TERM_BAD = 0, 1, 2, 3, 4, -1
 
 
 def build(out: str = LIBRARY, extra_flags: tuple[str, ...] = ()) -> str:
@@ -32,6 +32,20 @@ def build(out: str = LIBRARY, extra_flags: tuple[str, ...] = ()) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", *extra_flags, SOURCE, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [
+        ("temperature", ctypes.c_void_p),
+        ("seed", ctypes.c_void_p),
+        ("accept_uniform", ctypes.c_void_p),
+        ("draw_uniform", ctypes.c_void_p),
+        ("stop_offsets", ctypes.c_void_p),
+        ("stop_tokens", ctypes.c_void_p),
+        ("n_stop_tokens", ctypes.c_int64),
+        ("budget", ctypes.c_void_p),
+        ("emitted_len", ctypes.c_void_p),
+    ]
 
 
 class _Diag(ctypes.Structure):
@@ -61,6 +75,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
+    ]
+    lib.oracle_verify_opts.restype = ctypes.c_int
+    lib.oracle_verify_opts.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
+        ctypes.POINTER(_Options), ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
     ]
     lib.oracle_verify_profiled.restype = ctypes.c_int
     lib.oracle_verify_profiled.argtypes = [
@@ -98,15 +118,26 @@ def _dtype_code(logits: np.ndarray) -> int:
     raise TypeError(f"logits must be uint16 (bf16 bits) or float32, got {logits.dtype}")
 
 
+def stop_csr(stop_lists) -> tuple[np.ndarray, np.ndarray]:
+    """Per-request stop-token lists as (offsets [B + 1], tokens) int32 arrays."""
+    offs = np.concatenate([[0], np.cumsum([len(x) for x in stop_lists])]).astype(np.int32)
+    toks = np.asarray([t for x in stop_lists for t in x], dtype=np.int32)
+    return offs, toks
+
+
 def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, cu: np.ndarray,
-           temperature, seed, diag: bool = False, lib_path: str = LIBRARY) -> dict:
+           temperature, seed, diag: bool = False, lib_path: str = LIBRARY, *, accept_uniform=None,
+           draw_uniform=None, stop_lists=None, budget=None) -> dict:
     """Run the oracle on one ragged batch.
 
     target: (n_draft_rows + B, V); draft: (n_draft_rows, V) or None when temperature == 0;
     draft_tokens: (n_draft_rows,) int32; cu: (B + 1,) int32 exclusive prefix sums of K_i.
     temperature and seed are scalars, or arrays of B values (one sampling profile per request).
-    Returns accepted_len (B,), out_tokens (n_draft_rows + B,), and with ``diag`` the per-row LSEs,
-    argmaxes, ratios, margins, residual masses and terminal kinds.
+    accept_uniform (n_draft_rows,) / draw_uniform (n_draft_rows + B,): the caller's uniforms in
+    [0, 1), both or neither; stop_lists: B lists of stop tokens; budget: (B,) remaining outputs.
+    Returns accepted_len (B,), out_tokens (n_draft_rows + B,), emitted_len (B,) when stops or a
+    budget are given, and with ``diag`` the per-row LSEs, argmaxes, ratios, margins, residual
+    masses and terminal kinds.
     """
     lib = load(lib_path)
     target = np.ascontiguousarray(target)
@@ -136,7 +167,39 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
         )
         dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
         dg_p = ctypes.pointer(dg)
-    if np.ndim(temperature) == 0 and np.ndim(seed) == 0:
+    extras = accept_uniform is not None or draw_uniform is not None or stop_lists is not None or budget is not None
+    if extras:
+        keep = []  # arrays the options point into stay alive for the call
+
+        def arr(x, dtype, n):
+            a = np.ascontiguousarray(np.asarray(x, dtype=dtype).reshape(n))
+            keep.append(a)
+            return _ptr(a)
+
+        opt = _Options()
+        if np.ndim(temperature) or np.ndim(seed):
+            opt.temperature = arr(np.broadcast_to(np.asarray(temperature, dtype=np.float64), (B,)), np.float64, B)
+            sd = np.asarray([int(x) & 0xFFFFFFFFFFFFFFFF for x in np.ravel(seed)], dtype=np.uint64) \
+                if np.ndim(seed) else np.full(B, int(seed) & 0xFFFFFFFFFFFFFFFF, dtype=np.uint64)
+            opt.seed = arr(sd, np.uint64, B)
+        if accept_uniform is not None:
+            opt.accept_uniform = arr(accept_uniform, np.float64, n_d)
+        if draw_uniform is not None:
+            opt.draw_uniform = arr(draw_uniform, np.float64, n_d + B)
+        if stop_lists is not None:
+            offs, toks = stop_lists if isinstance(stop_lists, tuple) else stop_csr(stop_lists)
+            opt.stop_offsets = arr(offs, np.int32, B + 1)
+            opt.stop_tokens = arr(toks, np.int32, np.size(toks)) if np.size(toks) else None
+            opt.n_stop_tokens = int(np.size(toks))
+        if budget is not None:
+            opt.budget = arr(budget, np.int32, B)
+        res["emitted_len"] = np.full(B, -7, dtype=np.int32)
+        opt.emitted_len = _ptr(res["emitted_len"])
+        rc = lib.oracle_verify_opts(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
+                                    float(temperature) if np.ndim(temperature) == 0 else 0.0,
+                                    int(seed) & 0xFFFFFFFFFFFFFFFF if np.ndim(seed) == 0 else 0,
+                                    ctypes.byref(opt), _ptr(acc), _ptr(out), dg_p)
+    elif np.ndim(temperature) == 0 and np.ndim(seed) == 0:
         rc = lib.oracle_verify(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
                                float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(acc), _ptr(out), dg_p)
     else:

@@ -61,6 +61,7 @@ enum {
   ORACLE_TERM_BONUS = 1,
   ORACLE_TERM_RESIDUAL = 2,
   ORACLE_TERM_RESIDUAL_EMPTY = 3,
+  ORACLE_TERM_NONE = 4, /* stop token or budget within the accepted drafts: no extra token, no draw */
   ORACLE_TERM_BAD = -1
 };
 
@@ -75,6 +76,31 @@ typedef struct {
   double* resid_mass;     /* [B]              S, the total weight of the extra-token draw */
   int32_t* terminal_kind; /* [B]              one of ORACLE_TERM_* */
 } oracle_diag;
+
+/*
+ * Per-request options.  Every member may be NULL (0 for n_stop_tokens), which selects the
+ * behaviour of oracle_verify.
+ *  - temperature, seed [B]: one sampling profile per request (SDCP "Session Contract").
+ *  - accept_uniform [n_draft_rows], draw_uniform [n_draft_rows + B]: uniforms in [0, 1) supplied
+ *    by the caller, r per draft position and u per position (target-row layout).  With them the
+ *    accept test is SDCP Rule 2's strict one, r < p/q.  Both or neither.
+ *  - stop_offsets [B + 1], stop_tokens [n_stop_tokens]: request i stops at any of
+ *    stop_tokens[stop_offsets[i] .. stop_offsets[i + 1]).
+ *  - budget [B]: remaining output tokens of each request.
+ *  - emitted_len [B] out: tokens emitted after truncation (SDCP "Verification and Commit", step 7;
+ *    M7.8 section 0x09, "EOS and length-limit stopping").
+ */
+typedef struct {
+  const double* temperature;
+  const uint64_t* seed;
+  const double* accept_uniform;
+  const double* draw_uniform;
+  const int32_t* stop_offsets;
+  const int32_t* stop_tokens;
+  int64_t n_stop_tokens;
+  const int32_t* budget;
+  int32_t* emitted_len;
+} oracle_options;
 
 /* ---------------------------------------------------------------- Philox4x32-10 (SC'11) */
 
@@ -202,12 +228,42 @@ static void set_nan(double* p) {
   if (p) *p = NAN;
 }
 
+/* Is token x one of request i's stop tokens? */
+static int is_stop(const oracle_options* opt, int32_t i, int32_t x) {
+  if (!opt || !opt->stop_offsets) return 0;
+  for (int64_t s = opt->stop_offsets[i]; s < opt->stop_offsets[i + 1]; ++s)
+    if (opt->stop_tokens[s] == x) return 1;
+  return 0;
+}
+
+/*
+ * How many of the a + 1 candidate tokens (a accepted drafts, then the extra token) are emitted:
+ * none after the first stop token, and no more than the remaining budget.  The extra token is
+ * emitted only when the count reaches a + 1 (SDCP "Verification and Commit", step 7; M7.8 section
+ * 0x09: stopping inside the accepted drafts omits the correction or bonus).
+ */
+static int64_t emitted_count(const oracle_options* opt, int32_t i, const int32_t* drafts, int64_t a) {
+  int64_t n = a + 1;
+  for (int64_t j = 0; j < a; ++j)
+    if (is_stop(opt, i, drafts[j])) {
+      n = j + 1;
+      break;
+    }
+  if (opt && opt->budget) {
+    const int64_t b = opt->budget[i] > 0 ? opt->budget[i] : 0;
+    if (b < n) n = b;
+  }
+  return n;
+}
+
 static void verify_request(const void* target, const void* draft, int dtype, const int32_t* tokens,
                            const int32_t* cu, int32_t i, int64_t n_draft_rows, int32_t V, double T,
-                           uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* dg,
-                           double* w /* scratch [V] */) {
+                           uint64_t seed, const oracle_options* opt, int32_t* accepted_len, int32_t* out_tokens,
+                           oracle_diag* dg, double* w /* scratch [V] */) {
   const int64_t lo = cu[i], hi = cu[i + 1];
   const int64_t K = hi - lo;
+  int32_t* emitted = opt ? opt->emitted_len : NULL;
+  if (emitted) emitted[i] = 0;
   if (dg && dg->cdf_margin) dg->cdf_margin[i] = NAN;
   if (dg && dg->resid_mass) dg->resid_mass[i] = NAN;
   if (lo < 0 || hi > n_draft_rows || K < 0 || K > ORACLE_MAX_DEPTH) {
@@ -220,8 +276,13 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   const int64_t drow0 = lo;     /* draft rows of request i:  drow0 .. drow0 + K - 1 */
   int32_t* slots = out_tokens + trow0;
 
-  /* a temperature that is negative, NaN or infinite describes no sampling profile */
+  /* a temperature that is negative, NaN or infinite describes no sampling profile; a stop list
+     that does not lie inside the stop-token array describes no stop set */
   int bad = !(T >= 0.0) || isinf(T);
+  if (opt && opt->stop_offsets) {
+    const int64_t s0 = opt->stop_offsets[i], s1 = opt->stop_offsets[i + 1];
+    if (s0 < 0 || s1 < s0 || s1 > opt->n_stop_tokens) bad = 1;
+  }
   for (int64_t j = 0; j < K && !bad; ++j)
     if (tokens[drow0 + j] < 0 || tokens[drow0 + j] >= V) bad = 1;
   /* q_j(x_j) = 0 exactly when the draft logit at x_j is -inf; checked before any draw */
@@ -245,11 +306,13 @@ static void verify_request(const void* target, const void* draft, int dtype, con
     }
     if (dg && dg->target_argmax)
       for (int64_t j = 0; j <= K; ++j) dg->target_argmax[trow0 + j] = oracle_row_argmax(target, dtype, trow0 + j, V);
-    for (int64_t j = 0; j < a; ++j) slots[j] = tokens[drow0 + j];
-    slots[a] = oracle_row_argmax(target, dtype, trow0 + a, V);
-    for (int64_t j = a + 1; j <= K; ++j) slots[j] = -1;
+    const int64_t n = emitted_count(opt, i, tokens + drow0, a);
+    for (int64_t j = 0; j <= K; ++j) slots[j] = -1;
+    for (int64_t j = 0; j < a && j < n; ++j) slots[j] = tokens[drow0 + j];
+    if (n == a + 1) slots[a] = oracle_row_argmax(target, dtype, trow0 + a, V);
     accepted_len[i] = (int32_t)a;
-    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_GREEDY;
+    if (emitted) emitted[i] = (int32_t)n;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = n == a + 1 ? ORACLE_TERM_GREEDY : ORACLE_TERM_NONE;
     return;
   }
 
@@ -274,17 +337,38 @@ static void verify_request(const void* target, const void* draft, int dtype, con
     const double ratio = exp(log_ratio); /* p_j(x) / q_j(x) */
     if (dg && dg->ratio) dg->ratio[drow0 + j] = ratio;
     if (a < K) continue; /* positions after the first rejection are never tested */
-    uint32_t blk[4];
-    oracle_philox_block(seed, (uint32_t)i, (uint32_t)j, blk);
-    const double r = accept_uniform(blk);
+    int accept;
+    double r;
+    if (opt && opt->accept_uniform) { /* the caller's r in [0, 1): SDCP Rule 2, r < p/q */
+      r = opt->accept_uniform[drow0 + j];
+      accept = r < ratio;
+    } else { /* Philox r in (0, 1]: r <= p/q */
+      uint32_t blk[4];
+      oracle_philox_block(seed, (uint32_t)i, (uint32_t)j, blk);
+      r = accept_uniform(blk);
+      accept = r <= ratio;
+    }
     if (dg && dg->accept_margin) dg->accept_margin[drow0 + j] = fabs(r - ratio);
-    if (!(r <= ratio)) a = j;
+    if (!accept) a = j;
   }
 
   const int64_t t = a; /* the position whose extra token is drawn */
-  uint32_t blk[4];
-  oracle_philox_block(seed, (uint32_t)i, (uint32_t)t, blk);
-  const double u = draw_uniform(blk);
+  const int64_t n_emit = emitted_count(opt, i, tokens + drow0, a);
+  accepted_len[i] = (int32_t)a;
+  if (emitted) emitted[i] = (int32_t)n_emit;
+  if (n_emit < a + 1) { /* emission stops inside the accepted drafts: no extra token is drawn */
+    for (int64_t j = 0; j <= K; ++j) slots[j] = j < n_emit ? tokens[drow0 + j] : -1;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_NONE;
+    return;
+  }
+  double u;
+  if (opt && opt->draw_uniform) {
+    u = opt->draw_uniform[trow0 + t];
+  } else {
+    uint32_t blk[4];
+    oracle_philox_block(seed, (uint32_t)i, (uint32_t)t, blk);
+    u = draw_uniform(blk);
+  }
   int kind;
   if (t < K) {
     kind = ORACLE_TERM_RESIDUAL;
@@ -309,7 +393,6 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   for (int64_t j = 0; j < t; ++j) slots[j] = tokens[drow0 + j];
   slots[t] = y;
   for (int64_t j = t + 1; j <= K; ++j) slots[j] = -1;
-  accepted_len[i] = (int32_t)a;
   if (dg) {
     if (dg->cdf_margin) dg->cdf_margin[i] = margin;
     if (dg->resid_mass) dg->resid_mass[i] = S;
@@ -330,8 +413,9 @@ static void verify_request(const void* target, const void* draft, int dtype, con
  */
 static int verify_batch(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
                         const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, double T, uint64_t seed,
-                        const double* T_each, const uint64_t* seed_each, int32_t* accepted_len,
-                        int32_t* out_tokens, oracle_diag* diag) {
+                        const oracle_options* opt, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* diag) {
+  const double* T_each = opt ? opt->temperature : NULL;
+  const uint64_t* seed_each = opt ? opt->seed : NULL;
   int failed = 0;
 #pragma omp parallel reduction(| : failed)
   {
@@ -341,7 +425,7 @@ static int verify_batch(const void* target, const void* draft, int dtype, const 
     for (int32_t i = 0; i < B; ++i)
       if (w)
         verify_request(target, draft, dtype, draft_tokens, cu, i, n_draft_rows, V, T_each ? T_each[i] : T,
-                       seed_each ? seed_each[i] : seed, accepted_len, out_tokens, diag, w);
+                       seed_each ? seed_each[i] : seed, opt, accepted_len, out_tokens, diag, w);
     free(w);
   }
   return failed ? -2 : 0;
@@ -353,7 +437,27 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
   if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens) return -1;
   if (B <= 0 || V <= 0 || n_draft_rows < 0 || !(T >= 0.0) || isinf(T) || (T > 0.0 && !draft)) return -1;
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
-  return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, T, seed, NULL, NULL, accepted_len,
+  return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, T, seed, NULL, accepted_len,
+                      out_tokens, diag);
+}
+
+/*
+ * The general entry point: T and seed as in oracle_verify, refined by the per-request options
+ * (which may be NULL).  Per-request temperatures need draft logits whenever n_draft_rows > 0.
+ */
+int oracle_verify_opts(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
+                       const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, double T, uint64_t seed,
+                       const oracle_options* opt, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* diag) {
+  if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens) return -1;
+  if (B <= 0 || V <= 0 || n_draft_rows < 0) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
+  const int profiled = opt && opt->temperature;
+  if (opt && (!opt->temperature) != (!opt->seed)) return -1;
+  if (opt && (!opt->accept_uniform) != (!opt->draw_uniform)) return -1;
+  if (opt && opt->stop_offsets && (opt->n_stop_tokens < 0 || (opt->n_stop_tokens > 0 && !opt->stop_tokens))) return -1;
+  if (!profiled && (!(T >= 0.0) || isinf(T) || (T > 0.0 && !draft && n_draft_rows > 0))) return -1;
+  if (profiled && n_draft_rows > 0 && !draft) return -1;
+  return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, T, seed, opt, accepted_len,
                       out_tokens, diag);
 }
 
@@ -367,11 +471,10 @@ int oracle_verify(const void* target, const void* draft, int dtype, const int32_
 int oracle_verify_profiled(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
                            const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, const double* temperature,
                            const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* diag) {
-  if (!target || !draft_tokens || !cu || !accepted_len || !out_tokens || !temperature || !seed) return -1;
-  if (B <= 0 || V <= 0 || n_draft_rows < 0 || (n_draft_rows > 0 && !draft)) return -1;
-  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
-  return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, 0.0, 0, temperature, seed,
-                      accepted_len, out_tokens, diag);
+  if (!temperature || !seed) return -1;
+  oracle_options opt = {temperature, seed, NULL, NULL, NULL, NULL, 0, NULL, NULL};
+  return oracle_verify_opts(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, 0.0, 0, &opt, accepted_len,
+                            out_tokens, diag);
 }
 
 /* Number of OpenMP threads the oracle runs on (for reporting), and a way to change it (timing). */

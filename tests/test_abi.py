@@ -29,7 +29,8 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
-                          "sdv_read_ceiling", "sdv_verify_profiled", "sdv_status_string", "sdv_abi_version"}
+                          "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms",
+                          "sdv_status_string", "sdv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
@@ -109,6 +110,24 @@ def test_profiled_host_argument_checks(lib):
     assert call(dt=5) == -2
     assert call(wsb=need - 1) == -4
     assert call(B=0) == -1
+
+
+def test_opts_host_argument_checks(lib):
+    need = lib.sdv_workspace_bytes(2, 8, 1000, 0)
+
+    def call(**kw):
+        o = _native.SdvOptions()
+        for k, v in kw.items():
+            setattr(o, k, v)
+        return lib.sdv_verify_opts(FAKE, FAKE, FAKE, FAKE, 2, 8, 1000, 0, 1.0, 1, ctypes.byref(o), FAKE, FAKE, FAKE,
+                                   need, None, None)
+    assert call(accept_uniform=FAKE) == -1           # r without u
+    assert call(draw_uniform=FAKE) == -1             # u without r
+    assert call(temperature=FAKE) == -1              # temperatures without seeds
+    assert call(stop_offsets=FAKE, n_stop_tokens=-1) == -1
+    assert call(stop_offsets=FAKE, n_stop_tokens=3) == -1  # tokens missing
+    assert lib.sdv_verify_opts(FAKE, FAKE, FAKE, FAKE, 2, 8, 1000, 0, -1.0, 1, None, FAKE, FAKE, FAKE, need, None,
+                               None) == -1
 
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):

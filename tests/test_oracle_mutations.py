@@ -23,7 +23,12 @@ MUTATIONS = {
     "residual_without_clamp": ("w[v] = p > q ? p - q : 0.0;", "w[v] = p - q;"),
     "residual_sign_flipped": ("w[v] = p > q ? p - q : 0.0;", "w[v] = q > p ? q - p : 0.0;"),
     "ratio_inverted": ("const double ratio = exp(log_ratio);", "const double ratio = exp(-log_ratio);"),
-    "accept_comparison_reversed": ("if (!(r <= ratio)) a = j;", "if (!(r >= ratio)) a = j;"),
+    "accept_comparison_reversed": ("accept = r <= ratio;", "accept = r >= ratio;"),
+    "caller_accept_not_strict": ("accept = r < ratio;", "accept = r <= ratio;"),
+    "stop_token_not_emitted": ("n = j + 1;\n      break;", "n = j;\n      break;"),
+    "budget_ignored": ("if (b < n) n = b;", "(void)b;"),
+    "frontier_drawn_after_stop": ("if (n_emit < a + 1) {", "if (n_emit < a) {"),
+    "caller_draw_uniform_of_first_position": ("u = opt->draw_uniform[trow0 + t];", "u = opt->draw_uniform[trow0];"),
     "lse_drops_max": ("return m / T + log(s);", "return log(s);"),
     "residual_from_next_row": ("const double p = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);",
                                "const double p = exp(logit_at(target, dtype, trow0 + t + 1, V, v) / T - lse_t[t + 1]);"),
@@ -147,8 +152,41 @@ def _pin_profiles(lib_path):
     return True
 
 
+def _pin_stops(lib_path):
+    """SDCP's example round with stops and budgets, and the caller-uniform special cases."""
+    rows = np.zeros((4, 16), dtype=np.float32)
+    for r, g in enumerate([7, 9, 13, 5]):
+        rows[r, g] = 1.0
+    toks, cu = np.array([7, 9, 11], dtype=np.int32), offsets_from_depths([3])
+    for stop, budget, want in (([9], None, [7, 9]), ([13], None, [7, 9, 13]), ([], 1, [7]), ([], 2, [7, 9])):
+        res = oracle.verify(rows, None, toks, cu, 0.0, 0, lib_path=lib_path, stop_lists=[stop],
+                            budget=None if budget is None else [budget])
+        n = int(res["emitted_len"][0])
+        if res["out_tokens"][:n].tolist() != want or (res["out_tokens"][n:] != -1).any():
+            return False
+    # caller uniforms: r = 0 rejects exactly where p(x) = 0; the draw uses u of the drawn position
+    rng = np.random.default_rng(5)
+    target = rng.standard_normal((5, 12)).astype(np.float32)
+    draft = (target[:4] + rng.standard_normal((4, 12))).astype(np.float32)
+    tokens = rng.integers(0, 12, size=4).astype(np.int32)
+    target[2, tokens[2]] = -np.inf
+    u = np.array([0.1, 0.2, 0.999999, 0.4, 0.5])
+    res = oracle.verify(target, draft, tokens, offsets_from_depths([4]), 1.0, 0, lib_path=lib_path,
+                        accept_uniform=np.zeros(4), draw_uniform=u)
+    if res["accepted_len"][0] != 2:
+        return False
+    w = np.maximum(exact.softmax(target[2], 1.0) - exact.softmax(draft[2], 1.0), 0.0)
+    c = np.cumsum(w)
+    if res["out_tokens"][2] != np.searchsorted(c, u[2] * c[-1], side="right"):
+        return False
+    # a budget of exactly a emits the accepted drafts and no extra token
+    res = oracle.verify(target, draft, tokens, offsets_from_depths([4]), 1.0, 0, lib_path=lib_path,
+                        accept_uniform=np.zeros(4), draw_uniform=u, budget=[2])
+    return res["out_tokens"][:2].tolist() == tokens[:2].tolist() and (res["out_tokens"][2:] == -1).all()
+
+
 def test_unmutated_oracle_passes_every_pin(tmp_path):
-    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles):
+    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops):
         assert check(oracle.LIBRARY)
     assert _pin_philox(oracle.LIBRARY, tmp_path)
 
@@ -164,5 +202,6 @@ def test_planted_mistake_is_caught(tmp_path, name):
         "greedy_tie": _pin_greedy_tie(lib),
         "philox": _pin_philox(lib, tmp_path),
         "profiles": _pin_profiles(lib),
+        "stops_and_caller_uniforms": _pin_stops(lib),
     }
     assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"
