@@ -227,6 +227,31 @@ int sdv_sdcp_uniforms(int32_t B, const int32_t* cu, const uint64_t* seeds, const
                       const uint32_t* rounds, double* accept_uniform, double* draw_uniform);
 
 /*
+ * Post-verification commit of a batch ("M7.8 - Speculative Serving", sections 0x03C and 0x03D:
+ * the ragged results are unpadded and each request's emitted tokens appended to its logical
+ * sequence at contiguous positions; section 0x09 for the lengths after a round).  All arrays are
+ * DEVICE arrays; ragged_offsets, accepted_len and out_tokens are those of the verification call,
+ * emitted_len its sdv_options.emitted_len (NULL: every valid request emitted a_i + 1 tokens), and
+ * prefix_len [B] int32 each request's logical length P_i before the round.  Writes:
+ *   new_offsets   [B + 1]            exclusive prefix sums of the emitted counts n_i
+ *   new_tokens    [n_draft_rows + B] request i's emitted tokens at new_offsets[i] ..
+ *   new_positions [n_draft_rows + B] their logical positions P_i, P_i + 1, ...
+ *   lengths       [B][3]             (L_out, L_target, L_draft) = (P + E + F, P + E,
+ *                                    P + min(E, max(K - 1, 0))), E the accepted drafts emitted and
+ *                                    F = 1 when the extra token was emitted
+ *   next_token, next_position [B]    the last emitted token and its position, or -1 when none
+ * A rejected request (accepted_len -1) or one whose offsets fall outside [0, n_draft_rows] emits
+ * nothing.  With offsets that are not non-decreasing the counts can sum past n_draft_rows + B:
+ * new_offsets reports them as they are, and no token is written beyond the arrays.  Errors: B < 1,
+ * n_draft_rows < 0 or a NULL required pointer -> SDV_ERR_INVALID_ARG; n_draft_rows + B above
+ * INT32_MAX -> SDV_ERR_LIMIT.
+ */
+int sdv_commit(int32_t B, int64_t n_draft_rows, const int32_t* ragged_offsets, const int32_t* accepted_len,
+               const int32_t* emitted_len, const int32_t* out_tokens, const int32_t* prefix_len, int32_t* new_offsets,
+               int32_t* new_tokens, int32_t* new_positions, int32_t* lengths, int32_t* next_token,
+               int32_t* next_position, void* stream);
+
+/*
  * Raw Philox4x32-10 blocks on the device, for testing the verifier's uniforms: out[b] =
  * Philox4x32-10(counter = counters[b][0..3], key = keys[b][0..1]) for b < n.  counters [n][4],
  * keys [n][2], out [n][4] are uint32 device arrays.  n < 1 or NULL pointers -> SDV_ERR_INVALID_ARG.

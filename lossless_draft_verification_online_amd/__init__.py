@@ -14,7 +14,7 @@ from . import _native
 from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_RESIDUAL,
                       TERM_RESIDUAL_EMPTY, SdvError)
 
-__all__ = ["verify", "verify_ex", "workspace_bytes", "philox4x32_10", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+__all__ = ["verify", "verify_ex", "commit", "workspace_bytes", "philox4x32_10", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
            "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
 
 _DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
@@ -241,3 +241,32 @@ def read_ceiling(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     if rc != 0:
         raise SdvError(rc, "sdv_read_ceiling")
     return out
+
+
+def commit(offsets: torch.Tensor, accepted_len: torch.Tensor, out_tokens: torch.Tensor, prefix_len: torch.Tensor,
+           emitted_len: torch.Tensor | None = None) -> dict:
+    """sdv_commit: the emitted tokens of a verified batch packed per request at contiguous logical
+    positions, with each request's new lengths.  Returns device tensors offsets [B + 1],
+    tokens / positions [n_draft_rows + B] (the first offsets[B] are used), lengths [B, 3]
+    (L_out, L_target, L_draft), next_token [B], next_position [B]."""
+    dev = offsets.device
+    B = offsets.shape[0] - 1
+    n_d = out_tokens.shape[0] - B
+    for name, t, n in (("offsets", offsets, B + 1), ("accepted_len", accepted_len, B),
+                       ("out_tokens", out_tokens, n_d + B), ("prefix_len", prefix_len, B)):
+        _device_vector(t, torch.int32, n, dev, name)
+    _device_vector(emitted_len, torch.int32, B, dev, "emitted_len")
+    res = {"offsets": torch.empty(B + 1, dtype=torch.int32, device=dev),
+           "tokens": torch.full((n_d + B,), -1, dtype=torch.int32, device=dev),
+           "positions": torch.full((n_d + B,), -1, dtype=torch.int32, device=dev),
+           "lengths": torch.empty((B, 3), dtype=torch.int32, device=dev),
+           "next_token": torch.empty(B, dtype=torch.int32, device=dev),
+           "next_position": torch.empty(B, dtype=torch.int32, device=dev)}
+    with torch.cuda.device(dev):
+        rc = _native.lib().sdv_commit(
+            B, n_d, _ptr(offsets), _ptr(accepted_len), _ptr(emitted_len), _ptr(out_tokens), _ptr(prefix_len),
+            _ptr(res["offsets"]), _ptr(res["tokens"]), _ptr(res["positions"]), _ptr(res["lengths"]),
+            _ptr(res["next_token"]), _ptr(res["next_position"]), torch.cuda.current_stream(dev).cuda_stream)
+    if rc != 0:
+        raise SdvError(rc, "sdv_commit")
+    return res

@@ -80,6 +80,8 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
                                   + [ctypes.POINTER(SdvDiag)])
     L.sdv_sdcp_uniforms.restype = ctypes.c_int
     L.sdv_sdcp_uniforms.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 6
+    L.sdv_commit.restype = ctypes.c_int
+    L.sdv_commit.argtypes = [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 12
     L.sdv_philox4x32_10.restype = ctypes.c_int
     L.sdv_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.restype = ctypes.c_char_p

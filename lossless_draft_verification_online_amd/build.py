@@ -6,7 +6,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "sdv.hip"), os.path.join(PKG, "csrc", "sdcp_uniforms.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", "sdv.hip"), os.path.join(PKG, "csrc", "commit.hip"),
+           os.path.join(PKG, "csrc", "sdcp_uniforms.cpp")]
 DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "sdv_device.hpp"), os.path.join(ROOT, "include", "sdv.h")]
 LIBRARY = os.path.join(PKG, "libsdv.so")
 

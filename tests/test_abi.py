@@ -29,7 +29,7 @@ def lib():
 def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
-                          "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms",
+                          "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms", "sdv_commit",
                           "sdv_status_string", "sdv_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
@@ -128,6 +128,19 @@ def test_opts_host_argument_checks(lib):
     assert call(stop_offsets=FAKE, n_stop_tokens=3) == -1  # tokens missing
     assert lib.sdv_verify_opts(FAKE, FAKE, FAKE, FAKE, 2, 8, 1000, 0, -1.0, 1, None, FAKE, FAKE, FAKE, need, None,
                                None) == -1
+
+
+def test_commit_host_argument_checks(lib):
+    args = [FAKE] * 11
+    assert lib.sdv_commit(0, 4, *args, None) == -1
+    assert lib.sdv_commit(2, -1, *args, None) == -1
+    a = list(args)
+    a[0] = None  # ragged offsets
+    assert lib.sdv_commit(2, 4, *a, None) == -1
+    a = list(args)
+    a[3] = None  # out_tokens
+    assert lib.sdv_commit(2, 4, *a, None) == -1
+    assert lib.sdv_commit(2, 2**31, *args, None) == -3
 
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):
