@@ -45,6 +45,7 @@ class _Options(ctypes.Structure):
         ("n_stop_tokens", ctypes.c_int64),
         ("budget", ctypes.c_void_p),
         ("emitted_len", ctypes.c_void_p),
+        ("draft_probs", ctypes.c_void_p),
     ]
 
 
@@ -127,14 +128,15 @@ def stop_csr(stop_lists) -> tuple[np.ndarray, np.ndarray]:
 
 def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, cu: np.ndarray,
            temperature, seed, diag: bool = False, lib_path: str = LIBRARY, *, accept_uniform=None,
-           draw_uniform=None, stop_lists=None, budget=None) -> dict:
+           draw_uniform=None, stop_lists=None, budget=None, draft_probs=None) -> dict:
     """Run the oracle on one ragged batch.
 
     target: (n_draft_rows + B, V); draft: (n_draft_rows, V) or None when temperature == 0;
     draft_tokens: (n_draft_rows,) int32; cu: (B + 1,) int32 exclusive prefix sums of K_i.
     temperature and seed are scalars, or arrays of B values (one sampling profile per request).
     accept_uniform (n_draft_rows,) / draw_uniform (n_draft_rows + B,): the caller's uniforms in
-    [0, 1), both or neither; stop_lists: B lists of stop tokens; budget: (B,) remaining outputs.
+    [0, 1), both or neither; stop_lists: B lists of stop tokens; budget: (B,) remaining outputs;
+    draft_probs: (n_draft_rows, V) float32 draft distributions used in place of the draft logits.
     Returns accepted_len (B,), out_tokens (n_draft_rows + B,), emitted_len (B,) when stops or a
     budget are given, and with ``diag`` the per-row LSEs, argmaxes, ratios, margins, residual
     masses and terminal kinds.
@@ -167,7 +169,8 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
         )
         dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
         dg_p = ctypes.pointer(dg)
-    extras = accept_uniform is not None or draw_uniform is not None or stop_lists is not None or budget is not None
+    extras = (accept_uniform is not None or draw_uniform is not None or stop_lists is not None or budget is not None
+              or draft_probs is not None)
     if extras:
         keep = []  # arrays the options point into stay alive for the call
 
@@ -193,6 +196,8 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
             opt.n_stop_tokens = int(np.size(toks))
         if budget is not None:
             opt.budget = arr(budget, np.int32, B)
+        if draft_probs is not None:
+            opt.draft_probs = arr(draft_probs, np.float32, n_d * V)
         res["emitted_len"] = np.full(B, -7, dtype=np.int32)
         opt.emitted_len = _ptr(res["emitted_len"])
         rc = lib.oracle_verify_opts(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,

@@ -89,6 +89,10 @@ typedef struct {
  *  - budget [B]: remaining output tokens of each request.
  *  - emitted_len [B] out: tokens emitted after truncation (SDCP "Verification and Commit", step 7;
  *    M7.8 section 0x09, "EOS and length-limit stopping").
+ *  - draft_probs [n_draft_rows][V] binary32: the draft distributions themselves (SDCP's "q_rows",
+ *    section "Message Definitions"), used as given in place of softmax(draft logits / T); the
+ *    draft logits are then not read.  A zero (or negative, or NaN) q at a proposed token rejects
+ *    the request before any draw (SDCP "Verification and Commit", step 5).
  */
 typedef struct {
   const double* temperature;
@@ -100,6 +104,7 @@ typedef struct {
   int64_t n_stop_tokens;
   const int32_t* budget;
   int32_t* emitted_len;
+  const float* draft_probs;
 } oracle_options;
 
 /* ---------------------------------------------------------------- Philox4x32-10 (SC'11) */
@@ -285,10 +290,17 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   }
   for (int64_t j = 0; j < K && !bad; ++j)
     if (tokens[drow0 + j] < 0 || tokens[drow0 + j] >= V) bad = 1;
-  /* q_j(x_j) = 0 exactly when the draft logit at x_j is -inf; checked before any draw */
+  /* q_j(x_j) = 0 exactly when the draft logit at x_j is -inf, or when the given probability at x_j
+     is not positive; checked before any draw */
+  const float* qrows = opt ? opt->draft_probs : NULL;
   if (!bad && T > 0.0)
-    for (int64_t j = 0; j < K; ++j)
-      if (logit_at(draft, dtype, drow0 + j, V, tokens[drow0 + j]) == -INFINITY) bad = 1;
+    for (int64_t j = 0; j < K; ++j) {
+      if (qrows) {
+        if (!(qrows[(drow0 + j) * (int64_t)V + tokens[drow0 + j]] > 0.0f)) bad = 1;
+      } else if (logit_at(draft, dtype, drow0 + j, V, tokens[drow0 + j]) == -INFINITY) {
+        bad = 1;
+      }
+    }
   if (bad) {
     accepted_len[i] = -1;
     for (int64_t j = 0; j <= K; ++j) slots[j] = -1;
@@ -319,12 +331,12 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   /* ---- Rule 2 */
   double lse_t[ORACLE_MAX_DEPTH + 1], lse_d[ORACLE_MAX_DEPTH];
   for (int64_t j = 0; j <= K; ++j) lse_t[j] = oracle_row_lse(target, dtype, trow0 + j, V, T);
-  for (int64_t j = 0; j < K; ++j) lse_d[j] = oracle_row_lse(draft, dtype, drow0 + j, V, T);
+  for (int64_t j = 0; j < K; ++j) lse_d[j] = qrows ? NAN : oracle_row_lse(draft, dtype, drow0 + j, V, T);
   if (dg) {
     for (int64_t j = 0; j <= K; ++j)
       if (dg->target_lse) dg->target_lse[trow0 + j] = lse_t[j];
     for (int64_t j = 0; j < K; ++j) {
-      if (dg->draft_lse) dg->draft_lse[drow0 + j] = lse_d[j];
+      if (dg->draft_lse && !qrows) dg->draft_lse[drow0 + j] = lse_d[j];
       set_nan(dg->accept_margin ? &dg->accept_margin[drow0 + j] : NULL);
     }
   }
@@ -332,9 +344,14 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   int64_t a = K;
   for (int64_t j = 0; j < K; ++j) {
     const int32_t x = tokens[drow0 + j];
-    const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) / T -
-                             (lse_t[j] - lse_d[j]);
-    const double ratio = exp(log_ratio); /* p_j(x) / q_j(x) */
+    double ratio; /* p_j(x) / q_j(x) */
+    if (qrows) {
+      ratio = exp(logit_at(target, dtype, trow0 + j, V, x) / T - lse_t[j]) / (double)qrows[(drow0 + j) * (int64_t)V + x];
+    } else {
+      const double log_ratio =
+          (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) / T - (lse_t[j] - lse_d[j]);
+      ratio = exp(log_ratio);
+    }
     if (dg && dg->ratio) dg->ratio[drow0 + j] = ratio;
     if (a < K) continue; /* positions after the first rejection are never tested */
     int accept;
@@ -375,7 +392,8 @@ static void verify_request(const void* target, const void* draft, int dtype, con
     double S = 0.0;
     for (int32_t v = 0; v < V; ++v) {
       const double p = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
-      const double q = exp(logit_at(draft, dtype, drow0 + t, V, v) / T - lse_d[t]);
+      const double q = qrows ? (double)qrows[(drow0 + t) * (int64_t)V + v]
+                             : exp(logit_at(draft, dtype, drow0 + t, V, v) / T - lse_d[t]);
       w[v] = p > q ? p - q : 0.0;
       S += w[v];
     }
@@ -455,8 +473,9 @@ int oracle_verify_opts(const void* target, const void* draft, int dtype, const i
   if (opt && (!opt->temperature) != (!opt->seed)) return -1;
   if (opt && (!opt->accept_uniform) != (!opt->draw_uniform)) return -1;
   if (opt && opt->stop_offsets && (opt->n_stop_tokens < 0 || (opt->n_stop_tokens > 0 && !opt->stop_tokens))) return -1;
-  if (!profiled && (!(T >= 0.0) || isinf(T) || (T > 0.0 && !draft && n_draft_rows > 0))) return -1;
-  if (profiled && n_draft_rows > 0 && !draft) return -1;
+  const int have_draft = draft || (opt && opt->draft_probs);
+  if (!profiled && (!(T >= 0.0) || isinf(T) || (T > 0.0 && !have_draft && n_draft_rows > 0))) return -1;
+  if (profiled && n_draft_rows > 0 && !have_draft) return -1;
   return verify_batch(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, T, seed, opt, accepted_len,
                       out_tokens, diag);
 }
@@ -472,7 +491,7 @@ int oracle_verify_profiled(const void* target, const void* draft, int dtype, con
                            const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, const double* temperature,
                            const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* diag) {
   if (!temperature || !seed) return -1;
-  oracle_options opt = {temperature, seed, NULL, NULL, NULL, NULL, 0, NULL, NULL};
+  oracle_options opt = {temperature, seed, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL};
   return oracle_verify_opts(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, 0.0, 0, &opt, accepted_len,
                             out_tokens, diag);
 }

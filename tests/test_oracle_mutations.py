@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 MUTATIONS = {
     "residual_without_clamp": ("w[v] = p > q ? p - q : 0.0;", "w[v] = p - q;"),
     "residual_sign_flipped": ("w[v] = p > q ? p - q : 0.0;", "w[v] = q > p ? q - p : 0.0;"),
-    "ratio_inverted": ("const double ratio = exp(log_ratio);", "const double ratio = exp(-log_ratio);"),
+    "ratio_inverted": ("ratio = exp(log_ratio);", "ratio = exp(-log_ratio);"),
     "accept_comparison_reversed": ("accept = r <= ratio;", "accept = r >= ratio;"),
     "caller_accept_not_strict": ("accept = r < ratio;", "accept = r <= ratio;"),
     "stop_token_not_emitted": ("n = j + 1;\n      break;", "n = j;\n      break;"),
@@ -39,8 +39,10 @@ MUTATIONS = {
     "profile_temperature_of_first_request": ("T_each ? T_each[i] : T", "T_each ? T_each[0] : T"),
     "profile_seed_of_next_request": ("seed_each ? seed_each[i] : seed", "seed_each ? seed_each[(i + 1) % B] : seed"),
     "profile_invalid_temperature_accepted": ("int bad = !(T >= 0.0) || isinf(T);", "int bad = 0;"),
-    "temperature_ignored": ("const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) / T -",
-                            "const double log_ratio = (logit_at(target, dtype, trow0 + j, V, x) - logit_at(draft, dtype, drow0 + j, V, x)) -"),
+    "qrows_ratio_not_divided": ("lse_t[j]) / (double)qrows[(drow0 + j) * (int64_t)V + x];", "lse_t[j]);"),
+    "qrows_residual_from_wrong_row": ("const double q = qrows ? (double)qrows[(drow0 + t) * (int64_t)V + v]",
+                                      "const double q = qrows ? (double)qrows[(drow0 + (t > 0 ? t - 1 : t + 1)) * (int64_t)V + v]"),
+    "temperature_ignored": ("drow0 + j, V, x)) / T - (lse_t[j] - lse_d[j]);", "drow0 + j, V, x)) - (lse_t[j] - lse_d[j]);"),
 }
 
 
@@ -185,8 +187,28 @@ def _pin_stops(lib_path):
     return res["out_tokens"][:2].tolist() == tokens[:2].tolist() and (res["out_tokens"][2:] == -1).all()
 
 
+def _pin_qrows(lib_path):
+    """q rows equal to the rounded draft softmax: verdicts as the logit path's, up to near-ties."""
+    from oracle.compare import compare_verdicts
+    rng = np.random.default_rng(12)
+    depths = rng.integers(1, 6, size=200)
+    cu = offsets_from_depths(depths)
+    n_d, B, V = int(cu[-1]), 200, 24
+    target = (rng.standard_normal((n_d + B, V)) * 2).astype(np.float32)
+    draft = (target[np.concatenate([np.arange(cu[i], cu[i + 1]) + i for i in range(B)])]
+             + rng.standard_normal((n_d, V))).astype(np.float32)
+    z = draft.astype(np.float64)
+    q = np.exp(z - z.max(axis=1, keepdims=True))
+    q = (q / q.sum(axis=1, keepdims=True)).astype(np.float32)
+    g = -np.log(-np.log(rng.random((n_d, V))))
+    tokens = np.argmax(z + g, axis=1).astype(np.int32)
+    ref = oracle.verify(target, draft, tokens, cu, 1.0, 3, diag=True, lib_path=lib_path)
+    got = oracle.verify(target, None, tokens, cu, 1.0, 3, draft_probs=q, lib_path=lib_path)
+    return compare_verdicts(got["accepted_len"], got["out_tokens"], ref, cu, 1.0)["n_hard"] == 0
+
+
 def test_unmutated_oracle_passes_every_pin(tmp_path):
-    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops):
+    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops, _pin_qrows):
         assert check(oracle.LIBRARY)
     assert _pin_philox(oracle.LIBRARY, tmp_path)
 
@@ -203,5 +225,6 @@ def test_planted_mistake_is_caught(tmp_path, name):
         "philox": _pin_philox(lib, tmp_path),
         "profiles": _pin_profiles(lib),
         "stops_and_caller_uniforms": _pin_stops(lib),
+        "qrows": _pin_qrows(lib),
     }
     assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"
