@@ -177,6 +177,14 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
  *                     [0, n_stop_tokens] rejects that request (accepted_len -1, every slot -1).
  *  budget             [B] int32: the remaining output budget of each request (<= 0 emits nothing).
  *  emitted_len        [B] int32 out: the number of tokens request i emits.
+ *  draft_probs        [n_draft_rows][V] float (binary32): the draft distributions themselves, SDCP's
+ *                     "q_rows" (section "Message Definitions"; Rule 2 takes q[i] from them), used as
+ *                     given in place of softmax(draft_logits / T); draft_logits is then not read and
+ *                     may be NULL.  Each row must be the distribution the token was drawn from (sums
+ *                     to 1 up to rounding).  A q that is not positive at the proposed token rejects
+ *                     the request before any uniform is used (SDCP "Verification and Commit", step
+ *                     5).  The row pass then streams target rows only; q is read at the proposed
+ *                     tokens and, for a correction, over the rejected position's row.
  *
  * Emission (SDCP section "Verification and Commit", step 7; "M7.8 - Speculative Serving", section
  * 0x09, "EOS and length-limit stopping"): of the a_i + 1 candidate tokens (the accepted drafts,
@@ -195,6 +203,7 @@ typedef struct sdv_options {
   int64_t n_stop_tokens;
   const int32_t* budget;
   int32_t* emitted_len;
+  const float* draft_probs;
 } sdv_options;
 
 /*

@@ -62,7 +62,7 @@ def _profile_arrays(temperature, seed, B, dev):
     return temperature, seed
 
 
-def _check(target, draft, draft_tokens, offsets, temperature):
+def _check(target, draft, draft_tokens, offsets, temperature, draft_probs=None):
     if not target.is_cuda:
         raise ValueError("target logits must be on the GPU")
     if target.dtype not in _DTYPES:
@@ -80,9 +80,13 @@ def _check(target, draft, draft_tokens, offsets, temperature):
     B = offsets.shape[0] - 1
     if target.shape[0] != draft_tokens.shape[0] + B:
         raise ValueError("target logits must have n_draft_rows + B rows")
+    if draft_probs is not None:
+        if draft_probs.dtype != torch.float32 or draft_probs.device != target.device or not draft_probs.is_contiguous() \
+                or draft_probs.dim() != 2 or draft_probs.shape != (draft_tokens.shape[0], target.shape[1]):
+            raise ValueError("draft_probs must be a contiguous float32 [n_draft_rows, V] tensor on the logits' device")
     needs_draft = isinstance(temperature, torch.Tensor) or temperature > 0
-    if needs_draft and draft is None and draft_tokens.shape[0] > 0:
-        raise ValueError("sampling (any temperature > 0, or per-request profiles) needs draft logits")
+    if needs_draft and draft is None and draft_probs is None and draft_tokens.shape[0] > 0:
+        raise ValueError("sampling (any temperature > 0, or per-request profiles) needs draft logits or draft_probs")
 
 
 def _device_vector(t, dtype, n, dev, name):
@@ -98,16 +102,18 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
               temperature, seed, *, out: tuple | None = None, workspace: torch.Tensor | None = None,
               diag: tuple[str, ...] = (), events: list | None = None, accept_uniform: torch.Tensor | None = None,
               draw_uniform: torch.Tensor | None = None, stop_offsets: torch.Tensor | None = None,
-              stop_tokens: torch.Tensor | None = None, budget: torch.Tensor | None = None):
+              stop_tokens: torch.Tensor | None = None, budget: torch.Tensor | None = None,
+              draft_probs: torch.Tensor | None = None):
     """Run sdv_verify_ex; sdv_verify_profiled when temperature and seed are [B] device tensors (one
     sampling profile per request); sdv_verify_opts when the caller's uniforms (float64
     accept_uniform [n_draft_rows], draw_uniform [n_draft_rows + B]), stop lists (int32 CSR
-    stop_offsets [B + 1], stop_tokens) or a budget (int32 [B]) are given.  Returns
+    stop_offsets [B + 1], stop_tokens), a budget (int32 [B]) or draft_probs (float32
+    [n_draft_rows, V], the draft distributions in place of draft logits) are given.  Returns
     (accepted_len, out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag)
     and, with stop lists or a budget, "emitted_len".  ``events``: up to four torch.cuda.Event
     objects recorded before the first kernel and after each kernel.
     """
-    _check(target, draft, draft_tokens, offsets, temperature)
+    _check(target, draft, draft_tokens, offsets, temperature, draft_probs)
     dev = target.device
     B = offsets.shape[0] - 1
     profile = _profile_arrays(temperature, seed, B, dev)
@@ -121,7 +127,7 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
         stop_tokens = stop_tokens if stop_tokens is not None else torch.empty(0, dtype=torch.int32, device=dev)
         stop_tokens = _device_vector(stop_tokens, torch.int32, stop_tokens.shape[0], dev, "stop_tokens")
     budget = _device_vector(budget, torch.int32, B, dev, "budget")
-    use_opts = accept_uniform is not None or stop_offsets is not None or budget is not None
+    use_opts = accept_uniform is not None or stop_offsets is not None or budget is not None or draft_probs is not None
     n_d = draft_tokens.shape[0]
     V = target.shape[1]
     dt = _DTYPES[target.dtype]
@@ -156,6 +162,7 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
             if profile is not None:
                 opt.temperature, opt.seed = _ptr(profile[0]), _ptr(profile[1])
             opt.accept_uniform, opt.draw_uniform = _ptr(accept_uniform), _ptr(draw_uniform)
+            opt.draft_probs = _ptr(draft_probs)
             if stop_offsets is not None:
                 opt.stop_offsets, opt.stop_tokens = _ptr(stop_offsets), _ptr(stop_tokens)
                 opt.n_stop_tokens = stop_tokens.shape[0]

@@ -44,6 +44,7 @@ class SdvOptions(ctypes.Structure):
         ("n_stop_tokens", ctypes.c_int64),
         ("budget", ctypes.c_void_p),
         ("emitted_len", ctypes.c_void_p),
+        ("draft_probs", ctypes.c_void_p),
     ]
 
 

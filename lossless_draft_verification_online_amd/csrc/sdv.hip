@@ -66,6 +66,7 @@ struct Params {
   int64_t n_stop;
   const int32_t* budget;      // [B] remaining output tokens, or null: no limit
   int32_t* emitted_len;       // [B] out: tokens emitted after truncation, or null
+  const float* qrows;         // [n_d][V] draft distributions (binary32) in place of draft logits, or null
   DiagPtrs dg;
 };
 
@@ -225,53 +226,21 @@ __device__ __forceinline__ float resid_weight(float zt, float zd, float k2, floa
   return fmaxf(fmaf(-q, q_scale, p), 0.0f);
 }
 
-// Inverse CDF inside one chunk: the smallest v in [c0, c0 + n) whose running mass exceeds target.
-// Step 1: lane l sums the weights of its contiguous run [c0 + l*run, c0 + (l+1)*run) (16 vector
-// loads); a wave scan of the run totals (fp64) picks the run that crosses the target.  Step 2: the
-// wave re-reads that run, each lane taking run/64 consecutive elements, and a second scan picks the
-// element.  If rounding leaves the target unreached, the last element of positive weight is taken.
-template <class E, bool kVec, bool kResid>
-__device__ __forceinline__ int32_t search_chunk(const char* trow, const char* drow, int32_t c0, int32_t n, double target,
-                                float k2, float ref_t, float e_hi, float q_scale, int lane) {
+// Inverse CDF inside one chunk, element by element (rows that are not 16-byte aligned): the
+// smallest v in [c0, c0 + n) whose running mass exceeds target; weight(v) gives the weight of
+// element v.  Step 1: lane l sums the weights of its contiguous run [c0 + l*run, c0 + (l+1)*run); a
+// wave scan of the run totals (fp64) picks the run that crosses the target.  Step 2: each lane takes
+// run/64 consecutive elements of that run, and a second scan picks the element.  If rounding leaves
+// the target unreached, the last element of positive weight is taken.
+template <class E, class Weight>
+__device__ __forceinline__ int32_t search_chunk(int32_t c0, int32_t n, double target, Weight weight, int lane) {
   constexpr int run = kVecPerLane * E::kPerVec;  // 128 bf16 or 64 fp32 elements
   constexpr int per_lane = run / kWave;          // 2 or 1 elements per lane in step 2
-  auto weight = [&](float zt, float zd) -> float {
-    if constexpr (kResid) return resid_weight(zt, zd, k2, ref_t, e_hi, q_scale);
-    return fast_exp2(fmaf(zt, k2, -ref_t));
-  };
   const int32_t end = c0 + n;
   // step 1: run totals
   const int32_t b = c0 + lane * run;
   double tot = 0.0;
-  if constexpr (kVec) {
-    const u32x4* tp = reinterpret_cast<const u32x4*>(trow + (int64_t)b * E::kBytes);
-    const u32x4* dp = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)b * E::kBytes);
-    constexpr int kHalf = kVecPerLane / 2;  // two halves bound the registers held per lane
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      asm volatile("" ::: "memory");  // keep the second half's loads after the first half's use
-      u32x4 tb[kHalf], db[kHalf];
-#pragma unroll
-      for (int k = 0; k < kHalf; ++k) {
-        // vectors of this lane's run that lie inside the chunk: (end - b) / kPerVec of them
-        const int32_t nv = max((end - b) / E::kPerVec, 1);
-        tb[k] = (end - b) > 0 ? load_vec<E>(tp, h * kHalf + k, nv) : neg_inf_vec<E>();
-        if constexpr (kResid) db[k] = (end - b) > 0 ? load_vec<E>(dp, h * kHalf + k, nv) : neg_inf_vec<E>();
-      }
-#pragma unroll
-      for (int k = 0; k < kHalf; ++k) {
-        float ft[E::kPerVec], fd[E::kPerVec];
-        E::unpack(tb[k], ft);
-        if constexpr (kResid) E::unpack(db[k], fd);
-#pragma unroll
-        for (int q = 0; q < E::kPerVec; ++q) ft[q] = weight(ft[q], kResid ? fd[q] : 0.0f);
-        tot += (double)tree_sum(ft);
-      }
-    }
-  } else {
-    for (int32_t v = b; v < min(b + run, end); ++v)
-      tot += (double)weight(E::at(trow, v), kResid ? E::at(drow, v) : 0.0f);
-  }
+  for (int32_t v = b; v < min(b + run, end); ++v) tot += (double)weight(v);
   const double before = wave_exclusive_scan(tot, lane);
   const uint64_t hit = __ballot(b < end && before + tot > target);
   const uint64_t pos = __ballot(b < end && tot > 0.0);
@@ -286,7 +255,7 @@ __device__ __forceinline__ int32_t search_chunk(const char* trow, const char* dr
 #pragma unroll
   for (int q = 0; q < per_lane; ++q) {
     const int32_t v = bf + lane * per_lane + q;
-    w[q] = v < end ? weight(E::at(trow, v), kResid ? E::at(drow, v) : 0.0f) : 0.0f;
+    w[q] = v < end ? weight(v) : 0.0f;
     sub += (double)w[q];
   }
   const double sub_before = wave_exclusive_scan(sub, lane);
@@ -583,6 +552,168 @@ __device__ __forceinline__ int32_t search_chunk_block(const char* trow, const ch
   return __shfl(yl, l, kWave);
 }
 
+// ============================================================================ probability-row drafts
+// The draft side given as the distributions themselves (SDCP's q_rows: V binary32 values per
+// proposed position).  Weights live in the frame 2^(z_t k - ref_t) of the target row; q enters it
+// through q_scale = 2^(l2_t - ref_t).
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float resid_weight_q(float zt, float qv, float k2, float ref_t, float q_scale) {
+  const float p = fast_exp2(fmaf(zt, k2, -ref_t));
+  return fmaxf(fmaf(-qv, q_scale, p), 0.0f);
+}
+
+// Residual chunk masses of a (target row, q row) pair by the waves of one workgroup (16-byte
+// aligned rows).  Wave w takes full chunks w, w + n_waves, ... in quarters: the loads of the next
+// quarter are issued before the current one is reduced.  The partial last chunk, if any, is summed
+// element by element by the wave that owns it.
+template <class E>
+__device__ __forceinline__ void resid_masses_q(const char* tp, const float* qp, int32_t V, int32_t C, float k2,
+                                               float ref_t, float q_scale, double* lds_mass, int lane, int wave,
+                                               int n_waves) {
+  constexpr int kQuarter = kVecPerLane / 4;  // target vectors per lane in a quarter chunk
+  constexpr int kQV = E::kPerVec / 4;        // q vectors under one target vector
+  struct Stage {
+    u32x4 t[kQuarter];
+    f32x4 q[kQuarter][kQV];
+  };
+  const int32_t C_full = V / E::kChunk;
+  auto chunk_of = [&](int32_t s) { return wave + (s >> 2) * n_waves; };
+  auto load = [&](int32_t s, Stage& st) {
+    const int32_t c0 = chunk_of(s) * E::kChunk;
+    const int h = s & 3;
+    const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
+    const f32x4* qv = reinterpret_cast<const f32x4*>(qp + c0);
+#pragma unroll
+    for (int k = 0; k < kQuarter; ++k) {
+      const int vi = lane + kWave * (h * kQuarter + k);
+      st.t[k] = tv[vi];
+#pragma unroll
+      for (int m = 0; m < kQV; ++m) st.q[k][m] = qv[vi * kQV + m];
+    }
+  };
+  auto reduce = [&](const Stage& st) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < kQuarter; ++k) {
+      float ft[E::kPerVec], w[E::kPerVec];
+      E::unpack(st.t[k], ft);
+#pragma unroll
+      for (int m = 0; m < kQV; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * m + e] = resid_weight_q(ft[4 * m + e], st.q[k][m][e], k2, ref_t, q_scale);
+      acc += (double)tree_sum(w);
+    }
+    return acc;
+  };
+  const int32_t n_mine = C_full > wave ? (C_full - wave + n_waves - 1) / n_waves : 0;
+  const int32_t steps = 4 * n_mine;  // a multiple of 4: steps come in pairs
+  Stage A, Bs;
+  double acc = 0.0;
+  if (steps > 0) load(0, A);
+  for (int32_t s = 0; s < steps; s += 2) {
+    load(s + 1, Bs);
+    asm volatile("" ::: "memory");  // the next quarter is in flight while this one is reduced
+    acc += reduce(A);
+    asm volatile("" : "+v"(acc)::"memory");
+    if (s + 2 < steps) load(s + 2, A);
+    asm volatile("" ::: "memory");
+    acc += reduce(Bs);
+    asm volatile("" : "+v"(acc)::"memory");
+    if (((s + 1) & 3) == 3) {  // four quarters: the chunk is complete
+      acc = wave_sum(acc);
+      if (lane == 0) lds_mass[chunk_of(s + 1)] = acc;
+      acc = 0.0;
+    }
+  }
+  if (C_full < C && C_full % n_waves == wave) {  // the partial last chunk
+    const int32_t c0 = C_full * E::kChunk;
+    double m = 0.0;
+    for (int32_t v = c0 + lane; v < V; v += kWave) m += (double)resid_weight_q(E::at(tp, v), qp[v], k2, ref_t, q_scale);
+    m = wave_sum(m);
+    if (lane == 0) lds_mass[C_full] = m;
+  }
+}
+
+// Inverse CDF inside one chunk of a (target row, q row) pair by a whole workgroup (16-byte aligned
+// rows), laid out as the logit version: rows of 64 vectors, wave w sums rows w and w + n_waves, a
+// scan of the row sums picks the row, the owning wave scans its vector sums and walks the vector.
+// Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
+template <class E>
+__device__ __forceinline__ int32_t search_chunk_q_block(const char* trow, const float* qrow, int32_t c0, int32_t n,
+                                                        double target, float k2, float ref_t, float q_scale,
+                                                        double* scratch, int lane, int wave, int n_waves) {
+  constexpr int kRows = kVecPerLane;
+  constexpr int kQV = E::kPerVec / 4;
+  const int32_t nvec = n / E::kPerVec;
+  const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
+  const f32x4* qv = reinterpret_cast<const f32x4*>(qrow + c0);
+  auto weights = [&](const u32x4& t, const f32x4 (&q)[kQV], float (&w)[E::kPerVec]) {
+    float ft[E::kPerVec];
+    E::unpack(t, ft);
+#pragma unroll
+    for (int m = 0; m < kQV; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[4 * m + e] = resid_weight_q(ft[4 * m + e], q[m][e], k2, ref_t, q_scale);
+  };
+  u32x4 t[2];
+  f32x4 q[2][kQV];
+  float vs[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = wave + j * n_waves;
+    const int vi = row * kWave + lane;
+    const bool in = row < kRows && vi < nvec;
+    t[j] = in ? tv[vi] : neg_inf_vec<E>();
+#pragma unroll
+    for (int m = 0; m < kQV; ++m) q[j][m] = in ? qv[vi * kQV + m] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float w[E::kPerVec];
+    weights(t[j], q[j], w);
+    vs[j] = tree_sum(w);
+    const double rs = wave_sum((double)vs[j]);
+    if (lane == 0 && wave + j * n_waves < kRows) scratch[wave + j * n_waves] = rs;
+  }
+  __syncthreads();
+  const double rsum = lane < kRows ? scratch[lane] : 0.0;
+  const double rex = wave_exclusive_scan(rsum, lane);
+  const uint64_t rhit = __ballot(lane < kRows && rex + rsum > target);
+  const uint64_t rpos = __ballot(lane < kRows && rsum > 0.0);
+  if (!rhit && !rpos) return wave == 0 ? c0 + n - 1 : -1;
+  const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
+  const int owner = kr % n_waves;
+  if (wave != owner) return -1;
+  const int j = kr / n_waves;
+  const double rest = target - __shfl(rex, kr, kWave);
+  const float v = j == 0 ? vs[0] : vs[1];
+  const double vex = wave_exclusive_scan((double)v, lane);
+  const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
+  const uint64_t vpos = __ballot(v > 0.0f);
+  const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
+  float w[E::kPerVec];
+  if (j == 0) weights(t[0], q[0], w);
+  else weights(t[1], q[1], w);
+  const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+  int32_t yl = base + E::kPerVec - 1;
+  int32_t last_pos = -1;
+  double upto = vex;
+  bool found = false;
+#pragma unroll
+  for (int e = 0; e < E::kPerVec; ++e) {
+    upto += (double)w[e];
+    if (w[e] > 0.0f) last_pos = base + e;
+    if (!found && upto > rest) {
+      yl = base + e;
+      found = true;
+    }
+  }
+  if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
+  return __shfl(yl, l, kWave);
+}
+
 // ============================================================================ 2. verdicts
 
 // Row fold by one wave, lanes over chunks.  T > 0: l2 = R + log2(sum_c s_c 2^(ref_c - R)) with
@@ -672,7 +803,7 @@ struct Decision {
   double u;
 };
 
-template <class E, bool kVec>
+template <class E, bool kVec, bool kQ>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves);
@@ -684,7 +815,7 @@ constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 // The verdict of request i under one rule (k2 = log2(e)/T and the Philox key seed), by one
 // workgroup of 8 waves.  Shared memory: the folded rows, the decision, and the residual chunk masses
 // (C doubles, dynamic).  bad_profile rejects the request once its offsets have been screened.
-template <class E, bool kGreedy, bool kVec>
+template <class E, bool kGreedy, bool kVec, bool kQ>
 __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k2, uint64_t seed, bool bad_profile,
                                              double* lds_mass, RowFold* rows, Decision& dec) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -709,7 +840,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   // 1. all chunk records of the request's rows (r <= K target row r, r > K draft row r - K - 1)
   // are staged in shared memory in one pass when they fit, while wave 0 fetches the draft
   // tokens and the logits at them
-  const int n_rows = kGreedy ? K + 1 : 2 * K + 1;
+  const int n_rows = (kGreedy || kQ) ? K + 1 : 2 * K + 1;  // given q rows have no records
   const int64_t n_rec = (int64_t)n_rows * P.C;
   float2* lds_rec = reinterpret_cast<float2*>(lds_mass + P.C);
   const bool staged = n_rec <= P.lds_records;
@@ -728,7 +859,8 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     if constexpr (!kGreedy) {
       if (x >= 0 && x < P.V) {
         zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
-        zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+        // with q rows, zd carries q(x) itself
+        zd = kQ ? P.qrows[(int64_t)(drow0 + lane) * P.V + x] : E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
       }
     }
   }
@@ -770,10 +902,15 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
       Philox4 blk{0u, 0u, 0u, 0u};
       if (active) {
         ft = rows[lane];
-        fd = rows[K + 1 + lane];
-        qzero = zd == -INFINITY;
-        // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
-        ratio = exp2(((double)zt - (double)zd) * (double)k2 - (ft.l2 - fd.l2));
+        if constexpr (kQ) {  // p(x) = 2^(z_t k - l2_t), q(x) given
+          qzero = !(zd > 0.0f);
+          ratio = exp2((double)zt * (double)k2 - ft.l2) / (double)zd;
+        } else {
+          fd = rows[K + 1 + lane];
+          qzero = zd == -INFINITY;
+          // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
+          ratio = exp2(((double)zt - (double)zd) * (double)k2 - (ft.l2 - fd.l2));
+        }
         if (P.r_each) {  // the caller's r in [0, 1): SDCP Rule 2, r < p/q
           r = P.r_each[drow0 + lane];
           accept = r < ratio;
@@ -801,7 +938,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
         if (P.dg.target_lse)
           for (int j = lane; j <= K; j += kWave) P.dg.target_lse[trow0 + j] = rows[j].l2 * kLn2;
         if (active) {
-          if (P.dg.draft_lse) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
+          if (P.dg.draft_lse && !kQ) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
           if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
           if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
         }
@@ -817,9 +954,13 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
           // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and the factor 2^-(e - e_hi)
           d.kind = SDV_TERM_RESIDUAL;
           d.ref_t = __shfl(ft.ref, a, kWave);
-          const double e = (double)d.ref_t + __shfl(fd.l2, a, kWave) - __shfl(ft.l2, a, kWave);
-          d.e_hi = (float)e;
-          d.q_scale = (float)exp2((double)d.e_hi - e);
+          if constexpr (kQ) {  // q scaled into the frame: q 2^(l2_t - ref_t)
+            d.q_scale = (float)exp2(__shfl(ft.l2, a, kWave) - (double)d.ref_t);
+          } else {
+            const double e = (double)d.ref_t + __shfl(fd.l2, a, kWave) - __shfl(ft.l2, a, kWave);
+            d.e_hi = (float)e;
+            d.q_scale = (float)exp2((double)d.e_hi - e);
+          }
           d.u = P.u_each ? P.u_each[trow0 + a] : (double)__shfl(draw_uniform(blk), a, kWave);
         }
       }
@@ -827,12 +968,12 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     if (lane == 0) dec = d;
   }
   __syncthreads();
-  if constexpr (!kGreedy) draw_terminal<E, kVec>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
+  if constexpr (!kGreedy) draw_terminal<E, kVec, kQ>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
 }
 
 // One workgroup per request.  With a profile per request, the request's temperature selects the
 // rule at run time (uniformly over the workgroup).
-template <class E, int kMode, bool kVec>
+template <class E, int kMode, bool kVec, bool kQ>
 __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   extern __shared__ double lds_mass[];  // [C]
   __shared__ RowFold rows[kMaxRows];
@@ -841,15 +982,16 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   if constexpr (kMode == kModeProfiled) {
     const float k2 = k2_of(temperature_of(P.temp_each, i));
     const uint64_t seed = P.seed_each[i];
-    if (k2 > 0.0f) verdict_body<E, false, kVec>(P, i, k2, seed, false, lds_mass, rows, dec);
-    else verdict_body<E, true, kVec>(P, i, 0.0f, seed, !(k2 == 0.0f), lds_mass, rows, dec);
+    if (k2 > 0.0f) verdict_body<E, false, kVec, kQ>(P, i, k2, seed, false, lds_mass, rows, dec);
+    else verdict_body<E, true, kVec, false>(P, i, 0.0f, seed, !(k2 == 0.0f), lds_mass, rows, dec);
   } else {
-    verdict_body<E, kMode == kModeGreedy, kVec>(P, i, P.k2, P.seed, false, lds_mass, rows, dec);
+    verdict_body<E, kMode == kModeGreedy, kVec, kQ && kMode != kModeGreedy>(P, i, P.k2, P.seed, false, lds_mass, rows,
+                                                                            dec);
   }
 }
 
 // The correction or bonus draw of a request (T > 0), by the verdict workgroup.
-template <class E, bool kVec>
+template <class E, bool kVec, bool kQ>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves) {
@@ -857,10 +999,25 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const int32_t trow = trow0 + d.a;
   const char* tp = row_ptr<E>(P.target, trow, P.V);
   bool residual = d.kind == SDV_TERM_RESIDUAL;
-  const char* dp = residual ? row_ptr<E>(P.draft, drow0 + d.a, P.V) : nullptr;
+  const char* dp = residual && !kQ ? row_ptr<E>(P.draft, drow0 + d.a, P.V) : nullptr;
+  const float* qp = residual && kQ ? P.qrows + (int64_t)(drow0 + d.a) * P.V : nullptr;
 
   // residual masses of every chunk, into shared memory
-  if (residual) {
+  if (residual && kQ) {
+    if constexpr (kVec) {
+      resid_masses_q<E>(tp, qp, P.V, P.C, k2, d.ref_t, d.q_scale, lds_mass, lane, wave, n_waves);
+    } else {
+      for (int32_t c = wave; c < P.C; c += n_waves) {
+        const int32_t c0 = c * E::kChunk, c1 = min(c0 + E::kChunk, P.V);
+        double m = 0.0;
+        for (int32_t v = c0 + lane; v < c1; v += kWave)
+          m += (double)resid_weight_q(E::at(tp, v), qp[v], k2, d.ref_t, d.q_scale);
+        m = wave_sum(m);
+        if (lane == 0) lds_mass[c] = m;
+      }
+    }
+    __syncthreads();
+  } else if (residual) {
     if constexpr (kVec) {
       resid_masses_pipelined<E>(tp, dp, P.V, P.C, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
     } else {
@@ -898,14 +1055,26 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const int32_t n = min(E::kChunk, P.V - s0);
   int32_t y = -1;
   if constexpr (kVec) {
-    y = residual ? search_chunk_block<E, true>(tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C,
-                                               lane, wave, n_waves)
-                 : search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
-                                                lane, wave, n_waves);
+    if (residual && kQ)
+      y = search_chunk_q_block<E>(tp, qp, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave, n_waves);
+    else if (residual)
+      y = search_chunk_block<E, true>(tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane, wave,
+                                      n_waves);
+    else
+      y = search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C, lane, wave,
+                                       n_waves);
   } else {
     if (wave != 0) return;
-    y = residual ? search_chunk<E, false, true>(tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lane)
-                 : search_chunk<E, false, false>(tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lane);
+    const float ref_t = d.ref_t, e_hi = d.e_hi, q_scale = d.q_scale;
+    if (residual && kQ)
+      y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return resid_weight_q(E::at(tp, v), qp[v], k2, ref_t, q_scale); },
+                          lane);
+    else if (residual)
+      y = search_chunk<E>(s0, n, tgt,
+                          [&](int32_t v) { return resid_weight(E::at(tp, v), E::at(dp, v), k2, ref_t, e_hi, q_scale); },
+                          lane);
+    else
+      y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return fast_exp2(fmaf(E::at(tp, v), k2, -ref_t)); }, lane);
   }
   if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
     P.out_tokens[trow] = y;
@@ -992,7 +1161,8 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   auto record = [&](int k) {
     if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
   };
-  P.n_units = (int64_t)(kMode == kModeGreedy ? P.n_t : P.n_t + P.n_d) * P.C;
+  // the stream reads draft rows only when they are logits of a sampling rule
+  P.n_units = (int64_t)(kMode == kModeGreedy || P.qrows ? P.n_t : P.n_t + P.n_d) * P.C;
   record(0);
   hipLaunchKernelGGL((row_records<E, kMode, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
@@ -1003,7 +1173,13 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
   P.lds_records = want < room ? want : room;
   const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
-  hipLaunchKernelGGL((verdicts<E, kMode, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves), lds, stream, P);
+  const dim3 grid((unsigned)P.B), block(kWave * kVerdictWaves);
+  if constexpr (kMode != kModeGreedy) {  // the greedy rule never reads the draft side
+    if (P.qrows) hipLaunchKernelGGL((verdicts<E, kMode, kVec, true>), grid, block, lds, stream, P);
+    else hipLaunchKernelGGL((verdicts<E, kMode, kVec, false>), grid, block, lds, stream, P);
+  } else {
+    hipLaunchKernelGGL((verdicts<E, kMode, kVec, false>), grid, block, lds, stream, P);
+  }
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(2);
   return SDV_OK;
@@ -1041,21 +1217,24 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   if (n_draft_rows > 0 && !draft_tokens) return SDV_ERR_INVALID_ARG;
   float k2 = 0.0f;  // 0 selects the greedy rule
   const bool profiled = temp_each != nullptr || seed_each != nullptr;
+  const float* qrows = opt->draft_probs;
+  const bool have_draft = draft_logits != nullptr || qrows != nullptr;
   if (profiled) {
-    if (!temp_each || !seed_each || (n_draft_rows > 0 && !draft_logits)) return SDV_ERR_INVALID_ARG;
+    if (!temp_each || !seed_each || (n_draft_rows > 0 && !have_draft)) return SDV_ERR_INVALID_ARG;
   } else {
     if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;
     if (temperature > 0.0) {
       k2 = (float)(1.4426950408889634074 / temperature);  // log2(e) / T
       if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
-      if (n_draft_rows > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
+      if (n_draft_rows > 0 && !have_draft) return SDV_ERR_INVALID_ARG;
     }
   }
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % kAlign != 0) return SDV_ERR_WORKSPACE;
   const int esize = dtype == SDV_BF16 ? 2 : 4;
-  const void* draft = (profiled || k2 > 0.0f) ? draft_logits : nullptr;
+  const void* draft = (profiled || k2 > 0.0f) && !qrows ? draft_logits : nullptr;
+  const float* q = (profiled || k2 > 0.0f) ? qrows : nullptr;
   const bool vec = ((uintptr_t)target_logits % 16 == 0) && (draft == nullptr || (uintptr_t)draft % 16 == 0) &&
-                   ((int64_t)V * esize) % 16 == 0;
+                   ((int64_t)V * esize) % 16 == 0 && (q == nullptr || ((uintptr_t)q % 16 == 0 && V % 4 == 0));
   char* ws = static_cast<char*>(workspace);
   Params P{};
   P.target = target_logits;
@@ -1081,6 +1260,7 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.n_stop = opt->stop_offsets ? opt->n_stop_tokens : 0;
   P.budget = opt->budget;
   P.emitted_len = opt->emitted_len;
+  P.qrows = q;
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};

@@ -43,17 +43,21 @@ def profile_args(b, seed=None):
 def run_gpu(b, diag=(), seed=None, dev_inputs=None):
     t, d, x, cu = upload(b) if dev_inputs is None else dev_inputs
     temperature, sd = profile_args(b, seed)
-    acc, out, dg = sdv.verify_ex(t, d, x, cu, temperature, sd, diag=diag)
+    kw = {}
+    if b.qrows is not None:
+        kw["draft_probs"] = torch.from_numpy(b.qrows).to(DEV)
+    acc, out, dg = sdv.verify_ex(t, d, x, cu, temperature, sd, diag=diag, **kw)
     torch.cuda.synchronize()
     return acc.cpu().numpy(), out.cpu().numpy(), {k: v.cpu().numpy() for k, v in dg.items()}
 
 
 def run_oracle(b, seed=None):
+    kw = {} if b.qrows is None else {"draft_probs": b.qrows}
     if b.temp_each is not None:
         return oracle.verify(b.target, b.draft, b.tokens, b.cu, b.temp_each.astype(np.float64), b.seed_each,
-                             diag=True)
+                             diag=True, **kw)
     return oracle.verify(b.target, b.draft, b.tokens, b.cu, b.temperature, b.seed if seed is None else seed,
-                         diag=True)
+                         diag=True, **kw)
 
 
 def check_parity(b, seed=None, eps=1e-6, dev_inputs=None, diag=("terminal_kind",)):

@@ -1,0 +1,67 @@
+"""GPU parity of probability-row draft input (SDCP's q_rows, sdv_options.draft_probs) against the
+fp64 oracle given the same rows: verdicts bit for bit up to counted near-ties, p/q ratios to 1e-5
+relative; a zero q at a proposed token rejects that request alone."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import check_parity, log, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("V,dtype,T", [(32000, "bf16", 1.0), (20011, "bf16", 0.8), (8192, "bf16", 1.2),
+                                       (4096, "fp32", 1.0), (1001, "fp32", 0.7), (13, "fp32", 1.0)])
+def test_qrows_match_oracle(V, dtype, T):
+    rng = np.random.default_rng(V)
+    b = W.with_qrows(W.make_random(f"q_v{V}", rng.integers(0, 9, size=40), V, dtype, T, 3.0, 1.5, data_seed=V,
+                                   verify_seed=5))
+    acc, out, ref, cmp, dg = check_parity(b, diag=("ratio", "target_lse", "terminal_kind"))
+    np.testing.assert_allclose(dg["ratio"], ref["ratio"], rtol=1e-5)
+    np.testing.assert_allclose(np.exp(dg["target_lse"] - ref["target_lse"]), 1.0, rtol=1e-5)
+    log(f"  {cmp['n_excused']} near-tie excuses, {(ref['terminal_kind'] == 2).sum()} corrections")
+
+
+def test_full_size_ragged_b256_qrows():
+    check_parity(W.with_qrows(W.ragged_b256()))
+
+
+def test_qrows_with_profiles():
+    rng = np.random.default_rng(3)
+    base = W.make_random("q_prof", rng.integers(0, 9, size=64), 20011, "bf16", 1.0, 3.0, 1.0, data_seed=3,
+                         verify_seed=0, keep_draft=True)
+    t, s = W.mixed_profiles(base.B, rng, temps=(0.0, 0.9, 1.3))
+    pb = W.with_profiles(base, t, s, token_seed=4)
+    # each request's q rows at its own temperature (greedy requests: any rows, never read)
+    q = np.empty((pb.n_draft_rows, pb.V), dtype=np.float32)
+    req = np.repeat(np.arange(pb.B), pb.depths)
+    for T in np.unique(t):
+        rows = np.nonzero(t[req] == T)[0]
+        if rows.size:
+            sub = W.Batch(name="x", V=pb.V, dtype=pb.dtype, temperature=float(T) if T > 0 else 1.0, seed=0,
+                          target=pb.target, draft=pb.draft[rows], tokens=pb.tokens[rows],
+                          cu=W.offsets_from_depths([rows.size]))
+            q[rows] = W.with_qrows(sub).qrows
+    pb.qrows = q
+    pb.draft = None
+    check_parity(pb)
+
+
+def test_zero_q_at_the_token_rejects_only_that_request():
+    b = W.with_qrows(W.make_random("q_zero", [3, 4, 2], 4096, "fp32", 1.0, 2.0, 1.0, data_seed=8, verify_seed=2))
+    d = b.cu[1] + 2
+    b.qrows[d, b.tokens[d]] = 0.0
+    acc, out, dg = run_gpu(b, diag=("terminal_kind",))
+    assert acc[1] == -1 and dg["terminal_kind"][1] == -1 and (out[b.cu[1] + 1: b.cu[2] + 2] == -1).all()
+    ref = run_oracle(b)
+    assert ref["accepted_len"][1] == -1
+    for i in (0, 2):
+        s = slice(b.cu[i] + i, b.cu[i + 1] + i + 1)
+        assert acc[i] == ref["accepted_len"][i] and np.array_equal(out[s], ref["out_tokens"][s])

@@ -47,6 +47,7 @@ class Batch:
     meta: dict = field(default_factory=dict)
     temp_each: np.ndarray | None = None  # (B,) float32: one temperature per request, else None
     seed_each: np.ndarray | None = None  # (B,) uint64: one seed per request (with temp_each)
+    qrows: np.ndarray | None = None      # (n_draft_rows, V) float32 draft distributions, else None
 
     @property
     def B(self) -> int:
@@ -67,7 +68,9 @@ class Batch:
     def algorithmic_bytes(self) -> int:
         """Every logit the method needs, read once: target rows, plus the draft rows of every request
         that samples (T > 0)."""
-        if self.temp_each is not None:
+        if self.qrows is not None:  # the draft side is read where it is needed, counted per call
+            draft_rows = 0
+        elif self.temp_each is not None:
             draft_rows = int(np.sum(self.depths[self.temp_each > 0]))
         else:
             draft_rows = self.n_draft_rows if self.temperature > 0 else 0
@@ -164,6 +167,24 @@ def with_profiles(b: Batch, temps, seeds, token_seed: int) -> Batch:
     return Batch(name=b.name + "_profiled", V=b.V, dtype=b.dtype, temperature=float("nan"), seed=0,
                  target=b.target, draft=b.draft, tokens=tokens.astype(np.int32), cu=b.cu,
                  meta=dict(b.meta, token_seed=token_seed), temp_each=temps, seed_each=seeds)
+
+
+def with_qrows(b: Batch, temperature: float | None = None) -> Batch:
+    """The same batch with the draft side given as distributions (SDCP's q_rows): each row is
+    softmax(stored draft logits / T) in float64, rounded to float32; the draft tokens stay as drawn
+    from the draft logits at T (the same distribution)."""
+    if b.draft is None:
+        raise ValueError("q rows are built from the draft logits")
+    T = b.temperature if temperature is None else temperature
+    q = np.empty((b.n_draft_rows, b.V), dtype=np.float32)
+    for r0 in range(0, b.n_draft_rows, 64):
+        z = (bf16_to_f32(b.draft[r0:r0 + 64]) if b.dtype == "bf16" else b.draft[r0:r0 + 64]).astype(np.float64) / T
+        z -= z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        q[r0:r0 + 64] = e / e.sum(axis=1, keepdims=True)
+    return Batch(name=b.name + "_qrows", V=b.V, dtype=b.dtype, temperature=b.temperature, seed=b.seed,
+                 target=b.target, draft=None, tokens=b.tokens, cu=b.cu, meta=dict(b.meta),
+                 temp_each=b.temp_each, seed_each=b.seed_each, qrows=q)
 
 
 def mixed_profiles(B: int, rng: np.random.Generator, temps=(0.0, 0.6, 1.0, 1.5)) -> tuple[np.ndarray, np.ndarray]:
