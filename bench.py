@@ -13,7 +13,8 @@ one launch / its mean duration from HIP events recorded on the library's stream)
 a plain read of the same size with the row pass's loads, per-call percentiles, accepted-length
 statistics and the CPU oracle's rate on the host.
 
-  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1|ragged_b256_profiled]
+  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1|ragged_b256_profiled|
+                              ragged_b256_qrows]
                   [--steps K] [--warmup W]
 
 Profile summaries (rocprofv3 output -> text under profiles/):
@@ -65,6 +66,8 @@ def make_workload(name: str, set_index: int):
         return W.uniform_b64(data_seed=W.DATA_SEED_BASE + 3 + 1000 * set_index, verify_seed=3000)
     if name == "small_b1":
         return W.small_b1(set_index)
+    if name == "ragged_b256_qrows":  # the draft side as distributions (SDCP q_rows), float32
+        return W.with_qrows(W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000))
     if name == "ragged_b256_profiled":  # one sampling profile per request: a quarter greedy
         base = W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000)
         t, s = W.mixed_profiles(base.B, np.random.default_rng(W.DATA_SEED_BASE + 6 + set_index))
@@ -104,7 +107,8 @@ def cpu_baseline(batch, budget_s: float):
         t_end = time.perf_counter() + budget
         while True:
             t0 = time.perf_counter()
-            oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, *oracle_profile(batch))
+            oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, *oracle_profile(batch),
+                          **({} if batch.qrows is None else {"draft_probs": batch.qrows}))
             times.append(time.perf_counter() - t0)
             if len(times) >= 3 or time.perf_counter() > t_end:
                 return float(np.median(times)), len(times)
@@ -131,7 +135,18 @@ def reread_bytes(batch, acc: np.ndarray) -> int:
     chunk = min(CHUNK_BYTES, row)
     resid = int(np.sum(sampling & (acc >= 0) & (acc < K)))
     bonus = int(np.sum(sampling & (acc == K)))
+    if batch.qrows is not None:  # the q row of a correction is algorithmic; its target row is read again
+        return resid * (row + chunk) + bonus * chunk
     return resid * (2 * row + 2 * chunk) + bonus * chunk
+
+
+def qrow_bytes(batch, acc: np.ndarray) -> int:
+    """Algorithmic bytes of the draft side when it comes as q rows: the row of every correction."""
+    if batch.qrows is None:
+        return 0
+    K = batch.depths
+    sampling = batch.temp_each > 0 if batch.temp_each is not None else np.full(batch.B, batch.temperature > 0)
+    return int(np.sum(sampling & (acc >= 0) & (acc < K))) * batch.V * 4
 
 
 def acceptance_stats(batch, accs):
@@ -155,7 +170,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1",
-                                                           "ragged_b256_profiled"])
+                                                           "ragged_b256_profiled", "ragged_b256_qrows"])
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through the timed steps (0: enough for 1 GB, at least 2, at most 32)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing (0 = skip)")
@@ -186,7 +201,7 @@ def main():
     torch.cuda.set_device(dev)
     first = make_workload(args.workload, 0)
     if args.sets <= 0:  # rotate past the 256 MB memory-side cache: about 1 GB of inputs in all
-        per_set = first.target.nbytes + (first.draft.nbytes if first.draft is not None else 0)
+        per_set = first.target.nbytes + sum(x.nbytes for x in (first.draft, first.qrows) if x is not None)
         args.sets = int(min(32, max(2, -(-(1 << 30) // per_set))))
     log(f"[bench] generating {args.sets} input set(s) of {args.workload}")
     batches = [first] + [make_workload(args.workload, s) for s in range(1, args.sets)]
@@ -202,6 +217,8 @@ def main():
     for b in batches:
         sets.append(dict(target=up(b.target), draft=up(b.draft), tokens=torch.from_numpy(b.tokens).to(dev),
                          cu=torch.from_numpy(b.cu).to(dev), batch=b))
+        if b.qrows is not None:
+            sets[-1]["qrows"] = torch.from_numpy(b.qrows).to(dev)
         if b.temp_each is not None:  # one sampling profile per request, as device arrays
             sets[-1]["temp"] = torch.from_numpy(b.temp_each.astype(np.float32)).to(dev)
             sets[-1]["seeds"] = torch.from_numpy(b.seed_each.astype(np.uint64).view(np.int64)).to(dev)
@@ -209,6 +226,7 @@ def main():
     positions = [int(b.cu[-1]) for b in batches]
     rows = [int(b.cu[-1]) + b.B for b in batches]
     alg_bytes = [b.algorithmic_bytes() for b in batches]
+    stream_bytes = list(alg_bytes)  # what the row pass reads: every row it streams, once
     ws = torch.empty(max(sdv.workspace_bytes(b.B, b.n_draft_rows, b.V, sets[0]["target"].dtype) for b in batches),
                      dtype=torch.uint8, device=dev)
     outs = [(torch.empty(b.B, dtype=torch.int32, device=dev),
@@ -219,7 +237,7 @@ def main():
         b = s["batch"]
         temperature, seed = (s["temp"], s["seeds"]) if "temp" in s else (b.temperature, b.seed + k)
         sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], temperature, seed,
-                      out=outs[k % len(sets)], workspace=ws, events=events)
+                      out=outs[k % len(sets)], workspace=ws, events=events, draft_probs=s.get("qrows"))
 
     # correctness of the timed configuration, once, against the oracle
     parity = None
@@ -228,7 +246,8 @@ def main():
         log("[bench] checking one call against the oracle")
         step(0)
         torch.cuda.synchronize()
-        ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, *oracle_profile(B0), diag=True)
+        ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, *oracle_profile(B0), diag=True,
+                            **({} if B0.qrows is None else {"draft_probs": B0.qrows}))
         cmp = compare_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ref, B0.cu, oracle_profile(B0)[0])
         parity = {"requests": cmp["requests"], "hard_mismatches": cmp["n_hard"], "near_tie_excused": cmp["n_excused"]}
         if cmp["n_hard"]:
@@ -288,22 +307,26 @@ def main():
     del bufs
 
     # verdict statistics over a few more calls (untimed)
-    accs, rereads = [], []
+    accs, rereads, qbytes = [], [], [[] for _ in sets]
     for k in range(16):
         step(k)
         acc = outs[k % len(sets)][0].cpu().numpy()
         if k % len(sets) == 0:
             accs.append(acc)
         rereads.append(reread_bytes(batches[k % len(sets)], acc))
+        qbytes[k % len(sets)].append(qrow_bytes(batches[k % len(sets)], acc))
     stats = acceptance_stats(B0, accs)
+    if B0.qrows is not None:  # q rows read at the corrections are part of each call's algorithmic bytes
+        alg_bytes = [a + int(np.mean(q)) if q else a for a, q in zip(alg_bytes, qbytes)]
 
     ms_step = elapsed * 1e3 / args.steps
     mean_pos = float(np.mean([positions[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     mean_rows = float(np.mean([rows[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     mean_bytes = float(np.mean([alg_bytes[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
+    mean_stream = float(np.mean([stream_bytes[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     value = mean_pos / (ms_step * 1e-3)
     call_gbps = mean_bytes / (ms_step * 1e-3) / 1e9
-    rowpass_gbps = mean_bytes / (per_kernel[0] * 1e-3) / 1e9
+    rowpass_gbps = mean_stream / (per_kernel[0] * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -337,7 +360,7 @@ def main():
         "acceptance": stats,
         "roofline": {"bound": "hbm", "achieved": rowpass_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": rowpass_gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(args.workload),
-                     "kernel": "row_records", "algorithmic_bytes_per_launch": mean_bytes,
+                     "kernel": "row_records", "algorithmic_bytes_per_launch": mean_stream,
                      "frac_of_read_ceiling": rowpass_gbps / read_gbps},
         "parity": parity,
         "kernel_source_hash": kernel_source_hash(),

@@ -454,21 +454,28 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
     Half A, Bh;
     load(c, 0, A);
     asm volatile("" ::: "memory");
-    for (;;) {
+    // steady state: every load is unconditional (a load under a branch would leave the load counter
+    // unknown at the join and force a wait for every load in flight); the last chunk is peeled off
+    for (; c + n_waves < C_full; c += n_waves) {
       load(c, 1, Bh);
       asm volatile("" ::: "memory");  // the second half is in flight while the first is reduced
       double acc = reduce(A);
       asm volatile("" : "+v"(acc)::"memory");  // the first half is consumed before its registers reload
-      const int32_t cn = c + n_waves;
-      if (cn < C_full) load(cn, 0, A);
+      load(c + n_waves, 0, A);
       asm volatile("" ::: "memory");
       acc += reduce(Bh);
       asm volatile("" : "+v"(acc)::"memory");
       acc = wave_sum(acc);
       if (lane == 0) lds_mass[c] = acc;
-      c = cn;
-      if (c >= C_full) break;
     }
+    load(c, 1, Bh);
+    asm volatile("" ::: "memory");
+    double acc = reduce(A);
+    asm volatile("" : "+v"(acc)::"memory");
+    acc += reduce(Bh);
+    acc = wave_sum(acc);
+    if (lane == 0) lds_mass[c] = acc;
+    c += n_waves;
   }
   if (c < C) {  // the partial last chunk, if this wave owns it
     const int32_t c0 = c * E::kChunk;
@@ -564,68 +571,113 @@ __device__ __forceinline__ float resid_weight_q(float zt, float qv, float k2, fl
   return fmaxf(fmaf(-qv, q_scale, p), 0.0f);
 }
 
+// Four target elements under one 16-byte q vector: 8 bytes of bf16 or 16 bytes of fp32, so that
+// target and q loads are both contiguous across the lanes of a wave.
+template <class E>
+struct Quad;
+template <>
+struct Quad<Bf16> {
+  typedef uint32_t T __attribute__((ext_vector_type(2)));
+  __device__ static __forceinline__ void unpack(const T v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+template <>
+struct Quad<F32> {
+  typedef u32x4 T;
+  __device__ static __forceinline__ void unpack(const T v, float (&f)[4]) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+};
+
 // Residual chunk masses of a (target row, q row) pair by the waves of one workgroup (16-byte
-// aligned rows).  Wave w takes full chunks w, w + n_waves, ... in quarters: the loads of the next
-// quarter are issued before the current one is reduced.  The partial last chunk, if any, is summed
-// element by element by the wave that owns it.
+// aligned rows).  Wave w takes full chunks w, w + n_waves, ... in halves of 4-element quads
+// (quad l + 64 k for lane l): the loads of the next half are issued before the current one is
+// reduced.  The partial last chunk, if any, is summed element by element by the wave that owns it.
 template <class E>
 __device__ __forceinline__ void resid_masses_q(const char* tp, const float* qp, int32_t V, int32_t C, float k2,
                                                float ref_t, float q_scale, double* lds_mass, int lane, int wave,
                                                int n_waves) {
-  constexpr int kQuarter = kVecPerLane / 4;  // target vectors per lane in a quarter chunk
-  constexpr int kQV = E::kPerVec / 4;        // q vectors under one target vector
+  typedef typename Quad<E>::T TQ;
+  constexpr int kParts = 2;                               // stages per chunk
+  constexpr int kQuadsPerLane = E::kChunk / 4 / kWave;    // 32 (bf16) or 16 (fp32)
+  constexpr int kPart = kQuadsPerLane / kParts;           // quads per lane in one stage
   struct Stage {
-    u32x4 t[kQuarter];
-    f32x4 q[kQuarter][kQV];
+    TQ t[kPart];
+    f32x4 q[kPart];
   };
   const int32_t C_full = V / E::kChunk;
-  auto chunk_of = [&](int32_t s) { return wave + (s >> 2) * n_waves; };
+  auto chunk_of = [&](int32_t s) { return wave + (s / kParts) * n_waves; };
   auto load = [&](int32_t s, Stage& st) {
     const int32_t c0 = chunk_of(s) * E::kChunk;
-    const int h = s & 3;
-    const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
+    const int h = s % kParts;
+    const TQ* tv = reinterpret_cast<const TQ*>(tp + (int64_t)c0 * E::kBytes);
     const f32x4* qv = reinterpret_cast<const f32x4*>(qp + c0);
 #pragma unroll
-    for (int k = 0; k < kQuarter; ++k) {
-      const int vi = lane + kWave * (h * kQuarter + k);
-      st.t[k] = tv[vi];
-#pragma unroll
-      for (int m = 0; m < kQV; ++m) st.q[k][m] = qv[vi * kQV + m];
+    for (int k = 0; k < kPart; ++k) {
+      const int u = lane + kWave * (h * kPart + k);
+      st.t[k] = tv[u];
+      st.q[k] = qv[u];
     }
   };
   auto reduce = [&](const Stage& st) {
     double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < kQuarter; ++k) {
-      float ft[E::kPerVec], w[E::kPerVec];
-      E::unpack(st.t[k], ft);
+    for (int k = 0; k < kPart; k += 2) {
+      float ft[8], w[8];
+      Quad<E>::unpack(st.t[k], reinterpret_cast<float(&)[4]>(ft[0]));
+      Quad<E>::unpack(st.t[k + 1], reinterpret_cast<float(&)[4]>(ft[4]));
 #pragma unroll
-      for (int m = 0; m < kQV; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * m + e] = resid_weight_q(ft[4 * m + e], st.q[k][m][e], k2, ref_t, q_scale);
+      for (int e = 0; e < 4; ++e) {
+        w[e] = resid_weight_q(ft[e], st.q[k][e], k2, ref_t, q_scale);
+        w[4 + e] = resid_weight_q(ft[4 + e], st.q[k + 1][e], k2, ref_t, q_scale);
+      }
       acc += (double)tree_sum(w);
     }
     return acc;
   };
   const int32_t n_mine = C_full > wave ? (C_full - wave + n_waves - 1) / n_waves : 0;
-  const int32_t steps = 4 * n_mine;  // a multiple of 4: steps come in pairs
+  const int32_t steps = kParts * n_mine;  // even: steps come in pairs
   Stage A, Bs;
   double acc = 0.0;
-  if (steps > 0) load(0, A);
-  for (int32_t s = 0; s < steps; s += 2) {
-    load(s + 1, Bs);
-    asm volatile("" ::: "memory");  // the next quarter is in flight while this one is reduced
-    acc += reduce(A);
-    asm volatile("" : "+v"(acc)::"memory");
-    if (s + 2 < steps) load(s + 2, A);
-    asm volatile("" ::: "memory");
-    acc += reduce(Bs);
-    asm volatile("" : "+v"(acc)::"memory");
-    if (((s + 1) & 3) == 3) {  // four quarters: the chunk is complete
+  auto finish_chunk = [&](int32_t s) {  // after stage s: the chunk is complete when s ends a chunk
+    if ((s + 1) % kParts == 0) {
       acc = wave_sum(acc);
-      if (lane == 0) lds_mass[chunk_of(s + 1)] = acc;
+      if (lane == 0) lds_mass[chunk_of(s)] = acc;
       acc = 0.0;
     }
+  };
+  if (steps > 0) {
+    load(0, A);
+    // steady state: every load is unconditional (a load under a branch would leave the load counter
+    // unknown at the join and force a wait for every load in flight); the last pair is peeled off
+    int32_t s = 0;
+    for (; s + 2 < steps; s += 2) {
+      load(s + 1, Bs);
+      asm volatile("" ::: "memory");  // the next stage is in flight while this one is reduced
+      acc += reduce(A);
+      asm volatile("" : "+v"(acc)::"memory");
+      finish_chunk(s);
+      load(s + 2, A);
+      asm volatile("" ::: "memory");
+      acc += reduce(Bs);
+      asm volatile("" : "+v"(acc)::"memory");
+      finish_chunk(s + 1);
+    }
+    load(s + 1, Bs);
+    asm volatile("" ::: "memory");
+    acc += reduce(A);
+    asm volatile("" : "+v"(acc)::"memory");
+    finish_chunk(s);
+    acc += reduce(Bs);
+    asm volatile("" : "+v"(acc)::"memory");
+    finish_chunk(s + 1);
   }
   if (C_full < C && C_full % n_waves == wave) {  // the partial last chunk
     const int32_t c0 = C_full * E::kChunk;
@@ -818,7 +870,10 @@ constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 template <class E, bool kGreedy, bool kVec, bool kQ>
 __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k2, uint64_t seed, bool bad_profile,
                                              double* lds_mass, RowFold* rows, Decision& dec) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  // the wave index is uniform over the wave; saying so keeps every loop and load condition that
+  // depends on it a scalar branch (a lane-predicated load would force a wait for all loads in flight)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n_waves = blockDim.x / kWave;
 
   // screening: every wave reaches the same answer from the same loads
