@@ -86,6 +86,8 @@ def test_host_argument_errors(lib):
     assert _call(lib, ws=None, ws_bytes=need) == -4
     assert _call(lib, ws=FAKE + 8, ws_bytes=need) == -4  # not 256-byte aligned
     assert _call(lib, B=2**31 - 1, n_d=2**31 - 2, ws_bytes=2**62) == -3
+    assert lib.sdv_workspace_bytes(2, 8, 4096 * 8192 + 1, 0) == 0  # more than 4096 chunks per row
+    assert _call(lib, V=4096 * 8192 + 1, ws_bytes=2**40) == -3
     assert lib.sdv_philox4x32_10(None, FAKE, 4, FAKE, None) == -1
     assert lib.sdv_philox4x32_10(FAKE, FAKE, 0, FAKE, None) == -1
     assert lib.sdv_read_ceiling(None, 4, FAKE, None) == -1

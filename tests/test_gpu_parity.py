@@ -208,3 +208,28 @@ def test_read_ceiling_folds_every_word():
     got = sdv.read_ceiling(torch.from_numpy(words.view(np.int32)).to(DEV)).cpu().numpy().view(np.uint32)
     want = np.bitwise_xor.reduce(words.reshape(n_chunks, 4096), axis=1)
     assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------- size edges
+
+@pytest.mark.parametrize("V,dtype", [(262144, "bf16"), (128255, "bf16"), (151936, "fp32")])
+def test_large_and_odd_vocabularies(V, dtype):
+    """32 chunks per row (4 per wave in the residual pass), an odd vocabulary on the element-wise
+    path, and fp32 rows at the greedy workload's width."""
+    rng = np.random.default_rng(V % 1000)
+    b = W.make_random(f"v{V}_{dtype}", rng.integers(0, 9, size=24), V, dtype, 1.0, 3.0, rng.uniform(0.5, 3, 24),
+                      data_seed=V, verify_seed=11)
+    check_parity(b, diag=("terminal_kind", "target_lse"))
+
+
+def test_one_request_at_full_depth_and_width():
+    b = W.make_random("b1_k64_v128256", [64], 128256, "bf16", 1.0, 3.0, 0.3, data_seed=64, verify_seed=64)
+    acc, out, ref, cmp, _ = check_parity(b)
+    log(f"  accepted {acc[0]} of 64")
+
+
+def test_every_request_without_drafts_at_full_width():
+    b = W.make_random("b256_k0_v128256", np.zeros(256, dtype=int), 128256, "bf16", 1.0, 3.0, 1.0, data_seed=3,
+                      verify_seed=3)
+    acc, out, ref, cmp, dg = check_parity(b, diag=("terminal_kind",))
+    assert (acc == 0).all() and (dg["terminal_kind"] == 1).all()
