@@ -46,6 +46,9 @@ class _Options(ctypes.Structure):
         ("budget", ctypes.c_void_p),
         ("emitted_len", ctypes.c_void_p),
         ("draft_probs", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p),
+        ("top_p_milli", ctypes.c_void_p),
+        ("kept_tokens", ctypes.c_void_p),
     ]
 
 
@@ -59,6 +62,7 @@ class _Diag(ctypes.Structure):
         ("cdf_margin", ctypes.c_void_p),
         ("resid_mass", ctypes.c_void_p),
         ("terminal_kind", ctypes.c_void_p),
+        ("filter_margin", ctypes.c_void_p),
     ]
 
 
@@ -99,6 +103,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.oracle_row_lse.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
     lib.oracle_row_argmax.restype = ctypes.c_int32
     lib.oracle_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32]
+    lib.oracle_truncate_row.restype = ctypes.c_int32
+    lib.oracle_truncate_row.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_int64,
+        ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+    ]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_set_num_threads.restype = None
@@ -128,7 +137,8 @@ def stop_csr(stop_lists) -> tuple[np.ndarray, np.ndarray]:
 
 def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, cu: np.ndarray,
            temperature, seed, diag: bool = False, lib_path: str = LIBRARY, *, accept_uniform=None,
-           draw_uniform=None, stop_lists=None, budget=None, draft_probs=None) -> dict:
+           draw_uniform=None, stop_lists=None, budget=None, draft_probs=None, top_k=None,
+           top_p_milli=None) -> dict:
     """Run the oracle on one ragged batch.
 
     target: (n_draft_rows + B, V); draft: (n_draft_rows, V) or None when temperature == 0;
@@ -136,10 +146,13 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
     temperature and seed are scalars, or arrays of B values (one sampling profile per request).
     accept_uniform (n_draft_rows,) / draw_uniform (n_draft_rows + B,): the caller's uniforms in
     [0, 1), both or neither; stop_lists: B lists of stop tokens; budget: (B,) remaining outputs;
-    draft_probs: (n_draft_rows, V) float32 draft distributions used in place of the draft logits.
+    draft_probs: (n_draft_rows, V) float32 draft distributions used in place of the draft logits;
+    top_k / top_p_milli: (B,) the rest of each request's sampling profile (0 and 1000: no
+    truncation).
     Returns accepted_len (B,), out_tokens (n_draft_rows + B,), emitted_len (B,) when stops or a
-    budget are given, and with ``diag`` the per-row LSEs, argmaxes, ratios, margins, residual
-    masses and terminal kinds.
+    budget are given, kept_tokens (n_draft_rows + B + n_draft_rows,) when top-k / top-p are given,
+    and with ``diag`` the per-row LSEs, argmaxes, ratios, margins (filter_margin per row),
+    residual masses and terminal kinds.
     """
     lib = load(lib_path)
     target = np.ascontiguousarray(target)
@@ -166,11 +179,12 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
             target_argmax=np.full(n_t, -1, dtype=np.int32), ratio=np.full(n_d, np.nan),
             accept_margin=np.full(n_d, np.nan), cdf_margin=np.full(B, np.nan),
             resid_mass=np.full(B, np.nan), terminal_kind=np.full(B, -9, dtype=np.int32),
+            filter_margin=np.full(n_t + n_d, np.inf),
         )
         dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
         dg_p = ctypes.pointer(dg)
     extras = (accept_uniform is not None or draw_uniform is not None or stop_lists is not None or budget is not None
-              or draft_probs is not None)
+              or draft_probs is not None or top_k is not None or top_p_milli is not None)
     if extras:
         keep = []  # arrays the options point into stay alive for the call
 
@@ -198,6 +212,13 @@ def verify(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarra
             opt.budget = arr(budget, np.int32, B)
         if draft_probs is not None:
             opt.draft_probs = arr(draft_probs, np.float32, n_d * V)
+        if top_k is not None:
+            opt.top_k = arr(np.broadcast_to(np.asarray(top_k, dtype=np.int32), (B,)), np.int32, B)
+        if top_p_milli is not None:
+            opt.top_p_milli = arr(np.broadcast_to(np.asarray(top_p_milli, dtype=np.int32), (B,)), np.int32, B)
+        if top_k is not None or top_p_milli is not None:
+            res["kept_tokens"] = np.full(n_d + B + n_d, -7, dtype=np.int32)
+            opt.kept_tokens = _ptr(res["kept_tokens"])
         res["emitted_len"] = np.full(B, -7, dtype=np.int32)
         opt.emitted_len = _ptr(res["emitted_len"])
         rc = lib.oracle_verify_opts(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(cu), B, n_d, V,
@@ -250,6 +271,21 @@ def row_lse(row: np.ndarray, temperature: float) -> float:
 def row_argmax(row: np.ndarray) -> int:
     row = np.ascontiguousarray(row)
     return load().oracle_row_argmax(_ptr(row), _dtype_code(row), 0, row.shape[-1])
+
+
+def truncate_row(row: np.ndarray, temperature: float, top_k: int = 0, top_p_milli: int = 1000,
+                 lib_path: str = LIBRARY) -> dict:
+    """The tokens one row keeps under a sampling profile: keep (V,) bool, n kept, lse_kept =
+    ln sum over kept tokens of exp(z / T), and the top-p decision margin."""
+    row = np.ascontiguousarray(row)
+    V = row.shape[-1]
+    keep = np.zeros(V, dtype=np.uint8)
+    lse, margin = ctypes.c_double(), ctypes.c_double()
+    n = load(lib_path).oracle_truncate_row(_ptr(row), _dtype_code(row), 0, V, float(temperature), int(top_k),
+                                   int(top_p_milli), _ptr(keep), ctypes.byref(lse), ctypes.byref(margin))
+    if n < 0:
+        raise MemoryError("oracle_truncate_row ran out of memory")
+    return {"keep": keep.astype(bool), "n": int(n), "lse_kept": lse.value, "margin": margin.value}
 
 
 def num_threads() -> int:

@@ -21,8 +21,10 @@
  *    position after the last draft.  A request with no drafts (K = 0) therefore draws one
  *    ordinary target token ("M7.8 - Speculative Serving", section 0x09, the K = 0 case).
  *
- *  - p and q are softmax(z / T) of the target and draft logit rows (SDCP "Session Contract":
- *    temperature is the first step of the sampling profile; top-k / top-p are not applied).
+ *  - p and q are softmax(z / T) of the target and draft logit rows, then truncated by the
+ *    request's top-k and top-p when it has them (SDCP "Session Contract": the sampling profile
+ *    applies temperature, then top-k, then top-p, and p is the distribution after all three).
+ *    The draft side gets the same profile, since the drafter samples from its own row under it.
  *
  *  - Precondition (SDCP section "Verification and Commit", step 5): a proposal whose draft
  *    probability q_j(x_j) is zero at any position is rejected before any uniform is drawn.
@@ -42,6 +44,11 @@
  *    If rounding leaves no such v, y is the largest v with w_v > 0.
  *  - a residual with S = 0 (p == q exactly, which a rejection makes mathematically impossible)
  *    falls back to w = p.
+ *  - top-k / top-p rank tokens by probability, equal probabilities (equal logits) going to the
+ *    smaller token id, the one tie rule the pages state; top-k keeps the first top_k ranks (0, or
+ *    top_k >= V, keeps all); top-p keeps the shortest run of leading ranks whose mass, renormalised
+ *    over the top-k set, reaches top_p_milli / 1000, and never fewer than one token.  Given
+ *    probability rows are used as they are (the drafter has applied its profile already).
  *
  * Everything is evaluated in fp64: bf16 and fp32 inputs convert to fp64 exactly, sums run in
  * ascending token order, and the residual is formed as p_v - q_v directly.
@@ -75,6 +82,8 @@ typedef struct {
   double* cdf_margin;     /* [B]              margin of the extra-token draw, NaN when there was no draw */
   double* resid_mass;     /* [B]              S, the total weight of the extra-token draw */
   int32_t* terminal_kind; /* [B]              one of ORACLE_TERM_* */
+  double* filter_margin;  /* [n_target_rows + n_draft_rows] relative distance of each truncated row's
+                             top-p cut from its threshold; +inf where no top-p cut was taken */
 } oracle_diag;
 
 /*
@@ -93,6 +102,14 @@ typedef struct {
  *    section "Message Definitions"), used as given in place of softmax(draft logits / T); the
  *    draft logits are then not read.  A zero (or negative, or NaN) q at a proposed token rejects
  *    the request before any draw (SDCP "Verification and Commit", step 5).
+ *  - top_k [B], top_p_milli [B]: the rest of each request's sampling profile (SDCP "Session
+ *    Contract": top_k a count, top_p_milli the nucleus mass in thousandths, at most 1000).
+ *    top_k 0 and top_p_milli 1000 truncate nothing; a negative value, or top_p_milli above 1000,
+ *    describes no profile and rejects the request.  Applied to p and to the draft logits' q at
+ *    T > 0; a draft token outside q's kept set has q = 0 and rejects the request.
+ *  - kept_tokens [n_draft_rows + B + n_draft_rows] out: tokens each row keeps after truncation,
+ *    target rows first, then draft rows (V for a row that is not truncated); written for the
+ *    rows of requests at T > 0 whose profile is valid.
  */
 typedef struct {
   const double* temperature;
@@ -105,6 +122,9 @@ typedef struct {
   const int32_t* budget;
   int32_t* emitted_len;
   const float* draft_probs;
+  const int32_t* top_k;
+  const int32_t* top_p_milli;
+  int32_t* kept_tokens;
 } oracle_options;
 
 /* ---------------------------------------------------------------- Philox4x32-10 (SC'11) */
@@ -227,6 +247,79 @@ static int32_t inverse_cdf(const double* w, int32_t V, double u, double* S_out, 
   return V - 1;
 }
 
+/* ---------------------------------------------------------------- top-k / top-p */
+
+/* A token as the sampling profile ranks it: the larger logit first (the larger probability), the
+   smaller token id first among equal logits. */
+typedef struct {
+  double z;
+  int32_t v;
+} ranked_token;
+
+static int rank_order(const void* pa, const void* pb) {
+  const ranked_token* a = (const ranked_token*)pa;
+  const ranked_token* b = (const ranked_token*)pb;
+  if (a->z != b->z) return a->z > b->z ? -1 : 1;
+  return a->v < b->v ? -1 : (a->v > b->v);
+}
+
+/* A profile that truncates nothing: top_k 0 (or at least V) and top_p_milli 1000. */
+static int truncates(int64_t top_k, int32_t top_p_milli, int32_t V) {
+  return (top_k > 0 && top_k < V) || top_p_milli < 1000;
+}
+
+/*
+ * The tokens the sampling profile keeps in one row (SDCP "Session Contract": temperature, then
+ * top-k, then top-p).  The row's tokens are sorted into rank order; top-k keeps the first top_k
+ * ranks (all of them for 0 or top_k >= V); top-p then keeps the shortest run of leading ranks
+ * whose mass exp((z - m) / T), divided by the mass of the top-k set, reaches top_p_milli / 1000,
+ * and at least one token.
+ *
+ * keep [V] out: 1 for a kept token, 0 otherwise.  Returns the number of kept tokens and sets
+ * *lse_kept = ln sum over kept v of exp(z_v / T), summed in ascending v, and *margin = the
+ * distance of the top-p decision from its threshold relative to the top-k mass (+inf when top-p
+ * takes no decision).  Returns -1 if scratch memory runs out.
+ */
+int32_t oracle_truncate_row(const void* base, int dtype, int64_t row, int32_t V, double T, int64_t top_k,
+                            int32_t top_p_milli, unsigned char* keep, double* lse_kept, double* margin) {
+  ranked_token* order = (ranked_token*)malloc(sizeof(ranked_token) * (size_t)V);
+  if (!order) return -1;
+  double m = -INFINITY;
+  for (int32_t v = 0; v < V; ++v) {
+    order[v].z = logit_at(base, dtype, row, V, v);
+    order[v].v = v;
+    if (order[v].z > m) m = order[v].z;
+  }
+  qsort(order, (size_t)V, sizeof *order, rank_order);
+  int64_t n = (top_k > 0 && top_k < V) ? top_k : V;
+  *margin = INFINITY;
+  if (top_p_milli < 1000) {
+    double mass_k = 0.0;
+    for (int64_t r = 0; r < n; ++r) mass_k += exp((order[r].z - m) / T);
+    const double target = mass_k * ((double)top_p_milli / 1000.0);
+    double cum = 0.0;
+    for (int64_t r = 0; r < n; ++r) {
+      const double before = cum;
+      cum += exp((order[r].z - m) / T);
+      if (cum >= target) {
+        /* the first rank is kept whatever its mass, so only later ranks have a lower side */
+        const double over = (cum - target) / mass_k, under = (target - before) / mass_k;
+        *margin = (r == 0 || over < under) ? over : under;
+        n = r + 1;
+        break;
+      }
+    }
+  }
+  memset(keep, 0, (size_t)V);
+  for (int64_t r = 0; r < n; ++r) keep[order[r].v] = 1;
+  free(order);
+  double s = 0.0;
+  for (int32_t v = 0; v < V; ++v)
+    if (keep[v]) s += exp((logit_at(base, dtype, row, V, v) - m) / T);
+  *lse_kept = m == -INFINITY ? -INFINITY : m / T + log(s);
+  return (int32_t)n;
+}
+
 /* ---------------------------------------------------------------- one request */
 
 static void set_nan(double* p) {
@@ -261,10 +354,19 @@ static int64_t emitted_count(const oracle_options* opt, int32_t i, const int32_t
   return n;
 }
 
+/* Is token v kept in row j of a request's truncated rows?  A NULL mask keeps every token. */
+static int kept(const unsigned char* mask, int64_t j, int32_t V, int32_t v) {
+  return !mask || mask[j * (int64_t)V + v];
+}
+
+/*
+ * Request i.  n_t = n_draft_rows + B is the number of target rows (kept_tokens and filter_margin
+ * hold the draft rows after them).  w: scratch of V doubles.
+ */
 static void verify_request(const void* target, const void* draft, int dtype, const int32_t* tokens,
-                           const int32_t* cu, int32_t i, int64_t n_draft_rows, int32_t V, double T,
+                           const int32_t* cu, int32_t i, int64_t n_draft_rows, int64_t n_t, int32_t V, double T,
                            uint64_t seed, const oracle_options* opt, int32_t* accepted_len, int32_t* out_tokens,
-                           oracle_diag* dg, double* w /* scratch [V] */) {
+                           oracle_diag* dg, double* w) {
   const int64_t lo = cu[i], hi = cu[i + 1];
   const int64_t K = hi - lo;
   int32_t* emitted = opt ? opt->emitted_len : NULL;
@@ -281,30 +383,77 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   const int64_t drow0 = lo;     /* draft rows of request i:  drow0 .. drow0 + K - 1 */
   int32_t* slots = out_tokens + trow0;
 
-  /* a temperature that is negative, NaN or infinite describes no sampling profile; a stop list
-     that does not lie inside the stop-token array describes no stop set */
-  int bad = !(T >= 0.0) || isinf(T);
+  /* a temperature that is negative, NaN or infinite, a negative top_k, or a top_p_milli outside
+     [0, 1000] describes no sampling profile; a stop list that does not lie inside the stop-token
+     array describes no stop set */
+  const int64_t top_k = opt && opt->top_k ? opt->top_k[i] : 0;
+  const int32_t top_p_milli = opt && opt->top_p_milli ? opt->top_p_milli[i] : 1000;
+  int bad = !(T >= 0.0) || isinf(T) || top_k < 0 || top_p_milli < 0 || top_p_milli > 1000;
   if (opt && opt->stop_offsets) {
     const int64_t s0 = opt->stop_offsets[i], s1 = opt->stop_offsets[i + 1];
     if (s0 < 0 || s1 < s0 || s1 > opt->n_stop_tokens) bad = 1;
   }
   for (int64_t j = 0; j < K && !bad; ++j)
     if (tokens[drow0 + j] < 0 || tokens[drow0 + j] >= V) bad = 1;
-  /* q_j(x_j) = 0 exactly when the draft logit at x_j is -inf, or when the given probability at x_j
-     is not positive; checked before any draw */
+
+  /* Rule 2's rows: LSE of z/T over each row, or over its kept tokens when the profile truncates
+     (the greedy rule needs neither: the argmax is always kept) */
   const float* qrows = opt ? opt->draft_probs : NULL;
-  if (!bad && T > 0.0)
+  unsigned char* keep_t = NULL; /* [(K + 1) V] kept tokens of the target rows, NULL: all */
+  unsigned char* keep_d = NULL; /* [K V] of the draft rows */
+  double lse_t[ORACLE_MAX_DEPTH + 1], lse_d[ORACLE_MAX_DEPTH];
+  if (!bad && T > 0.0) {
+    const int cut = truncates(top_k, top_p_milli, V);
+    if (cut) {
+      keep_t = (unsigned char*)malloc((size_t)(K + 1) * (size_t)V);
+      if (!qrows && K > 0) keep_d = (unsigned char*)malloc((size_t)K * (size_t)V);
+      if (!keep_t || (!qrows && K > 0 && !keep_d)) abort(); /* test infrastructure: no partial answer */
+    }
+    for (int64_t j = 0; j <= K; ++j) {
+      double margin = INFINITY;
+      int32_t n = V;
+      if (cut)
+        n = oracle_truncate_row(target, dtype, trow0 + j, V, T, top_k, top_p_milli, keep_t + j * (int64_t)V,
+                                &lse_t[j], &margin);
+      else
+        lse_t[j] = oracle_row_lse(target, dtype, trow0 + j, V, T);
+      if (n < 0) abort();
+      if (opt && opt->kept_tokens) opt->kept_tokens[trow0 + j] = n;
+      if (dg && dg->filter_margin) dg->filter_margin[trow0 + j] = margin;
+    }
     for (int64_t j = 0; j < K; ++j) {
+      double margin = INFINITY;
+      int32_t n = V;
       if (qrows) {
-        if (!(qrows[(drow0 + j) * (int64_t)V + tokens[drow0 + j]] > 0.0f)) bad = 1;
-      } else if (logit_at(draft, dtype, drow0 + j, V, tokens[drow0 + j]) == -INFINITY) {
+        lse_d[j] = NAN;
+        continue;
+      }
+      if (cut)
+        n = oracle_truncate_row(draft, dtype, drow0 + j, V, T, top_k, top_p_milli, keep_d + j * (int64_t)V,
+                                &lse_d[j], &margin);
+      else
+        lse_d[j] = oracle_row_lse(draft, dtype, drow0 + j, V, T);
+      if (n < 0) abort();
+      if (opt && opt->kept_tokens) opt->kept_tokens[n_t + drow0 + j] = n;
+      if (dg && dg->filter_margin) dg->filter_margin[n_t + drow0 + j] = margin;
+    }
+    /* q_j(x_j) = 0 when the draft logit at x_j is -inf, when x_j is outside the kept tokens of the
+       draft row, or when the given probability at x_j is not positive; checked before any draw */
+    for (int64_t j = 0; j < K; ++j) {
+      const int32_t x = tokens[drow0 + j];
+      if (qrows) {
+        if (!(qrows[(drow0 + j) * (int64_t)V + x] > 0.0f)) bad = 1;
+      } else if (logit_at(draft, dtype, drow0 + j, V, x) == -INFINITY || !kept(keep_d, j, V, x)) {
         bad = 1;
       }
     }
+  }
   if (bad) {
     accepted_len[i] = -1;
     for (int64_t j = 0; j <= K; ++j) slots[j] = -1;
     if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_BAD;
+    free(keep_t);
+    free(keep_d);
     return;
   }
 
@@ -329,9 +478,6 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   }
 
   /* ---- Rule 2 */
-  double lse_t[ORACLE_MAX_DEPTH + 1], lse_d[ORACLE_MAX_DEPTH];
-  for (int64_t j = 0; j <= K; ++j) lse_t[j] = oracle_row_lse(target, dtype, trow0 + j, V, T);
-  for (int64_t j = 0; j < K; ++j) lse_d[j] = qrows ? NAN : oracle_row_lse(draft, dtype, drow0 + j, V, T);
   if (dg) {
     for (int64_t j = 0; j <= K; ++j)
       if (dg->target_lse) dg->target_lse[trow0 + j] = lse_t[j];
@@ -344,8 +490,10 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   int64_t a = K;
   for (int64_t j = 0; j < K; ++j) {
     const int32_t x = tokens[drow0 + j];
-    double ratio; /* p_j(x) / q_j(x) */
-    if (qrows) {
+    double ratio; /* p_j(x) / q_j(x); p_j(x) = 0 for a token the target row does not keep */
+    if (!kept(keep_t, j, V, x)) {
+      ratio = 0.0;
+    } else if (qrows) {
       ratio = exp(logit_at(target, dtype, trow0 + j, V, x) / T - lse_t[j]) / (double)qrows[(drow0 + j) * (int64_t)V + x];
     } else {
       const double log_ratio =
@@ -376,6 +524,8 @@ static void verify_request(const void* target, const void* draft, int dtype, con
   if (n_emit < a + 1) { /* emission stops inside the accepted drafts: no extra token is drawn */
     for (int64_t j = 0; j <= K; ++j) slots[j] = j < n_emit ? tokens[drow0 + j] : -1;
     if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_NONE;
+    free(keep_t);
+    free(keep_d);
     return;
   }
   double u;
@@ -391,19 +541,21 @@ static void verify_request(const void* target, const void* draft, int dtype, con
     kind = ORACLE_TERM_RESIDUAL;
     double S = 0.0;
     for (int32_t v = 0; v < V; ++v) {
-      const double p = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
+      const double p = kept(keep_t, t, V, v) ? exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) : 0.0;
       const double q = qrows ? (double)qrows[(drow0 + t) * (int64_t)V + v]
-                             : exp(logit_at(draft, dtype, drow0 + t, V, v) / T - lse_d[t]);
+                             : (kept(keep_d, t, V, v) ? exp(logit_at(draft, dtype, drow0 + t, V, v) / T - lse_d[t]) : 0.0);
       w[v] = p > q ? p - q : 0.0;
       S += w[v];
     }
     if (!(S > 0.0)) {
       kind = ORACLE_TERM_RESIDUAL_EMPTY;
-      for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
+      for (int32_t v = 0; v < V; ++v)
+        w[v] = kept(keep_t, t, V, v) ? exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) : 0.0;
     }
   } else {
     kind = ORACLE_TERM_BONUS;
-    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);
+    for (int32_t v = 0; v < V; ++v)
+      w[v] = kept(keep_t, t, V, v) ? exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) : 0.0;
   }
   double S, margin;
   const int32_t y = inverse_cdf(w, V, u, &S, &margin);
@@ -416,6 +568,8 @@ static void verify_request(const void* target, const void* draft, int dtype, con
     if (dg->resid_mass) dg->resid_mass[i] = S;
     if (dg->terminal_kind) dg->terminal_kind[i] = kind;
   }
+  free(keep_t);
+  free(keep_d);
 }
 
 /* ---------------------------------------------------------------- batch entry point */
@@ -442,7 +596,8 @@ static int verify_batch(const void* target, const void* draft, int dtype, const 
 #pragma omp for schedule(dynamic, 1)
     for (int32_t i = 0; i < B; ++i)
       if (w)
-        verify_request(target, draft, dtype, draft_tokens, cu, i, n_draft_rows, V, T_each ? T_each[i] : T,
+        verify_request(target, draft, dtype, draft_tokens, cu, i, n_draft_rows, n_draft_rows + B, V,
+                       T_each ? T_each[i] : T,
                        seed_each ? seed_each[i] : seed, opt, accepted_len, out_tokens, diag, w);
     free(w);
   }
@@ -491,7 +646,7 @@ int oracle_verify_profiled(const void* target, const void* draft, int dtype, con
                            const int32_t* cu, int32_t B, int64_t n_draft_rows, int32_t V, const double* temperature,
                            const uint64_t* seed, int32_t* accepted_len, int32_t* out_tokens, oracle_diag* diag) {
   if (!temperature || !seed) return -1;
-  oracle_options opt = {temperature, seed, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL};
+  oracle_options opt = {temperature, seed, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL};
   return oracle_verify_opts(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, 0.0, 0, &opt, accepted_len,
                             out_tokens, diag);
 }

@@ -2,8 +2,9 @@
 
 Each case plants one mistake in a copy of the oracle's C source (on the CPU only), builds it, and
 checks that at least one pin fails: the Monte Carlo against the exact enumeration, the
-closed-form LSE, the planted argmax tie, the rocRAND Philox values, or the per-request profile
-check (each request of a profiled batch against the scalar run with its own profile).
+closed-form LSE, the planted argmax tie, the rocRAND Philox values, the per-request profile
+check (each request of a profiled batch against the scalar run with its own profile), or the
+top-k / top-p pins of filter_pins.py.
 """
 import ctypes
 import os
@@ -14,6 +15,7 @@ import numpy as np
 import pytest
 from scipy import stats
 
+import filter_pins
 from oracle import exact, oracle
 from workloads import offsets_from_depths
 
@@ -30,19 +32,37 @@ MUTATIONS = {
     "frontier_drawn_after_stop": ("if (n_emit < a + 1) {", "if (n_emit < a) {"),
     "caller_draw_uniform_of_first_position": ("u = opt->draw_uniform[trow0 + t];", "u = opt->draw_uniform[trow0];"),
     "lse_drops_max": ("return m / T + log(s);", "return log(s);"),
-    "residual_from_next_row": ("const double p = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);",
+    "residual_from_next_row": ("const double p = kept(keep_t, t, V, v) ? exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) : 0.0;",
                                "const double p = exp(logit_at(target, dtype, trow0 + t + 1, V, v) / T - lse_t[t + 1]);"),
-    "bonus_from_draft_side": ("kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]);",
-                              "kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v) w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) * (v + 1);"),
+    "bonus_from_draft_side": ("      w[v] = kept(keep_t, t, V, v) ? exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) : 0.0;\n  }\n  double S, margin;",
+                              "      w[v] = exp(logit_at(target, dtype, trow0 + t, V, v) / T - lse_t[t]) * (v + 1);\n  }\n  double S, margin;"),
     "greedy_tie_to_largest": ("if (z > best_z) {", "if (z >= best_z) {"),
     "philox_key_bumped_every_round": ("if (round > 0) {", "if (round >= 0) {"),
     "profile_temperature_of_first_request": ("T_each ? T_each[i] : T", "T_each ? T_each[0] : T"),
     "profile_seed_of_next_request": ("seed_each ? seed_each[i] : seed", "seed_each ? seed_each[(i + 1) % B] : seed"),
-    "profile_invalid_temperature_accepted": ("int bad = !(T >= 0.0) || isinf(T);", "int bad = 0;"),
+    "profile_invalid_temperature_accepted": ("int bad = !(T >= 0.0) || isinf(T) ||", "int bad = 0 ||"),
     "qrows_ratio_not_divided": ("lse_t[j]) / (double)qrows[(drow0 + j) * (int64_t)V + x];", "lse_t[j]);"),
     "qrows_residual_from_wrong_row": ("const double q = qrows ? (double)qrows[(drow0 + t) * (int64_t)V + v]",
                                       "const double q = qrows ? (double)qrows[(drow0 + (t > 0 ? t - 1 : t + 1)) * (int64_t)V + v]"),
     "temperature_ignored": ("drow0 + j, V, x)) / T - (lse_t[j] - lse_d[j]);", "drow0 + j, V, x)) - (lse_t[j] - lse_d[j]);"),
+    # top-k / top-p
+    "rank_ties_to_larger_id": ("return a->v < b->v ? -1 : (a->v > b->v);", "return a->v > b->v ? -1 : (a->v < b->v);"),
+    "top_k_off_by_one": ("int64_t n = (top_k > 0 && top_k < V) ? top_k : V;",
+                         "int64_t n = (top_k > 0 && top_k < V) ? top_k + 1 : V;"),
+    "top_p_exceeds_instead_of_reaches": ("if (cum >= target) {", "if (cum > target) {"),
+    "top_p_not_renormalised_by_top_k": ("for (int64_t r = 0; r < n; ++r) mass_k += exp((order[r].z - m) / T);",
+                                        "for (int64_t r = 0; r < V; ++r) mass_k += exp((order[r].z - m) / T);"),
+    "truncated_target_not_renormalised": ("      if (n < 0) abort();\n      if (opt && opt->kept_tokens) opt->kept_tokens[trow0 + j] = n;",
+                                          "      if (n < 0) abort();\n      lse_t[j] = oracle_row_lse(target, dtype, trow0 + j, V, T);\n"
+                                          "      if (opt && opt->kept_tokens) opt->kept_tokens[trow0 + j] = n;"),
+    "truncated_draft_not_renormalised": ("      if (n < 0) abort();\n      if (opt && opt->kept_tokens) opt->kept_tokens[n_t + drow0 + j] = n;",
+                                         "      if (n < 0) abort();\n      lse_d[j] = oracle_row_lse(draft, dtype, drow0 + j, V, T);\n"
+                                         "      if (opt && opt->kept_tokens) opt->kept_tokens[n_t + drow0 + j] = n;"),
+    "ratio_ignores_target_cut": ("if (!kept(keep_t, j, V, x)) {\n      ratio = 0.0;", "if (0) {\n      ratio = 0.0;"),
+    "bonus_from_untruncated_p": ("kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v)\n      w[v] = kept(keep_t, t, V, v) ?",
+                                 "kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v)\n      w[v] = 1 ?"),
+    "residual_from_untruncated_q": (": (kept(keep_d, t, V, v) ? exp(", ": (1 ? exp("),
+    "invalid_top_p_accepted": ("top_p_milli < 0 || top_p_milli > 1000;", "top_p_milli < 0;"),
 }
 
 
@@ -207,8 +227,13 @@ def _pin_qrows(lib_path):
     return compare_verdicts(got["accepted_len"], got["out_tokens"], ref, cu, 1.0)["n_hard"] == 0
 
 
+def _pin_filters(lib_path):
+    """Every top-k / top-p pin of tests/filter_pins.py."""
+    return all(check(lib_path) for check in filter_pins.ALL)
+
+
 def test_unmutated_oracle_passes_every_pin(tmp_path):
-    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops, _pin_qrows):
+    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops, _pin_qrows, _pin_filters):
         assert check(oracle.LIBRARY)
     assert _pin_philox(oracle.LIBRARY, tmp_path)
 
@@ -226,5 +251,6 @@ def test_planted_mistake_is_caught(tmp_path, name):
         "profiles": _pin_profiles(lib),
         "stops_and_caller_uniforms": _pin_stops(lib),
         "qrows": _pin_qrows(lib),
+        "top_k_top_p": _pin_filters(lib),
     }
     assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"
