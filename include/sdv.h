@@ -12,8 +12,9 @@
  *  - Rule 1 (temperature 0) and Rule 2 (temperature > 0) of "Speculative Decoding Coordination
  *    Protocol (SDCP)", section "Acceptance Rules"; the accept test r <= p(x)/q(x) of "SOTA-227:
  *    Decode with a draft model and an accept-reject rule, which is exactly lossless", section
- *    "What to do".  p and q are softmax(z/T) of the target and draft logit rows (SDCP section
- *    "Session Contract": temperature, then top-k / top-p, which this library does not apply).
+ *    "What to do".  p and q are softmax(z/T) of the target and draft logit rows, truncated by
+ *    top-k and top-p when sdv_options carries them (SDCP section "Session Contract": the sampling
+ *    profile applies temperature, then top-k, then top-p).
  *  - Ragged batches ("M7.8 - Speculative Serving", section 0x00, background on the serving unit,
  *    N_query = sum_i (K_i + 1)):
  *    request i has K_i = cu[i+1] - cu[i] draft tokens, 0 <= K_i <= 64 (SDCP m_max <= 64).
@@ -36,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 1
+#define SDV_ABI_VERSION 2
 #define SDV_MAX_DEPTH 64 /* largest K_i a request may carry */
 #define SDV_MAX_EVENTS 4 /* timing hooks in sdv_diag */
 
@@ -74,8 +75,9 @@ typedef enum {
  *   terminal_kind  [B]                 one of sdv_terminal_kind
  *   events         hipEvent_t handles (cast to void*) recorded on the stream: events[0] before the
  *                  first kernel, events[1] after the row pass (one record per 16 KiB chunk of
- *                  every row read), events[2] after the verdict kernel (per request: fold, accept
- *                  scan, terminal draw).  events[3] is not used.
+ *                  every row read), events[3] after the truncation kernel (top-k / top-p through
+ *                  sdv_verify_opts; not recorded when it does not run), events[2] after the verdict
+ *                  kernel (per request: fold, accept scan, terminal draw).
  */
 typedef struct sdv_diag {
   double* target_lse;
@@ -177,6 +179,23 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
  *                     [0, n_stop_tokens] rejects that request (accepted_len -1, every slot -1).
  *  budget             [B] int32: the remaining output budget of each request (<= 0 emits nothing).
  *  emitted_len        [B] int32 out: the number of tokens request i emits.
+ *  top_k, top_p_milli [B] int32: the rest of each request's sampling profile (SDCP section
+ *                     "Session Contract": top_k a count, top_p_milli the nucleus mass in thousandths).
+ *                     At T > 0, p and (from draft logits) q are truncated after the temperature:
+ *                     tokens rank by probability, equal probabilities going to the smaller token
+ *                     id; top-k keeps the first top_k ranks; top-p then keeps the shortest run of
+ *                     leading ranks whose mass, renormalised over the top-k set, reaches
+ *                     top_p_milli / 1000, and never fewer than one token; the kept tokens are
+ *                     renormalised.  top_k 0 (or >= V) and top_p_milli 1000 truncate nothing; a
+ *                     negative value or top_p_milli > 1000 describes no profile and rejects the
+ *                     request (accepted_len -1, every slot -1).  A draft token outside the kept
+ *                     set of its draft row has q = 0 and rejects the request before any uniform
+ *                     is used.  Given q rows (draft_probs) are not truncated.  Rule 1 (T = 0) keeps
+ *                     its argmax under any truncation and ignores both.  Either may be NULL.
+ *  kept_tokens        [n_draft_rows + B + n_draft_rows] int32 out (with top_k or top_p_milli): the
+ *                     number of tokens each row keeps, target rows first, then draft rows (V for a
+ *                     row that is not truncated); written for the rows of requests at T > 0 (draft
+ *                     rows only when draft logits are used).
  *  draft_probs        [n_draft_rows][V] float (binary32): the draft distributions themselves, SDCP's
  *                     "q_rows" (section "Message Definitions"; Rule 2 takes q[i] from them), used as
  *                     given in place of softmax(draft_logits / T); draft_logits is then not read and
@@ -204,6 +223,9 @@ typedef struct sdv_options {
   const int32_t* budget;
   int32_t* emitted_len;
   const float* draft_probs;
+  const int32_t* top_k;
+  const int32_t* top_p_milli;
+  int32_t* kept_tokens;
 } sdv_options;
 
 /*

@@ -103,15 +103,18 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
               diag: tuple[str, ...] = (), events: list | None = None, accept_uniform: torch.Tensor | None = None,
               draw_uniform: torch.Tensor | None = None, stop_offsets: torch.Tensor | None = None,
               stop_tokens: torch.Tensor | None = None, budget: torch.Tensor | None = None,
-              draft_probs: torch.Tensor | None = None):
+              draft_probs: torch.Tensor | None = None, top_k: torch.Tensor | None = None,
+              top_p_milli: torch.Tensor | None = None):
     """Run sdv_verify_ex; sdv_verify_profiled when temperature and seed are [B] device tensors (one
     sampling profile per request); sdv_verify_opts when the caller's uniforms (float64
     accept_uniform [n_draft_rows], draw_uniform [n_draft_rows + B]), stop lists (int32 CSR
     stop_offsets [B + 1], stop_tokens), a budget (int32 [B]) or draft_probs (float32
-    [n_draft_rows, V], the draft distributions in place of draft logits) are given.  Returns
-    (accepted_len, out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag)
-    and, with stop lists or a budget, "emitted_len".  ``events``: up to four torch.cuda.Event
-    objects recorded before the first kernel and after each kernel.
+    [n_draft_rows, V], the draft distributions in place of draft logits) or the rest of the
+    sampling profiles (int32 top_k [B], top_p_milli [B]) are given.  Returns (accepted_len,
+    out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag), "emitted_len"
+    with stop lists or a budget, and "kept_tokens" (int32 [n_draft_rows + B + n_draft_rows]) with
+    top-k / top-p.  ``events``: up to four torch.cuda.Event objects, recorded as sdv_diag.events
+    describes.
     """
     _check(target, draft, draft_tokens, offsets, temperature, draft_probs)
     dev = target.device
@@ -127,7 +130,11 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
         stop_tokens = stop_tokens if stop_tokens is not None else torch.empty(0, dtype=torch.int32, device=dev)
         stop_tokens = _device_vector(stop_tokens, torch.int32, stop_tokens.shape[0], dev, "stop_tokens")
     budget = _device_vector(budget, torch.int32, B, dev, "budget")
-    use_opts = accept_uniform is not None or stop_offsets is not None or budget is not None or draft_probs is not None
+    top_k = _device_vector(top_k, torch.int32, B, dev, "top_k")
+    top_p_milli = _device_vector(top_p_milli, torch.int32, B, dev, "top_p_milli")
+    truncating = top_k is not None or top_p_milli is not None
+    use_opts = (accept_uniform is not None or stop_offsets is not None or budget is not None or draft_probs is not None
+                or truncating)
     n_d = draft_tokens.shape[0]
     V = target.shape[1]
     dt = _DTYPES[target.dtype]
@@ -170,6 +177,10 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
                 opt.budget = _ptr(budget)
                 dvals["emitted_len"] = torch.full((B,), -9, dtype=torch.int32, device=dev)
                 opt.emitted_len = dvals["emitted_len"].data_ptr()
+            if truncating:
+                opt.top_k, opt.top_p_milli = _ptr(top_k), _ptr(top_p_milli)
+                dvals["kept_tokens"] = torch.full((2 * n_d + B,), -9, dtype=torch.int32, device=dev)
+                opt.kept_tokens = dvals["kept_tokens"].data_ptr()
             scalar_t = 0.0 if profile is not None else float(temperature)
             scalar_s = 0 if profile is not None else int(seed) & 0xFFFFFFFFFFFFFFFF
             rc = _native.lib().sdv_verify_opts(

@@ -45,6 +45,9 @@ class SdvOptions(ctypes.Structure):
         ("budget", ctypes.c_void_p),
         ("emitted_len", ctypes.c_void_p),
         ("draft_probs", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p),
+        ("top_p_milli", ctypes.c_void_p),
+        ("kept_tokens", ctypes.c_void_p),
     ]
 
 

@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <climits>
+#include <type_traits>
 
 #include "../../include/sdv.h"
 #include "sdv_device.hpp"
@@ -42,6 +43,33 @@ struct DiagPtrs {
   float* accept_uniform;
   float* draw_uniform;
   int32_t* terminal_kind;
+};
+
+constexpr int32_t kMaxChunks = 4096;  // chunks per row: the verdict and cut kernels keep one value per chunk in LDS
+
+// The tokens a truncated row keeps (top-k / top-p) are its leading ranks in the order "larger logit
+// first, smaller id first among equal logits", so the last kept rank describes them: token v is
+// kept iff z_v > kappa, or z_v == kappa and v <= vcut.  A row that is not truncated has
+// kappa = -inf and vcut = INT32_MAX.
+struct Cut {
+  float kappa;
+  int32_t vcut;
+};
+
+__device__ __forceinline__ bool kept_by(const Cut c, float z, int32_t v) {
+  return z > c.kappa || (z == c.kappa && v <= c.vcut);
+}
+
+// The tokens the rows of a terminal draw keep: NoCut keeps every token (its tests fold away),
+// RowCuts holds the cuts of the target row (t) and of the draft row (d).
+struct NoCut {
+  __device__ __forceinline__ bool t(float, int32_t) const { return true; }
+  __device__ __forceinline__ bool d(float, int32_t) const { return true; }
+};
+struct RowCuts {
+  Cut ct, cd;
+  __device__ __forceinline__ bool t(float z, int32_t v) const { return kept_by(ct, z, v); }
+  __device__ __forceinline__ bool d(float z, int32_t v) const { return kept_by(cd, z, v); }
 };
 
 struct Params {
@@ -67,6 +95,10 @@ struct Params {
   const int32_t* budget;      // [B] remaining output tokens, or null: no limit
   int32_t* emitted_len;       // [B] out: tokens emitted after truncation, or null
   const float* qrows;         // [n_d][V] draft distributions (binary32) in place of draft logits, or null
+  const int32_t* top_k;       // [B] top-k of each request's profile, or null (0: none)
+  const int32_t* top_p_milli; // [B] top-p in thousandths, or null (1000: none)
+  int32_t* kept_tokens;       // [row slots] out: tokens each truncated row keeps, or null
+  Cut* cuts;                  // [row slots] the cut of every row (workspace), read when truncation is on
   DiagPtrs dg;
 };
 
@@ -217,13 +249,23 @@ __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32
   }
 }
 
-// Residual weight max(p - q, 0), both sides scaled by the same factor 2^(l2_t - ref_t).  The draft
-// side is 2^(z_d k - e); e is split into its fp32 rounding e_hi and a remainder that enters as the
-// factor q_scale = 2^(e_hi - e), applied by the final fused multiply-add.
-__device__ __forceinline__ float resid_weight(float zt, float zd, float k2, float ref_t, float e_hi, float q_scale) {
-  const float p = fast_exp2(fmaf(zt, k2, -ref_t));
-  const float q = fast_exp2(fmaf(zd, k2, -e_hi));
+// Residual weight max(p - q, 0) of token v, both sides scaled by the same factor 2^(l2_t - ref_t).
+// The draft side is 2^(z_d k - e); e is split into its fp32 rounding e_hi and a remainder that
+// enters as the factor q_scale = 2^(e_hi - e), applied by the final fused multiply-add.  A token a
+// row does not keep has zero probability on that side: its logit enters as -inf (selecting the
+// input rather than the output keeps the masked loops within the register file).
+template <class M>
+__device__ __forceinline__ float resid_weight(const M& m, float zt, float zd, int32_t v, float k2, float ref_t,
+                                              float e_hi, float q_scale) {
+  const float p = fast_exp2(fmaf(m.t(zt, v) ? zt : -INFINITY, k2, -ref_t));
+  const float q = fast_exp2(fmaf(m.d(zd, v) ? zd : -INFINITY, k2, -e_hi));
   return fmaxf(fmaf(-q, q_scale, p), 0.0f);
+}
+
+// Weight of token v in a draw from p itself (the frame 2^(z k - ref_t)).
+template <class M>
+__device__ __forceinline__ float p_weight(const M& m, float zt, int32_t v, float k2, float ref_t) {
+  return fast_exp2(fmaf(m.t(zt, v) ? zt : -INFINITY, k2, -ref_t));
 }
 
 // Inverse CDF inside one chunk, element by element (rows that are not 16-byte aligned): the
@@ -327,9 +369,9 @@ __device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, 
 
 // Residual mass of one chunk of the rejected row pair: coalesced 16-byte loads, fp32 per vector,
 // fp64 across vectors and lanes.
-template <class E, bool kVec>
-__device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* dp, int32_t c0, int32_t n, float k2, float ref_t,
-                                   float e_hi, float q_scale, int lane) {
+template <class E, bool kVec, class M>
+__device__ __forceinline__ double resid_chunk_mass(const M& m, const char* tp, const char* dp, int32_t c0, int32_t n,
+                                                   float k2, float ref_t, float e_hi, float q_scale, int lane) {
   double acc = 0.0;
   if constexpr (kVec) {
     const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
@@ -351,14 +393,15 @@ __device__ __forceinline__ double resid_chunk_mass(const char* tp, const char* d
         float ft[E::kPerVec], fd[E::kPerVec];
         E::unpack(tb[k], ft);
         E::unpack(db[k], fd);
+        const int32_t v0 = c0 + (lane + kWave * (h * kHalf + k)) * E::kPerVec;
 #pragma unroll
-        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, q_scale);
+        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
         acc += (double)tree_sum(ft);
       }
     }
   } else {
     for (int32_t v = c0 + lane; v < c0 + n; v += kWave)
-      acc += (double)resid_weight(E::at(tp, v), E::at(dp, v), k2, ref_t, e_hi, q_scale);
+      acc += (double)resid_weight(m, E::at(tp, v), E::at(dp, v), v, k2, ref_t, e_hi, q_scale);
   }
   return wave_sum(acc);
 }
@@ -417,10 +460,10 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
 // loads of full chunks carry no bounds test (a predicated load would leave the hardware load counter
 // uncertain and force a wait for every outstanding load); a row's last, partial chunk goes through
 // the bounds-tested path.
-template <class E>
-__device__ __forceinline__ void resid_masses_pipelined(const char* tp, const char* dp, int32_t V, int32_t C, float k2,
-                                                       float ref_t, float e_hi, float q_scale, double* lds_mass,
-                                                       int lane, int wave, int n_waves) {
+template <class E, class M>
+__device__ __forceinline__ void resid_masses_pipelined(const M& m, const char* tp, const char* dp, int32_t V, int32_t C,
+                                                       float k2, float ref_t, float e_hi, float q_scale,
+                                                       double* lds_mass, int lane, int wave, int n_waves) {
   constexpr int kHalf = kVecPerLane / 2;
   struct Half {
     u32x4 t[kHalf], d[kHalf];
@@ -435,15 +478,16 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
       b.d[k] = dv[vi];
     }
   };
-  auto reduce = [&](const Half& b) {
+  auto reduce = [&](const Half& b, int32_t c, int h) {
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < kHalf; ++k) {
       float ft[E::kPerVec], fd[E::kPerVec];
       E::unpack(b.t[k], ft);
       E::unpack(b.d[k], fd);
+      const int32_t v0 = c * E::kChunk + (lane + kWave * (h * kHalf + k)) * E::kPerVec;
 #pragma unroll
-      for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(ft[q], fd[q], k2, ref_t, e_hi, q_scale);
+      for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
       acc += (double)tree_sum(ft);
     }
     return acc;
@@ -459,27 +503,27 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
     for (; c + n_waves < C_full; c += n_waves) {
       load(c, 1, Bh);
       asm volatile("" ::: "memory");  // the second half is in flight while the first is reduced
-      double acc = reduce(A);
+      double acc = reduce(A, c, 0);
       asm volatile("" : "+v"(acc)::"memory");  // the first half is consumed before its registers reload
       load(c + n_waves, 0, A);
       asm volatile("" ::: "memory");
-      acc += reduce(Bh);
+      acc += reduce(Bh, c, 1);
       asm volatile("" : "+v"(acc)::"memory");
       acc = wave_sum(acc);
       if (lane == 0) lds_mass[c] = acc;
     }
     load(c, 1, Bh);
     asm volatile("" ::: "memory");
-    double acc = reduce(A);
+    double acc = reduce(A, c, 0);
     asm volatile("" : "+v"(acc)::"memory");
-    acc += reduce(Bh);
+    acc += reduce(Bh, c, 1);
     acc = wave_sum(acc);
     if (lane == 0) lds_mass[c] = acc;
     c += n_waves;
   }
   if (c < C) {  // the partial last chunk, if this wave owns it
     const int32_t c0 = c * E::kChunk;
-    const double cm = resid_chunk_mass<E, true>(tp, dp, c0, V - c0, k2, ref_t, e_hi, q_scale, lane);
+    const double cm = resid_chunk_mass<E, true>(m, tp, dp, c0, V - c0, k2, ref_t, e_hi, q_scale, lane);
     if (lane == 0) lds_mass[c] = cm;
   }
 }
@@ -488,21 +532,23 @@ __device__ __forceinline__ void resid_masses_pipelined(const char* tp, const cha
 // rows of 64 (vector k*64 + l for lane l), wave w sums rows w and w + n_waves, a scan of the row sums
 // picks the row, and the wave that owns it scans its 64 vector sums and walks the chosen vector.
 // Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
-template <class E, bool kResid>
-__device__ __forceinline__ int32_t search_chunk_block(const char* trow, const char* drow, int32_t c0, int32_t n,
-                                                      double target, float k2, float ref_t, float e_hi, float q_scale,
-                                                      double* scratch, int lane, int wave, int n_waves) {
+template <class E, bool kResid, class M>
+__device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* trow, const char* drow, int32_t c0,
+                                                      int32_t n, double target, float k2, float ref_t, float e_hi,
+                                                      float q_scale, double* scratch, int lane, int wave,
+                                                      int n_waves) {
   constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
   const int32_t nvec = n / E::kPerVec;
   const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
   const u32x4* dv = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)c0 * E::kBytes);
-  auto weights = [&](const u32x4& t, const u32x4& dd, float (&w)[E::kPerVec]) {
+  auto weights = [&](const u32x4& t, const u32x4& dd, int32_t v0, float (&w)[E::kPerVec]) {
     float ft[E::kPerVec], fd[E::kPerVec];
     E::unpack(t, ft);
     if constexpr (kResid) E::unpack(dd, fd);
 #pragma unroll
     for (int q = 0; q < E::kPerVec; ++q)
-      w[q] = kResid ? resid_weight(ft[q], fd[q], k2, ref_t, e_hi, q_scale) : fast_exp2(fmaf(ft[q], k2, -ref_t));
+      w[q] = kResid ? resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale)
+                    : p_weight(m, ft[q], v0 + q, k2, ref_t);
   };
   // rows owned by this wave: wave and wave + n_waves (n_waves == 8 covers the 16 rows)
   u32x4 t[2], dd[2];
@@ -516,7 +562,7 @@ __device__ __forceinline__ int32_t search_chunk_block(const char* trow, const ch
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float w[E::kPerVec];
-    weights(t[j], dd[j], w);
+    weights(t[j], dd[j], c0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
     vs[j] = tree_sum(w);
     const double rs = wave_sum((double)vs[j]);
     if (lane == 0 && wave + j * n_waves < kRows) scratch[wave + j * n_waves] = rs;
@@ -539,9 +585,9 @@ __device__ __forceinline__ int32_t search_chunk_block(const char* trow, const ch
   const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
   const uint64_t vpos = __ballot(v > 0.0f);
   const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
-  float w[E::kPerVec];
-  weights(j == 0 ? t[0] : t[1], j == 0 ? dd[0] : dd[1], w);
   const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+  float w[E::kPerVec];
+  weights(j == 0 ? t[0] : t[1], j == 0 ? dd[0] : dd[1], base, w);
   int32_t yl = base + E::kPerVec - 1;
   int32_t last_pos = -1;
   double upto = vex;
@@ -566,8 +612,10 @@ __device__ __forceinline__ int32_t search_chunk_block(const char* trow, const ch
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float resid_weight_q(float zt, float qv, float k2, float ref_t, float q_scale) {
-  const float p = fast_exp2(fmaf(zt, k2, -ref_t));
+template <class M>
+__device__ __forceinline__ float resid_weight_q(const M& m, float zt, float qv, int32_t v, float k2, float ref_t,
+                                                float q_scale) {
+  const float p = fast_exp2(fmaf(m.t(zt, v) ? zt : -INFINITY, k2, -ref_t));
   return fmaxf(fmaf(-qv, q_scale, p), 0.0f);
 }
 
@@ -600,10 +648,10 @@ struct Quad<F32> {
 // aligned rows).  Wave w takes full chunks w, w + n_waves, ... in halves of 4-element quads
 // (quad l + 64 k for lane l): the loads of the next half are issued before the current one is
 // reduced.  The partial last chunk, if any, is summed element by element by the wave that owns it.
-template <class E>
-__device__ __forceinline__ void resid_masses_q(const char* tp, const float* qp, int32_t V, int32_t C, float k2,
-                                               float ref_t, float q_scale, double* lds_mass, int lane, int wave,
-                                               int n_waves) {
+template <class E, class M>
+__device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const float* qp, int32_t V, int32_t C,
+                                               float k2, float ref_t, float q_scale, double* lds_mass, int lane,
+                                               int wave, int n_waves) {
   typedef typename Quad<E>::T TQ;
   constexpr int kParts = 2;                               // stages per chunk
   constexpr int kQuadsPerLane = E::kChunk / 4 / kWave;    // 32 (bf16) or 16 (fp32)
@@ -626,17 +674,20 @@ __device__ __forceinline__ void resid_masses_q(const char* tp, const float* qp, 
       st.q[k] = qv[u];
     }
   };
-  auto reduce = [&](const Stage& st) {
+  auto reduce = [&](const Stage& st, int32_t s) {
+    const int32_t c0 = chunk_of(s) * E::kChunk;
+    const int h = s % kParts;
     double acc = 0.0;
 #pragma unroll
     for (int k = 0; k < kPart; k += 2) {
       float ft[8], w[8];
       Quad<E>::unpack(st.t[k], reinterpret_cast<float(&)[4]>(ft[0]));
       Quad<E>::unpack(st.t[k + 1], reinterpret_cast<float(&)[4]>(ft[4]));
+      const int32_t v0 = c0 + 4 * (lane + kWave * (h * kPart + k)), v1 = v0 + 4 * kWave;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w[e] = resid_weight_q(ft[e], st.q[k][e], k2, ref_t, q_scale);
-        w[4 + e] = resid_weight_q(ft[4 + e], st.q[k + 1][e], k2, ref_t, q_scale);
+        w[e] = resid_weight_q(m, ft[e], st.q[k][e], v0 + e, k2, ref_t, q_scale);
+        w[4 + e] = resid_weight_q(m, ft[4 + e], st.q[k + 1][e], v1 + e, k2, ref_t, q_scale);
       }
       acc += (double)tree_sum(w);
     }
@@ -661,30 +712,30 @@ __device__ __forceinline__ void resid_masses_q(const char* tp, const float* qp, 
     for (; s + 2 < steps; s += 2) {
       load(s + 1, Bs);
       asm volatile("" ::: "memory");  // the next stage is in flight while this one is reduced
-      acc += reduce(A);
+      acc += reduce(A, s);
       asm volatile("" : "+v"(acc)::"memory");
       finish_chunk(s);
       load(s + 2, A);
       asm volatile("" ::: "memory");
-      acc += reduce(Bs);
+      acc += reduce(Bs, s + 1);
       asm volatile("" : "+v"(acc)::"memory");
       finish_chunk(s + 1);
     }
     load(s + 1, Bs);
     asm volatile("" ::: "memory");
-    acc += reduce(A);
+    acc += reduce(A, s);
     asm volatile("" : "+v"(acc)::"memory");
     finish_chunk(s);
-    acc += reduce(Bs);
+    acc += reduce(Bs, s + 1);
     asm volatile("" : "+v"(acc)::"memory");
     finish_chunk(s + 1);
   }
   if (C_full < C && C_full % n_waves == wave) {  // the partial last chunk
     const int32_t c0 = C_full * E::kChunk;
-    double m = 0.0;
-    for (int32_t v = c0 + lane; v < V; v += kWave) m += (double)resid_weight_q(E::at(tp, v), qp[v], k2, ref_t, q_scale);
-    m = wave_sum(m);
-    if (lane == 0) lds_mass[C_full] = m;
+    double cm = 0.0;
+    for (int32_t v = c0 + lane; v < V; v += kWave) cm += (double)resid_weight_q(m, E::at(tp, v), qp[v], v, k2, ref_t, q_scale);
+    cm = wave_sum(cm);
+    if (lane == 0) lds_mass[C_full] = cm;
   }
 }
 
@@ -692,22 +743,24 @@ __device__ __forceinline__ void resid_masses_q(const char* tp, const float* qp, 
 // rows), laid out as the logit version: rows of 64 vectors, wave w sums rows w and w + n_waves, a
 // scan of the row sums picks the row, the owning wave scans its vector sums and walks the vector.
 // Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
-template <class E>
-__device__ __forceinline__ int32_t search_chunk_q_block(const char* trow, const float* qrow, int32_t c0, int32_t n,
-                                                        double target, float k2, float ref_t, float q_scale,
-                                                        double* scratch, int lane, int wave, int n_waves) {
+template <class E, class M>
+__device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* trow, const float* qrow, int32_t c0,
+                                                        int32_t n, double target, float k2, float ref_t,
+                                                        float q_scale, double* scratch, int lane, int wave,
+                                                        int n_waves) {
   constexpr int kRows = kVecPerLane;
   constexpr int kQV = E::kPerVec / 4;
   const int32_t nvec = n / E::kPerVec;
   const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
   const f32x4* qv = reinterpret_cast<const f32x4*>(qrow + c0);
-  auto weights = [&](const u32x4& t, const f32x4 (&q)[kQV], float (&w)[E::kPerVec]) {
+  auto weights = [&](const u32x4& t, const f32x4 (&q)[kQV], int32_t v0, float (&w)[E::kPerVec]) {
     float ft[E::kPerVec];
     E::unpack(t, ft);
 #pragma unroll
-    for (int m = 0; m < kQV; ++m)
+    for (int g = 0; g < kQV; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[4 * m + e] = resid_weight_q(ft[4 * m + e], q[m][e], k2, ref_t, q_scale);
+      for (int e = 0; e < 4; ++e)
+        w[4 * g + e] = resid_weight_q(m, ft[4 * g + e], q[g][e], v0 + 4 * g + e, k2, ref_t, q_scale);
   };
   u32x4 t[2];
   f32x4 q[2][kQV];
@@ -719,12 +772,12 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const char* trow, const 
     const bool in = row < kRows && vi < nvec;
     t[j] = in ? tv[vi] : neg_inf_vec<E>();
 #pragma unroll
-    for (int m = 0; m < kQV; ++m) q[j][m] = in ? qv[vi * kQV + m] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < kQV; ++g) q[j][g] = in ? qv[vi * kQV + g] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     float w[E::kPerVec];
-    weights(t[j], q[j], w);
+    weights(t[j], q[j], c0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
     vs[j] = tree_sum(w);
     const double rs = wave_sum((double)vs[j]);
     if (lane == 0 && wave + j * n_waves < kRows) scratch[wave + j * n_waves] = rs;
@@ -745,10 +798,10 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const char* trow, const 
   const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
   const uint64_t vpos = __ballot(v > 0.0f);
   const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
-  float w[E::kPerVec];
-  if (j == 0) weights(t[0], q[0], w);
-  else weights(t[1], q[1], w);
   const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+  float w[E::kPerVec];
+  if (j == 0) weights(t[0], q[0], base, w);
+  else weights(t[1], q[1], base, w);
   int32_t yl = base + E::kPerVec - 1;
   int32_t last_pos = -1;
   double upto = vex;
@@ -766,7 +819,424 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const char* trow, const 
   return __shfl(yl, l, kWave);
 }
 
-// ============================================================================ 2. verdicts
+// ============================================================================ 2. truncation
+// SDCP ("Speculative Decoding Coordination Protocol (SDCP)", section "Session Contract") defines p
+// as the model's distribution after temperature, then top-k, then top-p.  One workgroup per logit
+// row finds the row's cut by an exact radix select over an order-preserving key of the logits:
+// counts and fixed-point masses per digit go into LDS histograms, the descending scan of a
+// histogram picks the digit that holds the top_k-th rank (top-k) or where the running mass
+// reaches the nucleus mass (top-p), and the next level refines inside that digit.  Ranks that tie
+// on a logit differ only in token id, so the last level ends on one logit value, and the number of
+// its copies to keep follows from counts alone.  A last pass over the row finds the token id of
+// the last kept copy and rewrites each chunk record's mass to the mass of the chunk's kept tokens,
+// so the verdict kernel's fold yields the truncated normaliser unchanged.
+
+constexpr int kCutWaves = 16;
+constexpr int kCutThreads = kWave * kCutWaves;
+constexpr int kCutUnroll = 8;          // 16-byte loads in flight per thread in a histogram pass
+constexpr int kRadixBins = 1 << 11;    // the widest digit
+constexpr float kFixScale = 0x1.0p37f;  // masses 2^(z k - R) <= ~1 as integers: V 2^37 < 2^63
+
+// Digits of the order key, most significant first: bf16 keys carry 16 bits (11 + 5), binary32
+// keys 32 (11 + 11 + 10).
+template <class E>
+struct Radix;
+template <>
+struct Radix<Bf16> {
+  static constexpr int kLevels = 2;
+  __device__ static constexpr int shift(int L) { return L == 0 ? 21 : 16; }
+  __device__ static constexpr int width(int L) { return L == 0 ? 11 : 5; }
+};
+template <>
+struct Radix<F32> {
+  static constexpr int kLevels = 3;
+  __device__ static constexpr int shift(int L) { return L == 0 ? 21 : (L == 1 ? 10 : 0); }
+  __device__ static constexpr int width(int L) { return L == 2 ? 10 : 11; }
+};
+
+// Order-preserving key: a larger logit has a larger key, and -0 shares the key of +0 (they are
+// equal logits).  key_logit inverts it.
+__device__ __forceinline__ uint32_t order_key(float z) {
+  const uint32_t b = z == 0.0f ? 0u : __float_as_uint(z);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint64_t fixed_mass(float z, float k2, float R) {
+  return (uint64_t)(fast_exp2(fmaf(z, k2, -R)) * kFixScale);
+}
+
+// Every logit of a row, visited by the workgroup with coalesced loads (f(z, v)).
+template <class E, bool kVec, class F>
+__device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
+  if constexpr (kVec) {
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rp);
+    const int32_t nvec = V / E::kPerVec;  // 16-byte rows: no partial vector
+    for (int32_t base = 0; base < nvec; base += kCutUnroll * kCutThreads) {
+      u32x4 buf[kCutUnroll];
+#pragma unroll
+      for (int u = 0; u < kCutUnroll; ++u) {
+        const int32_t vi = base + u * kCutThreads + (int32_t)threadIdx.x;
+        buf[u] = vi < nvec ? vp[vi] : neg_inf_vec<E>();
+      }
+#pragma unroll
+      for (int u = 0; u < kCutUnroll; ++u) {
+        const int32_t vi = base + u * kCutThreads + (int32_t)threadIdx.x;
+        if (vi < nvec) {
+          float z[E::kPerVec];
+          E::unpack(buf[u], z);
+#pragma unroll
+          for (int e = 0; e < E::kPerVec; ++e) f(z[e], vi * E::kPerVec + e);
+        }
+      }
+    }
+  } else {
+    for (int32_t v = threadIdx.x; v < V; v += kCutThreads) f(E::at(rp, v), v);
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+struct CutShared {
+  uint32_t wave_cnt[kCutWaves];
+  uint64_t wave_mass[kCutWaves];
+  float wave_ref[kCutWaves];
+  int32_t cand, last;
+  uint32_t pick_digit, pick_cnt_above, pick_cnt;
+  uint64_t pick_mass_above;
+};
+
+// The histogram of one digit level over the logits whose higher digits equal prefix: counts, and
+// masses 2^(z k - R) as fixed-point integers (integer sums do not depend on the order of the
+// atomic adds, so the cut is the same on every run).
+template <class E, bool kVec>
+__device__ __forceinline__ void histogram(const char* rp, int32_t V, float k2, float R, int L, uint32_t prefix,
+                                          uint32_t* cnt, uint64_t* mass) {
+  const int shift = Radix<E>::shift(L), nb = 1 << Radix<E>::width(L);
+  const int hi = shift + Radix<E>::width(L);
+  for (int b = threadIdx.x; b < nb; b += kCutThreads) {
+    cnt[b] = 0u;
+    mass[b] = 0ull;
+  }
+  __syncthreads();
+  for_each_logit<E, kVec>(rp, V, [&](float z, int32_t) {
+    const uint32_t key = order_key(z);
+    if (L > 0 && (key >> hi) != prefix) return;
+    const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
+    atomicAdd(&cnt[d], 1u);
+    atomicAdd(reinterpret_cast<unsigned long long*>(&mass[d]), (unsigned long long)fixed_mass(z, k2, R));
+  });
+  __syncthreads();
+}
+
+// The bin a selection lands in, scanning the bins from the largest digit down: by count, the bin
+// that holds the need-th logit; by mass, the first non-empty bin where mass_before plus the running
+// mass reaches target.  Leaves in sh the digit, the count and mass of the higher bins and the bin's
+// count.  If no bin qualifies (rounding), the last non-empty bin is taken.
+__device__ __forceinline__ void select_bin(const uint32_t* cnt, const uint64_t* mass, int nb, bool by_mass,
+                                           uint32_t need, double target, uint64_t mass_before, CutShared& sh) {
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  if (t == 0) {
+    sh.cand = INT32_MAX;
+    sh.last = -1;
+  }
+  const int p0 = 2 * t, p1 = 2 * t + 1;  // positions in descending digit order
+  const uint32_t c0 = p0 < nb ? cnt[nb - 1 - p0] : 0u, c1 = p1 < nb ? cnt[nb - 1 - p1] : 0u;
+  const uint64_t m0 = p0 < nb ? mass[nb - 1 - p0] : 0ull, m1 = p1 < nb ? mass[nb - 1 - p1] : 0ull;
+  uint32_t ci = c0 + c1;
+  uint64_t mi = m0 + m1;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t uc = __shfl_up(ci, o, kWave);
+    const uint64_t um = __shfl_up(mi, o, kWave);
+    if (lane >= o) {
+      ci += uc;
+      mi += um;
+    }
+  }
+  if (lane == kWave - 1) {
+    sh.wave_cnt[wave] = ci;
+    sh.wave_mass[wave] = mi;
+  }
+  __syncthreads();
+  uint32_t cb = 0u;
+  uint64_t mb = 0ull;
+  for (int w = 0; w < wave; ++w) {
+    cb += sh.wave_cnt[w];
+    mb += sh.wave_mass[w];
+  }
+  const uint32_t ce0 = cb + ci - (c0 + c1), ce1 = ce0 + c0;
+  const uint64_t me0 = mb + mi - (m0 + m1), me1 = me0 + m0;
+  auto hit = [&](uint32_t ce, uint64_t me, uint32_t c, uint64_t m) {
+    if (by_mass) return c > 0u && (double)(mass_before + me + m) >= target;
+    return ce < need && need <= ce + c;
+  };
+  int cand = INT32_MAX, last = -1;
+  if (p1 < nb && hit(ce1, me1, c1, m1)) cand = p1;
+  if (p0 < nb && hit(ce0, me0, c0, m0)) cand = p0;
+  if (p0 < nb && c0) last = p0;
+  if (p1 < nb && c1) last = p1;
+  atomicMin(&sh.cand, cand);
+  atomicMax(&sh.last, last);
+  __syncthreads();
+  const int ps = sh.cand != INT32_MAX ? sh.cand : max(sh.last, 0);
+  if (ps == p0 || ps == p1) {
+    const bool first = ps == p0;
+    sh.pick_digit = (uint32_t)(nb - 1 - ps);
+    sh.pick_cnt_above = first ? ce0 : ce1;
+    sh.pick_mass_above = first ? me0 : me1;
+    sh.pick_cnt = first ? c0 : c1;
+  }
+  __syncthreads();
+}
+
+// A radix selection's outcome: the key of the last kept logit value, how many tokens rank above
+// that value, their mass, and how many tokens carry the value.
+struct Selected {
+  uint32_t key;
+  uint32_t cnt_above;
+  uint64_t mass_above;
+  uint32_t ties;
+};
+
+// One workgroup per row slot (target rows, then draft rows when the draft side is logits).  Rows of
+// requests that sample with a truncating profile get their cut; every other row gets the trivial
+// one.  Writes cuts[slot], kept_tokens[slot] and, for a truncated row, the masses of its chunk
+// records.
+template <class E, bool kVec>
+__global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
+  __shared__ __align__(16) unsigned char smem[48 * 1024];
+  __shared__ CutShared sh;
+  uint32_t* cnt0 = reinterpret_cast<uint32_t*>(smem);  // level 0, kept for the whole selection
+  uint64_t* mass0 = reinterpret_cast<uint64_t*>(smem + 8 * 1024);
+  uint32_t* cntL = reinterpret_cast<uint32_t*>(smem + 24 * 1024);  // the deeper levels
+  uint64_t* massL = reinterpret_cast<uint64_t*>(smem + 32 * 1024);
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int32_t slot = blockIdx.x;
+  const bool target = slot < P.n_t;
+  const int32_t row = target ? slot : slot - P.n_t;
+  const int32_t i = request_of_row(P.cu, P.B, row, target);
+  const float k2 = P.temp_each ? k2_of(temperature_of(P.temp_each, i)) : P.k2;
+  const int32_t top_k = P.top_k ? P.top_k[i] : 0;
+  const int32_t milli = P.top_p_milli ? P.top_p_milli[i] : 1000;
+  const bool valid = top_k >= 0 && milli >= 0 && milli <= 1000;
+  const bool by_k = valid && top_k > 0 && top_k < P.V;
+  const bool by_p = valid && milli < 1000;
+  auto untruncated = [&]() {
+    if (t == 0) {
+      P.cuts[slot] = Cut{-INFINITY, INT32_MAX};
+      if (P.kept_tokens) P.kept_tokens[slot] = P.V;
+    }
+  };
+  // greedy or rejected requests, and profiles that truncate nothing (the draft rows of greedy
+  // requests have no records: they are never read)
+  if (!(k2 > 0.0f) || !(by_k || by_p)) return untruncated();
+  float2* rec = P.part + (int64_t)slot * P.C;
+  // the row's exponent reference R: the largest chunk reference (fl(max z * k))
+  float rl = -INFINITY;
+  for (int32_t c = t; c < P.C; c += kCutThreads) rl = fmaxf(rl, rec[c].x);
+  rl = wave_max(rl);
+  if (lane == 0) sh.wave_ref[wave] = rl;
+  __syncthreads();
+  float R = -INFINITY;
+  for (int w = 0; w < kCutWaves; ++w) R = fmaxf(R, sh.wave_ref[w]);
+  if (R == -INFINITY) return untruncated();  // a row of -inf only describes no distribution
+  const char* rp = target ? row_ptr<E>(P.target, row, P.V) : row_ptr<E>(P.draft, row, P.V);
+
+  histogram<E, kVec>(rp, P.V, k2, R, 0, 0u, cnt0, mass0);
+  int held_level = -1;  // the (level, prefix) whose histogram cntL / massL hold
+  uint32_t held_prefix = 0u;
+  constexpr int kLast = Radix<E>::kLevels - 1;
+  auto run = [&](bool by_mass, uint32_t need, double target_mass) {
+    uint32_t prefix = 0u, cnt_above = 0u, ties = 0u;
+    uint64_t mass_above = 0ull;
+    for (int L = 0; L <= kLast; ++L) {
+      const uint32_t* c = cnt0;
+      const uint64_t* m = mass0;
+      if (L > 0) {
+        if (held_level != L || held_prefix != prefix) {
+          histogram<E, kVec>(rp, P.V, k2, R, L, prefix, cntL, massL);
+          held_level = L;
+          held_prefix = prefix;
+        }
+        c = cntL;
+        m = massL;
+      }
+      select_bin(c, m, 1 << Radix<E>::width(L), by_mass, need - cnt_above, target_mass, mass_above, sh);
+      cnt_above += sh.pick_cnt_above;
+      mass_above += sh.pick_mass_above;
+      ties = sh.pick_cnt;
+      prefix = (prefix << Radix<E>::width(L)) | sh.pick_digit;
+    }
+    // below the last digit a bf16 key holds 16 copies of its sign bit's complement
+    constexpr int sl = Radix<E>::shift(kLast);
+    uint32_t key = prefix;
+    if constexpr (sl > 0) key = (prefix << sl) | (((prefix >> (31 - sl)) & 1u) ? 0u : ((1u << sl) - 1u));
+    return Selected{key, cnt_above, mass_above, ties};
+  };
+
+  // top-k: the top_k-th rank, and the mass of the top-k set
+  Selected s{0u, 0u, 0ull, 0u};
+  uint32_t n_eq = 0u;  // copies of the cut value that are kept
+  uint64_t mass_k = 0ull;
+  if (by_k) {
+    s = run(false, (uint32_t)top_k, 0.0);
+    n_eq = (uint32_t)top_k - s.cnt_above;
+    mass_k = s.mass_above + (uint64_t)n_eq * fixed_mass(key_logit(s.key), k2, R);
+  } else {
+    uint64_t part = 0ull;
+    for (int b = t; b < kRadixBins; b += kCutThreads) part += mass0[b];
+    part = wave_sum_u64(part);
+    if (lane == 0) sh.wave_mass[wave] = part;
+    __syncthreads();
+    for (int w = 0; w < kCutWaves; ++w) mass_k += sh.wave_mass[w];
+    __syncthreads();
+  }
+  // top-p: the shortest run of leading ranks whose mass reaches milli / 1000 of the top-k mass
+  if (by_p) {
+    const double target_mass = (double)mass_k * ((double)milli / 1000.0);
+    const Selected sp = run(true, 0u, target_mass);
+    const uint64_t e = fixed_mass(key_logit(sp.key), k2, R);
+    // the fewest copies (at least one) that reach the target; the selected bin's copies reach it,
+    // so the estimate starts within a rounding step of the answer and the corrections are short
+    uint64_t n = 1ull;
+    if (e > 0ull && (double)(sp.mass_above + e) < target_mass) {
+      const double est = ceil((target_mass - (double)sp.mass_above) / (double)e);
+      n = est >= (double)sp.ties ? (uint64_t)sp.ties : (uint64_t)est;
+      while (n > 1ull && (double)(sp.mass_above + (n - 1ull) * e) >= target_mass) --n;
+      while (n < sp.ties && (double)(sp.mass_above + n * e) < target_mass) ++n;
+    }
+    if (n > sp.ties) n = sp.ties;
+    if (by_k && sp.key == s.key && n > n_eq) n = n_eq;
+    s = sp;
+    n_eq = (uint32_t)n;
+  }
+  const float kappa = key_logit(s.key);
+  const int32_t kept = (int32_t)(s.cnt_above + n_eq);
+
+  // chunk masses of the kept tokens strictly above the cut value, and the copies of the cut value
+  // in each chunk (the LDS of the histograms is free again)
+  __syncthreads();
+  float* strict = reinterpret_cast<float*>(smem);
+  uint32_t* copies = reinterpret_cast<uint32_t*>(smem + 16 * 1024);
+  for (int32_t c = wave; c < P.C; c += kCutWaves) {
+    const int32_t c0 = c * E::kChunk, n = min(E::kChunk, P.V - c0);
+    const float ref_c = rec[c].x;
+    float acc = 0.0f;
+    uint32_t cp = 0u;
+    auto take = [&](float z) {
+      if (z > kappa) acc += fast_exp2(fmaf(z, k2, -ref_c));
+      cp += z == kappa ? 1u : 0u;
+    };
+    if constexpr (kVec) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+      const int32_t nvec = n / E::kPerVec;
+#pragma unroll
+      for (int k = 0; k < kVecPerLane; ++k) {
+        const int vi = lane + kWave * k;
+        if (vi < nvec) {
+          float z[E::kPerVec];
+          E::unpack(vp[vi], z);
+#pragma unroll
+          for (int e = 0; e < E::kPerVec; ++e) take(z[e]);
+        }
+      }
+    } else {
+      for (int32_t v = c0 + lane; v < c0 + n; v += kWave) take(E::at(rp, v));
+    }
+    acc = wave_sum(acc);
+    cp = wave_sum_u32(cp);
+    if (lane == 0) {
+      strict[c] = acc;
+      copies[c] = cp;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0: the kept copies per chunk in token order, the new chunk masses, and the chunk holding
+  // the last kept copy
+  uint32_t carry = 0u;
+  int32_t cstar = -1;
+  uint32_t rstar = 0u;
+  for (int32_t cb = 0; cb < P.C; cb += kWave) {
+    const int32_t c = cb + lane;
+    const uint32_t here = c < P.C ? copies[c] : 0u;
+    uint32_t incl = here;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t up = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += up;
+    }
+    const uint32_t before = carry + incl - here;
+    const uint32_t keep_here = n_eq > before ? min(n_eq - before, here) : 0u;
+    if (c < P.C) {
+      float s2 = strict[c];
+      if (keep_here > 0u && kappa > -INFINITY) s2 += (float)keep_here * fast_exp2(fmaf(kappa, k2, -rec[c].x));
+      rec[c].y = s2;
+    }
+    const uint64_t holds = __ballot(c < P.C && before < n_eq && n_eq <= before + here);
+    if (holds && cstar < 0) {
+      const int g = __ffsll((unsigned long long)holds) - 1;
+      cstar = cb + g;
+      rstar = __shfl(n_eq - before, g, kWave);
+    }
+    carry += __shfl(incl, kWave - 1, kWave);
+  }
+  // the token id of the last kept copy, unless every copy is kept
+  int32_t vcut = INT32_MAX;
+  if (n_eq < s.ties && cstar >= 0) {
+    const int32_t c0 = cstar * E::kChunk, end = min(c0 + E::kChunk, P.V);
+    uint32_t need = rstar;
+    for (int32_t b = c0; b < end; b += kWave * E::kPerVec) {
+      const int32_t v0 = b + lane * E::kPerVec;  // each lane takes kPerVec consecutive tokens
+      uint32_t mask = 0u;
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e)
+        if (v0 + e < end && E::at(rp, v0 + e) == kappa) mask |= 1u << e;
+      const uint32_t mine = (uint32_t)__popc(mask);
+      uint32_t incl = mine;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t up = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += up;
+      }
+      const uint32_t total = __shfl(incl, kWave - 1, kWave);
+      if (need <= total) {
+        const uint64_t at = __ballot(incl - mine < need && need <= incl);
+        const int g = __ffsll((unsigned long long)at) - 1;
+        int32_t v = -1;
+        uint32_t left = need - (incl - mine);
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e)
+          if ((mask >> e) & 1u) {
+            if (left == 1u && v < 0) v = v0 + e;
+            --left;
+          }
+        vcut = __shfl(v, g, kWave);
+        break;
+      }
+      need -= total;
+    }
+  }
+  if (lane == 0) {
+    P.cuts[slot] = Cut{kappa, vcut};
+    if (P.kept_tokens) P.kept_tokens[slot] = kept;
+  }
+}
+
+// ============================================================================ 3. verdicts
 
 // Row fold by one wave, lanes over chunks.  T > 0: l2 = R + log2(sum_c s_c 2^(ref_c - R)) with
 // R = max_c ref_c.  T = 0: the row argmax (chunk maxima with their first indices; ties to the
@@ -853,9 +1323,10 @@ struct Decision {
   int32_t a;
   float ref_t, e_hi, q_scale;
   double u;
+  Cut ct, cd;  // cuts of the drawn position's target and draft rows (truncating profiles)
 };
 
-template <class E, bool kVec, bool kQ>
+template <class E, bool kVec, bool kQ, bool kCut>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves);
@@ -866,8 +1337,10 @@ constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
 // The verdict of request i under one rule (k2 = log2(e)/T and the Philox key seed), by one
 // workgroup of 8 waves.  Shared memory: the folded rows, the decision, and the residual chunk masses
-// (C doubles, dynamic).  bad_profile rejects the request once its offsets have been screened.
-template <class E, bool kGreedy, bool kVec, bool kQ>
+// (C doubles, dynamic).  bad_profile rejects the request once its offsets have been screened.  With
+// kCut the rows' cuts (top-k / top-p) decide which tokens p and q keep; the chunk records already
+// hold the kept masses.
+template <class E, bool kGreedy, bool kVec, bool kQ, bool kCut>
 __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k2, uint64_t seed, bool bad_profile,
                                              double* lds_mass, RowFold* rows, Decision& dec) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -909,6 +1382,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   const bool active = lane < K;
   int32_t x = 0;
   float zt = 0.0f, zd = 0.0f;
+  bool keep_t = true, keep_d = true;  // x is kept by the target / draft row's truncation
   if (wave == 0 && active) {
     x = P.tokens[drow0 + lane];
     if constexpr (!kGreedy) {
@@ -916,6 +1390,10 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
         zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
         // with q rows, zd carries q(x) itself
         zd = kQ ? P.qrows[(int64_t)(drow0 + lane) * P.V + x] : E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+        if constexpr (kCut) {
+          keep_t = kept_by(P.cuts[trow0 + lane], zt, x);
+          if constexpr (!kQ) keep_d = kept_by(P.cuts[P.n_t + drow0 + lane], zd, x);
+        }
       }
     }
   }
@@ -930,7 +1408,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
 
   // 2. the verdict, by wave 0
   if (wave == 0) {
-    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0};
+    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0, Cut{-INFINITY, INT32_MAX}, Cut{-INFINITY, INT32_MAX}};
     if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
       write_reject(P, i, trow0, K, true, lane);
     } else if constexpr (kGreedy) {
@@ -962,10 +1440,11 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
           ratio = exp2((double)zt * (double)k2 - ft.l2) / (double)zd;
         } else {
           fd = rows[K + 1 + lane];
-          qzero = zd == -INFINITY;
+          qzero = zd == -INFINITY || !keep_d;  // a token the draft row does not keep has q = 0
           // log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
           ratio = exp2(((double)zt - (double)zd) * (double)k2 - (ft.l2 - fd.l2));
         }
+        if (!keep_t) ratio = 0.0;  // p(x) = 0
         if (P.r_each) {  // the caller's r in [0, 1): SDCP Rule 2, r < p/q
           r = P.r_each[drow0 + lane];
           accept = r < ratio;
@@ -998,6 +1477,10 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
           if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
         }
         d.a = a;
+        if constexpr (kCut) {
+          d.ct = P.cuts[trow0 + a];
+          d.cd = (!kQ && a < K) ? P.cuts[P.n_t + drow0 + a] : Cut{-INFINITY, INT32_MAX};
+        }
         if (!frontier) {  // emission stops inside the accepted drafts: nothing is drawn
           d.kind = SDV_TERM_NONE;
         } else if (a == K) {
@@ -1023,34 +1506,47 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     if (lane == 0) dec = d;
   }
   __syncthreads();
-  if constexpr (!kGreedy) draw_terminal<E, kVec, kQ>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
+  if constexpr (!kGreedy)
+    draw_terminal<E, kVec, kQ, kCut>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
 }
 
 // One workgroup per request.  With a profile per request, the request's temperature selects the
-// rule at run time (uniformly over the workgroup).
-template <class E, int kMode, bool kVec, bool kQ>
+// rule at run time (uniformly over the workgroup).  A top-k below 0 or a top-p outside
+// [0, 1000] thousandths describes no profile: the request is rejected under either rule.
+template <class E, int kMode, bool kVec, bool kQ, bool kCut>
 __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   extern __shared__ double lds_mass[];  // [C]
   __shared__ RowFold rows[kMaxRows];
   __shared__ Decision dec;
   const int32_t i = blockIdx.x;
+  const bool bad_truncation = (P.top_k && P.top_k[i] < 0) ||
+                              (P.top_p_milli && (P.top_p_milli[i] < 0 || P.top_p_milli[i] > 1000));
   if constexpr (kMode == kModeProfiled) {
     const float k2 = k2_of(temperature_of(P.temp_each, i));
     const uint64_t seed = P.seed_each[i];
-    if (k2 > 0.0f) verdict_body<E, false, kVec, kQ>(P, i, k2, seed, false, lds_mass, rows, dec);
-    else verdict_body<E, true, kVec, false>(P, i, 0.0f, seed, !(k2 == 0.0f), lds_mass, rows, dec);
+    if (k2 > 0.0f) verdict_body<E, false, kVec, kQ, kCut>(P, i, k2, seed, bad_truncation, lds_mass, rows, dec);
+    else verdict_body<E, true, kVec, false, false>(P, i, 0.0f, seed, !(k2 == 0.0f) || bad_truncation, lds_mass, rows, dec);
   } else {
-    verdict_body<E, kMode == kModeGreedy, kVec, kQ && kMode != kModeGreedy>(P, i, P.k2, P.seed, false, lds_mass, rows,
-                                                                            dec);
+    verdict_body<E, kMode == kModeGreedy, kVec, kQ && kMode != kModeGreedy, kCut && kMode != kModeGreedy>(
+        P, i, P.k2, P.seed, bad_truncation, lds_mass, rows, dec);
   }
 }
 
 // The correction or bonus draw of a request (T > 0), by the verdict workgroup.
-template <class E, bool kVec, bool kQ>
+template <class E, bool kVec, bool kQ, bool kCut>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves) {
   if (d.kind != SDV_TERM_BONUS && d.kind != SDV_TERM_RESIDUAL) return;  // uniform over the workgroup
+  typedef typename std::conditional<kCut, RowCuts, NoCut>::type Mask;
+  Mask m{};
+  if constexpr (kCut) {  // uniform over the workgroup: scalar registers
+    auto uniform = [](Cut c) {
+      return Cut{__int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c.kappa))),
+                 __builtin_amdgcn_readfirstlane(c.vcut)};
+    };
+    m = RowCuts{uniform(d.ct), uniform(d.cd)};
+  }
   const int32_t trow = trow0 + d.a;
   const char* tp = row_ptr<E>(P.target, trow, P.V);
   bool residual = d.kind == SDV_TERM_RESIDUAL;
@@ -1060,25 +1556,25 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   // residual masses of every chunk, into shared memory
   if (residual && kQ) {
     if constexpr (kVec) {
-      resid_masses_q<E>(tp, qp, P.V, P.C, k2, d.ref_t, d.q_scale, lds_mass, lane, wave, n_waves);
+      resid_masses_q<E>(m, tp, qp, P.V, P.C, k2, d.ref_t, d.q_scale, lds_mass, lane, wave, n_waves);
     } else {
       for (int32_t c = wave; c < P.C; c += n_waves) {
         const int32_t c0 = c * E::kChunk, c1 = min(c0 + E::kChunk, P.V);
-        double m = 0.0;
+        double cm = 0.0;
         for (int32_t v = c0 + lane; v < c1; v += kWave)
-          m += (double)resid_weight_q(E::at(tp, v), qp[v], k2, d.ref_t, d.q_scale);
-        m = wave_sum(m);
-        if (lane == 0) lds_mass[c] = m;
+          cm += (double)resid_weight_q(m, E::at(tp, v), qp[v], v, k2, d.ref_t, d.q_scale);
+        cm = wave_sum(cm);
+        if (lane == 0) lds_mass[c] = cm;
       }
     }
     __syncthreads();
   } else if (residual) {
     if constexpr (kVec) {
-      resid_masses_pipelined<E>(tp, dp, P.V, P.C, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
+      resid_masses_pipelined<E>(m, tp, dp, P.V, P.C, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
     } else {
       for (int32_t c = wave; c < P.C; c += n_waves) {
         const int32_t c0 = c * E::kChunk;
-        const double cm = resid_chunk_mass<E, false>(tp, dp, c0, min(E::kChunk, P.V - c0), k2, d.ref_t, d.e_hi,
+        const double cm = resid_chunk_mass<E, false>(m, tp, dp, c0, min(E::kChunk, P.V - c0), k2, d.ref_t, d.e_hi,
                                                      d.q_scale, lane);
         if (lane == 0) lds_mass[c] = cm;
       }
@@ -1096,6 +1592,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     residual = false;
     empty = true;
   }
+  // a draw from p takes the chunk masses from the row's records (kept masses under truncation)
   const float2* rec = rec_t + (int64_t)d.a * P.C;
   double tgt = 0.0;
   int32_t cs;
@@ -1111,25 +1608,26 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   int32_t y = -1;
   if constexpr (kVec) {
     if (residual && kQ)
-      y = search_chunk_q_block<E>(tp, qp, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave, n_waves);
+      y = search_chunk_q_block<E>(m, tp, qp, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave,
+                                  n_waves);
     else if (residual)
-      y = search_chunk_block<E, true>(tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane, wave,
-                                      n_waves);
+      y = search_chunk_block<E, true>(m, tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
+                                      wave, n_waves);
     else
-      y = search_chunk_block<E, false>(tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C, lane, wave,
-                                       n_waves);
+      y = search_chunk_block<E, false>(m, tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C, lane,
+                                       wave, n_waves);
   } else {
     if (wave != 0) return;
     const float ref_t = d.ref_t, e_hi = d.e_hi, q_scale = d.q_scale;
     if (residual && kQ)
-      y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return resid_weight_q(E::at(tp, v), qp[v], k2, ref_t, q_scale); },
-                          lane);
+      y = search_chunk<E>(
+          s0, n, tgt, [&](int32_t v) { return resid_weight_q(m, E::at(tp, v), qp[v], v, k2, ref_t, q_scale); }, lane);
     else if (residual)
-      y = search_chunk<E>(s0, n, tgt,
-                          [&](int32_t v) { return resid_weight(E::at(tp, v), E::at(dp, v), k2, ref_t, e_hi, q_scale); },
-                          lane);
+      y = search_chunk<E>(
+          s0, n, tgt,
+          [&](int32_t v) { return resid_weight(m, E::at(tp, v), E::at(dp, v), v, k2, ref_t, e_hi, q_scale); }, lane);
     else
-      y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return fast_exp2(fmaf(E::at(tp, v), k2, -ref_t)); }, lane);
+      y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return p_weight(m, E::at(tp, v), v, k2, ref_t); }, lane);
   }
   if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
     P.out_tokens[trow] = y;
@@ -1179,11 +1677,10 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 struct Layout {
   int32_t C;
   int64_t n_t, slots;
-  size_t part, total;
+  size_t part, cuts, total;
 };
 
 constexpr size_t kAlign = 256;
-constexpr int32_t kMaxChunks = 4096;          // residual chunk masses live in 32 KiB of shared memory
 constexpr size_t kVerdictLdsBytes = 48 * 1024;  // dynamic shared memory of the verdict workgroup
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -1207,6 +1704,7 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
     return at;
   };
   L->part = take((size_t)slots * C * sizeof(float2));
+  L->cuts = take((size_t)slots * sizeof(Cut));
   L->total = off;
   return SDV_OK;
 }
@@ -1222,6 +1720,15 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   hipLaunchKernelGGL((row_records<E, kMode, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(1);
+  // top-k / top-p: the cut of every logit row the verdicts read (the greedy rule keeps its argmax
+  // under any truncation, so it needs none)
+  const bool cut = kMode != kModeGreedy && (P.top_k || P.top_p_milli);
+  if (cut) {
+    const int64_t rows = P.qrows ? P.n_t : (int64_t)P.n_t + P.n_d;
+    hipLaunchKernelGGL((row_cuts<E, kVec>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+    record(3);
+  }
   // shared memory: C residual masses, then as many chunk records as the deepest request can need,
   // up to the budget; deeper requests fold straight from the workspace
   const int64_t want = (int64_t)(2 * SDV_MAX_DEPTH + 1) * P.C;
@@ -1230,10 +1737,15 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
   const dim3 grid((unsigned)P.B), block(kWave * kVerdictWaves);
   if constexpr (kMode != kModeGreedy) {  // the greedy rule never reads the draft side
-    if (P.qrows) hipLaunchKernelGGL((verdicts<E, kMode, kVec, true>), grid, block, lds, stream, P);
-    else hipLaunchKernelGGL((verdicts<E, kMode, kVec, false>), grid, block, lds, stream, P);
+    if (P.qrows) {
+      if (cut) hipLaunchKernelGGL((verdicts<E, kMode, kVec, true, true>), grid, block, lds, stream, P);
+      else hipLaunchKernelGGL((verdicts<E, kMode, kVec, true, false>), grid, block, lds, stream, P);
+    } else {
+      if (cut) hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, true>), grid, block, lds, stream, P);
+      else hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, false>), grid, block, lds, stream, P);
+    }
   } else {
-    hipLaunchKernelGGL((verdicts<E, kMode, kVec, false>), grid, block, lds, stream, P);
+    hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, false>), grid, block, lds, stream, P);
   }
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(2);
@@ -1316,6 +1828,10 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.budget = opt->budget;
   P.emitted_len = opt->emitted_len;
   P.qrows = q;
+  P.top_k = opt->top_k;
+  P.top_p_milli = opt->top_p_milli;
+  P.kept_tokens = opt->kept_tokens;
+  P.cuts = reinterpret_cast<Cut*>(ws + L.cuts);
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};

@@ -2,8 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY.  A request's verdict (accepted length and emitted tokens) must equal the
 oracle's exactly.  The only excuse is a first divergence at a decision the oracle itself took
-within ``eps`` of its threshold: an accept test with |r - p/q| < eps, or an extra-token draw whose
-CDF margin is below eps.  Greedy verdicts have no excuse.
+within ``eps`` of its threshold: an accept test with |r - p/q| < eps, an extra-token draw whose
+CDF margin is below eps, or (top-p) a row of the request whose nucleus cut lies within eps of its
+threshold, relative to the row's top-k mass (there the kept set itself may differ by one rank, and
+every probability of the row with it).  Greedy verdicts have no excuse.
 """
 from __future__ import annotations
 
@@ -29,6 +31,16 @@ def compare_verdicts(acc_gpu, out_gpu, ref: dict, cu, temperature, eps: float = 
         if acc_gpu[i] == acc_ref[i] and np.array_equal(out_gpu[s], out_ref[s]):
             continue
         t_i = temperature[i] if np.ndim(temperature) else temperature
+        fm = ref.get("filter_margin")
+        if t_i != 0 and fm is not None:
+            # a cut that moves by one rank can also decide whether a draft token is kept at all
+            n_t = out_ref.shape[0]
+            rows = list(range(int(cu[i]) + i, int(cu[i]) + i + K + 1))
+            rows += [n_t + int(cu[i]) + j for j in range(K) if n_t + int(cu[i]) + j < fm.shape[0]]
+            closest = float(np.min(fm[rows]))
+            if closest < eps:
+                excused.append((i, f"top-p cut at relative margin {closest:.3g}"))
+                continue
         if t_i == 0 or acc_ref[i] == -1 or acc_gpu[i] == -1:
             hard.append((i, f"accepted {acc_gpu[i]} vs {acc_ref[i]}"))
             continue

@@ -36,18 +36,20 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdv_abi_version() == 1
+    assert lib.sdv_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.sdv_status_string(code) not in (None, b"", b"unknown status")
     assert lib.sdv_status_string(17) == b"unknown status"
 
 
 def test_workspace_bytes(lib):
-    # row-pass records: 8 B per 16 KiB chunk of every target and draft row, 256-byte aligned
+    # row-pass records: 8 B per 16 KiB chunk of every target and draft row, then one 8-byte
+    # top-k / top-p cut per row, each array 256-byte aligned
     ws = lib.sdv_workspace_bytes(256, 1024, 128256, 0)
     chunks = (128256 + 8191) // 8192
     assert chunks == 16
-    assert ws == -(-(1280 + 1024) * chunks * 8 // 256) * 256
+    rows = 1280 + 1024
+    assert ws == -(-rows * chunks * 8 // 256) * 256 + -(-rows * 8 // 256) * 256
     assert ws % 256 == 0
     assert lib.sdv_workspace_bytes(0, 10, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, -1, 10, 0) == 0
