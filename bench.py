@@ -14,7 +14,7 @@ a plain read of the same size with the row pass's loads, per-call percentiles, a
 statistics and the CPU oracle's rate on the host.
 
   python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1|ragged_b256_profiled|
-                              ragged_b256_qrows]
+                              ragged_b256_qrows|ragged_b256_topk50_topp900]
                   [--steps K] [--warmup W]
 
 Profile summaries (rocprofv3 output -> text under profiles/):
@@ -42,6 +42,7 @@ METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=25
 KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
                   "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
 KERNELS = ["row_records", "verdicts"]
+TRUNCATION_KERNELS = ["row_records", "row_cuts", "verdicts"]
 CHUNK_BYTES = 16384
 
 
@@ -68,6 +69,9 @@ def make_workload(name: str, set_index: int):
         return W.small_b1(set_index)
     if name == "ragged_b256_qrows":  # the draft side as distributions (SDCP q_rows), float32
         return W.with_qrows(W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000))
+    if name == "ragged_b256_topk50_topp900":  # top-k 50, then top-p 0.9, on every request
+        return W.with_truncation(W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000),
+                                 50, 900)
     if name == "ragged_b256_profiled":  # one sampling profile per request: a quarter greedy
         base = W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000)
         t, s = W.mixed_profiles(base.B, np.random.default_rng(W.DATA_SEED_BASE + 6 + set_index))
@@ -75,20 +79,31 @@ def make_workload(name: str, set_index: int):
     raise SystemExit(f"unknown workload {name}")
 
 
-def pmc_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"row_records_{workload}_pmc.json")
+def pmc_path(workload: str, kernel: str = "row_records") -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per row_records launch from the committed rocprofv3 counter summary, if it was taken
+def traffic_from_profile(workload: str, kernel: str = "row_records"):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary, if it was taken
     on the current kernel source; else None."""
-    path = pmc_path(workload)
+    path = pmc_path(workload, kernel)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("row_records", {}).get("traffic_bytes_per_launch")
+    return rec.get(kernel, {}).get("traffic_bytes_per_launch")
+
+
+def truncated_bytes(b) -> int:
+    """Algorithmic bytes of the truncation kernel: every logit of every row it cuts, read once (the
+    target and draft rows of each request that samples with a profile that truncates)."""
+    if b.top_k is None:
+        return 0
+    T = b.temp_each if b.temp_each is not None else np.full(b.B, b.temperature)
+    cuts = (T > 0) & (((b.top_k > 0) & (b.top_k < b.V)) | ((b.top_p_milli >= 0) & (b.top_p_milli < 1000)))
+    rows = np.sum((b.depths + 1)[cuts]) + (0 if b.qrows is not None else np.sum(b.depths[cuts]))
+    return int(rows) * b.V * b.elem_bytes
 
 
 def oracle_profile(b):
@@ -96,6 +111,16 @@ def oracle_profile(b):
     if b.temp_each is not None:
         return b.temp_each.astype(np.float64), b.seed_each
     return b.temperature, b.seed
+
+
+def oracle_options(b) -> dict:
+    """The batch's other per-request inputs, as the oracle takes them."""
+    kw = {}
+    if b.qrows is not None:
+        kw["draft_probs"] = b.qrows
+    if b.top_k is not None:
+        kw["top_k"], kw["top_p_milli"] = b.top_k, b.top_p_milli
+    return kw
 
 
 def cpu_baseline(batch, budget_s: float):
@@ -108,7 +133,7 @@ def cpu_baseline(batch, budget_s: float):
         while True:
             t0 = time.perf_counter()
             oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, *oracle_profile(batch),
-                          **({} if batch.qrows is None else {"draft_probs": batch.qrows}))
+                          **oracle_options(batch))
             times.append(time.perf_counter() - t0)
             if len(times) >= 3 or time.perf_counter() > t_end:
                 return float(np.median(times)), len(times)
@@ -170,7 +195,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1",
-                                                           "ragged_b256_profiled", "ragged_b256_qrows"])
+                                                           "ragged_b256_profiled", "ragged_b256_qrows",
+                                                           "ragged_b256_topk50_topp900"])
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through the timed steps (0: enough for 1 GB, at least 2, at most 32)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing (0 = skip)")
@@ -181,6 +207,7 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--bench-json", help="bench output of the profiled run (for --summarize-trace)")
     ap.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (--summarize-pmc)")
+    ap.add_argument("--kernel", default="row_records", help="the kernel a counter summary is for (--summarize-pmc)")
     ap.add_argument("--command", default="", help="the command that produced the profile")
     args = ap.parse_args()
     if args.summarize_trace:
@@ -222,7 +249,12 @@ def main():
         if b.temp_each is not None:  # one sampling profile per request, as device arrays
             sets[-1]["temp"] = torch.from_numpy(b.temp_each.astype(np.float32)).to(dev)
             sets[-1]["seeds"] = torch.from_numpy(b.seed_each.astype(np.uint64).view(np.int64)).to(dev)
+        if b.top_k is not None:
+            sets[-1]["top_k"] = torch.from_numpy(b.top_k).to(dev)
+            sets[-1]["top_p_milli"] = torch.from_numpy(b.top_p_milli).to(dev)
     B0 = batches[0]
+    truncating = B0.top_k is not None
+    kernels = TRUNCATION_KERNELS if truncating else KERNELS
     positions = [int(b.cu[-1]) for b in batches]
     rows = [int(b.cu[-1]) + b.B for b in batches]
     alg_bytes = [b.algorithmic_bytes() for b in batches]
@@ -237,7 +269,8 @@ def main():
         b = s["batch"]
         temperature, seed = (s["temp"], s["seeds"]) if "temp" in s else (b.temperature, b.seed + k)
         sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], temperature, seed,
-                      out=outs[k % len(sets)], workspace=ws, events=events, draft_probs=s.get("qrows"))
+                      out=outs[k % len(sets)], workspace=ws, events=events, draft_probs=s.get("qrows"),
+                      top_k=s.get("top_k"), top_p_milli=s.get("top_p_milli"))
 
     # correctness of the timed configuration, once, against the oracle
     parity = None
@@ -247,7 +280,7 @@ def main():
         step(0)
         torch.cuda.synchronize()
         ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, *oracle_profile(B0), diag=True,
-                            **({} if B0.qrows is None else {"draft_probs": B0.qrows}))
+                            **oracle_options(B0))
         cmp = compare_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ref, B0.cu, oracle_profile(B0)[0])
         parity = {"requests": cmp["requests"], "hard_mismatches": cmp["n_hard"], "near_tie_excused": cmp["n_excused"]}
         if cmp["n_hard"]:
@@ -274,9 +307,10 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # a second pass with HIP events that the library records on its stream before the first kernel
-    # and after each kernel: per-kernel and per-call durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    # a second pass with HIP events that the library records on its stream: [0] before the first
+    # kernel, [1] after the row pass, [3] after the truncation kernel (when it runs), [2] after the
+    # verdicts; per-kernel and per-call durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record()  # instantiate the handles
@@ -284,9 +318,10 @@ def main():
     for k in range(args.steps):
         step(args.warmup + k, events=evs[k])
     torch.cuda.synchronize()
-    per_kernel = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)]))
-                  for j in range(len(KERNELS))]
-    per_call = np.array([evs[k][0].elapsed_time(evs[k][-1]) for k in range(args.steps)])
+    order = [0, 1, 3, 2] if truncating else [0, 1, 2]
+    per_kernel = [float(np.mean([evs[k][order[j]].elapsed_time(evs[k][order[j + 1]]) for k in range(args.steps)]))
+                  for j in range(len(kernels))]
+    per_call = np.array([evs[k][0].elapsed_time(evs[k][2]) for k in range(args.steps)])
 
     # the bandwidth yardstick: the row pass's loads with no arithmetic over buffers of the call's size
     n_chunks = int(np.mean(alg_bytes)) // CHUNK_BYTES
@@ -327,6 +362,13 @@ def main():
     value = mean_pos / (ms_step * 1e-3)
     call_gbps = mean_bytes / (ms_step * 1e-3) / 1e9
     rowpass_gbps = mean_stream / (per_kernel[0] * 1e-3) / 1e9
+    # the roofline object describes the longest kernel with algorithmic bytes of its own: the row
+    # pass, or the truncation kernel when it takes longer
+    roof_kernel, roof_bytes, roof_ms = "row_records", mean_stream, per_kernel[0]
+    if truncating and per_kernel[1] > per_kernel[0]:
+        roof_bytes = float(np.mean([truncated_bytes(batches[(args.warmup + k) % len(sets)]) for k in range(args.steps)]))
+        roof_kernel, roof_ms = "row_cuts", per_kernel[1]
+    roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -344,6 +386,8 @@ def main():
         "config": {"workload": B0.name, "B": B0.B, "V": B0.V,
                    "temperature": B0.temperature if B0.temp_each is None else
                    {f"{t:g}": int(n) for t, n in zip(*np.unique(B0.temp_each, return_counts=True))},
+                   **({} if B0.top_k is None else {"top_k": int(B0.top_k[0]), "top_p_milli": int(B0.top_p_milli[0]),
+                                                    "drafts": "argmax of the draft row"}),
                    "sum_K_per_call": positions, "input_sets": len(sets),
                    "algorithmic_bytes_per_call": alg_bytes},
         "hbm_gbps": call_gbps,
@@ -354,14 +398,16 @@ def main():
         "committed_tokens_per_s": stats["committed_tokens_per_call"] / (ms_step * 1e-3),
         "call_ms_events": {"median": float(np.median(per_call)), "p5": float(np.percentile(per_call, 5)),
                            "p95": float(np.percentile(per_call, 95)), "n": int(per_call.size)},
-        "kernel_ms": dict(zip(KERNELS, per_kernel)),
+        "kernel_ms": dict(zip(kernels, per_kernel)),
         "terminal_reread_bytes_per_call": float(np.mean(rereads)),
         "terminal_reread_frac_of_algorithmic": float(np.mean(rereads)) / mean_bytes,
         "acceptance": stats,
-        "roofline": {"bound": "hbm", "achieved": rowpass_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": rowpass_gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(args.workload),
-                     "kernel": "row_records", "algorithmic_bytes_per_launch": mean_stream,
-                     "frac_of_read_ceiling": rowpass_gbps / read_gbps},
+        "roofline": {"bound": "hbm", "achieved": roof_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": roof_gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(args.workload, roof_kernel),
+                     "kernel": roof_kernel, "algorithmic_bytes_per_launch": roof_bytes,
+                     "frac_of_read_ceiling": roof_gbps / read_gbps},
+        "row_pass": {"achieved_gbps": rowpass_gbps, "frac": rowpass_gbps / PEAK_HBM_GBPS,
+                     "algorithmic_bytes_per_launch": mean_stream},
         "parity": parity,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -376,7 +422,7 @@ def main():
 # ----------------------------------------------------------------------------- profile summaries
 
 def _short(name: str) -> str:
-    for k in KERNELS + ["read_kernel", "philox_kernel"]:
+    for k in TRUNCATION_KERNELS + ["read_kernel", "philox_kernel"]:
         if f"sdv{len(k)}{k}" in name or f"::{k}" in name or name.startswith(k):
             return k
     return name.split("(")[0][:48]
@@ -402,8 +448,9 @@ def summarize_trace(args):
     if bench:
         lines += ["", "The same run's bench line (HIP events on the library's stream):", "",
                   f"- kernel_ms: {json.dumps({k: round(v * 1e3, 2) for k, v in bench['kernel_ms'].items()})} (us)",
-                  f"- ms_per_step: {bench['ms_per_step'] * 1e3:.2f} us; roofline frac of row_records: "
-                  f"{bench['roofline']['frac']:.4f}; kernel_source_hash {bench['kernel_source_hash']}"]
+                  f"- ms_per_step: {bench['ms_per_step'] * 1e3:.2f} us; roofline frac of "
+                  f"{bench['roofline'].get('kernel', 'row_records')}: {bench['roofline']['frac']:.4f}; "
+                  f"kernel_source_hash {bench['kernel_source_hash']}"]
     out = os.path.join(ROOT, "profiles", f"kernels_{args.workload}_trace.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -433,11 +480,12 @@ def summarize_pmc(args):
     fetch, f_fac, f_copy = per_kernel(args.summarize_pmc[0], "FETCH_SIZE")
     write, w_fac, w_copy = per_kernel(args.summarize_pmc[1], "WRITE_SIZE")
     batches = [make_workload(args.workload, s) for s in range(2)]
-    alg = float(np.mean([b.algorithmic_bytes() for b in batches]))
+    kern = args.kernel
+    alg = float(np.mean([truncated_bytes(b) if kern == "row_cuts" else b.algorithmic_bytes() for b in batches]))
     rec = {"kernel_source_hash": kernel_source_hash(), "workload": args.workload, "command": args.command,
            "calibration": {"copy_bytes": copy_kib * 1024, "fetch_kib_read": f_copy, "write_kib_read": w_copy,
                            "fetch_factor": f_fac, "write_factor": w_fac},
-           "algorithmic_bytes_per_row_records_launch": alg}
+           f"algorithmic_bytes_per_{kern}_launch": alg}
     lines = [f"# HBM traffic per launch: {args.workload}", "", "Commands ($REPO is the repository root):", "",
              "```", args.command, "```", "",
              f"Calibration: a {args.copy_mib} MiB device copy reads FETCH_SIZE {f_copy:.0f} KiB "
@@ -449,12 +497,12 @@ def summarize_pmc(args):
         wb = write.get(k, 0.0) * 1024 * w_fac
         rec[k] = {"fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb}
         lines.append(f"| {k} | {fetch.get(k, 0):.0f} | {write.get(k, 0):.0f} | {fb:.4g} | {wb:.4g} |")
-    if "row_records" in rec:
-        lines += ["", f"row_records: traffic {rec['row_records']['traffic_bytes_per_launch']:.4g} B against "
+    if kern in rec:
+        lines += ["", f"{kern}: traffic {rec[kern]['traffic_bytes_per_launch']:.4g} B against "
                       f"{alg:.4g} algorithmic bytes per launch "
-                      f"(ratio {rec['row_records']['traffic_bytes_per_launch'] / alg:.4f})."]
-    json.dump(rec, open(pmc_path(args.workload), "w"), indent=1)
-    out = os.path.join(ROOT, "profiles", f"row_records_{args.workload}_pmc.md")
+                      f"(ratio {rec[kern]['traffic_bytes_per_launch'] / alg:.4f})."]
+    json.dump(rec, open(pmc_path(args.workload, kern), "w"), indent=1)
+    out = os.path.join(ROOT, "profiles", f"{kern}_{args.workload}_pmc.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

@@ -822,20 +822,32 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
 // ============================================================================ 2. truncation
 // SDCP ("Speculative Decoding Coordination Protocol (SDCP)", section "Session Contract") defines p
 // as the model's distribution after temperature, then top-k, then top-p.  One workgroup per logit
-// row finds the row's cut by an exact radix select over an order-preserving key of the logits:
-// counts and fixed-point masses per digit go into LDS histograms, the descending scan of a
-// histogram picks the digit that holds the top_k-th rank (top-k) or where the running mass
-// reaches the nucleus mass (top-p), and the next level refines inside that digit.  Ranks that tie
-// on a logit differ only in token id, so the last level ends on one logit value, and the number of
-// its copies to keep follows from counts alone.  A last pass over the row finds the token id of
-// the last kept copy and rewrites each chunk record's mass to the mass of the chunk's kept tokens,
-// so the verdict kernel's fold yields the truncated normaliser unchanged.
+// row finds the row's cut: the value of the last kept rank and how many of its copies are kept
+// (ranks that tie on a logit differ only in token id).  Both follow from a histogram over an
+// order-preserving key of the logits.
+//
+//  bf16 rows     one pass counts the logits of each of the 4096 keys below the row maximum's (the
+//                chunk records give the maximum); every copy of a key has the same mass, so counts
+//                alone give masses.  Logits below that window are only counted.  Profiles that cut
+//                inside the window (the cut of top-k / top-p lies among the largest logits) are
+//                settled from these counts;
+//  other cases   an exact radix select: per digit level, counts and fixed-point masses of the
+//                logits that share the higher digits, and the level's scan picks the digit
+//                holding the top_k-th rank (top-k) or where the running mass reaches the nucleus
+//                mass (top-p).
+//
+// Masses are 2^(z k - R) as fixed-point integers (R = fl(max z * k)): integer sums do not depend on
+// the order of the atomic adds, so the cut is the same on every run.  A last pass over the row
+// finds the token id of the last kept copy and rewrites each chunk record's mass to the mass of
+// the chunk's kept tokens, so the verdict kernel's fold yields the truncated normaliser unchanged.
 
-constexpr int kCutWaves = 16;
-constexpr int kCutThreads = kWave * kCutWaves;
-constexpr int kCutUnroll = 8;          // 16-byte loads in flight per thread in a histogram pass
-constexpr int kRadixBins = 1 << 11;    // the widest digit
-constexpr float kFixScale = 0x1.0p37f;  // masses 2^(z k - R) <= ~1 as integers: V 2^37 < 2^63
+constexpr int kCutWaves = 8;
+constexpr int kCutThreads = kWave * kCutWaves;  // several workgroups per CU: rows overlap
+constexpr int kRadixBins = 1 << 11;             // the widest digit
+constexpr int kBinsPerThread = kRadixBins / kCutThreads;
+constexpr int kRegionKeys = 4096;               // bf16 keys counted one by one below the maximum's
+constexpr int kKeysPerThread = kRegionKeys / kCutThreads;
+constexpr float kFixScale = 0x1.0p37f;          // masses <= ~1 as integers: V 2^37 < 2^63
 
 // Digits of the order key, most significant first: bf16 keys carry 16 bits (11 + 5), binary32
 // keys 32 (11 + 11 + 10).
@@ -863,38 +875,18 @@ __device__ __forceinline__ uint32_t order_key(float z) {
 __device__ __forceinline__ float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
+// The 16-bit key of a bf16 logit (its raw bits h), and the 32-bit key of a 16-bit one: below the
+// 16 bits a bf16 key holds 16 copies of its sign bit's complement.
+__device__ __forceinline__ uint32_t key16_of_bits(uint32_t h) {
+  h = h == 0x8000u ? 0u : h;
+  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t key16_to_key(uint32_t key) {
+  return (key << 16) | ((key & 0x8000u) ? 0u : 0xffffu);
+}
 
 __device__ __forceinline__ uint64_t fixed_mass(float z, float k2, float R) {
   return (uint64_t)(fast_exp2(fmaf(z, k2, -R)) * kFixScale);
-}
-
-// Every logit of a row, visited by the workgroup with coalesced loads (f(z, v)).
-template <class E, bool kVec, class F>
-__device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
-  if constexpr (kVec) {
-    const u32x4* vp = reinterpret_cast<const u32x4*>(rp);
-    const int32_t nvec = V / E::kPerVec;  // 16-byte rows: no partial vector
-    for (int32_t base = 0; base < nvec; base += kCutUnroll * kCutThreads) {
-      u32x4 buf[kCutUnroll];
-#pragma unroll
-      for (int u = 0; u < kCutUnroll; ++u) {
-        const int32_t vi = base + u * kCutThreads + (int32_t)threadIdx.x;
-        buf[u] = vi < nvec ? vp[vi] : neg_inf_vec<E>();
-      }
-#pragma unroll
-      for (int u = 0; u < kCutUnroll; ++u) {
-        const int32_t vi = base + u * kCutThreads + (int32_t)threadIdx.x;
-        if (vi < nvec) {
-          float z[E::kPerVec];
-          E::unpack(buf[u], z);
-#pragma unroll
-          for (int e = 0; e < E::kPerVec; ++e) f(z[e], vi * E::kPerVec + e);
-        }
-      }
-    }
-  } else {
-    for (int32_t v = threadIdx.x; v < V; v += kCutThreads) f(E::at(rp, v), v);
-  }
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
@@ -911,51 +903,20 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 struct CutShared {
   uint32_t wave_cnt[kCutWaves];
   uint64_t wave_mass[kCutWaves];
+  double wave_real[kCutWaves];
   float wave_ref[kCutWaves];
   int32_t cand, last;
   uint32_t pick_digit, pick_cnt_above, pick_cnt;
   uint64_t pick_mass_above;
 };
 
-// The histogram of one digit level over the logits whose higher digits equal prefix: counts, and
-// masses 2^(z k - R) as fixed-point integers (integer sums do not depend on the order of the
-// atomic adds, so the cut is the same on every run).
-template <class E, bool kVec>
-__device__ __forceinline__ void histogram(const char* rp, int32_t V, float k2, float R, int L, uint32_t prefix,
-                                          uint32_t* cnt, uint64_t* mass) {
-  const int shift = Radix<E>::shift(L), nb = 1 << Radix<E>::width(L);
-  const int hi = shift + Radix<E>::width(L);
-  for (int b = threadIdx.x; b < nb; b += kCutThreads) {
-    cnt[b] = 0u;
-    mass[b] = 0ull;
-  }
-  __syncthreads();
-  for_each_logit<E, kVec>(rp, V, [&](float z, int32_t) {
-    const uint32_t key = order_key(z);
-    if (L > 0 && (key >> hi) != prefix) return;
-    const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
-    atomicAdd(&cnt[d], 1u);
-    atomicAdd(reinterpret_cast<unsigned long long*>(&mass[d]), (unsigned long long)fixed_mass(z, k2, R));
-  });
-  __syncthreads();
-}
-
-// The bin a selection lands in, scanning the bins from the largest digit down: by count, the bin
-// that holds the need-th logit; by mass, the first non-empty bin where mass_before plus the running
-// mass reaches target.  Leaves in sh the digit, the count and mass of the higher bins and the bin's
-// count.  If no bin qualifies (rounding), the last non-empty bin is taken.
-__device__ __forceinline__ void select_bin(const uint32_t* cnt, const uint64_t* mass, int nb, bool by_mass,
-                                           uint32_t need, double target, uint64_t mass_before, CutShared& sh) {
+// Exclusive scan over the workgroup's threads, in thread order, of a (count, mass) pair, and the
+// totals.
+__device__ __forceinline__ void block_scan(uint32_t c, uint64_t m, uint32_t& c_before, uint64_t& m_before,
+                                           uint64_t& c_total, uint64_t& m_total, CutShared& sh) {
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  if (t == 0) {
-    sh.cand = INT32_MAX;
-    sh.last = -1;
-  }
-  const int p0 = 2 * t, p1 = 2 * t + 1;  // positions in descending digit order
-  const uint32_t c0 = p0 < nb ? cnt[nb - 1 - p0] : 0u, c1 = p1 < nb ? cnt[nb - 1 - p1] : 0u;
-  const uint64_t m0 = p0 < nb ? mass[nb - 1 - p0] : 0ull, m1 = p1 < nb ? mass[nb - 1 - p1] : 0ull;
-  uint32_t ci = c0 + c1;
-  uint64_t mi = m0 + m1;
+  uint32_t ci = c;
+  uint64_t mi = m;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const uint32_t uc = __shfl_up(ci, o, kWave);
@@ -971,38 +932,24 @@ __device__ __forceinline__ void select_bin(const uint32_t* cnt, const uint64_t* 
   }
   __syncthreads();
   uint32_t cb = 0u;
-  uint64_t mb = 0ull;
-  for (int w = 0; w < wave; ++w) {
-    cb += sh.wave_cnt[w];
-    mb += sh.wave_mass[w];
+  uint64_t mb = 0ull, ct = 0ull, mt = 0ull;
+  for (int w = 0; w < kCutWaves; ++w) {
+    if (w < wave) {
+      cb += sh.wave_cnt[w];
+      mb += sh.wave_mass[w];
+    }
+    ct += sh.wave_cnt[w];
+    mt += sh.wave_mass[w];
   }
-  const uint32_t ce0 = cb + ci - (c0 + c1), ce1 = ce0 + c0;
-  const uint64_t me0 = mb + mi - (m0 + m1), me1 = me0 + m0;
-  auto hit = [&](uint32_t ce, uint64_t me, uint32_t c, uint64_t m) {
-    if (by_mass) return c > 0u && (double)(mass_before + me + m) >= target;
-    return ce < need && need <= ce + c;
-  };
-  int cand = INT32_MAX, last = -1;
-  if (p1 < nb && hit(ce1, me1, c1, m1)) cand = p1;
-  if (p0 < nb && hit(ce0, me0, c0, m0)) cand = p0;
-  if (p0 < nb && c0) last = p0;
-  if (p1 < nb && c1) last = p1;
-  atomicMin(&sh.cand, cand);
-  atomicMax(&sh.last, last);
-  __syncthreads();
-  const int ps = sh.cand != INT32_MAX ? sh.cand : max(sh.last, 0);
-  if (ps == p0 || ps == p1) {
-    const bool first = ps == p0;
-    sh.pick_digit = (uint32_t)(nb - 1 - ps);
-    sh.pick_cnt_above = first ? ce0 : ce1;
-    sh.pick_mass_above = first ? me0 : me1;
-    sh.pick_cnt = first ? c0 : c1;
-  }
-  __syncthreads();
+  __syncthreads();  // the wave totals may be overwritten after this
+  c_before = cb + ci - c;
+  m_before = mb + mi - m;
+  c_total = ct;
+  m_total = mt;
 }
 
-// A radix selection's outcome: the key of the last kept logit value, how many tokens rank above
-// that value, their mass, and how many tokens carry the value.
+// A selection's outcome: the key of the last kept logit value, how many tokens rank above that
+// value, their mass, and how many tokens carry the value.
 struct Selected {
   uint32_t key;
   uint32_t cnt_above;
@@ -1010,18 +957,392 @@ struct Selected {
   uint32_t ties;
 };
 
+// The fewest copies (at least one) of a value of per-copy mass e that bring the running mass from
+// above to target; the selected value's copies reach it, so the estimate starts within a rounding
+// step of the answer and the corrections are short.  Capped at the copies there are.
+__device__ __forceinline__ uint32_t copies_to_reach(uint64_t above, uint64_t e, uint32_t ties, double target) {
+  uint64_t n = 1ull;
+  if (e > 0ull && (double)(above + e) < target) {
+    const double est = ceil((target - (double)above) / (double)e);
+    n = est >= (double)ties ? (uint64_t)ties : (uint64_t)est;
+    while (n > 1ull && (double)(above + (n - 1ull) * e) >= target) --n;
+    while (n < ties && (double)(above + n * e) < target) ++n;
+  }
+  return (uint32_t)(n > ties ? ties : n);
+}
+
+// The bin a selection lands in, scanning bins from the largest down: by count, the bin holding
+// the need-th logit; by mass, the first non-empty bin where mass_before plus the running mass
+// reaches target; failing both (rounding), the last non-empty bin.  bins[p] for p in rank order is
+// bin nb - 1 - p; thread t takes ranks kPer t .. kPer t + kPer - 1.  Leaves the bin, the count and
+// mass of the bins before it, and its count in sh.pick_*.
+template <int kPer, class BinCount, class BinMass>
+__device__ __forceinline__ void select_bin(int nb, BinCount count_of, BinMass mass_of, bool by_mass, uint32_t need,
+                                           double target, uint64_t mass_before, CutShared& sh) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    sh.cand = INT32_MAX;
+    sh.last = -1;
+  }
+  uint32_t c[kPer];
+  uint64_t m[kPer];
+  uint32_t csum = 0u;
+  uint64_t msum = 0ull;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int p = kPer * t + q;
+    c[q] = p < nb ? count_of(nb - 1 - p) : 0u;
+    m[q] = p < nb ? mass_of(nb - 1 - p) : 0ull;
+    csum += c[q];
+    msum += m[q];
+  }
+  uint32_t cb;
+  uint64_t mb, ct, mt;
+  block_scan(csum, msum, cb, mb, ct, mt, sh);
+  int cand = INT32_MAX, last = -1;
+  uint32_t run_c = cb;
+  uint64_t run_m = mb;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int p = kPer * t + q;
+    const bool hit = by_mass ? (c[q] > 0u && (double)(mass_before + run_m + m[q]) >= target)
+                             : (run_c < need && need <= run_c + c[q]);
+    if (p < nb && hit && cand == INT32_MAX) cand = p;
+    if (p < nb && c[q] > 0u) last = p;
+    run_c += c[q];
+    run_m += m[q];
+  }
+  atomicMin(&sh.cand, cand);
+  atomicMax(&sh.last, last);
+  __syncthreads();
+  const int ps = sh.cand != INT32_MAX ? sh.cand : max(sh.last, 0);
+  if (ps / kPer == t) {
+    uint32_t above_c = cb;
+    uint64_t above_m = mb;
+    for (int q = 0; q < ps - kPer * t; ++q) {
+      above_c += c[q];
+      above_m += m[q];
+    }
+    sh.pick_digit = (uint32_t)(nb - 1 - ps);
+    sh.pick_cnt_above = above_c;
+    sh.pick_mass_above = above_m;
+    sh.pick_cnt = c[ps - kPer * t];
+  }
+  __syncthreads();
+}
+
+// Every logit of a row, visited by the workgroup (f(z, bits, v); bits are the logit's raw 16 bits
+// for bf16 rows).  16-byte rows go by chunks, as the row pass reads them: wave w takes chunks w,
+// w + 8, ..., each loaded whole (16 vectors per lane, 16 KiB in flight per wave) before it is
+// visited; the partial last chunk goes through bounds-tested loads.
+template <class E, bool kVec, class F>
+__device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  auto visit = [&](const u32x4& v, int32_t vi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (E::kBytes == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f(__uint_as_float(w[q] << 16), w[q] & 0xffffu, vi * 8 + 2 * q);
+        f(__uint_as_float(w[q] & 0xffff0000u), w[q] >> 16, vi * 8 + 2 * q + 1);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f(__uint_as_float(w[q]), 0u, vi * 4 + q);
+    }
+  };
+  if constexpr (kVec) {
+    const u32x4* vp = reinterpret_cast<const u32x4*>(rp);
+    constexpr int32_t kVecPerChunk = E::kChunk / E::kPerVec;
+    const int32_t C_full = V / E::kChunk, nvec = V / E::kPerVec;  // 16-byte rows: no partial vector
+    for (int32_t c = wave; c < C_full; c += kCutWaves) {
+      const u32x4* cp = vp + (int64_t)c * kVecPerChunk;
+      u32x4 buf[kVecPerLane];
+#pragma unroll
+      for (int k = 0; k < kVecPerLane; ++k) buf[k] = cp[lane + kWave * k];
+#pragma unroll
+      for (int k = 0; k < kVecPerLane; ++k) {
+        // one vector at a time: its keys are not all computed ahead of the atomics
+        asm volatile("" : "+v"(buf[k])::"memory");
+        visit(buf[k], c * kVecPerChunk + lane + kWave * k);
+      }
+    }
+    if (C_full * kVecPerChunk < nvec && C_full % kCutWaves == wave) {  // the partial last chunk
+      for (int32_t vi = C_full * kVecPerChunk + lane; vi < nvec; vi += kWave) visit(vp[vi], vi);
+    }
+  } else {
+    for (int32_t v = threadIdx.x; v < V; v += kCutThreads) {
+      if constexpr (E::kBytes == 2) {
+        const uint32_t h = reinterpret_cast<const uint16_t*>(rp)[v];
+        f(__uint_as_float(h << 16), h, v);
+      } else {
+        f(E::at(rp, v), 0u, v);
+      }
+    }
+  }
+}
+
+// bf16 rows: the counts of the 4096 keys top - 4095 .. top, top just above the row maximum's key
+// (from R = fl(max z * k), whose quotient by k lies within a rounding step of the maximum).  Logits
+// below the window are counted apart.  With top-p over the whole row (no top-k) the nucleus mass
+// is a share of the row's mass, folded from the chunk records (binary32 chunk sums, fp64 across
+// chunks; their relative error stays below 1e-6).  Returns true with the cut in s / n_eq when the
+// selection ends inside the window; false sends the row to the radix select.
+template <bool kVec>
+__device__ __forceinline__ bool window_select(const char* rp, int32_t V, int32_t C, const float2* rec, float k2,
+                                              float R, bool by_k, int32_t top_k, bool by_p, int32_t milli,
+                                              uint32_t* cnt, CutShared& sh, Selected& s, uint32_t& n_eq) {
+  const int t = threadIdx.x;
+  const float m_hat = R / k2;
+  const uint32_t k_hat = key16_of_bits(__float_as_uint(m_hat) >> 16);
+  const uint32_t top = k_hat + 4u > 65535u ? 65535u : k_hat + 4u;
+  const uint32_t bottom = top >= (uint32_t)(kRegionKeys - 1) ? top - (uint32_t)(kRegionKeys - 1) : 0u;
+  for (int j = t; j < kRegionKeys; j += kCutThreads) cnt[j] = 0u;
+  __syncthreads();
+  uint32_t above = 0u;
+  for_each_logit<Bf16, kVec>(rp, V, [&](float, uint32_t h, int32_t) {
+    const uint32_t key = key16_of_bits(h);
+    if (key > top) ++above;
+    else if (key >= bottom) atomicAdd(&cnt[key - bottom], 1u);
+  });
+  // the row's mass in fixed point, from the chunk records
+  double part = 0.0;
+  for (int32_t c = t; c < C; c += kCutThreads)
+    if (rec[c].y > 0.0f) part += (double)rec[c].y * exp2((double)rec[c].x - (double)R);
+  part = wave_sum(part);
+  if ((t & (kWave - 1)) == 0) sh.wave_real[t / kWave] = part;
+  __syncthreads();
+  double row_mass = 0.0;
+  for (int w = 0; w < kCutWaves; ++w) row_mass += sh.wave_real[w];
+  const uint64_t mass_all = (uint64_t)(row_mass * (double)kFixScale);
+  {
+    uint32_t cb;
+    uint64_t mb, ct, mt;
+    block_scan(above, 0ull, cb, mb, ct, mt, sh);
+    if (ct != 0ull) return false;  // a logit above the window: the maximum was misjudged
+  }
+  // runs of kKeysPerThread keys, thread order = rank order
+  const int32_t hi = (int32_t)top - kKeysPerThread * t;
+  uint32_t c = 0u;
+  uint64_t m = 0ull;
+#pragma unroll
+  for (int j = 0; j < kKeysPerThread; ++j) {
+    const int32_t key = hi - j;
+    const uint32_t n = key >= (int32_t)bottom ? cnt[key - (int32_t)bottom] : 0u;
+    c += n;
+    if (by_p && n) m += (uint64_t)n * fixed_mass(key_logit(key16_to_key((uint32_t)key)), k2, R);
+  }
+  uint32_t cb;
+  uint64_t mb, ct, mt;
+  block_scan(c, m, cb, mb, ct, mt, sh);
+  if (by_k && (uint64_t)top_k > ct) return false;  // the top-k cut lies below the window
+  // the key inside a run where a selection lands, by the run's owner
+  auto pick_in_run = [&](bool by_mass, uint32_t need, double target) {
+    uint32_t run_c = cb;
+    uint64_t run_m = mb;
+    int32_t last = -1;
+    for (int j = 0; j < kKeysPerThread; ++j) {
+      const int32_t key = hi - j;
+      const uint32_t n = key >= (int32_t)bottom ? cnt[key - (int32_t)bottom] : 0u;
+      const uint64_t mm = (by_p && n) ? (uint64_t)n * fixed_mass(key_logit(key16_to_key((uint32_t)key)), k2, R) : 0ull;
+      const bool hit = by_mass ? (n > 0u && (double)(run_m + mm) >= target) : (run_c < need && need <= run_c + n);
+      if (n > 0u) last = j;
+      if (hit || (j == kKeysPerThread - 1 && by_mass)) {
+        if (!hit) {  // rounding left the target unreached: the last non-empty key of the run
+          run_c = cb;
+          run_m = mb;
+          for (int q = 0; q < last; ++q) {
+            const int32_t kq = hi - q;
+            const uint32_t nq = kq >= (int32_t)bottom ? cnt[kq - (int32_t)bottom] : 0u;
+            run_c += nq;
+            if (by_p && nq) run_m += (uint64_t)nq * fixed_mass(key_logit(key16_to_key((uint32_t)kq)), k2, R);
+          }
+          const int32_t kl = hi - max(last, 0);
+          sh.pick_digit = (uint32_t)kl;
+          sh.pick_cnt_above = run_c;
+          sh.pick_mass_above = run_m;
+          sh.pick_cnt = kl >= (int32_t)bottom ? cnt[kl - (int32_t)bottom] : 0u;
+          return;
+        }
+        sh.pick_digit = (uint32_t)key;
+        sh.pick_cnt_above = run_c;
+        sh.pick_mass_above = run_m;
+        sh.pick_cnt = n;
+        return;
+      }
+      run_c += n;
+      run_m += mm;
+    }
+  };
+  // top-k: the run holding rank top_k
+  uint64_t mass_k = mass_all;
+  if (by_k) {
+    if (cb < (uint32_t)top_k && (uint32_t)top_k <= cb + c) pick_in_run(false, (uint32_t)top_k, 0.0);
+    __syncthreads();
+    s = Selected{key16_to_key(sh.pick_digit), sh.pick_cnt_above, sh.pick_mass_above, sh.pick_cnt};
+    n_eq = (uint32_t)top_k - s.cnt_above;
+    mass_k = s.mass_above + (uint64_t)n_eq * fixed_mass(key_logit(s.key), k2, R);
+    __syncthreads();
+  }
+  if (!by_p) return true;
+  // top-p: the first run (in rank order) where the running mass reaches the target
+  const double target = (double)mass_k * ((double)milli / 1000.0);
+  if (t == 0) sh.cand = INT32_MAX;
+  __syncthreads();
+  if (c > 0u && (double)(mb + m) >= target) atomicMin(&sh.cand, t);
+  __syncthreads();
+  const int owner = sh.cand;
+  __syncthreads();
+  if (owner == INT32_MAX) return false;  // the nucleus reaches below the window
+  if (t == owner) pick_in_run(true, 0u, target);
+  __syncthreads();
+  const Selected sp{key16_to_key(sh.pick_digit), sh.pick_cnt_above, sh.pick_mass_above, sh.pick_cnt};
+  __syncthreads();
+  uint32_t n = copies_to_reach(sp.mass_above, fixed_mass(key_logit(sp.key), k2, R), sp.ties, target);
+  if (by_k && sp.key == s.key && n > n_eq) n = n_eq;
+  s = sp;
+  n_eq = n;
+  return true;
+}
+
+// The histogram of one radix digit level over the logits whose higher digits equal prefix: counts,
+// and (with_mass) fixed-point masses.
+template <class E, bool kVec>
+__device__ __forceinline__ void histogram(const char* rp, int32_t V, float k2, float R, int L, uint32_t prefix,
+                                          bool with_mass, uint32_t* cnt, uint64_t* mass) {
+  const int shift = Radix<E>::shift(L), nb = 1 << Radix<E>::width(L);
+  const int hi = shift + Radix<E>::width(L);
+  for (int b = threadIdx.x; b < nb; b += kCutThreads) {
+    cnt[b] = 0u;
+    mass[b] = 0ull;
+  }
+  __syncthreads();
+  for_each_logit<E, kVec>(rp, V, [&](float z, uint32_t, int32_t) {
+    const uint32_t key = order_key(z);
+    if (L > 0 && (key >> hi) != prefix) return;
+    const uint32_t d = (key >> shift) & (uint32_t)(nb - 1);
+    atomicAdd(&cnt[d], 1u);
+    if (with_mass) atomicAdd(reinterpret_cast<unsigned long long*>(&mass[d]), (unsigned long long)fixed_mass(z, k2, R));
+  });
+  __syncthreads();
+}
+
+// The exact radix select of top-k, then top-p (any row).  cnt0 / mass0 hold level 0 for the whole
+// selection, cntL / massL the deeper level last built (reused by top-p when its digits agree).
+template <class E, bool kVec>
+__device__ __forceinline__ void radix_select(const char* rp, int32_t V, float k2, float R, bool by_k, int32_t top_k,
+                                             bool by_p, int32_t milli, unsigned char* smem, CutShared& sh,
+                                             Selected& s, uint32_t& n_eq) {
+  uint32_t* cnt0 = reinterpret_cast<uint32_t*>(smem);
+  uint64_t* mass0 = reinterpret_cast<uint64_t*>(smem + 8 * 1024);
+  uint32_t* cntL = reinterpret_cast<uint32_t*>(smem + 24 * 1024);
+  uint64_t* massL = reinterpret_cast<uint64_t*>(smem + 32 * 1024);
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  histogram<E, kVec>(rp, V, k2, R, 0, 0u, by_p, cnt0, mass0);
+  int held_level = -1;
+  uint32_t held_prefix = 0u;
+  constexpr int kLast = Radix<E>::kLevels - 1;
+  auto run = [&](bool by_mass, uint32_t need, double target_mass) {
+    uint32_t prefix = 0u, cnt_above = 0u, ties = 0u;
+    uint64_t mass_above = 0ull;
+    for (int L = 0; L <= kLast; ++L) {
+      const uint32_t* c = cnt0;
+      const uint64_t* m = mass0;
+      if (L > 0) {
+        if (held_level != L || held_prefix != prefix) {
+          histogram<E, kVec>(rp, V, k2, R, L, prefix, by_p, cntL, massL);
+          held_level = L;
+          held_prefix = prefix;
+        }
+        c = cntL;
+        m = massL;
+      }
+      select_bin<kBinsPerThread>(
+          1 << Radix<E>::width(L), [&](int b) { return c[b]; }, [&](int b) { return m[b]; }, by_mass,
+          need - cnt_above, target_mass, mass_above, sh);
+      cnt_above += sh.pick_cnt_above;
+      mass_above += sh.pick_mass_above;
+      ties = sh.pick_cnt;
+      prefix = (prefix << Radix<E>::width(L)) | sh.pick_digit;
+      __syncthreads();
+    }
+    constexpr int sl = Radix<E>::shift(kLast);
+    uint32_t key = prefix;
+    if constexpr (sl > 0) key = (prefix << sl) | (((prefix >> (31 - sl)) & 1u) ? 0u : ((1u << sl) - 1u));
+    return Selected{key, cnt_above, mass_above, ties};
+  };
+  uint64_t mass_k = 0ull;
+  if (by_k) {
+    s = run(false, (uint32_t)top_k, 0.0);
+    n_eq = (uint32_t)top_k - s.cnt_above;
+    mass_k = s.mass_above + (uint64_t)n_eq * fixed_mass(key_logit(s.key), k2, R);
+  } else {
+    uint64_t part = 0ull;
+    for (int b = t; b < kRadixBins; b += kCutThreads) part += mass0[b];
+    part = wave_sum_u64(part);
+    if (lane == 0) sh.wave_mass[wave] = part;
+    __syncthreads();
+    for (int w = 0; w < kCutWaves; ++w) mass_k += sh.wave_mass[w];
+    __syncthreads();
+  }
+  if (by_p) {
+    const double target_mass = (double)mass_k * ((double)milli / 1000.0);
+    const Selected sp = run(true, 0u, target_mass);
+    uint32_t n = copies_to_reach(sp.mass_above, fixed_mass(key_logit(sp.key), k2, R), sp.ties, target_mass);
+    if (by_k && sp.key == s.key && n > n_eq) n = n_eq;
+    s = sp;
+    n_eq = n;
+  }
+}
+
+// Per chunk of a truncated row: the mass of its tokens above the cut value kappa (2^(z k - ref_c),
+// binary32, in the chunk record's frame) and the copies of kappa.  Wave w takes chunks w, w + 8, ...,
+// each loaded whole before it is summed; the partial last chunk goes through bounds-tested loads.
+template <class E, bool kVec>
+__device__ __forceinline__ void chunk_pass(const char* rp, int32_t V, int32_t C, const float2* rec, float kappa,
+                                           float k2, float* strict, uint32_t* copies, int lane, int wave) {
+  for (int32_t c = wave; c < C; c += kCutWaves) {
+    const int32_t c0 = c * E::kChunk, n = min(E::kChunk, V - c0);
+    const float ref_c = rec[c].x;
+    float acc = 0.0f;
+    uint32_t cp = 0u;
+    auto take = [&](float z) {
+      if (z > kappa) acc += fast_exp2(fmaf(z, k2, -ref_c));
+      cp += z == kappa ? 1u : 0u;
+    };
+    if (kVec && n == E::kChunk) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+      u32x4 buf[kVecPerLane];
+#pragma unroll
+      for (int k = 0; k < kVecPerLane; ++k) buf[k] = vp[lane + kWave * k];
+#pragma unroll
+      for (int k = 0; k < kVecPerLane; ++k) {
+        float z[E::kPerVec];
+        E::unpack(buf[k], z);
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) take(z[e]);
+      }
+    } else {
+      for (int32_t v = c0 + lane; v < c0 + n; v += kWave) take(E::at(rp, v));
+    }
+    acc = wave_sum(acc);
+    cp = wave_sum_u32(cp);
+    if (lane == 0) {
+      strict[c] = acc;
+      copies[c] = cp;
+    }
+  }
+}
+
 // One workgroup per row slot (target rows, then draft rows when the draft side is logits).  Rows of
-// requests that sample with a truncating profile get their cut; every other row gets the trivial
-// one.  Writes cuts[slot], kept_tokens[slot] and, for a truncated row, the masses of its chunk
-// records.
+// requests that sample with a profile that truncates get their cut; every other row gets the
+// trivial one.  Writes cuts[slot], kept_tokens[slot] and, for a truncated row, the masses of its
+// chunk records.
 template <class E, bool kVec>
 __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
   __shared__ __align__(16) unsigned char smem[48 * 1024];
   __shared__ CutShared sh;
-  uint32_t* cnt0 = reinterpret_cast<uint32_t*>(smem);  // level 0, kept for the whole selection
-  uint64_t* mass0 = reinterpret_cast<uint64_t*>(smem + 8 * 1024);
-  uint32_t* cntL = reinterpret_cast<uint32_t*>(smem + 24 * 1024);  // the deeper levels
-  uint64_t* massL = reinterpret_cast<uint64_t*>(smem + 32 * 1024);
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
   const int32_t slot = blockIdx.x;
@@ -1052,117 +1373,27 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
   __syncthreads();
   float R = -INFINITY;
   for (int w = 0; w < kCutWaves; ++w) R = fmaxf(R, sh.wave_ref[w]);
+  __syncthreads();
   if (R == -INFINITY) return untruncated();  // a row of -inf only describes no distribution
   const char* rp = target ? row_ptr<E>(P.target, row, P.V) : row_ptr<E>(P.draft, row, P.V);
 
-  histogram<E, kVec>(rp, P.V, k2, R, 0, 0u, cnt0, mass0);
-  int held_level = -1;  // the (level, prefix) whose histogram cntL / massL hold
-  uint32_t held_prefix = 0u;
-  constexpr int kLast = Radix<E>::kLevels - 1;
-  auto run = [&](bool by_mass, uint32_t need, double target_mass) {
-    uint32_t prefix = 0u, cnt_above = 0u, ties = 0u;
-    uint64_t mass_above = 0ull;
-    for (int L = 0; L <= kLast; ++L) {
-      const uint32_t* c = cnt0;
-      const uint64_t* m = mass0;
-      if (L > 0) {
-        if (held_level != L || held_prefix != prefix) {
-          histogram<E, kVec>(rp, P.V, k2, R, L, prefix, cntL, massL);
-          held_level = L;
-          held_prefix = prefix;
-        }
-        c = cntL;
-        m = massL;
-      }
-      select_bin(c, m, 1 << Radix<E>::width(L), by_mass, need - cnt_above, target_mass, mass_above, sh);
-      cnt_above += sh.pick_cnt_above;
-      mass_above += sh.pick_mass_above;
-      ties = sh.pick_cnt;
-      prefix = (prefix << Radix<E>::width(L)) | sh.pick_digit;
-    }
-    // below the last digit a bf16 key holds 16 copies of its sign bit's complement
-    constexpr int sl = Radix<E>::shift(kLast);
-    uint32_t key = prefix;
-    if constexpr (sl > 0) key = (prefix << sl) | (((prefix >> (31 - sl)) & 1u) ? 0u : ((1u << sl) - 1u));
-    return Selected{key, cnt_above, mass_above, ties};
-  };
-
-  // top-k: the top_k-th rank, and the mass of the top-k set
   Selected s{0u, 0u, 0ull, 0u};
   uint32_t n_eq = 0u;  // copies of the cut value that are kept
-  uint64_t mass_k = 0ull;
-  if (by_k) {
-    s = run(false, (uint32_t)top_k, 0.0);
-    n_eq = (uint32_t)top_k - s.cnt_above;
-    mass_k = s.mass_above + (uint64_t)n_eq * fixed_mass(key_logit(s.key), k2, R);
-  } else {
-    uint64_t part = 0ull;
-    for (int b = t; b < kRadixBins; b += kCutThreads) part += mass0[b];
-    part = wave_sum_u64(part);
-    if (lane == 0) sh.wave_mass[wave] = part;
-    __syncthreads();
-    for (int w = 0; w < kCutWaves; ++w) mass_k += sh.wave_mass[w];
-    __syncthreads();
-  }
-  // top-p: the shortest run of leading ranks whose mass reaches milli / 1000 of the top-k mass
-  if (by_p) {
-    const double target_mass = (double)mass_k * ((double)milli / 1000.0);
-    const Selected sp = run(true, 0u, target_mass);
-    const uint64_t e = fixed_mass(key_logit(sp.key), k2, R);
-    // the fewest copies (at least one) that reach the target; the selected bin's copies reach it,
-    // so the estimate starts within a rounding step of the answer and the corrections are short
-    uint64_t n = 1ull;
-    if (e > 0ull && (double)(sp.mass_above + e) < target_mass) {
-      const double est = ceil((target_mass - (double)sp.mass_above) / (double)e);
-      n = est >= (double)sp.ties ? (uint64_t)sp.ties : (uint64_t)est;
-      while (n > 1ull && (double)(sp.mass_above + (n - 1ull) * e) >= target_mass) --n;
-      while (n < sp.ties && (double)(sp.mass_above + n * e) < target_mass) ++n;
-    }
-    if (n > sp.ties) n = sp.ties;
-    if (by_k && sp.key == s.key && n > n_eq) n = n_eq;
-    s = sp;
-    n_eq = (uint32_t)n;
-  }
+  bool done = false;
+  if constexpr (E::kBytes == 2)
+    done = window_select<kVec>(rp, P.V, P.C, rec, k2, R, by_k, top_k, by_p, milli, reinterpret_cast<uint32_t*>(smem),
+                               sh, s, n_eq);
+  __syncthreads();
+  if (!done) radix_select<E, kVec>(rp, P.V, k2, R, by_k, top_k, by_p, milli, smem, sh, s, n_eq);
   const float kappa = key_logit(s.key);
   const int32_t kept = (int32_t)(s.cnt_above + n_eq);
 
   // chunk masses of the kept tokens strictly above the cut value, and the copies of the cut value
-  // in each chunk (the LDS of the histograms is free again)
+  // in each chunk (the histograms' LDS is free again)
   __syncthreads();
   float* strict = reinterpret_cast<float*>(smem);
   uint32_t* copies = reinterpret_cast<uint32_t*>(smem + 16 * 1024);
-  for (int32_t c = wave; c < P.C; c += kCutWaves) {
-    const int32_t c0 = c * E::kChunk, n = min(E::kChunk, P.V - c0);
-    const float ref_c = rec[c].x;
-    float acc = 0.0f;
-    uint32_t cp = 0u;
-    auto take = [&](float z) {
-      if (z > kappa) acc += fast_exp2(fmaf(z, k2, -ref_c));
-      cp += z == kappa ? 1u : 0u;
-    };
-    if constexpr (kVec) {
-      const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
-      const int32_t nvec = n / E::kPerVec;
-#pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) {
-        const int vi = lane + kWave * k;
-        if (vi < nvec) {
-          float z[E::kPerVec];
-          E::unpack(vp[vi], z);
-#pragma unroll
-          for (int e = 0; e < E::kPerVec; ++e) take(z[e]);
-        }
-      }
-    } else {
-      for (int32_t v = c0 + lane; v < c0 + n; v += kWave) take(E::at(rp, v));
-    }
-    acc = wave_sum(acc);
-    cp = wave_sum_u32(cp);
-    if (lane == 0) {
-      strict[c] = acc;
-      copies[c] = cp;
-    }
-  }
+  chunk_pass<E, kVec>(rp, P.V, P.C, rec, kappa, k2, strict, copies, lane, wave);
   __syncthreads();
   if (wave != 0) return;
   // wave 0: the kept copies per chunk in token order, the new chunk masses, and the chunk holding
@@ -1194,40 +1425,63 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
     }
     carry += __shfl(incl, kWave - 1, kWave);
   }
-  // the token id of the last kept copy, unless every copy is kept
+  // the token id of the last kept copy, unless every copy is kept: chunk cstar is loaded whole and
+  // searched in registers, its vectors in token order (vector k * 64 + lane)
   int32_t vcut = INT32_MAX;
   if (n_eq < s.ties && cstar >= 0) {
     const int32_t c0 = cstar * E::kChunk, end = min(c0 + E::kChunk, P.V);
     uint32_t need = rstar;
-    for (int32_t b = c0; b < end; b += kWave * E::kPerVec) {
-      const int32_t v0 = b + lane * E::kPerVec;  // each lane takes kPerVec consecutive tokens
-      uint32_t mask = 0u;
+    if constexpr (kVec) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+      const int32_t nvec = (end - c0) / E::kPerVec;
+      u32x4 buf[kVecPerLane];
 #pragma unroll
-      for (int e = 0; e < E::kPerVec; ++e)
-        if (v0 + e < end && E::at(rp, v0 + e) == kappa) mask |= 1u << e;
-      const uint32_t mine = (uint32_t)__popc(mask);
-      uint32_t incl = mine;
+      for (int k = 0; k < kVecPerLane; ++k) buf[k] = load_vec<E>(vp, lane + kWave * k, nvec);
 #pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t up = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += up;
-      }
-      const uint32_t total = __shfl(incl, kWave - 1, kWave);
-      if (need <= total) {
-        const uint64_t at = __ballot(incl - mine < need && need <= incl);
-        const int g = __ffsll((unsigned long long)at) - 1;
-        int32_t v = -1;
-        uint32_t left = need - (incl - mine);
+      for (int k = 0; k < kVecPerLane; ++k) {
+        float z[E::kPerVec];
+        E::unpack(buf[k], z);
+        uint32_t mask = 0u;
 #pragma unroll
         for (int e = 0; e < E::kPerVec; ++e)
-          if ((mask >> e) & 1u) {
-            if (left == 1u && v < 0) v = v0 + e;
-            --left;
-          }
-        vcut = __shfl(v, g, kWave);
-        break;
+          if (lane + kWave * k < nvec && z[e] == kappa) mask |= 1u << e;
+        const uint32_t mine = (uint32_t)__popc(mask);
+        uint32_t incl = mine;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t up = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += up;
+        }
+        const uint32_t total = __shfl(incl, kWave - 1, kWave);
+        if (need <= total) {
+          const uint64_t at = __ballot(incl - mine < need && need <= incl);
+          const int g = __ffsll((unsigned long long)at) - 1;
+          int32_t v = -1;
+          uint32_t left = need - (incl - mine);
+#pragma unroll
+          for (int e = 0; e < E::kPerVec; ++e)
+            if ((mask >> e) & 1u) {
+              if (left == 1u && v < 0) v = c0 + (lane + kWave * k) * E::kPerVec + e;
+              --left;
+            }
+          vcut = __shfl(v, g, kWave);
+          break;
+        }
+        need -= total;
       }
-      need -= total;
+    } else {
+      for (int32_t b = c0; b < end; b += kWave) {  // 64 consecutive tokens per step
+        const bool hit = b + lane < end && E::at(rp, b + lane) == kappa;
+        const uint64_t m = __ballot(hit);
+        const uint32_t total = (uint32_t)__popcll((unsigned long long)m);
+        if (need <= total) {
+          uint64_t mm = m;
+          for (uint32_t q = 1; q < need; ++q) mm &= mm - 1;  // drop the first need - 1 hits
+          vcut = b + __ffsll((unsigned long long)mm) - 1;
+          break;
+        }
+        need -= total;
+      }
     }
   }
   if (lane == 0) {

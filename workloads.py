@@ -48,6 +48,8 @@ class Batch:
     temp_each: np.ndarray | None = None  # (B,) float32: one temperature per request, else None
     seed_each: np.ndarray | None = None  # (B,) uint64: one seed per request (with temp_each)
     qrows: np.ndarray | None = None      # (n_draft_rows, V) float32 draft distributions, else None
+    top_k: np.ndarray | None = None      # (B,) int32 top-k of each request's profile, else None
+    top_p_milli: np.ndarray | None = None  # (B,) int32 top-p in thousandths, else None
 
     @property
     def B(self) -> int:
@@ -185,6 +187,18 @@ def with_qrows(b: Batch, temperature: float | None = None) -> Batch:
     return Batch(name=b.name + "_qrows", V=b.V, dtype=b.dtype, temperature=b.temperature, seed=b.seed,
                  target=b.target, draft=None, tokens=b.tokens, cu=b.cu, meta=dict(b.meta),
                  temp_each=b.temp_each, seed_each=b.seed_each, qrows=q)
+
+
+def with_truncation(b: Batch, top_k: int, top_p_milli: int) -> Batch:
+    """The same logits under a truncating profile (top-k, then top-p, after the temperature) on
+    every request.  The drafter proposes its argmax, the first rank of its row, which every
+    truncation keeps, so every proposal is valid without the generator computing a kept set."""
+    if b.draft is None:
+        raise ValueError("a truncated batch needs the draft logits")
+    return Batch(name=f"{b.name}_topk{top_k}_topp{top_p_milli}", V=b.V, dtype=b.dtype, temperature=b.temperature,
+                 seed=b.seed, target=b.target, draft=b.draft, tokens=_argmax_tokens(b.draft, b.dtype), cu=b.cu,
+                 meta=dict(b.meta, drafts="argmax"), temp_each=b.temp_each, seed_each=b.seed_each,
+                 top_k=np.full(b.B, top_k, dtype=np.int32), top_p_milli=np.full(b.B, top_p_milli, dtype=np.int32))
 
 
 def mixed_profiles(B: int, rng: np.random.Generator, temps=(0.0, 0.6, 1.0, 1.5)) -> tuple[np.ndarray, np.ndarray]:
