@@ -111,9 +111,9 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
     stop_offsets [B + 1], stop_tokens), a budget (int32 [B]) or draft_probs (float32
     [n_draft_rows, V], the draft distributions in place of draft logits) or the rest of the
     sampling profiles (int32 top_k [B], top_p_milli [B]) are given.  Returns (accepted_len,
-    out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag), "emitted_len"
-    with stop lists or a budget, and "kept_tokens" (int32 [n_draft_rows + B + n_draft_rows]) with
-    top-k / top-p.  ``events``: up to four torch.cuda.Event objects, recorded as sdv_diag.events
+    out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag, and with top-k /
+    top-p "kept_tokens", int32 [n_draft_rows + B + n_draft_rows]) and "emitted_len" with stop lists
+    or a budget.  ``events``: up to four torch.cuda.Event objects, recorded as sdv_diag.events
     describes.
     """
     _check(target, draft, draft_tokens, offsets, temperature, draft_probs)
@@ -151,6 +151,8 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
               "terminal_kind": (B, torch.int32)}
     dvals = {}
     dg = None
+    want_kept = "kept_tokens" in diag
+    diag = tuple(name for name in diag if name != "kept_tokens")
     if diag or events:
         dg = _native.SdvDiag()
         for name in diag:
@@ -179,8 +181,9 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
                 opt.emitted_len = dvals["emitted_len"].data_ptr()
             if truncating:
                 opt.top_k, opt.top_p_milli = _ptr(top_k), _ptr(top_p_milli)
-                dvals["kept_tokens"] = torch.full((2 * n_d + B,), -9, dtype=torch.int32, device=dev)
-                opt.kept_tokens = dvals["kept_tokens"].data_ptr()
+                if want_kept:
+                    dvals["kept_tokens"] = torch.full((2 * n_d + B,), -9, dtype=torch.int32, device=dev)
+                    opt.kept_tokens = dvals["kept_tokens"].data_ptr()
             scalar_t = 0.0 if profile is not None else float(temperature)
             scalar_s = 0 if profile is not None else int(seed) & 0xFFFFFFFFFFFFFFFF
             rc = _native.lib().sdv_verify_opts(

@@ -54,7 +54,7 @@ def drafter_tokens(b, top_k, milli, rng, n_bad=0):
     return tokens.astype(np.int32)
 
 
-def run_both(b, top_k, milli, diag=("terminal_kind", "target_lse")):
+def run_both(b, top_k, milli, diag=("terminal_kind", "target_lse", "kept_tokens")):
     t, d = to_device(b.target, b.dtype), to_device(b.draft, b.dtype)
     x, cu = torch.from_numpy(b.tokens).to(DEV), torch.from_numpy(b.cu).to(DEV)
     kw = {"top_k": torch.from_numpy(np.asarray(top_k, dtype=np.int32)).to(DEV),
@@ -207,7 +207,7 @@ def test_top_k_one_equals_the_greedy_rule_on_the_gpu():
     g_acc, g_out, _ = sdv.verify_ex(*ins, 0.0, 0)
     ones = torch.ones(b.B, dtype=torch.int32, device=DEV)
     for T in (0.5, 1.0, 2.0):
-        acc, out, extra = sdv.verify_ex(*ins, T, 11, top_k=ones)
+        acc, out, extra = sdv.verify_ex(*ins, T, 11, top_k=ones, diag=("kept_tokens",))
         torch.cuda.synchronize()
         assert torch.equal(acc, g_acc) and torch.equal(out, g_out)
         assert (extra["kept_tokens"] == 1).all()
