@@ -244,3 +244,39 @@ def test_full_size_b256_top_k_50_top_p_0_9():
     milli = np.full(b.B, 900, dtype=np.int32)
     b.tokens = drafter_tokens(b, top_k, milli, rng)
     check(b, top_k, milli)
+
+
+def test_cuts_below_the_window_take_the_radix_select():
+    """bf16 rows whose cut lies below the 4096 keys under the maximum: a top-k larger than the
+    window holds, and nuclei that reach deep into the tail at a high temperature.  These rows go
+    through the exact radix select (16-byte rows, the vector path)."""
+    rng = np.random.default_rng(71)
+    B, V = 24, 32000
+    depths = rng.integers(1, 5, size=B)
+    cu = W.offsets_from_depths(depths)
+    n_d = int(cu[-1])
+    tgt = (rng.standard_normal((n_d + B, V)) * 4).astype(np.float32)
+    drf = (tgt[np.concatenate([np.arange(cu[i], cu[i + 1]) + i for i in range(B)])]
+           + rng.standard_normal((n_d, V))).astype(np.float32)
+    b = W.Batch(name="below_window", V=V, dtype="bf16", temperature=6.0, seed=21, target=W.bf16_bits(tgt),
+                draft=W.bf16_bits(drf), tokens=np.zeros(n_d, dtype=np.int32), cu=cu)
+    top_k = rng.choice([20000, 31000, 0], size=B).astype(np.int32)
+    milli = rng.choice([1000, 999, 995], size=B).astype(np.int32)
+    milli[top_k == 0] = 999  # top-p alone, over a flat distribution
+    b.tokens = drafter_tokens(b, top_k, milli, rng)
+    acc, out, got, ref = check(b, top_k, milli)
+    # the cut of every truncated row lies below the window: fewer than 4096 distinct keys cannot hold it
+    assert (ref["kept_tokens"][: n_d + B] > 16000).all()
+
+
+@pytest.mark.parametrize("V", [32000, 128256])
+def test_binary32_rows_on_the_vector_path(V):
+    """binary32 rows of 16-byte length: the radix select over three digit levels, vector loads."""
+    rng = np.random.default_rng(V + 73)
+    base = W.make_random(f"trunc_fp32_{V}", rng.integers(0, 7, size=32), V, "fp32", 1.0, 3.0,
+                         rng.uniform(0.5, 3.0, size=32), data_seed=V + 74, verify_seed=V + 75, keep_draft=True)
+    t, s = W.mixed_profiles(base.B, rng)
+    b = W.with_profiles(base, t, s, token_seed=V + 76)
+    top_k, milli = _profiles(b.B, V, rng)
+    b.tokens = drafter_tokens(b, top_k, milli, rng, n_bad=2)
+    check(b, top_k, milli)
