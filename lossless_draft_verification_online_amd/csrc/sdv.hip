@@ -847,6 +847,8 @@ constexpr int kRadixBins = 1 << 11;             // the widest digit
 constexpr int kBinsPerThread = kRadixBins / kCutThreads;
 constexpr int kRegionKeys = 4096;               // bf16 keys counted one by one below the maximum's
 constexpr int kKeysPerThread = kRegionKeys / kCutThreads;
+constexpr int kTopKeys = 256;   // the window's top keys, also counted per chunk ...
+constexpr int kTopChunks = 32;  // ... for rows of up to 32 chunks (32 KiB of LDS)
 constexpr float kFixScale = 0x1.0p37f;          // masses <= ~1 as integers: V 2^37 < 2^63
 
 // Digits of the order key, most significant first: bf16 keys carry 16 bits (11 + 5), binary32
@@ -1085,26 +1087,36 @@ __device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
 
 // bf16 rows: the counts of the 4096 keys top - 4095 .. top, top just above the row maximum's key
 // (from R = fl(max z * k), whose quotient by k lies within a rounding step of the maximum).  Logits
-// below the window are counted apart.  With top-p over the whole row (no top-k) the nucleus mass
+// below the window are counted apart.  With top_cnt (rows of at most kTopChunks chunks) the top
+// kTopKeys keys are also counted per chunk: top_cnt[c * kTopKeys + (top - key)].  With top-p over the whole row (no top-k) the nucleus mass
 // is a share of the row's mass, folded from the chunk records (binary32 chunk sums, fp64 across
 // chunks; their relative error stays below 1e-6).  Returns true with the cut in s / n_eq when the
 // selection ends inside the window; false sends the row to the radix select.
 template <bool kVec>
 __device__ __forceinline__ bool window_select(const char* rp, int32_t V, int32_t C, const float2* rec, float k2,
                                               float R, bool by_k, int32_t top_k, bool by_p, int32_t milli,
-                                              uint32_t* cnt, CutShared& sh, Selected& s, uint32_t& n_eq) {
+                                              uint32_t* cnt, uint32_t* top_cnt, uint32_t& top_out, CutShared& sh,
+                                              Selected& s, uint32_t& n_eq) {
   const int t = threadIdx.x;
   const float m_hat = R / k2;
   const uint32_t k_hat = key16_of_bits(__float_as_uint(m_hat) >> 16);
   const uint32_t top = k_hat + 4u > 65535u ? 65535u : k_hat + 4u;
   const uint32_t bottom = top >= (uint32_t)(kRegionKeys - 1) ? top - (uint32_t)(kRegionKeys - 1) : 0u;
+  top_out = top;
   for (int j = t; j < kRegionKeys; j += kCutThreads) cnt[j] = 0u;
+  if (top_cnt)
+    for (int j = t; j < C * kTopKeys; j += kCutThreads) top_cnt[j] = 0u;
   __syncthreads();
   uint32_t above = 0u;
-  for_each_logit<Bf16, kVec>(rp, V, [&](float, uint32_t h, int32_t) {
+  for_each_logit<Bf16, kVec>(rp, V, [&](float, uint32_t h, int32_t v) {
     const uint32_t key = key16_of_bits(h);
-    if (key > top) ++above;
-    else if (key >= bottom) atomicAdd(&cnt[key - bottom], 1u);
+    if (key > top) {
+      ++above;
+    } else if (key >= bottom) {
+      atomicAdd(&cnt[key - bottom], 1u);
+      if (top_cnt && top - key < (uint32_t)kTopKeys)
+        atomicAdd(&top_cnt[(v / Bf16::kChunk) * kTopKeys + (top - key)], 1u);
+    }
   });
   // the row's mass in fixed point, from the chunk records
   double part = 0.0;
@@ -1380,20 +1392,44 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
   Selected s{0u, 0u, 0ull, 0u};
   uint32_t n_eq = 0u;  // copies of the cut value that are kept
   bool done = false;
+  uint32_t* top_cnt = (E::kBytes == 2 && P.C <= kTopChunks) ? reinterpret_cast<uint32_t*>(smem + 16 * 1024) : nullptr;
+  uint32_t top = 0u;
   if constexpr (E::kBytes == 2)
     done = window_select<kVec>(rp, P.V, P.C, rec, k2, R, by_k, top_k, by_p, milli, reinterpret_cast<uint32_t*>(smem),
-                               sh, s, n_eq);
+                               top_cnt, top, sh, s, n_eq);
   __syncthreads();
   if (!done) radix_select<E, kVec>(rp, P.V, k2, R, by_k, top_k, by_p, milli, smem, sh, s, n_eq);
   const float kappa = key_logit(s.key);
   const int32_t kept = (int32_t)(s.cnt_above + n_eq);
 
   // chunk masses of the kept tokens strictly above the cut value, and the copies of the cut value
-  // in each chunk (the histograms' LDS is free again)
+  // in each chunk: from the window's per-chunk counts when every kept key is among them (no second
+  // read of the row), else by a pass over the row (the histograms' LDS is free again)
   __syncthreads();
+  const bool from_counts = done && top_cnt && top - (s.key >> 16) < (uint32_t)kTopKeys;
   float* strict = reinterpret_cast<float*>(smem);
-  uint32_t* copies = reinterpret_cast<uint32_t*>(smem + 16 * 1024);
-  chunk_pass<E, kVec>(rp, P.V, P.C, rec, kappa, k2, strict, copies, lane, wave);
+  uint32_t* copies = reinterpret_cast<uint32_t*>(smem + (from_counts ? 8 * 1024 : 16 * 1024));
+  if (from_counts) {
+    const uint32_t kkey = s.key >> 16;
+    for (int32_t c = wave; c < P.C; c += kCutWaves) {
+      const float ref_c = rec[c].x;
+      float acc = 0.0f;
+      uint32_t cp = 0u;
+      for (int j = lane; j < kTopKeys && j <= (int)top; j += kWave) {
+        const uint32_t key = top - (uint32_t)j, n = top_cnt[c * kTopKeys + j];
+        if (n && key > kkey) acc += (float)n * fast_exp2(fmaf(key_logit(key16_to_key(key)), k2, -ref_c));
+        if (key == kkey) cp = n;
+      }
+      acc = wave_sum(acc);
+      cp = wave_sum_u32(cp);
+      if (lane == 0) {
+        strict[c] = acc;
+        copies[c] = cp;
+      }
+    }
+  } else {
+    chunk_pass<E, kVec>(rp, P.V, P.C, rec, kappa, k2, strict, copies, lane, wave);
+  }
   __syncthreads();
   if (wave != 0) return;
   // wave 0: the kept copies per chunk in token order, the new chunk masses, and the chunk holding
