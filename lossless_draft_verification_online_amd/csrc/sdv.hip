@@ -47,6 +47,24 @@ struct DiagPtrs {
 
 constexpr int32_t kMaxChunks = 4096;  // chunks per row: the verdict and cut kernels keep one value per chunk in LDS
 
+// Truncating bf16 calls: the row pass also counts, per chunk, the logits of each of the kHistKeys
+// 16-bit order keys at and below the chunk maximum's (one binade of positive logits), so that a cut
+// among the largest logits needs no second read of the row.  The chunk's top key carries kNoCounts
+// when its window would reach zero or -inf (then no counts are written).
+constexpr int kHistKeys = 128;
+constexpr uint32_t kNoCounts = 0x10000u;
+
+// Order keys of bf16 logits: a larger logit has a larger key and -0 shares the key of +0.
+// The 16-bit key of a bf16 logit (its raw bits h), and the 32-bit key of a 16-bit one: below the
+// 16 bits a bf16 key holds 16 copies of its sign bit's complement.
+__device__ __forceinline__ uint32_t key16_of_bits(uint32_t h) {
+  h = h == 0x8000u ? 0u : h;
+  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t key16_to_key(uint32_t key) {
+  return (key << 16) | ((key & 0x8000u) ? 0u : 0xffffu);
+}
+
 // The tokens a truncated row keeps (top-k / top-p) are its leading ranks in the order "larger logit
 // first, smaller id first among equal logits", so the last kept rank describes them: token v is
 // kept iff z_v > kappa, or z_v == kappa and v <= vcut.  A row that is not truncated has
@@ -99,6 +117,8 @@ struct Params {
   const int32_t* top_p_milli; // [B] top-p in thousandths, or null (1000: none)
   int32_t* kept_tokens;       // [row slots] out: tokens each truncated row keeps, or null
   Cut* cuts;                  // [row slots] the cut of every row (workspace), read when truncation is on
+  uint32_t* hist;             // [row slots][C][kHistKeys / 2] per-chunk key counts, two 16-bit counts a word
+  uint32_t* hist_top;         // [row slots][C] the chunk maximum's key, | kNoCounts without counts
   DiagPtrs dg;
 };
 
@@ -167,6 +187,46 @@ __device__ __forceinline__ void load_chunk(const char* rp, int32_t c0, int32_t n
   for (int k = 0; k < kVecPerLane; ++k) buf[k] = load_vec_nt<E>(vp, lane + kWave * k, nvec);
 }
 
+// The maximum of a loaded chunk (every lane holds it).
+template <class E>
+__device__ __forceinline__ float chunk_max(u32x4 (&buf)[kVecPerLane]) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) {
+    float f[E::kPerVec];
+    E::unpack(buf[k], f);
+#pragma unroll
+    for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
+  }
+  return wave_max(m);
+}
+
+// sum 2^(z k - ref) over a loaded chunk.  kCount (bf16 rows with a positive maximum) also counts
+// into the wave's counters h every logit z >= t, at hm - bits(z), hm the maximum's raw bits: bf16
+// logits are exact in binary32, so z >= t holds for exactly the kHistKeys keys at and below the
+// maximum's when t is the logit of the lowest of them (t = NaN counts nothing).
+template <class E, bool kCount>
+__device__ __forceinline__ float exp_sum(u32x4 (&buf)[kVecPerLane], float k2, float ref, float t, uint32_t hm,
+                                         uint32_t* h) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) {
+    // re-unpack from the raw words rather than keep every unpacked element live across the max
+    asm volatile("" : "+v"(buf[k]));
+    float f[E::kPerVec];
+    E::unpack(buf[k], f);
+    if constexpr (kCount) {
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e)
+        if (f[e] >= t) atomicAdd(&h[hm - (__float_as_uint(f[e]) >> 16)], 1u);
+    }
+#pragma unroll
+    for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
+    acc[k & 3] += tree_sum(f);
+  }
+  return wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+}
+
 // The record of a loaded chunk: (ref, sum 2^(z k - ref)) at T > 0, (max, first index of max) at T = 0.
 template <class E, bool kGreedy>
 __device__ __forceinline__ float2 record_of(u32x4 (&buf)[kVecPerLane], int32_t c0, float k2, int lane) {
@@ -189,29 +249,10 @@ __device__ __forceinline__ float2 record_of(u32x4 (&buf)[kVecPerLane], int32_t c
     wave_argmax(best, idx);
     return make_float2(best, __int_as_float(idx));
   } else {
-    float m = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-      float f[E::kPerVec];
-      E::unpack(buf[k], f);
-#pragma unroll
-      for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
-    }
-    m = wave_max(m);
+    const float m = chunk_max<E>(buf);
     if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
     const float ref = m * k2;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int k = 0; k < kVecPerLane; ++k) {
-      // re-unpack from the raw words rather than keep every unpacked element live across the max
-      asm volatile("" : "+v"(buf[k]));
-      float f[E::kPerVec];
-      E::unpack(buf[k], f);
-#pragma unroll
-      for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
-      acc[k & 3] += tree_sum(f);
-    }
-    return make_float2(ref, wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3])));
+    return make_float2(ref, exp_sum<E, false>(buf, k2, ref, 0.0f, 0u, nullptr));
   }
 }
 
@@ -247,6 +288,30 @@ __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32
       return make_float2(ref, wave_sum(s));
     }
   }
+}
+
+// The record of a loaded bf16 chunk at T > 0, and the counts of the kHistKeys keys at and below its
+// maximum's: out[j / 2] holds the counts of keys kmax - j (low half) and kmax - j - 1 (high half),
+// top = kmax.  Only a positive maximum whose window stays above +0 is counted; other chunks (a
+// maximum <= 0 or within kHistKeys steps of +0) carry top | kNoCounts.  h: the wave's kHistKeys
+// counters in shared memory.
+__device__ __forceinline__ float2 record_counting(u32x4 (&buf)[kVecPerLane], float k2, int lane, uint32_t* h,
+                                                  uint32_t* out, uint32_t* top) {
+  const float m = chunk_max<Bf16>(buf);
+  const uint32_t hm = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(m)) >> 16;
+  const uint32_t kmax = key16_of_bits(hm);
+  const bool counts = hm >= (uint32_t)kHistKeys && hm < 0x8000u;
+  if (lane == 0) *top = counts ? kmax : (kmax | kNoCounts);
+  if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+  const float ref = m * k2;
+  h[2 * lane] = 0u;
+  h[2 * lane + 1] = 0u;
+  __builtin_amdgcn_wave_barrier();  // a wave's shared-memory operations complete in order
+  const float t = counts ? __uint_as_float((hm - (uint32_t)(kHistKeys - 1)) << 16) : __builtin_nanf("");
+  const float s = exp_sum<Bf16, true>(buf, k2, ref, t, hm, h);
+  __builtin_amdgcn_wave_barrier();
+  out[lane] = h[2 * lane] | (h[2 * lane + 1] << 16);  // a chunk holds at most 8192 logits
+  return make_float2(ref, s);
 }
 
 // Residual weight max(p - q, 0) of token v, both sides scaled by the same factor 2^(l2_t - ref_t).
@@ -415,8 +480,11 @@ __device__ __forceinline__ float temperature_of(const float* temp_each, int32_t 
   return ((const __attribute__((address_space(4))) float*)temp_each)[i];
 }
 
-template <class E, int kMode, bool kVec>
+template <class E, int kMode, bool kVec, bool kHist>
 __global__ __launch_bounds__(256) void row_records(Params P) {
+  static_assert(!kHist || (E::kBytes == 2 && kVec && kMode != kModeGreedy), "counts: bf16 sampling, 16-byte rows");
+  static_assert(kHistKeys == 2 * kWave, "each lane writes one word of two counts");
+  __shared__ uint32_t hcnt[kHist ? 4 : 1][kHist ? kHistKeys : 1];
   const int lane = threadIdx.x & (kWave - 1);
   // the unit is wave-uniform; saying so lets the request lookup use scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -429,7 +497,11 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
   const int32_t c0 = c * E::kChunk;
   const int32_t n = min(E::kChunk, P.V - c0);
   float2 rec;
-  if constexpr (kMode != kModeProfiled) {
+  if constexpr (kHist && kMode != kModeProfiled) {
+    u32x4 buf[kVecPerLane];
+    load_chunk<E>(rp, c0, n, lane, buf);
+    rec = record_counting(buf, P.k2, lane, hcnt[wave], P.hist + u * (kHistKeys / 2), P.hist_top + u);
+  } else if constexpr (kMode != kModeProfiled) {
     rec = chunk_record<E, kMode == kModeGreedy, kVec>(rp, c0, n, P.k2, lane);
   } else {
     // a target row is always read, so its loads go out before the request lookup; a draft row is
@@ -443,7 +515,11 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
         if (!(k2 > 0.0f)) return;  // draft row of a greedy or rejected request: never read
         load_chunk<E>(rp, c0, n, lane, buf);
       }
-      rec = k2 > 0.0f ? record_of<E, false>(buf, c0, k2, lane) : record_of<E, true>(buf, c0, 0.0f, lane);
+      if constexpr (kHist)
+        rec = k2 > 0.0f ? record_counting(buf, k2, lane, hcnt[wave], P.hist + u * (kHistKeys / 2), P.hist_top + u)
+                        : record_of<E, true>(buf, c0, 0.0f, lane);
+      else
+        rec = k2 > 0.0f ? record_of<E, false>(buf, c0, k2, lane) : record_of<E, true>(buf, c0, 0.0f, lane);
     } else {
       const float k2 = k2_of(temperature_of(P.temp_each, request_of_row(P.cu, P.B, row, target)));
       if (!target && !(k2 > 0.0f)) return;
@@ -877,15 +953,6 @@ __device__ __forceinline__ uint32_t order_key(float z) {
 __device__ __forceinline__ float key_logit(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
-// The 16-bit key of a bf16 logit (its raw bits h), and the 32-bit key of a 16-bit one: below the
-// 16 bits a bf16 key holds 16 copies of its sign bit's complement.
-__device__ __forceinline__ uint32_t key16_of_bits(uint32_t h) {
-  h = h == 0x8000u ? 0u : h;
-  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
-}
-__device__ __forceinline__ uint32_t key16_to_key(uint32_t key) {
-  return (key << 16) | ((key & 0x8000u) ? 0u : 0xffffu);
-}
 
 __device__ __forceinline__ uint64_t fixed_mass(float z, float k2, float R) {
   return (uint64_t)(fast_exp2(fmaf(z, k2, -R)) * kFixScale);
@@ -908,6 +975,7 @@ struct CutShared {
   double wave_real[kCutWaves];
   float wave_ref[kCutWaves];
   int32_t cand, last;
+  uint32_t top;
   uint32_t pick_digit, pick_cnt_above, pick_cnt;
   uint64_t pick_mass_above;
 };
@@ -1085,24 +1153,13 @@ __device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
   }
 }
 
-// bf16 rows: the counts of the 4096 keys top - 4095 .. top, top just above the row maximum's key
-// (from R = fl(max z * k), whose quotient by k lies within a rounding step of the maximum).  Logits
-// below the window are counted apart.  With top_cnt (rows of at most kTopChunks chunks) the top
-// kTopKeys keys are also counted per chunk: top_cnt[c * kTopKeys + (top - key)].  With top-p over the whole row (no top-k) the nucleus mass
-// is a share of the row's mass, folded from the chunk records (binary32 chunk sums, fp64 across
-// chunks; their relative error stays below 1e-6).  Returns true with the cut in s / n_eq when the
-// selection ends inside the window; false sends the row to the radix select.
+// bf16 rows: the counts of the keys bottom .. top (cnt[key - bottom], at most kRegionKeys keys) by a
+// pass over the row.  With top_cnt (rows of at most kTopChunks chunks) the top kTopKeys keys are also
+// counted per chunk: top_cnt[c * kTopKeys + (top - key)].  Returns false when a logit lies above top.
 template <bool kVec>
-__device__ __forceinline__ bool window_select(const char* rp, int32_t V, int32_t C, const float2* rec, float k2,
-                                              float R, bool by_k, int32_t top_k, bool by_p, int32_t milli,
-                                              uint32_t* cnt, uint32_t* top_cnt, uint32_t& top_out, CutShared& sh,
-                                              Selected& s, uint32_t& n_eq) {
+__device__ __forceinline__ bool window_count(const char* rp, int32_t V, int32_t C, uint32_t top, uint32_t bottom,
+                                             uint32_t* cnt, uint32_t* top_cnt, CutShared& sh) {
   const int t = threadIdx.x;
-  const float m_hat = R / k2;
-  const uint32_t k_hat = key16_of_bits(__float_as_uint(m_hat) >> 16);
-  const uint32_t top = k_hat + 4u > 65535u ? 65535u : k_hat + 4u;
-  const uint32_t bottom = top >= (uint32_t)(kRegionKeys - 1) ? top - (uint32_t)(kRegionKeys - 1) : 0u;
-  top_out = top;
   for (int j = t; j < kRegionKeys; j += kCutThreads) cnt[j] = 0u;
   if (top_cnt)
     for (int j = t; j < C * kTopKeys; j += kCutThreads) top_cnt[j] = 0u;
@@ -1118,6 +1175,21 @@ __device__ __forceinline__ bool window_select(const char* rp, int32_t V, int32_t
         atomicAdd(&top_cnt[(v / Bf16::kChunk) * kTopKeys + (top - key)], 1u);
     }
   });
+  uint32_t cb;
+  uint64_t mb, ct, mt;
+  block_scan(above, 0ull, cb, mb, ct, mt, sh);
+  return ct == 0ull;
+}
+
+// The cut of top-k, then top-p, from the counts of the keys bottom .. top (bf16 rows; every copy of
+// a key has the same mass, so counts give masses).  With top-p over the whole row (no top-k) the
+// nucleus mass is a share of the row's mass, folded from the chunk records (binary32 chunk sums,
+// fp64 across chunks; their relative error stays below 1e-6).  Returns true with the cut in s /
+// n_eq when the selection ends on a counted key; false when it lies below them.
+__device__ __forceinline__ bool window_pick(const uint32_t* cnt, uint32_t top, uint32_t bottom, int32_t C,
+                                            const float2* rec, float k2, float R, bool by_k, int32_t top_k,
+                                            bool by_p, int32_t milli, CutShared& sh, Selected& s, uint32_t& n_eq) {
+  const int t = threadIdx.x;
   // the row's mass in fixed point, from the chunk records
   double part = 0.0;
   for (int32_t c = t; c < C; c += kCutThreads)
@@ -1128,12 +1200,6 @@ __device__ __forceinline__ bool window_select(const char* rp, int32_t V, int32_t
   double row_mass = 0.0;
   for (int w = 0; w < kCutWaves; ++w) row_mass += sh.wave_real[w];
   const uint64_t mass_all = (uint64_t)(row_mass * (double)kFixScale);
-  {
-    uint32_t cb;
-    uint64_t mb, ct, mt;
-    block_scan(above, 0ull, cb, mb, ct, mt, sh);
-    if (ct != 0ull) return false;  // a logit above the window: the maximum was misjudged
-  }
   // runs of kKeysPerThread keys, thread order = rank order
   const int32_t hi = (int32_t)top - kKeysPerThread * t;
   uint32_t c = 0u;
@@ -1347,99 +1413,49 @@ __device__ __forceinline__ void chunk_pass(const char* rp, int32_t V, int32_t C,
   }
 }
 
-// One workgroup per row slot (target rows, then draft rows when the draft side is logits).  Rows of
-// requests that sample with a profile that truncates get their cut; every other row gets the
-// trivial one.  Writes cuts[slot], kept_tokens[slot] and, for a truncated row, the masses of its
-// chunk records.
-template <class E, bool kVec>
-__global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
-  __shared__ __align__(16) unsigned char smem[48 * 1024];
-  __shared__ CutShared sh;
-  const int t = threadIdx.x, lane = t & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
-  const int32_t slot = blockIdx.x;
-  const bool target = slot < P.n_t;
-  const int32_t row = target ? slot : slot - P.n_t;
-  const int32_t i = request_of_row(P.cu, P.B, row, target);
-  const float k2 = P.temp_each ? k2_of(temperature_of(P.temp_each, i)) : P.k2;
-  const int32_t top_k = P.top_k ? P.top_k[i] : 0;
-  const int32_t milli = P.top_p_milli ? P.top_p_milli[i] : 1000;
-  const bool valid = top_k >= 0 && milli >= 0 && milli <= 1000;
-  const bool by_k = valid && top_k > 0 && top_k < P.V;
-  const bool by_p = valid && milli < 1000;
-  auto untruncated = [&]() {
-    if (t == 0) {
-      P.cuts[slot] = Cut{-INFINITY, INT32_MAX};
-      if (P.kept_tokens) P.kept_tokens[slot] = P.V;
-    }
-  };
-  // greedy or rejected requests, and profiles that truncate nothing (the draft rows of greedy
-  // requests have no records: they are never read)
-  if (!(k2 > 0.0f) || !(by_k || by_p)) return untruncated();
-  float2* rec = P.part + (int64_t)slot * P.C;
-  // the row's exponent reference R: the largest chunk reference (fl(max z * k))
-  float rl = -INFINITY;
-  for (int32_t c = t; c < P.C; c += kCutThreads) rl = fmaxf(rl, rec[c].x);
-  rl = wave_max(rl);
-  if (lane == 0) sh.wave_ref[wave] = rl;
-  __syncthreads();
-  float R = -INFINITY;
-  for (int w = 0; w < kCutWaves; ++w) R = fmaxf(R, sh.wave_ref[w]);
-  __syncthreads();
-  if (R == -INFINITY) return untruncated();  // a row of -inf only describes no distribution
-  const char* rp = target ? row_ptr<E>(P.target, row, P.V) : row_ptr<E>(P.draft, row, P.V);
+// The truncation profile of a row slot's request (SDCP "Session Contract").
+struct RowProfile {
+  bool target;
+  int32_t row, i;
+  float k2;
+  int32_t top_k, milli;
+  bool by_k, by_p;
+};
+__device__ __forceinline__ RowProfile row_profile(const Params& P, int32_t slot) {
+  RowProfile f;
+  f.target = slot < P.n_t;
+  f.row = f.target ? slot : slot - P.n_t;
+  f.i = request_of_row(P.cu, P.B, f.row, f.target);
+  f.k2 = P.temp_each ? k2_of(temperature_of(P.temp_each, f.i)) : P.k2;
+  f.top_k = P.top_k ? P.top_k[f.i] : 0;
+  f.milli = P.top_p_milli ? P.top_p_milli[f.i] : 1000;
+  const bool valid = f.top_k >= 0 && f.milli >= 0 && f.milli <= 1000;
+  f.by_k = valid && f.top_k > 0 && f.top_k < P.V;
+  f.by_p = valid && f.milli < 1000;
+  return f;
+}
 
-  Selected s{0u, 0u, 0ull, 0u};
-  uint32_t n_eq = 0u;  // copies of the cut value that are kept
-  bool done = false;
-  uint32_t* top_cnt = (E::kBytes == 2 && P.C <= kTopChunks) ? reinterpret_cast<uint32_t*>(smem + 16 * 1024) : nullptr;
-  uint32_t top = 0u;
-  if constexpr (E::kBytes == 2)
-    done = window_select<kVec>(rp, P.V, P.C, rec, k2, R, by_k, top_k, by_p, milli, reinterpret_cast<uint32_t*>(smem),
-                               top_cnt, top, sh, s, n_eq);
-  __syncthreads();
-  if (!done) radix_select<E, kVec>(rp, P.V, k2, R, by_k, top_k, by_p, milli, smem, sh, s, n_eq);
-  const float kappa = key_logit(s.key);
-  const int32_t kept = (int32_t)(s.cnt_above + n_eq);
+// A row the count kernel leaves to the full cut kernel carries vcut = kCutPending.
+constexpr int32_t kCutPending = INT32_MIN;
 
-  // chunk masses of the kept tokens strictly above the cut value, and the copies of the cut value
-  // in each chunk: from the window's per-chunk counts when every kept key is among them (no second
-  // read of the row), else by a pass over the row (the histograms' LDS is free again)
-  __syncthreads();
-  const bool from_counts = done && top_cnt && top - (s.key >> 16) < (uint32_t)kTopKeys;
-  float* strict = reinterpret_cast<float*>(smem);
-  uint32_t* copies = reinterpret_cast<uint32_t*>(smem + (from_counts ? 8 * 1024 : 16 * 1024));
-  if (from_counts) {
-    const uint32_t kkey = s.key >> 16;
-    for (int32_t c = wave; c < P.C; c += kCutWaves) {
-      const float ref_c = rec[c].x;
-      float acc = 0.0f;
-      uint32_t cp = 0u;
-      for (int j = lane; j < kTopKeys && j <= (int)top; j += kWave) {
-        const uint32_t key = top - (uint32_t)j, n = top_cnt[c * kTopKeys + j];
-        if (n && key > kkey) acc += (float)n * fast_exp2(fmaf(key_logit(key16_to_key(key)), k2, -ref_c));
-        if (key == kkey) cp = n;
-      }
-      acc = wave_sum(acc);
-      cp = wave_sum_u32(cp);
-      if (lane == 0) {
-        strict[c] = acc;
-        copies[c] = cp;
-      }
-    }
-  } else {
-    chunk_pass<E, kVec>(rp, P.V, P.C, rec, kappa, k2, strict, copies, lane, wave);
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  // wave 0: the kept copies per chunk in token order, the new chunk masses, and the chunk holding
-  // the last kept copy
+// The last steps of a row's cut, by one wave: the kept copies of the cut value per chunk in token
+// order, each chunk record's mass rewritten to the mass of the chunk's kept tokens, and the token id
+// of the last kept copy (unless every copy is kept: chunk cstar is loaded whole and searched in
+// registers, its vectors in token order, vector k * 64 + lane).  chunk(c) gives the chunk's mass
+// of kept tokens strictly above kappa (in its record's frame) and its copies of kappa.  Writes
+// cuts[slot] and kept_tokens[slot].
+template <class E, bool kVec, class ChunkFn>
+__device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const char* rp, float2* rec, float kappa,
+                                           float k2, uint32_t ties, uint32_t n_eq, int32_t kept, ChunkFn chunk,
+                                           int lane) {
   uint32_t carry = 0u;
   int32_t cstar = -1;
   uint32_t rstar = 0u;
   for (int32_t cb = 0; cb < P.C; cb += kWave) {
     const int32_t c = cb + lane;
-    const uint32_t here = c < P.C ? copies[c] : 0u;
+    float strict_c = 0.0f;
+    uint32_t here = 0u;
+    if (c < P.C) chunk(c, strict_c, here);
     uint32_t incl = here;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -1449,7 +1465,7 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
     const uint32_t before = carry + incl - here;
     const uint32_t keep_here = n_eq > before ? min(n_eq - before, here) : 0u;
     if (c < P.C) {
-      float s2 = strict[c];
+      float s2 = strict_c;
       if (keep_here > 0u && kappa > -INFINITY) s2 += (float)keep_here * fast_exp2(fmaf(kappa, k2, -rec[c].x));
       rec[c].y = s2;
     }
@@ -1461,10 +1477,8 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
     }
     carry += __shfl(incl, kWave - 1, kWave);
   }
-  // the token id of the last kept copy, unless every copy is kept: chunk cstar is loaded whole and
-  // searched in registers, its vectors in token order (vector k * 64 + lane)
   int32_t vcut = INT32_MAX;
-  if (n_eq < s.ties && cstar >= 0) {
+  if (n_eq < ties && cstar >= 0) {
     const int32_t c0 = cstar * E::kChunk, end = min(c0 + E::kChunk, P.V);
     uint32_t need = rstar;
     if constexpr (kVec) {
@@ -1524,6 +1538,261 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
     P.cuts[slot] = Cut{kappa, vcut};
     if (P.kept_tokens) P.kept_tokens[slot] = kept;
   }
+}
+
+// One workgroup per row slot (target rows, then draft rows when the draft side is logits).  Rows of
+// requests that sample with a profile that truncates get their cut; every other row gets the
+// trivial one.  Writes cuts[slot], kept_tokens[slot] and, for a truncated row, the masses of its
+// chunk records.  After the count kernel (hist set) only the rows it left pending are cut here.
+template <class E, bool kVec>
+__global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
+  __shared__ __align__(16) unsigned char smem[48 * 1024];
+  __shared__ CutShared sh;
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+  const int32_t slot = blockIdx.x;
+  if (P.hist && P.cuts[slot].vcut != kCutPending) return;
+  const RowProfile f = row_profile(P, slot);
+  const float k2 = f.k2;
+  const bool by_k = f.by_k, by_p = f.by_p;
+  const int32_t top_k = f.top_k, milli = f.milli;
+  auto untruncated = [&]() {
+    if (t == 0) {
+      P.cuts[slot] = Cut{-INFINITY, INT32_MAX};
+      if (P.kept_tokens) P.kept_tokens[slot] = P.V;
+    }
+  };
+  // greedy or rejected requests, and profiles that truncate nothing (the draft rows of greedy
+  // requests have no records: they are never read)
+  if (!(k2 > 0.0f) || !(by_k || by_p)) return untruncated();
+  float2* rec = P.part + (int64_t)slot * P.C;
+  // the row's exponent reference R: the largest chunk reference (fl(max z * k))
+  float rl = -INFINITY;
+  for (int32_t c = t; c < P.C; c += kCutThreads) rl = fmaxf(rl, rec[c].x);
+  rl = wave_max(rl);
+  if (lane == 0) sh.wave_ref[wave] = rl;
+  __syncthreads();
+  float R = -INFINITY;
+  for (int w = 0; w < kCutWaves; ++w) R = fmaxf(R, sh.wave_ref[w]);
+  __syncthreads();
+  if (R == -INFINITY) return untruncated();  // a row of -inf only describes no distribution
+  const char* rp = f.target ? row_ptr<E>(P.target, f.row, P.V) : row_ptr<E>(P.draft, f.row, P.V);
+
+  Selected s{0u, 0u, 0ull, 0u};
+  uint32_t n_eq = 0u;  // copies of the cut value that are kept
+  bool done = false;
+  uint32_t* top_cnt = (E::kBytes == 2 && P.C <= kTopChunks) ? reinterpret_cast<uint32_t*>(smem + 16 * 1024) : nullptr;
+  uint32_t top = 0u;
+  if constexpr (E::kBytes == 2) {
+    // the 4096 keys below one just above the row maximum's (R = fl(max z * k), whose quotient by k
+    // lies within a rounding step of the maximum)
+    const uint32_t k_hat = key16_of_bits(__float_as_uint(R / k2) >> 16);
+    top = k_hat + 4u > 65535u ? 65535u : k_hat + 4u;
+    const uint32_t bottom = top >= (uint32_t)(kRegionKeys - 1) ? top - (uint32_t)(kRegionKeys - 1) : 0u;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(smem);
+    done = window_count<kVec>(rp, P.V, P.C, top, bottom, cnt, top_cnt, sh) &&
+           window_pick(cnt, top, bottom, P.C, rec, k2, R, by_k, top_k, by_p, milli, sh, s, n_eq);
+  }
+  __syncthreads();
+  if (!done) radix_select<E, kVec>(rp, P.V, k2, R, by_k, top_k, by_p, milli, smem, sh, s, n_eq);
+  const float kappa = key_logit(s.key);
+  const int32_t kept = (int32_t)(s.cnt_above + n_eq);
+
+  // chunk masses of the kept tokens strictly above the cut value, and the copies of the cut value
+  // in each chunk: from the window's per-chunk counts when every kept key is among them (no second
+  // read of the row), else by a pass over the row (the histograms' LDS is free again)
+  __syncthreads();
+  const bool from_counts = done && top_cnt && top - (s.key >> 16) < (uint32_t)kTopKeys;
+  float* strict = reinterpret_cast<float*>(smem);
+  uint32_t* copies = reinterpret_cast<uint32_t*>(smem + (from_counts ? 8 * 1024 : 16 * 1024));
+  if (from_counts) {
+    const uint32_t kkey = s.key >> 16;
+    for (int32_t c = wave; c < P.C; c += kCutWaves) {
+      const float ref_c = rec[c].x;
+      float acc = 0.0f;
+      uint32_t cp = 0u;
+      for (int j = lane; j < kTopKeys && j <= (int)top; j += kWave) {
+        const uint32_t key = top - (uint32_t)j, n = top_cnt[c * kTopKeys + j];
+        if (n && key > kkey) acc += (float)n * fast_exp2(fmaf(key_logit(key16_to_key(key)), k2, -ref_c));
+        if (key == kkey) cp = n;
+      }
+      acc = wave_sum(acc);
+      cp = wave_sum_u32(cp);
+      if (lane == 0) {
+        strict[c] = acc;
+        copies[c] = cp;
+      }
+    }
+  } else {
+    chunk_pass<E, kVec>(rp, P.V, P.C, rec, kappa, k2, strict, copies, lane, wave);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  finish_cut<E, kVec>(P, slot, rp, rec, kappa, k2, s.ties, n_eq, kept,
+                      [&](int32_t c, float& st, uint32_t& cp) {
+                        st = strict[c];
+                        cp = copies[c];
+                      },
+                      lane);
+}
+
+// The count kernel: one wave per row slot of a truncating bf16 call whose row pass counted, per
+// chunk, the kHistKeys keys at and below the chunk maximum's.  Every chunk's window covers the
+// row's top kHistKeys keys (no chunk maximum lies above the row maximum), so their counts are the
+// sums of the chunks' counts.  When the cut of top-k, then top-p, lands among them it follows from
+// the counts alone (the same selection as the window's), and so do the kept masses of the chunks;
+// the row is read only where ties of the cut value leave a token id to find.  Otherwise (the cut
+// lies deeper, or a chunk that could not be counted reaches the window) the row is left pending
+// for row_cuts.  Lane l holds the keys top - 2l and top - 2l - 1.
+__global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int64_t slot64 = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t rows = P.qrows ? P.n_t : (int64_t)P.n_t + P.n_d;
+  if (slot64 >= rows) return;
+  const int32_t slot = (int32_t)slot64;
+  const RowProfile f = row_profile(P, slot);
+  auto write_cut = [&](Cut c, int32_t kept) {
+    if (lane == 0) {
+      P.cuts[slot] = c;
+      if (P.kept_tokens && c.vcut != kCutPending) P.kept_tokens[slot] = kept;
+    }
+  };
+  if (!(f.k2 > 0.0f) || !(f.by_k || f.by_p)) return write_cut(Cut{-INFINITY, INT32_MAX}, P.V);
+  float2* rec = P.part + (int64_t)slot * P.C;
+  const uint32_t* htop = P.hist_top + (int64_t)slot * P.C;
+  const uint16_t* hist = reinterpret_cast<const uint16_t*>(P.hist) + (int64_t)slot * P.C * kHistKeys;
+  // R (the largest chunk reference), the row's top key and whether an uncounted chunk reaches it
+  float R = -INFINITY;
+  uint32_t top = 0u;
+  for (int32_t c = lane; c < P.C; c += kWave) {
+    R = fmaxf(R, rec[c].x);
+    top = max(top, htop[c] & 0xffffu);
+  }
+  R = wave_max(R);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, o, kWave));
+  if (R == -INFINITY) return write_cut(Cut{-INFINITY, INT32_MAX}, P.V);  // a row of -inf only
+  bool bad = false;
+  for (int32_t c = lane; c < P.C; c += kWave)
+    bad |= (htop[c] & kNoCounts) && (htop[c] & 0xffffu) + (uint32_t)kHistKeys > top;
+  if (__ballot(bad)) return write_cut(Cut{0.0f, kCutPending}, 0);
+  // the counts of keys top - j0 and top - j0 - 1, summed over the chunks (an uncounted chunk lies
+  // wholly below the window and adds nothing)
+  const int j0 = 2 * lane;
+  uint32_t n0 = 0u, n1 = 0u;
+  constexpr int kBatch = 8;  // chunks whose counts are loaded before any is added
+  for (int32_t cb = 0; cb < P.C; cb += kWave) {
+    const uint32_t mine = cb + lane < P.C ? htop[cb + lane] : kNoCounts;
+    const int nc = min(kWave, P.C - cb);
+    for (int q0 = 0; q0 < nc; q0 += kBatch) {
+      uint32_t a[kBatch], b[kBatch];
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        a[r] = b[r] = 0u;
+        const int q = q0 + r;
+        const uint32_t tq = q < nc ? (uint32_t)__builtin_amdgcn_readlane((int)mine, q) : kNoCounts;
+        if (tq & kNoCounts) continue;
+        const int d = j0 - (int)(top - tq);  // chunk-local index of key top - j0
+        const uint16_t* hc = hist + (int64_t)(cb + q) * kHistKeys;
+        if (d >= 0 && d < kHistKeys) a[r] = hc[d];
+        if (d + 1 >= 0 && d + 1 < kHistKeys) b[r] = hc[d + 1];
+      }
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        n0 += a[r];
+        n1 += b[r];
+      }
+    }
+  }
+  const uint32_t key0 = top - (uint32_t)j0, key1 = key0 - 1u;
+  const uint64_t e0 = fixed_mass(key_logit(key16_to_key(key0)), f.k2, R);
+  const uint64_t e1 = fixed_mass(key_logit(key16_to_key(key1)), f.k2, R);
+  const uint64_t m0 = f.by_p ? (uint64_t)n0 * e0 : 0ull, m1 = f.by_p ? (uint64_t)n1 * e1 : 0ull;
+  // inclusive scans over the lanes (rank order) of the counts and masses
+  uint32_t ci = n0 + n1;
+  uint64_t mi = m0 + m1;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t uc = __shfl_up(ci, o, kWave);
+    const uint64_t um = __shfl_up(mi, o, kWave);
+    if (lane >= o) {
+      ci += uc;
+      mi += um;
+    }
+  }
+  const uint32_t c_before = ci - n0 - n1;
+  const uint64_t m_before = mi - m0 - m1;
+  // the key at which a selection lands, by its lane: (key, count above, mass above, copies)
+  auto land = [&](bool at0, bool at1, Selected& out) {
+    const uint64_t who = __ballot(at0 || at1);
+    if (!who) return false;
+    const int g = __ffsll((unsigned long long)who) - 1;
+    const bool first = at0;
+    const uint32_t key = __shfl(first ? key0 : key1, g, kWave);
+    const uint32_t above = __shfl(first ? c_before : c_before + n0, g, kWave);
+    const uint64_t mass = __shfl(first ? m_before : m_before + m0, g, kWave);
+    const uint32_t ties = __shfl(first ? n0 : n1, g, kWave);
+    out = Selected{key16_to_key(key), above, mass, ties};
+    return true;
+  };
+  Selected s{0u, 0u, 0ull, 0u};
+  uint32_t n_eq = 0u;
+  uint64_t mass_k = 0ull;
+  if (f.by_k) {
+    const uint32_t need = (uint32_t)f.top_k;
+    if (!land(c_before < need && need <= c_before + n0, c_before + n0 < need && need <= ci, s))
+      return write_cut(Cut{0.0f, kCutPending}, 0);  // the top-k cut lies below the window
+    n_eq = need - s.cnt_above;
+    mass_k = s.mass_above + (uint64_t)n_eq * fixed_mass(key_logit(s.key), f.k2, R);
+  } else if (f.by_p) {
+    // the row's mass in fixed point, from the chunk records (fp64 across chunks)
+    double part = 0.0;
+    for (int32_t c = lane; c < P.C; c += kWave)
+      if (rec[c].y > 0.0f) part += (double)rec[c].y * exp2((double)rec[c].x - (double)R);
+    mass_k = (uint64_t)(wave_sum(part) * (double)kFixScale);
+  }
+  if (f.by_p) {
+    // the first key (rank order) where the running mass reaches the nucleus mass
+    const double target = (double)mass_k * ((double)f.milli / 1000.0);
+    Selected sp;
+    if (!land(n0 > 0u && (double)(m_before + m0) >= target, n1 > 0u && (double)(mi) >= target, sp))
+      return write_cut(Cut{0.0f, kCutPending}, 0);  // the nucleus reaches below the window
+    uint32_t n = copies_to_reach(sp.mass_above, fixed_mass(key_logit(sp.key), f.k2, R), sp.ties, target);
+    if (f.by_k && sp.key == s.key && n > n_eq) n = n_eq;
+    s = sp;
+    n_eq = n;
+  }
+  const float kappa = key_logit(s.key);
+  const int32_t kept = (int32_t)(s.cnt_above + n_eq);
+  const char* rp = f.target ? row_ptr<Bf16>(P.target, f.row, P.V) : row_ptr<Bf16>(P.draft, f.row, P.V);
+  const uint32_t kkey = s.key >> 16;
+  // per chunk (lanes over chunks): the kept mass above kappa and the copies of kappa, from the
+  // chunk's own counts (8 keys per 16-byte load; a chunk row of counts is 256 bytes)
+  finish_cut<Bf16, true>(P, slot, rp, rec, kappa, f.k2, s.ties, n_eq, kept,
+                         [&](int32_t c, float& st, uint32_t& cp) {
+                           const uint32_t tc = htop[c];
+                           st = 0.0f;
+                           cp = 0u;
+                           if ((tc & kNoCounts) || (tc & 0xffffu) < kkey) return;  // nothing kept here
+                           const float ref_c = rec[c].x;
+                           const int span = (int)((tc & 0xffffu) - kkey);  // keys kept: d = 0 .. span
+                           const u32x4* hv = reinterpret_cast<const u32x4*>(hist + (int64_t)c * kHistKeys);
+                           for (int d8 = 0; d8 <= span / 8; ++d8) {
+                             const u32x4 v = hv[d8];
+                             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                             for (int q = 0; q < 8; ++q) {
+                               const int d = 8 * d8 + q;
+                               const uint32_t n = (w[q / 2] >> (16 * (q & 1))) & 0xffffu;
+                               if (d < span && n)
+                                 st += (float)n *
+                                       fast_exp2(fmaf(key_logit(key16_to_key((tc & 0xffffu) - (uint32_t)d)), f.k2, -ref_c));
+                               if (d == span) cp = n;
+                             }
+                           }
+                         },
+                         lane);
 }
 
 // ============================================================================ 3. verdicts
@@ -1967,7 +2236,7 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 struct Layout {
   int32_t C;
   int64_t n_t, slots;
-  size_t part, cuts, total;
+  size_t part, cuts, hist, hist_top, total;  // hist and hist_top: bf16 only (else 0 bytes)
 };
 
 constexpr size_t kAlign = 256;
@@ -1995,6 +2264,9 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   };
   L->part = take((size_t)slots * C * sizeof(float2));
   L->cuts = take((size_t)slots * sizeof(Cut));
+  const size_t counts = dtype == SDV_BF16 ? (size_t)slots * C : 0;  // per-chunk key counts of truncating calls
+  L->hist = take(counts * kHistKeys * sizeof(uint16_t));
+  L->hist_top = take(counts * sizeof(uint32_t));
   L->total = off;
   return SDV_OK;
 }
@@ -2006,15 +2278,27 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   };
   // the stream reads draft rows only when they are logits of a sampling rule
   P.n_units = (int64_t)(kMode == kModeGreedy || P.qrows ? P.n_t : P.n_t + P.n_d) * P.C;
+  // top-k / top-p: the cut of every logit row the verdicts read (the greedy rule keeps its argmax
+  // under any truncation, so it needs none); bf16 rows get per-chunk key counts from the row pass
+  const bool cut = kMode != kModeGreedy && (P.top_k || P.top_p_milli);
+  const dim3 units((unsigned)((P.n_units + 3) / 4));
   record(0);
-  hipLaunchKernelGGL((row_records<E, kMode, kVec>), dim3((unsigned)((P.n_units + 3) / 4)), dim3(256), 0, stream, P);
+  if constexpr (E::kBytes == 2 && kVec && kMode != kModeGreedy) {
+    if (!cut) P.hist = nullptr;
+    if (P.hist) hipLaunchKernelGGL((row_records<E, kMode, kVec, true>), units, dim3(256), 0, stream, P);
+    else hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), units, dim3(256), 0, stream, P);
+  } else {
+    P.hist = nullptr;
+    hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), units, dim3(256), 0, stream, P);
+  }
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(1);
-  // top-k / top-p: the cut of every logit row the verdicts read (the greedy rule keeps its argmax
-  // under any truncation, so it needs none)
-  const bool cut = kMode != kModeGreedy && (P.top_k || P.top_p_milli);
   if (cut) {
     const int64_t rows = P.qrows ? P.n_t : (int64_t)P.n_t + P.n_d;
+    if (P.hist) {  // rows the counts settle; the rest are left pending for row_cuts
+      hipLaunchKernelGGL(row_cuts_counted, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, P);
+      if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+    }
     hipLaunchKernelGGL((row_cuts<E, kVec>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
     record(3);
@@ -2122,6 +2406,8 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.top_p_milli = opt->top_p_milli;
   P.kept_tokens = opt->kept_tokens;
   P.cuts = reinterpret_cast<Cut*>(ws + L.cuts);
+  P.hist = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist) : nullptr;
+  P.hist_top = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist_top) : nullptr;
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};

@@ -280,3 +280,58 @@ def test_binary32_rows_on_the_vector_path(V):
     top_k, milli = _profiles(b.B, V, rng)
     b.tokens = drafter_tokens(b, top_k, milli, rng, n_bad=2)
     check(b, top_k, milli)
+
+
+def _counted_row(kind, V, rng):
+    """Rows for the row pass's per-chunk key counts (bf16, one binade below each chunk maximum)."""
+    z = rng.standard_normal(V).astype(np.float32) * 3
+    if kind == 1:  # every logit negative: no chunk is counted, the window pass decides
+        z -= 30
+    elif kind == 2:  # one chunk of zeros, -0 and denormals: not counted, and far below the row's top
+        z[8192:16384] = rng.choice(np.array([0.0, -0.0, 1e-39, 5e-39], dtype=np.float32), 8192)
+    elif kind == 3:  # a tiny positive maximum: its window would reach +0
+        z = rng.standard_normal(V).astype(np.float32) - 5
+        z[rng.choice(V, 4, replace=False)] = np.array([1e-39, 2e-39, 3e-39, 4e-39], dtype=np.float32)
+    elif kind == 4:  # a staircase of 300 keys below 8.0, three copies each, over a negative floor
+        z = rng.standard_normal(V).astype(np.float32) - 10
+        steps = W.bf16_to_f32(np.uint16(0x4100) - np.arange(300, dtype=np.uint16))
+        z[rng.choice(V, 900, replace=False)] = np.repeat(steps, 3)
+    elif kind == 5:  # peaked: three large logits over a N(0, 1) floor
+        z = rng.standard_normal(V).astype(np.float32)
+        z[rng.choice(V, 3, replace=False)] = np.array([14.0, 13.5, 13.0], dtype=np.float32)
+    return z
+
+
+def test_row_pass_counts_and_their_fallbacks():
+    """Truncating bf16 calls count, in the row pass, the keys of the binade below each chunk's
+    maximum, and cut from those counts when the cut lies inside that binade.  Rows here put the cut
+    just inside and just outside it (a staircase of keys: top-k 382 ends on the 128th key, 385 on the
+    129th), make a nucleus end inside it (a peaked row with top-p alone) or beyond it, and give
+    chunks that cannot be counted (a maximum <= 0, or one whose binade would reach +0), alone or
+    next to counted ones."""
+    rng = np.random.default_rng(79)
+    B, V, K = 48, 3 * 8192 + 1000, 2
+    kinds = np.arange(B) % 6
+    cu = W.offsets_from_depths(np.full(B, K))
+    n_d = B * K
+    tgt = np.empty((n_d + B, V), dtype=np.float32)
+    drf = np.empty((n_d, V), dtype=np.float32)
+    for i in range(B):
+        for j in range(K + 1):
+            tgt[cu[i] + i + j] = _counted_row(kinds[i], V, rng)
+        for j in range(K):  # the target row with a tenth of its logits moved: drafts are often accepted
+            d = tgt[cu[i] + i + j].copy()
+            moved = rng.random(V) < 0.1
+            d[moved] += rng.standard_normal(int(moved.sum())).astype(np.float32)
+            drf[cu[i] + j] = d
+    b = W.Batch(name="row_pass_counts", V=V, dtype="bf16", temperature=0.8, seed=13, target=W.bf16_bits(tgt),
+                draft=W.bf16_bits(drf), tokens=np.zeros(n_d, dtype=np.int32), cu=cu)
+    choices = {0: ([50, 200, 0], [900, 1000, 950]), 1: ([50, 0], [900]), 2: ([50, 0], [900, 950]),
+               3: ([5, 50], [900, 1000]), 4: ([382, 384, 385, 386, 900], [1000, 990, 900]),
+               5: ([0], [500, 900, 990])}
+    nth = np.arange(B) // 6  # each kind's requests cycle through its profiles
+    top_k = np.array([choices[k][0][n % len(choices[k][0])] for k, n in zip(kinds, nth)], dtype=np.int32)
+    milli = np.array([choices[k][1][n % len(choices[k][1])] for k, n in zip(kinds, nth)], dtype=np.int32)
+    b.tokens = drafter_tokens(b, top_k, milli, rng)
+    acc, out, got, ref = check(b, top_k, milli)
+    assert (acc >= 0).all()
