@@ -29,6 +29,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -42,7 +43,8 @@ METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=25
 KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
                   "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
 KERNELS = ["row_records", "verdicts"]
-TRUNCATION_KERNELS = ["row_records", "row_cuts", "verdicts"]
+TRUNCATION_KERNELS = ["row_records", "cuts", "verdicts"]  # "cuts": row_cuts_counted, then row_cuts
+TRACE_KERNELS = ["row_records", "row_cuts_counted", "row_cuts", "verdicts", "read_kernel", "philox_kernel"]
 CHUNK_BYTES = 16384
 
 
@@ -367,7 +369,7 @@ def main():
     roof_kernel, roof_bytes, roof_ms = "row_records", mean_stream, per_kernel[0]
     if truncating and per_kernel[1] > per_kernel[0]:
         roof_bytes = float(np.mean([truncated_bytes(batches[(args.warmup + k) % len(sets)]) for k in range(args.steps)]))
-        roof_kernel, roof_ms = "row_cuts", per_kernel[1]
+        roof_kernel, roof_ms = "cuts", per_kernel[1]
     roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
 
     result = {
@@ -422,8 +424,8 @@ def main():
 # ----------------------------------------------------------------------------- profile summaries
 
 def _short(name: str) -> str:
-    for k in TRUNCATION_KERNELS + ["read_kernel", "philox_kernel"]:
-        if f"sdv{len(k)}{k}" in name or f"::{k}" in name or name.startswith(k):
+    for k in TRACE_KERNELS:  # longer names first where one name starts another
+        if re.search(rf"(sdv{len(k)}{k}[EI])|(::{k}[(<])|(^{k}[(<])", name):
             return k
     return name.split("(")[0][:48]
 

@@ -95,7 +95,7 @@ typedef struct sdv_diag {
  * The workspace needs no initialisation and holds nothing between calls.  It holds 8 bytes per
  * chunk of every logit row (16 KiB of logits) and 8 bytes per row; bf16 batches add 260 bytes per
  * chunk, where the row pass of a top-k / top-p call counts the logits just below each chunk's
- * maximum.
+ * maximum, and 4 bytes per row.
  */
 size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype);
 

@@ -119,6 +119,7 @@ struct Params {
   Cut* cuts;                  // [row slots] the cut of every row (workspace), read when truncation is on
   uint32_t* hist;             // [row slots][C][kHistKeys / 2] per-chunk key counts, two 16-bit counts a word
   uint32_t* hist_top;         // [row slots][C] the chunk maximum's key, | kNoCounts without counts
+  int32_t* pending;           // [1 + row slots] rows the count kernel leaves to row_cuts: count, then slots
   DiagPtrs dg;
 };
 
@@ -497,6 +498,7 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
   const int32_t c0 = c * E::kChunk;
   const int32_t n = min(E::kChunk, P.V - c0);
   float2 rec;
+  if (kHist && u == 0 && lane == 0) P.pending[0] = 0;  // the count kernel appends to an empty list
   if constexpr (kHist && kMode != kModeProfiled) {
     u32x4 buf[kVecPerLane];
     load_chunk<E>(rp, c0, n, lane, buf);
@@ -1435,18 +1437,15 @@ __device__ __forceinline__ RowProfile row_profile(const Params& P, int32_t slot)
   return f;
 }
 
-// A row the count kernel leaves to the full cut kernel carries vcut = kCutPending.
-constexpr int32_t kCutPending = INT32_MIN;
-
 // The last steps of a row's cut, by one wave: the kept copies of the cut value per chunk in token
 // order, each chunk record's mass rewritten to the mass of the chunk's kept tokens, and the token id
 // of the last kept copy (unless every copy is kept: chunk cstar is loaded whole and searched in
-// registers, its vectors in token order, vector k * 64 + lane).  chunk(c) gives the chunk's mass
-// of kept tokens strictly above kappa (in its record's frame) and its copies of kappa.  Writes
-// cuts[slot] and kept_tokens[slot].
+// registers, its vectors in token order, vector k * 64 + lane).  chunks(cb, st, cp), called by
+// every lane, gives chunk cb + lane's mass of kept tokens strictly above kappa (in its record's
+// frame) and its copies of kappa (0 past the last chunk).  Writes cuts[slot] and kept_tokens[slot].
 template <class E, bool kVec, class ChunkFn>
 __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const char* rp, float2* rec, float kappa,
-                                           float k2, uint32_t ties, uint32_t n_eq, int32_t kept, ChunkFn chunk,
+                                           float k2, uint32_t ties, uint32_t n_eq, int32_t kept, ChunkFn chunks,
                                            int lane) {
   uint32_t carry = 0u;
   int32_t cstar = -1;
@@ -1455,7 +1454,7 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
     const int32_t c = cb + lane;
     float strict_c = 0.0f;
     uint32_t here = 0u;
-    if (c < P.C) chunk(c, strict_c, here);
+    chunks(cb, strict_c, here);
     uint32_t incl = here;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -1540,18 +1539,13 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
   }
 }
 
-// One workgroup per row slot (target rows, then draft rows when the draft side is logits).  Rows of
-// requests that sample with a profile that truncates get their cut; every other row gets the
-// trivial one.  Writes cuts[slot], kept_tokens[slot] and, for a truncated row, the masses of its
-// chunk records.  After the count kernel (hist set) only the rows it left pending are cut here.
+// The cut of one row slot by a workgroup of kCutThreads.  Rows of requests that sample with a
+// profile that truncates get their cut; every other row gets the trivial one.  Writes cuts[slot],
+// kept_tokens[slot] and, for a truncated row, the masses of its chunk records.
 template <class E, bool kVec>
-__global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
-  __shared__ __align__(16) unsigned char smem[48 * 1024];
-  __shared__ CutShared sh;
+__device__ __forceinline__ void cut_row(const Params& P, int32_t slot, unsigned char* smem, CutShared& sh) {
   const int t = threadIdx.x, lane = t & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
-  const int32_t slot = blockIdx.x;
-  if (P.hist && P.cuts[slot].vcut != kCutPending) return;
   const RowProfile f = row_profile(P, slot);
   const float k2 = f.k2;
   const bool by_k = f.by_k, by_p = f.by_p;
@@ -1627,13 +1621,31 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
     chunk_pass<E, kVec>(rp, P.V, P.C, rec, kappa, k2, strict, copies, lane, wave);
   }
   __syncthreads();
-  if (wave != 0) return;
-  finish_cut<E, kVec>(P, slot, rp, rec, kappa, k2, s.ties, n_eq, kept,
-                      [&](int32_t c, float& st, uint32_t& cp) {
-                        st = strict[c];
-                        cp = copies[c];
-                      },
-                      lane);
+  if (wave == 0)
+    finish_cut<E, kVec>(P, slot, rp, rec, kappa, k2, s.ties, n_eq, kept,
+                        [&](int32_t cb, float& st, uint32_t& cp) {
+                          const int32_t c = cb + lane;
+                          st = c < P.C ? strict[c] : 0.0f;
+                          cp = c < P.C ? copies[c] : 0u;
+                        },
+                        lane);
+  __syncthreads();  // the shared memory is free for the next row
+}
+
+// Full cuts: one workgroup per row slot (target rows, then draft rows when the draft side is
+// logits), or (kPending), after the count kernel, one per row it left pending (workgroup k takes
+// the k-th; the others end at once).
+template <class E, bool kVec, bool kPending>
+__global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
+  __shared__ __align__(16) unsigned char smem[48 * 1024];
+  __shared__ CutShared sh;
+  if constexpr (kPending) {
+    // the list is uniform: saying so keeps the row's addressing scalar
+    if ((int32_t)blockIdx.x < P.pending[0])
+      cut_row<E, kVec>(P, __builtin_amdgcn_readfirstlane(P.pending[1 + blockIdx.x]), smem, sh);
+  } else {
+    cut_row<E, kVec>(P, (int32_t)blockIdx.x, smem, sh);
+  }
 }
 
 // The count kernel: one wave per row slot of a truncating bf16 call whose row pass counted, per
@@ -1645,6 +1657,13 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
 // lies deeper, or a chunk that could not be counted reaches the window) the row is left pending
 // for row_cuts.  Lane l holds the keys top - 2l and top - 2l - 1.
 __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
+  // per wave: the lanes' contributions to 16 chunks, transposed (rows padded to 65 words), and
+  // the 64 chunk sums of a batch
+  constexpr int kTr = 16, kTrStride = kWave + 1;
+  __shared__ float tr_mass[4][kTr * kTrStride];
+  __shared__ uint32_t tr_copies[4][kTr * kTrStride];
+  __shared__ float sum_mass[4][kWave];
+  __shared__ uint32_t sum_copies[4][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int64_t slot64 = (int64_t)blockIdx.x * 4 + wave;
@@ -1655,8 +1674,11 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   auto write_cut = [&](Cut c, int32_t kept) {
     if (lane == 0) {
       P.cuts[slot] = c;
-      if (P.kept_tokens && c.vcut != kCutPending) P.kept_tokens[slot] = kept;
+      if (P.kept_tokens) P.kept_tokens[slot] = kept;
     }
+  };
+  auto leave_pending = [&]() {
+    if (lane == 0) P.pending[1 + atomicAdd(&P.pending[0], 1)] = slot;
   };
   if (!(f.k2 > 0.0f) || !(f.by_k || f.by_p)) return write_cut(Cut{-INFINITY, INT32_MAX}, P.V);
   float2* rec = P.part + (int64_t)slot * P.C;
@@ -1676,28 +1698,32 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   bool bad = false;
   for (int32_t c = lane; c < P.C; c += kWave)
     bad |= (htop[c] & kNoCounts) && (htop[c] & 0xffffu) + (uint32_t)kHistKeys > top;
-  if (__ballot(bad)) return write_cut(Cut{0.0f, kCutPending}, 0);
-  // the counts of keys top - j0 and top - j0 - 1, summed over the chunks (an uncounted chunk lies
-  // wholly below the window and adds nothing)
+  if (__ballot(bad)) return leave_pending();
   const int j0 = 2 * lane;
+  // the counts of keys top - j0 and top - j0 - 1 in chunks cb + q0 .. cb + q0 + kBatch - 1 of the
+  // batch of 64 whose tops the lanes hold (mine), loaded before any is used
+  constexpr int kBatch = 8;
+  auto load_counts = [&](int32_t cb, int q0, int nc, uint32_t mine, uint32_t (&a)[kBatch], uint32_t (&b)[kBatch]) {
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      a[r] = b[r] = 0u;
+      const int q = q0 + r;
+      const uint32_t tq = q < nc ? (uint32_t)__builtin_amdgcn_readlane((int)mine, q) : kNoCounts;
+      if (tq & kNoCounts) continue;  // an uncounted chunk lies wholly below the window
+      const int d = j0 - (int)(top - tq);  // chunk-local index of key top - j0
+      const uint16_t* hc = hist + (int64_t)(cb + q) * kHistKeys;
+      if (d >= 0 && d < kHistKeys) a[r] = hc[d];
+      if (d + 1 >= 0 && d + 1 < kHistKeys) b[r] = hc[d + 1];
+    }
+  };
+  // summed over the chunks
   uint32_t n0 = 0u, n1 = 0u;
-  constexpr int kBatch = 8;  // chunks whose counts are loaded before any is added
   for (int32_t cb = 0; cb < P.C; cb += kWave) {
     const uint32_t mine = cb + lane < P.C ? htop[cb + lane] : kNoCounts;
     const int nc = min(kWave, P.C - cb);
     for (int q0 = 0; q0 < nc; q0 += kBatch) {
       uint32_t a[kBatch], b[kBatch];
-#pragma unroll
-      for (int r = 0; r < kBatch; ++r) {
-        a[r] = b[r] = 0u;
-        const int q = q0 + r;
-        const uint32_t tq = q < nc ? (uint32_t)__builtin_amdgcn_readlane((int)mine, q) : kNoCounts;
-        if (tq & kNoCounts) continue;
-        const int d = j0 - (int)(top - tq);  // chunk-local index of key top - j0
-        const uint16_t* hc = hist + (int64_t)(cb + q) * kHistKeys;
-        if (d >= 0 && d < kHistKeys) a[r] = hc[d];
-        if (d + 1 >= 0 && d + 1 < kHistKeys) b[r] = hc[d + 1];
-      }
+      load_counts(cb, q0, nc, mine, a, b);
 #pragma unroll
       for (int r = 0; r < kBatch; ++r) {
         n0 += a[r];
@@ -1742,7 +1768,7 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   if (f.by_k) {
     const uint32_t need = (uint32_t)f.top_k;
     if (!land(c_before < need && need <= c_before + n0, c_before + n0 < need && need <= ci, s))
-      return write_cut(Cut{0.0f, kCutPending}, 0);  // the top-k cut lies below the window
+      return leave_pending();  // the top-k cut lies below the window
     n_eq = need - s.cnt_above;
     mass_k = s.mass_above + (uint64_t)n_eq * fixed_mass(key_logit(s.key), f.k2, R);
   } else if (f.by_p) {
@@ -1757,7 +1783,7 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
     const double target = (double)mass_k * ((double)f.milli / 1000.0);
     Selected sp;
     if (!land(n0 > 0u && (double)(m_before + m0) >= target, n1 > 0u && (double)(mi) >= target, sp))
-      return write_cut(Cut{0.0f, kCutPending}, 0);  // the nucleus reaches below the window
+      return leave_pending();  // the nucleus reaches below the window
     uint32_t n = copies_to_reach(sp.mass_above, fixed_mass(key_logit(sp.key), f.k2, R), sp.ties, target);
     if (f.by_k && sp.key == s.key && n > n_eq) n = n_eq;
     s = sp;
@@ -1767,30 +1793,49 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   const int32_t kept = (int32_t)(s.cnt_above + n_eq);
   const char* rp = f.target ? row_ptr<Bf16>(P.target, f.row, P.V) : row_ptr<Bf16>(P.draft, f.row, P.V);
   const uint32_t kkey = s.key >> 16;
-  // per chunk (lanes over chunks): the kept mass above kappa and the copies of kappa, from the
-  // chunk's own counts (8 keys per 16-byte load; a chunk row of counts is 256 bytes)
+  // per chunk: the kept mass above kappa (in the chunk record's frame) and the copies of kappa,
+  // from the chunk's counts of the lanes' keys (a second pass over counts that are still cached)
+  const float z0 = key_logit(key16_to_key(key0)), z1 = key_logit(key16_to_key(key1));
   finish_cut<Bf16, true>(P, slot, rp, rec, kappa, f.k2, s.ties, n_eq, kept,
-                         [&](int32_t c, float& st, uint32_t& cp) {
-                           const uint32_t tc = htop[c];
-                           st = 0.0f;
-                           cp = 0u;
-                           if ((tc & kNoCounts) || (tc & 0xffffu) < kkey) return;  // nothing kept here
-                           const float ref_c = rec[c].x;
-                           const int span = (int)((tc & 0xffffu) - kkey);  // keys kept: d = 0 .. span
-                           const u32x4* hv = reinterpret_cast<const u32x4*>(hist + (int64_t)c * kHistKeys);
-                           for (int d8 = 0; d8 <= span / 8; ++d8) {
-                             const u32x4 v = hv[d8];
-                             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                         [&](int32_t cb, float& st, uint32_t& cp) {
+                           const int nc = min(kWave, P.C - cb);
+                           const uint32_t mine = cb + lane < P.C ? htop[cb + lane] : kNoCounts;
+                           const float mine_ref = cb + lane < P.C ? rec[cb + lane].x : 0.0f;
+                           for (int q0 = 0; q0 < nc; q0 += kTr) {
+                             // this lane's two keys in chunks cb + q0 .. cb + q0 + 15: row r of the
+                             // transposed block holds chunk q0 + r, column l lane l's share
 #pragma unroll
-                             for (int q = 0; q < 8; ++q) {
-                               const int d = 8 * d8 + q;
-                               const uint32_t n = (w[q / 2] >> (16 * (q & 1))) & 0xffffu;
-                               if (d < span && n)
-                                 st += (float)n *
-                                       fast_exp2(fmaf(key_logit(key16_to_key((tc & 0xffffu) - (uint32_t)d)), f.k2, -ref_c));
-                               if (d == span) cp = n;
+                             for (int h = 0; h < kTr; h += kBatch) {
+                               uint32_t a[kBatch], b[kBatch];
+                               load_counts(cb, q0 + h, nc, mine, a, b);
+#pragma unroll
+                               for (int r = 0; r < kBatch; ++r) {
+                                 const int q = q0 + h + r;
+                                 const float ref_q =
+                                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_ref), q < nc ? q : 0));
+                                 float m = 0.0f;
+                                 if (a[r] && key0 > kkey) m += (float)a[r] * fast_exp2(fmaf(z0, f.k2, -ref_q));
+                                 if (b[r] && key1 > kkey) m += (float)b[r] * fast_exp2(fmaf(z1, f.k2, -ref_q));
+                                 tr_mass[wave][(h + r) * kTrStride + lane] = m;
+                                 tr_copies[wave][(h + r) * kTrStride + lane] = key0 == kkey ? a[r] : (key1 == kkey ? b[r] : 0u);
+                               }
                              }
+                             __builtin_amdgcn_wave_barrier();  // a wave's shared-memory operations complete in order
+                             if (lane < kTr && q0 + lane < nc) {  // lane r sums row r in lane order
+                               float m = 0.0f;
+                               uint32_t e = 0u;
+                               for (int l = 0; l < kWave; ++l) {
+                                 m += tr_mass[wave][lane * kTrStride + l];
+                                 e += tr_copies[wave][lane * kTrStride + l];
+                               }
+                               sum_mass[wave][q0 + lane] = m;
+                               sum_copies[wave][q0 + lane] = e;
+                             }
+                             __builtin_amdgcn_wave_barrier();
                            }
+                           st = lane < nc ? sum_mass[wave][lane] : 0.0f;
+                           cp = lane < nc ? sum_copies[wave][lane] : 0u;
+                           __builtin_amdgcn_wave_barrier();
                          },
                          lane);
 }
@@ -2236,7 +2281,7 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 struct Layout {
   int32_t C;
   int64_t n_t, slots;
-  size_t part, cuts, hist, hist_top, total;  // hist and hist_top: bf16 only (else 0 bytes)
+  size_t part, cuts, hist, hist_top, pending, total;  // hist, hist_top, pending: bf16 only (else 0 bytes)
 };
 
 constexpr size_t kAlign = 256;
@@ -2267,6 +2312,7 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   const size_t counts = dtype == SDV_BF16 ? (size_t)slots * C : 0;  // per-chunk key counts of truncating calls
   L->hist = take(counts * kHistKeys * sizeof(uint16_t));
   L->hist_top = take(counts * sizeof(uint32_t));
+  L->pending = take(dtype == SDV_BF16 ? (size_t)(slots + 1) * sizeof(int32_t) : 0);
   L->total = off;
   return SDV_OK;
 }
@@ -2299,7 +2345,15 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
       hipLaunchKernelGGL(row_cuts_counted, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, P);
       if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
     }
-    hipLaunchKernelGGL((row_cuts<E, kVec>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
+    if constexpr (E::kBytes == 2 && kVec) {
+      if (P.hist) {  // the rows the count kernel left pending
+        hipLaunchKernelGGL((row_cuts<E, kVec, true>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
+      } else {
+        hipLaunchKernelGGL((row_cuts<E, kVec, false>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
+      }
+    } else {
+      hipLaunchKernelGGL((row_cuts<E, kVec, false>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
+    }
     if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
     record(3);
   }
@@ -2408,6 +2462,7 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.cuts = reinterpret_cast<Cut*>(ws + L.cuts);
   P.hist = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist) : nullptr;
   P.hist_top = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist_top) : nullptr;
+  P.pending = dtype == SDV_BF16 ? reinterpret_cast<int32_t*>(ws + L.pending) : nullptr;
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};

@@ -44,14 +44,15 @@ def test_abi_version_and_status_strings(lib):
 
 def test_workspace_bytes(lib):
     # row-pass records: 8 B per 16 KiB chunk of every target and draft row, then one 8-byte
-    # top-k / top-p cut per row, then (bf16) 128 16-bit key counts and a 4-byte top key per chunk,
-    # each array 256-byte aligned
+    # top-k / top-p cut per row, then (bf16) 128 16-bit key counts and a 4-byte top key per chunk
+    # and a list of rows (a count, then one 4-byte slot per row), each array 256-byte aligned
     up = lambda n: -(-n // 256) * 256
     ws = lib.sdv_workspace_bytes(256, 1024, 128256, 0)
     chunks = (128256 + 8191) // 8192
     assert chunks == 16
     rows = 1280 + 1024
-    assert ws == up(rows * chunks * 8) + up(rows * 8) + up(rows * chunks * 256) + up(rows * chunks * 4)
+    assert ws == (up(rows * chunks * 8) + up(rows * 8) + up(rows * chunks * 256) + up(rows * chunks * 4)
+                  + up((rows + 1) * 4))
     assert ws % 256 == 0
     # binary32 rows: 4096 logits per chunk, no key counts
     chunks32 = (128256 + 4095) // 4096
