@@ -57,48 +57,124 @@ __device__ __forceinline__ const char* row_ptr(const void* base, int64_t row, in
 }
 
 // ----------------------------------------------------------------------------- wave64 reductions
-// xor butterflies: at every level both partners add the same two values, so every lane ends with
-// the bit-identical result.
+// Butterflies with every lane of the wave active.  Inside a row of 16 lanes the partner comes by a
+// DPP move: lane ^ 1 and lane ^ 2 (quad permutes), then the mirror inside 8 lanes and inside 16
+// (after the quad steps each quad holds one value, so a mirror combines whole quads, then whole
+// halves).  Across rows the gfx950 row swaps hand every lane both rows' values: rows 2r and 2r + 1
+// (permlane16 swap), then the two halves of the wave (permlane32 swap).  Both partners combine the
+// same two operands with a commutative operation, so every lane ends with the bit-identical result.
+// Scans use DPP row shifts by 1, 2, 4, 8, then the row broadcasts of lanes 15 and 31.
+
+namespace wave_detail {
+constexpr int kXor1 = 0xb1, kXor2 = 0x4e, kHalfMirror = 0x141, kMirror = 0x140, kRowShr = 0x110, kBcast15 = 0x142,
+              kBcast31 = 0x143;
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {  // lanes the control leaves without a source read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xf, false);
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp(float v) {
+  return __uint_as_float(dpp<kCtrl, kRowMask>(__float_as_uint(v)));
+}
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ double dpp(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp<kCtrl, kRowMask>((uint32_t)b), hi = dpp<kCtrl, kRowMask>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+// Both rows' (or halves') values of a 32-bit word: lower in lo, upper in hi, in every lane.
+template <int kSpan>
+__device__ __forceinline__ void both(uint32_t v, uint32_t& lo, uint32_t& hi) {
+  if constexpr (kSpan == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+  }
+}
+template <int kSpan>
+__device__ __forceinline__ void both(double v, double& lo, double& hi) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  uint32_t l0, l1, h0, h1;
+  both<kSpan>((uint32_t)b, l0, l1);
+  both<kSpan>((uint32_t)(b >> 32), h0, h1);
+  lo = __longlong_as_double((long long)(((uint64_t)h0 << 32) | l0));
+  hi = __longlong_as_double((long long)(((uint64_t)h1 << 32) | l1));
+}
+// An all-reduce with a commutative combine on floats or doubles.
+template <class T, class Op>
+__device__ __forceinline__ T all_reduce(T v, Op op) {
+  v = op(v, dpp<kXor1>(v));
+  v = op(v, dpp<kXor2>(v));
+  v = op(v, dpp<kHalfMirror>(v));
+  v = op(v, dpp<kMirror>(v));
+  T lo, hi;
+  if constexpr (sizeof(T) == 4) {
+    uint32_t a, b;
+    both<16>(__float_as_uint(v), a, b);
+    v = op(__uint_as_float(a), __uint_as_float(b));
+    both<32>(__float_as_uint(v), a, b);
+    return op(__uint_as_float(a), __uint_as_float(b));
+  } else {
+    both<16>(v, lo, hi);
+    v = op(lo, hi);
+    both<32>(v, lo, hi);
+    return op(lo, hi);
+  }
+}
+}  // namespace wave_detail
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_detail::all_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_detail::all_reduce(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_detail::all_reduce(v, [](double a, double b) { return a + b; });
 }
 
 // Larger value wins; equal values go to the smaller index.
 __device__ __forceinline__ void wave_argmax(float& v, int32_t& idx) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, kWave);
-    const int32_t oi = __shfl_xor(idx, o, kWave);
+  using namespace wave_detail;
+  auto take = [&](float ov, int32_t oi) {
     if (ov > v || (ov == v && oi < idx)) {
       v = ov;
       idx = oi;
     }
-  }
+  };
+  take(__uint_as_float(dpp<kXor1>(__float_as_uint(v))), (int32_t)dpp<kXor1>((uint32_t)idx));
+  take(__uint_as_float(dpp<kXor2>(__float_as_uint(v))), (int32_t)dpp<kXor2>((uint32_t)idx));
+  take(__uint_as_float(dpp<kHalfMirror>(__float_as_uint(v))), (int32_t)dpp<kHalfMirror>((uint32_t)idx));
+  take(__uint_as_float(dpp<kMirror>(__float_as_uint(v))), (int32_t)dpp<kMirror>((uint32_t)idx));
+  uint32_t va, vb, ia, ib;
+  both<16>(__float_as_uint(v), va, vb);
+  both<16>((uint32_t)idx, ia, ib);
+  v = __uint_as_float(va);
+  idx = (int32_t)ia;
+  take(__uint_as_float(vb), (int32_t)ib);
+  both<32>(__float_as_uint(v), va, vb);
+  both<32>((uint32_t)idx, ia, ib);
+  v = __uint_as_float(va);
+  idx = (int32_t)ia;
+  take(__uint_as_float(vb), (int32_t)ib);
 }
 
-// Exclusive prefix sum over the wave (lane order), fp64.
-__device__ __forceinline__ double wave_exclusive_scan(double v, int lane) {
+// Exclusive prefix sum over the wave (lane order), fp64: the inclusive scan less the lane's value.
+__device__ __forceinline__ double wave_exclusive_scan(double v, int) {
+  using namespace wave_detail;
   double incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double up = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += up;
-  }
+  incl += dpp<kRowShr + 1>(incl);
+  incl += dpp<kRowShr + 2>(incl);
+  incl += dpp<kRowShr + 4>(incl);
+  incl += dpp<kRowShr + 8>(incl);
+  incl += dpp<kBcast15, 0xa>(incl);
+  incl += dpp<kBcast31, 0xc>(incl);
   return incl - v;
 }
 
