@@ -355,7 +355,7 @@ __device__ __forceinline__ int32_t search_chunk(int32_t c0, int32_t n, double ta
   if (!hit && !pos) return end - 1;
   // the run to open: the crossing run, or else the last run with positive mass
   const int f = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)pos);
-  const double rest = target - __shfl(before, f, kWave);
+  const double rest = target - lane_value(before, f);
   // step 2: per_lane consecutive elements per lane inside run f
   const int32_t bf = c0 + f * run;
   float w[per_lane];
@@ -385,14 +385,14 @@ __device__ __forceinline__ int32_t search_chunk(int32_t c0, int32_t n, double ta
         found = true;
       }
     }
-    y = __shfl(yl, g, kWave);
+    y = lane_value(yl, g);
   } else if (pos2) {
     const int h = 63 - __clzll((long long)pos2);
     int32_t yl = -1;
 #pragma unroll
     for (int q = 0; q < per_lane; ++q)
       if (w[q] > 0.0f) yl = bf + lane * per_lane + q;
-    y = __shfl(yl, h, kWave);
+    y = lane_value(yl, h);
   }
   return y;
 }
@@ -413,14 +413,14 @@ __device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, 
     const uint64_t hit = __ballot(c0 + lane < C && carry + excl + m > U);
     if (hit) {
       const int f = __ffsll((unsigned long long)hit) - 1;
-      *target_in_chunk = U - (carry + __shfl(excl, f, kWave));
+      *target_in_chunk = U - (carry + lane_value(excl, f));
       return c0 + f;
     }
     const uint64_t pos = __ballot(c0 + lane < C && m > 0.0);
     if (pos) {
       const int h = 63 - __clzll((long long)pos);
       last_pos = c0 + h;
-      last_before = carry + __shfl(excl, h, kWave);
+      last_before = carry + lane_value(excl, h);
     }
     carry += wave_sum(m);
   }
@@ -656,7 +656,7 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
   const int owner = kr % n_waves;
   if (wave != owner) return -1;
   const int j = kr / n_waves;
-  const double rest = target - __shfl(rex, kr, kWave);
+  const double rest = target - lane_value(rex, kr);
   // the owning wave: scan its 64 vector sums of row kr, then walk the chosen vector
   const float v = j == 0 ? vs[0] : vs[1];
   const double vex = wave_exclusive_scan((double)v, lane);
@@ -680,7 +680,7 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
     }
   }
   if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
-  return __shfl(yl, l, kWave);
+  return lane_value(yl, l);
 }
 
 // ============================================================================ probability-row drafts
@@ -870,7 +870,7 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
   const int owner = kr % n_waves;
   if (wave != owner) return -1;
   const int j = kr / n_waves;
-  const double rest = target - __shfl(rex, kr, kWave);
+  const double rest = target - lane_value(rex, kr);
   const float v = j == 0 ? vs[0] : vs[1];
   const double vex = wave_exclusive_scan((double)v, lane);
   const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
@@ -894,7 +894,7 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
     }
   }
   if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
-  return __shfl(yl, l, kWave);
+  return lane_value(yl, l);
 }
 
 // ============================================================================ 2. truncation
@@ -960,16 +960,6 @@ __device__ __forceinline__ uint64_t fixed_mass(float z, float k2, float R) {
   return (uint64_t)(fast_exp2(fmaf(z, k2, -R)) * kFixScale);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
 
 struct CutShared {
   uint32_t wave_cnt[kCutWaves];
@@ -989,15 +979,8 @@ __device__ __forceinline__ void block_scan(uint32_t c, uint64_t m, uint32_t& c_b
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   uint32_t ci = c;
   uint64_t mi = m;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t uc = __shfl_up(ci, o, kWave);
-    const uint64_t um = __shfl_up(mi, o, kWave);
-    if (lane >= o) {
-      ci += uc;
-      mi += um;
-    }
-  }
+  ci = wave_inclusive_scan(ci);
+  mi = wave_inclusive_scan(mi);
   if (lane == kWave - 1) {
     sh.wave_cnt[wave] = ci;
     sh.wave_mass[wave] = mi;
@@ -1455,12 +1438,7 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
     float strict_c = 0.0f;
     uint32_t here = 0u;
     chunks(cb, strict_c, here);
-    uint32_t incl = here;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t up = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += up;
-    }
+    const uint32_t incl = wave_inclusive_scan(here);
     const uint32_t before = carry + incl - here;
     const uint32_t keep_here = n_eq > before ? min(n_eq - before, here) : 0u;
     if (c < P.C) {
@@ -1472,9 +1450,9 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
     if (holds && cstar < 0) {
       const int g = __ffsll((unsigned long long)holds) - 1;
       cstar = cb + g;
-      rstar = __shfl(n_eq - before, g, kWave);
+      rstar = lane_value(n_eq - before, g);
     }
-    carry += __shfl(incl, kWave - 1, kWave);
+    carry += lane_value(incl, kWave - 1);
   }
   int32_t vcut = INT32_MAX;
   if (n_eq < ties && cstar >= 0) {
@@ -1495,13 +1473,8 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
         for (int e = 0; e < E::kPerVec; ++e)
           if (lane + kWave * k < nvec && z[e] == kappa) mask |= 1u << e;
         const uint32_t mine = (uint32_t)__popc(mask);
-        uint32_t incl = mine;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-          const uint32_t up = __shfl_up(incl, o, kWave);
-          if (lane >= o) incl += up;
-        }
-        const uint32_t total = __shfl(incl, kWave - 1, kWave);
+        const uint32_t incl = wave_inclusive_scan(mine);
+        const uint32_t total = lane_value(incl, kWave - 1);
         if (need <= total) {
           const uint64_t at = __ballot(incl - mine < need && need <= incl);
           const int g = __ffsll((unsigned long long)at) - 1;
@@ -1513,7 +1486,7 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
               if (left == 1u && v < 0) v = c0 + (lane + kWave * k) * E::kPerVec + e;
               --left;
             }
-          vcut = __shfl(v, g, kWave);
+          vcut = lane_value(v, g);
           break;
         }
         need -= total;
@@ -1692,8 +1665,7 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
     top = max(top, htop[c] & 0xffffu);
   }
   R = wave_max(R);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, o, kWave));
+  top = wave_max_u32(top);
   if (R == -INFINITY) return write_cut(Cut{-INFINITY, INT32_MAX}, P.V);  // a row of -inf only
   bool bad = false;
   for (int32_t c = lane; c < P.C; c += kWave)
@@ -1738,15 +1710,8 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   // inclusive scans over the lanes (rank order) of the counts and masses
   uint32_t ci = n0 + n1;
   uint64_t mi = m0 + m1;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t uc = __shfl_up(ci, o, kWave);
-    const uint64_t um = __shfl_up(mi, o, kWave);
-    if (lane >= o) {
-      ci += uc;
-      mi += um;
-    }
-  }
+  ci = wave_inclusive_scan(ci);
+  mi = wave_inclusive_scan(mi);
   const uint32_t c_before = ci - n0 - n1;
   const uint64_t m_before = mi - m0 - m1;
   // the key at which a selection lands, by its lane: (key, count above, mass above, copies)
@@ -1755,10 +1720,10 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
     if (!who) return false;
     const int g = __ffsll((unsigned long long)who) - 1;
     const bool first = at0;
-    const uint32_t key = __shfl(first ? key0 : key1, g, kWave);
-    const uint32_t above = __shfl(first ? c_before : c_before + n0, g, kWave);
-    const uint64_t mass = __shfl(first ? m_before : m_before + m0, g, kWave);
-    const uint32_t ties = __shfl(first ? n0 : n1, g, kWave);
+    const uint32_t key = lane_value(first ? key0 : key1, g);
+    const uint32_t above = lane_value(first ? c_before : c_before + n0, g);
+    const uint64_t mass = lane_value(first ? m_before : m_before + m0, g);
+    const uint32_t ties = lane_value(first ? n0 : n1, g);
     out = Selected{key16_to_key(key), above, mass, ties};
     return true;
   };
@@ -2095,15 +2060,15 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
           // weights in the frame 2^(z_t k - ref_t) of the rejected target row; draft side
           // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and the factor 2^-(e - e_hi)
           d.kind = SDV_TERM_RESIDUAL;
-          d.ref_t = __shfl(ft.ref, a, kWave);
+          d.ref_t = lane_value(ft.ref, a);
           if constexpr (kQ) {  // q scaled into the frame: q 2^(l2_t - ref_t)
-            d.q_scale = (float)exp2(__shfl(ft.l2, a, kWave) - (double)d.ref_t);
+            d.q_scale = (float)exp2(lane_value(ft.l2, a) - (double)d.ref_t);
           } else {
-            const double e = (double)d.ref_t + __shfl(fd.l2, a, kWave) - __shfl(ft.l2, a, kWave);
+            const double e = (double)d.ref_t + lane_value(fd.l2, a) - lane_value(ft.l2, a);
             d.e_hi = (float)e;
             d.q_scale = (float)exp2((double)d.e_hi - e);
           }
-          d.u = P.u_each ? P.u_each[trow0 + a] : (double)__shfl(draw_uniform(blk), a, kWave);
+          d.u = P.u_each ? P.u_each[trow0 + a] : (double)lane_value(draw_uniform(blk), a);
         }
       }
     }

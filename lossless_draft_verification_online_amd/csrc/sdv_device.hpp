@@ -77,10 +77,13 @@ __device__ __forceinline__ float dpp(float v) {
   return __uint_as_float(dpp<kCtrl, kRowMask>(__float_as_uint(v)));
 }
 template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ uint64_t dpp(uint64_t v) {
+  const uint64_t lo = dpp<kCtrl, kRowMask>((uint32_t)v), hi = dpp<kCtrl, kRowMask>((uint32_t)(v >> 32));
+  return (hi << 32) | lo;
+}
+template <int kCtrl, int kRowMask = 0xf>
 __device__ __forceinline__ double dpp(double v) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint64_t lo = dpp<kCtrl, kRowMask>((uint32_t)b), hi = dpp<kCtrl, kRowMask>((uint32_t)(b >> 32));
-  return __longlong_as_double((long long)((hi << 32) | lo));
+  return __longlong_as_double((long long)dpp<kCtrl, kRowMask>((uint64_t)__double_as_longlong(v)));
 }
 // Both rows' (or halves') values of a 32-bit word: lower in lo, upper in hi, in every lane.
 template <int kSpan>
@@ -96,15 +99,28 @@ __device__ __forceinline__ void both(uint32_t v, uint32_t& lo, uint32_t& hi) {
   }
 }
 template <int kSpan>
-__device__ __forceinline__ void both(double v, double& lo, double& hi) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
+__device__ __forceinline__ void both(uint64_t v, uint64_t& lo, uint64_t& hi) {
   uint32_t l0, l1, h0, h1;
-  both<kSpan>((uint32_t)b, l0, l1);
-  both<kSpan>((uint32_t)(b >> 32), h0, h1);
-  lo = __longlong_as_double((long long)(((uint64_t)h0 << 32) | l0));
-  hi = __longlong_as_double((long long)(((uint64_t)h1 << 32) | l1));
+  both<kSpan>((uint32_t)v, l0, l1);
+  both<kSpan>((uint32_t)(v >> 32), h0, h1);
+  lo = ((uint64_t)h0 << 32) | l0;
+  hi = ((uint64_t)h1 << 32) | l1;
 }
-// An all-reduce with a commutative combine on floats or doubles.
+template <int kSpan>
+__device__ __forceinline__ void both(float v, float& lo, float& hi) {
+  uint32_t a, b;
+  both<kSpan>(__float_as_uint(v), a, b);
+  lo = __uint_as_float(a);
+  hi = __uint_as_float(b);
+}
+template <int kSpan>
+__device__ __forceinline__ void both(double v, double& lo, double& hi) {
+  uint64_t a, b;
+  both<kSpan>((uint64_t)__double_as_longlong(v), a, b);
+  lo = __longlong_as_double((long long)a);
+  hi = __longlong_as_double((long long)b);
+}
+// An all-reduce with a commutative combine (binary32, binary64, 32- or 64-bit unsigned).
 template <class T, class Op>
 __device__ __forceinline__ T all_reduce(T v, Op op) {
   v = op(v, dpp<kXor1>(v));
@@ -112,18 +128,21 @@ __device__ __forceinline__ T all_reduce(T v, Op op) {
   v = op(v, dpp<kHalfMirror>(v));
   v = op(v, dpp<kMirror>(v));
   T lo, hi;
-  if constexpr (sizeof(T) == 4) {
-    uint32_t a, b;
-    both<16>(__float_as_uint(v), a, b);
-    v = op(__uint_as_float(a), __uint_as_float(b));
-    both<32>(__float_as_uint(v), a, b);
-    return op(__uint_as_float(a), __uint_as_float(b));
-  } else {
-    both<16>(v, lo, hi);
-    v = op(lo, hi);
-    both<32>(v, lo, hi);
-    return op(lo, hi);
-  }
+  both<16>(v, lo, hi);
+  v = op(lo, hi);
+  both<32>(v, lo, hi);
+  return op(lo, hi);
+}
+// Inclusive prefix sum in lane order.
+template <class T>
+__device__ __forceinline__ T inclusive_scan(T v) {
+  v += dpp<kRowShr + 1>(v);
+  v += dpp<kRowShr + 2>(v);
+  v += dpp<kRowShr + 4>(v);
+  v += dpp<kRowShr + 8>(v);
+  v += dpp<kBcast15, 0xa>(v);
+  v += dpp<kBcast31, 0xc>(v);
+  return v;
 }
 }  // namespace wave_detail
 
@@ -167,15 +186,37 @@ __device__ __forceinline__ void wave_argmax(float& v, int32_t& idx) {
 
 // Exclusive prefix sum over the wave (lane order), fp64: the inclusive scan less the lane's value.
 __device__ __forceinline__ double wave_exclusive_scan(double v, int) {
-  using namespace wave_detail;
-  double incl = v;
-  incl += dpp<kRowShr + 1>(incl);
-  incl += dpp<kRowShr + 2>(incl);
-  incl += dpp<kRowShr + 4>(incl);
-  incl += dpp<kRowShr + 8>(incl);
-  incl += dpp<kBcast15, 0xa>(incl);
-  incl += dpp<kBcast31, 0xc>(incl);
-  return incl - v;
+  return wave_detail::inclusive_scan(v) - v;
+}
+
+// Inclusive prefix sums over the wave (lane order) of 32- and 64-bit unsigned integers.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) { return wave_detail::inclusive_scan(v); }
+__device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t v) { return wave_detail::inclusive_scan(v); }
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return wave_detail::all_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  return wave_detail::all_reduce(v, [](uint64_t a, uint64_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_detail::all_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
+// The value of lane src (the same index in every lane) in every lane.
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+}
+__device__ __forceinline__ int32_t lane_value(int32_t v, int src) { return __builtin_amdgcn_readlane(v, src); }
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+__device__ __forceinline__ uint64_t lane_value(uint64_t v, int src) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), src) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+}
+__device__ __forceinline__ double lane_value(double v, int src) {
+  return __longlong_as_double((long long)lane_value((uint64_t)__double_as_longlong(v), src));
 }
 
 // Sum of the eight (or four) elements of one vector as a balanced tree.
