@@ -210,6 +210,8 @@ template <class E, bool kCount>
 __device__ __forceinline__ float exp_sum(u32x4 (&buf)[kVecPerLane], float k2, float ref, float t, uint32_t hm,
                                          uint32_t* h) {
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t one = 1u;
+  if constexpr (kCount) asm volatile("" : "+v"(one));  // held in a register, not rematerialized per add
 #pragma unroll
   for (int k = 0; k < kVecPerLane; ++k) {
     // re-unpack from the raw words rather than keep every unpacked element live across the max
@@ -219,7 +221,7 @@ __device__ __forceinline__ float exp_sum(u32x4 (&buf)[kVecPerLane], float k2, fl
     if constexpr (kCount) {
 #pragma unroll
       for (int e = 0; e < E::kPerVec; ++e)
-        if (f[e] >= t) atomicAdd(&h[hm - (__float_as_uint(f[e]) >> 16)], 1u);
+        if (f[e] >= t) atomicAdd(&h[hm - (__float_as_uint(f[e]) >> 16)], one);
     }
 #pragma unroll
     for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
