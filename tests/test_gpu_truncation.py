@@ -123,7 +123,7 @@ def _profiles(B, V, rng):
     return top_k, milli
 
 
-@pytest.mark.parametrize("dtype,V", [("bf16", 32000), ("fp32", 4099), ("bf16", 1000)])
+@pytest.mark.parametrize("dtype,V", [("bf16", 32000), ("fp32", 4099), ("bf16", 1000), ("bf16", 1001)])
 def test_mixed_profiles_match_oracle(dtype, V):
     rng = np.random.default_rng(V)
     base = W.make_random(f"trunc_{dtype}_{V}", rng.integers(0, 9, size=64), V, dtype, 1.0, 3.0,
@@ -335,3 +335,24 @@ def test_row_pass_counts_and_their_fallbacks():
     b.tokens = drafter_tokens(b, top_k, milli, rng)
     acc, out, got, ref = check(b, top_k, milli)
     assert (acc >= 0).all()
+
+
+def test_wide_rows_span_several_batches_of_chunks():
+    """bf16 rows of 74 chunks (V = 600,000): the count kernel sums and scans chunk counts in batches
+    of 64 chunks, and the full cut kernel's window pass has no per-chunk window counts (more than 32
+    chunks), so its rows take the chunk pass.  Top-k values put cuts inside and below the counted
+    binade."""
+    rng = np.random.default_rng(83)
+    B, V = 6, 600000
+    depths = np.array([2, 1, 0, 2, 1, 2])
+    cu = W.offsets_from_depths(depths)
+    n_d = int(cu[-1])
+    tgt = (rng.standard_normal((n_d + B, V)) * 3).astype(np.float32)
+    t_of_d = np.concatenate([np.arange(cu[i], cu[i + 1]) + i for i in range(B)])
+    drf = (tgt[t_of_d] + rng.standard_normal((n_d, V)) * 0.7).astype(np.float32)
+    b = W.Batch(name="wide", V=V, dtype="bf16", temperature=1.0, seed=31, target=W.bf16_bits(tgt),
+                draft=W.bf16_bits(drf), tokens=np.zeros(n_d, dtype=np.int32), cu=cu)
+    top_k = np.array([50, 0, 300, 5000, 1, 0], dtype=np.int32)
+    milli = np.array([900, 950, 1000, 990, 1000, 500], dtype=np.int32)
+    b.tokens = drafter_tokens(b, top_k, milli, rng)
+    check(b, top_k, milli)
