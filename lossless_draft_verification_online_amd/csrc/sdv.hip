@@ -725,15 +725,15 @@ struct Quad<F32> {
 };
 
 // Residual chunk masses of a (target row, q row) pair by the waves of one workgroup (16-byte
-// aligned rows).  Wave w takes full chunks w, w + n_waves, ... in halves of 4-element quads
-// (quad l + 64 k for lane l): the loads of the next half are issued before the current one is
+// aligned rows).  Wave w takes full chunks w, w + n_waves, ... in quarters of 4-element quads
+// (quad l + 64 k for lane l): the loads of the next quarter are issued before the current one is
 // reduced.  The partial last chunk, if any, is summed element by element by the wave that owns it.
 template <class E, class M>
 __device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const float* qp, int32_t V, int32_t C,
                                                float k2, float ref_t, float q_scale, double* lds_mass, int lane,
                                                int wave, int n_waves) {
   typedef typename Quad<E>::T TQ;
-  constexpr int kParts = 2;                               // stages per chunk
+  constexpr int kParts = 4;                               // stages per chunk
   constexpr int kQuadsPerLane = E::kChunk / 4 / kWave;    // 32 (bf16) or 16 (fp32)
   constexpr int kPart = kQuadsPerLane / kParts;           // quads per lane in one stage
   struct Stage {
@@ -777,6 +777,12 @@ __device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const
   const int32_t steps = kParts * n_mine;  // even: steps come in pairs
   Stage A, Bs;
   double acc = 0.0;
+  // the loads just issued come before the reduction of the stage held: its registers pass through
+  // an empty asm placed after them, so the reduction cannot be scheduled above those loads
+  auto pin = [&](Stage& st) {
+#pragma unroll
+    for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.t[k]), "+v"(st.q[k])::"memory");
+  };
   auto finish_chunk = [&](int32_t s) {  // after stage s: the chunk is complete when s ends a chunk
     if ((s + 1) % kParts == 0) {
       acc = wave_sum(acc);
@@ -791,18 +797,18 @@ __device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const
     int32_t s = 0;
     for (; s + 2 < steps; s += 2) {
       load(s + 1, Bs);
-      asm volatile("" ::: "memory");  // the next stage is in flight while this one is reduced
+      pin(A);  // the next stage is in flight while this one is reduced
       acc += reduce(A, s);
       asm volatile("" : "+v"(acc)::"memory");
       finish_chunk(s);
       load(s + 2, A);
-      asm volatile("" ::: "memory");
+      pin(Bs);
       acc += reduce(Bs, s + 1);
       asm volatile("" : "+v"(acc)::"memory");
       finish_chunk(s + 1);
     }
     load(s + 1, Bs);
-    asm volatile("" ::: "memory");
+    pin(A);
     acc += reduce(A, s);
     asm volatile("" : "+v"(acc)::"memory");
     finish_chunk(s);
