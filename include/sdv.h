@@ -47,7 +47,7 @@ typedef enum {
   SDV_OK = 0,
   SDV_ERR_INVALID_ARG = -1, /* a required pointer is NULL, or a size / temperature is out of range */
   SDV_ERR_UNSUPPORTED = -2, /* dtype not one of sdv_dtype */
-  SDV_ERR_LIMIT = -3,       /* the batch exceeds an index or launch-size limit of this build */
+  SDV_ERR_LIMIT = -3,       /* the batch exceeds an index or launch-size limit of the library */
   SDV_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than sdv_workspace_bytes() */
   SDV_ERR_HIP = -5          /* a kernel launch failed; the stream state is as HIP reports it */
 } sdv_status;
