@@ -78,16 +78,31 @@ __device__ __forceinline__ bool kept_by(const Cut c, float z, int32_t v) {
   return z > c.kappa || (z == c.kappa && v <= c.vcut);
 }
 
+// The smallest binary32 value above kappa (NaN above +inf, so that nothing lies above it): z > kappa
+// iff z >= above(kappa) for every z.
+__device__ __forceinline__ float above(float kappa) {
+  const uint32_t b = __float_as_uint(kappa);
+  if (kappa == INFINITY) return __builtin_nanf("");
+  if ((b & 0x7fffffffu) == 0u) return __uint_as_float(1u);  // +-0: the smallest subnormal
+  return __uint_as_float((b & 0x80000000u) ? b - 1u : b + 1u);
+}
+
 // The tokens the rows of a terminal draw keep: NoCut keeps every token (its tests fold away),
-// RowCuts holds the cuts of the target row (t) and of the draft row (d).
+// RowCuts holds the cuts of the target row (t) and of the draft row (d), each as a threshold on the
+// logit that depends on the token id: kappa up to vcut, the next value above kappa after it (the
+// same test as kept_by, one compare on the logit and one on the id).
 struct NoCut {
   __device__ __forceinline__ bool t(float, int32_t) const { return true; }
   __device__ __forceinline__ bool d(float, int32_t) const { return true; }
 };
 struct RowCuts {
   Cut ct, cd;
-  __device__ __forceinline__ bool t(float z, int32_t v) const { return kept_by(ct, z, v); }
-  __device__ __forceinline__ bool d(float z, int32_t v) const { return kept_by(cd, z, v); }
+  float t_up, d_up;
+  __device__ __forceinline__ RowCuts() : ct{-INFINITY, INT32_MAX}, cd{-INFINITY, INT32_MAX}, t_up(-INFINITY), d_up(-INFINITY) {}
+  __device__ __forceinline__ RowCuts(Cut t_cut, Cut d_cut)
+      : ct(t_cut), cd(d_cut), t_up(above(t_cut.kappa)), d_up(above(d_cut.kappa)) {}
+  __device__ __forceinline__ bool t(float z, int32_t v) const { return z >= (v <= ct.vcut ? ct.kappa : t_up); }
+  __device__ __forceinline__ bool d(float z, int32_t v) const { return z >= (v <= cd.vcut ? cd.kappa : d_up); }
 };
 
 struct Params {
