@@ -2,13 +2,15 @@
 //
 // The step verifies every request of a ragged batch at once (SDCP "Verification and Commit",
 // steps 5 to 7; Rule 1 and Rule 2 of its section "Acceptance Rules"; the r <= p/q test of
-// "SOTA-227", section "What to do").  Two kernels run on the caller's stream:
+// "SOTA-227", section "What to do").  Two kernels run on the caller's stream (two more between
+// them when a call carries top-k / top-p, section 2):
 //
 //  row_records   The stream.  One wave64 per 16 KiB chunk of every logit row reads the chunk once
 //                with 16-byte loads.  At T > 0 it records the chunk's exponent reference
 //                ref = fl(max z * k) and s = sum 2^(z k - ref), k = log2(e)/T; at T = 0 the chunk's
 //                maximum and the smallest index reaching it.  Waves never wait on each other, so
-//                nothing interrupts the stream.
+//                nothing interrupts the stream.  In a top-k / top-p call on bf16 rows it also counts
+//                the logits of the 128 keys at and below each chunk's maximum.
 //  verdicts      One workgroup of 8 waves per request.  The waves fold the request's rows from
 //                their chunk records (fp64, lanes over chunks) into shared memory; wave 0 gathers the
 //                target and draft logits at each draft token, forms p/q, draws r from Philox
@@ -922,25 +924,26 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
 
 // ============================================================================ 2. truncation
 // SDCP ("Speculative Decoding Coordination Protocol (SDCP)", section "Session Contract") defines p
-// as the model's distribution after temperature, then top-k, then top-p.  One workgroup per logit
-// row finds the row's cut: the value of the last kept rank and how many of its copies are kept
-// (ranks that tie on a logit differ only in token id).  Both follow from a histogram over an
-// order-preserving key of the logits.
+// as the model's distribution after temperature, then top-k, then top-p.  Each logit row gets its
+// cut: the value of the last kept rank and how many of its copies are kept (ranks that tie on a
+// logit differ only in token id).  Both follow from counts over an order-preserving key of the
+// logits: every copy of a key has the same mass, so counts give masses.
 //
-//  bf16 rows     one pass counts the logits of each of the 4096 keys below the row maximum's (the
-//                chunk records give the maximum); every copy of a key has the same mass, so counts
-//                alone give masses.  Logits below that window are only counted.  Profiles that cut
-//                inside the window (the cut of top-k / top-p lies among the largest logits) are
-//                settled from these counts;
-//  other cases   an exact radix select: per digit level, counts and fixed-point masses of the
-//                logits that share the higher digits, and the level's scan picks the digit
-//                holding the top_k-th rank (top-k) or where the running mass reaches the nucleus
-//                mass (top-p).
+//  row_cuts_counted  bf16 rows of 16-byte length: the row pass has counted, per chunk, the 128 keys
+//                    at and below the chunk maximum's (section 1); one wave per row sums them into
+//                    the row's top 128 keys and settles the cut when it lands there.  Other rows go
+//                    on a list for row_cuts.
+//  row_cuts          one workgroup per row (or per listed row): bf16 rows count the 4096 keys below
+//                    the row maximum's in one pass and settle cuts that land there; everything else
+//                    goes through an exact radix select: per digit level, counts and fixed-point
+//                    masses of the logits that share the higher digits, and the level's scan picks
+//                    the digit holding the top_k-th rank (top-k) or where the running mass reaches
+//                    the nucleus mass (top-p).
 //
 // Masses are 2^(z k - R) as fixed-point integers (R = fl(max z * k)): integer sums do not depend on
-// the order of the atomic adds, so the cut is the same on every run.  A last pass over the row
-// finds the token id of the last kept copy and rewrites each chunk record's mass to the mass of
-// the chunk's kept tokens, so the verdict kernel's fold yields the truncated normaliser unchanged.
+// the order of the atomic adds, so the cut is the same on every run.  The last steps (finish_cut)
+// find the token id of the last kept copy and rewrite each chunk record's mass to the mass of the
+// chunk's kept tokens, so the verdict kernel's fold yields the truncated normaliser unchanged.
 
 constexpr int kCutWaves = 8;
 constexpr int kCutThreads = kWave * kCutWaves;  // several workgroups per CU: rows overlap
