@@ -168,6 +168,24 @@ __device__ __forceinline__ int32_t request_of_row(const int32_t* cu, int32_t B, 
   return lo;
 }
 
+// The same lookup by a whole wave (every lane active): lanes test 64 evenly spaced requests, and
+// the last one whose first row is at or before row narrows the range to one lane's share; the
+// first rows are non-decreasing in i, so the lanes that pass form a prefix.
+__device__ __forceinline__ int32_t request_of_row_wave(const int32_t* cu, int32_t B, int32_t row, bool target,
+                                                       int lane) {
+  int32_t lo = 0, span = B;  // the request lies in [lo, lo + span)
+  while (span > 1) {
+    const int32_t step = (span + kWave - 1) / kWave;
+    const int32_t i = lo + lane * step;
+    const bool at_or_before = i < lo + span && (int64_t)cu[i] + (target ? i : 0) <= row;
+    const uint64_t pass = __ballot(at_or_before);
+    const int32_t last = pass ? 63 - __clzll((long long)pass) : 0;
+    lo += last * step;
+    span = min(step, span - last * step);
+  }
+  return lo;
+}
+
 // ============================================================================ offsets
 
 // cu[0] = 0, non-decreasing, cu[B] = n_d.  Anything else rejects the whole batch.
@@ -1424,7 +1442,7 @@ __device__ __forceinline__ void chunk_pass(const char* rp, int32_t V, int32_t C,
   }
 }
 
-// The truncation profile of a row slot's request (SDCP "Session Contract").
+// The truncation profile of a row slot's request (SDCP "Session Contract"), by a whole wave.
 struct RowProfile {
   bool target;
   int32_t row, i;
@@ -1436,7 +1454,7 @@ __device__ __forceinline__ RowProfile row_profile(const Params& P, int32_t slot)
   RowProfile f;
   f.target = slot < P.n_t;
   f.row = f.target ? slot : slot - P.n_t;
-  f.i = request_of_row(P.cu, P.B, f.row, f.target);
+  f.i = request_of_row_wave(P.cu, P.B, f.row, f.target, (int)(threadIdx.x & (kWave - 1)));
   f.k2 = P.temp_each ? k2_of(temperature_of(P.temp_each, f.i)) : P.k2;
   f.top_k = P.top_k ? P.top_k[f.i] : 0;
   f.milli = P.top_p_milli ? P.top_p_milli[f.i] : 1000;
@@ -1700,7 +1718,7 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   const int j0 = 2 * lane;
   // the counts of keys top - j0 and top - j0 - 1 in chunks cb + q0 .. cb + q0 + kBatch - 1 of the
   // batch of 64 whose tops the lanes hold (mine), loaded before any is used
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   auto load_counts = [&](int32_t cb, int q0, int nc, uint32_t mine, uint32_t (&a)[kBatch], uint32_t (&b)[kBatch]) {
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
@@ -1714,18 +1732,18 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
       if (d + 1 >= 0 && d + 1 < kHistKeys) b[r] = hc[d + 1];
     }
   };
-  // summed over the chunks
+  // summed over the chunks; rows of at most kBatch chunks keep their counts for the chunk masses
   uint32_t n0 = 0u, n1 = 0u;
+  uint32_t a_held[kBatch], b_held[kBatch];
   for (int32_t cb = 0; cb < P.C; cb += kWave) {
     const uint32_t mine = cb + lane < P.C ? htop[cb + lane] : kNoCounts;
     const int nc = min(kWave, P.C - cb);
     for (int q0 = 0; q0 < nc; q0 += kBatch) {
-      uint32_t a[kBatch], b[kBatch];
-      load_counts(cb, q0, nc, mine, a, b);
+      load_counts(cb, q0, nc, mine, a_held, b_held);
 #pragma unroll
       for (int r = 0; r < kBatch; ++r) {
-        n0 += a[r];
-        n1 += b[r];
+        n0 += a_held[r];
+        n1 += b_held[r];
       }
     }
   }
@@ -1795,10 +1813,19 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
                            for (int q0 = 0; q0 < nc; q0 += kTr) {
                              // this lane's two keys in chunks cb + q0 .. cb + q0 + 15: row r of the
                              // transposed block holds chunk q0 + r, column l lane l's share
-#pragma unroll
-                             for (int h = 0; h < kTr; h += kBatch) {
+                             static_assert(kTr == kBatch, "one batch of counts per transposed block");
+                             {
+                               constexpr int h = 0;
                                uint32_t a[kBatch], b[kBatch];
-                               load_counts(cb, q0 + h, nc, mine, a, b);
+                               if (P.C <= kBatch) {  // the counts summed above, still in registers
+#pragma unroll
+                                 for (int r = 0; r < kBatch; ++r) {
+                                   a[r] = a_held[r];
+                                   b[r] = b_held[r];
+                                 }
+                               } else {
+                                 load_counts(cb, q0, nc, mine, a, b);
+                               }
 #pragma unroll
                                for (int r = 0; r < kBatch; ++r) {
                                  const int q = q0 + h + r;
