@@ -218,8 +218,9 @@ def main():
         return summarize_pmc(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         raise SystemExit("bench.py measures one GPU: the verification step is built and measured on a single "
-                         "MI355X; requests shard across GPUs with no exchange (see the design notes), and "
-                         "no multi-GPU figure is produced.")
+                         "MI355X. Requests are independent and would shard across GPUs by request with no "
+                         "exchange, each GPU running this same step on its share; no multi-GPU figure is "
+                         "produced.")
 
     import torch
 

@@ -31,7 +31,7 @@
  *    Out-of-range draft tokens and depths beyond 64 (SDCP "Session Contract", m_max <= 64) are
  *    rejected the same way.  A rejected request reports accepted_len = -1.
  *
- * Readings where the pages leave a step open (each one is listed in the design notes):
+ * Readings where the pages leave a step open:
  *  - uniforms: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
  *    1, 2, 3", SC'11) with key = (seed & 0xffffffff, seed >> 32) and counter =
  *    (position, request, 0, 0).  Word 0 feeds the accept test, word 1 the extra-token draw, which
