@@ -1972,8 +1972,10 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   const int n_waves = blockDim.x / kWave;
 
   // screening: every wave reaches the same answer from the same loads
+  // the request's offsets load beside the batch-wide screening (i < B: both are in bounds)
+  const int32_t lo_raw = P.cu[i], hi_raw = P.cu[i + 1];
   const bool ok_offsets = offsets_valid(P, lane);
-  const int32_t lo = ok_offsets ? P.cu[i] : 0, hi = ok_offsets ? P.cu[i + 1] : 0;
+  const int32_t lo = ok_offsets ? lo_raw : 0, hi = ok_offsets ? hi_raw : 0;
   const int K = hi - lo;
   const int32_t trow0 = lo + i, drow0 = lo;
   if (!ok_offsets || K > SDV_MAX_DEPTH) {  // malformed batch, or the depth limit: no slot written
