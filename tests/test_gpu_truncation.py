@@ -356,3 +356,34 @@ def test_wide_rows_span_several_batches_of_chunks():
     milli = np.array([900, 950, 1000, 990, 1000, 500], dtype=np.int32)
     b.tokens = drafter_tokens(b, top_k, milli, rng)
     check(b, top_k, milli)
+
+
+def test_truncated_repeat_launches_are_deterministic():
+    """The cuts rest on integer counts and fixed-point masses, and every reduction has a fixed
+    order, so repeated calls give bit-identical outputs, kept counts and truncated LSEs: rows that
+    the count kernel settles and rows it leaves to the full cut kernel alike."""
+    rng = np.random.default_rng(89)
+    B, V, K = 24, 3 * 8192 + 1000, 2
+    kinds = np.arange(B) % 6
+    cu = W.offsets_from_depths(np.full(B, K))
+    n_d = B * K
+    tgt = np.stack([_counted_row(kinds[r // (K + 1)], V, rng) for r in range(n_d + B)])
+    drf = np.stack([_counted_row(kinds[d // K], V, rng) for d in range(n_d)])
+    b = W.Batch(name="repeat_cuts", V=V, dtype="bf16", temperature=0.8, seed=17, target=W.bf16_bits(tgt),
+                draft=W.bf16_bits(drf), tokens=np.zeros(n_d, dtype=np.int32), cu=cu)
+    top_k = np.array([[50, 0, 50, 5, 385, 0][k] for k in kinds], dtype=np.int32)
+    milli = np.array([[900, 900, 950, 1000, 990, 900][k] for k in kinds], dtype=np.int32)
+    b.tokens = drafter_tokens(b, top_k, milli, rng)
+    ins = (to_device(b.target, b.dtype), to_device(b.draft, b.dtype), torch.from_numpy(b.tokens).to(DEV),
+           torch.from_numpy(b.cu).to(DEV))
+    kw = {"top_k": torch.from_numpy(top_k).to(DEV), "top_p_milli": torch.from_numpy(milli).to(DEV)}
+    diag = ("kept_tokens", "target_lse", "ratio")
+    runs = []
+    for _ in range(12):
+        acc, out, extra = sdv.verify_ex(*ins, b.temperature, b.seed, diag=diag, **kw)
+        torch.cuda.synchronize()
+        runs.append((acc.cpu().numpy(), out.cpu().numpy(), {k: v.cpu().numpy() for k, v in extra.items()}))
+    for acc, out, extra in runs[1:]:
+        assert np.array_equal(acc, runs[0][0]) and np.array_equal(out, runs[0][1])
+        for k in diag:
+            assert np.array_equal(extra[k], runs[0][2][k], equal_nan=True), k
