@@ -763,6 +763,8 @@ struct Quad<F32> {
 // aligned rows).  Wave w takes full chunks w, w + n_waves, ... in quarters of 4-element quads
 // (quad l + 64 k for lane l): the loads of the next quarter are issued before the current one is
 // reduced.  The partial last chunk, if any, is summed element by element by the wave that owns it.
+// q loads are non-temporal; target loads are plain, since non-temporal ones here slow the row pass
+// of the next call.
 template <class E, class M>
 __device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const float* qp, int32_t V, int32_t C,
                                                float k2, float ref_t, float q_scale, double* lds_mass, int lane,
@@ -786,7 +788,7 @@ __device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const
     for (int k = 0; k < kPart; ++k) {
       const int u = lane + kWave * (h * kPart + k);
       st.t[k] = tv[u];
-      st.q[k] = qv[u];
+      st.q[k] = __builtin_nontemporal_load(qv + u);  // q rows never enter the row pass
     }
   };
   auto reduce = [&](const Stage& st, int32_t s) {
