@@ -52,9 +52,10 @@ constexpr int32_t kMaxChunks = 4096;  // chunks per row: the verdict and cut ker
 // Truncating bf16 calls: the row pass also counts, per chunk, the logits of each of the kHistKeys
 // 16-bit order keys at and below the chunk maximum's (one binade of positive logits), so that a cut
 // among the largest logits needs no second read of the row.  The chunk's top key carries kNoCounts
-// when its window would reach zero or -inf (then no counts are written).
+// when its window would reach zero or -inf (then its counts are all zero).
 constexpr int kHistKeys = 128;
 constexpr uint32_t kNoCounts = 0x10000u;
+constexpr uint32_t kCountNothing = 0x40000000u;  // a stand-in maximum more than kHistKeys + 63 above every 16-bit pattern
 
 // Order keys of bf16 logits: a larger logit has a larger key and -0 shares the key of +0.
 // The 16-bit key of a bf16 logit (its raw bits h), and the 32-bit key of a 16-bit one: below the
@@ -237,13 +238,15 @@ __device__ __forceinline__ float chunk_max(u32x4 (&buf)[kVecPerLane]) {
   return wave_max(m);
 }
 
-// sum 2^(z k - ref) over a loaded chunk.  kCount (bf16 rows with a positive maximum) also counts
-// into the wave's counters h every logit z >= t, at hm - bits(z), hm the maximum's raw bits: bf16
-// logits are exact in binary32, so z >= t holds for exactly the kHistKeys keys at and below the
-// maximum's when t is the logit of the lowest of them (t = NaN counts nothing).
+// sum 2^(z k - ref) over a loaded chunk.  kCount (bf16 only) also counts every logit into the
+// wave's counters h: at d = hm - bits(z) (raw bf16 bits, unsigned arithmetic) when d < kHistKeys,
+// else at the lane's spare counter `spare` (kHistKeys + lane, never read).  For a positive hm that
+// selects exactly the kHistKeys keys at and below hm; negative logits, -0, the -inf padding and
+// NaN wrap to a large d.  hm = kCountNothing sends every logit to the spare counter.  Every logit
+// takes the same unmasked shared-memory add: no compare, no exec-mask change per logit.
 template <class E, bool kCount>
-__device__ __forceinline__ float exp_sum(u32x4 (&buf)[kVecPerLane], float k2, float ref, float t, uint32_t hm,
-                                         uint32_t* h) {
+__device__ __forceinline__ float exp_sum(u32x4 (&buf)[kVecPerLane], float k2, float ref, uint32_t hm,
+                                         uint32_t spare, uint32_t* h) {
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   uint32_t one = 1u;
   if constexpr (kCount) asm volatile("" : "+v"(one));  // held in a register, not rematerialized per add
@@ -251,13 +254,17 @@ __device__ __forceinline__ float exp_sum(u32x4 (&buf)[kVecPerLane], float k2, fl
   for (int k = 0; k < kVecPerLane; ++k) {
     // re-unpack from the raw words rather than keep every unpacked element live across the max
     asm volatile("" : "+v"(buf[k]));
+    if constexpr (kCount) {
+      const uint32_t wd[4] = {buf[k].x, buf[k].y, buf[k].z, buf[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t d_lo = hm - (wd[j] & 0xffffu), d_hi = hm - (wd[j] >> 16);
+        atomicAdd(&h[d_lo < spare ? d_lo : spare], one);
+        atomicAdd(&h[d_hi < spare ? d_hi : spare], one);
+      }
+    }
     float f[E::kPerVec];
     E::unpack(buf[k], f);
-    if constexpr (kCount) {
-#pragma unroll
-      for (int e = 0; e < E::kPerVec; ++e)
-        if (f[e] >= t) atomicAdd(&h[hm - (__float_as_uint(f[e]) >> 16)], one);
-    }
 #pragma unroll
     for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
     acc[k & 3] += tree_sum(f);
@@ -290,7 +297,7 @@ __device__ __forceinline__ float2 record_of(u32x4 (&buf)[kVecPerLane], int32_t c
     const float m = chunk_max<E>(buf);
     if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
     const float ref = m * k2;
-    return make_float2(ref, exp_sum<E, false>(buf, k2, ref, 0.0f, 0u, nullptr));
+    return make_float2(ref, exp_sum<E, false>(buf, k2, ref, 0u, 0u, nullptr));
   }
 }
 
@@ -331,8 +338,8 @@ __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32
 // The record of a loaded bf16 chunk at T > 0, and the counts of the kHistKeys keys at and below its
 // maximum's: out[j / 2] holds the counts of keys kmax - j (low half) and kmax - j - 1 (high half),
 // top = kmax.  Only a positive maximum whose window stays above +0 is counted; other chunks (a
-// maximum <= 0 or within kHistKeys steps of +0) carry top | kNoCounts.  h: the wave's kHistKeys
-// counters in shared memory.
+// maximum <= 0 or within kHistKeys steps of +0) carry top | kNoCounts and zero counts.  h: the
+// wave's kHistKeys counters and kWave spare counters in shared memory.
 __device__ __forceinline__ float2 record_counting(u32x4 (&buf)[kVecPerLane], float k2, int lane, uint32_t* h,
                                                   uint32_t* out, uint32_t* top) {
   const float m = chunk_max<Bf16>(buf);
@@ -345,8 +352,7 @@ __device__ __forceinline__ float2 record_counting(u32x4 (&buf)[kVecPerLane], flo
   h[2 * lane] = 0u;
   h[2 * lane + 1] = 0u;
   __builtin_amdgcn_wave_barrier();  // a wave's shared-memory operations complete in order
-  const float t = counts ? __uint_as_float((hm - (uint32_t)(kHistKeys - 1)) << 16) : __builtin_nanf("");
-  const float s = exp_sum<Bf16, true>(buf, k2, ref, t, hm, h);
+  const float s = exp_sum<Bf16, true>(buf, k2, ref, counts ? hm : kCountNothing, kHistKeys + lane, h);
   __builtin_amdgcn_wave_barrier();
   out[lane] = h[2 * lane] | (h[2 * lane + 1] << 16);  // a chunk holds at most 8192 logits
   return make_float2(ref, s);
@@ -522,7 +528,7 @@ template <class E, int kMode, bool kVec, bool kHist>
 __global__ __launch_bounds__(256) void row_records(Params P) {
   static_assert(!kHist || (E::kBytes == 2 && kVec && kMode != kModeGreedy), "counts: bf16 sampling, 16-byte rows");
   static_assert(kHistKeys == 2 * kWave, "each lane writes one word of two counts");
-  __shared__ uint32_t hcnt[kHist ? 4 : 1][kHist ? kHistKeys : 1];
+  __shared__ uint32_t hcnt[kHist ? 4 : 1][kHist ? kHistKeys + kWave : 1];  // counters, then spares
   const int lane = threadIdx.x & (kWave - 1);
   // the unit is wave-uniform; saying so lets the request lookup use scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
