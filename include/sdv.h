@@ -95,7 +95,8 @@ typedef struct sdv_diag {
  * The workspace needs no initialisation and holds nothing between calls.  It holds 8 bytes per
  * chunk of every logit row (16 KiB of logits) and 8 bytes per row; bf16 batches add 260 bytes per
  * chunk, where the row pass of a top-k / top-p call counts the logits just below each chunk's
- * maximum, and 4 bytes per row.
+ * maximum, and 4 bytes per row.  Each request adds 8 bytes per chunk of a row and 4 bytes, where
+ * the verdict workgroups that share a correction publish its residual masses.
  */
 size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype);
 
@@ -207,6 +208,12 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
  *                     the request before any uniform is used (SDCP "Verification and Commit", step
  *                     5).  The row pass then streams target rows only; q is read at the proposed
  *                     tokens and, for a correction, over the rejected position's row.
+ *  verdict_split      workgroups per request in the verdict pass (0: chosen from B and V; values
+ *                     above the number of 16 KiB chunks per row count as that number; negative ->
+ *                     SDV_ERR_INVALID_ARG).  The workgroups of a request share a correction's pass
+ *                     over the rejected position's rows; every chunk's residual mass is computed
+ *                     the same way whichever workgroup computes it, so no output depends on the
+ *                     value.  A performance setting, not part of the method.
  *
  * Emission (SDCP section "Verification and Commit", step 7; "M7.8 - Speculative Serving", section
  * 0x09, "EOS and length-limit stopping"): of the a_i + 1 candidate tokens (the accepted drafts,
@@ -229,6 +236,7 @@ typedef struct sdv_options {
   const int32_t* top_k;
   const int32_t* top_p_milli;
   int32_t* kept_tokens;
+  int32_t verdict_split;
 } sdv_options;
 
 /*

@@ -48,6 +48,7 @@ class SdvOptions(ctypes.Structure):
         ("top_k", ctypes.c_void_p),
         ("top_p_milli", ctypes.c_void_p),
         ("kept_tokens", ctypes.c_void_p),
+        ("verdict_split", ctypes.c_int32),
     ]
 
 

@@ -27,6 +27,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -138,6 +139,9 @@ struct Params {
   uint32_t* hist;             // [row slots][C][kHistKeys / 2] per-chunk key counts, two 16-bit counts a word
   uint32_t* hist_top;         // [row slots][C] the chunk maximum's key, | kNoCounts without counts
   int32_t* pending;           // [1 + row slots] rows the count kernel leaves to row_cuts: count, then slots
+  int32_t split;              // verdict workgroups per request (split > 1: the residual pass is shared)
+  double* split_mass;         // [B][C] residual chunk masses published by the workgroups of a request
+  uint32_t* split_count;      // [B] workgroups of a request done with their masses (zeroed by the row pass)
   DiagPtrs dg;
 };
 
@@ -533,6 +537,8 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
   // the unit is wave-uniform; saying so lets the request lookup use scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
+  if (P.split > 1 && blockIdx.x == 0)  // the verdict workgroups of a request count up from zero
+    for (int32_t j = threadIdx.x; j < P.B; j += blockDim.x) P.split_count[j] = 0u;
   if (u >= P.n_units) return;
   const int32_t slot = (int32_t)(u / P.C);
   const int32_t c = (int32_t)(u - (int64_t)slot * P.C);
@@ -1969,7 +1975,9 @@ constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 // workgroup of 8 waves.  Shared memory: the folded rows, the decision, and the residual chunk masses
 // (C doubles, dynamic).  bad_profile rejects the request once its offsets have been screened.  With
 // kCut the rows' cuts (top-k / top-p) decide which tokens p and q keep; the chunk records already
-// hold the kept masses.
+// hold the kept masses.  With P.split workgroups per request (blockIdx.y = 0 .. split - 1) every
+// one reaches the same decision from the same loads; the first writes it, and a correction's
+// residual pass is shared among them (draw_terminal).
 template <class E, bool kGreedy, bool kVec, bool kQ, bool kCut>
 __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k2, uint64_t seed, bool bad_profile,
                                              double* lds_mass, RowFold* rows, Decision& dec) {
@@ -1978,6 +1986,10 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   // depends on it a scalar branch (a lane-predicated load would force a wait for all loads in flight)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n_waves = blockDim.x / kWave;
+  const bool lead = blockIdx.y == 0;  // the workgroup that writes the decision
+  if constexpr (kGreedy) {
+    if (!lead) return;  // nothing to share
+  }
 
   // screening: every wave reaches the same answer from the same loads
   // the request's offsets load beside the batch-wide screening (i < B: both are in bounds)
@@ -1987,11 +1999,11 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   const int K = hi - lo;
   const int32_t trow0 = lo + i, drow0 = lo;
   if (!ok_offsets || K > SDV_MAX_DEPTH) {  // malformed batch, or the depth limit: no slot written
-    if (wave == 0) write_reject(P, i, 0, 0, false, lane);
+    if (wave == 0 && lead) write_reject(P, i, 0, 0, false, lane);
     return;
   }
   if (bad_profile || !stop_list_valid(P, i)) {  // no profile, or no stop set: every slot is -1
-    if (wave == 0) write_reject(P, i, trow0, K, true, lane);
+    if (wave == 0 && lead) write_reject(P, i, trow0, K, true, lane);
     return;
   }
   const float2* rec_t = P.part + (int64_t)trow0 * P.C;
@@ -2042,7 +2054,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   if (wave == 0) {
     Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0, Cut{-INFINITY, INT32_MAX}, Cut{-INFINITY, INT32_MAX}};
     if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
-      write_reject(P, i, trow0, K, true, lane);
+      if (lead) write_reject(P, i, trow0, K, true, lane);
     } else if constexpr (kGreedy) {
       const int32_t g = lane <= K ? rows[lane].argmax : 0;
       const uint64_t miss = __ballot(active && x != g);
@@ -2087,26 +2099,28 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
         }
       }
       if (__ballot(qzero) != 0) {  // q(x) = 0 somewhere: rejected before any uniform is used
-        write_reject(P, i, trow0, K, true, lane);
+        if (lead) write_reject(P, i, trow0, K, true, lane);
       } else {
         const uint64_t rej = __ballot(active && !accept);
         const int a = rej ? __ffsll((unsigned long long)rej) - 1 : K;
         const int n_emit = emitted_count(P, i, x, a, lane);
         const bool frontier = n_emit == a + 1;
-        // slot a is written by the draw below when the extra token is emitted
-        for (int j = lane; j <= K; j += kWave)
-          if (j != a || !frontier) P.out_tokens[trow0 + j] = j < a && j < n_emit ? x : -1;
-        if (lane == 0) {
-          P.accepted_len[i] = a;
-          if (P.emitted_len) P.emitted_len[i] = n_emit;
-          if (!frontier && P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_NONE;
-        }
-        if (P.dg.target_lse)
-          for (int j = lane; j <= K; j += kWave) P.dg.target_lse[trow0 + j] = rows[j].l2 * kLn2;
-        if (active) {
-          if (P.dg.draft_lse && !kQ) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
-          if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
-          if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
+        if (lead) {
+          // slot a is written by the draw below when the extra token is emitted
+          for (int j = lane; j <= K; j += kWave)
+            if (j != a || !frontier) P.out_tokens[trow0 + j] = j < a && j < n_emit ? x : -1;
+          if (lane == 0) {
+            P.accepted_len[i] = a;
+            if (P.emitted_len) P.emitted_len[i] = n_emit;
+            if (!frontier && P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_NONE;
+          }
+          if (P.dg.target_lse)
+            for (int j = lane; j <= K; j += kWave) P.dg.target_lse[trow0 + j] = rows[j].l2 * kLn2;
+          if (active) {
+            if (P.dg.draft_lse && !kQ) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
+            if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
+            if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
+          }
         }
         d.a = a;
         if constexpr (kCut) {
@@ -2164,12 +2178,17 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   }
 }
 
-// The correction or bonus draw of a request (T > 0), by the verdict workgroup.
+// The correction or bonus draw of a request (T > 0), by the verdict workgroup.  With P.split
+// workgroups per request, workgroup s computes the residual masses of chunks [s C / split,
+// (s + 1) C / split) and publishes them; the last one to finish (a counter per request) reads the
+// others' and draws.  A bonus draw needs no residual pass: the first workgroup draws it alone.
 template <class E, bool kVec, bool kQ, bool kCut>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves) {
   if (d.kind != SDV_TERM_BONUS && d.kind != SDV_TERM_RESIDUAL) return;  // uniform over the workgroup
+  const int32_t n_split = gridDim.y, part = blockIdx.y;
+  if (d.kind == SDV_TERM_BONUS && part != 0) return;
   typedef typename std::conditional<kCut, RowCuts, NoCut>::type Mask;
   Mask m{};
   if constexpr (kCut) {  // uniform over the workgroup: scalar registers
@@ -2185,12 +2204,21 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const char* dp = residual && !kQ ? row_ptr<E>(P.draft, drow0 + d.a, P.V) : nullptr;
   const float* qp = residual && kQ ? P.qrows + (int64_t)(drow0 + d.a) * P.V : nullptr;
 
-  // residual masses of every chunk, into shared memory
+  // residual masses of this workgroup's chunks [c_lo, c_hi), into shared memory; the vector passes
+  // see the range as a row of its own (tokens from c_lo's first, masks shifted to match)
+  const int32_t c_lo = (int32_t)((int64_t)P.C * part / n_split), c_hi = (int32_t)((int64_t)P.C * (part + 1) / n_split);
+  const int32_t v_lo = c_lo * E::kChunk, V_r = min(P.V, c_hi * E::kChunk) - v_lo;
+  Mask m_r = m;
+  if constexpr (kCut) {
+    m_r.ct.vcut -= v_lo;
+    m_r.cd.vcut -= v_lo;
+  }
   if (residual && kQ) {
     if constexpr (kVec) {
-      resid_masses_q<E>(m, tp, qp, P.V, P.C, k2, d.ref_t, d.q_scale, lds_mass, lane, wave, n_waves);
+      resid_masses_q<E>(m_r, tp + (int64_t)v_lo * E::kBytes, qp + v_lo, V_r, c_hi - c_lo, k2, d.ref_t, d.q_scale,
+                        lds_mass + c_lo, lane, wave, n_waves);
     } else {
-      for (int32_t c = wave; c < P.C; c += n_waves) {
+      for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
         const int32_t c0 = c * E::kChunk, c1 = min(c0 + E::kChunk, P.V);
         double cm = 0.0;
         for (int32_t v = c0 + lane; v < c1; v += kWave)
@@ -2202,9 +2230,10 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     __syncthreads();
   } else if (residual) {
     if constexpr (kVec) {
-      resid_masses_pipelined<E>(m, tp, dp, P.V, P.C, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass, lane, wave, n_waves);
+      resid_masses_pipelined<E>(m_r, tp + (int64_t)v_lo * E::kBytes, dp + (int64_t)v_lo * E::kBytes, V_r,
+                                c_hi - c_lo, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + c_lo, lane, wave, n_waves);
     } else {
-      for (int32_t c = wave; c < P.C; c += n_waves) {
+      for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
         const int32_t c0 = c * E::kChunk;
         const double cm = resid_chunk_mass<E, false>(m, tp, dp, c0, min(E::kChunk, P.V - c0), k2, d.ref_t, d.e_hi,
                                                      d.q_scale, lane);
@@ -2212,6 +2241,28 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
       }
     }
     __syncthreads();
+  }
+  if (residual && n_split > 1) {
+    // publish this range; the workgroup whose increment completes the count takes every mass.
+    // Wave 0 alone stores, fences (device scope: the other workgroups may sit on other XCDs, whose
+    // L2s are not coherent with this one's) and counts; nothing waits on another workgroup.
+    __shared__ int32_t last;
+    if (wave == 0) {
+      double* pub = P.split_mass + (int64_t)i * P.C;
+      for (int32_t c = c_lo + lane; c < c_hi; c += kWave) pub[c] = lds_mass[c];
+      __threadfence();
+      uint32_t before = 0u;
+      if (lane == 0) before = atomicAdd(&P.split_count[i], 1u);
+      const bool is_last = lane_value(before, 0) == (uint32_t)(n_split - 1);
+      if (is_last) {
+        __threadfence();
+        for (int32_t c = lane; c < P.C; c += kWave)
+          if (c < c_lo || c >= c_hi) lds_mass[c] = pub[c];
+      }
+      if (lane == 0) last = is_last;
+    }
+    __syncthreads();
+    if (!last) return;
   }
   // every wave picks the same chunk from the same masses
   double S = 0.0;
@@ -2309,11 +2360,22 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
 struct Layout {
   int32_t C;
   int64_t n_t, slots;
-  size_t part, cuts, hist, hist_top, pending, total;  // hist, hist_top, pending: bf16 only (else 0 bytes)
+  size_t part, cuts, hist, hist_top, pending, split_mass, split_count, total;  // hist, hist_top, pending: bf16 only
 };
 
 constexpr size_t kAlign = 256;
 constexpr size_t kVerdictLdsBytes = 48 * 1024;  // dynamic shared memory of the verdict workgroup
+constexpr int64_t kComputeUnits = 256;          // MI355X
+
+// Verdict workgroups per request: a batch too small to occupy the compute units shares each
+// correction's residual pass among several, four chunks apiece.  A compute unit's vector memory
+// path bounds the pass, so spreading it over more units pays even with half of each workgroup's
+// waves idle; below four chunks the publication of the masses costs more than the pass saves.
+constexpr int32_t kSplitChunks = 4;
+inline int32_t verdict_split(int32_t B, int32_t C) {
+  const int64_t by_units = kComputeUnits / B, by_chunks = C / kSplitChunks;
+  return (int32_t)std::max<int64_t>(1, std::min(by_units, by_chunks));
+}
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Returns SDV_OK and fills the layout, or the status the shape violates.
@@ -2341,6 +2403,8 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   L->hist = take(counts * kHistKeys * sizeof(uint16_t));
   L->hist_top = take(counts * sizeof(uint32_t));
   L->pending = take(dtype == SDV_BF16 ? (size_t)(slots + 1) * sizeof(int32_t) : 0);
+  L->split_mass = take((size_t)B * C * sizeof(double));
+  L->split_count = take((size_t)B * sizeof(uint32_t));
   L->total = off;
   return SDV_OK;
 }
@@ -2356,6 +2420,8 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   // under any truncation, so it needs none); bf16 rows get per-chunk key counts from the row pass
   const bool cut = kMode != kModeGreedy && (P.top_k || P.top_p_milli);
   const dim3 units((unsigned)((P.n_units + 3) / 4));
+  // verdict workgroups per request (the row pass zeroes their counters)
+  P.split = kMode == kModeGreedy ? 1 : (P.split > 0 ? std::min(P.split, P.C) : verdict_split(P.B, P.C));
   record(0);
   if constexpr (E::kBytes == 2 && kVec && kMode != kModeGreedy) {
     if (!cut) P.hist = nullptr;
@@ -2391,7 +2457,7 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
   P.lds_records = want < room ? want : room;
   const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
-  const dim3 grid((unsigned)P.B), block(kWave * kVerdictWaves);
+  const dim3 grid((unsigned)P.B, (unsigned)P.split), block(kWave * kVerdictWaves);
   if constexpr (kMode != kModeGreedy) {  // the greedy rule never reads the draft side
     if (P.qrows) {
       if (cut) hipLaunchKernelGGL((verdicts<E, kMode, kVec, true, true>), grid, block, lds, stream, P);
@@ -2431,6 +2497,7 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   const float* temp_each = opt->temperature;
   const uint64_t* seed_each = opt->seed;
   if ((opt->accept_uniform == nullptr) != (opt->draw_uniform == nullptr)) return SDV_ERR_INVALID_ARG;
+  if (opt->verdict_split < 0) return SDV_ERR_INVALID_ARG;
   if (opt->stop_offsets && (opt->n_stop_tokens < 0 || (opt->n_stop_tokens > 0 && !opt->stop_tokens)))
     return SDV_ERR_INVALID_ARG;
   Layout L;
@@ -2491,6 +2558,9 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.hist = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist) : nullptr;
   P.hist_top = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist_top) : nullptr;
   P.pending = dtype == SDV_BF16 ? reinterpret_cast<int32_t*>(ws + L.pending) : nullptr;
+  P.split = opt->verdict_split;  // 0: chosen at launch
+  P.split_mass = reinterpret_cast<double*>(ws + L.split_mass);
+  P.split_count = reinterpret_cast<uint32_t*>(ws + L.split_count);
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};

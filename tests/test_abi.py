@@ -45,18 +45,20 @@ def test_abi_version_and_status_strings(lib):
 def test_workspace_bytes(lib):
     # row-pass records: 8 B per 16 KiB chunk of every target and draft row, then one 8-byte
     # top-k / top-p cut per row, then (bf16) 128 16-bit key counts and a 4-byte top key per chunk
-    # and a list of rows (a count, then one 4-byte slot per row), each array 256-byte aligned
+    # and a list of rows (a count, then one 4-byte slot per row), then one 8-byte residual mass per
+    # chunk of each request and a 4-byte counter per request, each array 256-byte aligned
     up = lambda n: -(-n // 256) * 256
     ws = lib.sdv_workspace_bytes(256, 1024, 128256, 0)
     chunks = (128256 + 8191) // 8192
     assert chunks == 16
     rows = 1280 + 1024
     assert ws == (up(rows * chunks * 8) + up(rows * 8) + up(rows * chunks * 256) + up(rows * chunks * 4)
-                  + up((rows + 1) * 4))
+                  + up((rows + 1) * 4) + up(256 * chunks * 8) + up(256 * 4))
     assert ws % 256 == 0
     # binary32 rows: 4096 logits per chunk, no key counts
     chunks32 = (128256 + 4095) // 4096
-    assert lib.sdv_workspace_bytes(256, 1024, 128256, 1) == up(rows * chunks32 * 8) + up(rows * 8)
+    assert lib.sdv_workspace_bytes(256, 1024, 128256, 1) == (up(rows * chunks32 * 8) + up(rows * 8)
+                                                              + up(256 * chunks32 * 8) + up(256 * 4))
     assert lib.sdv_workspace_bytes(0, 10, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, -1, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, 0, 10, 7) == 0
@@ -136,6 +138,7 @@ def test_opts_host_argument_checks(lib):
     assert call(temperature=FAKE) == -1              # temperatures without seeds
     assert call(stop_offsets=FAKE, n_stop_tokens=-1) == -1
     assert call(stop_offsets=FAKE, n_stop_tokens=3) == -1  # tokens missing
+    assert call(verdict_split=-1) == -1
     assert lib.sdv_verify_opts(FAKE, FAKE, FAKE, FAKE, 2, 8, 1000, 0, -1.0, 1, None, FAKE, FAKE, FAKE, need, None,
                                None) == -1
 
