@@ -13,8 +13,8 @@ one launch / its mean duration from HIP events recorded on the library's stream)
 a plain read of the same size with the row pass's loads, per-call percentiles, accepted-length
 statistics and the CPU oracle's rate on the host.
 
-  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1|ragged_b256_profiled|
-                              ragged_b256_qrows|ragged_b256_topk50_topp900]
+  python bench.py [--workload ragged_b256|greedy_b512|uniform_b64|small_b1|small_b1_v128256|
+                              ragged_b256_profiled|ragged_b256_qrows|ragged_b256_topk50_topp900]
                   [--steps K] [--warmup W]
 
 Profile summaries (rocprofv3 output -> text under profiles/):
@@ -69,6 +69,8 @@ def make_workload(name: str, set_index: int):
         return W.uniform_b64(data_seed=W.DATA_SEED_BASE + 3 + 1000 * set_index, verify_seed=3000)
     if name == "small_b1":
         return W.small_b1(set_index)
+    if name == "small_b1_v128256":
+        return W.small_b1_v128256(data_seed=W.DATA_SEED_BASE + 8 + 1000 * set_index, verify_seed=8000)
     if name == "ragged_b256_qrows":  # the draft side as distributions (SDCP q_rows), float32
         return W.with_qrows(W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000))
     if name == "ragged_b256_topk50_topp900":  # top-k 50, then top-p 0.9, on every request
@@ -197,7 +199,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1",
-                                                           "ragged_b256_profiled", "ragged_b256_qrows",
+                                                           "small_b1_v128256", "ragged_b256_profiled",
+                                                           "ragged_b256_qrows",
                                                            "ragged_b256_topk50_topp900"])
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through the timed steps (0: enough for 1 GB, at least 2, at most 32)")

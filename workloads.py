@@ -246,6 +246,13 @@ def exactness_batch(case: int, trial_block: int, B: int = 4096, K: int = 3, V: i
                  meta={"case": case, "trial_block": trial_block})
 
 
+def small_b1_v128256(data_seed: int = DATA_SEED_BASE + 8, verify_seed: int = 8000) -> Batch:
+    """B=1, K=4, V=128256, bf16: target ~ N(0, 3^2), draft = target + N(0, 1.5^2), T = 1 (one request
+    of the target workload's vocabulary: the latency of a lone session's round)."""
+    return make_random("b1_k4_v128256_bf16", [4], 128256, "bf16", 1.0, 3.0, 1.5, data_seed=data_seed,
+                       verify_seed=verify_seed)
+
+
 def uniform_b64(data_seed: int = DATA_SEED_BASE + 3, verify_seed: int = 3000) -> Batch:
     """B=64, K=5, V=32000, bf16: target ~ N(0, 3^2), draft = target + N(0, 1.5^2), T = 0.8."""
     return make_random("b64_k5_v32000_bf16", np.full(64, 5), 32000, "bf16", 0.8, 3.0, 1.5,
