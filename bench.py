@@ -53,9 +53,14 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernels' code: line comments and blank lines are left out, so a profile stays
+    valid across changes to comments alone (the sources hold no '//' inside a string literal)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        for line in open(os.path.join(ROOT, p), encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -18,11 +18,13 @@
 //                terminals come from the folded argmax.  A bonus is drawn from p at position K
 //                using the bonus row's chunk records and one chunk re-read; a correction needs the
 //                chunk masses of max(p - q, 0) on the rejected row pair, which the 8 waves compute
-//                into shared memory before wave 0 draws.
+//                into shared memory before wave 0 draws.  A batch too small to occupy the compute
+//                units gets several workgroups per request, which share that pass (section 3).
 //
-// Nothing is handed between workgroups inside a kernel: the kernel boundary orders the stream
-// before the verdicts.  No matrix cores are involved: nothing here is a contraction, and the
-// roofline is HBM bandwidth.
+// The kernel boundary orders the stream before the verdicts.  Inside a kernel only the verdict
+// workgroups of one request hand anything over: a correction's chunk masses, through the
+// workspace, behind a device-scope fence and a counter; no workgroup ever waits for another.  No
+// matrix cores are involved: nothing here is a contraction, and the roofline is HBM bandwidth.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -2156,9 +2158,10 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     draw_terminal<E, kVec, kQ, kCut>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
 }
 
-// One workgroup per request.  With a profile per request, the request's temperature selects the
-// rule at run time (uniformly over the workgroup).  A top-k below 0 or a top-p outside
-// [0, 1000] thousandths describes no profile: the request is rejected under either rule.
+// Workgroups (blockIdx.x, s), s < P.split, verify request blockIdx.x.  With a profile per request,
+// the request's temperature selects the rule at run time (uniformly over the workgroup).  A top-k
+// below 0 or a top-p outside [0, 1000] thousandths describes no profile: the request is rejected
+// under either rule.
 template <class E, int kMode, bool kVec, bool kQ, bool kCut>
 __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   extern __shared__ double lds_mass[];  // [C]
