@@ -94,3 +94,30 @@ def test_automatic_split_of_a_small_batch_matches_oracle():
     b = W.make_random("split_auto_b3", [4, 0, 7], 128256, "bf16", 1.0, 3.0, 1.5, data_seed=81, verify_seed=82)
     for seed in range(4):
         check_parity(b, seed=int(rng.integers(0, 2**62)))
+
+
+def test_split_counters_restart_every_call():
+    # one workspace, filled with 0xff bytes first, for calls of two shapes: the row pass of every
+    # call zeroes the counters, so stale or garbage counts never decide which workgroup draws
+    rng = np.random.default_rng(9)
+    b1 = W.make_random("split_ws_a", [4, 7, 2], 65536, "bf16", 1.0, 3.0, 1.5, data_seed=91, verify_seed=92)
+    b2 = W.make_random("split_ws_b", rng.integers(1, 9, size=5), 98304, "bf16", 1.0, 3.0, 1.5, data_seed=93,
+                       verify_seed=94)
+    need = max(int(sdv._native.lib().sdv_workspace_bytes(b.B, b.n_draft_rows, b.V, 0)) for b in (b1, b2))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
+    inputs = {b.name: upload(b) for b in (b1, b2)}
+    fresh = {b.name: _run(b, 1, inputs[b.name]) for b in (b1, b2)}
+
+    def shared(b, split):
+        t, d, x, cu = inputs[b.name]
+        acc, out, dg = sdv.verify_ex(t, d, x, cu, b.temperature, b.seed, diag=DIAG, verdict_split=split, workspace=ws)
+        torch.cuda.synchronize()
+        return acc.cpu().numpy(), out.cpu().numpy(), {k: v.cpu().numpy() for k, v in dg.items()}
+    for b, split in [(b1, 8), (b2, 3), (b1, 2), (b2, 12), (b1, 8)]:
+        got, ref = shared(b, split), fresh[b.name]
+        np.testing.assert_array_equal(got[0], ref[0])
+        np.testing.assert_array_equal(got[1], ref[1])
+        for k in DIAG:
+            np.testing.assert_array_equal(got[2][k], ref[2][k])
+    log(f"  shared workspace: {need} bytes, {int((fresh[b1.name][2]['terminal_kind'] == 2).sum())} + "
+        f"{int((fresh[b2.name][2]['terminal_kind'] == 2).sum())} corrections")
