@@ -66,11 +66,13 @@ def test_split_outputs_are_bit_identical(V, dtype):
     _same_for_every_split(b, sorted({2, 3, C - 1, C, C + 5}))
 
 
-def test_split_with_q_rows():
+@pytest.mark.parametrize("V,dtype", [(65536, "bf16"), (65537, "bf16"), (40000, "fp32")])
+def test_split_with_q_rows(V, dtype):
     rng = np.random.default_rng(5)
-    b = W.with_qrows(W.make_random("split_q", rng.integers(0, 9, size=40), 65536, "bf16", 0.9, 3.0, 1.5,
+    b = W.with_qrows(W.make_random(f"split_q_{dtype}_{V}", rng.integers(0, 9, size=40), V, dtype, 0.9, 3.0, 1.5,
                                    data_seed=51, verify_seed=52))
-    _same_for_every_split(b, [2, 3, 8])
+    C = -(-V // (8192 if dtype == "bf16" else 4096))
+    _same_for_every_split(b, sorted({2, 3, C}))
 
 
 def test_split_with_top_k_top_p():
