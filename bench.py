@@ -64,6 +64,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+WORKLOADS = ["ragged_b256", "greedy_b512", "uniform_b64", "small_b1", "small_b1_v128256", "ragged_b256_profiled",
+             "ragged_b256_qrows", "ragged_b256_topk50_topp900"]
+
+
 def make_workload(name: str, set_index: int):
     import workloads as W
     if name == "ragged_b256":
@@ -203,10 +207,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="ragged_b256", choices=["ragged_b256", "greedy_b512", "uniform_b64", "small_b1",
-                                                           "small_b1_v128256", "ragged_b256_profiled",
-                                                           "ragged_b256_qrows",
-                                                           "ragged_b256_topk50_topp900"])
+    ap.add_argument("--workload", default="ragged_b256", choices=WORKLOADS)
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through the timed steps (0: enough for 1 GB, at least 2, at most 32)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle timing (0 = skip)")
