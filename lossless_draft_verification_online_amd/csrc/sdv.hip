@@ -1920,6 +1920,18 @@ __device__ __forceinline__ RowFold fold_row(const float2* p, int32_t C, int lane
   return f;
 }
 
+// The T > 0 fold of a row of at most 16 chunks by one row of 16 lanes (lane c holds chunk c, or
+// (-inf, 0) past the last), four rows per wave.  The same values as fold_row: there the other
+// lanes only add +0 to the sum and -inf to the maximum.
+__device__ __forceinline__ RowFold fold_row16(float2 r) {
+  RowFold f{0.0, -INFINITY, 0};
+  const float R = row16_max(r.x);
+  f.ref = R;
+  const double s = r.y > 0.0f ? (double)r.y * exp2((double)r.x - (double)R) : 0.0;
+  f.l2 = (double)R + log2(row16_sum(s));  // a row of -inf only: -inf
+  return f;
+}
+
 __device__ __forceinline__ void write_reject(const Params& P, int32_t i, int32_t trow0, int K, bool write_slots, int lane) {
   if (write_slots)
     for (int j = lane; j <= K; j += kWave) P.out_tokens[trow0 + j] = -1;
@@ -2044,11 +2056,23 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     }
   }
   __syncthreads();
-  for (int r = wave; r < n_rows; r += n_waves) {
-    const float2* p = staged ? lds_rec + (int64_t)r * P.C
-                             : (r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C);
-    const RowFold f = fold_row<kGreedy>(p, P.C, lane);
-    if (lane == 0) rows[r] = f;
+  auto records_of = [&](int r) {
+    return staged ? lds_rec + (int64_t)r * P.C
+                  : (r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C);
+  };
+  if (!kGreedy && P.C <= 16) {  // four rows per wave, one per row of 16 lanes
+    const int g = lane >> 4, c = lane & 15;
+    for (int r0 = 4 * wave; r0 < n_rows; r0 += 4 * n_waves) {
+      const int r = r0 + g;
+      const float2 rec = r < n_rows && c < P.C ? records_of(r)[c] : make_float2(-INFINITY, 0.0f);
+      const RowFold f = fold_row16(rec);
+      if (c == 0 && r < n_rows) rows[r] = f;
+    }
+  } else {
+    for (int r = wave; r < n_rows; r += n_waves) {
+      const RowFold f = fold_row<kGreedy>(records_of(r), P.C, lane);
+      if (lane == 0) rows[r] = f;
+    }
   }
   __syncthreads();
 

@@ -120,13 +120,19 @@ __device__ __forceinline__ void both(double v, double& lo, double& hi) {
   lo = __longlong_as_double((long long)a);
   hi = __longlong_as_double((long long)b);
 }
-// An all-reduce with a commutative combine (binary32, binary64, 32- or 64-bit unsigned).
+// The same combine within each row of 16 lanes: every lane ends with its row's value.
 template <class T, class Op>
-__device__ __forceinline__ T all_reduce(T v, Op op) {
+__device__ __forceinline__ T row_reduce(T v, Op op) {
   v = op(v, dpp<kXor1>(v));
   v = op(v, dpp<kXor2>(v));
   v = op(v, dpp<kHalfMirror>(v));
-  v = op(v, dpp<kMirror>(v));
+  return op(v, dpp<kMirror>(v));
+}
+// An all-reduce with a commutative combine (binary32, binary64, 32- or 64-bit unsigned): the rows
+// of 16 lanes first, then across rows.
+template <class T, class Op>
+__device__ __forceinline__ T all_reduce(T v, Op op) {
+  v = row_reduce(v, op);
   T lo, hi;
   both<16>(v, lo, hi);
   v = op(lo, hi);
@@ -156,6 +162,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ double wave_sum(double v) {
   return wave_detail::all_reduce(v, [](double a, double b) { return a + b; });
+}
+
+// Per row of 16 lanes.
+__device__ __forceinline__ float row16_max(float v) {
+  return wave_detail::row_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ double row16_sum(double v) {
+  return wave_detail::row_reduce(v, [](double a, double b) { return a + b; });
 }
 
 // Larger value wins; equal values go to the smaller index.
