@@ -91,7 +91,7 @@ def test_split_with_profiles():
 
 
 def test_automatic_split_of_a_small_batch_matches_oracle():
-    # B = 3 requests of 128256-token rows: 16 chunks per row, two workgroups per request
+    # B = 3 requests of 128256-token rows: 16 chunks per row, four workgroups per request
     rng = np.random.default_rng(8)
     b = W.make_random("split_auto_b3", [4, 0, 7], 128256, "bf16", 1.0, 3.0, 1.5, data_seed=81, verify_seed=82)
     for seed in range(4):
