@@ -1920,15 +1920,17 @@ __device__ __forceinline__ RowFold fold_row(const float2* p, int32_t C, int lane
   return f;
 }
 
-// The T > 0 fold of a row of at most 16 chunks by one row of 16 lanes (lane c holds chunk c, or
-// (-inf, 0) past the last), four rows per wave.  The same values as fold_row: there the other
-// lanes only add +0 to the sum and -inf to the maximum.
-__device__ __forceinline__ RowFold fold_row16(float2 r) {
+// The T > 0 fold of a row of at most 16 (32) chunks by one row of 16 lanes (one half wave): lane c
+// holds chunk c, or (-inf, 0) past the last; four (two) rows per wave.  The same values as
+// fold_row: there the other lanes only add +0 to the sum and -inf to the maximum.
+template <int kLanes>
+__device__ __forceinline__ RowFold fold_row_narrow(float2 r) {
+  static_assert(kLanes == 16 || kLanes == 32, "a row of 16 lanes or a half wave");
   RowFold f{0.0, -INFINITY, 0};
-  const float R = row16_max(r.x);
+  const float R = kLanes == 16 ? row16_max(r.x) : half_max(r.x);
   f.ref = R;
   const double s = r.y > 0.0f ? (double)r.y * exp2((double)r.x - (double)R) : 0.0;
-  f.l2 = (double)R + log2(row16_sum(s));  // a row of -inf only: -inf
+  f.l2 = (double)R + log2(kLanes == 16 ? row16_sum(s) : half_sum(s));  // a row of -inf only: -inf
   return f;
 }
 
@@ -2060,14 +2062,20 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
     return staged ? lds_rec + (int64_t)r * P.C
                   : (r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C);
   };
-  if (!kGreedy && P.C <= 16) {  // four rows per wave, one per row of 16 lanes
-    const int g = lane >> 4, c = lane & 15;
-    for (int r0 = 4 * wave; r0 < n_rows; r0 += 4 * n_waves) {
+  auto fold_narrow = [&](auto lanes) {  // kWave / lanes rows per wave
+    constexpr int kLanes = decltype(lanes)::value, kPer = kWave / kLanes;
+    const int g = lane / kLanes, c = lane % kLanes;
+    for (int r0 = kPer * wave; r0 < n_rows; r0 += kPer * n_waves) {
       const int r = r0 + g;
       const float2 rec = r < n_rows && c < P.C ? records_of(r)[c] : make_float2(-INFINITY, 0.0f);
-      const RowFold f = fold_row16(rec);
+      const RowFold f = fold_row_narrow<kLanes>(rec);
       if (c == 0 && r < n_rows) rows[r] = f;
     }
+  };
+  if (!kGreedy && P.C <= 16) {
+    fold_narrow(std::integral_constant<int, 16>{});
+  } else if (!kGreedy && P.C <= 32) {
+    fold_narrow(std::integral_constant<int, 32>{});
   } else {
     for (int r = wave; r < n_rows; r += n_waves) {
       const RowFold f = fold_row<kGreedy>(records_of(r), P.C, lane);

@@ -128,14 +128,20 @@ __device__ __forceinline__ T row_reduce(T v, Op op) {
   v = op(v, dpp<kHalfMirror>(v));
   return op(v, dpp<kMirror>(v));
 }
-// An all-reduce with a commutative combine (binary32, binary64, 32- or 64-bit unsigned): the rows
-// of 16 lanes first, then across rows.
+// The same combine within each half wave (32 lanes).
 template <class T, class Op>
-__device__ __forceinline__ T all_reduce(T v, Op op) {
+__device__ __forceinline__ T half_reduce(T v, Op op) {
   v = row_reduce(v, op);
   T lo, hi;
   both<16>(v, lo, hi);
-  v = op(lo, hi);
+  return op(lo, hi);
+}
+// An all-reduce with a commutative combine (binary32, binary64, 32- or 64-bit unsigned): the rows
+// of 16 lanes first, then the half waves, then across them.
+template <class T, class Op>
+__device__ __forceinline__ T all_reduce(T v, Op op) {
+  v = half_reduce(v, op);
+  T lo, hi;
   both<32>(v, lo, hi);
   return op(lo, hi);
 }
@@ -170,6 +176,14 @@ __device__ __forceinline__ float row16_max(float v) {
 }
 __device__ __forceinline__ double row16_sum(double v) {
   return wave_detail::row_reduce(v, [](double a, double b) { return a + b; });
+}
+
+// Per half wave (32 lanes).
+__device__ __forceinline__ float half_max(float v) {
+  return wave_detail::half_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ double half_sum(double v) {
+  return wave_detail::half_reduce(v, [](double a, double b) { return a + b; });
 }
 
 // Larger value wins; equal values go to the smaller index.

@@ -53,7 +53,8 @@ def test_device_uniforms_match_oracle_blocks():
 # ----------------------------------------------------------------------------- row quantities
 
 @pytest.mark.parametrize("V,dtype", [(1000, "fp32"), (32000, "bf16"), (8192, "bf16"), (8193, "bf16"),
-                                     (20011, "bf16"), (13, "fp32"), (4099, "fp32")])
+                                     (20011, "bf16"), (13, "fp32"), (4099, "fp32"), (151936, "bf16"),
+                                     (200003, "bf16")])
 def test_row_lse_and_ratio(V, dtype):
     rng = np.random.default_rng(V)
     depths = rng.integers(0, 9, size=12)
