@@ -661,7 +661,9 @@ __device__ __forceinline__ void resid_masses_pipelined(const M& m, const char* t
 // rows of 64 (vector k*64 + l for lane l), wave w sums rows w and w + n_waves, a scan of the row sums
 // picks the row, and the wave that owns it scans its 64 vector sums and walks the chosen vector.
 // Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
-template <class E, bool kResid, class M>
+// kFraction: target is a uniform u in [0, 1), scaled here by the chunk's total weight (the row sums
+// of the first step); a residual chunk without positive weight returns -2 in every wave.
+template <class E, bool kResid, bool kFraction = false, class M>
 __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* trow, const char* drow, int32_t c0,
                                                       int32_t n, double target, float k2, float ref_t, float e_hi,
                                                       float q_scale, double* scratch, int lane, int wave,
@@ -700,14 +702,22 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
   // every wave scans the 16 row sums the same way
   const double rsum = lane < kRows ? scratch[lane] : 0.0;
   const double rex = wave_exclusive_scan(rsum, lane);
-  const uint64_t rhit = __ballot(lane < kRows && rex + rsum > target);
+  double tgt = target;
+  if constexpr (kFraction) {
+    const double total = lane_value(rex + rsum, kRows - 1);
+    if constexpr (kResid) {
+      if (!(total > 0.0)) return -2;
+    }
+    tgt = target * total;
+  }
+  const uint64_t rhit = __ballot(lane < kRows && rex + rsum > tgt);
   const uint64_t rpos = __ballot(lane < kRows && rsum > 0.0);
   if (!rhit && !rpos) return wave == 0 ? c0 + n - 1 : -1;
   const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
   const int owner = kr % n_waves;
   if (wave != owner) return -1;
   const int j = kr / n_waves;
-  const double rest = target - lane_value(rex, kr);
+  const double rest = tgt - lane_value(rex, kr);
   // the owning wave: scan its 64 vector sums of row kr, then walk the chosen vector
   const float v = j == 0 ? vs[0] : vs[1];
   const double vex = wave_exclusive_scan((double)v, lane);
@@ -2239,6 +2249,9 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const char* dp = residual && !kQ ? row_ptr<E>(P.draft, drow0 + d.a, P.V) : nullptr;
   const float* qp = residual && kQ ? P.qrows + (int64_t)(drow0 + d.a) * P.V : nullptr;
 
+  // a row of one chunk (16-byte aligned logit rows): the in-chunk search totals the weights itself,
+  // so neither the mass pass nor the pick of a chunk runs (a split is 1 here: C / 4 < 1)
+  const bool one_chunk = kVec && !kQ && P.C == 1;
   // residual masses of this workgroup's chunks [c_lo, c_hi), into shared memory; the vector passes
   // see the range as a row of its own (tokens from c_lo's first, masks shifted to match)
   const int32_t c_lo = (int32_t)((int64_t)P.C * part / n_split), c_hi = (int32_t)((int64_t)P.C * (part + 1) / n_split);
@@ -2263,7 +2276,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
       }
     }
     __syncthreads();
-  } else if (residual) {
+  } else if (residual && !one_chunk) {
     if constexpr (kVec) {
       resid_masses_pipelined<E>(m_r, tp + (int64_t)v_lo * E::kBytes, dp + (int64_t)v_lo * E::kBytes, V_r,
                                 c_hi - c_lo, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + c_lo, lane, wave, n_waves);
@@ -2298,6 +2311,30 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     }
     __syncthreads();
     if (!last) return;
+  }
+  auto write_token = [&](int32_t y, bool empty) {
+    if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
+      P.out_tokens[trow] = y;
+      if (P.dg.draw_uniform) P.dg.draw_uniform[i] = (float)d.u;
+      if (P.dg.terminal_kind)
+        P.dg.terminal_kind[i] =
+            d.kind == SDV_TERM_BONUS ? SDV_TERM_BONUS : (empty ? SDV_TERM_RESIDUAL_EMPTY : SDV_TERM_RESIDUAL);
+    }
+  };
+  if constexpr (kVec && !kQ) {
+    if (one_chunk) {
+      int32_t y = -1;
+      bool empty = false;
+      if (residual) {
+        y = search_chunk_block<E, true, true>(m, tp, dp, 0, P.V, (double)d.u, k2, d.ref_t, d.e_hi, d.q_scale,
+                                              lds_mass + P.C, lane, wave, n_waves);
+        empty = y == -2;  // no positive residual weight in floating point: draw from p_t
+      }
+      if (!residual || empty)
+        y = search_chunk_block<E, false, true>(m, tp, nullptr, 0, P.V, (double)d.u, k2, d.ref_t, 0.0f, 0.0f,
+                                               lds_mass + P.C, lane, wave, n_waves);
+      return write_token(y, empty);
+    }
   }
   // every wave picks the same chunk from the same masses
   double S = 0.0;
@@ -2347,12 +2384,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     else
       y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return p_weight(m, E::at(tp, v), v, k2, ref_t); }, lane);
   }
-  if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
-    P.out_tokens[trow] = y;
-    if (P.dg.draw_uniform) P.dg.draw_uniform[i] = (float)d.u;
-    if (P.dg.terminal_kind)
-      P.dg.terminal_kind[i] = d.kind == SDV_TERM_BONUS ? SDV_TERM_BONUS : (empty ? SDV_TERM_RESIDUAL_EMPTY : SDV_TERM_RESIDUAL);
-  }
+  write_token(y, empty);
 }
 
 // ============================================================================ Philox test hook
