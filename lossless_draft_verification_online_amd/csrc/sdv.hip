@@ -51,6 +51,7 @@ struct DiagPtrs {
 };
 
 constexpr int32_t kMaxChunks = 4096;  // chunks per row: the verdict and cut kernels keep one value per chunk in LDS
+constexpr int kVerdictWaves = 8;      // waves of a verdict workgroup
 
 // Truncating bf16 calls: the row pass also counts, per chunk, the logits of each of the kHistKeys
 // 16-bit order keys at and below the chunk maximum's (one binade of positive logits), so that a cut
@@ -681,17 +682,18 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
       w[q] = kResid ? resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale)
                     : p_weight(m, ft[q], v0 + q, k2, ref_t);
   };
-  // rows owned by this wave: wave and wave + n_waves (n_waves == 8 covers the 16 rows)
-  u32x4 t[2], dd[2];
-  float vs[2];
+  // rows owned by this wave: wave + j n_waves, j < kPer (n_waves == kVerdictWaves)
+  constexpr int kPer = kRows / kVerdictWaves;
+  u32x4 t[kPer], dd[kPer];
+  float vs[kPer];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     const int vi = (wave + j * n_waves) * kWave + lane;
     t[j] = wave + j * n_waves < kRows ? load_vec<E>(tv, vi, nvec) : neg_inf_vec<E>();
     dd[j] = (kResid && wave + j * n_waves < kRows) ? load_vec<E>(dv, vi, nvec) : neg_inf_vec<E>();
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     float w[E::kPerVec];
     weights(t[j], dd[j], c0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
     vs[j] = tree_sum(w);
@@ -719,14 +721,19 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
   const int j = kr / n_waves;
   const double rest = tgt - lane_value(rex, kr);
   // the owning wave: scan its 64 vector sums of row kr, then walk the chosen vector
-  const float v = j == 0 ? vs[0] : vs[1];
+  float v = vs[0];  // j is uniform: selects, not an indexed register array
+#pragma unroll
+  for (int jj = 1; jj < kPer; ++jj)
+    if (jj == j) v = vs[jj];
   const double vex = wave_exclusive_scan((double)v, lane);
   const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
   const uint64_t vpos = __ballot(v > 0.0f);
   const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
   const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
   float w[E::kPerVec];
-  weights(j == 0 ? t[0] : t[1], j == 0 ? dd[0] : dd[1], base, w);
+#pragma unroll
+  for (int jj = 0; jj < kPer; ++jj)
+    if (jj == j) weights(t[jj], dd[jj], base, w);
   int32_t yl = base + E::kPerVec - 1;
   int32_t last_pos = -1;
   double upto = vex;
@@ -909,11 +916,12 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
       for (int e = 0; e < 4; ++e)
         w[4 * g + e] = resid_weight_q(m, ft[4 * g + e], q[g][e], v0 + 4 * g + e, k2, ref_t, q_scale);
   };
-  u32x4 t[2];
-  f32x4 q[2][kQV];
-  float vs[2];
+  constexpr int kPer = kRows / kVerdictWaves;  // rows of 64 vectors per wave
+  u32x4 t[kPer];
+  f32x4 q[kPer][kQV];
+  float vs[kPer];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     const int row = wave + j * n_waves;
     const int vi = row * kWave + lane;
     const bool in = row < kRows && vi < nvec;
@@ -922,7 +930,7 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
     for (int g = 0; g < kQV; ++g) q[j][g] = in ? qv[vi * kQV + g] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < kPer; ++j) {
     float w[E::kPerVec];
     weights(t[j], q[j], c0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
     vs[j] = tree_sum(w);
@@ -940,15 +948,19 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
   if (wave != owner) return -1;
   const int j = kr / n_waves;
   const double rest = target - lane_value(rex, kr);
-  const float v = j == 0 ? vs[0] : vs[1];
+  float v = vs[0];
+#pragma unroll
+  for (int jj = 1; jj < kPer; ++jj)
+    if (jj == j) v = vs[jj];
   const double vex = wave_exclusive_scan((double)v, lane);
   const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
   const uint64_t vpos = __ballot(v > 0.0f);
   const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
   const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
   float w[E::kPerVec];
-  if (j == 0) weights(t[0], q[0], base, w);
-  else weights(t[1], q[1], base, w);
+#pragma unroll
+  for (int jj = 0; jj < kPer; ++jj)
+    if (jj == j) weights(t[jj], q[jj], base, w);
   int32_t yl = base + E::kPerVec - 1;
   int32_t last_pos = -1;
   double upto = vex;
@@ -1993,8 +2005,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves);
 
-constexpr int kVerdictWaves = 8;
-static_assert(2 * kVerdictWaves >= kVecPerLane, "the in-chunk search gives each wave two rows of 64 vectors");
+static_assert(kVecPerLane % kVerdictWaves == 0, "the in-chunk search gives each wave whole rows of 64 vectors");
 constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
 // The verdict of request i under one rule (k2 = log2(e)/T and the Philox key seed), by one
