@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 2
+#define SDV_ABI_VERSION 3
 #define SDV_MAX_DEPTH 64 /* largest K_i a request may carry */
 #define SDV_MAX_EVENTS 4 /* timing hooks in sdv_diag */
 
@@ -78,6 +78,16 @@ typedef enum {
  *                  every row read), events[3] after the truncation kernel (top-k / top-p through
  *                  sdv_verify_opts; not recorded when it does not run), events[2] after the verdict
  *                  kernel (per request: fold, accept scan, terminal draw).
+ *   target_logit   [n_draft_rows]      z_target[x_j], the stored target logit at each draft token,
+ *                                      widened to binary32 (T > 0)
+ *   draft_logit    [n_draft_rows]      z_draft[x_j], the same on the draft row (T > 0, draft logits;
+ *                                      with sdv_options.draft_probs it holds q_j(x_j) as given)
+ *   terminal_mass  [B]                 S, the total weight of the extra-token draw in probability
+ *                                      units: sum_v max(p_t(v) - q_t(v), 0) for a correction, the
+ *                                      mass of p_K (1 up to rounding) for a bonus or for a draw from
+ *                                      p_t after an empty residual (T > 0, requests that draw)
+ * The gathers and S are the quantities the accept test and the inverse CDF are built from (SDCP
+ * "Acceptance Rules", Rule 2: p_i(x_i)/q_i(x_i) and normalize(max(p - q, 0))).
  */
 typedef struct sdv_diag {
   double* target_lse;
@@ -88,6 +98,9 @@ typedef struct sdv_diag {
   float* draw_uniform;
   int32_t* terminal_kind;
   void* events[SDV_MAX_EVENTS];
+  float* target_logit;
+  float* draft_logit;
+  double* terminal_mass;
 } sdv_diag;
 
 /*
@@ -299,6 +312,16 @@ int sdv_commit(int32_t B, int64_t n_draft_rows, const int32_t* ragged_offsets, c
  * keys [n][2], out [n][4] are uint32 device arrays.  n < 1 or NULL pointers -> SDV_ERR_INVALID_ARG.
  */
 int sdv_philox4x32_10(const uint32_t* counters, const uint32_t* keys, int64_t n, uint32_t* out, void* stream);
+
+/*
+ * The verifier's own Philox blocks on the device, for testing its uniforms (the keying of sdv_verify:
+ * key = (seed low 32 bits, seed high 32 bits), counter = (position j, request i, 0, 0); SDCP
+ * "Acceptance Rules", Rule 2, one uniform per position and purpose: word 0 feeds the accept test,
+ * word 1 the draw of the extra token).  Writes words[(i * P + j) * 4 + w] = word w of the block of
+ * (request i, position j) for i < B, j < P: a uint32 device array of B * P * 4 words owned by the
+ * caller.  B < 1, P < 1, NULL words -> SDV_ERR_INVALID_ARG; B * P above 2^31 - 1 -> SDV_ERR_LIMIT.
+ */
+int sdv_philox_uniforms(uint64_t seed, int32_t B, int32_t P, uint32_t* words, void* stream);
 
 /*
  * Measurement hook: the bandwidth yardstick of the row pass.  Decoding is limited by memory

@@ -11,11 +11,11 @@ import ctypes
 import torch
 
 from . import _native
-from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_RESIDUAL,
-                      TERM_RESIDUAL_EMPTY, SdvError)
+from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_NONE,
+                      TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, SdvError)
 
-__all__ = ["verify", "verify_ex", "commit", "workspace_bytes", "philox4x32_10", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
-           "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
+__all__ = ["verify", "verify_ex", "commit", "workspace_bytes", "philox4x32_10", "philox_uniforms", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+           "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_NONE", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
 
 _DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
 _WORKSPACE: dict = {}
@@ -149,7 +149,8 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
     shapes = {"target_lse": (n_d + B, torch.float64), "draft_lse": (n_d, torch.float64),
               "target_argmax": (n_d + B, torch.int32), "ratio": (n_d, torch.float64),
               "accept_uniform": (n_d, torch.float32), "draw_uniform": (B, torch.float32),
-              "terminal_kind": (B, torch.int32)}
+              "terminal_kind": (B, torch.int32), "target_logit": (n_d, torch.float32),
+              "draft_logit": (n_d, torch.float32), "terminal_mass": (B, torch.float64)}
     dvals = {}
     dg = None
     want_kept = "kept_tokens" in diag
@@ -244,6 +245,18 @@ def philox4x32_10(counters: torch.Tensor, keys: torch.Tensor) -> torch.Tensor:
                                              torch.cuda.current_stream(counters.device).cuda_stream)
     if rc != 0:
         raise SdvError(rc, "sdv_philox4x32_10")
+    return out
+
+
+def philox_uniforms(seed: int, B: int, P: int, device="cuda") -> torch.Tensor:
+    """The verifier's Philox blocks (sdv_philox_uniforms): int32 [B, P, 4] views of the uint32 words of
+    the block of (request i, position j), counter (j, i, 0, 0), key = seed."""
+    out = torch.empty((B, P, 4), dtype=torch.int32, device=device)
+    with torch.cuda.device(out.device):
+        rc = _native.lib().sdv_philox_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, B, P, _ptr(out),
+                                               torch.cuda.current_stream(out.device).cuda_stream)
+    if rc != 0:
+        raise SdvError(rc, "sdv_philox_uniforms")
     return out
 
 

@@ -11,7 +11,7 @@ SDV_MAX_DEPTH = 64
 SDV_MAX_EVENTS = 4
 STATUS = {0: "SDV_OK", -1: "SDV_ERR_INVALID_ARG", -2: "SDV_ERR_UNSUPPORTED", -3: "SDV_ERR_LIMIT",
           -4: "SDV_ERR_WORKSPACE", -5: "SDV_ERR_HIP"}
-TERM_GREEDY, TERM_BONUS, TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, TERM_BAD = 0, 1, 2, 3, -1
+TERM_GREEDY, TERM_BONUS, TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, TERM_NONE, TERM_BAD = 0, 1, 2, 3, 4, -1
 
 
 class SdvDiag(ctypes.Structure):
@@ -24,6 +24,9 @@ class SdvDiag(ctypes.Structure):
         ("draw_uniform", ctypes.c_void_p),
         ("terminal_kind", ctypes.c_void_p),
         ("events", ctypes.c_void_p * SDV_MAX_EVENTS),
+        ("target_logit", ctypes.c_void_p),
+        ("draft_logit", ctypes.c_void_p),
+        ("terminal_mass", ctypes.c_void_p),
     ]
 
 
@@ -89,6 +92,8 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_commit.argtypes = [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 12
     L.sdv_philox4x32_10.restype = ctypes.c_int
     L.sdv_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.sdv_philox_uniforms.restype = ctypes.c_int
+    L.sdv_philox_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.restype = ctypes.c_char_p
     L.sdv_read_ceiling.restype = ctypes.c_int
     L.sdv_read_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]

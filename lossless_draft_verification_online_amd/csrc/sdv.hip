@@ -48,6 +48,9 @@ struct DiagPtrs {
   float* accept_uniform;
   float* draw_uniform;
   int32_t* terminal_kind;
+  float* target_logit;
+  float* draft_logit;
+  double* terminal_mass;
 };
 
 constexpr int32_t kMaxChunks = 4096;  // chunks per row: the verdict and cut kernels keep one value per chunk in LDS
@@ -450,9 +453,11 @@ __device__ __forceinline__ int32_t search_chunk(int32_t c0, int32_t n, double ta
 // Masses m_c (fp64) of the chunks of one row; returns the chunk holding u * S and the target inside it.
 // mass(c) is evaluated by every lane for its chunks; chunks are visited in ascending order.
 template <class MassFn>
-__device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, double* target_in_chunk, int lane) {
+__device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, double* target_in_chunk, double* total,
+                                              int lane) {
   double S = 0.0;
   for (int32_t c0 = 0; c0 < C; c0 += kWave) S += wave_sum(c0 + lane < C ? mass(c0 + lane) : 0.0);
+  *total = S;
   const double U = u * S;
   double carry = 0.0;
   int32_t last_pos = -1;
@@ -661,14 +666,15 @@ __device__ __forceinline__ void resid_masses_pipelined(const M& m, const char* t
 // Inverse CDF inside one chunk (16-byte aligned rows) by a whole workgroup: the chunk's vectors form
 // rows of 64 (vector k*64 + l for lane l), wave w sums rows w and w + n_waves, a scan of the row sums
 // picks the row, and the wave that owns it scans its 64 vector sums and walks the chosen vector.
-// Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
+// Returns the token in the owning wave and -1 in the others.  row_sums holds at least 16 doubles.
 // kFraction: target is a uniform u in [0, 1), scaled here by the chunk's total weight (the row sums
-// of the first step); a residual chunk without positive weight returns -2 in every wave.
+// of the first step), which every wave also stores into *total; a residual chunk without positive
+// weight returns -2 in every wave.
 template <class E, bool kResid, bool kFraction = false, class M>
 __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* trow, const char* drow, int32_t c0,
                                                       int32_t n, double target, float k2, float ref_t, float e_hi,
-                                                      float q_scale, double* scratch, int lane, int wave,
-                                                      int n_waves) {
+                                                      float q_scale, double* row_sums, int lane, int wave,
+                                                      int n_waves, double* total = nullptr) {
   constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
   const int32_t nvec = n / E::kPerVec;
   const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
@@ -698,19 +704,20 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
     weights(t[j], dd[j], c0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
     vs[j] = tree_sum(w);
     const double rs = wave_sum((double)vs[j]);
-    if (lane == 0 && wave + j * n_waves < kRows) scratch[wave + j * n_waves] = rs;
+    if (lane == 0 && wave + j * n_waves < kRows) row_sums[wave + j * n_waves] = rs;
   }
   __syncthreads();
   // every wave scans the 16 row sums the same way
-  const double rsum = lane < kRows ? scratch[lane] : 0.0;
+  const double rsum = lane < kRows ? row_sums[lane] : 0.0;
   const double rex = wave_exclusive_scan(rsum, lane);
   double tgt = target;
   if constexpr (kFraction) {
-    const double total = lane_value(rex + rsum, kRows - 1);
+    const double sum = lane_value(rex + rsum, kRows - 1);
+    *total = sum;
     if constexpr (kResid) {
-      if (!(total > 0.0)) return -2;
+      if (!(sum > 0.0)) return -2;
     }
-    tgt = target * total;
+    tgt = target * sum;
   }
   const uint64_t rhit = __ballot(lane < kRows && rex + rsum > tgt);
   const uint64_t rpos = __ballot(lane < kRows && rsum > 0.0);
@@ -896,11 +903,11 @@ __device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const
 // Inverse CDF inside one chunk of a (target row, q row) pair by a whole workgroup (16-byte aligned
 // rows), laid out as the logit version: rows of 64 vectors, wave w sums rows w and w + n_waves, a
 // scan of the row sums picks the row, the owning wave scans its vector sums and walks the vector.
-// Returns the token in the owning wave and -1 in the others.  scratch holds at least 16 doubles.
+// Returns the token in the owning wave and -1 in the others.  row_sums holds at least 16 doubles.
 template <class E, class M>
 __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* trow, const float* qrow, int32_t c0,
                                                         int32_t n, double target, float k2, float ref_t,
-                                                        float q_scale, double* scratch, int lane, int wave,
+                                                        float q_scale, double* row_sums, int lane, int wave,
                                                         int n_waves) {
   constexpr int kRows = kVecPerLane;
   constexpr int kQV = E::kPerVec / 4;
@@ -935,10 +942,10 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
     weights(t[j], q[j], c0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
     vs[j] = tree_sum(w);
     const double rs = wave_sum((double)vs[j]);
-    if (lane == 0 && wave + j * n_waves < kRows) scratch[wave + j * n_waves] = rs;
+    if (lane == 0 && wave + j * n_waves < kRows) row_sums[wave + j * n_waves] = rs;
   }
   __syncthreads();
-  const double rsum = lane < kRows ? scratch[lane] : 0.0;
+  const double rsum = lane < kRows ? row_sums[lane] : 0.0;
   const double rex = wave_exclusive_scan(rsum, lane);
   const uint64_t rhit = __ballot(lane < kRows && rex + rsum > target);
   const uint64_t rpos = __ballot(lane < kRows && rsum > 0.0);
@@ -1997,6 +2004,7 @@ struct Decision {
   int32_t a;
   float ref_t, e_hi, q_scale;
   double u;
+  double l2_t;   // base-2 LSE of the drawn target row: weights in the frame 2^(z k - ref_t) sum to 2^(l2_t - ref_t)
   Cut ct, cd;  // cuts of the drawn position's target and draft rows (truncating profiles)
 };
 
@@ -2107,7 +2115,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
 
   // 2. the verdict, by wave 0
   if (wave == 0) {
-    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0, Cut{-INFINITY, INT32_MAX}, Cut{-INFINITY, INT32_MAX}};
+    Decision d{SDV_TERM_BAD, 0, 0.0f, 0.0f, 0.0f, 0.0, 0.0, Cut{-INFINITY, INT32_MAX}, Cut{-INFINITY, INT32_MAX}};
     if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
       if (lead) write_reject(P, i, trow0, K, true, lane);
     } else if constexpr (kGreedy) {
@@ -2175,6 +2183,8 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
             if (P.dg.draft_lse && !kQ) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
             if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
             if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
+            if (P.dg.target_logit) P.dg.target_logit[drow0 + lane] = zt;
+            if (P.dg.draft_logit) P.dg.draft_logit[drow0 + lane] = zd;
           }
         }
         d.a = a;
@@ -2187,12 +2197,14 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
         } else if (a == K) {
           d.kind = SDV_TERM_BONUS;
           d.ref_t = rows[K].ref;
+          d.l2_t = rows[K].l2;
           d.u = P.u_each ? P.u_each[trow0 + K] : (double)draw_uniform(verifier_block(seed, (uint32_t)i, (uint32_t)K));
         } else {
           // weights in the frame 2^(z_t k - ref_t) of the rejected target row; draft side
           // 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and the factor 2^-(e - e_hi)
           d.kind = SDV_TERM_RESIDUAL;
           d.ref_t = lane_value(ft.ref, a);
+          d.l2_t = lane_value(ft.l2, a);
           if constexpr (kQ) {  // q scaled into the frame: q 2^(l2_t - ref_t)
             d.q_scale = (float)exp2(lane_value(ft.l2, a) - (double)d.ref_t);
           } else {
@@ -2323,10 +2335,12 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     __syncthreads();
     if (!last) return;
   }
-  auto write_token = [&](int32_t y, bool empty) {
+  // S: the total weight of the draw in the frame 2^(z k - ref_t), reported in probability units
+  auto write_token = [&](int32_t y, bool empty, double S) {
     if (y >= 0 && lane == 0) {  // the one wave that resolved the token writes it
       P.out_tokens[trow] = y;
       if (P.dg.draw_uniform) P.dg.draw_uniform[i] = (float)d.u;
+      if (P.dg.terminal_mass) P.dg.terminal_mass[i] = S * exp2((double)d.ref_t - d.l2_t);
       if (P.dg.terminal_kind)
         P.dg.terminal_kind[i] =
             d.kind == SDV_TERM_BONUS ? SDV_TERM_BONUS : (empty ? SDV_TERM_RESIDUAL_EMPTY : SDV_TERM_RESIDUAL);
@@ -2336,15 +2350,19 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     if (one_chunk) {
       int32_t y = -1;
       bool empty = false;
+      double S = 0.0;
       if (residual) {
         y = search_chunk_block<E, true, true>(m, tp, dp, 0, P.V, (double)d.u, k2, d.ref_t, d.e_hi, d.q_scale,
-                                              lds_mass + P.C, lane, wave, n_waves);
+                                              lds_mass + P.C, lane, wave, n_waves, &S);
         empty = y == -2;  // no positive residual weight in floating point: draw from p_t
+        // the fallback search rewrites the row sums every wave has just read: all reads come first
+        // (empty is the same in every wave, so the barrier is uniform)
+        if (empty) __syncthreads();
       }
       if (!residual || empty)
         y = search_chunk_block<E, false, true>(m, tp, nullptr, 0, P.V, (double)d.u, k2, d.ref_t, 0.0f, 0.0f,
-                                               lds_mass + P.C, lane, wave, n_waves);
-      return write_token(y, empty);
+                                               lds_mass + P.C, lane, wave, n_waves, &S);
+      return write_token(y, empty, S);
     }
   }
   // every wave picks the same chunk from the same masses
@@ -2363,11 +2381,11 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   double tgt = 0.0;
   int32_t cs;
   if (residual) {
-    cs = pick_chunk(P.C, (double)d.u, [&](int32_t c) { return lds_mass[c]; }, &tgt, lane);
+    cs = pick_chunk(P.C, (double)d.u, [&](int32_t c) { return lds_mass[c]; }, &tgt, &S, lane);
   } else {
     cs = pick_chunk(
         P.C, (double)d.u, [&](int32_t c) { return (double)rec[c].y * exp2((double)rec[c].x - (double)d.ref_t); },
-        &tgt, lane);
+        &tgt, &S, lane);
   }
   const int32_t s0 = cs * E::kChunk;
   const int32_t n = min(E::kChunk, P.V - s0);
@@ -2395,7 +2413,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     else
       y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return p_weight(m, E::at(tp, v), v, k2, ref_t); }, lane);
   }
-  write_token(y, empty);
+  write_token(y, empty, S);
 }
 
 // ============================================================================ Philox test hook
@@ -2409,6 +2427,18 @@ __global__ void philox_kernel(const uint32_t* __restrict__ ctr, const uint32_t* 
   out[4 * b + 1] = r.w1;
   out[4 * b + 2] = r.w2;
   out[4 * b + 3] = r.w3;
+}
+
+// The verifier's blocks for requests i < B and positions j < P, laid out [i][j][4].
+__global__ void philox_grid_kernel(uint64_t seed, int32_t B, int32_t P, uint32_t* __restrict__ words) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= (int64_t)B * P) return;
+  const int32_t i = (int32_t)(b / P), j = (int32_t)(b - (int64_t)i * P);
+  const Philox4 r = verifier_block(seed, (uint32_t)i, (uint32_t)j);
+  words[4 * b] = r.w0;
+  words[4 * b + 1] = r.w1;
+  words[4 * b + 2] = r.w2;
+  words[4 * b + 3] = r.w3;
 }
 
 // ============================================================================ read ceiling
@@ -2640,8 +2670,9 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.split_mass = reinterpret_cast<double*>(ws + L.split_mass);
   P.split_count = reinterpret_cast<uint32_t*>(ws + L.split_count);
   if (diag) {
-    P.dg = DiagPtrs{diag->target_lse, diag->draft_lse, diag->target_argmax, diag->ratio,
-                    diag->accept_uniform, diag->draw_uniform, diag->terminal_kind};
+    P.dg = DiagPtrs{diag->target_lse,     diag->draft_lse,    diag->target_argmax, diag->ratio,
+                    diag->accept_uniform, diag->draw_uniform, diag->terminal_kind, diag->target_logit,
+                    diag->draft_logit,    diag->terminal_mass};
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == SDV_BF16) return launch_any<Bf16>(P, vec, s, diag);
@@ -2651,11 +2682,6 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
 }  // namespace sdv
 
 extern "C" {
-
-size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype) {
-  sdv::Layout L;
-  return sdv::make_layout(B, n_draft_rows, V, dtype, &L) == SDV_OK ? L.total : 0;
-}
 
 int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                   const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
@@ -2701,6 +2727,15 @@ int sdv_philox4x32_10(const uint32_t* counters, const uint32_t* keys, int64_t n,
   if ((n + 255) / 256 > INT32_MAX) return SDV_ERR_LIMIT;
   hipLaunchKernelGGL(sdv::philox_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      reinterpret_cast<hipStream_t>(stream), counters, keys, n, out);
+  return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
+}
+
+int sdv_philox_uniforms(uint64_t seed, int32_t B, int32_t P, uint32_t* words, void* stream) {
+  if (!words || B < 1 || P < 1) return SDV_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)B * P;
+  if (n > INT32_MAX) return SDV_ERR_LIMIT;
+  hipLaunchKernelGGL(sdv::philox_grid_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), seed, B, P, words);
   return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
 }
 

@@ -30,13 +30,13 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
                           "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms", "sdv_commit",
-                          "sdv_status_string", "sdv_abi_version"}
+                          "sdv_status_string", "sdv_abi_version", "sdv_philox_uniforms"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdv_abi_version() == 2
+    assert lib.sdv_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.sdv_status_string(code) not in (None, b"", b"unknown status")
     assert lib.sdv_status_string(17) == b"unknown status"
@@ -104,6 +104,10 @@ def test_host_argument_errors(lib):
     assert lib.sdv_read_ceiling(FAKE, 0, FAKE, None) == -1
     assert lib.sdv_read_ceiling(FAKE + 8, 4, FAKE, None) == -1  # not 16-byte aligned
     assert lib.sdv_read_ceiling(FAKE, 4, None, None) == -1
+    assert lib.sdv_philox_uniforms(1, 4, 4, None, None) == -1
+    assert lib.sdv_philox_uniforms(1, 0, 4, FAKE, None) == -1
+    assert lib.sdv_philox_uniforms(1, 4, 0, FAKE, None) == -1
+    assert lib.sdv_philox_uniforms(1, 2**20, 2**12, FAKE, None) == -3
 
 
 def test_profiled_host_argument_checks(lib):

@@ -16,6 +16,7 @@ import pytest
 from scipy import stats
 
 import filter_pins
+import keying_pins
 from oracle import exact, oracle
 from workloads import offsets_from_depths
 
@@ -63,6 +64,15 @@ MUTATIONS = {
                                  "kind = ORACLE_TERM_BONUS;\n    for (int32_t v = 0; v < V; ++v)\n      w[v] = 1 ?"),
     "residual_from_untruncated_q": (": (kept(keep_d, t, V, v) ? exp(", ": (1 ? exp("),
     "invalid_top_p_accepted": ("top_p_milli < 0 || top_p_milli > 1000;", "top_p_milli < 0;"),
+    # which Philox block and word each decision takes
+    "draw_from_block_of_position_0": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)t, blk);\n    u = draw_uniform(blk);",
+                                      "oracle_philox_block(seed, (uint32_t)i, 0u, blk);\n    u = draw_uniform(blk);"),
+    "draw_from_word_2": ("return (double)(w[1] >> 8) / 16777216.0;", "return (double)(w[2] >> 8) / 16777216.0;"),
+    "accept_from_block_of_next_position": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)j, blk);\n      r = accept_uniform(blk);",
+                                           "oracle_philox_block(seed, (uint32_t)i, (uint32_t)(j + 1), blk);\n      r = accept_uniform(blk);"),
+    "accept_from_word_3": ("return (double)((w[0] >> 8) + 1u) / 16777216.0;", "return (double)((w[3] >> 8) + 1u) / 16777216.0;"),
+    "draw_counter_request_and_position_swapped": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)t, blk);\n    u = draw_uniform(blk);",
+                                                  "oracle_philox_block(seed, (uint32_t)t, (uint32_t)i, blk);\n    u = draw_uniform(blk);"),
 }
 
 
@@ -232,8 +242,14 @@ def _pin_filters(lib_path):
     return all(check(lib_path) for check in filter_pins.ALL)
 
 
+def _pin_keying(lib_path):
+    """Every Philox keying pin of tests/keying_pins.py (block and word of each decision)."""
+    return all(check(lib_path) for check in keying_pins.ALL)
+
+
 def test_unmutated_oracle_passes_every_pin(tmp_path):
-    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops, _pin_qrows, _pin_filters):
+    for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops, _pin_qrows, _pin_filters,
+                  _pin_keying):
         assert check(oracle.LIBRARY)
     assert _pin_philox(oracle.LIBRARY, tmp_path)
 
@@ -252,5 +268,6 @@ def test_planted_mistake_is_caught(tmp_path, name):
         "stops_and_caller_uniforms": _pin_stops(lib),
         "qrows": _pin_qrows(lib),
         "top_k_top_p": _pin_filters(lib),
+        "keying": _pin_keying(lib),
     }
     assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"

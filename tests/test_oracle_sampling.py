@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 from scipy import stats
 
+import keying_pins
 from oracle import exact, oracle
 from workloads import exactness_batch, exactness_case, offsets_from_depths
 
@@ -182,6 +183,27 @@ def test_k0_is_categorical_sampling_by_searchsorted():
             y = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
             if res["cdf_margin"][i] > 1e-12:
                 assert res["out_tokens"][i] == y
+
+
+def test_bonus_draw_takes_the_block_of_position_k():
+    """Every draft accepted (draft rows equal to the target rows): the bonus at t = K_i is the
+    categorical draw from p_K with u from Philox block (i, K_i), word 1 (keying_pins)."""
+    assert keying_pins.pin_forced_bonus()
+    assert keying_pins.pin_forced_bonus(T=0.7, seed=99)
+
+
+def test_correction_draw_takes_the_block_of_the_rejected_position():
+    """A rejection forced at t = 0..3: the correction is the categorical draw from max(p_t - q_t, 0)
+    with u from Philox block (i, t), word 1."""
+    assert keying_pins.pin_forced_rejection()
+    assert keying_pins.pin_forced_rejection(T=1.3, seed=7)
+
+
+def test_accept_test_takes_word_0_of_the_block_of_its_position():
+    """Ratios placed half a 2^-24 step above or below r from block (i, j), word 0, at positions
+    j = 0..3: every decision follows that r."""
+    assert keying_pins.pin_accept_edges()
+    assert keying_pins.pin_accept_edges(seed=2**63 + 12345)
 
 
 def test_draft_equal_to_target_accepts_everything():
