@@ -2683,6 +2683,11 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
 
 extern "C" {
 
+size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype) {
+  sdv::Layout L;
+  return sdv::make_layout(B, n_draft_rows, V, dtype, &L) == SDV_OK ? L.total : 0;
+}
+
 int sdv_verify_ex(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                   const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
                   double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
