@@ -334,6 +334,29 @@ int sdv_philox_uniforms(uint64_t seed, int32_t B, int32_t P, uint32_t* words, vo
  */
 int sdv_read_ceiling(const void* src, int64_t n_chunks, uint32_t* out, void* stream);
 
+/*
+ * sdv_verify for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The same verification as sdv_verify (same kernels,
+ * same outputs) with no workspace argument: the library's scratch is a static device array of
+ * SDV_NOALLOC_SCRATCH_BYTES bytes that each GPU the library runs on holds until the process ends (its
+ * address is looked up once per device, on the first call with that device current).  The call
+ * allocates and frees nothing.
+ *   sdv_noalloc_bytes   the scratch a batch of this shape needs (0 on invalid shapes): 8 bytes per
+ *                       16 KiB chunk of every row, 8 bytes per row, 8 bytes per chunk of a row and
+ *                       4 bytes per request (no room for top-k / top-p counts: sdv_verify never
+ *                       truncates), each array rounded up to 256 bytes.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind; each call clears
+ * what it needs zeroed itself.  Calls that overlap in time on one GPU (on different streams) race on
+ * the array: serialize them, for instance on one stream.  Errors as in sdv_verify, plus
+ * SDV_ERR_LIMIT when sdv_noalloc_bytes(...) exceeds SDV_NOALLOC_SCRATCH_BYTES (nothing is launched)
+ * and SDV_ERR_HIP when the current device cannot be queried or the array's address cannot be found.
+ */
+#define SDV_NOALLOC_SCRATCH_BYTES (8u << 20) /* 8 MiB per GPU */
+size_t sdv_noalloc_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype);
+int sdv_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                       double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* sdv_status_string(int status);
 

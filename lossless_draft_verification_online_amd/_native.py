@@ -9,6 +9,7 @@ from .build import LIBRARY
 SDV_BF16, SDV_FP32 = 0, 1
 SDV_MAX_DEPTH = 64
 SDV_MAX_EVENTS = 4
+SDV_NOALLOC_SCRATCH_BYTES = 8 << 20
 STATUS = {0: "SDV_OK", -1: "SDV_ERR_INVALID_ARG", -2: "SDV_ERR_UNSUPPORTED", -3: "SDV_ERR_LIMIT",
           -4: "SDV_ERR_WORKSPACE", -5: "SDV_ERR_HIP"}
 TERM_GREEDY, TERM_BONUS, TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, TERM_NONE, TERM_BAD = 0, 1, 2, 3, 4, -1
@@ -78,6 +79,10 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
     L.sdv_verify.restype = ctypes.c_int
     L.sdv_verify.argtypes = list(_VERIFY_ARGS)
+    L.sdv_verify_noalloc.restype = ctypes.c_int
+    L.sdv_verify_noalloc.argtypes = list(_VERIFY_ARGS[:12]) + [ctypes.c_void_p]
+    L.sdv_noalloc_bytes.restype = ctypes.c_size_t
+    L.sdv_noalloc_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
     L.sdv_verify_ex.restype = ctypes.c_int
     L.sdv_verify_ex.argtypes = list(_VERIFY_ARGS) + [ctypes.POINTER(SdvDiag)]
     L.sdv_verify_profiled.restype = ctypes.c_int

@@ -31,6 +31,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/sdv.h"
@@ -2486,8 +2487,10 @@ inline int32_t verdict_split(int32_t B, int32_t C) {
 }
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Returns SDV_OK and fills the layout, or the status the shape violates.
-inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype, Layout* L) {
+// Returns SDV_OK and fills the layout, or the status the shape violates.  counts: room for the
+// key counts and the pending-row list of top-k / top-p calls on bf16 rows (calls that never
+// truncate, such as sdv_verify, need none).
+inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype, Layout* L, bool counts_room = true) {
   if (dtype != SDV_BF16 && dtype != SDV_FP32) return SDV_ERR_UNSUPPORTED;
   if (B < 1 || n_draft_rows < 0 || V < 1) return SDV_ERR_INVALID_ARG;
   const int64_t n_t = n_draft_rows + B;
@@ -2507,10 +2510,11 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   };
   L->part = take((size_t)slots * C * sizeof(float2));
   L->cuts = take((size_t)slots * sizeof(Cut));
-  const size_t counts = dtype == SDV_BF16 ? (size_t)slots * C : 0;  // per-chunk key counts of truncating calls
+  const bool bf16_counts = dtype == SDV_BF16 && counts_room;
+  const size_t counts = bf16_counts ? (size_t)slots * C : 0;  // per-chunk key counts of truncating calls
   L->hist = take(counts * kHistKeys * sizeof(uint16_t));
   L->hist_top = take(counts * sizeof(uint32_t));
-  L->pending = take(dtype == SDV_BF16 ? (size_t)(slots + 1) * sizeof(int32_t) : 0);
+  L->pending = take(bf16_counts ? (size_t)(slots + 1) * sizeof(int32_t) : 0);
   L->split_mass = take((size_t)B * C * sizeof(double));
   L->split_count = take((size_t)B * sizeof(uint32_t));
   L->total = off;
@@ -2594,12 +2598,48 @@ int launch_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
   return launch_vec<E, kModeSampling>(P, vec, stream, diag);
 }
 
+// ---------------------------------------------------------------------------- the no-alloc entry point
+// sdv_verify_noalloc keeps its workspace in this array instead of the caller's: each GPU the library
+// runs on holds one copy, at its own address, until the process ends.  In host code the name stands
+// for a host-side shadow, not a device address: kernels get the address hipGetSymbolAddress returns
+// for the device that is current, looked up once per device and kept in noalloc_base.
+static __device__ __align__(256) unsigned char scratch[SDV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mutex;
+void* noalloc_base[kMaxDevices];  // the device address of scratch on each device, once looked up
+
+// The address of the current device's copy of scratch, or null (with *status set) on failure.
+void* noalloc_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    *status = SDV_ERR_HIP;
+    return nullptr;
+  }
+  if (dev >= kMaxDevices) {
+    *status = SDV_ERR_LIMIT;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> hold(noalloc_mutex);
+  if (!noalloc_base[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *status = SDV_ERR_HIP;
+      return nullptr;
+    }
+    noalloc_base[dev] = ptr;
+  }
+  return noalloc_base[dev];
+}
+
 // Validation and launch shared by the entry points.  temp_each / seed_each are null for one profile
 // per batch (temperature, seed), else device arrays of B values.
 int verify_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                 const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
                 double temperature, uint64_t seed, const sdv_options* opt, int32_t* accepted_len,
-                int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+                int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag,
+                bool noalloc = false) {
+  const bool counts_room = !noalloc;  // the static scratch holds no top-k / top-p counts
   const sdv_options none{};
   if (!opt) opt = &none;
   const float* temp_each = opt->temperature;
@@ -2609,8 +2649,9 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   if (opt->stop_offsets && (opt->n_stop_tokens < 0 || (opt->n_stop_tokens > 0 && !opt->stop_tokens)))
     return SDV_ERR_INVALID_ARG;
   Layout L;
-  const int shape = make_layout(B, n_draft_rows, V, dtype, &L);
+  const int shape = make_layout(B, n_draft_rows, V, dtype, &L, counts_room);
   if (shape != SDV_OK) return shape;
+  if (!counts_room && (opt->top_k || opt->top_p_milli)) return SDV_ERR_INVALID_ARG;
   if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
   if (n_draft_rows > 0 && !draft_tokens) return SDV_ERR_INVALID_ARG;
   float k2 = 0.0f;  // 0 selects the greedy rule
@@ -2626,6 +2667,13 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
       if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
       if (n_draft_rows > 0 && !have_draft) return SDV_ERR_INVALID_ARG;
     }
+  }
+  if (noalloc) {  // every argument has passed its checks: now the device's static scratch
+    if (L.total > (size_t)SDV_NOALLOC_SCRATCH_BYTES) return SDV_ERR_LIMIT;
+    int status = SDV_OK;
+    workspace = noalloc_scratch(&status);
+    if (!workspace) return status;
+    workspace_bytes = SDV_NOALLOC_SCRATCH_BYTES;
   }
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % kAlign != 0) return SDV_ERR_WORKSPACE;
   const int esize = dtype == SDV_BF16 ? 2 : 4;
@@ -2663,9 +2711,10 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.top_p_milli = opt->top_p_milli;
   P.kept_tokens = opt->kept_tokens;
   P.cuts = reinterpret_cast<Cut*>(ws + L.cuts);
-  P.hist = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist) : nullptr;
-  P.hist_top = dtype == SDV_BF16 ? reinterpret_cast<uint32_t*>(ws + L.hist_top) : nullptr;
-  P.pending = dtype == SDV_BF16 ? reinterpret_cast<int32_t*>(ws + L.pending) : nullptr;
+  const bool bf16_counts = dtype == SDV_BF16 && counts_room;
+  P.hist = bf16_counts ? reinterpret_cast<uint32_t*>(ws + L.hist) : nullptr;
+  P.hist_top = bf16_counts ? reinterpret_cast<uint32_t*>(ws + L.hist_top) : nullptr;
+  P.pending = bf16_counts ? reinterpret_cast<int32_t*>(ws + L.pending) : nullptr;
   P.split = opt->verdict_split;  // 0: chosen at launch
   P.split_mass = reinterpret_cast<double*>(ws + L.split_mass);
   P.split_count = reinterpret_cast<uint32_t*>(ws + L.split_count);
@@ -2682,6 +2731,19 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
 }  // namespace sdv
 
 extern "C" {
+
+size_t sdv_noalloc_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype) {
+  sdv::Layout L;
+  return sdv::make_layout(B, n_draft_rows, V, dtype, &L, false) == SDV_OK ? L.total : 0;
+}
+
+int sdv_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
+                       double temperature, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, void* stream) {
+  return sdv::verify_impl(target_logits, draft_logits, draft_tokens, ragged_offsets, B, n_draft_rows, V, dtype,
+                          temperature, seed, nullptr, accepted_len, out_tokens, nullptr, 0, stream, nullptr, true);
+}
+
 
 size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype) {
   sdv::Layout L;

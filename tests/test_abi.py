@@ -30,7 +30,8 @@ def test_every_declared_function_is_exported(lib):
     names = declared_functions()
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
                           "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms", "sdv_commit",
-                          "sdv_status_string", "sdv_abi_version", "sdv_philox_uniforms"}
+                          "sdv_status_string", "sdv_abi_version", "sdv_philox_uniforms",
+                          "sdv_verify_noalloc", "sdv_noalloc_bytes"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
@@ -162,3 +163,29 @@ def test_commit_host_argument_checks(lib):
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):
     assert lib.sdv_verify_ex(FAKE, FAKE, FAKE, FAKE, 0, 8, 1000, 0, 1.0, 1, FAKE, FAKE, FAKE, 0, None, None) == -1
+
+
+def test_noalloc_host_checks(lib):
+    """sdv_verify_noalloc: argument errors and batches beyond the static scratch return before the
+    device is touched (so these run without a GPU); sdv_noalloc_bytes leaves out the top-k / top-p
+    counts that sdv_workspace_bytes includes."""
+    up = lambda n: -(-n // 256) * 256
+    rows, chunks = 1280 + 1024, 16
+    assert lib.sdv_noalloc_bytes(256, 1024, 128256, 0) == (up(rows * chunks * 8) + up(rows * 8) + up(256 * chunks * 8)
+                                                          + up(256 * 4))
+    assert lib.sdv_noalloc_bytes(256, 1024, 128256, 1) == lib.sdv_workspace_bytes(256, 1024, 128256, 1)
+    assert lib.sdv_noalloc_bytes(0, 10, 10, 0) == 0
+    assert _native.SDV_NOALLOC_SCRATCH_BYTES == 8 << 20
+
+    def call(**kw):
+        a = dict(t=FAKE, d=FAKE, x=FAKE, cu=FAKE, B=4, n_d=8, V=1000, dt=0, T=1.0, seed=1, acc=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.sdv_verify_noalloc(a["t"], a["d"], a["x"], a["cu"], a["B"], a["n_d"], a["V"], a["dt"], a["T"],
+                                      a["seed"], a["acc"], a["out"], None)
+    assert call(dt=5) == -2
+    assert call(B=0) == -1
+    assert call(t=None) == -1
+    assert call(acc=None) == -1
+    assert call(T=float("nan")) == -1
+    assert call(d=None) == -1
+    assert call(B=4096, n_d=60000, V=128256) == -3  # beyond SDV_NOALLOC_SCRATCH_BYTES
