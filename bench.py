@@ -43,8 +43,10 @@ METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=25
 KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
                   "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
 KERNELS = ["row_records", "verdicts"]
+FUSED_KERNELS = ["fused_prologue", "fused_verify"]
 TRUNCATION_KERNELS = ["row_records", "cuts", "verdicts"]  # "cuts": row_cuts_counted, then row_cuts
-TRACE_KERNELS = ["row_records", "row_cuts_counted", "row_cuts", "verdicts", "read_kernel", "philox_kernel"]
+TRACE_KERNELS = ["fused_prologue", "fused_verify", "row_records", "row_cuts_counted", "row_cuts", "verdicts",
+                 "read_kernel", "philox_kernel"]
 CHUNK_BYTES = 16384
 
 
@@ -220,6 +222,9 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (--summarize-pmc)")
     ap.add_argument("--kernel", default="row_records", help="the kernel a counter summary is for (--summarize-pmc)")
     ap.add_argument("--command", default="", help="the command that produced the profile")
+    ap.add_argument("--path", default="auto", choices=["auto", "two-kernel"],
+                    help="auto: the library's choice (the fused path where it applies); two-kernel: always the "
+                         "row pass, then the verdict kernel")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args)
@@ -266,7 +271,11 @@ def main():
             sets[-1]["top_p_milli"] = torch.from_numpy(b.top_p_milli).to(dev)
     B0 = batches[0]
     truncating = B0.top_k is not None
-    kernels = TRUNCATION_KERNELS if truncating else KERNELS
+    # the library runs the fused path for one profile per batch, rows of 16-byte length, draft logits
+    # and no truncation, unless asked for the two-kernel one
+    fused = (args.path == "auto" and not truncating and B0.qrows is None and B0.temp_each is None
+             and (B0.V * B0.elem_bytes) % 16 == 0)
+    kernels = FUSED_KERNELS if fused else (TRUNCATION_KERNELS if truncating else KERNELS)
     positions = [int(b.cu[-1]) for b in batches]
     rows = [int(b.cu[-1]) + b.B for b in batches]
     alg_bytes = [b.algorithmic_bytes() for b in batches]
@@ -282,7 +291,8 @@ def main():
         temperature, seed = (s["temp"], s["seeds"]) if "temp" in s else (b.temperature, b.seed + k)
         sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], temperature, seed,
                       out=outs[k % len(sets)], workspace=ws, events=events, draft_probs=s.get("qrows"),
-                      top_k=s.get("top_k"), top_p_milli=s.get("top_p_milli"))
+                      top_k=s.get("top_k"), top_p_milli=s.get("top_p_milli"),
+                      verdict_path=1 if args.path == "two-kernel" else 0)
 
     # correctness of the timed configuration, once, against the oracle
     parity = None
@@ -320,8 +330,9 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # a second pass with HIP events that the library records on its stream: [0] before the first
-    # kernel, [1] after the row pass, [3] after the truncation kernel (when it runs), [2] after the
-    # verdicts; per-kernel and per-call durations
+    # kernel; two-kernel path: [1] after the row pass, [3] after the truncation kernel (when it runs),
+    # [2] after the verdicts; fused path: [1] after the prologue, [2] after the fused kernel;
+    # per-kernel and per-call durations
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
@@ -373,10 +384,11 @@ def main():
     mean_stream = float(np.mean([stream_bytes[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     value = mean_pos / (ms_step * 1e-3)
     call_gbps = mean_bytes / (ms_step * 1e-3) / 1e9
-    rowpass_gbps = mean_stream / (per_kernel[0] * 1e-3) / 1e9
-    # the roofline object describes the longest kernel with algorithmic bytes of its own: the row
-    # pass, or the truncation kernel when it takes longer
-    roof_kernel, roof_bytes, roof_ms = "row_records", mean_stream, per_kernel[0]
+    stream_ms = per_kernel[1] if fused else per_kernel[0]
+    rowpass_gbps = mean_stream / (stream_ms * 1e-3) / 1e9
+    # the roofline object describes the longest kernel with algorithmic bytes of its own: the fused
+    # kernel, or the row pass, or the truncation kernel when it takes longer
+    roof_kernel, roof_bytes, roof_ms = ("fused_verify" if fused else "row_records"), mean_stream, stream_ms
     if truncating and per_kernel[1] > per_kernel[0]:
         roof_bytes = float(np.mean([truncated_bytes(batches[(args.warmup + k) % len(sets)]) for k in range(args.steps)]))
         roof_kernel, roof_ms = "cuts", per_kernel[1]
@@ -395,7 +407,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if B0.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": B0.name, "B": B0.B, "V": B0.V,
+        "config": {"workload": B0.name, "B": B0.B, "V": B0.V, "path": "fused" if fused else "two-kernel",
                    "temperature": B0.temperature if B0.temp_each is None else
                    {f"{t:g}": int(n) for t, n in zip(*np.unique(B0.temp_each, return_counts=True))},
                    **({} if B0.top_k is None else {"top_k": int(B0.top_k[0]), "top_p_milli": int(B0.top_p_milli[0]),
@@ -417,9 +429,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": roof_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": roof_gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(args.workload, roof_kernel),
                      "kernel": roof_kernel, "algorithmic_bytes_per_launch": roof_bytes,
-                     "frac_of_read_ceiling": roof_gbps / read_gbps},
-        "row_pass": {"achieved_gbps": rowpass_gbps, "frac": rowpass_gbps / PEAK_HBM_GBPS,
-                     "algorithmic_bytes_per_launch": mean_stream},
+                     "frac_of_read_ceiling": roof_gbps / read_gbps,
+                     "call_frac": call_gbps / PEAK_HBM_GBPS},
+        "row_pass": {"kernel": "fused_verify" if fused else "row_records", "achieved_gbps": rowpass_gbps,
+                     "frac": rowpass_gbps / PEAK_HBM_GBPS, "algorithmic_bytes_per_launch": mean_stream},
         "parity": parity,
         "kernel_source_hash": kernel_source_hash(),
     }

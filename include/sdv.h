@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 3
+#define SDV_ABI_VERSION 4
 #define SDV_MAX_DEPTH 64 /* largest K_i a request may carry */
 #define SDV_MAX_EVENTS 4 /* timing hooks in sdv_diag */
 
@@ -74,10 +74,12 @@ typedef enum {
  *   draw_uniform   [B]                 u of the drawn position                        (T > 0)
  *   terminal_kind  [B]                 one of sdv_terminal_kind
  *   events         hipEvent_t handles (cast to void*) recorded on the stream: events[0] before the
- *                  first kernel, events[1] after the row pass (one record per 16 KiB chunk of
- *                  every row read), events[3] after the truncation kernel (top-k / top-p through
- *                  sdv_verify_opts; not recorded when it does not run), events[2] after the verdict
- *                  kernel (per request: fold, accept scan, terminal draw).
+ *                  first kernel; in the two-kernel path events[1] after the row pass (one record per
+ *                  16 KiB chunk of every row read), events[3] after the truncation kernel (top-k /
+ *                  top-p through sdv_verify_opts; not recorded when it does not run), events[2]
+ *                  after the verdict kernel (per request: fold, accept scan, terminal draw); in the
+ *                  fused path (sdv_options.verdict_path) events[1] after the prologue (offsets
+ *                  checked, counters cleared) and events[2] after the fused kernel.
  *   target_logit   [n_draft_rows]      z_target[x_j], the stored target logit at each draft token,
  *                                      widened to binary32 (T > 0)
  *   draft_logit    [n_draft_rows]      z_draft[x_j], the same on the draft row (T > 0, draft logits;
@@ -227,6 +229,12 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
  *                     over the rejected position's rows; every chunk's residual mass is computed
  *                     the same way whichever workgroup computes it, so no output depends on the
  *                     value.  A performance setting, not part of the method.
+ *  verdict_path       0: calls with one profile for the batch, rows of 16-byte length, draft logits
+ *                     and no top-k / top-p run the fused path (one kernel streams the rows and
+ *                     finishes every request while the rest are still being read), other calls the
+ *                     two-kernel path (the stream, then the verdicts); 1: always the two-kernel path;
+ *                     other values -> SDV_ERR_INVALID_ARG.  A verdict_split above 0 also selects the
+ *                     two-kernel path.  Both paths give the same outputs; a performance setting.
  *
  * Emission (SDCP section "Verification and Commit", step 7; "M7.8 - Speculative Serving", section
  * 0x09, "EOS and length-limit stopping"): of the a_i + 1 candidate tokens (the accepted drafts,
@@ -250,6 +258,7 @@ typedef struct sdv_options {
   const int32_t* top_p_milli;
   int32_t* kept_tokens;
   int32_t verdict_split;
+  int32_t verdict_path;
 } sdv_options;
 
 /*

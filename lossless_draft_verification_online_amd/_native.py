@@ -53,6 +53,7 @@ class SdvOptions(ctypes.Structure):
         ("top_p_milli", ctypes.c_void_p),
         ("kept_tokens", ctypes.c_void_p),
         ("verdict_split", ctypes.c_int32),
+        ("verdict_path", ctypes.c_int32),
     ]
 
 

@@ -37,7 +37,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdv_abi_version() == 3
+    assert lib.sdv_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.sdv_status_string(code) not in (None, b"", b"unknown status")
     assert lib.sdv_status_string(17) == b"unknown status"
@@ -53,13 +53,20 @@ def test_workspace_bytes(lib):
     chunks = (128256 + 8191) // 8192
     assert chunks == 16
     rows = 1280 + 1024
+    # then the fused path's state: the request of every draft row, seven counters per request, a
+    # 128-byte task description and 16-aligned chunk masses per request, four global words
+    fused = lambda B, n_d, cs: up(n_d * 4) + up(7 * B * 4) + up(B * 128) + up(B * cs * 8) + up(16)
     assert ws == (up(rows * chunks * 8) + up(rows * 8) + up(rows * chunks * 256) + up(rows * chunks * 4)
-                  + up((rows + 1) * 4) + up(256 * chunks * 8) + up(256 * 4))
+                  + up((rows + 1) * 4) + up(256 * chunks * 8) + up(256 * 4) + fused(256, 1024, 16))
     assert ws % 256 == 0
     # binary32 rows: 4096 logits per chunk, no key counts
     chunks32 = (128256 + 4095) // 4096
     assert lib.sdv_workspace_bytes(256, 1024, 128256, 1) == (up(rows * chunks32 * 8) + up(rows * 8)
-                                                              + up(256 * chunks32 * 8) + up(256 * 4))
+                                                              + up(256 * chunks32 * 8) + up(256 * 4)
+                                                              + fused(256, 1024, 32))
+    # records fill whole 128-byte lines per row: 16 at least
+    assert lib.sdv_workspace_bytes(4, 8, 1000, 1) == (up(20 * 16 * 8) + up(20 * 8) + up(4 * 8) + up(4 * 4)
+                                                      + fused(4, 8, 16))  # 12 target and 8 draft rows
     assert lib.sdv_workspace_bytes(0, 10, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, -1, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, 0, 10, 7) == 0
@@ -171,8 +178,9 @@ def test_noalloc_host_checks(lib):
     counts that sdv_workspace_bytes includes."""
     up = lambda n: -(-n // 256) * 256
     rows, chunks = 1280 + 1024, 16
+    fused = up(1024 * 4) + up(7 * 256 * 4) + up(256 * 128) + up(256 * chunks * 8) + up(16)
     assert lib.sdv_noalloc_bytes(256, 1024, 128256, 0) == (up(rows * chunks * 8) + up(rows * 8) + up(256 * chunks * 8)
-                                                          + up(256 * 4))
+                                                          + up(256 * 4) + fused)
     assert lib.sdv_noalloc_bytes(256, 1024, 128256, 1) == lib.sdv_workspace_bytes(256, 1024, 128256, 1)
     assert lib.sdv_noalloc_bytes(0, 10, 10, 0) == 0
     assert _native.SDV_NOALLOC_SCRATCH_BYTES == 8 << 20
