@@ -43,10 +43,9 @@ METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=25
 KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
                   "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
 KERNELS = ["row_records", "verdicts"]
-FUSED_KERNELS = ["fused_prologue", "fused_verify"]
 TRUNCATION_KERNELS = ["row_records", "cuts", "verdicts"]  # "cuts": row_cuts_counted, then row_cuts
-TRACE_KERNELS = ["fused_prologue", "fused_verify", "row_records", "row_cuts_counted", "row_cuts", "verdicts",
-                 "read_kernel", "philox_kernel"]
+TRACE_KERNELS = ["row_records", "row_cuts_counted", "row_cuts", "verdicts", "read_reg_kernel", "read_lds_kernel",
+                 "read_strided_kernel", "philox_kernel"]
 CHUNK_BYTES = 16384
 
 
@@ -222,14 +221,15 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (--summarize-pmc)")
     ap.add_argument("--kernel", default="row_records", help="the kernel a counter summary is for (--summarize-pmc)")
     ap.add_argument("--command", default="", help="the command that produced the profile")
-    ap.add_argument("--path", default="auto", choices=["auto", "two-kernel"],
-                    help="auto: the library's choice (the fused path where it applies); two-kernel: always the "
-                         "row pass, then the verdict kernel")
+    ap.add_argument("--yardsticks", action="store_true",
+                    help="time the read yardsticks (three read shapes) and torch's fill_ at the workload's size")
     args = ap.parse_args()
     if args.summarize_trace:
         return summarize_trace(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.yardsticks:
+        return yardsticks(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         raise SystemExit("bench.py measures one GPU: the verification step is built and measured on a single "
                          "MI355X. Requests are independent and would shard across GPUs by request with no "
@@ -271,11 +271,7 @@ def main():
             sets[-1]["top_p_milli"] = torch.from_numpy(b.top_p_milli).to(dev)
     B0 = batches[0]
     truncating = B0.top_k is not None
-    # the library runs the fused path for one profile per batch, rows of 16-byte length, draft logits
-    # and no truncation, unless asked for the two-kernel one
-    fused = (args.path == "auto" and not truncating and B0.qrows is None and B0.temp_each is None
-             and (B0.V * B0.elem_bytes) % 16 == 0)
-    kernels = FUSED_KERNELS if fused else (TRUNCATION_KERNELS if truncating else KERNELS)
+    kernels = TRUNCATION_KERNELS if truncating else KERNELS
     positions = [int(b.cu[-1]) for b in batches]
     rows = [int(b.cu[-1]) + b.B for b in batches]
     alg_bytes = [b.algorithmic_bytes() for b in batches]
@@ -291,8 +287,7 @@ def main():
         temperature, seed = (s["temp"], s["seeds"]) if "temp" in s else (b.temperature, b.seed + k)
         sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], temperature, seed,
                       out=outs[k % len(sets)], workspace=ws, events=events, draft_probs=s.get("qrows"),
-                      top_k=s.get("top_k"), top_p_milli=s.get("top_p_milli"),
-                      verdict_path=1 if args.path == "two-kernel" else 0)
+                      top_k=s.get("top_k"), top_p_milli=s.get("top_p_milli"))
 
     # correctness of the timed configuration, once, against the oracle
     parity = None
@@ -330,9 +325,8 @@ def main():
     elapsed = time.perf_counter() - t0
 
     # a second pass with HIP events that the library records on its stream: [0] before the first
-    # kernel; two-kernel path: [1] after the row pass, [3] after the truncation kernel (when it runs),
-    # [2] after the verdicts; fused path: [1] after the prologue, [2] after the fused kernel;
-    # per-kernel and per-call durations
+    # kernel, [1] after the row pass, [3] after the truncation kernel (when it runs), [2] after the
+    # verdicts; per-kernel and per-call durations
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
@@ -384,11 +378,10 @@ def main():
     mean_stream = float(np.mean([stream_bytes[(args.warmup + k) % len(sets)] for k in range(args.steps)]))
     value = mean_pos / (ms_step * 1e-3)
     call_gbps = mean_bytes / (ms_step * 1e-3) / 1e9
-    stream_ms = per_kernel[1] if fused else per_kernel[0]
-    rowpass_gbps = mean_stream / (stream_ms * 1e-3) / 1e9
-    # the roofline object describes the longest kernel with algorithmic bytes of its own: the fused
-    # kernel, or the row pass, or the truncation kernel when it takes longer
-    roof_kernel, roof_bytes, roof_ms = ("fused_verify" if fused else "row_records"), mean_stream, stream_ms
+    rowpass_gbps = mean_stream / (per_kernel[0] * 1e-3) / 1e9
+    # the roofline object describes the longest kernel with algorithmic bytes of its own: the row
+    # pass, or the truncation kernel when it takes longer
+    roof_kernel, roof_bytes, roof_ms = "row_records", mean_stream, per_kernel[0]
     if truncating and per_kernel[1] > per_kernel[0]:
         roof_bytes = float(np.mean([truncated_bytes(batches[(args.warmup + k) % len(sets)]) for k in range(args.steps)]))
         roof_kernel, roof_ms = "cuts", per_kernel[1]
@@ -407,7 +400,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if B0.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": B0.name, "B": B0.B, "V": B0.V, "path": "fused" if fused else "two-kernel",
+        "config": {"workload": B0.name, "B": B0.B, "V": B0.V,
                    "temperature": B0.temperature if B0.temp_each is None else
                    {f"{t:g}": int(n) for t, n in zip(*np.unique(B0.temp_each, return_counts=True))},
                    **({} if B0.top_k is None else {"top_k": int(B0.top_k[0]), "top_p_milli": int(B0.top_p_milli[0]),
@@ -431,8 +424,8 @@ def main():
                      "kernel": roof_kernel, "algorithmic_bytes_per_launch": roof_bytes,
                      "frac_of_read_ceiling": roof_gbps / read_gbps,
                      "call_frac": call_gbps / PEAK_HBM_GBPS},
-        "row_pass": {"kernel": "fused_verify" if fused else "row_records", "achieved_gbps": rowpass_gbps,
-                     "frac": rowpass_gbps / PEAK_HBM_GBPS, "algorithmic_bytes_per_launch": mean_stream},
+        "row_pass": {"achieved_gbps": rowpass_gbps, "frac": rowpass_gbps / PEAK_HBM_GBPS,
+                     "algorithmic_bytes_per_launch": mean_stream},
         "parity": parity,
         "kernel_source_hash": kernel_source_hash(),
     }
@@ -442,6 +435,43 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def yardsticks(args):
+    """Reads with no arithmetic in three shapes (sdv_read_yardstick: 0 the row pass's loads, 1
+    direct-to-LDS loads in two-wave workgroups, 2 a persistent grid with two chunks in flight per
+    wave) and torch's fill_ (writes), each over two rotated buffers of the workload's algorithmic
+    bytes; one JSON line of mean event times and rates."""
+    import torch
+
+    import lossless_draft_verification_online_amd as sdv
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_chunks = make_workload(args.workload, 0).algorithmic_bytes() // CHUNK_BYTES
+    nbytes = n_chunks * CHUNK_BYTES
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    for b in bufs:
+        b.fill_(1)
+    folded = torch.empty(n_chunks, dtype=torch.int32, device=dev)
+    reps = max(args.steps, 10)
+    out = {"yardsticks": args.workload, "bytes": nbytes, "reps": reps}
+    runs = {f"read_shape{s}": (lambda k, s=s: sdv.read_ceiling(bufs[k % 2], folded, shape=s)) for s in range(3)}
+    runs["torch_fill"] = lambda k: bufs[k % 2].fill_(k & 0xff)
+    for name, fn in runs.items():
+        for k in range(10):
+            fn(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(reps):
+            fn(k)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out[name] = {"us": us, "gbps": nbytes / (us * 1e-6) / 1e9}
+        log(f"[yardsticks] {name}: {us:.2f} us, {nbytes / (us * 1e-6) / 1e9:.0f} GB/s")
+    print(json.dumps(out), flush=True)
 
 
 # ----------------------------------------------------------------------------- profile summaries

@@ -74,12 +74,10 @@ typedef enum {
  *   draw_uniform   [B]                 u of the drawn position                        (T > 0)
  *   terminal_kind  [B]                 one of sdv_terminal_kind
  *   events         hipEvent_t handles (cast to void*) recorded on the stream: events[0] before the
- *                  first kernel; in the two-kernel path events[1] after the row pass (one record per
- *                  16 KiB chunk of every row read), events[3] after the truncation kernel (top-k /
- *                  top-p through sdv_verify_opts; not recorded when it does not run), events[2]
- *                  after the verdict kernel (per request: fold, accept scan, terminal draw); in the
- *                  fused path (sdv_options.verdict_path) events[1] after the prologue (offsets
- *                  checked, counters cleared) and events[2] after the fused kernel.
+ *                  first kernel, events[1] after the row pass (one record per 16 KiB chunk of
+ *                  every row read), events[3] after the truncation kernel (top-k / top-p through
+ *                  sdv_verify_opts; not recorded when it does not run), events[2] after the verdict
+ *                  kernel (per request: fold, accept scan, terminal draw).
  *   target_logit   [n_draft_rows]      z_target[x_j], the stored target logit at each draft token,
  *                                      widened to binary32 (T > 0)
  *   draft_logit    [n_draft_rows]      z_draft[x_j], the same on the draft row (T > 0, draft logits;
@@ -229,12 +227,6 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
  *                     over the rejected position's rows; every chunk's residual mass is computed
  *                     the same way whichever workgroup computes it, so no output depends on the
  *                     value.  A performance setting, not part of the method.
- *  verdict_path       0: calls with one profile for the batch, rows of 16-byte length, draft logits
- *                     and no top-k / top-p run the fused path (one kernel streams the rows and
- *                     finishes every request while the rest are still being read), other calls the
- *                     two-kernel path (the stream, then the verdicts); 1: always the two-kernel path;
- *                     other values -> SDV_ERR_INVALID_ARG.  A verdict_split above 0 also selects the
- *                     two-kernel path.  Both paths give the same outputs; a performance setting.
  *
  * Emission (SDCP section "Verification and Commit", step 7; "M7.8 - Speculative Serving", section
  * 0x09, "EOS and length-limit stopping"): of the a_i + 1 candidate tokens (the accepted drafts,
@@ -258,7 +250,6 @@ typedef struct sdv_options {
   const int32_t* top_p_milli;
   int32_t* kept_tokens;
   int32_t verdict_split;
-  int32_t verdict_path;
 } sdv_options;
 
 /*
@@ -333,14 +324,21 @@ int sdv_philox4x32_10(const uint32_t* counters, const uint32_t* keys, int64_t n,
 int sdv_philox_uniforms(uint64_t seed, int32_t B, int32_t P, uint32_t* words, void* stream);
 
 /*
- * Measurement hook: the bandwidth yardstick of the row pass.  Decoding is limited by memory
+ * Measurement hooks: the bandwidth yardsticks of the row pass.  Decoding is limited by memory
  * bandwidth, not arithmetic (SDCP, section "Introduction", its background paragraph; "SOTA-227",
- * section "Why it is free rather than a trade"); this kernel reads n_chunks consecutive 16 KiB
- * chunks of src (device, 16-byte aligned, n_chunks * 16384 bytes) with exactly the row pass's loads
- * and no arithmetic, and writes out[c] (device uint32 [n_chunks]) = the xor of the 4096 words of
- * chunk c.  Its rate is the best a single read-once stream of this shape reaches.  n_chunks < 1,
- * NULL or misaligned pointers -> SDV_ERR_INVALID_ARG.
+ * section "Why it is free rather than a trade"); these kernels read n_chunks consecutive 16 KiB
+ * chunks of src (device, 16-byte aligned, n_chunks * 16384 bytes) with no arithmetic, and write
+ * out[c] (device uint32 [n_chunks]) = the xor of the 4096 words of chunk c.
+ *   shape 0  the row pass's loads: 16-byte non-temporal register loads, one chunk per wave, four
+ *            waves per workgroup (its rate is the best a read-once stream of the row pass's shape
+ *            reaches)
+ *   shape 1  direct-to-LDS loads, one chunk per wave, two waves per workgroup
+ *   shape 2  register loads from a persistent grid (eight 256-thread workgroups per compute unit)
+ *            whose waves stride over the chunks with two chunks in flight
+ * sdv_read_ceiling is shape 0.  n_chunks < 1, a shape outside [0, 2], NULL or misaligned pointers ->
+ * SDV_ERR_INVALID_ARG.
  */
+int sdv_read_yardstick(const void* src, int64_t n_chunks, int32_t shape, uint32_t* out, void* stream);
 int sdv_read_ceiling(const void* src, int64_t n_chunks, uint32_t* out, void* stream);
 
 /*

@@ -104,15 +104,14 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
               draw_uniform: torch.Tensor | None = None, stop_offsets: torch.Tensor | None = None,
               stop_tokens: torch.Tensor | None = None, budget: torch.Tensor | None = None,
               draft_probs: torch.Tensor | None = None, top_k: torch.Tensor | None = None,
-              top_p_milli: torch.Tensor | None = None, verdict_split: int = 0, verdict_path: int = 0):
+              top_p_milli: torch.Tensor | None = None, verdict_split: int = 0):
     """Run sdv_verify_ex; sdv_verify_profiled when temperature and seed are [B] device tensors (one
     sampling profile per request); sdv_verify_opts when the caller's uniforms (float64
     accept_uniform [n_draft_rows], draw_uniform [n_draft_rows + B]), stop lists (int32 CSR
     stop_offsets [B + 1], stop_tokens), a budget (int32 [B]) or draft_probs (float32
     [n_draft_rows, V], the draft distributions in place of draft logits) or the rest of the
     sampling profiles (int32 top_k [B], top_p_milli [B]) or verdict_split (workgroups per request
-    in the verdict pass, 0: automatic) or verdict_path (1: the two-kernel path even where the fused
-    one applies) are given.  Returns (accepted_len,
+    in the verdict pass, 0: automatic) are given.  Returns (accepted_len,
     out_tokens, extra): extra holds the named diagnostic arrays (fields of sdv_diag, and with top-k /
     top-p "kept_tokens", int32 [n_draft_rows + B + n_draft_rows]) and "emitted_len" with stop lists
     or a budget.  ``events``: up to four torch.cuda.Event objects, recorded as sdv_diag.events
@@ -136,7 +135,7 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
     top_p_milli = _device_vector(top_p_milli, torch.int32, B, dev, "top_p_milli")
     truncating = top_k is not None or top_p_milli is not None
     use_opts = (accept_uniform is not None or stop_offsets is not None or budget is not None or draft_probs is not None
-                or truncating or verdict_split != 0 or verdict_path != 0)
+                or truncating or verdict_split != 0)
     n_d = draft_tokens.shape[0]
     V = target.shape[1]
     dt = _DTYPES[target.dtype]
@@ -176,7 +175,6 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
             opt.accept_uniform, opt.draw_uniform = _ptr(accept_uniform), _ptr(draw_uniform)
             opt.draft_probs = _ptr(draft_probs)
             opt.verdict_split = int(verdict_split)
-            opt.verdict_path = int(verdict_path)
             if stop_offsets is not None:
                 opt.stop_offsets, opt.stop_tokens = _ptr(stop_offsets), _ptr(stop_tokens)
                 opt.n_stop_tokens = stop_tokens.shape[0]
@@ -265,9 +263,10 @@ def philox_uniforms(seed: int, B: int, P: int, device="cuda") -> torch.Tensor:
 READ_CHUNK_BYTES = 16384
 
 
-def read_ceiling(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """The row pass's loads with no arithmetic over a contiguous device buffer of whole 16 KiB
-    chunks: returns the xor of each chunk's 32-bit words (int32 view), one per chunk."""
+def read_ceiling(src: torch.Tensor, out: torch.Tensor | None = None, shape: int = 0) -> torch.Tensor:
+    """Reads with no arithmetic over a contiguous device buffer of whole 16 KiB chunks
+    (sdv_read_yardstick; shape 0: the row pass's loads): returns the xor of each chunk's 32-bit words
+    (int32 view), one per chunk."""
     nbytes = src.numel() * src.element_size()
     if not src.is_contiguous() or nbytes % READ_CHUNK_BYTES:
         raise ValueError("read_ceiling needs a contiguous buffer of whole 16 KiB chunks")
@@ -275,9 +274,10 @@ def read_ceiling(src: torch.Tensor, out: torch.Tensor | None = None) -> torch.Te
     if out is None:
         out = torch.empty(n, dtype=torch.int32, device=src.device)
     with torch.cuda.device(src.device):
-        rc = _native.lib().sdv_read_ceiling(_ptr(src), n, _ptr(out), torch.cuda.current_stream(src.device).cuda_stream)
+        rc = _native.lib().sdv_read_yardstick(_ptr(src), n, int(shape), _ptr(out),
+                                              torch.cuda.current_stream(src.device).cuda_stream)
     if rc != 0:
-        raise SdvError(rc, "sdv_read_ceiling")
+        raise SdvError(rc, "sdv_read_yardstick")
     return out
 
 

@@ -53,7 +53,6 @@ class SdvOptions(ctypes.Structure):
         ("top_p_milli", ctypes.c_void_p),
         ("kept_tokens", ctypes.c_void_p),
         ("verdict_split", ctypes.c_int32),
-        ("verdict_path", ctypes.c_int32),
     ]
 
 
@@ -101,6 +100,8 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_philox_uniforms.restype = ctypes.c_int
     L.sdv_philox_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.restype = ctypes.c_char_p
+    L.sdv_read_yardstick.restype = ctypes.c_int
+    L.sdv_read_yardstick.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_read_ceiling.restype = ctypes.c_int
     L.sdv_read_ceiling.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_status_string.argtypes = [ctypes.c_int]

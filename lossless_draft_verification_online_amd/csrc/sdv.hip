@@ -125,7 +125,6 @@ struct Params {
   int32_t* out_tokens;
   float2* part;         // [row slots][Cs] chunk records; target row r is slot r, draft row d slot n_t + d
   int32_t B, n_d, n_t, V, C;
-  int32_t Cs;           // record stride of a row: C in the two-kernel path, C rounded up to 16 in the fused one
   int64_t n_units;
   int64_t lds_records;  // chunk records the verdict kernel can stage in shared memory
   float k2;  // log2(e) / T, or 0 for the greedy rule (one profile for the whole batch)
@@ -148,9 +147,11 @@ struct Params {
   uint32_t* hist_top;         // [row slots][C] the chunk maximum's key, | kNoCounts without counts
   int32_t* pending;           // [1 + row slots] rows the count kernel leaves to row_cuts: count, then slots
   int32_t split;              // verdict workgroups per request (split > 1: the residual pass is shared)
-  int32_t path;               // 0: the fused path where it applies, 1: always the two-kernel path
-  double* split_mass;         // [B][C] residual chunk masses published by the workgroups of a request
-  uint32_t* split_count;      // [B] workgroups of a request done with their masses (zeroed by the row pass)
+  double* split_mass;         // [B][Cm] residual chunk masses of a request's correction, published by the waves or
+                              // workgroups that compute them (each request's on 128-byte lines of their own)
+  uint32_t* split_count;      // [B][kLineWords] masses published per request (zeroed by the row pass), a line each
+  int32_t Cm;                 // C rounded up to 16: a request's masses fill whole 128-byte lines
+  int32_t* batch_ok;          // [1] the offsets are valid (written by the row pass's first workgroup)
   DiagPtrs dg;
 };
 
@@ -202,13 +203,21 @@ __device__ __forceinline__ int32_t request_of_row_wave(const int32_t* cu, int32_
 
 // ============================================================================ offsets
 
-// cu[0] = 0, non-decreasing, cu[B] = n_d.  Anything else rejects the whole batch.
-__device__ __forceinline__ bool offsets_valid(const Params& P, int lane) {
+// cu[0] = 0, non-decreasing, cu[B] = n_d.  Anything else rejects the whole batch.  One wave of the row
+// pass checks this once per call and writes the answer for the verdict kernels.
+__device__ __forceinline__ void screen_offsets(const Params& P, int lane) {
   bool bad = false;
   for (int32_t j = lane; j < P.B; j += kWave) bad |= P.cu[j] > P.cu[j + 1];
   if (lane == 0) bad |= P.cu[0] != 0 || P.cu[P.B] != P.n_d;
-  return __ballot(bad) == 0;
+  const bool ok = __ballot(bad) == 0;
+  if (lane == 0) *P.batch_ok = ok ? 1 : 0;
 }
+
+// Counters that waves on different compute units add to sit one to a 128-byte line: the atomic unit
+// takes a line at a time, so counters sharing a line queue behind each other (measured on MI355X: a
+// stream that counted 36 units on each of 32 counters packed in a line ran 38% slower than one with a
+// counter per line).
+constexpr int kLineWords = 32;
 
 // ============================================================================ 1. the stream
 
@@ -235,6 +244,24 @@ __device__ __forceinline__ void load_chunk(const char* rp, int32_t c0, int32_t n
   const int32_t nvec = n / E::kPerVec;
 #pragma unroll
   for (int k = 0; k < kVecPerLane; ++k) buf[k] = load_vec_nt<E>(vp, lane + kWave * k, nvec);
+}
+
+// The same 16 vectors per lane, moved by direct-to-LDS loads into the wave's 16 KiB slice `lds` and
+// read back (a read yardstick's shape; vectors past the row's end are not loaded and read as -inf).
+constexpr int kCpolNt = 2;  // cache-policy bits of a non-temporal load
+template <class E>
+__device__ __forceinline__ void load_chunk_lds(const char* rp, int32_t c0, int32_t n, int lane, u32x4* lds,
+                                               u32x4 (&buf)[kVecPerLane]) {
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
+  const int32_t nvec = n / E::kPerVec;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k)
+    if (lane + kWave * k < nvec)
+      __builtin_amdgcn_global_load_lds(vp + lane + kWave * k, (lds_ptr)(lds + kWave * k), 16, 0, kCpolNt);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) buf[k] = lane + kWave * k < nvec ? lds[lane + kWave * k] : neg_inf_vec<E>();
 }
 
 // The maximum of a loaded chunk (every lane holds it).
@@ -492,7 +519,8 @@ __device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, 
 }
 
 // Residual mass of one chunk of the rejected row pair: coalesced 16-byte loads, fp32 per vector,
-// fp64 across vectors and lanes.
+// fp64 across vectors and lanes; each half chunk is summed on its own and the halves added, the order
+// of resid_masses_pipelined, so every pass gives a chunk the same mass.
 template <class E, bool kVec, class M>
 __device__ __forceinline__ double resid_chunk_mass(const M& m, const char* tp, const char* dp, int32_t c0, int32_t n,
                                                    float k2, float ref_t, float e_hi, float q_scale, int lane) {
@@ -505,6 +533,7 @@ __device__ __forceinline__ double resid_chunk_mass(const M& m, const char* tp, c
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       asm volatile("" ::: "memory");  // keep the second half's loads after the first half's use
+      double half = 0.0;
       u32x4 tb[kHalf], db[kHalf];
 #pragma unroll
       for (int k = 0; k < kHalf; ++k) {
@@ -520,8 +549,9 @@ __device__ __forceinline__ double resid_chunk_mass(const M& m, const char* tp, c
         const int32_t v0 = c0 + (lane + kWave * (h * kHalf + k)) * E::kPerVec;
 #pragma unroll
         for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
-        acc += (double)tree_sum(ft);
+        half += (double)tree_sum(ft);
       }
+      acc += half;
     }
   } else {
     for (int32_t v = c0 + lane; v < c0 + n; v += kWave)
@@ -539,17 +569,22 @@ __device__ __forceinline__ float temperature_of(const float* temp_each, int32_t 
   return ((const __attribute__((address_space(4))) float*)temp_each)[i];
 }
 
+constexpr int kRowWaves = 4;  // waves per row-pass workgroup
+
 template <class E, int kMode, bool kVec, bool kHist>
-__global__ __launch_bounds__(256) void row_records(Params P) {
+__global__ __launch_bounds__(kWave * kRowWaves) void row_records(Params P) {
   static_assert(!kHist || (E::kBytes == 2 && kVec && kMode != kModeGreedy), "counts: bf16 sampling, 16-byte rows");
   static_assert(kHistKeys == 2 * kWave, "each lane writes one word of two counts");
-  __shared__ uint32_t hcnt[kHist ? 4 : 1][kHist ? kHistKeys + kWave : 1];  // counters, then spares
+  __shared__ uint32_t hcnt_all[kHist ? kRowWaves : 1][kHist ? kHistKeys + kWave : 1];  // counters, then spares
   const int lane = threadIdx.x & (kWave - 1);
   // the unit is wave-uniform; saying so lets the request lookup use scalar loads
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-  if (P.split > 1 && blockIdx.x == 0)  // the verdict workgroups of a request count up from zero
-    for (int32_t j = threadIdx.x; j < P.B; j += blockDim.x) P.split_count[j] = 0u;
+  uint32_t* hcnt = hcnt_all[kHist ? wave : 0];
+  if (blockIdx.x == 0) {  // once per call: the offsets, and the verdicts' counters from zero
+    if (wave == 0) screen_offsets(P, lane);
+    for (int32_t j = threadIdx.x; j < P.B; j += blockDim.x) P.split_count[(int64_t)j * kLineWords] = 0u;
+  }
   if (u >= P.n_units) return;
   const int32_t slot = (int32_t)(u / P.C);
   const int32_t c = (int32_t)(u - (int64_t)slot * P.C);
@@ -562,7 +597,7 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
   if constexpr (kHist && kMode != kModeProfiled) {
     u32x4 buf[kVecPerLane];
     load_chunk<E>(rp, c0, n, lane, buf);
-    rec = record_counting(buf, P.k2, lane, hcnt[wave], P.hist + u * (kHistKeys / 2), P.hist_top + u);
+    rec = record_counting(buf, P.k2, lane, hcnt, P.hist + u * (kHistKeys / 2), P.hist_top + u);
   } else if constexpr (kMode != kModeProfiled) {
     rec = chunk_record<E, kMode == kModeGreedy, kVec>(rp, c0, n, P.k2, lane);
   } else {
@@ -578,7 +613,7 @@ __global__ __launch_bounds__(256) void row_records(Params P) {
         load_chunk<E>(rp, c0, n, lane, buf);
       }
       if constexpr (kHist)
-        rec = k2 > 0.0f ? record_counting(buf, k2, lane, hcnt[wave], P.hist + u * (kHistKeys / 2), P.hist_top + u)
+        rec = k2 > 0.0f ? record_counting(buf, k2, lane, hcnt, P.hist + u * (kHistKeys / 2), P.hist_top + u)
                         : record_of<E, true>(buf, c0, 0.0f, lane);
       else
         rec = k2 > 0.0f ? record_of<E, false>(buf, c0, k2, lane) : record_of<E, true>(buf, c0, 0.0f, lane);
@@ -2042,7 +2077,7 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   // screening: every wave reaches the same answer from the same loads
   // the request's offsets load beside the batch-wide screening (i < B: both are in bounds)
   const int32_t lo_raw = P.cu[i], hi_raw = P.cu[i + 1];
-  const bool ok_offsets = offsets_valid(P, lane);
+  const bool ok_offsets = *P.batch_ok != 0;
   const int32_t lo = ok_offsets ? lo_raw : 0, hi = ok_offsets ? hi_raw : 0;
   const int K = hi - lo;
   const int32_t trow0 = lo + i, drow0 = lo;
@@ -2322,11 +2357,11 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     // L2s are not coherent with this one's) and counts; nothing waits on another workgroup.
     __shared__ int32_t last;
     if (wave == 0) {
-      double* pub = P.split_mass + (int64_t)i * P.C;
+      double* pub = P.split_mass + (int64_t)i * P.Cm;
       for (int32_t c = c_lo + lane; c < c_hi; c += kWave) pub[c] = lds_mass[c];
       __threadfence();
       uint32_t before = 0u;
-      if (lane == 0) before = atomicAdd(&P.split_count[i], 1u);
+      if (lane == 0) before = atomicAdd(&P.split_count[(int64_t)i * kLineWords], 1u);
       const bool is_last = lane_value(before, 0) == (uint32_t)(n_split - 1);
       if (is_last) {
         __threadfence();
@@ -2419,652 +2454,6 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   write_token(y, empty, S);
 }
 
-// ============================================================================ 4. the fused path
-// One launch streams every row and finishes each request while the rest of the batch is still
-// being read, so the verdicts and the correction passes overlap the stream instead of following it.
-//
-//  fused_prologue  one workgroup: validates the offsets once, maps every draft row to its request,
-//                  and clears the counters below.
-//  fused_verify    waves, each on its own (no barrier, no wait on another wave):
-//   * stream units, request by request: the target and draft chunks of each draft position, then
-//     the bonus rows of every request at the end.  Each unit publishes its chunk record and counts
-//     itself on its request; the wave that completes a request's draft positions decides it (fold,
-//     accept scan, greedy token), and the wave that completes a bonus row meets the decision there.
-//   * a correction (first rejection t) is posted as a task whose chunks any wave may take: the
-//     residual mass of one chunk of the rejected row pair.  The poster takes chunks of its own task
-//     until none is left, so a task never depends on another wave showing up; every stream wave,
-//     and a set of helper waves at the end of the grid, takes chunks of open tasks before it ends.
-//     The wave that completes a task's last chunk picks the chunk holding u * S and searches it.
-//   * a bonus draw (every draft accepted) needs no residual pass: whichever of the decider and the
-//     bonus row's last unit comes second draws from the bonus row's records.
-//
-// Waves hand data to waves that may run on other XCDs, whose L2s are not coherent with each other:
-// everything handed over (records, decisions, task descriptions, chunk masses) is stored with
-// device-scope relaxed atomic stores (written through to the coherent level), the storing wave
-// waits for those stores to complete (vmcnt 0) before it counts itself on a device-scope atomic
-// counter, and the wave that reads the handed-over data does so with device-scope atomic loads after
-// its own count told it the data is complete.  No L2-wide fence is issued.  Such a load is fresh only
-// if the reader's L2 holds no older copy of the line, so nothing handed over shares a 128-byte line
-// with data that changes later in the call: records are laid out 16 to a row (one line per row of up
-// to 16 chunks), chunk masses likewise, a task description fills a line, and the small per-request
-// flags read after a hand-over (decision kind, task ready) are read by atomic read-modify-writes,
-// which resolve at the coherent level.
-
-constexpr int kFusedStealTries = 2;    // chunk takes a stream wave attempts before it ends
-constexpr int kFusedHelperTries = 48;  // the same for a helper wave
-constexpr int kFusedHelperWaves = 1024;
-
-// A correction as its decider posts it: the rejected position a of request i and the weights' frame.
-struct FusedTask {
-  int32_t i, a;
-  float ref_t, e_hi;
-  float q_scale;
-  int32_t pad;
-  double u, l2_t;
-};
-
-constexpr int kTaskWords = 16;  // a task description per 128-byte line
-static_assert(sizeof(FusedTask) <= 8 * kTaskWords, "a task description fits its line");
-
-struct FusedState {
-  int32_t* req_of_pair;        // [n_d] the request of every draft row (prologue)
-  uint32_t* req_count;         // [B] stream units done of the request's draft positions
-  uint32_t* bonus_count;       // [B] stream units done of the request's bonus row
-  uint32_t* gate;              // [B] the decider and the bonus row's last unit meet here
-  int32_t* kind;               // [B] the decision's terminal kind, read by the second at the gate
-  uint64_t* tasks;             // [B][kTaskWords] posted corrections
-  uint32_t* ready;             // [B] task k is fully posted
-  uint32_t* next_chunk;        // [B] chunks of task k taken so far (never above C)
-  uint32_t* done_chunks;       // [B] chunks of task k whose masses are published
-  double* mass;                // [B][Cs] residual chunk masses of each task
-  uint32_t* globals;           // [0] tasks posted, [1] the first task that may have chunks left, [2] batch ok
-};
-
-__device__ __forceinline__ void publish(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t fetch(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t fetch(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish_f2(float2* p, float2 v) {
-  publish(reinterpret_cast<uint64_t*>(p), ((uint64_t)__float_as_uint(v.y) << 32) | __float_as_uint(v.x));
-}
-__device__ __forceinline__ float2 fetch_f2(const float2* p) {
-  const uint64_t b = fetch(reinterpret_cast<const uint64_t*>(p));
-  return make_float2(__uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
-}
-__device__ __forceinline__ void publish_f64(double* p, double v) {
-  publish(reinterpret_cast<uint64_t*>(p), (uint64_t)__double_as_longlong(v));
-}
-__device__ __forceinline__ double fetch_f64(const double* p) {
-  return __longlong_as_double((long long)fetch(reinterpret_cast<const uint64_t*>(p)));
-}
-// Every store this wave has issued is complete (and, for the atomic stores above, coherent).
-__device__ __forceinline__ void stores_complete() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Lane 0 adds one to a device-scope counter; every lane gets the value before the add.
-__device__ __forceinline__ uint32_t count_on(uint32_t* p, int lane) {
-  uint32_t before = 0u;
-  if (lane == 0) before = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return lane_value(before, 0);
-}
-// A flag read at the coherent level (an atomic or of 0).
-__device__ __forceinline__ uint32_t fetch_coherent(uint32_t* p) {
-  return __hip_atomic_fetch_or(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t swap_if(uint32_t* p, uint32_t expect, uint32_t want) {
-  __hip_atomic_compare_exchange_strong(p, &expect, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return expect;  // the value found
-}
-// A wave-uniform 32-bit load through the scalar cache (read-only inputs only).
-__device__ __forceinline__ int32_t scalar_at(const int32_t* p, int64_t k) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[k];
-}
-
-// ---------------------------------------------------------------------------- prologue
-
-__global__ __launch_bounds__(1024) void fused_prologue(Params P, FusedState F) {
-  const int t = threadIdx.x;
-  bool bad = false;
-  for (int32_t j = t; j < P.B; j += blockDim.x) bad |= P.cu[j] > P.cu[j + 1];
-  if (t == 0) bad |= P.cu[0] != 0 || P.cu[P.B] != P.n_d;
-  const bool ok = !__syncthreads_or(bad);
-  for (int32_t j = t; j < P.B; j += blockDim.x) {
-    F.req_count[j] = 0u;
-    F.bonus_count[j] = 0u;
-    F.gate[j] = 0u;
-    F.ready[j] = 0u;
-    F.next_chunk[j] = 0u;
-    F.done_chunks[j] = 0u;
-    if (ok)
-      for (int32_t d = P.cu[j]; d < P.cu[j + 1]; ++d) F.req_of_pair[d] = j;
-  }
-  if (t == 0) {
-    F.globals[0] = 0u;
-    F.globals[1] = 0u;
-    F.globals[2] = ok ? 1u : 0u;
-  }
-}
-
-// ---------------------------------------------------------------------------- row folds from published records
-
-// Folds rows 0 .. n_rows-1 of a request (slot_of(r) gives row r's record slot) into rows[r], by one
-// wave: rows of at most 16 (32) chunks four (two) to an instruction, wider rows one at a time.
-template <bool kGreedy, class SlotOf>
-__device__ __forceinline__ void fold_published(const Params& P, int n_rows, SlotOf slot_of, RowFold* rows, int lane) {
-  auto rec = [&](int r, int32_t c) { return fetch_f2(P.part + (int64_t)slot_of(r) * P.Cs + c); };
-  if (P.C <= 32) {
-    const int lanes = P.C <= 16 ? 16 : 32, per = kWave / lanes;
-    const int g = lane / lanes, c = lane % lanes;
-    // records of up to eight instructions' rows are loaded before any is folded
-    for (int r0 = 0; r0 < n_rows; r0 += 8 * per) {
-      float2 v[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int r = r0 + s * per + g;
-        v[s] = r < n_rows && c < P.C ? rec(r, c) : make_float2(-INFINITY, kGreedy ? __int_as_float(INT32_MAX) : 0.0f);
-      }
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        if (r0 + s * per >= n_rows) break;
-        const int r = r0 + s * per + g;
-        RowFold f{0.0, -INFINITY, 0};
-        if constexpr (kGreedy) {
-          float best = v[s].x;
-          int32_t idx = __float_as_int(v[s].y);
-          if (lanes == 16) row16_argmax(best, idx);
-          else half_argmax(best, idx);
-          f.argmax = idx == INT32_MAX ? 0 : idx;
-        } else {
-          f = lanes == 16 ? fold_row_narrow<16>(v[s]) : fold_row_narrow<32>(v[s]);
-        }
-        if (c == 0 && r < n_rows) rows[r] = f;
-      }
-    }
-  } else {
-    for (int r = 0; r < n_rows; ++r) {
-      RowFold f{0.0, -INFINITY, 0};
-      if constexpr (kGreedy) {
-        float best = -INFINITY;
-        int32_t idx = INT32_MAX;
-        for (int32_t c = lane; c < P.C; c += kWave) {
-          const float2 x = rec(r, c);
-          const int32_t xi = __float_as_int(x.y);
-          if (x.x > best || (x.x == best && xi < idx)) {
-            best = x.x;
-            idx = xi;
-          }
-        }
-        wave_argmax(best, idx);
-        f.argmax = idx == INT32_MAX ? 0 : idx;
-      } else {
-        float R = -INFINITY;
-        for (int32_t c = lane; c < P.C; c += kWave) R = fmaxf(R, rec(r, c).x);
-        R = wave_max(R);
-        f.ref = R;
-        if (R == -INFINITY) {
-          f.l2 = -(double)INFINITY;
-        } else {
-          double s = 0.0;
-          for (int32_t c = lane; c < P.C; c += kWave) {
-            const float2 x = rec(r, c);
-            if (x.y > 0.0f) s += (double)x.y * exp2((double)x.x - (double)R);
-          }
-          f.l2 = (double)R + log2(wave_sum(s));
-        }
-      }
-      if (lane == 0) rows[r] = f;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();  // a wave's shared-memory accesses complete in order
-}
-
-// ---------------------------------------------------------------------------- the in-chunk search by one wave
-
-// Inverse CDF inside one chunk (16-byte aligned rows) by one wave: the chunk's vectors form rows of
-// 64 (vector k*64 + l in lane l); the row sums (fp64 over the lanes) are scanned in lane order to
-// pick the row, the lanes' vector sums of that row to pick the vector, and the vector is walked.
-// The same quantities in the same order as the workgroup search of the two-kernel path.  If
-// rounding leaves the target unreached, the last element of positive weight is taken.
-template <class E, bool kResid, class M>
-__device__ __forceinline__ int32_t search_chunk_wave(const M& m, const char* trow, const char* drow, int32_t c0,
-                                                     int32_t n, double target, float k2, float ref_t, float e_hi,
-                                                     float q_scale, int lane) {
-  constexpr int kRows = kVecPerLane;
-  const int32_t nvec = n / E::kPerVec;
-  const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
-  const u32x4* dv = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)c0 * E::kBytes);
-  auto weights = [&](const u32x4& t, const u32x4& dd, int32_t v0, float (&w)[E::kPerVec]) {
-    float ft[E::kPerVec], fd[E::kPerVec];
-    E::unpack(t, ft);
-    if constexpr (kResid) E::unpack(dd, fd);
-#pragma unroll
-    for (int q = 0; q < E::kPerVec; ++q)
-      w[q] = kResid ? resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale) : p_weight(m, ft[q], v0 + q, k2, ref_t);
-  };
-  float vs[kRows];
-  double rsum = 0.0;  // lane k < kRows ends with row k's sum
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {  // two halves of eight rows keep the loads of a half in flight
-    constexpr int kH = kRows / 2;
-    u32x4 t[kH], dd[kH];
-#pragma unroll
-    for (int k = 0; k < kH; ++k) {
-      const int vi = (h * kH + k) * kWave + lane;
-      t[k] = load_vec<E>(tv, vi, nvec);
-      dd[k] = kResid ? load_vec<E>(dv, vi, nvec) : t[k];
-    }
-#pragma unroll
-    for (int k = 0; k < kH; ++k) {
-      float w[E::kPerVec];
-      weights(t[k], dd[k], c0 + ((h * kH + k) * kWave + lane) * E::kPerVec, w);
-      vs[h * kH + k] = tree_sum(w);
-      const double rs = wave_sum((double)vs[h * kH + k]);
-      if (lane == h * kH + k) rsum = rs;
-    }
-  }
-  const double rex = wave_exclusive_scan(lane < kRows ? rsum : 0.0, lane);
-  const uint64_t rhit = __ballot(lane < kRows && rex + rsum > target);
-  const uint64_t rpos = __ballot(lane < kRows && rsum > 0.0);
-  if (!rhit && !rpos) return c0 + n - 1;
-  const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
-  const double rest = target - lane_value(rex, kr);
-  float v = vs[0];  // kr is uniform: selects, not an indexed register array
-#pragma unroll
-  for (int k = 1; k < kRows; ++k)
-    if (k == kr) v = vs[k];
-  const double vex = wave_exclusive_scan((double)v, lane);
-  const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
-  const uint64_t vpos = __ballot(v > 0.0f);
-  const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
-  // the chosen row again (its lines were just read): every lane recomputes its vector's weights
-  const int vi = kr * kWave + lane;
-  const int32_t base = c0 + vi * E::kPerVec;
-  float w[E::kPerVec];
-  weights(load_vec<E>(tv, vi, nvec), kResid ? load_vec<E>(dv, vi, nvec) : neg_inf_vec<E>(), base, w);
-  int32_t yl = base + E::kPerVec - 1;
-  int32_t last_pos = -1;
-  double upto = vex;
-  bool found = false;
-#pragma unroll
-  for (int q = 0; q < E::kPerVec; ++q) {
-    upto += (double)w[q];
-    if (w[q] > 0.0f) last_pos = base + q;
-    if (!found && upto > rest) {
-      yl = base + q;
-      found = true;
-    }
-  }
-  if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
-  return lane_value(yl, l);
-}
-
-// ---------------------------------------------------------------------------- terminal draws
-
-// The token of request i at target row trow: every lane writes nothing but lane 0.
-__device__ __forceinline__ void fused_write_token(const Params& P, int32_t i, int32_t trow, int32_t y, int kind,
-                                                  double u, double S_frame, float ref_t, double l2_t, int lane) {
-  if (lane != 0) return;
-  P.out_tokens[trow] = y;
-  if (P.dg.draw_uniform) P.dg.draw_uniform[i] = (float)u;
-  if (P.dg.terminal_kind) P.dg.terminal_kind[i] = kind;
-  if (P.dg.terminal_mass) P.dg.terminal_mass[i] = S_frame * exp2((double)ref_t - l2_t);
-}
-
-// A draw from p at target row trow (bonus, or a correction whose residual came out empty), by one
-// wave: chunk masses from the row's published records, then the in-chunk search.
-template <class E>
-__device__ __forceinline__ void fused_draw_p(const Params& P, int32_t i, int32_t trow, float k2, double u,
-                                             float ref_t, double l2_t, int kind, int lane) {
-  const float2* rec = P.part + (int64_t)trow * P.Cs;
-  double tgt = 0.0, S = 0.0;
-  float2 mine = lane < P.C ? fetch_f2(rec + lane) : make_float2(-INFINITY, 0.0f);
-  auto mass = [&](int32_t c) {
-    const float2 r = c < kWave ? mine : fetch_f2(rec + c);
-    return (double)r.y * exp2((double)r.x - (double)ref_t);
-  };
-  const int32_t cs = pick_chunk(P.C, u, mass, &tgt, &S, lane);
-  const int32_t s0 = cs * E::kChunk;
-  const char* tp = row_ptr<E>(P.target, trow, P.V);
-  const int32_t y =
-      search_chunk_wave<E, false>(NoCut{}, tp, nullptr, s0, min(E::kChunk, P.V - s0), tgt, k2, ref_t, 0.0f, 0.0f, lane);
-  fused_write_token(P, i, trow, y, kind, u, S, ref_t, l2_t, lane);
-}
-
-// The bonus draw (sampling) or bonus token (greedy) of request i with K drafts, by one wave.
-template <class E, bool kGreedy>
-__device__ __forceinline__ void fused_bonus(const Params& P, int32_t i, int K, RowFold* rows, int lane) {
-  const int32_t trow = P.cu[i] + i + K;
-  fold_published<kGreedy>(P, 1, [&](int) { return trow; }, rows, lane);
-  const RowFold f = rows[0];
-  if constexpr (kGreedy) {
-    if (lane == 0) {
-      P.out_tokens[trow] = f.argmax;
-      if (P.dg.target_argmax) P.dg.target_argmax[trow] = f.argmax;
-      if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_GREEDY;
-    }
-  } else {
-    if (P.dg.target_lse && lane == 0) P.dg.target_lse[trow] = f.l2 * kLn2;
-    const double u = P.u_each ? P.u_each[trow] : (double)draw_uniform(verifier_block(P.seed, (uint32_t)i, (uint32_t)K));
-    fused_draw_p<E>(P, i, trow, P.k2, u, f.ref, f.l2, SDV_TERM_BONUS, lane);
-  }
-}
-
-// The diagnostics of the bonus row alone (a request decided without drawing there).
-template <bool kGreedy>
-__device__ __forceinline__ void fused_bonus_diag(const Params& P, int32_t i, int K, RowFold* rows, int lane) {
-  if (!(kGreedy ? P.dg.target_argmax != nullptr : P.dg.target_lse != nullptr)) return;
-  const int32_t trow = P.cu[i] + i + K;
-  fold_published<kGreedy>(P, 1, [&](int) { return trow; }, rows, lane);
-  if (lane == 0) {
-    if constexpr (kGreedy) P.dg.target_argmax[trow] = rows[0].argmax;
-    else P.dg.target_lse[trow] = rows[0].l2 * kLn2;
-  }
-}
-
-// ---------------------------------------------------------------------------- correction tasks
-
-// Takes the next chunk of task k, or returns -1 when every chunk is taken.  The count never passes
-// C, and each failed exchange means another wave took a chunk, so the loop ends.
-__device__ __forceinline__ int32_t take_chunk(const Params& P, const FusedState& F, uint32_t k, int lane) {
-  uint32_t got = 0xffffffffu;
-  if (lane == 0) {
-    uint32_t c = fetch(F.next_chunk + k);
-    while (c < (uint32_t)P.C) {
-      const uint32_t found = swap_if(F.next_chunk + k, c, c + 1u);
-      if (found == c) {
-        got = c;
-        break;
-      }
-      c = found;
-    }
-  }
-  return (int32_t)lane_value(got, 0);
-}
-
-// Publishes a correction; returns its task index.
-__device__ __forceinline__ uint32_t post_task(const FusedState& F, const FusedTask& t, int lane) {
-  const uint32_t k = count_on(F.globals + 0, lane);
-  if (lane == 0) {
-    uint64_t* dst = F.tasks + (int64_t)k * kTaskWords;
-    const uint64_t* src = reinterpret_cast<const uint64_t*>(&t);
-#pragma unroll
-    for (int w = 0; w < (int)(sizeof(FusedTask) / 8); ++w) publish(dst + w, src[w]);
-  }
-  stores_complete();
-  if (lane == 0) publish(F.ready + k, 1u);
-  return k;
-}
-
-__device__ __forceinline__ FusedTask read_task(const FusedState& F, uint32_t k) {
-  FusedTask t;
-  uint64_t* dst = reinterpret_cast<uint64_t*>(&t);
-  const uint64_t* src = F.tasks + (int64_t)k * kTaskWords;
-#pragma unroll
-  for (int w = 0; w < (int)(sizeof(FusedTask) / 8); ++w) dst[w] = fetch(src + w);
-  return t;
-}
-
-// The correction draw of task k once every chunk mass is published, by the wave that published the
-// last one.
-template <class E>
-__device__ __forceinline__ void finish_task(const Params& P, const FusedState& F, uint32_t k, const FusedTask& t,
-                                            int lane) {
-  const int32_t trow = P.cu[t.i] + t.i + t.a, drow = P.cu[t.i] + t.a;
-  const double* ms = F.mass + (int64_t)k * P.Cs;
-  const double mine = lane < P.C ? fetch_f64(ms + lane) : 0.0;
-  auto mass = [&](int32_t c) { return c < kWave ? mine : fetch_f64(ms + c); };
-  double S = 0.0;
-  for (int32_t c0 = 0; c0 < P.C; c0 += kWave) S += wave_sum(c0 + lane < P.C ? mass(c0 + lane) : 0.0);
-  if (!(S > 0.0)) {  // no positive residual weight in floating point: draw from p_t
-    fused_draw_p<E>(P, t.i, trow, P.k2, t.u, t.ref_t, t.l2_t, SDV_TERM_RESIDUAL_EMPTY, lane);
-    return;
-  }
-  double tgt = 0.0;
-  const int32_t cs = pick_chunk(P.C, t.u, mass, &tgt, &S, lane);
-  const int32_t s0 = cs * E::kChunk;
-  const int32_t y = search_chunk_wave<E, true>(NoCut{}, row_ptr<E>(P.target, trow, P.V), row_ptr<E>(P.draft, drow, P.V),
-                                               s0, min(E::kChunk, P.V - s0), tgt, P.k2, t.ref_t, t.e_hi, t.q_scale, lane);
-  fused_write_token(P, t.i, trow, y, SDV_TERM_RESIDUAL, t.u, S, t.ref_t, t.l2_t, lane);
-}
-
-// Residual mass of chunk c of task k, published; the wave that completes the task draws.
-template <class E>
-__device__ __forceinline__ void run_chunk(const Params& P, const FusedState& F, uint32_t k, const FusedTask& t,
-                                          int32_t c, int lane) {
-  const int32_t trow = P.cu[t.i] + t.i + t.a, drow = P.cu[t.i] + t.a;
-  const int32_t c0 = c * E::kChunk;
-  const double cm = resid_chunk_mass<E, true>(NoCut{}, row_ptr<E>(P.target, trow, P.V), row_ptr<E>(P.draft, drow, P.V),
-                                              c0, min(E::kChunk, P.V - c0), P.k2, t.ref_t, t.e_hi, t.q_scale, lane);
-  if (lane == 0) publish_f64(F.mass + (int64_t)k * P.Cs + c, cm);
-  stores_complete();
-  if (count_on(F.done_chunks + k, lane) == (uint32_t)P.C - 1u) finish_task<E>(P, F, k, t, lane);
-}
-
-// Takes chunks of the oldest open task, up to `tries` times; ends as soon as no posted task has a
-// chunk left.
-template <class E>
-__device__ __forceinline__ void steal(const Params& P, const FusedState& F, int tries, int lane) {
-  for (int n = 0; n < tries; ++n) {
-    const uint32_t k = lane_value(lane == 0 ? fetch(F.globals + 1) : 0u, 0);
-    const uint32_t posted = lane_value(lane == 0 ? fetch(F.globals + 0) : 0u, 0);
-    if (k >= posted) return;
-    if (lane_value(lane == 0 ? fetch_coherent(F.ready + k) : 0u, 0) == 0u) return;  // still being posted
-    const int32_t c = take_chunk(P, F, k, lane);
-    if (c < 0) {  // every chunk of k is taken: move the cursor on (whoever sees it first)
-      if (lane == 0) swap_if(F.globals + 1, k, k + 1u);
-      continue;
-    }
-    const FusedTask t = read_task(F, k);
-    run_chunk<E>(P, F, k, t, c, lane);
-  }
-}
-
-// ---------------------------------------------------------------------------- the decision
-
-// Decides request i once all of its draft positions are streamed, by one wave (rows: the wave's
-// shared-memory slice).  Rules, uniforms and outputs are those of the two-kernel verdict pass.
-template <class E, bool kGreedy>
-__device__ __forceinline__ void fused_decide(const Params& P, const FusedState& F, int32_t i, RowFold* rows, int lane) {
-  const int32_t lo = P.cu[i], hi = P.cu[i + 1];
-  const int K = hi - lo;
-  const int32_t trow0 = lo + i, drow0 = lo;
-  auto meet = [&](int kind) {  // publish the decision, then meet the bonus row's last unit
-    if (lane == 0) publish(reinterpret_cast<uint32_t*>(F.kind) + i, (uint32_t)kind);
-    stores_complete();
-    if (count_on(F.gate + i, lane) == 1u) {  // the bonus row is complete
-      if (kind == SDV_TERM_BONUS) fused_bonus<E, kGreedy>(P, i, K, rows, lane);
-      else if (kind != SDV_TERM_BAD) fused_bonus_diag<kGreedy>(P, i, K, rows, lane);
-    }
-  };
-  if (K > SDV_MAX_DEPTH) {  // the depth limit: no slot written
-    write_reject(P, i, 0, 0, false, lane);
-    return meet(SDV_TERM_BAD);
-  }
-  if (!stop_list_valid(P, i)) {
-    write_reject(P, i, trow0, K, true, lane);
-    return meet(SDV_TERM_BAD);
-  }
-  // fold the target rows (0 .. K-1) and, sampling, the draft rows (K .. 2K-1); meanwhile the
-  // tokens and the logits at them load
-  const bool active = lane < K;
-  int32_t x = 0;
-  float zt = 0.0f, zd = 0.0f;
-  if (active) {
-    x = P.tokens[drow0 + lane];
-    if constexpr (!kGreedy) {
-      if (x >= 0 && x < P.V) {
-        zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
-        zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
-      }
-    }
-  }
-  fold_published<kGreedy>(P, kGreedy ? K : 2 * K,
-                          [&](int r) { return r < K ? trow0 + r : P.n_t + drow0 + (r - K); }, rows, lane);
-  if (__ballot(active && (x < 0 || x >= P.V)) != 0) {
-    write_reject(P, i, trow0, K, true, lane);
-    return meet(SDV_TERM_BAD);
-  }
-  if constexpr (kGreedy) {
-    const int32_t g = active ? rows[lane].argmax : 0;
-    const uint64_t miss = __ballot(active && x != g);
-    const int a = miss ? __ffsll((unsigned long long)miss) - 1 : K;
-    const int n_emit = emitted_count(P, i, x, a, lane);
-    const bool frontier = n_emit == a + 1;
-    for (int j = lane; j <= K; j += kWave)
-      if (j != K || !frontier || a < K) P.out_tokens[trow0 + j] = j >= n_emit ? -1 : (j < a ? x : rows[a].argmax);
-    if (P.dg.target_argmax && active) P.dg.target_argmax[trow0 + lane] = rows[lane].argmax;
-    if (lane == 0) {
-      P.accepted_len[i] = a;
-      if (P.emitted_len) P.emitted_len[i] = n_emit;
-      if (P.dg.terminal_kind && (!frontier || a < K))
-        P.dg.terminal_kind[i] = frontier ? SDV_TERM_GREEDY : SDV_TERM_NONE;
-    }
-    return meet(frontier && a == K ? SDV_TERM_BONUS : SDV_TERM_GREEDY);
-  } else {
-    RowFold ft{0.0, 0.0f, 0}, fd{0.0, 0.0f, 0};
-    double ratio = 0.0, r = 1.0;
-    bool accept = true;
-    Philox4 blk{0u, 0u, 0u, 0u};
-    if (active) {
-      ft = rows[lane];
-      fd = rows[K + lane];
-      ratio = exp2(((double)zt - (double)zd) * (double)P.k2 - (ft.l2 - fd.l2));
-      if (P.r_each) {  // the caller's r in [0, 1): SDCP Rule 2, r < p/q
-        r = P.r_each[drow0 + lane];
-        accept = r < ratio;
-      } else {  // Philox r in (0, 1]: r <= p/q
-        blk = verifier_block(P.seed, (uint32_t)i, (uint32_t)lane);
-        r = (double)accept_uniform(blk);
-        accept = r <= ratio;
-      }
-    }
-    if (__ballot(active && zd == -INFINITY) != 0) {  // q(x) = 0: rejected before any uniform is used
-      write_reject(P, i, trow0, K, true, lane);
-      return meet(SDV_TERM_BAD);
-    }
-    const uint64_t rej = __ballot(active && !accept);
-    const int a = rej ? __ffsll((unsigned long long)rej) - 1 : K;
-    const int n_emit = emitted_count(P, i, x, a, lane);
-    const bool frontier = n_emit == a + 1;
-    for (int j = lane; j <= K; j += kWave)
-      if (j != a || !frontier) P.out_tokens[trow0 + j] = j < a && j < n_emit ? x : -1;
-    if (lane == 0) {
-      P.accepted_len[i] = a;
-      if (P.emitted_len) P.emitted_len[i] = n_emit;
-      if (!frontier && P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_NONE;
-    }
-    if (active) {
-      if (P.dg.target_lse) P.dg.target_lse[trow0 + lane] = ft.l2 * kLn2;
-      if (P.dg.draft_lse) P.dg.draft_lse[drow0 + lane] = fd.l2 * kLn2;
-      if (P.dg.ratio) P.dg.ratio[drow0 + lane] = ratio;
-      if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + lane] = (float)r;
-      if (P.dg.target_logit) P.dg.target_logit[drow0 + lane] = zt;
-      if (P.dg.draft_logit) P.dg.draft_logit[drow0 + lane] = zd;
-    }
-    if (!frontier) return meet(SDV_TERM_NONE);
-    if (a == K) return meet(SDV_TERM_BONUS);
-    // a correction at a: weights in the frame 2^(z_t k - ref_t) of the rejected target row, the
-    // draft side 2^(z_d k - e) with e = ref_t + l2_d - l2_t carried as e_hi and 2^-(e - e_hi)
-    FusedTask t{};
-    t.i = i;
-    t.a = a;
-    t.ref_t = lane_value(ft.ref, a);
-    t.l2_t = lane_value(ft.l2, a);
-    const double e = (double)t.ref_t + lane_value(fd.l2, a) - t.l2_t;
-    t.e_hi = (float)e;
-    t.q_scale = (float)exp2((double)t.e_hi - e);
-    t.u = P.u_each ? P.u_each[trow0 + a] : (double)lane_value(draw_uniform(blk), a);
-    const uint32_t k = post_task(F, t, lane);  // posted first: other waves may start on it at once
-    meet(SDV_TERM_RESIDUAL);
-    for (int32_t c = take_chunk(P, F, k, lane); c >= 0; c = take_chunk(P, F, k, lane)) run_chunk<E>(P, F, k, t, c, lane);
-  }
-}
-
-// The bonus row of request i is complete: a request with no drafts is decided here; otherwise the
-// decision is met at the gate.
-template <class E, bool kGreedy>
-__device__ __forceinline__ void fused_bonus_ready(const Params& P, const FusedState& F, int32_t i, RowFold* rows,
-                                                  int lane) {
-  const int32_t lo = P.cu[i];
-  const int K = P.cu[i + 1] - lo;
-  if (K == 0) {
-    if (!stop_list_valid(P, i)) {
-      write_reject(P, i, lo + i, 0, true, lane);
-      return;
-    }
-    const int n_emit = emitted_count(P, i, 0, 0, lane);
-    if (lane == 0) {
-      P.accepted_len[i] = 0;
-      if (P.emitted_len) P.emitted_len[i] = n_emit;
-    }
-    if (n_emit == 1) return fused_bonus<E, kGreedy>(P, i, 0, rows, lane);
-    if (lane == 0) {
-      P.out_tokens[lo + i] = -1;
-      if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_NONE;
-    }
-    return fused_bonus_diag<kGreedy>(P, i, 0, rows, lane);
-  }
-  if (count_on(F.gate + i, lane) == 1u) {  // the decision is published
-    const int kind = (int)lane_value(lane == 0 ? fetch_coherent(reinterpret_cast<uint32_t*>(F.kind) + i) : 0u, 0);
-    if (kind == SDV_TERM_BONUS) fused_bonus<E, kGreedy>(P, i, K, rows, lane);
-    else if (kind != SDV_TERM_BAD) fused_bonus_diag<kGreedy>(P, i, K, rows, lane);
-  }
-}
-
-// ---------------------------------------------------------------------------- the kernel
-
-template <class E, bool kGreedy>
-__global__ __launch_bounds__(256) void fused_verify(Params P, FusedState F) {
-  __shared__ RowFold fold_rows[4][kMaxRows];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
-  RowFold* rows = fold_rows[wave];
-  if (scalar_at(reinterpret_cast<const int32_t*>(F.globals), 2) == 0) {  // malformed offsets: every request rejected
-    if (w < P.B) write_reject(P, (int32_t)w, 0, 0, false, lane);
-    return;
-  }
-  const int64_t per_pair = (kGreedy ? 1 : 2) * (int64_t)P.C;
-  const int64_t n_pair = per_pair * P.n_d, n_stream = n_pair + (int64_t)P.B * P.C;
-  if (w < n_stream) {
-    int32_t i, slot, c;
-    bool bonus = false;
-    if (w < n_pair) {
-      const int32_t d = (int32_t)(w / per_pair);
-      const int32_t r = (int32_t)(w - (int64_t)d * per_pair);
-      i = scalar_at(F.req_of_pair, d);
-      const bool draft = !kGreedy && r >= P.C;
-      c = draft ? r - P.C : r;
-      slot = draft ? P.n_t + d : d + i;
-    } else {
-      const int64_t q = w - n_pair;
-      i = (int32_t)(q / P.C);
-      c = (int32_t)(q - (int64_t)i * P.C);
-      slot = scalar_at(P.cu, i + 1) + i;
-      bonus = true;
-    }
-    const char* rp = slot < P.n_t ? row_ptr<E>(P.target, slot, P.V) : row_ptr<E>(P.draft, slot - P.n_t, P.V);
-    const int32_t c0 = c * E::kChunk;
-    const float2 rec = chunk_record<E, kGreedy, true>(rp, c0, min(E::kChunk, P.V - c0), P.k2, lane);
-    if (lane == 0) publish_f2(P.part + (int64_t)slot * P.Cs + c, rec);
-    stores_complete();
-    if (bonus) {
-      if (count_on(F.bonus_count + i, lane) == (uint32_t)P.C - 1u) fused_bonus_ready<E, kGreedy>(P, F, i, rows, lane);
-    } else {
-      const int32_t K = scalar_at(P.cu, i + 1) - scalar_at(P.cu, i);
-      if (count_on(F.req_count + i, lane) == (uint32_t)(per_pair * K) - 1u) fused_decide<E, kGreedy>(P, F, i, rows, lane);
-    }
-  }
-  if constexpr (!kGreedy) steal<E>(P, F, w < n_stream ? kFusedStealTries : kFusedHelperTries, lane);
-}
-
 // ============================================================================ Philox test hook
 
 __global__ void philox_kernel(const uint32_t* __restrict__ ctr, const uint32_t* __restrict__ key, int64_t n,
@@ -3090,13 +2479,41 @@ __global__ void philox_grid_kernel(uint64_t seed, int32_t B, int32_t P, uint32_t
   words[4 * b + 3] = r.w3;
 }
 
-// ============================================================================ read ceiling
-// The row pass's access pattern with no arithmetic: one wave per 16 KiB chunk, sixteen 16-byte
-// non-temporal loads per lane, the words folded by xor so that no load is dead.  Its rate is the
-// bandwidth a one-pass stream can reach, the yardstick for the row pass.
+// ============================================================================ read yardsticks
+// Reads of whole 16 KiB chunks with no arithmetic, the words folded by xor so that no load is dead;
+// each writes out[c] = the xor of chunk c's 4096 words.  Shape 0 is the row pass's (16-byte
+// non-temporal register loads, one chunk per wave, four waves per workgroup): its rate is the
+// bandwidth a one-pass stream of that shape reaches, the row pass's yardstick.  The other shapes
+// check that yardstick against different ways of reading: direct-to-LDS loads in two-wave
+// workgroups (1), and a persistent grid of eight workgroups per compute unit whose waves stride over
+// the chunks with two in flight (2).
 
-__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n_chunks,
-                                                    uint32_t* __restrict__ out) {
+__device__ __forceinline__ uint32_t fold_chunk(const u32x4 (&buf)[kVecPerLane]) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) x ^= buf[k].x ^ buf[k].y ^ buf[k].z ^ buf[k].w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, kWave);
+  return x;
+}
+
+constexpr int kLdsReadWaves = 2;
+__global__ __launch_bounds__(kWave * kLdsReadWaves) void read_lds_kernel(const u32x4* __restrict__ src, int64_t n_chunks,
+                                                                     uint32_t* __restrict__ out) {
+  __shared__ u32x4 chunk_lds[kLdsReadWaves][kVecPerLane * kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t c = (int64_t)blockIdx.x * kLdsReadWaves + wave;
+  if (c >= n_chunks) return;
+  u32x4 buf[kVecPerLane];
+  load_chunk_lds<Bf16>(reinterpret_cast<const char*>(src + c * (kChunkBytes / 16)), 0, Bf16::kChunk, lane,
+                       chunk_lds[wave], buf);
+  const uint32_t x = fold_chunk(buf);
+  if (lane == 0) out[c] = x;
+}
+
+__global__ __launch_bounds__(256) void read_reg_kernel(const u32x4* __restrict__ src, int64_t n_chunks,
+                                                       uint32_t* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t c = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (c >= n_chunks) return;
@@ -3104,23 +2521,39 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   u32x4 buf[kVecPerLane];
 #pragma unroll
   for (int k = 0; k < kVecPerLane; ++k) buf[k] = __builtin_nontemporal_load(v + lane + kWave * k);
-  uint32_t x = 0;
-#pragma unroll
-  for (int k = 0; k < kVecPerLane; ++k) x ^= buf[k].x ^ buf[k].y ^ buf[k].z ^ buf[k].w;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, kWave);
+  const uint32_t x = fold_chunk(buf);
   if (lane == 0) out[c] = x;
+}
+
+__global__ __launch_bounds__(256) void read_strided_kernel(const u32x4* __restrict__ src, int64_t n_chunks,
+                                                           uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t c = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave); c < n_chunks;
+       c += 2 * waves) {
+    const bool second = c + waves < n_chunks;
+    const u32x4* v = src + c * (kChunkBytes / 16);
+    const u32x4* w = src + (second ? c + waves : c) * (kChunkBytes / 16);
+    u32x4 a[kVecPerLane], b[kVecPerLane];
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) a[k] = __builtin_nontemporal_load(v + lane + kWave * k);
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) b[k] = __builtin_nontemporal_load(w + lane + kWave * k);
+    const uint32_t xa = fold_chunk(a), xb = fold_chunk(b);
+    if (lane == 0) {
+      out[c] = xa;
+      if (second) out[c + waves] = xb;
+    }
+  }
 }
 
 // ============================================================================ host side
 
 struct Layout {
-  int32_t C, Cs;
+  int32_t C;
   int64_t n_t, slots;
   size_t part, cuts, hist, hist_top, pending, split_mass, split_count, total;  // hist, hist_top, pending: bf16 only
-  size_t req_of_pair, counters, tasks, fmass, globals;                         // the fused path's state
 };
-constexpr int kFusedCounters = 7;  // req_count, bonus_count, gate, kind, ready, next_chunk, done_chunks
 
 constexpr size_t kAlign = 256;
 constexpr size_t kVerdictLdsBytes = 48 * 1024;  // dynamic shared memory of the verdict workgroup
@@ -3150,7 +2583,6 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
   const int32_t C = (int32_t)((V + (int64_t)chunk - 1) / chunk);
   if ((slots * C + 3) / 4 > INT32_MAX || C > kMaxChunks) return SDV_ERR_LIMIT;
   L->C = C;
-  L->Cs = (C + 15) / 16 * 16;  // a row's records fill whole 128-byte lines
   L->n_t = n_t;
   L->slots = slots;
   size_t off = 0;
@@ -3159,72 +2591,40 @@ inline int make_layout(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype
     off += align_up(bytes);
     return at;
   };
-  L->part = take((size_t)slots * L->Cs * sizeof(float2));
+  L->part = take((size_t)slots * C * sizeof(float2));
   L->cuts = take((size_t)slots * sizeof(Cut));
   const bool bf16_counts = dtype == SDV_BF16 && counts_room;
   const size_t counts = bf16_counts ? (size_t)slots * C : 0;  // per-chunk key counts of truncating calls
   L->hist = take(counts * kHistKeys * sizeof(uint16_t));
   L->hist_top = take(counts * sizeof(uint32_t));
   L->pending = take(bf16_counts ? (size_t)(slots + 1) * sizeof(int32_t) : 0);
-  L->split_mass = take((size_t)B * C * sizeof(double));
-  L->split_count = take((size_t)B * sizeof(uint32_t));
-  L->req_of_pair = take((size_t)n_draft_rows * sizeof(int32_t));
-  L->counters = take((size_t)kFusedCounters * B * sizeof(uint32_t));
-  L->tasks = take((size_t)B * kTaskWords * sizeof(uint64_t));
-  L->fmass = take((size_t)B * L->Cs * sizeof(double));
-  L->globals = take(4 * sizeof(uint32_t));
+  L->split_mass = take((size_t)B * ((C + 15) / 16 * 16) * sizeof(double));
+  L->split_count = take((size_t)B * kLineWords * sizeof(uint32_t) + sizeof(int32_t));  // counters, then the batch flag
   L->total = off;
   return SDV_OK;
 }
 
-// The fused path: the prologue, then one kernel for the stream, the verdicts and the draws.
-template <class E, bool kGreedy>
-int launch_fused(Params& P, const FusedState& F, hipStream_t stream, const sdv_diag* diag) {
-  auto record = [&](int k) {
-    if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
-  };
-  record(0);
-  hipLaunchKernelGGL(fused_prologue, dim3(1), dim3(1024), 0, stream, P, F);
-  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
-  record(1);
-  const int64_t waves = ((kGreedy ? 1 : 2) * (int64_t)P.n_d + P.B) * P.C + (kGreedy ? 0 : kFusedHelperWaves);
-  if ((waves + 3) / 4 > INT32_MAX) return SDV_ERR_LIMIT;
-  hipLaunchKernelGGL((fused_verify<E, kGreedy>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, P, F);
-  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
-  record(2);
-  return SDV_OK;
-}
-
 template <class E, int kMode, bool kVec>
-int launch(Params& P, const FusedState& F, hipStream_t stream, const sdv_diag* diag) {
+int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   auto record = [&](int k) {
     if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
   };
-  // one profile for the batch, 16-byte rows, draft logits, no truncation: the fused path, unless the
-  // caller asks for the two-kernel one (or for a verdict split, which only that path has)
-  if constexpr (kVec && kMode != kModeProfiled) {
-    if (P.path == 0 && P.split == 0 && !P.qrows && !P.top_k && !P.top_p_milli) {
-      P.Cs = (P.C + 15) / 16 * 16;
-      return launch_fused<E, kMode == kModeGreedy>(P, F, stream, diag);
-    }
-  }
-  P.Cs = P.C;
   // the stream reads draft rows only when they are logits of a sampling rule
   P.n_units = (int64_t)(kMode == kModeGreedy || P.qrows ? P.n_t : P.n_t + P.n_d) * P.C;
   // top-k / top-p: the cut of every logit row the verdicts read (the greedy rule keeps its argmax
   // under any truncation, so it needs none); bf16 rows get per-chunk key counts from the row pass
   const bool cut = kMode != kModeGreedy && (P.top_k || P.top_p_milli);
-  const dim3 units((unsigned)((P.n_units + 3) / 4));
+  const dim3 units((unsigned)((P.n_units + kRowWaves - 1) / kRowWaves));
   // verdict workgroups per request (the row pass zeroes their counters)
   P.split = kMode == kModeGreedy ? 1 : (P.split > 0 ? std::min(P.split, P.C) : verdict_split(P.B, P.C));
   record(0);
   if constexpr (E::kBytes == 2 && kVec && kMode != kModeGreedy) {
     if (!cut) P.hist = nullptr;
-    if (P.hist) hipLaunchKernelGGL((row_records<E, kMode, kVec, true>), units, dim3(256), 0, stream, P);
-    else hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), units, dim3(256), 0, stream, P);
+    if (P.hist) hipLaunchKernelGGL((row_records<E, kMode, kVec, true>), units, dim3(kWave * kRowWaves), 0, stream, P);
+    else hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), units, dim3(kWave * kRowWaves), 0, stream, P);
   } else {
     P.hist = nullptr;
-    hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), units, dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), units, dim3(kWave * kRowWaves), 0, stream, P);
   }
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(1);
@@ -3270,15 +2670,15 @@ int launch(Params& P, const FusedState& F, hipStream_t stream, const sdv_diag* d
 }
 
 template <class E, int kMode>
-int launch_vec(Params& P, const FusedState& F, bool vec, hipStream_t stream, const sdv_diag* diag) {
-  return vec ? launch<E, kMode, true>(P, F, stream, diag) : launch<E, kMode, false>(P, F, stream, diag);
+int launch_vec(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
+  return vec ? launch<E, kMode, true>(P, stream, diag) : launch<E, kMode, false>(P, stream, diag);
 }
 
 template <class E>
-int launch_any(Params& P, const FusedState& F, bool vec, hipStream_t stream, const sdv_diag* diag) {
-  if (P.temp_each) return launch_vec<E, kModeProfiled>(P, F, vec, stream, diag);
-  if (P.k2 == 0.0f) return launch_vec<E, kModeGreedy>(P, F, vec, stream, diag);
-  return launch_vec<E, kModeSampling>(P, F, vec, stream, diag);
+int launch_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
+  if (P.temp_each) return launch_vec<E, kModeProfiled>(P, vec, stream, diag);
+  if (P.k2 == 0.0f) return launch_vec<E, kModeGreedy>(P, vec, stream, diag);
+  return launch_vec<E, kModeSampling>(P, vec, stream, diag);
 }
 
 // ---------------------------------------------------------------------------- the no-alloc entry point
@@ -3329,7 +2729,6 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   const uint64_t* seed_each = opt->seed;
   if ((opt->accept_uniform == nullptr) != (opt->draw_uniform == nullptr)) return SDV_ERR_INVALID_ARG;
   if (opt->verdict_split < 0) return SDV_ERR_INVALID_ARG;
-  if (opt->verdict_path != 0 && opt->verdict_path != 1) return SDV_ERR_INVALID_ARG;
   if (opt->stop_offsets && (opt->n_stop_tokens < 0 || (opt->n_stop_tokens > 0 && !opt->stop_tokens)))
     return SDV_ERR_INVALID_ARG;
   Layout L;
@@ -3402,28 +2801,16 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   P.split = opt->verdict_split;  // 0: chosen at launch
   P.split_mass = reinterpret_cast<double*>(ws + L.split_mass);
   P.split_count = reinterpret_cast<uint32_t*>(ws + L.split_count);
+  P.batch_ok = reinterpret_cast<int32_t*>(P.split_count + (int64_t)B * kLineWords);
+  P.Cm = (L.C + 15) / 16 * 16;
   if (diag) {
     P.dg = DiagPtrs{diag->target_lse,     diag->draft_lse,    diag->target_argmax, diag->ratio,
                     diag->accept_uniform, diag->draw_uniform, diag->terminal_kind, diag->target_logit,
                     diag->draft_logit,    diag->terminal_mass};
   }
-  P.path = opt->verdict_path;
-  FusedState F{};
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.counters);
-  F.req_of_pair = reinterpret_cast<int32_t*>(ws + L.req_of_pair);
-  F.req_count = counters;
-  F.bonus_count = counters + B;
-  F.gate = counters + 2 * (int64_t)B;
-  F.kind = reinterpret_cast<int32_t*>(counters + 3 * (int64_t)B);
-  F.ready = counters + 4 * (int64_t)B;
-  F.next_chunk = counters + 5 * (int64_t)B;
-  F.done_chunks = counters + 6 * (int64_t)B;
-  F.tasks = reinterpret_cast<uint64_t*>(ws + L.tasks);
-  F.mass = reinterpret_cast<double*>(ws + L.fmass);
-  F.globals = reinterpret_cast<uint32_t*>(ws + L.globals);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == SDV_BF16) return launch_any<Bf16>(P, F, vec, s, diag);
-  return launch_any<F32>(P, F, vec, s, diag);
+  if (dtype == SDV_BF16) return launch_any<Bf16>(P, vec, s, diag);
+  return launch_any<F32>(P, vec, s, diag);
 }
 
 }  // namespace sdv
@@ -3504,12 +2891,26 @@ int sdv_philox_uniforms(uint64_t seed, int32_t B, int32_t P, uint32_t* words, vo
   return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
 }
 
-int sdv_read_ceiling(const void* src, int64_t n_chunks, uint32_t* out, void* stream) {
-  if (!src || !out || n_chunks < 1 || (uintptr_t)src % 16 != 0) return SDV_ERR_INVALID_ARG;
-  if ((n_chunks + 3) / 4 > INT32_MAX) return SDV_ERR_LIMIT;
-  hipLaunchKernelGGL(sdv::read_kernel, dim3((unsigned)((n_chunks + 3) / 4)), dim3(256), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const sdv::u32x4*>(src), n_chunks, out);
+int sdv_read_yardstick(const void* src, int64_t n_chunks, int32_t shape, uint32_t* out, void* stream) {
+  if (!src || !out || n_chunks < 1 || (uintptr_t)src % 16 != 0 || shape < 0 || shape > 2) return SDV_ERR_INVALID_ARG;
+  if ((n_chunks + 1) / 2 > INT32_MAX) return SDV_ERR_LIMIT;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const sdv::u32x4* v = static_cast<const sdv::u32x4*>(src);
+  if (shape == 0) {
+    hipLaunchKernelGGL(sdv::read_reg_kernel, dim3((unsigned)((n_chunks + 3) / 4)), dim3(256), 0, s, v, n_chunks, out);
+  } else if (shape == 1) {
+    hipLaunchKernelGGL(sdv::read_lds_kernel,
+                       dim3((unsigned)((n_chunks + sdv::kLdsReadWaves - 1) / sdv::kLdsReadWaves)),
+                       dim3(sdv::kWave * sdv::kLdsReadWaves), 0, s, v, n_chunks, out);
+  } else {
+    const int64_t groups = std::min<int64_t>(8 * sdv::kComputeUnits, (n_chunks + 3) / 4);
+    hipLaunchKernelGGL(sdv::read_strided_kernel, dim3((unsigned)groups), dim3(256), 0, s, v, n_chunks, out);
+  }
   return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
+}
+
+int sdv_read_ceiling(const void* src, int64_t n_chunks, uint32_t* out, void* stream) {
+  return sdv_read_yardstick(src, n_chunks, 0, out, stream);
 }
 
 const char* sdv_status_string(int status) {

@@ -212,33 +212,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int32_t& idx) {
   take(__uint_as_float(vb), (int32_t)ib);
 }
 
-// The same per row of 16 lanes (every lane ends with its row's winner), and per half wave.
-__device__ __forceinline__ void row16_argmax(float& v, int32_t& idx) {
-  using namespace wave_detail;
-  auto take = [&](float ov, int32_t oi) {
-    if (ov > v || (ov == v && oi < idx)) {
-      v = ov;
-      idx = oi;
-    }
-  };
-  take(__uint_as_float(dpp<kXor1>(__float_as_uint(v))), (int32_t)dpp<kXor1>((uint32_t)idx));
-  take(__uint_as_float(dpp<kXor2>(__float_as_uint(v))), (int32_t)dpp<kXor2>((uint32_t)idx));
-  take(__uint_as_float(dpp<kHalfMirror>(__float_as_uint(v))), (int32_t)dpp<kHalfMirror>((uint32_t)idx));
-  take(__uint_as_float(dpp<kMirror>(__float_as_uint(v))), (int32_t)dpp<kMirror>((uint32_t)idx));
-}
-__device__ __forceinline__ void half_argmax(float& v, int32_t& idx) {
-  row16_argmax(v, idx);
-  uint32_t va, vb, ia, ib;
-  wave_detail::both<16>(__float_as_uint(v), va, vb);
-  wave_detail::both<16>((uint32_t)idx, ia, ib);
-  v = __uint_as_float(va);
-  idx = (int32_t)ia;
-  if (__uint_as_float(vb) > v || (__uint_as_float(vb) == v && (int32_t)ib < idx)) {
-    v = __uint_as_float(vb);
-    idx = (int32_t)ib;
-  }
-}
-
 // Exclusive prefix sum over the wave (lane order), fp64: the inclusive scan less the lane's value.
 __device__ __forceinline__ double wave_exclusive_scan(double v, int) {
   return wave_detail::inclusive_scan(v) - v;

@@ -31,7 +31,7 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
                           "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms", "sdv_commit",
                           "sdv_status_string", "sdv_abi_version", "sdv_philox_uniforms",
-                          "sdv_verify_noalloc", "sdv_noalloc_bytes"}
+                          "sdv_verify_noalloc", "sdv_noalloc_bytes", "sdv_read_yardstick"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
@@ -46,27 +46,25 @@ def test_abi_version_and_status_strings(lib):
 def test_workspace_bytes(lib):
     # row-pass records: 8 B per 16 KiB chunk of every target and draft row, then one 8-byte
     # top-k / top-p cut per row, then (bf16) 128 16-bit key counts and a 4-byte top key per chunk
-    # and a list of rows (a count, then one 4-byte slot per row), then one 8-byte residual mass per
-    # chunk of each request and a 4-byte counter per request, each array 256-byte aligned
+    # and a list of rows (a count, then one 4-byte slot per row), then each request's residual masses
+    # (8 B per chunk, rows of masses rounded up to 16 chunks: whole 128-byte lines), then a 128-byte
+    # counter line per request and the batch's offset flag, each array 256-byte aligned
     up = lambda n: -(-n // 256) * 256
+    line = lambda c: -(-c // 16) * 16
+    verdict = lambda B, c: up(B * line(c) * 8) + up(B * 128 + 4)
     ws = lib.sdv_workspace_bytes(256, 1024, 128256, 0)
     chunks = (128256 + 8191) // 8192
     assert chunks == 16
     rows = 1280 + 1024
-    # then the fused path's state: the request of every draft row, seven counters per request, a
-    # 128-byte task description and 16-aligned chunk masses per request, four global words
-    fused = lambda B, n_d, cs: up(n_d * 4) + up(7 * B * 4) + up(B * 128) + up(B * cs * 8) + up(16)
     assert ws == (up(rows * chunks * 8) + up(rows * 8) + up(rows * chunks * 256) + up(rows * chunks * 4)
-                  + up((rows + 1) * 4) + up(256 * chunks * 8) + up(256 * 4) + fused(256, 1024, 16))
+                  + up((rows + 1) * 4) + verdict(256, chunks))
     assert ws % 256 == 0
     # binary32 rows: 4096 logits per chunk, no key counts
     chunks32 = (128256 + 4095) // 4096
     assert lib.sdv_workspace_bytes(256, 1024, 128256, 1) == (up(rows * chunks32 * 8) + up(rows * 8)
-                                                              + up(256 * chunks32 * 8) + up(256 * 4)
-                                                              + fused(256, 1024, 32))
-    # records fill whole 128-byte lines per row: 16 at least
-    assert lib.sdv_workspace_bytes(4, 8, 1000, 1) == (up(20 * 16 * 8) + up(20 * 8) + up(4 * 8) + up(4 * 4)
-                                                      + fused(4, 8, 16))  # 12 target and 8 draft rows
+                                                              + verdict(256, chunks32))
+    # a row of one chunk: its masses still fill a line
+    assert lib.sdv_workspace_bytes(4, 8, 1000, 1) == up(20 * 8) + up(20 * 8) + verdict(4, 1)  # 12 + 8 rows
     assert lib.sdv_workspace_bytes(0, 10, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, -1, 10, 0) == 0
     assert lib.sdv_workspace_bytes(1, 0, 10, 7) == 0
@@ -112,6 +110,9 @@ def test_host_argument_errors(lib):
     assert lib.sdv_read_ceiling(FAKE, 0, FAKE, None) == -1
     assert lib.sdv_read_ceiling(FAKE + 8, 4, FAKE, None) == -1  # not 16-byte aligned
     assert lib.sdv_read_ceiling(FAKE, 4, None, None) == -1
+    assert lib.sdv_read_yardstick(FAKE, 4, 3, FAKE, None) == -1  # no such shape
+    assert lib.sdv_read_yardstick(FAKE, 4, -1, FAKE, None) == -1
+    assert lib.sdv_read_yardstick(FAKE + 8, 4, 1, FAKE, None) == -1
     assert lib.sdv_philox_uniforms(1, 4, 4, None, None) == -1
     assert lib.sdv_philox_uniforms(1, 0, 4, FAKE, None) == -1
     assert lib.sdv_philox_uniforms(1, 4, 0, FAKE, None) == -1
@@ -178,9 +179,8 @@ def test_noalloc_host_checks(lib):
     counts that sdv_workspace_bytes includes."""
     up = lambda n: -(-n // 256) * 256
     rows, chunks = 1280 + 1024, 16
-    fused = up(1024 * 4) + up(7 * 256 * 4) + up(256 * 128) + up(256 * chunks * 8) + up(16)
     assert lib.sdv_noalloc_bytes(256, 1024, 128256, 0) == (up(rows * chunks * 8) + up(rows * 8) + up(256 * chunks * 8)
-                                                          + up(256 * 4) + fused)
+                                                          + up(256 * 128 + 4))
     assert lib.sdv_noalloc_bytes(256, 1024, 128256, 1) == lib.sdv_workspace_bytes(256, 1024, 128256, 1)
     assert lib.sdv_noalloc_bytes(0, 10, 10, 0) == 0
     assert _native.SDV_NOALLOC_SCRATCH_BYTES == 8 << 20
