@@ -221,6 +221,7 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy (--summarize-pmc)")
     ap.add_argument("--kernel", default="row_records", help="the kernel a counter summary is for (--summarize-pmc)")
     ap.add_argument("--command", default="", help="the command that produced the profile")
+    ap.add_argument("--summary-name", default="", help="file name (no suffix) of a --summarize-trace summary")
     ap.add_argument("--yardsticks", action="store_true",
                     help="time the read yardsticks (three read shapes) and torch's fill_ at the workload's size")
     args = ap.parse_args()
@@ -491,7 +492,9 @@ def summarize_trace(args):
         for line in open(args.bench_json):
             if line.startswith("{"):
                 bench = json.loads(line)
-    workload = bench["config"]["workload"] if bench else "unknown"
+                if "yardsticks" in bench:
+                    bench["config"] = {"workload": f"read shapes at the size of {bench['yardsticks']}"}
+    workload = bench["config"]["workload"] if bench else args.workload
     lines = [f"# Kernel durations: {workload}", "", "Command ($REPO is the repository root):", "", "```",
              args.command, "```", "",
              "| kernel | calls | total ms | mean us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
@@ -500,13 +503,21 @@ def summarize_trace(args):
         lines.append(f"| {_short(r['Name'])} | {n} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                      f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
-    if bench:
+    if bench and "yardsticks" in bench:
+        lines += ["", "The same run's event timings (mean per launch over two rotated buffers of "
+                  f"{bench['bytes']} bytes):", ""]
+        lines += [f"- {k}: {v['us']:.2f} us, {v['gbps']:.0f} GB/s" for k, v in bench.items() if isinstance(v, dict) and "us" in v]
+        lines += ["", "Shapes: read_reg_kernel = shape 0 (the row pass's loads: one wave per 16 KiB chunk, 16 "
+                  "non-temporal 16-byte loads per lane, four waves per workgroup); read_lds_kernel = shape 1 "
+                  "(direct-to-LDS loads, two waves per workgroup); read_strided_kernel = shape 2 (a persistent "
+                  "grid, two chunks in flight per wave); vectorized_elementwise_kernel = torch's fill_ (writes)."]
+    elif bench:
         lines += ["", "The same run's bench line (HIP events on the library's stream):", "",
                   f"- kernel_ms: {json.dumps({k: round(v * 1e3, 2) for k, v in bench['kernel_ms'].items()})} (us)",
                   f"- ms_per_step: {bench['ms_per_step'] * 1e3:.2f} us; roofline frac of "
                   f"{bench['roofline'].get('kernel', 'row_records')}: {bench['roofline']['frac']:.4f}; "
                   f"kernel_source_hash {bench['kernel_source_hash']}"]
-    out = os.path.join(ROOT, "profiles", f"kernels_{args.workload}_trace.md")
+    out = os.path.join(ROOT, "profiles", f"{args.summary_name or f'kernels_{args.workload}_trace'}.md")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SDV_ABI_VERSION 4
+#define SDV_ABI_VERSION 5
 #define SDV_MAX_DEPTH 64 /* largest K_i a request may carry */
 #define SDV_MAX_EVENTS 4 /* timing hooks in sdv_diag */
 
@@ -305,6 +305,34 @@ int sdv_commit(int32_t B, int64_t n_draft_rows, const int32_t* ragged_offsets, c
                const int32_t* emitted_len, const int32_t* out_tokens, const int32_t* prefix_len, int32_t* new_offsets,
                int32_t* new_tokens, int32_t* new_positions, int32_t* lengths, int32_t* next_token,
                int32_t* next_position, void* stream);
+
+/*
+ * The repadded form of a verified batch ("M7.8 - Speculative Serving", section 0x03D: the unpadded
+ * results are appended to each request's logical sequence and the batch is padded again to a
+ * rectangle; section 0x03C's position invariant: the non-padding tokens of a row sit at logical
+ * positions 0 .. L - 1 and padding takes no position).  All arrays are DEVICE arrays.
+ * ragged_offsets, accepted_len, out_tokens and emitted_len are as for sdv_commit; prefix_offsets
+ * [B + 1] and prefix_tokens [n_prefix_tokens] hold each request's logical sequence before the round
+ * in CSR form (request i: prefix_tokens[prefix_offsets[i] .. prefix_offsets[i + 1] - 1]).  Row i of
+ * the [B][width] outputs holds that prefix followed by the request's emitted tokens, L_i tokens in
+ * all, at positions 0 .. L_i - 1:
+ *   token_ids    [B][width] int32   the tokens, pad_id in padding cells
+ *   position_ids [B][width] int32   logical positions, -1 in padding cells
+ *   mask         [B][width] uint8   1 for a token, 0 for padding
+ *   row_len      [B]        int32   L_i
+ * left_pad != 0 puts the padding before the tokens (every row ends in the last column), 0 after.
+ * The section's width is the longest L_i (lengths[3 i] of sdv_commit); a row with L_i > width is
+ * written as padding only and reports L_i, so the caller can see it did not fit.  A row whose
+ * prefix offsets decrease or fall outside [0, n_prefix_tokens] is padding only and reports -1; a
+ * rejected request (accepted_len -1) keeps its prefix unchanged.  No KV block table is produced.
+ * Errors: B < 1, n_draft_rows < 0, n_prefix_tokens < 0, width < 1, or a NULL required pointer
+ * (prefix_tokens may be NULL when n_prefix_tokens is 0) -> SDV_ERR_INVALID_ARG; n_draft_rows + B
+ * above INT32_MAX, n_prefix_tokens above INT32_MAX - 128 or B * width above 2^40 -> SDV_ERR_LIMIT.
+ */
+int sdv_repad(int32_t B, int64_t n_draft_rows, const int32_t* ragged_offsets, const int32_t* accepted_len,
+              const int32_t* emitted_len, const int32_t* out_tokens, const int32_t* prefix_offsets,
+              const int32_t* prefix_tokens, int64_t n_prefix_tokens, int32_t width, int32_t pad_id, int32_t left_pad,
+              int32_t* token_ids, int32_t* position_ids, uint8_t* mask, int32_t* row_len, void* stream);
 
 /*
  * Raw Philox4x32-10 blocks on the device, for testing the verifier's uniforms: out[b] =

@@ -14,7 +14,7 @@ from . import _native
 from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_NONE,
                       TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, SdvError)
 
-__all__ = ["verify", "verify_ex", "commit", "workspace_bytes", "philox4x32_10", "philox_uniforms", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+__all__ = ["verify", "verify_ex", "commit", "repad", "workspace_bytes", "philox4x32_10", "philox_uniforms", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
            "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_NONE", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
 
 _DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
@@ -307,4 +307,35 @@ def commit(offsets: torch.Tensor, accepted_len: torch.Tensor, out_tokens: torch.
             _ptr(res["next_token"]), _ptr(res["next_position"]), torch.cuda.current_stream(dev).cuda_stream)
     if rc != 0:
         raise SdvError(rc, "sdv_commit")
+    return res
+
+
+def repad(offsets: torch.Tensor, accepted_len: torch.Tensor, out_tokens: torch.Tensor, prefix_offsets: torch.Tensor,
+          prefix_tokens: torch.Tensor, width: int, pad_id: int = 0, left_pad: bool = True,
+          emitted_len: torch.Tensor | None = None) -> dict:
+    """sdv_repad: each request's prefix (CSR: prefix_offsets [B + 1], prefix_tokens) followed by its
+    emitted tokens, as rows of a [B, width] batch at logical positions 0 .. L - 1.  Returns device
+    tensors token_ids [B, width] int32 (pad_id in padding), position_ids [B, width] int32 (-1 in
+    padding), mask [B, width] uint8, row_len [B] int32 (L; -1 for malformed prefix offsets)."""
+    dev = offsets.device
+    B = offsets.shape[0] - 1
+    n_d = out_tokens.shape[0] - B
+    for name, t, n in (("offsets", offsets, B + 1), ("accepted_len", accepted_len, B),
+                       ("out_tokens", out_tokens, n_d + B), ("prefix_offsets", prefix_offsets, B + 1)):
+        _device_vector(t, torch.int32, n, dev, name)
+    _device_vector(emitted_len, torch.int32, B, dev, "emitted_len")
+    n_p = prefix_tokens.numel()
+    _device_vector(prefix_tokens, torch.int32, n_p, dev, "prefix_tokens")
+    res = {"token_ids": torch.empty((B, width), dtype=torch.int32, device=dev),
+           "position_ids": torch.empty((B, width), dtype=torch.int32, device=dev),
+           "mask": torch.empty((B, width), dtype=torch.uint8, device=dev),
+           "row_len": torch.empty(B, dtype=torch.int32, device=dev)}
+    with torch.cuda.device(dev):
+        rc = _native.lib().sdv_repad(
+            B, n_d, _ptr(offsets), _ptr(accepted_len), _ptr(emitted_len), _ptr(out_tokens), _ptr(prefix_offsets),
+            _ptr(prefix_tokens) if n_p else None, n_p, int(width), int(pad_id), int(bool(left_pad)),
+            _ptr(res["token_ids"]), _ptr(res["position_ids"]), _ptr(res["mask"]), _ptr(res["row_len"]),
+            torch.cuda.current_stream(dev).cuda_stream)
+    if rc != 0:
+        raise SdvError(rc, "sdv_repad")
     return res

@@ -95,6 +95,9 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_sdcp_uniforms.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 6
     L.sdv_commit.restype = ctypes.c_int
     L.sdv_commit.argtypes = [ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 12
+    L.sdv_repad.restype = ctypes.c_int
+    L.sdv_repad.argtypes = ([ctypes.c_int32, ctypes.c_int64] + [ctypes.c_void_p] * 6 +
+                            [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 5)
     L.sdv_philox4x32_10.restype = ctypes.c_int
     L.sdv_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.sdv_philox_uniforms.restype = ctypes.c_int

@@ -1,8 +1,9 @@
 // Post-verification commit of a ragged batch ("M7.8 - Speculative Serving", sections 0x03C and
-// 0x03D: unpad, append, repad; section 0x09 for the lengths after a round).  One workgroup: a
-// block-wide exclusive scan of the emitted counts, then every request copies its emitted tokens to
-// their packed place and writes its new lengths.  The work is a few loads per request; what it
-// costs is latency, so one workgroup with the scan in shared memory is the whole design.
+// 0x03D: unpad, append, repad; section 0x09 for the lengths after a round).  sdv_commit is one
+// workgroup: a block-wide exclusive scan of the emitted counts, then every request copies its
+// emitted tokens to their packed place and writes its new lengths.  The work is a few loads per
+// request; what it costs is latency, so one workgroup with the scan in shared memory is the whole
+// design.  sdv_repad writes the rectangular form, one thread per cell.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,6 +77,47 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(int32_t B, int64_t n_d
   if (t == 0) new_offsets[B] = carry_s;
 }
 
+// Repad (section 0x03D): row i of the [B, width] batch holds request i's prefix followed by its
+// emitted tokens at logical positions 0 .. L_i - 1, padding elsewhere (pad_id, position -1, mask 0).
+// One thread per cell, grid-stride over B * width; each thread recomputes its row's few scalars
+// (cached loads), so no cell waits for another and the writes stay coalesced along the row.
+constexpr int kRepadThreads = 256;
+
+__global__ __launch_bounds__(kRepadThreads) void repad_kernel(int32_t B, int64_t n_d, const int32_t* __restrict__ cu,
+                                                              const int32_t* __restrict__ acc,
+                                                              const int32_t* __restrict__ emitted,
+                                                              const int32_t* __restrict__ out_tokens,
+                                                              const int32_t* __restrict__ po,
+                                                              const int32_t* __restrict__ ptok, int64_t n_prefix,
+                                                              int32_t width, int32_t pad_id, int32_t left_pad,
+                                                              int32_t* token_ids, int32_t* position_ids, uint8_t* mask,
+                                                              int32_t* row_len) {
+  const int64_t cells = (int64_t)B * width;
+  for (int64_t e = (int64_t)blockIdx.x * kRepadThreads + threadIdx.x; e < cells;
+       e += (int64_t)gridDim.x * kRepadThreads) {
+    const int32_t i = (int32_t)(e / width), c = (int32_t)(e - (int64_t)i * width);
+    const int32_t lo = po[i], hi = po[i + 1];
+    const bool ok = lo >= 0 && hi >= lo && (int64_t)hi <= n_prefix;
+    const int32_t P = ok ? hi - lo : 0;
+    const int32_t n = ok ? emitted_of(cu, acc, emitted, i, n_d) : 0;
+    const int64_t L = (int64_t)P + n;
+    if (c == 0) row_len[i] = ok ? (int32_t)L : -1;
+    int32_t tok = pad_id, pos = -1;
+    uint8_t m = 0;
+    if (ok && L <= width) {
+      const int64_t k = c - (left_pad ? width - L : 0);  // the cell's logical position
+      if (k >= 0 && k < L) {
+        tok = k < P ? ptok[lo + k] : out_tokens[(int64_t)cu[i] + i + (k - P)];
+        pos = (int32_t)k;
+        m = 1;
+      }
+    }
+    token_ids[e] = tok;
+    position_ids[e] = pos;
+    mask[e] = m;
+  }
+}
+
 }  // namespace commit_impl
 
 extern "C" int sdv_commit(int32_t B, int64_t n_draft_rows, const int32_t* ragged_offsets, const int32_t* accepted_len,
@@ -90,5 +132,26 @@ extern "C" int sdv_commit(int32_t B, int64_t n_draft_rows, const int32_t* ragged
                      reinterpret_cast<hipStream_t>(stream), B, n_draft_rows, ragged_offsets, accepted_len,
                      emitted_len, out_tokens,
                      prefix_len, new_offsets, new_tokens, new_positions, lengths, next_token, next_position);
+  return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
+}
+
+extern "C" int sdv_repad(int32_t B, int64_t n_draft_rows, const int32_t* ragged_offsets, const int32_t* accepted_len,
+                         const int32_t* emitted_len, const int32_t* out_tokens, const int32_t* prefix_offsets,
+                         const int32_t* prefix_tokens, int64_t n_prefix_tokens, int32_t width, int32_t pad_id,
+                         int32_t left_pad, int32_t* token_ids, int32_t* position_ids, uint8_t* mask, int32_t* row_len,
+                         void* stream) {
+  if (B < 1 || n_draft_rows < 0 || n_prefix_tokens < 0 || width < 1 || !ragged_offsets || !accepted_len ||
+      !out_tokens || !prefix_offsets || (n_prefix_tokens > 0 && !prefix_tokens) || !token_ids || !position_ids ||
+      !mask || !row_len)
+    return SDV_ERR_INVALID_ARG;
+  if (n_draft_rows + B > INT32_MAX || n_prefix_tokens > INT32_MAX - 128 || (int64_t)B * width > ((int64_t)1 << 40))
+    return SDV_ERR_LIMIT;
+  const int64_t cells = (int64_t)B * width;
+  const int64_t blocks = (cells + commit_impl::kRepadThreads - 1) / commit_impl::kRepadThreads;
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  hipLaunchKernelGGL(commit_impl::repad_kernel, dim3(grid), dim3(commit_impl::kRepadThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), B, n_draft_rows, ragged_offsets, accepted_len, emitted_len,
+                     out_tokens, prefix_offsets, prefix_tokens, n_prefix_tokens, width, pad_id, left_pad != 0,
+                     token_ids, position_ids, mask, row_len);
   return hipGetLastError() == hipSuccess ? SDV_OK : SDV_ERR_HIP;
 }

@@ -53,3 +53,39 @@ def commit(cu, accepted_len, out_tokens, prefix_len, emitted_len=None) -> dict:
             next_position[i] = positions[offsets[i + 1] - 1]
     return {"offsets": offsets, "tokens": tokens, "positions": positions, "lengths": lengths,
             "next_token": next_token, "next_position": next_position}
+
+
+def repad(cu, accepted_len, out_tokens, prefix_offsets, prefix_tokens, width, pad_id, left_pad,
+          emitted_len=None) -> dict:
+    """The repad step of section 0x03D: request i's logical sequence is its prefix (prefix_tokens
+    [prefix_offsets[i] : prefix_offsets[i + 1]]) followed by the tokens it emitted this round (as
+    ``commit`` finds them), and row i of a [B, width] batch holds that sequence at logical positions
+    0 .. L_i - 1 with padding in the other columns: token pad_id, position -1 (padding takes no
+    logical position, section 0x03C's position invariant) and mask 0.  With left_pad the padding
+    comes first, so every row ends in the last column.  A row whose sequence is longer than width
+    is all padding and reports its length L_i > width; a row whose prefix offsets are decreasing or
+    outside [0, len(prefix_tokens)] is all padding and reports -1."""
+    po = np.asarray(prefix_offsets, dtype=np.int64)
+    pt = np.asarray(prefix_tokens, dtype=np.int64).reshape(-1)
+    B = po.shape[0] - 1
+    new = commit(cu, accepted_len, out_tokens, np.zeros(B, dtype=np.int64), emitted_len)
+    token_ids = np.full((B, width), pad_id, dtype=np.int32)
+    position_ids = np.full((B, width), -1, dtype=np.int32)
+    mask = np.zeros((B, width), dtype=np.uint8)
+    row_len = np.zeros(B, dtype=np.int32)
+    for i in range(B):
+        lo, hi = int(po[i]), int(po[i + 1])
+        if lo < 0 or hi < lo or hi > pt.shape[0]:
+            row_len[i] = -1
+            continue
+        logical = list(pt[lo:hi]) + list(new["tokens"][new["offsets"][i]:new["offsets"][i + 1]])
+        L = len(logical)
+        row_len[i] = L
+        if L > width:
+            continue
+        first = width - L if left_pad else 0
+        for k in range(L):
+            token_ids[i, first + k] = logical[k]
+            position_ids[i, first + k] = k
+            mask[i, first + k] = 1
+    return {"token_ids": token_ids, "position_ids": position_ids, "mask": mask, "row_len": row_len}

@@ -31,13 +31,13 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
                           "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms", "sdv_commit",
                           "sdv_status_string", "sdv_abi_version", "sdv_philox_uniforms",
-                          "sdv_verify_noalloc", "sdv_noalloc_bytes", "sdv_read_yardstick"}
+                          "sdv_verify_noalloc", "sdv_noalloc_bytes", "sdv_read_yardstick", "sdv_repad"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.sdv_abi_version() == 4
+    assert lib.sdv_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.sdv_status_string(code) not in (None, b"", b"unknown status")
     assert lib.sdv_status_string(17) == b"unknown status"
@@ -167,6 +167,24 @@ def test_commit_host_argument_checks(lib):
     a[3] = None  # out_tokens
     assert lib.sdv_commit(2, 4, *a, None) == -1
     assert lib.sdv_commit(2, 2**31, *args, None) == -3
+
+
+def test_repad_host_argument_checks(lib):
+    def call(B=2, n_d=4, n_p=6, width=8, **ptrs):
+        p = dict(cu=FAKE, acc=FAKE, emitted=None, out=FAKE, po=FAKE, pt=FAKE, tok=FAKE, pos=FAKE, mask=FAKE, rl=FAKE)
+        p.update(ptrs)
+        return lib.sdv_repad(B, n_d, p["cu"], p["acc"], p["emitted"], p["out"], p["po"], p["pt"], n_p, width, 0, 1,
+                             p["tok"], p["pos"], p["mask"], p["rl"], None)
+    assert call(B=0) == -1
+    assert call(n_d=-1) == -1
+    assert call(n_p=-1) == -1
+    assert call(width=0) == -1
+    for name in ("cu", "acc", "out", "po", "tok", "pos", "mask", "rl"):
+        assert call(**{name: None}) == -1, name
+    assert call(pt=None) == -1             # prefix tokens missing while n_prefix_tokens > 0
+    assert call(n_d=2**31) == -3
+    assert call(n_p=2**31) == -3
+    assert call(B=2**20, width=2**21) == -3  # B * width above 2^40
 
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):

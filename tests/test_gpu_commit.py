@@ -75,3 +75,58 @@ def test_malformed_offsets_emit_nothing_and_stay_in_bounds():
     assert np.array_equal(got["offsets"].cpu().numpy(), ref["offsets"])
     assert np.array_equal(got["tokens"].cpu().numpy(), ref["tokens"][:10])
     assert np.array_equal(got["lengths"].cpu().numpy(), ref["lengths"])
+
+
+def _compare_repad(cu, acc, out, po, pt, width, pad_id, left, emitted=None):
+    got = sdv.repad(_dev(cu), _dev(acc), _dev(out), _dev(po), _dev(pt), width, pad_id, left,
+                    None if emitted is None else _dev(emitted))
+    torch.cuda.synchronize()
+    ref = C.repad(cu, acc, out, po, pt, width, pad_id, left, emitted_len=emitted)
+    for k in ("token_ids", "position_ids", "mask", "row_len"):
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+    return ref
+
+
+def test_repad_after_gpu_verification_with_stops():
+    """Section 0x03D's repad of a verified batch: prefix + emitted tokens per row, both padding
+    sides, at the section's width (the longest row) and at a width the longest rows overflow."""
+    rng = np.random.default_rng(21)
+    b = W.make_random("repad", rng.integers(0, 9, size=150), 4099, "fp32", 1.0, 2.0, 1.0, data_seed=22, verify_seed=23)
+    stops = [[int(b.tokens[b.cu[i]])] if b.cu[i + 1] > b.cu[i] and rng.random() < 0.3 else [] for i in range(b.B)]
+    offs, toks = oracle.stop_csr(stops)
+    budget = rng.integers(0, 12, size=b.B).astype(np.int32)
+    acc, out, extra = sdv.verify_ex(to_device(b.target, b.dtype), to_device(b.draft, b.dtype), _dev(b.tokens),
+                                    _dev(b.cu), 1.0, 23, stop_offsets=_dev(offs), stop_tokens=_dev(toks),
+                                    budget=_dev(budget))
+    torch.cuda.synchronize()
+    acc, out, emitted = acc.cpu().numpy(), out.cpu().numpy(), extra["emitted_len"].cpu().numpy()
+    plen = rng.integers(0, 40, size=b.B)
+    po = np.concatenate([[0], np.cumsum(plen)])
+    pt = rng.integers(0, 4099, size=int(po[-1]))
+    width = int(np.max(plen + emitted))
+    for w in (width, width - 2):
+        for left in (True, False):
+            ref = _compare_repad(b.cu, acc, out, po, pt, w, -5, left, emitted)
+    assert (ref["row_len"] > width - 2).any()
+
+
+@pytest.mark.parametrize("B,width", [(1, 7), (3000, 1000)])
+def test_repad_grid_stride_and_malformed_prefixes(B, width):
+    """3000 x 1000 cells exceed one pass of the grid (8192 workgroups of 256 threads), so cells are
+    revisited by the stride loop; a few rows get decreasing or out-of-range prefix offsets."""
+    rng = np.random.default_rng(B)
+    cu = W.offsets_from_depths(rng.integers(0, 9, size=B))
+    K = np.diff(cu)
+    acc = np.array([rng.integers(0, k + 1) if rng.random() > 0.05 else -1 for k in K], dtype=np.int32)
+    out = rng.integers(0, 50000, size=int(cu[-1]) + B).astype(np.int32)
+    emitted = np.array([rng.integers(-1, a + 3) for a in np.maximum(acc, 0)], dtype=np.int32)
+    po = np.concatenate([[0], np.cumsum(rng.integers(0, width, size=B))]).astype(np.int64)
+    pt = rng.integers(0, 50000, size=int(po[-1]))
+    if B > 2:
+        po[B // 2] = po[B // 2 + 1] + 3  # row B/2 - 1 grows, row B/2 decreases
+        po[B // 2 + 3] = po[-1] + 5  # beyond the prefix tokens: rows B/2 + 2 and B/2 + 3
+        po[B // 2] = min(po[B // 2], po[-1])
+    for left in (True, False):
+        ref = _compare_repad(cu, acc, out, po, pt, width, 0, left, emitted)
+    if B > 2:
+        assert (ref["row_len"] == -1).sum() >= 2

@@ -58,3 +58,59 @@ def test_without_emitted_len_every_valid_request_emits_a_plus_one():
     assert res["tokens"].tolist() == [5, 7, 9]
     assert res["positions"].tolist() == [0, 1, 4]
     assert res["lengths"].tolist() == [[2, 1, 1], [5, 4, 4], [9, 9, 9]]
+
+
+def test_repad_hand_worked_example():
+    """tests/golden/repad_example.json: three requests (one accepted draft plus the extra token, a
+    K = 0 round, a rejected request) repadded to width 5, padding on either side."""
+    g = json.load(open(os.path.join(GOLDEN, "repad_example.json")))
+    for side, left in (("left_pad", True), ("right_pad", False)):
+        res = C.repad(g["ragged_offsets"], g["accepted_len"], np.array(g["out_tokens"], dtype=np.int32),
+                      g["prefix_offsets"], g["prefix_tokens"], g["width"], g["pad_id"], left)
+        for key in ("token_ids", "position_ids", "mask", "row_len"):
+            assert res[key].tolist() == g[side][key], (side, key)
+
+
+def test_repad_invariants_on_oracle_verdicts():
+    """Section 0x03C's position invariant (the unpadded positions of each row are 0 .. L - 1 and
+    padding takes none), unpadding recovers the prefix followed by the packed commit's tokens, both
+    padding sides hold the same sequence, and a row longer than the width is all padding."""
+    rng = np.random.default_rng(11)
+    depths = rng.integers(0, 9, size=90)
+    b = make_random("repad", depths, 48, "fp32", 1.0, 2.0, 1.0, data_seed=11, verify_seed=12)
+    stops = [list(rng.choice(48, size=rng.integers(0, 3), replace=False)) for _ in range(b.B)]
+    budget = rng.integers(0, 8, size=b.B)
+    v = oracle.verify(b.target, b.draft, b.tokens, b.cu, 1.0, 12, stop_lists=stops, budget=budget)
+    plen = rng.integers(0, 20, size=b.B)
+    po = np.concatenate([[0], np.cumsum(plen)])
+    pt = rng.integers(0, 48, size=int(po[-1]))
+    packed = C.commit(b.cu, v["accepted_len"], v["out_tokens"], plen, emitted_len=v["emitted_len"])
+    width = int(np.max(packed["lengths"][:, 0])) - 3  # the longest rows do not fit
+    sides = [C.repad(b.cu, v["accepted_len"], v["out_tokens"], po, pt, width, -7, left, v["emitted_len"])
+             for left in (True, False)]
+    for i in range(b.B):
+        want = list(pt[po[i]:po[i + 1]]) + list(packed["tokens"][packed["offsets"][i]:packed["offsets"][i + 1]])
+        L = len(want)
+        assert L == packed["lengths"][i, 0]
+        for res in sides:
+            assert res["row_len"][i] == L
+            keep = res["mask"][i].astype(bool)
+            if L > width:
+                assert not keep.any() and (res["token_ids"][i] == -7).all() and (res["position_ids"][i] == -1).all()
+                continue
+            assert res["token_ids"][i][keep].tolist() == want
+            assert res["position_ids"][i][keep].tolist() == list(range(L))
+            assert (res["token_ids"][i][~keep] == -7).all() and (res["position_ids"][i][~keep] == -1).all()
+        if L <= width:
+            assert sides[0]["mask"][i, width - L:].all() and sides[1]["mask"][i, :L].all()
+    assert (sides[0]["row_len"] > width).any()
+
+
+def test_repad_malformed_prefix_offsets_mark_their_row_alone():
+    cu = offsets_from_depths([1, 1, 1])
+    acc = np.array([0, 1, 0])
+    out = np.array([3, -1, 4, 5, 6, -1], dtype=np.int32)
+    res = C.repad(cu, acc, out, [0, 2, 1, 3], [9, 9, 9], 4, 0, True)
+    assert res["row_len"].tolist() == [3, -1, 3]
+    assert not res["mask"][1].any()
+    assert res["token_ids"][0].tolist() == [0, 9, 9, 3] and res["token_ids"][2].tolist() == [0, 9, 9, 6]
