@@ -93,6 +93,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
         ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
     ]
+    lib.oracle_verify_tree.restype = ctypes.c_int
+    lib.oracle_verify_tree.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
+    ]
     lib.oracle_philox4x32_10.restype = None
     lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.oracle_philox_block.restype = None
@@ -294,3 +300,52 @@ def num_threads() -> int:
 
 def set_num_threads(n: int) -> None:
     load().oracle_set_num_threads(n)
+
+
+def verify_tree(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, parents: np.ndarray,
+                cu: np.ndarray, temperature: float, seed: int, diag: bool = False, lib_path: str = LIBRARY) -> dict:
+    """Run the oracle's token-tree verification (oracle_verify_tree) on one batch.
+
+    target: (n_nodes + B, V), row cu[i] + i at request i's root and cu[i] + i + n + 1 after node n;
+    draft: (n_nodes, V), row cu[i] + n the distribution node n was drawn from (None when
+    temperature == 0); draft_tokens, parents: (n_nodes,) int32, parents in [-1, n - 1] within the
+    request; cu: (B + 1,) node offsets.  Returns accepted_len (B,), out_tokens (n_nodes + B,),
+    accepted_nodes (n_nodes,), and with ``diag`` the LSEs, argmaxes, ratios and accept margins of
+    the nodes tested (NaN elsewhere), cdf margins, residual masses and terminal kinds.
+    """
+    lib = load(lib_path)
+    target = np.ascontiguousarray(target)
+    dt = _dtype_code(target)
+    if draft is not None:
+        draft = np.ascontiguousarray(draft)
+        if _dtype_code(draft) != dt:
+            raise TypeError("target and draft must share a dtype")
+    draft_tokens = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    B = cu.shape[0] - 1
+    n = draft_tokens.shape[0]
+    V = target.shape[1]
+    if target.shape[0] != n + B or parents.shape[0] != n:
+        raise ValueError("target must have n_nodes + B rows and parents n_nodes entries")
+    acc = np.full(B, -7, dtype=np.int32)
+    out = np.full(n + B, -7, dtype=np.int32)
+    nodes = np.full(n, -7, dtype=np.int32)
+    res: dict = {"accepted_len": acc, "out_tokens": out, "accepted_nodes": nodes}
+    dg_p = None
+    if diag:
+        res.update(
+            target_lse=np.full(n + B, np.nan), draft_lse=np.full(n, np.nan),
+            target_argmax=np.full(n + B, -1, dtype=np.int32), ratio=np.full(n, np.nan),
+            accept_margin=np.full(n, np.nan), cdf_margin=np.full(B, np.nan),
+            resid_mass=np.full(B, np.nan), terminal_kind=np.full(B, -9, dtype=np.int32),
+            filter_margin=np.full(2 * n + B, np.inf),
+        )
+        dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
+        dg_p = ctypes.pointer(dg)
+    rc = lib.oracle_verify_tree(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(parents), _ptr(cu), B, n, V,
+                                float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(acc), _ptr(out), _ptr(nodes),
+                                dg_p)
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree rejected the batch ({rc})")
+    return res

@@ -26,6 +26,9 @@
  *    applies temperature, then top-k, then top-p, and p is the distribution after all three).
  *    The draft side gets the same profile, since the drafter samples from its own row under it.
  *
+ *  - Token trees (multi-step speculative sampling over a tree of drafts, a published method the
+ *    pages do not define): the section "token trees" below.
+ *
  *  - Precondition (SDCP section "Verification and Commit", step 5): a proposal whose draft
  *    probability q_j(x_j) is zero at any position is rejected before any uniform is drawn.
  *    Out-of-range draft tokens and depths beyond 64 (SDCP "Session Contract", m_max <= 64) are
@@ -649,6 +652,213 @@ int oracle_verify_profiled(const void* target, const void* draft, int dtype, con
   oracle_options opt = {temperature, seed, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL};
   return oracle_verify_opts(target, draft, dtype, draft_tokens, cu, B, n_draft_rows, V, 0.0, 0, &opt, accepted_len,
                             out_tokens, diag);
+}
+
+/* ---------------------------------------------------------------- token trees
+ *
+ * Tree verification by multi-step speculative sampling: Miao et al., "SpecInfer: Accelerating
+ * Large Language Model Serving with Tree-based Speculative Inference and Verification" (ASPLOS
+ * 2024), section 4, the token tree verifier and its stochastic rule.  The pages define no tree rule
+ * (SDCP section "Scope" leaves tree-structured speculation out of its first version; M7.8 names
+ * trees among the proposal shapes a verifier meets); this is the reading taken:
+ *
+ *  - request i has N_i nodes n = 0 .. N_i - 1 (offsets cu as for linear drafts, N_i <= 64); node
+ *    n has parent parents[cu[i] + n] in [-1, n - 1] (-1: the root, the last committed token) and
+ *    token tokens[cu[i] + n], sampled from q_n = softmax(draft row cu[i] + n / T), the drafter's
+ *    distribution at its parent's context (siblings from one drafter carry equal draft rows);
+ *  - target rows: cu[i] + i at the root, cu[i] + i + n + 1 after node n; a chain (node n the
+ *    parent of node n + 1) is exactly a linear draft;
+ *  - Rule 2 (T > 0): at the current node, with p its target distribution, the children are tested
+ *    in ascending node order.  Child c is accepted iff r_c <= p(x_c) / q_c(x_c), and the walk moves
+ *    to c with p = c's target distribution.  On a rejection p <- normalize(max(p - q_c, 0)) and the
+ *    next child is tested.  When every child is rejected the extra token is drawn from that
+ *    residual p; at a node without children it is drawn from the node's target distribution.
+ *    The paper takes the children in random order; for children drawn independently each
+ *    stage's law needs only that the tested child is drawn from its own q, so any fixed order is
+ *    exact and the caller's order is used;
+ *  - Rule 1 (T = 0): the first child (ascending node order) whose token equals the target argmax at
+ *    the current node (ties to the smallest id) is accepted; when none does, the extra token is that
+ *    argmax;
+ *  - uniforms: r_c is word 0 of the Philox block keyed (seed; counter (c, i, 0, 0)), the node's
+ *    own index taking the place of the position; the extra token's u is word 1 of the block of the
+ *    target row it is drawn from (0 at the root, n + 1 after node n).  On a chain both are the
+ *    linear draft's;
+ *  - a residual with S = 0 (impossible in exact arithmetic after a rejection) restarts from the
+ *    current node's target distribution;
+ *  - bad requests (accepted_len -1, every slot -1): a token outside [0, V), a parent outside
+ *    [-1, n - 1], a temperature that describes no profile, and at T > 0 a node whose draft
+ *    probability at its own token is zero.
+ * Outputs: accepted_len[i] = a, the depth of the accepted path; out_tokens[cu[i] + i + d] for
+ * d < a the path's tokens, then the extra token, then -1 up to slot N_i; accepted_nodes[cu[i] + d]
+ * for d < a the path's node indices, then -1 up to N_i - 1.  diag: target_lse / draft_lse of
+ * every row, ratio and accept_margin at the nodes tested (NaN elsewhere), cdf_margin, terminal_kind,
+ * and resid_mass = the product of the stage masses S of the draw's residual (1 for a bonus).
+ */
+static void verify_tree_request(const void* target, const void* draft, int dtype, const int32_t* tokens,
+                                const int32_t* parents, const int32_t* cu, int32_t i, int64_t n_nodes, int32_t V,
+                                double T, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens,
+                                int32_t* accepted_nodes, oracle_diag* dg, double* p, double* q) {
+  const int64_t lo = cu[i], hi = cu[i + 1];
+  const int64_t N = hi - lo;
+  if (dg && dg->cdf_margin) dg->cdf_margin[i] = NAN;
+  if (dg && dg->resid_mass) dg->resid_mass[i] = NAN;
+  if (lo < 0 || hi > n_nodes || N < 0 || N > ORACLE_MAX_DEPTH) { /* no slot can be named */
+    accepted_len[i] = -1;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_BAD;
+    return;
+  }
+  const int64_t trow0 = lo + i, drow0 = lo;
+  int32_t* slots = out_tokens + trow0;
+  int32_t* path = accepted_nodes + drow0; /* [N]: the accepted nodes, then -1 */
+  for (int64_t d = 0; d < N; ++d) path[d] = -1;
+  for (int64_t d = 0; d <= N; ++d) slots[d] = -1;
+  if (dg) {
+    for (int64_t n = 0; n < N; ++n) {
+      set_nan(dg->ratio ? &dg->ratio[drow0 + n] : NULL);
+      set_nan(dg->accept_margin ? &dg->accept_margin[drow0 + n] : NULL);
+    }
+  }
+
+  int bad = !(T >= 0.0) || isinf(T);
+  for (int64_t n = 0; n < N && !bad; ++n) {
+    const int32_t x = tokens[drow0 + n], par = parents[drow0 + n];
+    if (x < 0 || x >= V || par < -1 || par >= n) bad = 1;
+  }
+  double lse_t[ORACLE_MAX_DEPTH + 1], lse_d[ORACLE_MAX_DEPTH];
+  if (!bad && T > 0.0) {
+    for (int64_t r = 0; r <= N; ++r) lse_t[r] = oracle_row_lse(target, dtype, trow0 + r, V, T);
+    for (int64_t n = 0; n < N; ++n) {
+      lse_d[n] = oracle_row_lse(draft, dtype, drow0 + n, V, T);
+      if (logit_at(draft, dtype, drow0 + n, V, tokens[drow0 + n]) == -INFINITY) bad = 1; /* q_n(x_n) = 0 */
+    }
+  }
+  if (bad) {
+    accepted_len[i] = -1;
+    if (dg && dg->terminal_kind) dg->terminal_kind[i] = ORACLE_TERM_BAD;
+    return;
+  }
+
+  int64_t a = 0;
+  int64_t u = -1; /* the current node; -1 is the root, whose target row is 0 */
+  int32_t y;
+  int kind;
+  if (T == 0.0) { /* ---- Rule 1 */
+    for (;;) {
+      const int32_t g = oracle_row_argmax(target, dtype, trow0 + u + 1, V);
+      if (dg && dg->target_argmax) dg->target_argmax[trow0 + u + 1] = g;
+      int64_t next = -1;
+      for (int64_t c = u + 1; c < N && next < 0; ++c) /* a child's index exceeds its parent's */
+        if (parents[drow0 + c] == u && tokens[drow0 + c] == g) next = c;
+      if (next < 0) {
+        y = g;
+        break;
+      }
+      path[a++] = (int32_t)next;
+      u = next;
+    }
+    kind = ORACLE_TERM_GREEDY;
+  } else { /* ---- Rule 2 */
+    if (dg) {
+      for (int64_t r = 0; r <= N; ++r)
+        if (dg->target_lse) dg->target_lse[trow0 + r] = lse_t[r];
+      for (int64_t n = 0; n < N; ++n)
+        if (dg->draft_lse) dg->draft_lse[drow0 + n] = lse_d[n];
+    }
+    for (;;) {
+      const int64_t row = u + 1; /* the current node's target row within the request */
+      for (int32_t v = 0; v < V; ++v) p[v] = exp(logit_at(target, dtype, trow0 + row, V, v) / T - lse_t[row]);
+      int rejected = 0, empty = 0;
+      int pending = 0;   /* p holds the last residual unnormalized, its total S_last */
+      double S_last = 1.0;
+      double mass = 1.0; /* product of the earlier stages' masses */
+      int64_t next = -1;
+      for (int64_t c = u + 1; c < N && next < 0; ++c) {
+        if (parents[drow0 + c] != u) continue;
+        if (pending) { /* normalize(max(p - q, 0)) */
+          for (int32_t v = 0; v < V; ++v) p[v] /= S_last;
+          mass *= S_last;
+          pending = 0;
+        }
+        const int32_t x = tokens[drow0 + c];
+        for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, drow0 + c, V, v) / T - lse_d[c]);
+        /* the first child sees the node's own p: its ratio in the log form of the linear walk */
+        const double ratio =
+            rejected ? p[x] / q[x]
+                     : exp((logit_at(target, dtype, trow0 + row, V, x) - logit_at(draft, dtype, drow0 + c, V, x)) / T -
+                           (lse_t[row] - lse_d[c]));
+        uint32_t blk[4];
+        oracle_philox_block(seed, (uint32_t)i, (uint32_t)c, blk);
+        const double r = accept_uniform(blk);
+        if (dg && dg->ratio) dg->ratio[drow0 + c] = ratio;
+        if (dg && dg->accept_margin) dg->accept_margin[drow0 + c] = fabs(r - ratio);
+        if (r <= ratio) {
+          next = c;
+          break;
+        }
+        double S = 0.0;
+        for (int32_t v = 0; v < V; ++v) {
+          p[v] = p[v] > q[v] ? p[v] - q[v] : 0.0;
+          S += p[v];
+        }
+        rejected = 1;
+        if (S > 0.0) {
+          pending = 1;
+          S_last = S;
+          empty = 0;
+        } else { /* restart from the node's target distribution */
+          for (int32_t v = 0; v < V; ++v) p[v] = exp(logit_at(target, dtype, trow0 + row, V, v) / T - lse_t[row]);
+          pending = 0;
+          mass = 1.0;
+          empty = 1;
+        }
+      }
+      if (next >= 0) {
+        path[a++] = (int32_t)next;
+        u = next;
+        continue;
+      }
+      uint32_t blk[4];
+      oracle_philox_block(seed, (uint32_t)i, (uint32_t)row, blk);
+      double S, margin;
+      y = inverse_cdf(p, V, draw_uniform(blk), &S, &margin); /* normalizes a pending residual itself */
+      kind = !rejected ? ORACLE_TERM_BONUS : (empty ? ORACLE_TERM_RESIDUAL_EMPTY : ORACLE_TERM_RESIDUAL);
+      if (dg && dg->cdf_margin) dg->cdf_margin[i] = margin;
+      if (dg && dg->resid_mass) dg->resid_mass[i] = mass * S;
+      break;
+    }
+  }
+  for (int64_t d = 0; d < a; ++d) slots[d] = tokens[drow0 + path[d]];
+  slots[a] = y;
+  accepted_len[i] = (int32_t)a;
+  if (dg && dg->terminal_kind) dg->terminal_kind[i] = kind;
+}
+
+/*
+ * Token-tree batches (see above).  target [n_nodes + B][V], draft [n_nodes][V] (may be NULL when
+ * T == 0), draft_tokens and parents [n_nodes], cu [B + 1] node offsets, accepted_len [B],
+ * out_tokens [n_nodes + B], accepted_nodes [n_nodes].  Returns 0, or -1 for arguments that
+ * describe no batch.
+ */
+int oracle_verify_tree(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
+                       const int32_t* parents, const int32_t* cu, int32_t B, int64_t n_nodes, int32_t V, double T,
+                       uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, int32_t* accepted_nodes,
+                       oracle_diag* diag) {
+  if (!target || !draft_tokens || !parents || !cu || !accepted_len || !out_tokens || !accepted_nodes) return -1;
+  if (B <= 0 || V <= 0 || n_nodes < 0 || !(T >= 0.0) || isinf(T) || (T > 0.0 && !draft && n_nodes > 0)) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* p = (double*)malloc(sizeof(double) * 2 * (size_t)V);
+    if (!p) failed = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int32_t i = 0; i < B; ++i)
+      if (p)
+        verify_tree_request(target, draft, dtype, draft_tokens, parents, cu, i, n_nodes, V, T, seed, accepted_len,
+                            out_tokens, accepted_nodes, diag, p, p + V);
+    free(p);
+  }
+  return failed ? -2 : 0;
 }
 
 /* Number of OpenMP threads the oracle runs on (for reporting), and a way to change it (timing). */

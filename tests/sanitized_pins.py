@@ -20,7 +20,7 @@ from workloads import offsets_from_depths  # noqa: E402
 
 def oracle_pins(lib_path):
     for check in (M._pin_lse, M._pin_greedy_tie, M._pin_profiles, M._pin_stops, M._pin_qrows, M._pin_filters,
-                  M._pin_keying, M._pin_monte_carlo):
+                  M._pin_keying, M._pin_tree, M._pin_monte_carlo):
         assert check(lib_path), check.__name__
         print(f"pin ok: {check.__name__}", flush=True)
 

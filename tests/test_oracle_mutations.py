@@ -17,6 +17,7 @@ from scipy import stats
 
 import filter_pins
 import keying_pins
+import tree_pins
 from oracle import exact, oracle
 from workloads import offsets_from_depths
 
@@ -73,6 +74,21 @@ MUTATIONS = {
     "accept_from_word_3": ("return (double)((w[0] >> 8) + 1u) / 16777216.0;", "return (double)((w[3] >> 8) + 1u) / 16777216.0;"),
     "draw_counter_request_and_position_swapped": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)t, blk);\n    u = draw_uniform(blk);",
                                                   "oracle_philox_block(seed, (uint32_t)t, (uint32_t)i, blk);\n    u = draw_uniform(blk);"),
+    # token trees
+    "tree_residual_not_updated": ("          p[v] = p[v] > q[v] ? p[v] - q[v] : 0.0;\n          S += p[v];",
+                                  "          S += p[v] > q[v] ? p[v] - q[v] : 0.0;"),
+    "tree_residual_left_unnormalized": ("          for (int32_t v = 0; v < V; ++v) p[v] /= S_last;\n", ""),
+    "tree_accept_block_of_depth": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)c, blk);",
+                                   "oracle_philox_block(seed, (uint32_t)i, (uint32_t)a, blk);"),
+    "tree_draw_block_of_node_index": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)row, blk);",
+                                      "oracle_philox_block(seed, (uint32_t)i, (uint32_t)(row > 0 ? row - 1 : 0), blk);"),
+    "tree_q_of_first_sibling": ("for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, drow0 + c, V, v) / T - lse_d[c]);",
+                                "for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, drow0 + u + 1, V, v) / T - lse_d[u + 1]);"),
+    "tree_stops_at_first_rejection": ("      for (int64_t c = u + 1; c < N && next < 0; ++c) {\n        if (parents[drow0 + c] != u) continue;",
+                                      "      for (int64_t c = u + 1; c < N && next < 0 && !rejected; ++c) {\n        if (parents[drow0 + c] != u) continue;"),
+    "tree_greedy_last_matching_child": ("      for (int64_t c = u + 1; c < N && next < 0; ++c) /* a child's index exceeds its parent's */",
+                                        "      for (int64_t c = u + 1; c < N; ++c) /* a child's index exceeds its parent's */"),
+    "tree_parent_check_off_by_one": ("if (x < 0 || x >= V || par < -1 || par >= n) bad = 1;", "if (x < 0 || x >= V || par < -1 || par > n) bad = 1;"),
 }
 
 
@@ -247,9 +263,14 @@ def _pin_keying(lib_path):
     return all(check(lib_path) for check in keying_pins.ALL)
 
 
+def _pin_tree(lib_path):
+    """Every token-tree pin of tests/tree_pins.py."""
+    return all(check(lib_path) for check in tree_pins.ALL)
+
+
 def test_unmutated_oracle_passes_every_pin(tmp_path):
     for check in (_pin_monte_carlo, _pin_lse, _pin_greedy_tie, _pin_profiles, _pin_stops, _pin_qrows, _pin_filters,
-                  _pin_keying):
+                  _pin_keying, _pin_tree):
         assert check(oracle.LIBRARY)
     assert _pin_philox(oracle.LIBRARY, tmp_path)
 
@@ -269,5 +290,6 @@ def test_planted_mistake_is_caught(tmp_path, name):
         "qrows": _pin_qrows(lib),
         "top_k_top_p": _pin_filters(lib),
         "keying": _pin_keying(lib),
+        "tree": _pin_tree(lib),
     }
     assert not all(results.values()), f"planted mistake {name!r} passed every pin: {results}"
