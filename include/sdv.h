@@ -266,6 +266,56 @@ int sdv_verify_opts(const void* target_logits, const void* draft_logits, const i
                     const sdv_diag* diag);
 
 /*
+ * Verification of token trees: multi-step speculative sampling over a tree of drafts (Miao et al.,
+ * "SpecInfer: Accelerating Large Language Model Serving with Tree-based Speculative Inference and
+ * Verification", ASPLOS 2024, section 4, the token tree verifier).  The pages define no tree rule
+ * (SDCP section "Scope" leaves tree-structured speculation out of its first version); Rules 1 and 2
+ * of SDCP "Acceptance Rules" are applied node by node as follows.
+ *
+ * Request i holds N_i = cu[i + 1] - cu[i] <= 64 nodes n = 0 .. N_i - 1 (ragged_offsets as for
+ * linear drafts).  All arrays are DEVICE arrays:
+ *   parents       [n_nodes] int32   node n's parent within its request, in [-1, n - 1] (-1: the
+ *                                   root, the last committed token); nodes come in an order where
+ *                                   every parent precedes its children
+ *   draft_tokens  [n_nodes] int32   node n's token
+ *   target_logits [n_nodes + B][V]  row cu[i] + i at the root, cu[i] + i + n + 1 after node n
+ *   draft_logits  [n_nodes][V]      row cu[i] + n: the logits node n's token was drawn from (at its
+ *                                   parent's context; siblings from one drafter carry equal rows);
+ *                                   may be NULL when temperature == 0
+ * A chain (every node the parent of the next) is exactly a linear draft of sdv_verify, with the
+ * same uniforms and results.
+ *   T > 0: at the current node (the root first), with p its target distribution softmax(z / T),
+ *          the children are tested in node order: child c is accepted iff r_c <= p(x_c) / q_c(x_c)
+ *          with q_c = softmax(draft row of c / T), and the walk moves to c; a rejection replaces p
+ *          by normalize(max(p - q_c, 0)) and the next child is tested.  When every child is
+ *          rejected the extra token is drawn from that p; at a node without children it is drawn
+ *          from the node's own target distribution.  r_c: word 0 of the Philox block keyed (seed;
+ *          counter (c, i, 0, 0)); the draw: word 1 of the block of the target row it is drawn from
+ *          (0 at the root, n + 1 after node n), by the inverse CDF in ascending token id.
+ *   T = 0: the first child (node order) whose token equals the target argmax of the current node
+ *          (ties to the smallest id) is accepted; when none does, that argmax is the extra token.
+ * Outputs: accepted_len [B] the depth a of the accepted path; out_tokens [n_nodes + B] the path's
+ * tokens at cu[i] + i .. cu[i] + i + a - 1, the extra token at cu[i] + i + a, -1 up to
+ * cu[i] + i + N_i; accepted_nodes [n_nodes] the path's node indices (within the request) at
+ * cu[i] .. cu[i] + a - 1, -1 up to cu[i] + N_i - 1.
+ * Bad requests (accepted_len -1, every slot -1): a token outside [0, V), a parent outside
+ * [-1, n - 1], or at T > 0 a node whose draft logit at its own token is -inf (q = 0).  Offsets that
+ * are not valid, or a request of more than 64 nodes, reject without writing slots, as sdv_verify.
+ * workspace: sdv_workspace_bytes(B, n_nodes, V, dtype).  diag (may be NULL): target_lse,
+ * draft_lse, target_logit / draft_logit (z_t at the parent's row and z_d at each node's token),
+ * ratio and accept_uniform at the nodes tested (others untouched), target_argmax of the rows
+ * visited (T = 0), draw_uniform, terminal_kind, terminal_mass (the residual's mass in probability
+ * units, M = product of the stage masses; about 1 for a bonus) and the events (row pass, verdicts).
+ * Per-request profiles, truncation, stop lists and caller uniforms are not taken on this path.
+ * Errors as sdv_verify; NULL parents, draft_tokens or accepted_nodes with n_nodes > 0 ->
+ * SDV_ERR_INVALID_ARG.
+ */
+int sdv_verify_tree(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                    const int32_t* parents, const int32_t* ragged_offsets, int32_t B, int64_t n_nodes, int32_t V,
+                    int32_t dtype, double temperature, uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes,
+                    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
+
+/*
  * SDCP's verifier uniforms, computed on the HOST for sdv_options ("Speculative Decoding
  * Coordination Protocol (SDCP)", section "Acceptance Rules", Rule 2).  For request i, with profile
  * seed seeds[i], session id sessions[16 i .. 16 i + 15] and round rounds[i], each value is the first

@@ -14,7 +14,7 @@ from . import _native
 from ._native import (SDV_BF16, SDV_FP32, SDV_MAX_DEPTH, TERM_BAD, TERM_BONUS, TERM_GREEDY, TERM_NONE,
                       TERM_RESIDUAL, TERM_RESIDUAL_EMPTY, SdvError)
 
-__all__ = ["verify", "verify_ex", "commit", "repad", "workspace_bytes", "philox4x32_10", "philox_uniforms", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
+__all__ = ["verify", "verify_ex", "verify_tree", "commit", "repad", "workspace_bytes", "philox4x32_10", "philox_uniforms", "read_ceiling", "sdcp_uniforms", "abi_version", "SdvError", "SDV_MAX_DEPTH",
            "TERM_BAD", "TERM_BONUS", "TERM_GREEDY", "TERM_NONE", "TERM_RESIDUAL", "TERM_RESIDUAL_EMPTY", "library_path"]
 
 _DTYPES = {torch.bfloat16: SDV_BF16, torch.float32: SDV_FP32}
@@ -207,6 +207,52 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
         raise SdvError(rc, "sdv_verify_opts" if use_opts else
                        ("sdv_verify_profiled" if profile is not None else "sdv_verify_ex"))
     return accepted_len, out_tokens, dvals
+
+
+def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, parents: torch.Tensor,
+                offsets: torch.Tensor, temperature: float, seed: int, *, workspace: torch.Tensor | None = None,
+                diag: tuple[str, ...] = (), events: list | None = None):
+    """sdv_verify_tree: token trees (int32 parents [n_nodes], each node's parent within its request,
+    -1 for the root; target rows cu[i] + i at the root and cu[i] + i + n + 1 after node n; draft row
+    cu[i] + n the logits node n was drawn from).  Returns (accepted_len [B], out_tokens
+    [n_nodes + B], accepted_nodes [n_nodes], extra) with the named sdv_diag arrays in extra."""
+    _check(target, draft, draft_tokens, offsets, temperature, None)
+    dev = target.device
+    B = offsets.shape[0] - 1
+    n = draft_tokens.shape[0]
+    _device_vector(parents, torch.int32, n, dev, "parents")
+    V = target.shape[1]
+    dt = _DTYPES[target.dtype]
+    accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tokens = torch.empty(n + B, dtype=torch.int32, device=dev)
+    accepted_nodes = torch.empty(n, dtype=torch.int32, device=dev)
+    need = int(_native.lib().sdv_workspace_bytes(B, n, V, dt))
+    ws = _workspace(need, dev) if workspace is None else workspace
+    shapes = {"target_lse": (n + B, torch.float64), "draft_lse": (n, torch.float64),
+              "target_argmax": (n + B, torch.int32), "ratio": (n, torch.float64),
+              "accept_uniform": (n, torch.float32), "draw_uniform": (B, torch.float32),
+              "terminal_kind": (B, torch.int32), "target_logit": (n, torch.float32),
+              "draft_logit": (n, torch.float32), "terminal_mass": (B, torch.float64)}
+    dvals = {}
+    dg = None
+    if diag or events:
+        dg = _native.SdvDiag()
+        for name in diag:
+            m, t = shapes[name]
+            dvals[name] = torch.full((m,), -9 if t == torch.int32 else float("nan"), dtype=t, device=dev)
+            setattr(dg, name, dvals[name].data_ptr())
+        for k, ev in enumerate(events or []):
+            if ev is not None:
+                dg.events[k] = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
+    with torch.cuda.device(dev):
+        rc = _native.lib().sdv_verify_tree(
+            _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(parents), _ptr(offsets), B, n, V, dt,
+            float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(accepted_nodes),
+            _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(), torch.cuda.current_stream(dev).cuda_stream,
+            ctypes.byref(dg) if dg is not None else None)
+    if rc != 0:
+        raise SdvError(rc, "sdv_verify_tree")
+    return accepted_len, out_tokens, accepted_nodes, dvals
 
 
 def sdcp_uniforms(offsets, seeds, sessions, rounds):

@@ -152,6 +152,8 @@ struct Params {
   uint32_t* split_count;      // [B][kLineWords] masses published per request (zeroed by the row pass), a line each
   int32_t Cm;                 // C rounded up to 16: a request's masses fill whole 128-byte lines
   int32_t* batch_ok;          // [1] the offsets are valid (written by the row pass's first workgroup)
+  const int32_t* parents;     // [n_d] token trees: each node's parent within its request (-1: the root), or null
+  int32_t* accepted_nodes;    // [n_d] token trees, out: the accepted path's nodes, then -1
   DiagPtrs dg;
 };
 
@@ -2054,6 +2056,53 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
 static_assert(kVecPerLane % kVerdictWaves == 0, "the in-chunk search gives each wave whole rows of 64 vectors");
 constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
+// Folds a request's rows: rows r <= K_t are its target rows r (records at rec_t), rows r > K_t its
+// draft rows r - K_t - 1 (records at rec_d).  All chunk records go to shared memory in one pass when
+// they fit the budget (else the fold reads the workspace); `overlap` runs between the staging loads
+// and the barrier (wave 0's gathers hide under them).  rows[r] receives the fold of row r.
+template <bool kGreedy, class Overlap>
+__device__ __forceinline__ void stage_and_fold(const Params& P, const float2* rec_t, const float2* rec_d, int K_t,
+                                               int n_rows, double* lds_mass, RowFold* rows, int lane, int wave,
+                                               int n_waves, Overlap overlap) {
+  const int64_t n_rec = (int64_t)n_rows * P.C;
+  float2* lds_rec = reinterpret_cast<float2*>(lds_mass + P.C);
+  const bool staged = n_rec <= P.lds_records;
+  if (staged) {
+    for (int64_t q = threadIdx.x; q < n_rec; q += blockDim.x) {
+      const int64_t r = q / P.C;
+      const int32_t c = (int32_t)(q - r * P.C);
+      lds_rec[q] = r <= K_t ? rec_t[r * P.C + c] : rec_d[(r - K_t - 1) * P.C + c];
+    }
+  }
+  overlap();
+  __syncthreads();
+  auto records_of = [&](int r) {
+    return staged ? lds_rec + (int64_t)r * P.C
+                  : (r <= K_t ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K_t - 1) * P.C);
+  };
+  auto fold_narrow = [&](auto lanes) {  // kWave / lanes rows per wave
+    constexpr int kLanes = decltype(lanes)::value, kPer = kWave / kLanes;
+    const int g = lane / kLanes, c = lane % kLanes;
+    for (int r0 = kPer * wave; r0 < n_rows; r0 += kPer * n_waves) {
+      const int r = r0 + g;
+      const float2 rec = r < n_rows && c < P.C ? records_of(r)[c] : make_float2(-INFINITY, 0.0f);
+      const RowFold f = fold_row_narrow<kLanes>(rec);
+      if (c == 0 && r < n_rows) rows[r] = f;
+    }
+  };
+  if (!kGreedy && P.C <= 16) {
+    fold_narrow(std::integral_constant<int, 16>{});
+  } else if (!kGreedy && P.C <= 32) {
+    fold_narrow(std::integral_constant<int, 32>{});
+  } else {
+    for (int r = wave; r < n_rows; r += n_waves) {
+      const RowFold f = fold_row<kGreedy>(records_of(r), P.C, lane);
+      if (lane == 0) rows[r] = f;
+    }
+  }
+  __syncthreads();
+}
+
 // The verdict of request i under one rule (k2 = log2(e)/T and the Philox key seed), by one
 // workgroup of 8 waves.  Shared memory: the folded rows, the decision, and the residual chunk masses
 // (C doubles, dynamic).  bad_profile rejects the request once its offsets have been screened.  With
@@ -2096,60 +2145,26 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   // are staged in shared memory in one pass when they fit, while wave 0 fetches the draft
   // tokens and the logits at them
   const int n_rows = (kGreedy || kQ) ? K + 1 : 2 * K + 1;  // given q rows have no records
-  const int64_t n_rec = (int64_t)n_rows * P.C;
-  float2* lds_rec = reinterpret_cast<float2*>(lds_mass + P.C);
-  const bool staged = n_rec <= P.lds_records;
-  if (staged) {
-    for (int64_t q = threadIdx.x; q < n_rec; q += blockDim.x) {
-      const int64_t r = q / P.C;
-      const int32_t c = (int32_t)(q - r * P.C);
-      lds_rec[q] = r <= K ? rec_t[r * P.C + c] : rec_d[(r - K - 1) * P.C + c];
-    }
-  }
   const bool active = lane < K;
   int32_t x = 0;
   float zt = 0.0f, zd = 0.0f;
   bool keep_t = true, keep_d = true;  // x is kept by the target / draft row's truncation
-  if (wave == 0 && active) {
-    x = P.tokens[drow0 + lane];
-    if constexpr (!kGreedy) {
-      if (x >= 0 && x < P.V) {
-        zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
-        // with q rows, zd carries q(x) itself
-        zd = kQ ? P.qrows[(int64_t)(drow0 + lane) * P.V + x] : E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
-        if constexpr (kCut) {
-          keep_t = kept_by(P.cuts[trow0 + lane], zt, x);
-          if constexpr (!kQ) keep_d = kept_by(P.cuts[P.n_t + drow0 + lane], zd, x);
+  stage_and_fold<kGreedy>(P, rec_t, rec_d, K, n_rows, lds_mass, rows, lane, wave, n_waves, [&] {
+    if (wave == 0 && active) {
+      x = P.tokens[drow0 + lane];
+      if constexpr (!kGreedy) {
+        if (x >= 0 && x < P.V) {
+          zt = E::at(row_ptr<E>(P.target, trow0 + lane, P.V), x);
+          // with q rows, zd carries q(x) itself
+          zd = kQ ? P.qrows[(int64_t)(drow0 + lane) * P.V + x] : E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+          if constexpr (kCut) {
+            keep_t = kept_by(P.cuts[trow0 + lane], zt, x);
+            if constexpr (!kQ) keep_d = kept_by(P.cuts[P.n_t + drow0 + lane], zd, x);
+          }
         }
       }
     }
-  }
-  __syncthreads();
-  auto records_of = [&](int r) {
-    return staged ? lds_rec + (int64_t)r * P.C
-                  : (r <= K ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K - 1) * P.C);
-  };
-  auto fold_narrow = [&](auto lanes) {  // kWave / lanes rows per wave
-    constexpr int kLanes = decltype(lanes)::value, kPer = kWave / kLanes;
-    const int g = lane / kLanes, c = lane % kLanes;
-    for (int r0 = kPer * wave; r0 < n_rows; r0 += kPer * n_waves) {
-      const int r = r0 + g;
-      const float2 rec = r < n_rows && c < P.C ? records_of(r)[c] : make_float2(-INFINITY, 0.0f);
-      const RowFold f = fold_row_narrow<kLanes>(rec);
-      if (c == 0 && r < n_rows) rows[r] = f;
-    }
-  };
-  if (!kGreedy && P.C <= 16) {
-    fold_narrow(std::integral_constant<int, 16>{});
-  } else if (!kGreedy && P.C <= 32) {
-    fold_narrow(std::integral_constant<int, 32>{});
-  } else {
-    for (int r = wave; r < n_rows; r += n_waves) {
-      const RowFold f = fold_row<kGreedy>(records_of(r), P.C, lane);
-      if (lane == 0) rows[r] = f;
-    }
-  }
-  __syncthreads();
+  });
 
   // 2. the verdict, by wave 0
   if (wave == 0) {
@@ -2454,6 +2469,338 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   write_token(y, empty, S);
 }
 
+// ============================================================================ 4. token trees
+// Tree verification by multi-step speculative sampling (Miao et al., "SpecInfer", ASPLOS 2024,
+// section 4: the token tree verifier).  Request i holds N_i <= 64 nodes; node n has parent
+// P.parents[cu[i] + n] in [-1, n - 1] and token P.tokens[cu[i] + n], drawn from the distribution of
+// draft row cu[i] + n.  Target row cu[i] + i is the root's, cu[i] + i + n + 1 follows node n: the
+// linear layout, so the row pass is unchanged and a chain of nodes is a linear draft.
+//
+// At the current node, with p its target distribution, the children are tested in node order.
+// Child c is accepted iff r_c <= p(x_c) / q_c(x_c), r_c from the Philox block (c, i); after l
+// rejections p is the residual R_l / M_l, with
+//   R_0 = p,  R_j = max(R_{j-1} - M_{j-1} q_{c_j}, 0),  M_j = sum_v R_j(v)  (M_0 = 1),
+// the unnormalized form of p <- normalize(max(p - q, 0)) applied j times.  Each rejection costs one
+// pass over the node's target row and the rejected children's draft rows (M_j and its chunk
+// masses); the extra token is drawn from R_l by those chunk masses and a search inside one chunk,
+// or, when no child was rejected, from the node's own target row by its records.  u comes from the
+// block of the node's target row.  At T = 0 the first child equal to the node's target argmax is
+// accepted.  The walk runs in wave 0; the passes use the whole workgroup.
+
+// Weight R_l(v) in fp32 (probability units): the node's target logit zt and the rejected
+// children's draft logits zd[j] at v, exponents carried as (hi, lo) float pairs.
+struct ChainFrame {
+  int32_t l;                       // rejected children so far
+  float k2, t_hi, t_lo;            // the node's target row: log2 p(v) = zt k2 - (t_hi + t_lo)
+  float d_hi[SDV_MAX_DEPTH], d_lo[SDV_MAX_DEPTH];  // rejected child j's draft row, the same form
+  float m[SDV_MAX_DEPTH];          // M_j, the mass before rejection j + 1 (m[0] = 1)
+  int32_t drow[SDV_MAX_DEPTH];     // rejected child j's draft row (batch index)
+};
+
+__device__ __forceinline__ float chain_p(const ChainFrame& f, float zt) {
+  return fast_exp2(fmaf(zt, f.k2, -f.t_hi) - f.t_lo);
+}
+__device__ __forceinline__ float chain_step(const ChainFrame& f, int j, float R, float zd) {
+  const float q = fast_exp2(fmaf(zd, f.k2, -f.d_hi[j]) - f.d_lo[j]);
+  return fmaxf(fmaf(-f.m[j], q, R), 0.0f);
+}
+
+// R_l(v) for one element (rows given as byte pointers of the logits).
+template <class E>
+__device__ __forceinline__ float chain_weight(const ChainFrame& f, const char* trow, const void* draft, int32_t V,
+                                              int32_t v) {
+  float R = chain_p(f, E::at(trow, v));
+  for (int j = 0; j < f.l; ++j) R = chain_step(f, j, R, E::at(row_ptr<E>(draft, f.drow[j], V), v));
+  return R;
+}
+
+// Chunk masses of R_l into lds_mass[0 .. C) by the whole workgroup (wave w takes chunks w,
+// w + n_waves, ...): 16-byte vectors, four in flight per lane, fp32 per vector, fp64 across vectors.
+template <class E, bool kVec>
+__device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* trow, const void* draft, int32_t V,
+                                             int32_t C, double* lds_mass, int lane, int wave, int n_waves) {
+  for (int32_t c = wave; c < C; c += n_waves) {
+    const int32_t c0 = c * E::kChunk, n = min(E::kChunk, V - c0);
+    double acc = 0.0;
+    if constexpr (kVec) {
+      const int32_t nvec = n / E::kPerVec;
+      const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
+      constexpr int kGroup = 4;
+      for (int g0 = 0; g0 < kVecPerLane; g0 += kGroup) {
+        float R[kGroup][E::kPerVec];
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+          float z[E::kPerVec];
+          E::unpack(load_vec<E>(tv, lane + kWave * (g0 + k), nvec), z);
+#pragma unroll
+          for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_p(f, z[e]);
+        }
+        for (int j = 0; j < f.l; ++j) {
+          const u32x4* dv = reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
+          u32x4 b[kGroup];
+#pragma unroll
+          for (int k = 0; k < kGroup; ++k) b[k] = load_vec<E>(dv, lane + kWave * (g0 + k), nvec);
+#pragma unroll
+          for (int k = 0; k < kGroup; ++k) {
+            float z[E::kPerVec];
+            E::unpack(b[k], z);
+#pragma unroll
+            for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_step(f, j, R[k][e], z[e]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
+      }
+    } else {
+      for (int32_t v = c0 + lane; v < c0 + n; v += kWave) acc += (double)chain_weight<E>(f, trow, draft, V, v);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) lds_mass[c] = acc;
+  }
+}
+
+// What wave 0 hands the workgroup after each step of the walk.
+struct TreeStep {
+  int32_t action;  // kTreePass: chunk masses of the frame's R_l; kTreeDraw: the extra token; kTreeDone
+  int32_t kind;    // sdv_terminal_kind of the draw
+  int32_t row;     // the current node's target row within the request (0: the root)
+  int32_t token;   // T = 0: the extra token
+  double u;        // T > 0: the draw's uniform
+};
+constexpr int32_t kTreePass = 0, kTreeDraw = 1, kTreeDone = 2;
+
+template <class E, bool kGreedy, bool kVec>
+__global__ __launch_bounds__(kWave * kVerdictWaves) void tree_verdicts(Params P) {
+  extern __shared__ double lds_mass[];  // [C], then staged records
+  __shared__ RowFold rows[kMaxRows];
+  __shared__ ChainFrame frame;
+  __shared__ TreeStep step;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n_waves = blockDim.x / kWave;
+  const int32_t i = blockIdx.x;
+  const float k2 = P.k2;
+
+  const int32_t lo_raw = P.cu[i], hi_raw = P.cu[i + 1];
+  const bool ok_offsets = *P.batch_ok != 0;
+  const int32_t lo = ok_offsets ? lo_raw : 0, hi = ok_offsets ? hi_raw : 0;
+  const int N = hi - lo;
+  const int32_t trow0 = lo + i, drow0 = lo;
+  auto reject = [&](bool write_slots) {  // wave 0
+    if (write_slots) {
+      for (int j = lane; j <= N; j += kWave) P.out_tokens[trow0 + j] = -1;
+      for (int j = lane; j < N; j += kWave) P.accepted_nodes[drow0 + j] = -1;
+    }
+    if (lane == 0) {
+      P.accepted_len[i] = -1;
+      if (P.dg.terminal_kind) P.dg.terminal_kind[i] = SDV_TERM_BAD;
+    }
+  };
+  if (!ok_offsets || N > SDV_MAX_DEPTH) {  // malformed batch, or too many nodes: no slot written
+    if (wave == 0) reject(false);
+    return;
+  }
+  const float2* rec_t = P.part + (int64_t)trow0 * P.C;
+  const float2* rec_d = P.part + (int64_t)(P.n_t + drow0) * P.C;
+
+  // 1. rows folded; wave 0 loads the nodes and, at T > 0, gathers z_t(x) from each node's parent row
+  // and z_d(x) from its own draft row
+  const bool active = lane < N;
+  int32_t x = 0, par = -1;
+  float zt = 0.0f, zd = 0.0f;
+  bool bad_node = false;
+  const int n_rows = kGreedy ? N + 1 : 2 * N + 1;
+  stage_and_fold<kGreedy>(P, rec_t, rec_d, N, n_rows, lds_mass, rows, lane, wave, n_waves, [&] {
+    if (wave == 0 && active) {
+      x = P.tokens[drow0 + lane];
+      par = P.parents[drow0 + lane];
+      bad_node = x < 0 || x >= P.V || par < -1 || par >= lane;
+      if (!kGreedy && !bad_node) {
+        zt = E::at(row_ptr<E>(P.target, trow0 + par + 1, P.V), x);
+        zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+      }
+    }
+  });
+
+  // 2. the walk (wave 0), with a pass by the whole workgroup after each rejection.  Wave 0 keeps
+  // the walk in registers: lane d the node accepted at depth d; lane j the draft row, its LSE and
+  // M_j of the j-th rejected child of the current node.
+  int a = 0;                   // accepted depth
+  int32_t path_node = -1;      // lane d < a: the node accepted at depth d
+  int32_t u = -1;              // the current node (-1: the root)
+  int32_t cpos = 0;            // children of u below this node index have been tested
+  int l = 0;                   // rejected children in the current residual
+  bool rejected = false;       // some child of u was rejected
+  double M_l = 1.0;            // mass of the current residual R_l
+  int32_t rej_drow = 0;        // lane j < l: the rejected child's draft row
+  double rej_l2 = 0.0, rej_m = 0.0;  // lane j < l: its draft row's base-2 LSE, and M_j
+  double l2d_self = 0.0;       // lane n: the base-2 LSE of node n's draft row
+  bool done = false;           // the request is rejected: nothing to draw
+  if (wave == 0) {
+    if (__ballot(active && bad_node) != 0 || (!kGreedy && __ballot(active && zd == -INFINITY) != 0)) {
+      reject(true);  // a malformed node, or q(x) = 0 at some node: before any uniform is used
+      done = true;
+    } else if constexpr (!kGreedy) {
+      if (active) l2d_self = rows[N + 1 + lane].l2;
+      if (P.dg.target_lse)
+        for (int r = lane; r <= N; r += kWave) P.dg.target_lse[trow0 + r] = rows[r].l2 * kLn2;
+      if (active) {
+        if (P.dg.draft_lse) P.dg.draft_lse[drow0 + lane] = l2d_self * kLn2;
+        if (P.dg.target_logit) P.dg.target_logit[drow0 + lane] = zt;
+        if (P.dg.draft_logit) P.dg.draft_logit[drow0 + lane] = zd;
+      }
+    }
+  }
+  for (;;) {
+    if (wave == 0) {
+      int32_t action = kTreeDone, token = -1;
+      if (done) {
+        // nothing: every wave leaves below
+      } else if constexpr (kGreedy) {
+        for (;;) {  // follow the first child equal to the node's argmax
+          token = rows[u + 1].argmax;
+          if (P.dg.target_argmax && lane == 0) P.dg.target_argmax[trow0 + u + 1] = token;
+          const uint64_t hit = __ballot(active && par == u && x == token);
+          if (!hit) break;
+          const int32_t c = __ffsll((unsigned long long)hit) - 1;
+          if (lane == a) path_node = c;
+          ++a;
+          u = c;
+        }
+        action = kTreeDraw;
+      } else {
+        for (;;) {
+          const uint64_t kids = __ballot(active && par == u && lane >= cpos);
+          if (!kids) {  // every child tested and rejected, or none: the extra token
+            action = kTreeDraw;
+            break;
+          }
+          const int32_t c = __ffsll((unsigned long long)kids) - 1;  // children in node order
+          cpos = c + 1;
+          const double l2u = rows[u + 1].l2, l2dc = lane_value(l2d_self, c);
+          const double ztc = (double)lane_value(zt, c), zdc = (double)lane_value(zd, c);
+          double ratio;
+          if (l == 0) {  // the node's own p: log2 p(x)/q(x) = (z_t - z_d) k - (l2_t - l2_d)
+            ratio = exp2((ztc - zdc) * (double)k2 - (l2u - l2dc));
+          } else {  // R_l(x) / (M_l q(x)); lane j < l gathers rejected child j's draft logit at x
+            const int32_t xc = lane_value(x, c);
+            const float zj = lane < l ? E::at(row_ptr<E>(P.draft, rej_drow, P.V), xc) : 0.0f;
+            double R = exp2(ztc * (double)k2 - l2u);
+            for (int j = 0; j < l; ++j)
+              R = fmax(R - lane_value(rej_m, j) * exp2((double)lane_value(zj, j) * (double)k2 - lane_value(rej_l2, j)),
+                       0.0);
+            ratio = R / (M_l * exp2(zdc * (double)k2 - l2dc));
+          }
+          const Philox4 blk = verifier_block(P.seed, (uint32_t)i, (uint32_t)c);
+          const double r = (double)accept_uniform(blk);
+          if (lane == 0) {
+            if (P.dg.ratio) P.dg.ratio[drow0 + c] = ratio;
+            if (P.dg.accept_uniform) P.dg.accept_uniform[drow0 + c] = (float)r;
+          }
+          if (r <= ratio) {  // accepted: c becomes the current node (its children follow it in node order)
+            if (lane == a) path_node = c;
+            ++a;
+            u = c;
+            l = 0;
+            M_l = 1.0;
+            rejected = false;
+            continue;
+          }
+          // rejected: c joins the residual; the workgroup computes the chunk masses of R_{l+1}
+          if (lane == l) {
+            rej_drow = drow0 + c;
+            rej_l2 = l2dc;
+            rej_m = M_l;
+          }
+          ++l;
+          rejected = true;
+          action = kTreePass;
+          break;
+        }
+      }
+      if (lane == 0) {
+        step.action = action;
+        step.row = u + 1;
+        step.token = token;
+        if constexpr (!kGreedy) {
+          step.kind = !rejected ? SDV_TERM_BONUS : (l == 0 ? SDV_TERM_RESIDUAL_EMPTY : SDV_TERM_RESIDUAL);
+          step.u = (double)draw_uniform(verifier_block(P.seed, (uint32_t)i, (uint32_t)(u + 1)));
+        } else {
+          step.kind = SDV_TERM_GREEDY;
+        }
+      }
+      if constexpr (!kGreedy) {  // the residual's frame, for the pass and the in-chunk search
+        if (!done) {
+          const double l2 = rows[u + 1].l2;
+          if (lane == 0) {
+            frame.l = l;
+            frame.k2 = k2;
+            frame.t_hi = (float)l2;
+            frame.t_lo = (float)(l2 - (double)(float)l2);
+          }
+          if (lane < l) {
+            frame.drow[lane] = rej_drow;
+            frame.d_hi[lane] = (float)rej_l2;
+            frame.d_lo[lane] = (float)(rej_l2 - (double)(float)rej_l2);
+            frame.m[lane] = (float)rej_m;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (step.action != kTreePass) break;  // uniform: every wave read the same shared value
+    chain_masses<E, kVec>(frame, row_ptr<E>(P.target, trow0 + step.row, P.V), P.draft, P.V, P.C, lds_mass, lane, wave,
+                          n_waves);
+    __syncthreads();
+    if (wave == 0) {  // M_l; a residual without positive mass restarts from the node's own p
+      double S = 0.0;
+      for (int32_t c = lane; c < P.C; c += kWave) S += lds_mass[c];
+      S = wave_sum(S);
+      if (S > 0.0) {
+        M_l = S;
+      } else {
+        l = 0;
+        M_l = 1.0;
+      }
+    }
+  }
+  if (step.action != kTreeDraw || wave != 0) return;
+
+  // 3. the extra token (wave 0) and the outputs
+  const int32_t row = step.row;
+  int32_t y = step.token;
+  double S = 1.0;
+  if constexpr (!kGreedy) {
+    const char* tp = row_ptr<E>(P.target, trow0 + row, P.V);
+    double tgt = 0.0;
+    if (step.kind == SDV_TERM_RESIDUAL) {  // R_l by the chunk masses of the last pass
+      const int32_t cs = pick_chunk(P.C, step.u, [&](int32_t c) { return lds_mass[c]; }, &tgt, &S, lane);
+      const int32_t s0 = cs * E::kChunk;
+      y = search_chunk<E>(s0, min(E::kChunk, P.V - s0), tgt,
+                          [&](int32_t v) { return chain_weight<E>(frame, tp, P.draft, P.V, v); }, lane);
+    } else {  // the node's own p, by its records (the frame 2^(z k - ref))
+      const float2* rec = rec_t + (int64_t)row * P.C;
+      const float ref = rows[row].ref;
+      const int32_t cs = pick_chunk(
+          P.C, step.u, [&](int32_t c) { return (double)rec[c].y * exp2((double)rec[c].x - (double)ref); }, &tgt, &S,
+          lane);
+      const int32_t s0 = cs * E::kChunk;
+      y = search_chunk<E>(s0, min(E::kChunk, P.V - s0), tgt,
+                          [&](int32_t v) { return fast_exp2(fmaf(E::at(tp, v), k2, -ref)); }, lane);
+      S *= exp2((double)ref - rows[row].l2);  // probability units
+    }
+  }
+  const int32_t path_tok = __shfl(x, path_node < 0 ? 0 : path_node, kWave);
+  for (int d = lane; d <= N; d += kWave) P.out_tokens[trow0 + d] = d < a ? path_tok : (d == a ? y : -1);
+  for (int d = lane; d < N; d += kWave) P.accepted_nodes[drow0 + d] = d < a ? path_node : -1;
+  if (lane == 0) {
+    P.accepted_len[i] = a;
+    if (P.dg.terminal_kind) P.dg.terminal_kind[i] = step.kind;
+    if (!kGreedy && P.dg.draw_uniform) P.dg.draw_uniform[i] = (float)step.u;
+    if (!kGreedy && P.dg.terminal_mass) P.dg.terminal_mass[i] = S;
+  }
+}
+
 // ============================================================================ Philox test hook
 
 __global__ void philox_kernel(const uint32_t* __restrict__ ctr, const uint32_t* __restrict__ key, int64_t n,
@@ -2681,6 +3028,39 @@ int launch_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
   return launch_vec<E, kModeSampling>(P, vec, stream, diag);
 }
 
+// Token trees: the row pass as for linear drafts (the layout is the same), then one verdict
+// workgroup per request walks its tree.
+template <class E, bool kGreedy, bool kVec>
+int launch_tree(Params& P, hipStream_t stream, const sdv_diag* diag) {
+  auto record = [&](int k) {
+    if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
+  };
+  constexpr int kMode = kGreedy ? kModeGreedy : kModeSampling;
+  P.n_units = (int64_t)(kGreedy ? P.n_t : P.n_t + P.n_d) * P.C;
+  P.hist = nullptr;
+  P.split = 1;
+  record(0);
+  hipLaunchKernelGGL((row_records<E, kMode, kVec, false>), dim3((unsigned)((P.n_units + kRowWaves - 1) / kRowWaves)),
+                     dim3(kWave * kRowWaves), 0, stream, P);
+  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+  record(1);
+  const int64_t want = (int64_t)(2 * SDV_MAX_DEPTH + 1) * P.C;
+  const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
+  P.lds_records = want < room ? want : room;
+  const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
+  hipLaunchKernelGGL((tree_verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves), lds, stream, P);
+  if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+  record(2);
+  return SDV_OK;
+}
+
+template <class E>
+int launch_tree_any(Params& P, bool vec, hipStream_t stream, const sdv_diag* diag) {
+  if (P.k2 == 0.0f)
+    return vec ? launch_tree<E, true, true>(P, stream, diag) : launch_tree<E, true, false>(P, stream, diag);
+  return vec ? launch_tree<E, false, true>(P, stream, diag) : launch_tree<E, false, false>(P, stream, diag);
+}
+
 // ---------------------------------------------------------------------------- the no-alloc entry point
 // sdv_verify_noalloc keeps its workspace in this array instead of the caller's: each GPU the library
 // runs on holds one copy, at its own address, until the process ends.  In host code the name stands
@@ -2813,9 +3193,72 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   return launch_any<F32>(P, vec, s, diag);
 }
 
+int verify_tree_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                     const int32_t* parents, const int32_t* ragged_offsets, int32_t B, int64_t n_nodes, int32_t V,
+                     int32_t dtype, double temperature, uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes,
+                     int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+  Layout L;
+  const int shape = make_layout(B, n_nodes, V, dtype, &L);
+  if (shape != SDV_OK) return shape;
+  if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
+  if (n_nodes > 0 && (!draft_tokens || !parents || !accepted_nodes)) return SDV_ERR_INVALID_ARG;
+  if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;
+  float k2 = 0.0f;
+  if (temperature > 0.0) {
+    k2 = (float)(1.4426950408889634074 / temperature);
+    if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
+    if (n_nodes > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
+  }
+  if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % kAlign != 0) return SDV_ERR_WORKSPACE;
+  const int esize = dtype == SDV_BF16 ? 2 : 4;
+  const void* draft = k2 > 0.0f ? draft_logits : nullptr;
+  const bool vec = ((uintptr_t)target_logits % 16 == 0) && (draft == nullptr || (uintptr_t)draft % 16 == 0) &&
+                   ((int64_t)V * esize) % 16 == 0;
+  char* ws = static_cast<char*>(workspace);
+  Params P{};
+  P.target = target_logits;
+  P.draft = draft;
+  P.tokens = draft_tokens;
+  P.parents = parents;
+  P.accepted_nodes = accepted_nodes;
+  P.cu = ragged_offsets;
+  P.accepted_len = accepted_len;
+  P.out_tokens = out_tokens;
+  P.part = reinterpret_cast<float2*>(ws + L.part);
+  P.B = B;
+  P.n_d = (int32_t)n_nodes;
+  P.n_t = (int32_t)L.n_t;
+  P.V = V;
+  P.C = L.C;
+  P.k2 = k2;
+  P.seed = seed;
+  P.cuts = reinterpret_cast<Cut*>(ws + L.cuts);
+  P.split_mass = reinterpret_cast<double*>(ws + L.split_mass);
+  P.split_count = reinterpret_cast<uint32_t*>(ws + L.split_count);
+  P.batch_ok = reinterpret_cast<int32_t*>(P.split_count + (int64_t)B * kLineWords);
+  P.Cm = (L.C + 15) / 16 * 16;
+  if (diag) {
+    P.dg = DiagPtrs{diag->target_lse,     diag->draft_lse,    diag->target_argmax, diag->ratio,
+                    diag->accept_uniform, diag->draw_uniform, diag->terminal_kind, diag->target_logit,
+                    diag->draft_logit,    diag->terminal_mass};
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == SDV_BF16) return launch_tree_any<Bf16>(P, vec, s, diag);
+  return launch_tree_any<F32>(P, vec, s, diag);
+}
+
 }  // namespace sdv
 
 extern "C" {
+
+int sdv_verify_tree(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                    const int32_t* parents, const int32_t* ragged_offsets, int32_t B, int64_t n_nodes, int32_t V,
+                    int32_t dtype, double temperature, uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes,
+                    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+  return sdv::verify_tree_impl(target_logits, draft_logits, draft_tokens, parents, ragged_offsets, B, n_nodes, V,
+                               dtype, temperature, seed, accepted_len, accepted_nodes, out_tokens, workspace,
+                               workspace_bytes, stream, diag);
+}
 
 size_t sdv_noalloc_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype) {
   sdv::Layout L;

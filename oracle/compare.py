@@ -55,3 +55,47 @@ def compare_verdicts(acc_gpu, out_gpu, ref: dict, cu, temperature, eps: float = 
             what = f"drawn token {out_gpu[s][a_r]} vs {out_ref[s][a_r]}, oracle CDF margin {margin:.3g}"
         (excused if margin < eps else hard).append((i, what))
     return {"requests": B, "hard": hard, "excused": excused, "n_hard": len(hard), "n_excused": len(excused)}
+
+
+def compare_tree_verdicts(acc_gpu, out_gpu, nodes_gpu, ref: dict, cu, parents, temperature,
+                          eps: float = 1e-6) -> dict:
+    """Token trees.  ref: oracle.verify_tree(..., diag=True).  A request must match the oracle's
+    accepted depth, path (accepted_nodes) and tokens exactly; the only excuse is a first divergence
+    at a decision the oracle took within eps of its threshold: an accept test of a child of the last
+    common node (|r - ratio| < eps at a child the oracle tested there), or, with equal paths, the
+    extra token's draw (CDF margin < eps).  Greedy trees have no excuse."""
+    acc_gpu, out_gpu, nodes_gpu = np.asarray(acc_gpu), np.asarray(out_gpu), np.asarray(nodes_gpu)
+    cu, parents = np.asarray(cu), np.asarray(parents)
+    acc_ref, out_ref, nodes_ref = ref["accepted_len"], ref["out_tokens"], ref["accepted_nodes"]
+    B = acc_ref.shape[0]
+    hard, excused = [], []
+    for i in range(B):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        N = hi - lo
+        if acc_ref[i] == -1 and not (0 <= N <= 64 and lo >= 0 and hi <= nodes_ref.shape[0]):
+            if acc_gpu[i] != -1:
+                hard.append((i, "invalid request not rejected"))
+            continue
+        s = slice(lo + i, hi + i + 1)
+        if (acc_gpu[i] == acc_ref[i] and np.array_equal(out_gpu[s], out_ref[s])
+                and np.array_equal(nodes_gpu[lo:hi], nodes_ref[lo:hi])):
+            continue
+        if temperature == 0 or acc_ref[i] == -1 or acc_gpu[i] == -1:
+            hard.append((i, f"accepted {acc_gpu[i]} vs {acc_ref[i]}"))
+            continue
+        a_g, a_r = int(acc_gpu[i]), int(acc_ref[i])
+        pg, pr = nodes_gpu[lo:lo + a_g].tolist(), nodes_ref[lo:lo + a_r].tolist()
+        d = 0
+        while d < min(a_g, a_r) and pg[d] == pr[d]:
+            d += 1
+        if d < max(a_g, a_r):  # the walks part at depth d: an accept test among the children of the common node
+            u = pr[d - 1] if d > 0 else -1
+            kids = [lo + c for c in range(N) if parents[lo + c] == u]
+            m = ref["accept_margin"][kids]
+            margin = float(np.nanmin(m)) if np.isfinite(m).any() else np.inf
+            what = f"paths part at depth {d} (node {u}), smallest oracle accept margin there {margin:.3g}"
+        else:
+            margin = ref["cdf_margin"][i]
+            what = f"drawn token {out_gpu[s][a_r]} vs {out_ref[s][a_r]}, oracle CDF margin {margin:.3g}"
+        (excused if margin < eps else hard).append((i, what))
+    return {"requests": B, "hard": hard, "excused": excused, "n_hard": len(hard), "n_excused": len(excused)}

@@ -31,7 +31,8 @@ def test_every_declared_function_is_exported(lib):
     assert set(names) >= {"sdv_verify", "sdv_verify_ex", "sdv_workspace_bytes", "sdv_philox4x32_10",
                           "sdv_read_ceiling", "sdv_verify_profiled", "sdv_verify_opts", "sdv_sdcp_uniforms", "sdv_commit",
                           "sdv_status_string", "sdv_abi_version", "sdv_philox_uniforms",
-                          "sdv_verify_noalloc", "sdv_noalloc_bytes", "sdv_read_yardstick", "sdv_repad"}
+                          "sdv_verify_noalloc", "sdv_noalloc_bytes", "sdv_read_yardstick", "sdv_repad",
+                          "sdv_verify_tree"}
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sdv.h but not exported"
 
@@ -185,6 +186,26 @@ def test_repad_host_argument_checks(lib):
     assert call(n_d=2**31) == -3
     assert call(n_p=2**31) == -3
     assert call(B=2**20, width=2**21) == -3  # B * width above 2^40
+
+
+def test_verify_tree_host_argument_checks(lib):
+    def call(B=1, n=2, V=8, dtype=1, T=1.0, ws_bytes=1 << 20, **ptrs):
+        p = dict(target=FAKE, draft=FAKE, tokens=FAKE, parents=FAKE, cu=FAKE, acc=FAKE, nodes=FAKE, out=FAKE, ws=FAKE)
+        p.update(ptrs)
+        return lib.sdv_verify_tree(p["target"], p["draft"], p["tokens"], p["parents"], p["cu"], B, n, V, dtype, T, 1,
+                                   p["acc"], p["nodes"], p["out"], p["ws"], ws_bytes, None, None)
+    assert call(B=0) == -1
+    assert call(V=0) == -1
+    assert call(dtype=7) == -2
+    assert call(T=-1.0) == -1
+    assert call(T=float("nan")) == -1
+    assert call(T=1e-45) == -1  # log2(e) / T overflows binary32
+    assert call(draft=None) == -1  # T > 0 needs draft rows
+    for name in ("target", "tokens", "parents", "cu", "acc", "nodes", "out"):
+        assert call(**{name: None}) == -1, name
+    need = lib.sdv_workspace_bytes(1, 2, 8, 1)
+    assert call(ws_bytes=need - 1) == -4
+    assert call(ws=None) == -4
 
 
 def test_verify_ex_accepts_null_diag_checks_first(lib):

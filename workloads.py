@@ -50,6 +50,7 @@ class Batch:
     qrows: np.ndarray | None = None      # (n_draft_rows, V) float32 draft distributions, else None
     top_k: np.ndarray | None = None      # (B,) int32 top-k of each request's profile, else None
     top_p_milli: np.ndarray | None = None  # (B,) int32 top-p in thousandths, else None
+    parents: np.ndarray | None = None    # (n_draft_rows,) int32: token trees, each node's parent (-1: root)
 
     @property
     def B(self) -> int:
@@ -276,3 +277,48 @@ def greedy_b512(data_seed: int = DATA_SEED_BASE + 5, verify_seed: int = 5000, B:
     proposes its argmax; ties go to the lowest index."""
     return make_random(f"greedy_b{B}_k4_v{V}_bf16", np.full(B, 4), V, "bf16", 0.0, 4.0, 1.0,
                        data_seed=data_seed, verify_seed=verify_seed)
+
+
+def tree_parents(kind: str, n: int, rng: np.random.Generator, branching: int = 2) -> np.ndarray:
+    """Parents of an n-node tree in node order (every parent precedes its children; -1 is the
+    root): "chain", "star" (all children of the root), "kary" (breadth-first, `branching` children
+    per node), or "random" (each node's parent uniform over the root and the earlier nodes)."""
+    if kind == "chain":
+        return np.arange(-1, n - 1, dtype=np.int32)
+    if kind == "star":
+        return np.full(n, -1, dtype=np.int32)
+    if kind == "kary":
+        return np.array([(k // branching) - 1 if k >= branching else -1 for k in range(n)], dtype=np.int32)
+    if kind == "random":
+        return np.array([rng.integers(-1, k) if k > 0 else -1 for k in range(n)], dtype=np.int32)
+    raise ValueError(kind)
+
+
+def make_tree(name: str, sizes, kind: str, V: int, dtype: str, temperature: float, target_sigma: float,
+              draft_sigma: float, data_seed: int, verify_seed: int, branching: int = 2) -> Batch:
+    """Token-tree batch: request i holds sizes[i] nodes in the given shape.  Target rows are
+    Gaussian (row 0 of a request at the root, row n + 1 after node n).  The drafter's row at a node's
+    context is that context's target row plus Gaussian noise, shared by all of the node's children
+    (draft row of node n = the row its token was drawn from), and each child's token is drawn from
+    it independently (Gumbel-max at temperature T, or its argmax at T = 0)."""
+    rng = np.random.Generator(np.random.Philox(data_seed))
+    sizes = np.asarray(sizes, dtype=np.int64)
+    B = sizes.shape[0]
+    cu = offsets_from_depths(sizes)
+    n = int(cu[-1])
+    parents = np.concatenate([tree_parents(kind, int(k), rng, branching) for k in sizes]).astype(np.int32) \
+        if n else np.zeros(0, dtype=np.int32)
+    tgt = rng.standard_normal((n + B, V), dtype=np.float32)
+    tgt *= np.float32(target_sigma)
+    noise = rng.standard_normal((n + B, V), dtype=np.float32)  # one drafter row per context (target row)
+    noise *= np.float32(draft_sigma)
+    req = np.repeat(np.arange(B), sizes)
+    ctx_row = cu[req] + req + parents + 1  # the target row of each node's parent context
+    drf = tgt[ctx_row] + noise[ctx_row]
+    target = _store(tgt, dtype)
+    draft = _store(drf, dtype)
+    del tgt, noise, drf
+    tokens = _argmax_tokens(draft, dtype) if temperature == 0 else _gumbel_tokens(rng, draft, dtype, temperature)
+    return Batch(name=name, V=V, dtype=dtype, temperature=float(temperature), seed=int(verify_seed),
+                 target=target, draft=draft if temperature > 0 else None, tokens=tokens, cu=cu, parents=parents,
+                 meta={"data_seed": data_seed, "kind": kind, "target_sigma": target_sigma, "draft_sigma": draft_sigma})
