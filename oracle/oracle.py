@@ -96,7 +96,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.oracle_verify_tree.restype = ctypes.c_int
     lib.oracle_verify_tree.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(_Diag),
     ]
     lib.oracle_philox4x32_10.restype = None
@@ -303,13 +303,15 @@ def set_num_threads(n: int) -> None:
 
 
 def verify_tree(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.ndarray, parents: np.ndarray,
-                cu: np.ndarray, temperature: float, seed: int, diag: bool = False, lib_path: str = LIBRARY) -> dict:
+                cu: np.ndarray, temperature: float, seed: int, diag: bool = False, lib_path: str = LIBRARY,
+                draft_row: np.ndarray | None = None) -> dict:
     """Run the oracle's token-tree verification (oracle_verify_tree) on one batch.
 
     target: (n_nodes + B, V), row cu[i] + i at request i's root and cu[i] + i + n + 1 after node n;
-    draft: (n_nodes, V), row cu[i] + n the distribution node n was drawn from (None when
-    temperature == 0); draft_tokens, parents: (n_nodes,) int32, parents in [-1, n - 1] within the
-    request; cu: (B + 1,) node offsets.  Returns accepted_len (B,), out_tokens (n_nodes + B,),
+    draft: (n_draft_rows, V), the distributions the nodes were drawn from (None when temperature == 0):
+    row draft_row[cu[i] + n] for node n, or row cu[i] + n without draft_row (n_draft_rows = n_nodes);
+    draft_tokens, parents: (n_nodes,) int32, parents in [-1, n - 1] within the request; cu: (B + 1,)
+    node offsets.  Returns accepted_len (B,), out_tokens (n_nodes + B,),
     accepted_nodes (n_nodes,), and with ``diag`` the LSEs, argmaxes, ratios and accept margins of
     the nodes tested (NaN elsewhere), cdf margins, residual masses and terminal kinds.
     """
@@ -328,6 +330,11 @@ def verify_tree(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.n
     V = target.shape[1]
     if target.shape[0] != n + B or parents.shape[0] != n:
         raise ValueError("target must have n_nodes + B rows and parents n_nodes entries")
+    if draft_row is not None:
+        draft_row = np.ascontiguousarray(draft_row, dtype=np.int32)
+        if draft_row.shape[0] != n:
+            raise ValueError("draft_row must have n_nodes entries")
+    n_dr = n if draft_row is None else (draft.shape[0] if draft is not None else int(draft_row.max(initial=-1)) + 1)
     acc = np.full(B, -7, dtype=np.int32)
     out = np.full(n + B, -7, dtype=np.int32)
     nodes = np.full(n, -7, dtype=np.int32)
@@ -343,7 +350,8 @@ def verify_tree(target: np.ndarray, draft: np.ndarray | None, draft_tokens: np.n
         )
         dg = _Diag(*[_ptr(res[f]) for f, _ in _Diag._fields_])
         dg_p = ctypes.pointer(dg)
-    rc = lib.oracle_verify_tree(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(parents), _ptr(cu), B, n, V,
+    rc = lib.oracle_verify_tree(_ptr(target), _ptr(draft), dt, _ptr(draft_tokens), _ptr(parents), _ptr(draft_row), n_dr,
+                                _ptr(cu), B, n, V,
                                 float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(acc), _ptr(out), _ptr(nodes),
                                 dg_p)
     if rc != 0:

@@ -664,8 +664,9 @@ int oracle_verify_profiled(const void* target, const void* draft, int dtype, con
  *
  *  - request i has N_i nodes n = 0 .. N_i - 1 (offsets cu as for linear drafts, N_i <= 64); node
  *    n has parent parents[cu[i] + n] in [-1, n - 1] (-1: the root, the last committed token) and
- *    token tokens[cu[i] + n], sampled from q_n = softmax(draft row cu[i] + n / T), the drafter's
- *    distribution at its parent's context (siblings from one drafter carry equal draft rows);
+ *    token tokens[cu[i] + n], sampled from q_n = softmax(draft row d / T), the drafter's
+ *    distribution at its parent's context, with d = draft_row[cu[i] + n] when the caller gives
+ *    row indices (siblings from one drafter then share one row) and d = cu[i] + n otherwise;
  *  - target rows: cu[i] + i at the root, cu[i] + i + n + 1 after node n; a chain (node n the
  *    parent of node n + 1) is exactly a linear draft;
  *  - Rule 2 (T > 0): at the current node, with p its target distribution, the children are tested
@@ -686,8 +687,8 @@ int oracle_verify_profiled(const void* target, const void* draft, int dtype, con
  *  - a residual with S = 0 (impossible in exact arithmetic after a rejection) restarts from the
  *    current node's target distribution;
  *  - bad requests (accepted_len -1, every slot -1): a token outside [0, V), a parent outside
- *    [-1, n - 1], a temperature that describes no profile, and at T > 0 a node whose draft
- *    probability at its own token is zero.
+ *    [-1, n - 1], a draft row index outside [0, n_draft_rows), a temperature that describes no
+ *    profile, and at T > 0 a node whose draft probability at its own token is zero.
  * Outputs: accepted_len[i] = a, the depth of the accepted path; out_tokens[cu[i] + i + d] for
  * d < a the path's tokens, then the extra token, then -1 up to slot N_i; accepted_nodes[cu[i] + d]
  * for d < a the path's node indices, then -1 up to N_i - 1.  diag: target_lse / draft_lse of
@@ -695,9 +696,10 @@ int oracle_verify_profiled(const void* target, const void* draft, int dtype, con
  * and resid_mass = the product of the stage masses S of the draw's residual (1 for a bonus).
  */
 static void verify_tree_request(const void* target, const void* draft, int dtype, const int32_t* tokens,
-                                const int32_t* parents, const int32_t* cu, int32_t i, int64_t n_nodes, int32_t V,
-                                double T, uint64_t seed, int32_t* accepted_len, int32_t* out_tokens,
-                                int32_t* accepted_nodes, oracle_diag* dg, double* p, double* q) {
+                                const int32_t* parents, const int32_t* draft_row, int64_t n_draft_rows,
+                                const int32_t* cu, int32_t i, int64_t n_nodes, int32_t V, double T, uint64_t seed,
+                                int32_t* accepted_len, int32_t* out_tokens, int32_t* accepted_nodes, oracle_diag* dg,
+                                double* p, double* q) {
   const int64_t lo = cu[i], hi = cu[i + 1];
   const int64_t N = hi - lo;
   if (dg && dg->cdf_margin) dg->cdf_margin[i] = NAN;
@@ -720,16 +722,18 @@ static void verify_tree_request(const void* target, const void* draft, int dtype
   }
 
   int bad = !(T >= 0.0) || isinf(T);
+  int64_t qrow[ORACLE_MAX_DEPTH]; /* the draft row of each node */
   for (int64_t n = 0; n < N && !bad; ++n) {
     const int32_t x = tokens[drow0 + n], par = parents[drow0 + n];
-    if (x < 0 || x >= V || par < -1 || par >= n) bad = 1;
+    qrow[n] = draft_row ? draft_row[drow0 + n] : drow0 + n;
+    if (x < 0 || x >= V || par < -1 || par >= n || qrow[n] < 0 || qrow[n] >= n_draft_rows) bad = 1;
   }
   double lse_t[ORACLE_MAX_DEPTH + 1], lse_d[ORACLE_MAX_DEPTH];
   if (!bad && T > 0.0) {
     for (int64_t r = 0; r <= N; ++r) lse_t[r] = oracle_row_lse(target, dtype, trow0 + r, V, T);
     for (int64_t n = 0; n < N; ++n) {
-      lse_d[n] = oracle_row_lse(draft, dtype, drow0 + n, V, T);
-      if (logit_at(draft, dtype, drow0 + n, V, tokens[drow0 + n]) == -INFINITY) bad = 1; /* q_n(x_n) = 0 */
+      lse_d[n] = oracle_row_lse(draft, dtype, qrow[n], V, T);
+      if (logit_at(draft, dtype, qrow[n], V, tokens[drow0 + n]) == -INFINITY) bad = 1; /* q_n(x_n) = 0 */
     }
   }
   if (bad) {
@@ -780,11 +784,11 @@ static void verify_tree_request(const void* target, const void* draft, int dtype
           pending = 0;
         }
         const int32_t x = tokens[drow0 + c];
-        for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, drow0 + c, V, v) / T - lse_d[c]);
+        for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, qrow[c], V, v) / T - lse_d[c]);
         /* the first child sees the node's own p: its ratio in the log form of the linear walk */
         const double ratio =
             rejected ? p[x] / q[x]
-                     : exp((logit_at(target, dtype, trow0 + row, V, x) - logit_at(draft, dtype, drow0 + c, V, x)) / T -
+                     : exp((logit_at(target, dtype, trow0 + row, V, x) - logit_at(draft, dtype, qrow[c], V, x)) / T -
                            (lse_t[row] - lse_d[c]));
         uint32_t blk[4];
         oracle_philox_block(seed, (uint32_t)i, (uint32_t)c, blk);
@@ -834,17 +838,19 @@ static void verify_tree_request(const void* target, const void* draft, int dtype
 }
 
 /*
- * Token-tree batches (see above).  target [n_nodes + B][V], draft [n_nodes][V] (may be NULL when
- * T == 0), draft_tokens and parents [n_nodes], cu [B + 1] node offsets, accepted_len [B],
- * out_tokens [n_nodes + B], accepted_nodes [n_nodes].  Returns 0, or -1 for arguments that
- * describe no batch.
+ * Token-tree batches (see above).  target [n_nodes + B][V], draft [n_draft_rows][V] (may be NULL
+ * when T == 0), draft_tokens and parents [n_nodes], draft_row [n_nodes] each node's draft row (NULL:
+ * node cu[i] + n takes row cu[i] + n, and n_draft_rows must be n_nodes), cu [B + 1] node offsets,
+ * accepted_len [B], out_tokens [n_nodes + B], accepted_nodes [n_nodes].  Returns 0, or -1 for
+ * arguments that describe no batch.
  */
 int oracle_verify_tree(const void* target, const void* draft, int dtype, const int32_t* draft_tokens,
-                       const int32_t* parents, const int32_t* cu, int32_t B, int64_t n_nodes, int32_t V, double T,
-                       uint64_t seed, int32_t* accepted_len, int32_t* out_tokens, int32_t* accepted_nodes,
-                       oracle_diag* diag) {
+                       const int32_t* parents, const int32_t* draft_row, int64_t n_draft_rows, const int32_t* cu,
+                       int32_t B, int64_t n_nodes, int32_t V, double T, uint64_t seed, int32_t* accepted_len,
+                       int32_t* out_tokens, int32_t* accepted_nodes, oracle_diag* diag) {
   if (!target || !draft_tokens || !parents || !cu || !accepted_len || !out_tokens || !accepted_nodes) return -1;
   if (B <= 0 || V <= 0 || n_nodes < 0 || !(T >= 0.0) || isinf(T) || (T > 0.0 && !draft && n_nodes > 0)) return -1;
+  if (n_draft_rows < 0 || (!draft_row && n_draft_rows != n_nodes)) return -1;
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP32) return -1;
   int failed = 0;
 #pragma omp parallel reduction(| : failed)
@@ -854,8 +860,8 @@ int oracle_verify_tree(const void* target, const void* draft, int dtype, const i
 #pragma omp for schedule(dynamic, 1)
     for (int32_t i = 0; i < B; ++i)
       if (p)
-        verify_tree_request(target, draft, dtype, draft_tokens, parents, cu, i, n_nodes, V, T, seed, accepted_len,
-                            out_tokens, accepted_nodes, diag, p, p + V);
+        verify_tree_request(target, draft, dtype, draft_tokens, parents, draft_row, n_draft_rows, cu, i, n_nodes, V,
+                            T, seed, accepted_len, out_tokens, accepted_nodes, diag, p, p + V);
     free(p);
   }
   return failed ? -2 : 0;

@@ -82,13 +82,14 @@ MUTATIONS = {
                                    "oracle_philox_block(seed, (uint32_t)i, (uint32_t)a, blk);"),
     "tree_draw_block_of_node_index": ("oracle_philox_block(seed, (uint32_t)i, (uint32_t)row, blk);",
                                       "oracle_philox_block(seed, (uint32_t)i, (uint32_t)(row > 0 ? row - 1 : 0), blk);"),
-    "tree_q_of_first_sibling": ("for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, drow0 + c, V, v) / T - lse_d[c]);",
-                                "for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, drow0 + u + 1, V, v) / T - lse_d[u + 1]);"),
+    "tree_q_of_first_sibling": ("for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, qrow[c], V, v) / T - lse_d[c]);",
+                                "for (int32_t v = 0; v < V; ++v) q[v] = exp(logit_at(draft, dtype, qrow[u + 1], V, v) / T - lse_d[u + 1]);"),
     "tree_stops_at_first_rejection": ("      for (int64_t c = u + 1; c < N && next < 0; ++c) {\n        if (parents[drow0 + c] != u) continue;",
                                       "      for (int64_t c = u + 1; c < N && next < 0 && !rejected; ++c) {\n        if (parents[drow0 + c] != u) continue;"),
     "tree_greedy_last_matching_child": ("      for (int64_t c = u + 1; c < N && next < 0; ++c) /* a child's index exceeds its parent's */",
                                         "      for (int64_t c = u + 1; c < N; ++c) /* a child's index exceeds its parent's */"),
-    "tree_parent_check_off_by_one": ("if (x < 0 || x >= V || par < -1 || par >= n) bad = 1;", "if (x < 0 || x >= V || par < -1 || par > n) bad = 1;"),
+    "tree_draft_row_index_ignored": ("qrow[n] = draft_row ? draft_row[drow0 + n] : drow0 + n;", "qrow[n] = drow0 + n < n_draft_rows ? drow0 + n : 0;"),
+    "tree_parent_check_off_by_one": ("if (x < 0 || x >= V || par < -1 || par >= n ||", "if (x < 0 || x >= V || par < -1 || par > n ||"),
 }
 
 

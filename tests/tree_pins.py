@@ -233,4 +233,46 @@ def pin_tree_keying(lib_path: str = oracle.LIBRARY, seed: int = 0x7EE5) -> bool:
     return True
 
 
-ALL = (pin_hand_worked, pin_chain_equals_linear, pin_greedy_brute_force, pin_lossless, pin_tree_keying)
+def shared_rows(b):
+    """The batch's per-node draft rows folded to one row per parent context: (rows, draft_row)."""
+    req = np.repeat(np.arange(b.B), np.diff(b.cu))
+    ctx = b.cu[req] + req + b.parents + 1  # each node's parent context, as a target row index
+    keys, first, draft_row = np.unique(ctx, return_index=True, return_inverse=True)
+    return np.ascontiguousarray(b.draft[first]), draft_row.astype(np.int32)
+
+
+def pin_shared_draft_rows(lib_path: str = oracle.LIBRARY) -> bool:
+    """Siblings that share one draft row by index give the verdicts (and diagnostics) of the same
+    tree with a copy of that row per node; an index outside the rows rejects its request alone."""
+    from workloads import make_tree
+    for T, kind in ((1.0, "random"), (0.8, "kary"), (0.0, "star")):
+        rng = np.random.default_rng(86)
+        b = make_tree("shared", rng.integers(0, 20, size=40), kind, 200, "fp32", T, 2.0, 1.0, data_seed=87,
+                      verify_seed=3)
+        draft = b.draft if T > 0 else np.zeros((b.n_draft_rows, b.V), np.float32)
+        rows, idx = shared_rows(type(b)(**{**b.__dict__, "draft": draft}))
+        if T > 0 and rows.shape[0] >= b.n_draft_rows:
+            return False  # the batch must actually share rows
+        full = oracle.verify_tree(b.target, b.draft, b.tokens, b.parents, b.cu, T, 5, diag=True, lib_path=lib_path)
+        comp = oracle.verify_tree(b.target, rows if T > 0 else None, b.tokens, b.parents, b.cu, T, 5, diag=True,
+                                  lib_path=lib_path, draft_row=idx)
+        for k in ("accepted_len", "out_tokens", "accepted_nodes", "terminal_kind"):
+            if not np.array_equal(full[k], comp[k]):
+                return False
+        for k in ("ratio", "resid_mass", "draft_lse"):
+            if not np.array_equal(full[k], comp[k], equal_nan=True):
+                return False
+        if T > 0:
+            bad = idx.copy()
+            i = int(np.argmax(np.diff(b.cu) > 0))  # a request with nodes
+            bad[b.cu[i]] = rows.shape[0]
+            res = oracle.verify_tree(b.target, rows, b.tokens, b.parents, b.cu, T, 5, lib_path=lib_path, draft_row=bad)
+            others = np.arange(b.B) != i
+            if res["accepted_len"][i] != -1 or not np.array_equal(res["accepted_len"][others],
+                                                                   full["accepted_len"][others]):
+                return False
+    return True
+
+
+ALL = (pin_hand_worked, pin_chain_equals_linear, pin_greedy_brute_force, pin_lossless, pin_tree_keying,
+       pin_shared_draft_rows)
