@@ -66,7 +66,7 @@ def kernel_source_hash() -> str:
 
 
 WORKLOADS = ["ragged_b256", "greedy_b512", "uniform_b64", "small_b1", "small_b1_v128256", "ragged_b256_profiled",
-             "ragged_b256_qrows", "ragged_b256_topk50_topp900"]
+             "ragged_b256_qrows", "ragged_b256_topk50_topp900", "tree_b64_v128256"]
 
 
 def make_workload(name: str, set_index: int):
@@ -90,6 +90,10 @@ def make_workload(name: str, set_index: int):
         base = W.ragged_b256(data_seed=W.DATA_SEED_BASE + 4 + 1000 * set_index, verify_seed=4000)
         t, s = W.mixed_profiles(base.B, np.random.default_rng(W.DATA_SEED_BASE + 6 + set_index))
         return W.with_profiles(base, t, s, token_seed=W.DATA_SEED_BASE + 7 + set_index)
+    if name == "tree_b64_v128256":  # token trees: 64 random trees of 8 to 24 nodes
+        sizes = np.random.default_rng(W.DATA_SEED_BASE + 9 + 1000 * set_index).integers(8, 25, size=64)
+        return W.make_tree("tree_b64_n8to24_v128256_bf16", sizes, "random", 128256, "bf16", 1.0, 3.0, 1.5,
+                           data_seed=W.DATA_SEED_BASE + 10 + 1000 * set_index, verify_seed=9000, shared=True)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -146,8 +150,12 @@ def cpu_baseline(batch, budget_s: float):
         t_end = time.perf_counter() + budget
         while True:
             t0 = time.perf_counter()
-            oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, *oracle_profile(batch),
-                          **oracle_options(batch))
+            if batch.parents is not None:
+                oracle.verify_tree(batch.target, batch.draft, batch.tokens, batch.parents, batch.cu, batch.temperature,
+                                   batch.seed, draft_row=batch.draft_row)
+            else:
+                oracle.verify(batch.target, batch.draft, batch.tokens, batch.cu, *oracle_profile(batch),
+                              **oracle_options(batch))
             times.append(time.perf_counter() - t0)
             if len(times) >= 3 or time.perf_counter() > t_end:
                 return float(np.median(times)), len(times)
@@ -158,8 +166,9 @@ def cpu_baseline(batch, budget_s: float):
     t1, _ = timed(0.0)
     oracle.set_num_threads(cores)
     pos = int(batch.cu[-1])
+    what = "nodes" if batch.parents is not None else "sum K_i"
     return {"value": pos / t, "unit": "positions/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} oracle calls on one full {batch.name} batch (sum K_i = {pos}), median "
+            "sample": f"{n} oracle calls on one full {batch.name} batch ({what} = {pos}), median "
                       f"{t * 1e3:.1f} ms per call, fp64 C with OpenMP",
             "single_thread_value": pos / t1}
 
@@ -190,13 +199,13 @@ def qrow_bytes(batch, acc: np.ndarray) -> int:
 
 def acceptance_stats(batch, accs):
     """Mean accepted length, committed tokens per call and the acceptance rate by depth
-    (accepts at j / requests that reached j with a draft there)."""
+    (accepts at j / requests that reached j with a draft there; linear drafts only)."""
     K = batch.depths
     a = np.stack(accs)                      # calls x B
     ok = a >= 0
     committed = float(np.mean(np.sum(np.where(ok, a + 1, 0), axis=1)))
     by_depth = []
-    for j in range(int(K.max()) if K.size else 0):
+    for j in range(int(K.max()) if K.size and batch.parents is None else 0):
         reach = ok & (K[None, :] > j) & (a >= j)
         by_depth.append(float(np.sum(reach & (a > j)) / max(1, np.sum(reach))))
     return {"mean_accepted_len": float(np.mean(a[ok])), "committed_tokens_per_call": committed,
@@ -270,7 +279,12 @@ def main():
         if b.top_k is not None:
             sets[-1]["top_k"] = torch.from_numpy(b.top_k).to(dev)
             sets[-1]["top_p_milli"] = torch.from_numpy(b.top_p_milli).to(dev)
+        if b.parents is not None:
+            sets[-1]["parents"] = torch.from_numpy(b.parents).to(dev)
+            if b.draft_row is not None:
+                sets[-1]["draft_row"] = torch.from_numpy(b.draft_row).to(dev)
     B0 = batches[0]
+    tree = B0.parents is not None
     truncating = B0.top_k is not None
     kernels = TRUNCATION_KERNELS if truncating else KERNELS
     positions = [int(b.cu[-1]) for b in batches]
@@ -280,14 +294,19 @@ def main():
     ws = torch.empty(max(sdv.workspace_bytes(b.B, b.n_draft_rows, b.V, sets[0]["target"].dtype) for b in batches),
                      dtype=torch.uint8, device=dev)
     outs = [(torch.empty(b.B, dtype=torch.int32, device=dev),
-             torch.empty(b.n_draft_rows + b.B, dtype=torch.int32, device=dev)) for b in batches]
+             torch.empty(b.n_draft_rows + b.B, dtype=torch.int32, device=dev),
+             torch.empty(b.n_draft_rows, dtype=torch.int32, device=dev)) for b in batches]
 
     def step(k, events=None):
         s = sets[k % len(sets)]
         b = s["batch"]
         temperature, seed = (s["temp"], s["seeds"]) if "temp" in s else (b.temperature, b.seed + k)
+        if tree:
+            sdv.verify_tree(s["target"], s["draft"], s["tokens"], s["parents"], s["cu"], temperature, seed,
+                            draft_row=s.get("draft_row"), out=outs[k % len(sets)], workspace=ws, events=events)
+            return
         sdv.verify_ex(s["target"], s["draft"], s["tokens"], s["cu"], temperature, seed,
-                      out=outs[k % len(sets)], workspace=ws, events=events, draft_probs=s.get("qrows"),
+                      out=outs[k % len(sets)][:2], workspace=ws, events=events, draft_probs=s.get("qrows"),
                       top_k=s.get("top_k"), top_p_milli=s.get("top_p_milli"))
 
     # correctness of the timed configuration, once, against the oracle
@@ -297,9 +316,17 @@ def main():
         log("[bench] checking one call against the oracle")
         step(0)
         torch.cuda.synchronize()
-        ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, *oracle_profile(B0), diag=True,
-                            **oracle_options(B0))
-        cmp = compare_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ref, B0.cu, oracle_profile(B0)[0])
+        if tree:
+            from oracle.compare import compare_tree_verdicts
+            ref = oracle.verify_tree(B0.target, B0.draft, B0.tokens, B0.parents, B0.cu, B0.temperature, B0.seed,
+                                     diag=True, draft_row=B0.draft_row)
+            cmp = compare_tree_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), outs[0][2].cpu().numpy(),
+                                        ref, B0.cu, B0.parents, B0.temperature)
+        else:
+            ref = oracle.verify(B0.target, B0.draft, B0.tokens, B0.cu, *oracle_profile(B0), diag=True,
+                                **oracle_options(B0))
+            cmp = compare_verdicts(outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy(), ref, B0.cu,
+                                   oracle_profile(B0)[0])
         parity = {"requests": cmp["requests"], "hard_mismatches": cmp["n_hard"], "near_tie_excused": cmp["n_excused"]}
         if cmp["n_hard"]:
             raise SystemExit(f"GPU verdicts differ from the oracle: {cmp['hard'][:5]}")
@@ -366,7 +393,7 @@ def main():
         acc = outs[k % len(sets)][0].cpu().numpy()
         if k % len(sets) == 0:
             accs.append(acc)
-        rereads.append(reread_bytes(batches[k % len(sets)], acc))
+        rereads.append(0 if tree else reread_bytes(batches[k % len(sets)], acc))
         qbytes[k % len(sets)].append(qrow_bytes(batches[k % len(sets)], acc))
     stats = acceptance_stats(B0, accs)
     if B0.qrows is not None:  # q rows read at the corrections are part of each call's algorithmic bytes
@@ -417,8 +444,8 @@ def main():
         "call_ms_events": {"median": float(np.median(per_call)), "p5": float(np.percentile(per_call, 5)),
                            "p95": float(np.percentile(per_call, 95)), "n": int(per_call.size)},
         "kernel_ms": dict(zip(kernels, per_kernel)),
-        "terminal_reread_bytes_per_call": float(np.mean(rereads)),
-        "terminal_reread_frac_of_algorithmic": float(np.mean(rereads)) / mean_bytes,
+        "terminal_reread_bytes_per_call": None if tree else float(np.mean(rereads)),
+        "terminal_reread_frac_of_algorithmic": None if tree else float(np.mean(rereads)) / mean_bytes,
         "acceptance": stats,
         "roofline": {"bound": "hbm", "achieved": roof_gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": roof_gbps / PEAK_HBM_GBPS, "traffic": traffic_from_profile(args.workload, roof_kernel),

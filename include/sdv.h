@@ -279,9 +279,12 @@ int sdv_verify_opts(const void* target_logits, const void* draft_logits, const i
  *                                   every parent precedes its children
  *   draft_tokens  [n_nodes] int32   node n's token
  *   target_logits [n_nodes + B][V]  row cu[i] + i at the root, cu[i] + i + n + 1 after node n
- *   draft_logits  [n_nodes][V]      row cu[i] + n: the logits node n's token was drawn from (at its
- *                                   parent's context; siblings from one drafter carry equal rows);
- *                                   may be NULL when temperature == 0
+ *   draft_row     [n_nodes] int32   node n's draft row, in [0, n_draft_rows) (siblings from one
+ *                                   drafter share their parent context's row); NULL: node cu[i] + n
+ *                                   takes row cu[i] + n, and n_draft_rows must equal n_nodes
+ *   draft_logits  [n_draft_rows][V] the logits the nodes' tokens were drawn from (at each node's
+ *                                   parent's context), n_draft_rows <= n_nodes; may be NULL when
+ *                                   temperature == 0
  * A chain (every node the parent of the next) is exactly a linear draft of sdv_verify, with the
  * same uniforms and results.
  *   T > 0: at the current node (the root first), with p its target distribution softmax(z / T),
@@ -299,7 +302,8 @@ int sdv_verify_opts(const void* target_logits, const void* draft_logits, const i
  * cu[i] + i + N_i; accepted_nodes [n_nodes] the path's node indices (within the request) at
  * cu[i] .. cu[i] + a - 1, -1 up to cu[i] + N_i - 1.
  * Bad requests (accepted_len -1, every slot -1): a token outside [0, V), a parent outside
- * [-1, n - 1], or at T > 0 a node whose draft logit at its own token is -inf (q = 0).  Offsets that
+ * [-1, n - 1], at T > 0 a draft row index outside [0, n_draft_rows) or a node whose draft logit at
+ * its own token is -inf (q = 0).  Offsets that
  * are not valid, or a request of more than 64 nodes, reject without writing slots, as sdv_verify.
  * workspace: sdv_workspace_bytes(B, n_nodes, V, dtype).  diag (may be NULL): target_lse,
  * draft_lse, target_logit / draft_logit (z_t at the parent's row and z_d at each node's token),
@@ -307,13 +311,17 @@ int sdv_verify_opts(const void* target_logits, const void* draft_logits, const i
  * visited (T = 0), draw_uniform, terminal_kind, terminal_mass (the residual's mass in probability
  * units, M = product of the stage masses; about 1 for a bonus) and the events (row pass, verdicts).
  * Per-request profiles, truncation, stop lists and caller uniforms are not taken on this path.
- * Errors as sdv_verify; NULL parents, draft_tokens or accepted_nodes with n_nodes > 0 ->
- * SDV_ERR_INVALID_ARG.
+ * Errors as sdv_verify; NULL parents, draft_tokens or accepted_nodes with n_nodes > 0, n_draft_rows
+ * outside [0, n_nodes] (or other than n_nodes without draft_row), or T > 0 with n_draft_rows > 0 and
+ * NULL draft_logits -> SDV_ERR_INVALID_ARG.  A rejected sibling that shares the previous rejected
+ * sibling's draft row costs its residual pass no extra row: consecutive rejections on one row are
+ * applied to one load of it.
  */
 int sdv_verify_tree(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                    const int32_t* parents, const int32_t* ragged_offsets, int32_t B, int64_t n_nodes, int32_t V,
-                    int32_t dtype, double temperature, uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes,
-                    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
+                    const int32_t* parents, const int32_t* draft_row, const int32_t* ragged_offsets, int32_t B,
+                    int64_t n_nodes, int64_t n_draft_rows, int32_t V, int32_t dtype, double temperature,
+                    uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag);
 
 /*
  * SDCP's verifier uniforms, computed on the HOST for sdv_options ("Speculative Decoding

@@ -210,22 +210,34 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
 
 
 def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: torch.Tensor, parents: torch.Tensor,
-                offsets: torch.Tensor, temperature: float, seed: int, *, workspace: torch.Tensor | None = None,
-                diag: tuple[str, ...] = (), events: list | None = None):
+                offsets: torch.Tensor, temperature: float, seed: int, *, draft_row: torch.Tensor | None = None,
+                out: tuple | None = None, workspace: torch.Tensor | None = None, diag: tuple[str, ...] = (),
+                events: list | None = None):
     """sdv_verify_tree: token trees (int32 parents [n_nodes], each node's parent within its request,
-    -1 for the root; target rows cu[i] + i at the root and cu[i] + i + n + 1 after node n; draft row
-    cu[i] + n the logits node n was drawn from).  Returns (accepted_len [B], out_tokens
-    [n_nodes + B], accepted_nodes [n_nodes], extra) with the named sdv_diag arrays in extra."""
-    _check(target, draft, draft_tokens, offsets, temperature, None)
+    -1 for the root; target rows cu[i] + i at the root and cu[i] + i + n + 1 after node n; the logits
+    node n was drawn from: draft row draft_row[cu[i] + n] (int32 [n_nodes]; siblings may share a
+    row), or row cu[i] + n without draft_row).  Returns (accepted_len [B], out_tokens
+    [n_nodes + B], accepted_nodes [n_nodes], extra) with the named sdv_diag arrays in extra; ``out``
+    may hold those three output tensors."""
+    _check(target, None, draft_tokens, offsets, 0.0, None)
     dev = target.device
     B = offsets.shape[0] - 1
     n = draft_tokens.shape[0]
     _device_vector(parents, torch.int32, n, dev, "parents")
+    _device_vector(draft_row, torch.int32, n, dev, "draft_row")
+    n_dr = n if draft_row is None else (draft.shape[0] if draft is not None else 0)
+    if draft is not None:
+        if draft.dtype != target.dtype or draft.device != dev or not draft.is_contiguous() or draft.dim() != 2 \
+                or draft.shape[1] != target.shape[1] or draft.shape[0] != n_dr:
+            raise ValueError("draft logits must be a contiguous [n_draft_rows, V] tensor like the target's")
+    elif temperature > 0 and n_dr > 0:
+        raise ValueError("temperature > 0 needs the draft logits")
     V = target.shape[1]
     dt = _DTYPES[target.dtype]
-    accepted_len = torch.empty(B, dtype=torch.int32, device=dev)
-    out_tokens = torch.empty(n + B, dtype=torch.int32, device=dev)
-    accepted_nodes = torch.empty(n, dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty(n + B, dtype=torch.int32, device=dev),
+               torch.empty(n, dtype=torch.int32, device=dev))
+    accepted_len, out_tokens, accepted_nodes = out
     need = int(_native.lib().sdv_workspace_bytes(B, n, V, dt))
     ws = _workspace(need, dev) if workspace is None else workspace
     shapes = {"target_lse": (n + B, torch.float64), "draft_lse": (n, torch.float64),
@@ -246,7 +258,7 @@ def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: 
                 dg.events[k] = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
     with torch.cuda.device(dev):
         rc = _native.lib().sdv_verify_tree(
-            _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(parents), _ptr(offsets), B, n, V, dt,
+            _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(parents), _ptr(draft_row), _ptr(offsets), B, n, n_dr, V, dt,
             float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(accepted_nodes),
             _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(), torch.cuda.current_stream(dev).cuda_stream,
             ctypes.byref(dg) if dg is not None else None)

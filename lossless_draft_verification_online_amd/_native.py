@@ -86,8 +86,8 @@ def lib(path: str = LIBRARY) -> ctypes.CDLL:
     L.sdv_verify_ex.restype = ctypes.c_int
     L.sdv_verify_ex.argtypes = list(_VERIFY_ARGS) + [ctypes.POINTER(SdvDiag)]
     L.sdv_verify_tree.restype = ctypes.c_int
-    L.sdv_verify_tree.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_double, ctypes.c_uint64] + [ctypes.c_void_p] * 4 +
+    L.sdv_verify_tree.argtypes = ([ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_double, ctypes.c_uint64] + [ctypes.c_void_p] * 4 +
                                   [ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(SdvDiag)])
     L.sdv_verify_profiled.restype = ctypes.c_int
     L.sdv_verify_profiled.argtypes = (list(_VERIFY_ARGS[:8]) + [ctypes.c_void_p, ctypes.c_void_p]

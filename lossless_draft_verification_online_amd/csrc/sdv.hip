@@ -153,6 +153,8 @@ struct Params {
   int32_t Cm;                 // C rounded up to 16: a request's masses fill whole 128-byte lines
   int32_t* batch_ok;          // [1] the offsets are valid (written by the row pass's first workgroup)
   const int32_t* parents;     // [n_d] token trees: each node's parent within its request (-1: the root), or null
+  const int32_t* draft_row;   // [n_d] token trees: each node's draft row, or null (node d: row d)
+  int32_t n_dr;               // token trees: draft rows given (and streamed)
   int32_t* accepted_nodes;    // [n_d] token trees, out: the accepted path's nodes, then -1
   DiagPtrs dg;
 };
@@ -2057,11 +2059,11 @@ static_assert(kVecPerLane % kVerdictWaves == 0, "the in-chunk search gives each 
 constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
 // Folds a request's rows: rows r <= K_t are its target rows r (records at rec_t), rows r > K_t its
-// draft rows r - K_t - 1 (records at rec_d).  All chunk records go to shared memory in one pass when
-// they fit the budget (else the fold reads the workspace); `overlap` runs between the staging loads
-// and the barrier (wave 0's gathers hide under them).  rows[r] receives the fold of row r.
-template <bool kGreedy, class Overlap>
-__device__ __forceinline__ void stage_and_fold(const Params& P, const float2* rec_t, const float2* rec_d, int K_t,
+// draft rows j = r - K_t - 1 (records at draft_rec(j)).  All chunk records go to shared memory in one
+// pass when they fit the budget (else the fold reads the workspace); `overlap` runs between the
+// staging loads and the barrier (wave 0's gathers hide under them).  rows[r] receives the fold of row r.
+template <bool kGreedy, class DraftRec, class Overlap>
+__device__ __forceinline__ void stage_and_fold(const Params& P, const float2* rec_t, DraftRec draft_rec, int K_t,
                                                int n_rows, double* lds_mass, RowFold* rows, int lane, int wave,
                                                int n_waves, Overlap overlap) {
   const int64_t n_rec = (int64_t)n_rows * P.C;
@@ -2071,14 +2073,14 @@ __device__ __forceinline__ void stage_and_fold(const Params& P, const float2* re
     for (int64_t q = threadIdx.x; q < n_rec; q += blockDim.x) {
       const int64_t r = q / P.C;
       const int32_t c = (int32_t)(q - r * P.C);
-      lds_rec[q] = r <= K_t ? rec_t[r * P.C + c] : rec_d[(r - K_t - 1) * P.C + c];
+      lds_rec[q] = r <= K_t ? rec_t[r * P.C + c] : draft_rec((int)(r - K_t - 1))[c];
     }
   }
   overlap();
   __syncthreads();
   auto records_of = [&](int r) {
     return staged ? lds_rec + (int64_t)r * P.C
-                  : (r <= K_t ? rec_t + (int64_t)r * P.C : rec_d + (int64_t)(r - K_t - 1) * P.C);
+                  : (r <= K_t ? rec_t + (int64_t)r * P.C : draft_rec(r - K_t - 1));
   };
   auto fold_narrow = [&](auto lanes) {  // kWave / lanes rows per wave
     constexpr int kLanes = decltype(lanes)::value, kPer = kWave / kLanes;
@@ -2149,7 +2151,8 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   int32_t x = 0;
   float zt = 0.0f, zd = 0.0f;
   bool keep_t = true, keep_d = true;  // x is kept by the target / draft row's truncation
-  stage_and_fold<kGreedy>(P, rec_t, rec_d, K, n_rows, lds_mass, rows, lane, wave, n_waves, [&] {
+  auto draft_rec = [&](int j) { return rec_d + (int64_t)j * P.C; };
+  stage_and_fold<kGreedy>(P, rec_t, draft_rec, K, n_rows, lds_mass, rows, lane, wave, n_waves, [&] {
     if (wave == 0 && active) {
       x = P.tokens[drow0 + lane];
       if constexpr (!kGreedy) {
@@ -2473,8 +2476,9 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
 // Tree verification by multi-step speculative sampling (Miao et al., "SpecInfer", ASPLOS 2024,
 // section 4: the token tree verifier).  Request i holds N_i <= 64 nodes; node n has parent
 // P.parents[cu[i] + n] in [-1, n - 1] and token P.tokens[cu[i] + n], drawn from the distribution of
-// draft row cu[i] + n.  Target row cu[i] + i is the root's, cu[i] + i + n + 1 follows node n: the
-// linear layout, so the row pass is unchanged and a chain of nodes is a linear draft.
+// draft row P.draft_row[cu[i] + n] (siblings from one drafter share a row), or of row cu[i] + n.
+// Target row cu[i] + i is the root's, cu[i] + i + n + 1 follows node n: the linear layout, so the
+// row pass is unchanged and a chain of nodes is a linear draft.
 //
 // At the current node, with p its target distribution, the children are tested in node order.
 // Child c is accepted iff r_c <= p(x_c) / q_c(x_c), r_c from the Philox block (c, i); after l
@@ -2500,9 +2504,18 @@ struct ChainFrame {
 __device__ __forceinline__ float chain_p(const ChainFrame& f, float zt) {
   return fast_exp2(fmaf(zt, f.k2, -f.t_hi) - f.t_lo);
 }
-__device__ __forceinline__ float chain_step(const ChainFrame& f, int j, float R, float zd) {
-  const float q = fast_exp2(fmaf(zd, f.k2, -f.d_hi[j]) - f.d_lo[j]);
-  return fmaxf(fmaf(-f.m[j], q, R), 0.0f);
+
+// Rejected children j0 .. j1 - 1 share one draft row: its q is loaded and exponentiated once and
+// every step of the run applied to it.
+__device__ __forceinline__ int chain_run_end(const ChainFrame& f, int j0) {
+  int j1 = j0 + 1;
+  while (j1 < f.l && f.drow[j1] == f.drow[j0]) ++j1;
+  return j1;
+}
+__device__ __forceinline__ float chain_run(const ChainFrame& f, int j0, int j1, float R, float zd) {
+  const float q = fast_exp2(fmaf(zd, f.k2, -f.d_hi[j0]) - f.d_lo[j0]);
+  for (int j = j0; j < j1; ++j) R = fmaxf(fmaf(-f.m[j], q, R), 0.0f);
+  return R;
 }
 
 // R_l(v) for one element (rows given as byte pointers of the logits).
@@ -2510,9 +2523,16 @@ template <class E>
 __device__ __forceinline__ float chain_weight(const ChainFrame& f, const char* trow, const void* draft, int32_t V,
                                               int32_t v) {
   float R = chain_p(f, E::at(trow, v));
-  for (int j = 0; j < f.l; ++j) R = chain_step(f, j, R, E::at(row_ptr<E>(draft, f.drow[j], V), v));
+  for (int j = 0; j < f.l;) {
+    const int j1 = chain_run_end(f, j);
+    R = chain_run(f, j, j1, R, E::at(row_ptr<E>(draft, f.drow[j], V), v));
+    j = j1;
+  }
   return R;
 }
+
+constexpr int kTreeWaves = 16;  // waves of a tree verdict workgroup (the passes are VALU-bound per CU)
+constexpr int kTreeGroup = 4;  // vectors per lane in flight per row in a residual pass
 
 // Chunk masses of R_l into lds_mass[0 .. C) by the whole workgroup (wave w takes chunks w,
 // w + n_waves, ...): 16-byte vectors, four in flight per lane, fp32 per vector, fp64 across vectors.
@@ -2525,7 +2545,7 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
     if constexpr (kVec) {
       const int32_t nvec = n / E::kPerVec;
       const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
-      constexpr int kGroup = 4;
+      constexpr int kGroup = kTreeGroup;
       for (int g0 = 0; g0 < kVecPerLane; g0 += kGroup) {
         float R[kGroup][E::kPerVec];
 #pragma unroll
@@ -2535,17 +2555,27 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
 #pragma unroll
           for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_p(f, z[e]);
         }
-        for (int j = 0; j < f.l; ++j) {
+        for (int j = 0; j < f.l;) {  // one load and one exponential per run of rejections on one row
+          const int j1 = chain_run_end(f, j);
           const u32x4* dv = reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
           u32x4 b[kGroup];
 #pragma unroll
           for (int k = 0; k < kGroup; ++k) b[k] = load_vec<E>(dv, lane + kWave * (g0 + k), nvec);
+          const float d_hi = f.d_hi[j], d_lo = f.d_lo[j];
+          float q[kGroup][E::kPerVec];
 #pragma unroll
           for (int k = 0; k < kGroup; ++k) {
             float z[E::kPerVec];
             E::unpack(b[k], z);
 #pragma unroll
-            for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_step(f, j, R[k][e], z[e]);
+            for (int e = 0; e < E::kPerVec; ++e) q[k][e] = fast_exp2(fmaf(z[e], f.k2, -d_hi) - d_lo);
+          }
+          for (; j < j1; ++j) {
+            const float m = f.m[j];
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k)
+#pragma unroll
+              for (int e = 0; e < E::kPerVec; ++e) R[k][e] = fmaxf(fmaf(-m, q[k][e], R[k][e]), 0.0f);
           }
         }
 #pragma unroll
@@ -2570,7 +2600,7 @@ struct TreeStep {
 constexpr int32_t kTreePass = 0, kTreeDraw = 1, kTreeDone = 2;
 
 template <class E, bool kGreedy, bool kVec>
-__global__ __launch_bounds__(kWave * kVerdictWaves) void tree_verdicts(Params P) {
+__global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
   extern __shared__ double lds_mass[];  // [C], then staged records
   __shared__ RowFold rows[kMaxRows];
   __shared__ ChainFrame frame;
@@ -2601,23 +2631,30 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void tree_verdicts(Params P)
     return;
   }
   const float2* rec_t = P.part + (int64_t)trow0 * P.C;
-  const float2* rec_d = P.part + (int64_t)(P.n_t + drow0) * P.C;
+  // the draft row of node j; an index outside the rows (the request is then rejected below) reads row 0
+  auto draft_row_of = [&](int j) {
+    const int32_t d = P.draft_row ? P.draft_row[drow0 + j] : drow0 + j;
+    return (uint32_t)d < (uint32_t)P.n_dr ? d : 0;
+  };
+  auto draft_rec = [&](int j) { return P.part + (int64_t)(P.n_t + draft_row_of(j)) * P.C; };
 
   // 1. rows folded; wave 0 loads the nodes and, at T > 0, gathers z_t(x) from each node's parent row
-  // and z_d(x) from its own draft row
+  // and z_d(x) from its draft row
   const bool active = lane < N;
-  int32_t x = 0, par = -1;
+  int32_t x = 0, par = -1, qrow = 0;
   float zt = 0.0f, zd = 0.0f;
   bool bad_node = false;
   const int n_rows = kGreedy ? N + 1 : 2 * N + 1;
-  stage_and_fold<kGreedy>(P, rec_t, rec_d, N, n_rows, lds_mass, rows, lane, wave, n_waves, [&] {
+  stage_and_fold<kGreedy>(P, rec_t, draft_rec, N, n_rows, lds_mass, rows, lane, wave, n_waves, [&] {
     if (wave == 0 && active) {
       x = P.tokens[drow0 + lane];
       par = P.parents[drow0 + lane];
-      bad_node = x < 0 || x >= P.V || par < -1 || par >= lane;
+      const int32_t d = P.draft_row ? P.draft_row[drow0 + lane] : drow0 + lane;
+      bad_node = x < 0 || x >= P.V || par < -1 || par >= lane || (!kGreedy && (d < 0 || d >= P.n_dr));
+      qrow = bad_node ? 0 : d;
       if (!kGreedy && !bad_node) {
         zt = E::at(row_ptr<E>(P.target, trow0 + par + 1, P.V), x);
-        zd = E::at(row_ptr<E>(P.draft, drow0 + lane, P.V), x);
+        zd = E::at(row_ptr<E>(P.draft, qrow, P.V), x);
       }
     }
   });
@@ -2707,8 +2744,9 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void tree_verdicts(Params P)
             continue;
           }
           // rejected: c joins the residual; the workgroup computes the chunk masses of R_{l+1}
+          const int32_t qc = lane_value(qrow, c);
           if (lane == l) {
-            rej_drow = drow0 + c;
+            rej_drow = qc;
             rej_l2 = l2dc;
             rej_m = M_l;
           }
@@ -3036,7 +3074,7 @@ int launch_tree(Params& P, hipStream_t stream, const sdv_diag* diag) {
     if (diag && diag->events[k]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(diag->events[k]), stream);
   };
   constexpr int kMode = kGreedy ? kModeGreedy : kModeSampling;
-  P.n_units = (int64_t)(kGreedy ? P.n_t : P.n_t + P.n_d) * P.C;
+  P.n_units = (int64_t)(kGreedy ? P.n_t : P.n_t + P.n_dr) * P.C;
   P.hist = nullptr;
   P.split = 1;
   record(0);
@@ -3048,7 +3086,7 @@ int launch_tree(Params& P, hipStream_t stream, const sdv_diag* diag) {
   const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
   P.lds_records = want < room ? want : room;
   const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
-  hipLaunchKernelGGL((tree_verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kVerdictWaves), lds, stream, P);
+  hipLaunchKernelGGL((tree_verdicts<E, kGreedy, kVec>), dim3((unsigned)P.B), dim3(kWave * kTreeWaves), lds, stream, P);
   if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
   record(2);
   return SDV_OK;
@@ -3194,20 +3232,23 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
 }
 
 int verify_tree_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                     const int32_t* parents, const int32_t* ragged_offsets, int32_t B, int64_t n_nodes, int32_t V,
-                     int32_t dtype, double temperature, uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes,
-                     int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+                     const int32_t* parents, const int32_t* draft_row, const int32_t* ragged_offsets, int32_t B,
+                     int64_t n_nodes, int64_t n_draft_rows, int32_t V, int32_t dtype, double temperature,
+                     uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                     void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
   Layout L;
   const int shape = make_layout(B, n_nodes, V, dtype, &L);
   if (shape != SDV_OK) return shape;
   if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
   if (n_nodes > 0 && (!draft_tokens || !parents || !accepted_nodes)) return SDV_ERR_INVALID_ARG;
+  // draft rows: one per node, or (with indices) at most one per node, so the workspace holds them
+  if (draft_row ? (n_draft_rows < 0 || n_draft_rows > n_nodes) : n_draft_rows != n_nodes) return SDV_ERR_INVALID_ARG;
   if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;
   float k2 = 0.0f;
   if (temperature > 0.0) {
     k2 = (float)(1.4426950408889634074 / temperature);
     if (!isfinite(k2) || !(k2 > 0.0f)) return SDV_ERR_INVALID_ARG;
-    if (n_nodes > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
+    if (n_draft_rows > 0 && !draft_logits) return SDV_ERR_INVALID_ARG;
   }
   if (!workspace || workspace_bytes < L.total || (uintptr_t)workspace % kAlign != 0) return SDV_ERR_WORKSPACE;
   const int esize = dtype == SDV_BF16 ? 2 : 4;
@@ -3220,6 +3261,8 @@ int verify_tree_impl(const void* target_logits, const void* draft_logits, const 
   P.draft = draft;
   P.tokens = draft_tokens;
   P.parents = parents;
+  P.draft_row = draft_row;
+  P.n_dr = (int32_t)n_draft_rows;
   P.accepted_nodes = accepted_nodes;
   P.cu = ragged_offsets;
   P.accepted_len = accepted_len;
@@ -3252,12 +3295,13 @@ int verify_tree_impl(const void* target_logits, const void* draft_logits, const 
 extern "C" {
 
 int sdv_verify_tree(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
-                    const int32_t* parents, const int32_t* ragged_offsets, int32_t B, int64_t n_nodes, int32_t V,
-                    int32_t dtype, double temperature, uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes,
-                    int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
-  return sdv::verify_tree_impl(target_logits, draft_logits, draft_tokens, parents, ragged_offsets, B, n_nodes, V,
-                               dtype, temperature, seed, accepted_len, accepted_nodes, out_tokens, workspace,
-                               workspace_bytes, stream, diag);
+                    const int32_t* parents, const int32_t* draft_row, const int32_t* ragged_offsets, int32_t B,
+                    int64_t n_nodes, int64_t n_draft_rows, int32_t V, int32_t dtype, double temperature,
+                    uint64_t seed, int32_t* accepted_len, int32_t* accepted_nodes, int32_t* out_tokens,
+                    void* workspace, size_t workspace_bytes, void* stream, const sdv_diag* diag) {
+  return sdv::verify_tree_impl(target_logits, draft_logits, draft_tokens, parents, draft_row, ragged_offsets, B,
+                               n_nodes, n_draft_rows, V, dtype, temperature, seed, accepted_len, accepted_nodes,
+                               out_tokens, workspace, workspace_bytes, stream, diag);
 }
 
 size_t sdv_noalloc_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype) {

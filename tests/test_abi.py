@@ -189,11 +189,12 @@ def test_repad_host_argument_checks(lib):
 
 
 def test_verify_tree_host_argument_checks(lib):
-    def call(B=1, n=2, V=8, dtype=1, T=1.0, ws_bytes=1 << 20, **ptrs):
-        p = dict(target=FAKE, draft=FAKE, tokens=FAKE, parents=FAKE, cu=FAKE, acc=FAKE, nodes=FAKE, out=FAKE, ws=FAKE)
+    def call(B=1, n=2, n_dr=2, V=8, dtype=1, T=1.0, ws_bytes=1 << 20, **ptrs):
+        p = dict(target=FAKE, draft=FAKE, tokens=FAKE, parents=FAKE, rows=None, cu=FAKE, acc=FAKE, nodes=FAKE, out=FAKE,
+                 ws=FAKE)
         p.update(ptrs)
-        return lib.sdv_verify_tree(p["target"], p["draft"], p["tokens"], p["parents"], p["cu"], B, n, V, dtype, T, 1,
-                                   p["acc"], p["nodes"], p["out"], p["ws"], ws_bytes, None, None)
+        return lib.sdv_verify_tree(p["target"], p["draft"], p["tokens"], p["parents"], p["rows"], p["cu"], B, n, n_dr, V,
+                                   dtype, T, 1, p["acc"], p["nodes"], p["out"], p["ws"], ws_bytes, None, None)
     assert call(B=0) == -1
     assert call(V=0) == -1
     assert call(dtype=7) == -2
@@ -201,6 +202,9 @@ def test_verify_tree_host_argument_checks(lib):
     assert call(T=float("nan")) == -1
     assert call(T=1e-45) == -1  # log2(e) / T overflows binary32
     assert call(draft=None) == -1  # T > 0 needs draft rows
+    assert call(n_dr=1) == -1  # one row per node without indices
+    assert call(rows=FAKE, n_dr=3) == -1  # more draft rows than nodes
+    assert call(rows=FAKE, n_dr=-1) == -1
     for name in ("target", "tokens", "parents", "cu", "acc", "nodes", "out"):
         assert call(**{name: None}) == -1, name
     need = lib.sdv_workspace_bytes(1, 2, 8, 1)

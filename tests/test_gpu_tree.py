@@ -33,7 +33,8 @@ def _i32(a):
 def run_tree(b, diag=(), seed=None):
     acc, out, nodes, dg = sdv.verify_tree(to_device(b.target, b.dtype), to_device(b.draft, b.dtype), _i32(b.tokens),
                                           _i32(b.parents), _i32(b.cu), b.temperature,
-                                          b.seed if seed is None else seed, diag=diag)
+                                          b.seed if seed is None else seed, diag=diag,
+                                          draft_row=None if b.draft_row is None else _i32(b.draft_row))
     torch.cuda.synchronize()
     return acc.cpu().numpy(), out.cpu().numpy(), nodes.cpu().numpy(), {k: v.cpu().numpy() for k, v in dg.items()}
 
@@ -42,7 +43,8 @@ def check_tree(b, seed=None, diag=()):
     seed = b.seed if seed is None else seed
     log(f"tree parity: {b.name} B={b.B} nodes={b.n_draft_rows} V={b.V} {b.dtype} T={b.temperature} seed={seed}")
     acc, out, nodes, dg = run_tree(b, diag=diag, seed=seed)
-    ref = oracle.verify_tree(b.target, b.draft, b.tokens, b.parents, b.cu, b.temperature, seed, diag=True)
+    ref = oracle.verify_tree(b.target, b.draft, b.tokens, b.parents, b.cu, b.temperature, seed, diag=True,
+                             draft_row=b.draft_row)
     res = compare_tree_verdicts(acc, out, nodes, ref, b.cu, b.parents, b.temperature)
     assert res["n_hard"] == 0, res["hard"][:5]
     assert res["n_excused"] <= max(1, b.B // 100), res["excused"]
@@ -153,6 +155,30 @@ def test_tree_diagnostics():
                         + b.parents + 1, b.tokens]
     assert np.array_equal(dg["target_logit"], zt.astype(np.float32))
     assert np.array_equal(dg["draft_logit"], b.draft_f32()[np.arange(b.n_draft_rows), b.tokens])
+
+
+@pytest.mark.parametrize("kind,V,dtype,T", [("random", 128256, "bf16", 1.0), ("star", 32000, "bf16", 0.8),
+                                             ("kary", 1001, "fp32", 1.0)])
+def test_shared_draft_rows(kind, V, dtype, T):
+    """Siblings sharing their parent context's draft row by index: parity with the oracle, and the
+    same verdicts as the same tree with a copy of the row per node."""
+    rng = np.random.default_rng(V + 11)
+    sizes = rng.integers(0, 40, size=32)
+    shared = W.make_tree("shared", sizes, kind, V, dtype, T, 2.5, 1.5, data_seed=V + 12, verify_seed=41, shared=True)
+    full = W.make_tree("shared", sizes, kind, V, dtype, T, 2.5, 1.5, data_seed=V + 12, verify_seed=41)
+    assert shared.draft.shape[0] < full.draft.shape[0]
+    got = check_tree(shared)
+    ref = run_tree(full)
+    for g, r in zip(got[:3], ref[:3]):
+        assert np.array_equal(g, r)
+    bad = W.make_tree("shared", sizes, kind, V, dtype, T, 2.5, 1.5, data_seed=V + 12, verify_seed=41, shared=True)
+    i = int(np.argmax(sizes > 0))
+    bad.draft_row = bad.draft_row.copy()
+    bad.draft_row[bad.cu[i]] = bad.draft.shape[0]  # past the rows: request i alone is rejected
+    acc, out, nodes, _ = run_tree(bad)
+    assert acc[i] == -1 and (out[bad.cu[i] + i: bad.cu[i + 1] + i + 1] == -1).all()
+    others = np.arange(bad.B) != i
+    assert np.array_equal(acc[others], got[0][others])
 
 
 def test_tree_argument_errors():

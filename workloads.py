@@ -51,6 +51,7 @@ class Batch:
     top_k: np.ndarray | None = None      # (B,) int32 top-k of each request's profile, else None
     top_p_milli: np.ndarray | None = None  # (B,) int32 top-p in thousandths, else None
     parents: np.ndarray | None = None    # (n_draft_rows,) int32: token trees, each node's parent (-1: root)
+    draft_row: np.ndarray | None = None  # (n_draft_rows,) int32: token trees, each node's draft row (shared rows)
 
     @property
     def B(self) -> int:
@@ -75,8 +76,9 @@ class Batch:
             draft_rows = 0
         elif self.temp_each is not None:
             draft_rows = int(np.sum(self.depths[self.temp_each > 0]))
-        else:
-            draft_rows = self.n_draft_rows if self.temperature > 0 else 0
+        else:  # token trees may share draft rows among siblings
+            given = self.draft.shape[0] if self.draft is not None and self.draft_row is not None else self.n_draft_rows
+            draft_rows = given if self.temperature > 0 else 0
         return (self.target.shape[0] + draft_rows) * self.V * self.elem_bytes
 
     def target_f32(self) -> np.ndarray:
@@ -295,12 +297,14 @@ def tree_parents(kind: str, n: int, rng: np.random.Generator, branching: int = 2
 
 
 def make_tree(name: str, sizes, kind: str, V: int, dtype: str, temperature: float, target_sigma: float,
-              draft_sigma: float, data_seed: int, verify_seed: int, branching: int = 2) -> Batch:
+              draft_sigma: float, data_seed: int, verify_seed: int, branching: int = 2, shared: bool = False) -> Batch:
     """Token-tree batch: request i holds sizes[i] nodes in the given shape.  Target rows are
     Gaussian (row 0 of a request at the root, row n + 1 after node n).  The drafter's row at a node's
     context is that context's target row plus Gaussian noise, shared by all of the node's children
     (draft row of node n = the row its token was drawn from), and each child's token is drawn from
-    it independently (Gumbel-max at temperature T, or its argmax at T = 0)."""
+    it independently (Gumbel-max at temperature T, or its argmax at T = 0).  shared: the draft side
+    holds that row once per parent context, and draft_row gives each node's row (else one copy per
+    node)."""
     rng = np.random.Generator(np.random.Philox(data_seed))
     sizes = np.asarray(sizes, dtype=np.int64)
     B = sizes.shape[0]
@@ -319,6 +323,12 @@ def make_tree(name: str, sizes, kind: str, V: int, dtype: str, temperature: floa
     draft = _store(drf, dtype)
     del tgt, noise, drf
     tokens = _argmax_tokens(draft, dtype) if temperature == 0 else _gumbel_tokens(rng, draft, dtype, temperature)
+    draft_row = None
+    if shared:  # one row per parent context, in context order
+        ctx, first, draft_row = np.unique(ctx_row, return_index=True, return_inverse=True)
+        draft = np.ascontiguousarray(draft[first])
+        draft_row = draft_row.astype(np.int32)
     return Batch(name=name, V=V, dtype=dtype, temperature=float(temperature), seed=int(verify_seed),
                  target=target, draft=draft if temperature > 0 else None, tokens=tokens, cu=cu, parents=parents,
+                 draft_row=draft_row,
                  meta={"data_seed": data_seed, "kind": kind, "target_sigma": target_sigma, "draft_sigma": draft_sigma})
