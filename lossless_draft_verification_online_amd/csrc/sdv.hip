@@ -705,19 +705,21 @@ __device__ __forceinline__ void resid_masses_pipelined(const M& m, const char* t
   }
 }
 
-// Inverse CDF inside one chunk (16-byte aligned rows) by a whole workgroup: the chunk's vectors form
-// rows of 64 (vector k*64 + l for lane l), wave w sums rows w and w + n_waves, a scan of the row sums
-// picks the row, and the wave that owns it scans its 64 vector sums and walks the chosen vector.
-// Returns the token in the owning wave and -1 in the others.  row_sums holds at least 16 doubles.
-// kFraction: target is a uniform u in [0, 1), scaled here by the chunk's total weight (the row sums
-// of the first step), which every wave also stores into *total; a residual chunk without positive
-// weight returns -2 in every wave.
-template <class E, bool kResid, bool kFraction = false, class M>
+// Inverse CDF inside kChunks consecutive chunks (16-byte aligned rows) by a whole workgroup: the
+// vectors form rows of 64 (vector k*64 + l for lane l), wave w sums rows w, w + n_waves, ..., a scan
+// of the row sums picks the row, and the wave that owns it scans its 64 vector sums and walks the
+// chosen vector.  Returns the token in the owning wave and -1 in the others.  row_sums holds at least
+// 16 kChunks doubles.  kFraction: target is a uniform u in [0, 1), scaled here by the range's total
+// weight (the row sums of the first step), which every wave also stores into *total; a residual
+// range without positive weight returns -2 in every wave.  With kFraction over a whole row of up to
+// four chunks this one pass replaces the mass pass, the pick of a chunk and the search in it.
+template <class E, bool kResid, bool kFraction = false, int kChunks = 1, class M>
 __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* trow, const char* drow, int32_t c0,
                                                       int32_t n, double target, float k2, float ref_t, float e_hi,
                                                       float q_scale, double* row_sums, int lane, int wave,
                                                       int n_waves, double* total = nullptr) {
-  constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
+  constexpr int kRows = kVecPerLane * kChunks;  // 16 rows of 64 vectors per chunk
+  static_assert(kRows % kVerdictWaves == 0 && kRows <= kWave, "whole rows per wave, one scan of the row sums");
   const int32_t nvec = n / E::kPerVec;
   const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
   const u32x4* dv = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)c0 * E::kBytes);
@@ -2329,8 +2331,10 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   const float* qp = residual && kQ ? P.qrows + (int64_t)(drow0 + d.a) * P.V : nullptr;
 
   // a row of one chunk (16-byte aligned logit rows): the in-chunk search totals the weights itself,
-  // so neither the mass pass nor the pick of a chunk runs (a split is 1 here: C / 4 < 1)
+  // so neither the mass pass nor the pick of a chunk runs (a split is 1 here: C / 4 < 1); a correction
+  // on rows of up to four chunks takes the same single pass over the whole pair when it is not split
   const bool one_chunk = kVec && !kQ && P.C == 1;
+  const bool few_chunks = kVec && !kQ && residual && P.C <= 4 && n_split == 1;
   // residual masses of this workgroup's chunks [c_lo, c_hi), into shared memory; the vector passes
   // see the range as a row of its own (tokens from c_lo's first, masks shifted to match)
   const int32_t c_lo = (int32_t)((int64_t)P.C * part / n_split), c_hi = (int32_t)((int64_t)P.C * (part + 1) / n_split);
@@ -2355,7 +2359,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
       }
     }
     __syncthreads();
-  } else if (residual && !one_chunk) {
+  } else if (residual && !one_chunk && !few_chunks) {
     if constexpr (kVec) {
       resid_masses_pipelined<E>(m_r, tp + (int64_t)v_lo * E::kBytes, dp + (int64_t)v_lo * E::kBytes, V_r,
                                 c_hi - c_lo, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + c_lo, lane, wave, n_waves);
@@ -2403,22 +2407,28 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     }
   };
   if constexpr (kVec && !kQ) {
-    if (one_chunk) {
+    auto single_pass = [&](auto chunks) {
+      constexpr int kC = decltype(chunks)::value;
       int32_t y = -1;
       bool empty = false;
       double S = 0.0;
       if (residual) {
-        y = search_chunk_block<E, true, true>(m, tp, dp, 0, P.V, (double)d.u, k2, d.ref_t, d.e_hi, d.q_scale,
-                                              lds_mass + P.C, lane, wave, n_waves, &S);
+        y = search_chunk_block<E, true, true, kC>(m, tp, dp, 0, P.V, (double)d.u, k2, d.ref_t, d.e_hi, d.q_scale,
+                                                  lds_mass + P.C, lane, wave, n_waves, &S);
         empty = y == -2;  // no positive residual weight in floating point: draw from p_t
         // the fallback search rewrites the row sums every wave has just read: all reads come first
         // (empty is the same in every wave, so the barrier is uniform)
         if (empty) __syncthreads();
       }
       if (!residual || empty)
-        y = search_chunk_block<E, false, true>(m, tp, nullptr, 0, P.V, (double)d.u, k2, d.ref_t, 0.0f, 0.0f,
-                                               lds_mass + P.C, lane, wave, n_waves, &S);
-      return write_token(y, empty, S);
+        y = search_chunk_block<E, false, true, kC>(m, tp, nullptr, 0, P.V, (double)d.u, k2, d.ref_t, 0.0f, 0.0f,
+                                                   lds_mass + P.C, lane, wave, n_waves, &S);
+      write_token(y, empty, S);
+    };
+    if (one_chunk) return single_pass(std::integral_constant<int, 1>{});
+    if (few_chunks) {
+      if (P.C == 2) return single_pass(std::integral_constant<int, 2>{});
+      return single_pass(std::integral_constant<int, 4>{});
     }
   }
   // every wave picks the same chunk from the same masses
