@@ -65,3 +65,25 @@ def test_zero_q_at_the_token_rejects_only_that_request():
     for i in (0, 2):
         s = slice(b.cu[i] + i, b.cu[i + 1] + i + 1)
         assert acc[i] == ref["accepted_len"][i] and np.array_equal(out[s], ref["out_tokens"][s])
+
+
+@pytest.mark.parametrize("V,dtype", [(4096, "fp32"), (32000, "bf16"), (128256, "bf16")])
+def test_empty_residual_falls_back_to_p(V, dtype):
+    """q rows given as 1.5 p (used as given, SDCP's q_rows): every ratio is 2/3, and after a rejection
+    max(p - q, 0) is zero at every token, so the extra token is drawn from p itself
+    (SDV_TERM_RESIDUAL_EMPTY) on rows of 1, 4 and 16 chunks.  With logit drafts an empty residual
+    cannot follow a rejection: it needs p <= q at every token, i.e. p = q, whose ratio 1 always
+    accepts."""
+    rng = np.random.default_rng(V + 1)
+    b = W.with_qrows(W.make_random(f"q_empty_v{V}", rng.integers(1, 9, size=40), V, dtype, 1.0, 2.0, 1.0,
+                                   data_seed=V + 2, verify_seed=6))
+    z = b.target_f32().astype(np.float64)
+    req = np.repeat(np.arange(b.B), b.depths)
+    rows = b.cu[req] + req + (np.arange(b.n_draft_rows) - b.cu[req])  # the target row of each draft position
+    p = np.exp(z[rows] - z[rows].max(axis=1, keepdims=True))
+    b.qrows = (1.5 * p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    acc, out, ref, cmp, dg = check_parity(b, diag=("terminal_kind",))
+    empty = ref["terminal_kind"] == 3
+    assert empty.sum() >= 5, "the batch must exercise the empty residual"
+    same = acc == ref["accepted_len"]
+    assert np.array_equal(dg["terminal_kind"][same], ref["terminal_kind"][same])
