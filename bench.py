@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--kernel", default="row_records", help="the kernel a counter summary is for (--summarize-pmc)")
     ap.add_argument("--command", default="", help="the command that produced the profile")
     ap.add_argument("--summary-name", default="", help="file name (no suffix) of a --summarize-trace summary")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph holding one step per input set (no host work between calls)")
     ap.add_argument("--yardsticks", action="store_true",
                     help="time the read yardsticks (three read shapes) and torch's fill_ at the workload's size")
     args = ap.parse_args()
@@ -345,12 +347,30 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.graph:  # one step per input set, captured once and replayed: every kernel of every step runs
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(len(sets)):
+                step(k)
+        torch.cuda.synchronize()
+        replays = max(1, args.steps // len(sets))
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] timing {replays} replays of {len(sets)} steps")
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        args.steps = replays * len(sets)
+    else:
+        log(f"[bench] timing {args.steps} steps")
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            step(args.warmup + k)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
 
     # a second pass with HIP events that the library records on its stream: [0] before the first
     # kernel, [1] after the row pass, [3] after the truncation kernel (when it runs), [2] after the
@@ -428,7 +448,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if B0.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": B0.name, "B": B0.B, "V": B0.V,
+        "config": {"workload": B0.name, "B": B0.B, "V": B0.V, "timing": "hip_graph_replay" if args.graph else "eager",
                    "temperature": B0.temperature if B0.temp_each is None else
                    {f"{t:g}": int(n) for t, n in zip(*np.unique(B0.temp_each, return_counts=True))},
                    **({} if B0.top_k is None else {"top_k": int(B0.top_k[0]), "top_p_milli": int(B0.top_p_milli[0]),
