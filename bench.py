@@ -44,7 +44,7 @@ KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
                   "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
 KERNELS = ["row_records", "verdicts"]
 TRUNCATION_KERNELS = ["row_records", "cuts", "verdicts"]  # "cuts": row_cuts_counted, then row_cuts
-TRACE_KERNELS = ["row_records", "row_cuts_counted", "row_cuts", "verdicts", "read_reg_kernel", "read_lds_kernel",
+TRACE_KERNELS = ["row_records", "row_cuts_counted", "row_cuts", "tree_verdicts", "verdicts", "read_reg_kernel", "read_lds_kernel",
                  "read_strided_kernel", "philox_kernel"]
 CHUNK_BYTES = 16384
 
