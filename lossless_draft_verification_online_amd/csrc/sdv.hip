@@ -20,6 +20,9 @@
 //                chunk masses of max(p - q, 0) on the rejected row pair, which the 8 waves compute
 //                into shared memory before wave 0 draws.  A batch too small to occupy the compute
 //                units gets several workgroups per request, which share that pass (section 3).
+//  tree_verdicts Token trees (section 4), in place of verdicts: one workgroup of 16 waves per
+//                request walks its tree in wave 0, and the whole workgroup computes the residual
+//                masses after each rejected child.
 //
 // The kernel boundary orders the stream before the verdicts.  Inside a kernel only the verdict
 // workgroups of one request hand anything over: a correction's chunk masses, through the
