@@ -53,7 +53,7 @@ def check_tree(b, seed=None, diag=()):
 
 @pytest.mark.parametrize("kind", ["random", "kary", "star"])
 @pytest.mark.parametrize("V,dtype,T", [(1000, "fp32", 1.0), (1001, "fp32", 0.7), (32000, "bf16", 0.8),
-                                       (128256, "bf16", 1.0)])
+                                       (32003, "bf16", 1.0), (16384, "bf16", 0.3), (128256, "bf16", 1.0)])
 def test_tree_parity(kind, V, dtype, T):
     """Random, binary and star trees of 0 to 24 nodes; 16-byte aligned rows and an odd vocabulary
     (element loads); several chunks per row and a ragged last chunk."""
