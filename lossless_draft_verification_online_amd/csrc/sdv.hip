@@ -2611,6 +2611,85 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
   }
 }
 
+// Inverse CDF inside one chunk (16-byte aligned rows) by the whole workgroup: the chunk's vectors form
+// 16 rows of 64 (vector r*64 + l for lane l); wave w sums rows w, w + n_waves, ..., every wave scans
+// the row sums, and the wave owning the crossing row recomputes its vectors, scans their sums across
+// the lanes and walks the chosen vector.  kChain: the weights are R_l(v) of the frame f; else the
+// node's own p in the frame 2^(z k - ref).  If rounding leaves the target unreached, the last element
+// of positive weight is taken.  row_sums holds 16 doubles; the token is returned in every wave.
+template <class E, bool kChain>
+__device__ __forceinline__ int32_t tree_search_block(const ChainFrame& f, const char* trow, const void* draft,
+                                                     int32_t V, int32_t c0, int32_t n, double target, float ref,
+                                                     double* row_sums, int32_t* token, int lane, int wave,
+                                                     int n_waves) {
+  const int32_t nvec = n / E::kPerVec;
+  const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
+  auto weights = [&](int vi, float (&w)[E::kPerVec]) {
+    float z[E::kPerVec];
+    E::unpack(load_vec<E>(tv, vi, nvec), z);
+    if constexpr (kChain) {
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) w[e] = chain_p(f, z[e]);
+      for (int j = 0; j < f.l;) {
+        const int j1 = chain_run_end(f, j);
+        const u32x4* dv = reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
+        float zd[E::kPerVec];
+        E::unpack(load_vec<E>(dv, vi, nvec), zd);
+#pragma unroll
+        for (int e = 0; e < E::kPerVec; ++e) w[e] = chain_run(f, j, j1, w[e], zd[e]);
+        j = j1;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) w[e] = fast_exp2(fmaf(z[e], f.k2, -ref));
+    }
+  };
+  for (int r = wave; r < kVecPerLane; r += n_waves) {
+    float w[E::kPerVec];
+    weights(r * kWave + lane, w);
+    const double rs = wave_sum((double)tree_sum(w));
+    if (lane == 0) row_sums[r] = rs;
+  }
+  __syncthreads();
+  const double rsum = lane < kVecPerLane ? row_sums[lane] : 0.0;
+  const double rex = wave_exclusive_scan(rsum, lane);
+  const uint64_t rhit = __ballot(lane < kVecPerLane && rex + rsum > target);
+  const uint64_t rpos = __ballot(lane < kVecPerLane && rsum > 0.0);
+  if (!rhit && !rpos) {
+    if (wave == 0 && lane == 0) *token = c0 + n - 1;
+  } else {
+    const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
+    if (wave == kr % n_waves) {
+      const double rest = target - lane_value(rex, kr);
+      float w[E::kPerVec];
+      weights(kr * kWave + lane, w);  // the same weights as the row sum's
+      const float v = tree_sum(w);
+      const double vex = wave_exclusive_scan((double)v, lane);
+      const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
+      const uint64_t vpos = __ballot(v > 0.0f);
+      const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
+      const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+      int32_t yl = base + E::kPerVec - 1, last_pos = -1;
+      double upto = vex;
+      bool found = false;
+#pragma unroll
+      for (int q = 0; q < E::kPerVec; ++q) {
+        upto += (double)w[q];
+        if (w[q] > 0.0f) last_pos = base + q;
+        if (!found && upto > rest) {
+          yl = base + q;
+          found = true;
+        }
+      }
+      if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
+      const int32_t y = lane_value(yl, l);
+      if (lane == 0) *token = y;
+    }
+  }
+  __syncthreads();
+  return *token;
+}
+
 // What wave 0 hands the workgroup after each step of the walk.
 struct TreeStep {
   int32_t action;  // kTreePass: chunk masses of the frame's R_l; kTreeDraw: the extra token; kTreeDone
@@ -2824,32 +2903,39 @@ __global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
       }
     }
   }
-  if (step.action != kTreeDraw || wave != 0) return;
+  if (step.action != kTreeDraw) return;  // uniform: every wave read the same shared value
 
-  // 3. the extra token (wave 0) and the outputs
+  // 3. the extra token (every wave picks the chunk; 16-byte aligned rows are searched by the whole
+  // workgroup, others by wave 0 alone) and the outputs (wave 0)
   const int32_t row = step.row;
   int32_t y = step.token;
   double S = 1.0;
   if constexpr (!kGreedy) {
+    if (!kVec && wave != 0) return;
     const char* tp = row_ptr<E>(P.target, trow0 + row, P.V);
+    const bool chain = step.kind == SDV_TERM_RESIDUAL;  // R_l by the chunk masses of the last pass
+    const float2* rec = rec_t + (int64_t)row * P.C;     // else the node's own p, by its records
+    const float ref = rows[row].ref;                    // (the frame 2^(z k - ref))
     double tgt = 0.0;
-    if (step.kind == SDV_TERM_RESIDUAL) {  // R_l by the chunk masses of the last pass
-      const int32_t cs = pick_chunk(P.C, step.u, [&](int32_t c) { return lds_mass[c]; }, &tgt, &S, lane);
-      const int32_t s0 = cs * E::kChunk;
-      y = search_chunk<E>(s0, min(E::kChunk, P.V - s0), tgt,
-                          [&](int32_t v) { return chain_weight<E>(frame, tp, P.draft, P.V, v); }, lane);
-    } else {  // the node's own p, by its records (the frame 2^(z k - ref))
-      const float2* rec = rec_t + (int64_t)row * P.C;
-      const float ref = rows[row].ref;
-      const int32_t cs = pick_chunk(
-          P.C, step.u, [&](int32_t c) { return (double)rec[c].y * exp2((double)rec[c].x - (double)ref); }, &tgt, &S,
-          lane);
-      const int32_t s0 = cs * E::kChunk;
-      y = search_chunk<E>(s0, min(E::kChunk, P.V - s0), tgt,
-                          [&](int32_t v) { return fast_exp2(fmaf(E::at(tp, v), k2, -ref)); }, lane);
-      S *= exp2((double)ref - rows[row].l2);  // probability units
+    const int32_t cs =
+        chain ? pick_chunk(P.C, step.u, [&](int32_t c) { return lds_mass[c]; }, &tgt, &S, lane)
+              : pick_chunk(P.C, step.u, [&](int32_t c) { return (double)rec[c].y * exp2((double)rec[c].x - (double)ref); },
+                           &tgt, &S, lane);
+    const int32_t s0 = cs * E::kChunk, n = min(E::kChunk, P.V - s0);
+    __shared__ int32_t drawn;
+    if constexpr (kVec) {
+      y = chain ? tree_search_block<E, true>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn, lane,
+                                             wave, n_waves)
+                : tree_search_block<E, false>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn, lane,
+                                              wave, n_waves);
+    } else {
+      y = chain ? search_chunk<E>(s0, n, tgt, [&](int32_t v) { return chain_weight<E>(frame, tp, P.draft, P.V, v); },
+                                  lane)
+                : search_chunk<E>(s0, n, tgt, [&](int32_t v) { return fast_exp2(fmaf(E::at(tp, v), k2, -ref)); }, lane);
     }
+    if (!chain) S *= exp2((double)ref - rows[row].l2);  // probability units
   }
+  if (wave != 0) return;
   const int32_t path_tok = __shfl(x, path_node < 0 ? 0 : path_node, kWave);
   for (int d = lane; d <= N; d += kWave) P.out_tokens[trow0 + d] = d < a ? path_tok : (d == a ? y : -1);
   for (int d = lane; d < N; d += kWave) P.accepted_nodes[drow0 + d] = d < a ? path_node : -1;
