@@ -116,9 +116,12 @@ size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t d
 /*
  * Verify one ragged batch (SDCP "Verification and Commit", steps 5 to 7, for every request).
  *
- *   target_logits  [n_draft_rows + B][V] row-major, dtype elements (bf16 as raw 16-bit words)
- *   draft_logits   [n_draft_rows][V]     same dtype; may be NULL when temperature == 0 (it is not
- *                                        read then) or when n_draft_rows == 0
+ *   target_logits  [n_draft_rows + B][V] row-major, dtype elements (bf16 as raw 16-bit words),
+ *                                        the base aligned to the element size (2 or 4 bytes); rows
+ *                                        that are 16-byte aligned (base and V * size) take the
+ *                                        fastest loads, any other V costs a few element loads a chunk
+ *   draft_logits   [n_draft_rows][V]     same dtype and alignment; may be NULL when temperature == 0
+ *                                        (it is not read then) or when n_draft_rows == 0
  *   draft_tokens   [n_draft_rows] int32  the proposed token of each draft position
  *   ragged_offsets [B + 1] int32         cu[0] = 0, non-decreasing, cu[B] = n_draft_rows
  *   B, n_draft_rows, V                   host values: B >= 1, n_draft_rows >= 0, V >= 1
@@ -134,9 +137,9 @@ size_t sdv_workspace_bytes(int32_t B, int64_t n_draft_rows, int32_t V, int32_t d
  *   stream         hipStream_t (as void*), NULL for the null stream
  *
  * Errors.  Argument errors are detected on the host and returned synchronously; nothing is
- * launched then: NULL required pointers, B < 1, n_draft_rows < 0, V < 1, temperature negative,
- * NaN or infinite (or so small that log2(e)/T overflows), T > 0 with NULL draft_logits while
- * n_draft_rows > 0 -> SDV_ERR_INVALID_ARG; unknown dtype -> SDV_ERR_UNSUPPORTED; sizes beyond the
+ * launched then: NULL required pointers, logits not aligned to their element size, B < 1,
+ * n_draft_rows < 0, V < 1, temperature negative, NaN or infinite (or so small that log2(e)/T
+ * overflows), T > 0 with NULL draft_logits while n_draft_rows > 0 -> SDV_ERR_INVALID_ARG; unknown dtype -> SDV_ERR_UNSUPPORTED; sizes beyond the
  * 32-bit row / launch limits -> SDV_ERR_LIMIT; small workspace -> SDV_ERR_WORKSPACE.
  * Per-request errors are decided on the device before any uniform is used (SDCP step 5 and
  * problem types "sdcp-bad-proposal" / "sdcp-limit"): a request whose depth is outside [0, 64] or
@@ -213,7 +216,7 @@ int sdv_verify_profiled(const void* target_logits, const void* draft_logits, con
  *                     number of tokens each row keeps, target rows first, then draft rows (V for a
  *                     row that is not truncated); written for the rows of requests at T > 0 (draft
  *                     rows only when draft logits are used).
- *  draft_probs        [n_draft_rows][V] float (binary32): the draft distributions themselves, SDCP's
+ *  draft_probs        [n_draft_rows][V] float (binary32, 4-byte aligned): the draft distributions, SDCP's
  *                     "q_rows" (section "Message Definitions"; Rule 2 takes q[i] from them), used as
  *                     given in place of softmax(draft_logits / T); draft_logits is then not read and
  *                     may be NULL.  Each row must be the distribution the token was drawn from (sums

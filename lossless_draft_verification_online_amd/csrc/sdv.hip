@@ -348,37 +348,93 @@ __device__ __forceinline__ float2 record_of(u32x4 (&buf)[kVecPerLane], int32_t c
   }
 }
 
+// A chunk [c0, c0 + n) of a row that is only element-aligned, split at 16-byte boundaries: the
+// aligned vectors inside it (from element c0 + head on) are loaded like an aligned row's, and the
+// at most kPerVec - 1 elements before the first of them and after the last, one per lane (lanes
+// [0, head) take the head, the next lanes the tail).  Every load stays inside the chunk.
+struct SplitEdge {
+  int32_t head;  // elements before the first aligned vector
+  float z;       // the lane's edge element, -inf on lanes without one
+  int32_t v;     // its index in the row
+};
+template <class E>
+__device__ __forceinline__ SplitEdge load_split_chunk(const char* rp, int32_t c0, int32_t n, int lane,
+                                                      u32x4 (&buf)[kVecPerLane]) {
+  const uintptr_t b0 = (uintptr_t)(rp + (int64_t)c0 * E::kBytes);
+  const int32_t head = min(n, (int32_t)((((b0 + 15) & ~(uintptr_t)15) - b0) / E::kBytes));
+  const int32_t body = (n - head) / E::kPerVec * E::kPerVec;
+  load_chunk<E>(rp, c0 + head, body, lane, buf);
+  const int32_t e = lane < head ? lane : head + body + (lane - head);
+  SplitEdge s;
+  s.head = head;
+  s.v = c0 + e;
+  s.z = e < n ? E::at(rp, s.v) : -INFINITY;
+  return s;
+}
+
+// The record of a split chunk (as record_of: the vectors' elements plus the lane's edge element).
+template <class E, bool kGreedy>
+__device__ __forceinline__ float2 record_of_split(u32x4 (&buf)[kVecPerLane], const SplitEdge& s, int32_t c0, float k2,
+                                                  int lane) {
+  if constexpr (kGreedy) {
+    float best = -INFINITY;
+    int32_t idx = INT32_MAX;
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+      float f[E::kPerVec];
+      E::unpack(buf[k], f);
+      const int32_t e0 = c0 + s.head + (lane + kWave * k) * E::kPerVec;
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) {
+        if (f[e] > best) {
+          best = f[e];
+          idx = e0 + e;
+        }
+      }
+    }
+    // the edge element may precede the vectors: equal values go to the smaller index
+    if (s.z > best || (s.z == best && s.z != -INFINITY && s.v < idx)) {
+      best = s.z;
+      idx = s.v;
+    }
+    wave_argmax(best, idx);
+    return make_float2(best, __int_as_float(idx));
+  } else {
+    float m = s.z;
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+      float f[E::kPerVec];
+      E::unpack(buf[k], f);
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) m = fmaxf(m, f[e]);
+    }
+    m = wave_max(m);
+    if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+    const float ref = m * k2;
+    float acc[4] = {fast_exp2(fmaf(s.z, k2, -ref)), 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < kVecPerLane; ++k) {
+      asm volatile("" : "+v"(buf[k]));
+      float f[E::kPerVec];
+      E::unpack(buf[k], f);
+#pragma unroll
+      for (int e = 0; e < E::kPerVec; ++e) f[e] = fast_exp2(fmaf(f[e], k2, -ref));
+      acc[k & 3] += tree_sum(f);
+    }
+    return make_float2(ref, wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3])));
+  }
+}
+
 // One 16 KiB chunk: (ref, sum 2^(z k - ref)) at T > 0, (max, first index of max) at T = 0.
 template <class E, bool kGreedy, bool kVec>
 __device__ __forceinline__ float2 chunk_record(const char* rp, int32_t c0, int32_t n, float k2, int lane) {
+  u32x4 buf[kVecPerLane];
   if constexpr (kVec) {
-    u32x4 buf[kVecPerLane];
     load_chunk<E>(rp, c0, n, lane, buf);
     return record_of<E, kGreedy>(buf, c0, k2, lane);
   } else {
-    const int32_t c1 = c0 + n;
-    if constexpr (kGreedy) {
-      float best = -INFINITY;
-      int32_t idx = INT32_MAX;
-      for (int32_t v = c0 + lane; v < c1; v += kWave) {
-        const float z = E::at(rp, v);
-        if (z > best) {
-          best = z;
-          idx = v;
-        }
-      }
-      wave_argmax(best, idx);
-      return make_float2(best, __int_as_float(idx));
-    } else {
-      float m = -INFINITY;
-      for (int32_t v = c0 + lane; v < c1; v += kWave) m = fmaxf(m, E::at(rp, v));
-      m = wave_max(m);
-      if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
-      const float ref = m * k2;
-      float s = 0.0f;
-      for (int32_t v = c0 + lane; v < c1; v += kWave) s += fast_exp2(fmaf(E::at(rp, v), k2, -ref));
-      return make_float2(ref, wave_sum(s));
-    }
+    const SplitEdge s = load_split_chunk<E>(rp, c0, n, lane, buf);
+    return record_of_split<E, kGreedy>(buf, s, c0, k2, lane);
   }
 }
 
@@ -3258,6 +3314,10 @@ void* noalloc_scratch(int* status) {
 
 // Validation and launch shared by the entry points.  temp_each / seed_each are null for one profile
 // per batch (temperature, seed), else device arrays of B values.
+// Logits are read in their own width (and rows that are not 16-byte aligned in 16-byte pieces from
+// the first 16-byte boundary on), so each base must sit on an element boundary.
+bool element_aligned(const void* p, int32_t dtype) { return (uintptr_t)p % (dtype == SDV_BF16 ? 2 : 4) == 0; }
+
 int verify_impl(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                 const int32_t* ragged_offsets, int32_t B, int64_t n_draft_rows, int32_t V, int32_t dtype,
                 double temperature, uint64_t seed, const sdv_options* opt, int32_t* accepted_len,
@@ -3278,6 +3338,9 @@ int verify_impl(const void* target_logits, const void* draft_logits, const int32
   if (!counts_room && (opt->top_k || opt->top_p_milli)) return SDV_ERR_INVALID_ARG;
   if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
   if (n_draft_rows > 0 && !draft_tokens) return SDV_ERR_INVALID_ARG;
+  if (!element_aligned(target_logits, dtype) || !element_aligned(draft_logits, dtype) ||
+      (uintptr_t)opt->draft_probs % 4 != 0)
+    return SDV_ERR_INVALID_ARG;
   float k2 = 0.0f;  // 0 selects the greedy rule
   const bool profiled = temp_each != nullptr || seed_each != nullptr;
   const float* qrows = opt->draft_probs;
@@ -3364,6 +3427,7 @@ int verify_tree_impl(const void* target_logits, const void* draft_logits, const 
   if (shape != SDV_OK) return shape;
   if (!target_logits || !ragged_offsets || !accepted_len || !out_tokens) return SDV_ERR_INVALID_ARG;
   if (n_nodes > 0 && (!draft_tokens || !parents || !accepted_nodes)) return SDV_ERR_INVALID_ARG;
+  if (!element_aligned(target_logits, dtype) || !element_aligned(draft_logits, dtype)) return SDV_ERR_INVALID_ARG;
   // draft rows: one per node, or (with indices) at most one per node, so the workspace holds them
   if (draft_row ? (n_draft_rows < 0 || n_draft_rows > n_nodes) : n_draft_rows != n_nodes) return SDV_ERR_INVALID_ARG;
   if (!(temperature >= 0.0) || !isfinite(temperature)) return SDV_ERR_INVALID_ARG;

@@ -99,6 +99,9 @@ def test_host_argument_errors(lib):
     assert _call(lib, T=float("inf"), ws_bytes=need) == -1
     assert _call(lib, T=1e-300, ws_bytes=need) == -1  # log2(e)/T overflows fp32
     assert _call(lib, draft=None, ws_bytes=need) == -1  # sampling needs draft logits
+    assert _call(lib, target=FAKE + 1, ws_bytes=need) == -1  # bf16 logits off their 2-byte boundary
+    assert _call(lib, draft=FAKE + 1, ws_bytes=need) == -1
+    assert _call(lib, target=FAKE + 2, dtype=1, ws_bytes=2 * need) == -1  # fp32 off its 4-byte boundary
     assert _call(lib, ws_bytes=need - 1) == -4
     assert _call(lib, ws=None, ws_bytes=need) == -4
     assert _call(lib, ws=FAKE + 8, ws_bytes=need) == -4  # not 256-byte aligned
@@ -152,6 +155,7 @@ def test_opts_host_argument_checks(lib):
     assert call(temperature=FAKE) == -1              # temperatures without seeds
     assert call(stop_offsets=FAKE, n_stop_tokens=-1) == -1
     assert call(stop_offsets=FAKE, n_stop_tokens=3) == -1  # tokens missing
+    assert call(draft_probs=FAKE + 2) == -1          # q rows off their 4-byte boundary
     assert call(verdict_split=-1) == -1
     assert lib.sdv_verify_opts(FAKE, FAKE, FAKE, FAKE, 2, 8, 1000, 0, -1.0, 1, None, FAKE, FAKE, FAKE, need, None,
                                None) == -1
@@ -205,6 +209,8 @@ def test_verify_tree_host_argument_checks(lib):
     assert call(n_dr=1) == -1  # one row per node without indices
     assert call(rows=FAKE, n_dr=3) == -1  # more draft rows than nodes
     assert call(rows=FAKE, n_dr=-1) == -1
+    assert call(target=FAKE + 2) == -1  # fp32 logits off their 4-byte boundary
+    assert call(draft=FAKE + 6) == -1
     for name in ("target", "tokens", "parents", "cu", "acc", "nodes", "out"):
         assert call(**{name: None}) == -1, name
     need = lib.sdv_workspace_bytes(1, 2, 8, 1)

@@ -83,6 +83,55 @@ def test_row_argmax_exact_with_ties(V):
     np.testing.assert_array_equal(dg["target_argmax"], np.argmax(W.bf16_to_f32(b.target), axis=1))
 
 
+def _off_grid(a, dtype, shift):
+    """a on the device, `shift` elements into a fresh buffer: its rows sit on element boundaries only."""
+    if a is None:
+        return None
+    t = to_device(a, dtype)
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+    view = flat[shift:shift + t.numel()].view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 != 0
+    return view
+
+
+@pytest.mark.parametrize("V,dtype,T,shift", [(8192, "bf16", 1.0, 3), (8192, "bf16", 0.0, 5), (4096, "fp32", 0.8, 1),
+                                             (20011, "bf16", 1.0, 7), (20011, "bf16", 0.0, 1), (4099, "fp32", 0.0, 2),
+                                             (9, "bf16", 0.0, 3)])
+def test_rows_off_the_16_byte_grid(V, dtype, T, shift):
+    """Logit bases on an element boundary only, so every chunk is read as head elements, 16-byte
+    vectors and tail elements: normalisers, argmaxes and verdicts against the oracle, with maxima
+    planted at a row's first and last element and ties between those edges and the vectors."""
+    rng = np.random.default_rng(V + shift)
+    depths = rng.integers(0, 7, size=12)
+    b = W.make_random(f"offgrid_v{V}_{dtype}_s{shift}", depths, V, dtype, T, 3.0, rng.uniform(0.5, 3, 12), V + shift,
+                      91)
+    f32 = (lambda a: W.bf16_to_f32(a).copy()) if dtype == "bf16" else (lambda a: a.copy())
+    back = W.bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    tv = f32(b.target)
+    for r in range(tv.shape[0]):
+        top = tv[r].max() + 1.0
+        kind = r % 4
+        if kind == 0:
+            tv[r, 0] = top                      # the head's first element
+        elif kind == 1:
+            tv[r, V - 1] = top                  # the tail's last element
+        elif kind == 2:
+            tv[r, [0, V // 2]] = top            # a head element tied with a vector element
+        else:
+            tv[r, [V // 2, V - 1]] = top        # a vector element tied with a tail element
+    b.target = back(tv)
+    dev = (_off_grid(b.target, dtype, shift), _off_grid(b.draft, dtype, shift), torch.from_numpy(b.tokens).to(DEV),
+           torch.from_numpy(b.cu).to(DEV))
+    diag = ("target_argmax",) if T == 0.0 else ("target_lse", "draft_lse", "terminal_kind")
+    _, _, ref, _, dg = check_parity(b, dev_inputs=dev, diag=diag)
+    if T == 0.0:
+        np.testing.assert_array_equal(dg["target_argmax"], np.argmax(tv, axis=1))
+    else:
+        np.testing.assert_allclose(dg["target_lse"], ref["target_lse"], rtol=0, atol=RTOL_PROB)
+        np.testing.assert_allclose(dg["draft_lse"], ref["draft_lse"], rtol=0, atol=RTOL_PROB)
+
+
 # ----------------------------------------------------------------------------- the five workloads
 
 def test_workload_b1_v1000_fp32_100_rounds():
