@@ -581,44 +581,39 @@ __device__ __forceinline__ int32_t pick_chunk(int32_t C, double u, MassFn mass, 
   return last_pos;
 }
 
-// Residual mass of one chunk of the rejected row pair: coalesced 16-byte loads, fp32 per vector,
-// fp64 across vectors and lanes; each half chunk is summed on its own and the halves added, the order
-// of resid_masses_pipelined, so every pass gives a chunk the same mass.
-template <class E, bool kVec, class M>
+// Residual mass of one chunk of the rejected row pair (16-byte aligned rows): coalesced 16-byte
+// loads, fp32 per vector, fp64 across vectors and lanes; each half chunk is summed on its own and the
+// halves added, the order of resid_masses_pipelined, so every pass gives a chunk the same mass.
+template <class E, class M>
 __device__ __forceinline__ double resid_chunk_mass(const M& m, const char* tp, const char* dp, int32_t c0, int32_t n,
                                                    float k2, float ref_t, float e_hi, float q_scale, int lane) {
+  const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
+  const u32x4* dv = reinterpret_cast<const u32x4*>(dp + (int64_t)c0 * E::kBytes);
+  const int32_t nvec = n / E::kPerVec;
+  constexpr int kHalf = kVecPerLane / 2;  // two halves keep the register footprint at one chunk
   double acc = 0.0;
-  if constexpr (kVec) {
-    const u32x4* tv = reinterpret_cast<const u32x4*>(tp + (int64_t)c0 * E::kBytes);
-    const u32x4* dv = reinterpret_cast<const u32x4*>(dp + (int64_t)c0 * E::kBytes);
-    const int32_t nvec = n / E::kPerVec;
-    constexpr int kHalf = kVecPerLane / 2;  // two halves keep the register footprint at one chunk
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      asm volatile("" ::: "memory");  // keep the second half's loads after the first half's use
-      double half = 0.0;
-      u32x4 tb[kHalf], db[kHalf];
+  for (int h = 0; h < 2; ++h) {
+    asm volatile("" ::: "memory");  // keep the second half's loads after the first half's use
+    double half = 0.0;
+    u32x4 tb[kHalf], db[kHalf];
 #pragma unroll
-      for (int k = 0; k < kHalf; ++k) {
-        const int vi = lane + kWave * (h * kHalf + k);
-        tb[k] = load_vec<E>(tv, vi, nvec);
-        db[k] = load_vec<E>(dv, vi, nvec);
-      }
-#pragma unroll
-      for (int k = 0; k < kHalf; ++k) {
-        float ft[E::kPerVec], fd[E::kPerVec];
-        E::unpack(tb[k], ft);
-        E::unpack(db[k], fd);
-        const int32_t v0 = c0 + (lane + kWave * (h * kHalf + k)) * E::kPerVec;
-#pragma unroll
-        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
-        half += (double)tree_sum(ft);
-      }
-      acc += half;
+    for (int k = 0; k < kHalf; ++k) {
+      const int vi = lane + kWave * (h * kHalf + k);
+      tb[k] = load_vec<E>(tv, vi, nvec);
+      db[k] = load_vec<E>(dv, vi, nvec);
     }
-  } else {
-    for (int32_t v = c0 + lane; v < c0 + n; v += kWave)
-      acc += (double)resid_weight(m, E::at(tp, v), E::at(dp, v), v, k2, ref_t, e_hi, q_scale);
+#pragma unroll
+    for (int k = 0; k < kHalf; ++k) {
+      float ft[E::kPerVec], fd[E::kPerVec];
+      E::unpack(tb[k], ft);
+      E::unpack(db[k], fd);
+      const int32_t v0 = c0 + (lane + kWave * (h * kHalf + k)) * E::kPerVec;
+#pragma unroll
+      for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
+      half += (double)tree_sum(ft);
+    }
+    acc += half;
   }
   return wave_sum(acc);
 }
@@ -768,7 +763,7 @@ __device__ __forceinline__ void resid_masses_pipelined(const M& m, const char* t
   }
   if (c < C) {  // the partial last chunk, if this wave owns it
     const int32_t c0 = c * E::kChunk;
-    const double cm = resid_chunk_mass<E, true>(m, tp, dp, c0, V - c0, k2, ref_t, e_hi, q_scale, lane);
+    const double cm = resid_chunk_mass<E>(m, tp, dp, c0, V - c0, k2, ref_t, e_hi, q_scale, lane);
     if (lane == 0) lds_mass[c] = cm;
   }
 }
@@ -849,6 +844,249 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
   const uint64_t vpos = __ballot(v > 0.0f);
   const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
   const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+  float w[E::kPerVec];
+#pragma unroll
+  for (int jj = 0; jj < kPer; ++jj)
+    if (jj == j) weights(t[jj], dd[jj], base, w);
+  int32_t yl = base + E::kPerVec - 1;
+  int32_t last_pos = -1;
+  double upto = vex;
+  bool found = false;
+#pragma unroll
+  for (int q = 0; q < E::kPerVec; ++q) {
+    upto += (double)w[q];
+    if (w[q] > 0.0f) last_pos = base + q;
+    if (!found && upto > rest) {
+      yl = base + q;
+      found = true;
+    }
+  }
+  if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
+  return lane_value(yl, l);
+}
+
+// ---------------------------------------------------------------------------- rows off the 16-byte grid
+// A chunk [c0, c0 + n) of a row pair whose rows are only element-aligned, split on the target row's
+// 16-byte grid: `body` vectors from element c0 + head on are aligned in the target row, and the
+// draft bytes under vector j are the 16 bytes `shift` past the aligned draft vector dv[j] (one shift
+// for the whole pair: the difference of the two rows' addresses modulo 16).  The head and tail
+// elements go one per lane.  A vector whose aligned draft pieces would reach outside the draft row
+// joins the head or the tail, so every load stays inside its row: at most 2 kPerVec - 1 elements
+// on each side, 30 lanes for bf16.  With the target row as its own draft (dp = tp) the split is the
+// row pass's.
+struct PairSplit {
+  int32_t head, body;  // elements before the first vector; vectors
+  uint32_t shift;      // bytes from an aligned draft vector to the draft bytes under a target vector
+  const u32x4* tv;     // target vector j
+  const u32x4* dv;     // draft pieces of vector j: dv[j] and (shift > 0) dv[j + 1]
+};
+template <class E>
+__device__ __forceinline__ PairSplit pair_split(const char* tp, const char* dp, int32_t V, int32_t c0, int32_t n) {
+  PairSplit s;
+  const uintptr_t t0 = (uintptr_t)(tp + (int64_t)c0 * E::kBytes);
+  s.head = min(n, (int32_t)((((t0 + 15) & ~(uintptr_t)15) - t0) / E::kBytes));
+  s.body = (n - s.head) / E::kPerVec;
+  const uintptr_t x = (uintptr_t)(dp + (int64_t)(c0 + s.head) * E::kBytes);
+  s.shift = (uint32_t)(x & 15);
+  uintptr_t dal = x - s.shift;
+  if (s.body > 0 && dal < (uintptr_t)dp) {  // the first low piece would start before the draft row
+    s.head += E::kPerVec;
+    s.body -= 1;
+    dal += 16;
+  }
+  const uintptr_t d_end = (uintptr_t)(dp + (int64_t)V * E::kBytes);
+  if (s.body > 0 && s.shift != 0 && dal + 16 * (uintptr_t)s.body + 16 > d_end) s.body -= 1;  // the last high piece
+  s.tv = reinterpret_cast<const u32x4*>(tp + (int64_t)(c0 + s.head) * E::kBytes);
+  s.dv = reinterpret_cast<const u32x4*>(dal);
+  return s;
+}
+
+// The 16 bytes `shift` bytes into (lo, hi); shift is a multiple of 2 and the same in every lane, so
+// the word selects are scalar-conditioned moves and the 2-byte step one v_alignbit per word.  The
+// words stay named values: selecting between elements of an array here becomes a select of
+// addresses, which puts the array in scratch memory.
+__device__ __forceinline__ u32x4 funnel16(const u32x4 lo, const u32x4 hi, uint32_t shift) {
+  const bool two = (shift & 8) != 0, one = (shift & 4) != 0;
+  const uint32_t bits = (shift & 3) * 8;
+  const uint32_t a0 = two ? lo.z : lo.x, a1 = two ? lo.w : lo.y, a2 = two ? hi.x : lo.z, a3 = two ? hi.y : lo.w,
+                 a4 = two ? hi.z : hi.x, a5 = two ? hi.w : hi.y;
+  const uint32_t c0 = one ? a1 : a0, c1 = one ? a2 : a1, c2 = one ? a3 : a2, c3 = one ? a4 : a3, c4 = one ? a5 : a4;
+  return u32x4{__builtin_amdgcn_alignbit(c1, c0, bits), __builtin_amdgcn_alignbit(c2, c1, bits),
+               __builtin_amdgcn_alignbit(c3, c2, bits), __builtin_amdgcn_alignbit(c4, c3, bits)};
+}
+
+// Body vector j of a split pair (body >= 1): the target vector, -inf from j = body on, and the draft
+// bytes under it.  Indices are clamped into the body so that every load is unconditional.
+template <class E, bool kResid>
+__device__ __forceinline__ void load_split_pair(const PairSplit& s, int j, u32x4& t, u32x4& d) {
+  const int jc = min(j, s.body - 1);
+  t = s.tv[jc];
+  if constexpr (kResid) {
+    const u32x4 lo = s.dv[jc];
+    const u32x4 hi = s.dv[s.shift != 0 ? jc + 1 : jc];
+    d = funnel16(lo, hi, s.shift);
+  }
+  if (j >= s.body) t = neg_inf_vec<E>();
+}
+
+// The chunk-relative element a lane takes at a split's edges (lanes [0, head): the head, then the
+// tail), or -1.
+__device__ __forceinline__ int32_t split_edge(const PairSplit& s, int32_t n, int per_vec, int lane) {
+  const int32_t e = lane < s.head ? lane : s.head + s.body * per_vec + (lane - s.head);
+  return e < n ? e : -1;
+}
+
+// Residual mass of one chunk of a rejected row pair off the 16-byte grid, by one wave.  The edge
+// elements load first; the body goes in quarters of 4 vectors per lane, the loads of the next
+// quarter issued before the current one is reduced.  Every quarter loads (indices clamped into the
+// body), so no load sits under a branch and the waits count only the loads ahead of the data used.
+template <class E, class M>
+__device__ __forceinline__ double resid_chunk_mass_split(const M& m, const char* tp, const char* dp, int32_t V,
+                                                         int32_t c0, int32_t n, float k2, float ref_t, float e_hi,
+                                                         float q_scale, int lane) {
+  const PairSplit s = pair_split<E>(tp, dp, V, c0, n);
+  const int32_t e = split_edge(s, n, E::kPerVec, lane);
+  float zt = -INFINITY, zd = -INFINITY;
+  if (e >= 0) {
+    zt = E::at(tp, c0 + e);
+    zd = E::at(dp, c0 + e);
+  }
+  double acc = 0.0;
+  if (s.body > 0) {
+    constexpr int kParts = 4, kPart = kVecPerLane / kParts;
+    struct Stage {
+      u32x4 t[kPart], lo[kPart], hi[kPart];
+    };
+    auto load = [&](int h, Stage& st) {
+#pragma unroll
+      for (int k = 0; k < kPart; ++k) {
+        const int jc = min(lane + kWave * (h * kPart + k), s.body - 1);
+        st.t[k] = s.tv[jc];
+        st.lo[k] = s.dv[jc];
+        st.hi[k] = s.dv[s.shift != 0 ? jc + 1 : jc];
+      }
+    };
+    auto pin = [&](Stage& st) {  // the reduction of this stage stays below the loads just issued
+#pragma unroll
+      for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.t[k]), "+v"(st.lo[k]), "+v"(st.hi[k])::"memory");
+    };
+    auto reduce = [&](const Stage& st, int h) {
+      double part = 0.0;
+#pragma unroll
+      for (int k = 0; k < kPart; ++k) {
+        const int j = lane + kWave * (h * kPart + k);
+        float ft[E::kPerVec], fd[E::kPerVec];
+        E::unpack(j < s.body ? st.t[k] : neg_inf_vec<E>(), ft);
+        E::unpack(funnel16(st.lo[k], st.hi[k], s.shift), fd);
+        const int32_t v0 = c0 + s.head + j * E::kPerVec;
+#pragma unroll
+        for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
+        part += (double)tree_sum(ft);
+      }
+      return part;
+    };
+    Stage A, B;
+    load(0, A);
+    load(1, B);
+    pin(A);
+    acc += reduce(A, 0);
+    load(2, A);
+    pin(B);
+    acc += reduce(B, 1);
+    load(3, B);
+    pin(A);
+    acc += reduce(A, 2);
+    pin(B);
+    acc += reduce(B, 3);
+  }
+  if (e >= 0) acc += (double)resid_weight(m, zt, zd, c0 + e, k2, ref_t, e_hi, q_scale);
+  return wave_sum(acc);
+}
+
+// Inverse CDF inside one chunk off the 16-byte grid by a whole workgroup, as search_chunk_block
+// with two more segments: the head's elements before the 16 rows of body vectors and the tail's
+// after them (wave 0 weighs both).  The scan runs over the 18 segment sums; an edge segment is
+// walked by wave 0 lane by lane.  Returns the token in the wave that resolves it, -1 in the
+// others.  row_sums holds at least 18 doubles.
+template <class E, bool kResid, class M>
+__device__ __forceinline__ int32_t search_chunk_split(const M& m, const char* trow, const char* drow, int32_t V,
+                                                      int32_t c0, int32_t n, double target, float k2, float ref_t,
+                                                      float e_hi, float q_scale, double* row_sums, int lane, int wave,
+                                                      int n_waves) {
+  constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
+  constexpr int kPer = kRows / kVerdictWaves;
+  constexpr int kSeg = kRows + 2;  // the head, the rows, the tail
+  const PairSplit s = pair_split<E>(trow, kResid ? drow : trow, V, c0, n);
+  auto weights = [&](const u32x4& t, const u32x4& dd, int32_t v0, float (&w)[E::kPerVec]) {
+    float ft[E::kPerVec], fd[E::kPerVec];
+    E::unpack(t, ft);
+    if constexpr (kResid) E::unpack(dd, fd);
+#pragma unroll
+    for (int q = 0; q < E::kPerVec; ++q)
+      w[q] = kResid ? resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale)
+                    : p_weight(m, ft[q], v0 + q, k2, ref_t);
+  };
+  const int32_t b0 = c0 + s.head;  // the first body element
+  u32x4 t[kPer], dd[kPer];
+  float vs[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    t[j] = neg_inf_vec<E>();
+    dd[j] = neg_inf_vec<E>();
+    if (s.body > 0) load_split_pair<E, kResid>(s, (wave + j * n_waves) * kWave + lane, t[j], dd[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    float w[E::kPerVec];
+    weights(t[j], dd[j], b0 + ((wave + j * n_waves) * kWave + lane) * E::kPerVec, w);
+    vs[j] = tree_sum(w);
+    const double rs = wave_sum((double)vs[j]);
+    if (lane == 0) row_sums[1 + wave + j * n_waves] = rs;
+  }
+  const int32_t e = split_edge(s, n, E::kPerVec, lane);
+  float ew = 0.0f;
+  if (wave == 0) {
+    if (e >= 0)
+      ew = kResid ? resid_weight(m, E::at(trow, c0 + e), E::at(drow, c0 + e), c0 + e, k2, ref_t, e_hi, q_scale)
+                  : p_weight(m, E::at(trow, c0 + e), c0 + e, k2, ref_t);
+    const double hs = wave_sum(lane < s.head ? (double)ew : 0.0);
+    const double ts = wave_sum(lane < s.head ? 0.0 : (double)ew);
+    if (lane == 0) {
+      row_sums[0] = hs;
+      row_sums[kSeg - 1] = ts;
+    }
+  }
+  __syncthreads();
+  const double rsum = lane < kSeg ? row_sums[lane] : 0.0;
+  const double rex = wave_exclusive_scan(rsum, lane);
+  const uint64_t rhit = __ballot(lane < kSeg && rex + rsum > target);
+  const uint64_t rpos = __ballot(lane < kSeg && rsum > 0.0);
+  if (!rhit && !rpos) return wave == 0 ? c0 + n - 1 : -1;
+  const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
+  const double rest = target - lane_value(rex, kr);
+  if (kr == 0 || kr == kSeg - 1) {  // an edge segment (positive sum): wave 0 walks its lanes in order
+    if (wave != 0) return -1;
+    const bool mine = e >= 0 && (kr == 0) == (lane < s.head);
+    const double w = mine ? (double)ew : 0.0;
+    const double ex = wave_exclusive_scan(w, lane);
+    const uint64_t hit = __ballot(rhit && mine && ex + w > rest);
+    const uint64_t pos = __ballot(mine && w > 0.0);
+    const int l = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)pos);
+    return lane_value(c0 + e, l);
+  }
+  const int row = kr - 1;
+  const int owner = row % n_waves;
+  if (wave != owner) return -1;
+  const int j = row / n_waves;
+  float v = vs[0];  // j is uniform: selects, not an indexed register array
+#pragma unroll
+  for (int jj = 1; jj < kPer; ++jj)
+    if (jj == j) v = vs[jj];
+  const double vex = wave_exclusive_scan((double)v, lane);
+  const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
+  const uint64_t vpos = __ballot(v > 0.0f);
+  const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
+  const int32_t base = b0 + (row * kWave + lane) * E::kPerVec;
   float w[E::kPerVec];
 #pragma unroll
   for (int jj = 0; jj < kPer; ++jj)
@@ -2434,8 +2672,8 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     } else {
       for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
         const int32_t c0 = c * E::kChunk;
-        const double cm = resid_chunk_mass<E, false>(m, tp, dp, c0, min(E::kChunk, P.V - c0), k2, d.ref_t, d.e_hi,
-                                                     d.q_scale, lane);
+        const double cm = resid_chunk_mass_split<E>(m, tp, dp, P.V, c0, min(E::kChunk, P.V - c0), k2, d.ref_t,
+                                                    d.e_hi, d.q_scale, lane);
         if (lane == 0) lds_mass[c] = cm;
       }
     }
@@ -2535,17 +2773,18 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
       y = search_chunk_block<E, false>(m, tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C, lane,
                                        wave, n_waves);
   } else {
-    if (wave != 0) return;
-    const float ref_t = d.ref_t, e_hi = d.e_hi, q_scale = d.q_scale;
-    if (residual && kQ)
+    if (residual && kQ) {
+      if (wave != 0) return;
+      const float ref_t = d.ref_t, q_scale = d.q_scale;
       y = search_chunk<E>(
           s0, n, tgt, [&](int32_t v) { return resid_weight_q(m, E::at(tp, v), qp[v], v, k2, ref_t, q_scale); }, lane);
-    else if (residual)
-      y = search_chunk<E>(
-          s0, n, tgt,
-          [&](int32_t v) { return resid_weight(m, E::at(tp, v), E::at(dp, v), v, k2, ref_t, e_hi, q_scale); }, lane);
-    else
-      y = search_chunk<E>(s0, n, tgt, [&](int32_t v) { return p_weight(m, E::at(tp, v), v, k2, ref_t); }, lane);
+    } else if (residual) {
+      y = search_chunk_split<E, true>(m, tp, dp, P.V, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
+                                      wave, n_waves);
+    } else {
+      y = search_chunk_split<E, false>(m, tp, nullptr, P.V, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
+                                       lane, wave, n_waves);
+    }
   }
   write_token(y, empty, S);
 }
