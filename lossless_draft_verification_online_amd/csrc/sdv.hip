@@ -354,6 +354,8 @@ __device__ __forceinline__ float2 record_of(u32x4 (&buf)[kVecPerLane], int32_t c
 // [0, head) take the head, the next lanes the tail).  Every load stays inside the chunk.
 struct SplitEdge {
   int32_t head;  // elements before the first aligned vector
+  int32_t body;  // aligned vectors
+  bool ok;       // the lane holds an edge element
   float z;       // the lane's edge element, -inf on lanes without one
   int32_t v;     // its index in the row
 };
@@ -367,8 +369,10 @@ __device__ __forceinline__ SplitEdge load_split_chunk(const char* rp, int32_t c0
   const int32_t e = lane < head ? lane : head + body + (lane - head);
   SplitEdge s;
   s.head = head;
+  s.body = body / E::kPerVec;
+  s.ok = e < n;
   s.v = c0 + e;
-  s.z = e < n ? E::at(rp, s.v) : -INFINITY;
+  s.z = s.ok ? E::at(rp, s.v) : -INFINITY;
   return s;
 }
 
@@ -458,6 +462,39 @@ __device__ __forceinline__ float2 record_counting(u32x4 (&buf)[kVecPerLane], flo
   const float s = exp_sum<Bf16, true>(buf, k2, ref, counts ? hm : kCountNothing, kHistKeys + lane, h);
   __builtin_amdgcn_wave_barrier();
   out[lane] = h[2 * lane] | (h[2 * lane + 1] << 16);  // a chunk holds at most 8192 logits
+  return make_float2(ref, s);
+}
+
+// record_counting over a bf16 chunk split at 16-byte boundaries (load_split_chunk): the lane's edge
+// element is counted and summed beside the vectors (a lane without one counts the -inf pattern,
+// which lands on its spare counter).
+__device__ __forceinline__ float2 record_counting_split(u32x4 (&buf)[kVecPerLane], const SplitEdge& se, float k2,
+                                                        int lane, uint32_t* h, uint32_t* out, uint32_t* top) {
+  float ml = se.z;
+#pragma unroll
+  for (int k = 0; k < kVecPerLane; ++k) {
+    float f[Bf16::kPerVec];
+    Bf16::unpack(buf[k], f);
+#pragma unroll
+    for (int e = 0; e < Bf16::kPerVec; ++e) ml = fmaxf(ml, f[e]);
+  }
+  const float m = wave_max(ml);
+  const uint32_t hm = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(m)) >> 16;
+  const uint32_t kmax = key16_of_bits(hm);
+  const bool counts = hm >= (uint32_t)kHistKeys && hm < 0x8000u;
+  if (lane == 0) *top = counts ? kmax : (kmax | kNoCounts);
+  if (m == -INFINITY) return make_float2(-INFINITY, 0.0f);
+  const float ref = m * k2;
+  h[2 * lane] = 0u;
+  h[2 * lane + 1] = 0u;
+  __builtin_amdgcn_wave_barrier();  // a wave's shared-memory operations complete in order
+  const uint32_t hc = counts ? hm : kCountNothing, spare = kHistKeys + lane;
+  float s = exp_sum<Bf16, true>(buf, k2, ref, hc, spare, h);
+  const uint32_t d = hc - (se.ok ? __float_as_uint(se.z) >> 16 : 0xff80u);
+  atomicAdd(&h[d < spare ? d : spare], 1u);
+  s += wave_sum(fast_exp2(fmaf(se.z, k2, -ref)));
+  __builtin_amdgcn_wave_barrier();
+  out[lane] = h[2 * lane] | (h[2 * lane + 1] << 16);
   return make_float2(ref, s);
 }
 
@@ -640,7 +677,7 @@ constexpr int64_t kWideRowUnits = 16384;
 
 template <class E, int kMode, bool kVec, bool kHist, int kWaves = kRowWaves>
 __global__ __launch_bounds__(kWave * kWaves) void row_records(Params P) {
-  static_assert(!kHist || (E::kBytes == 2 && kVec && kMode != kModeGreedy), "counts: bf16 sampling, 16-byte rows");
+  static_assert(!kHist || (E::kBytes == 2 && kMode != kModeGreedy), "counts: bf16 sampling rows");
   static_assert(kHistKeys == 2 * kWave, "each lane writes one word of two counts");
   __shared__ uint32_t hcnt_all[kHist ? kWaves : 1][kHist ? kHistKeys + kWave : 1];  // counters, then spares
   const int lane = threadIdx.x & (kWave - 1);
@@ -663,8 +700,13 @@ __global__ __launch_bounds__(kWave * kWaves) void row_records(Params P) {
   if (kHist && u == 0 && lane == 0) P.pending[0] = 0;  // the count kernel appends to an empty list
   if constexpr (kHist && kMode != kModeProfiled) {
     u32x4 buf[kVecPerLane];
-    load_chunk<E>(rp, c0, n, lane, buf);
-    rec = record_counting(buf, P.k2, lane, hcnt, P.hist + u * (kHistKeys / 2), P.hist_top + u);
+    if constexpr (kVec) {
+      load_chunk<E>(rp, c0, n, lane, buf);
+      rec = record_counting(buf, P.k2, lane, hcnt, P.hist + u * (kHistKeys / 2), P.hist_top + u);
+    } else {
+      const SplitEdge se = load_split_chunk<E>(rp, c0, n, lane, buf);
+      rec = record_counting_split(buf, se, P.k2, lane, hcnt, P.hist + u * (kHistKeys / 2), P.hist_top + u);
+    }
   } else if constexpr (kMode != kModeProfiled) {
     rec = chunk_record<E, kMode == kModeGreedy, kVec>(rp, c0, n, P.k2, lane);
   } else {
@@ -687,8 +729,14 @@ __global__ __launch_bounds__(kWave * kWaves) void row_records(Params P) {
     } else {
       const float k2 = k2_of(temperature_of(P.temp_each, request_of_row(P.cu, P.B, row, target)));
       if (!target && !(k2 > 0.0f)) return;
-      rec = k2 > 0.0f ? chunk_record<E, false, false>(rp, c0, n, k2, lane)
-                      : chunk_record<E, true, false>(rp, c0, n, 0.0f, lane);
+      u32x4 buf[kVecPerLane];
+      const SplitEdge se = load_split_chunk<E>(rp, c0, n, lane, buf);
+      if constexpr (kHist)
+        rec = k2 > 0.0f ? record_counting_split(buf, se, k2, lane, hcnt, P.hist + u * (kHistKeys / 2), P.hist_top + u)
+                        : record_of_split<E, true>(buf, se, c0, 0.0f, lane);
+      else
+        rec = k2 > 0.0f ? record_of_split<E, false>(buf, se, c0, k2, lane)
+                        : record_of_split<E, true>(buf, se, c0, 0.0f, lane);
     }
   }
   if (lane == 0) P.part[u] = rec;
@@ -931,7 +979,8 @@ __device__ __forceinline__ void load_split_pair(const PairSplit& s, int j, u32x4
 
 // The chunk-relative element a lane takes at a split's edges (lanes [0, head): the head, then the
 // tail), or -1.
-__device__ __forceinline__ int32_t split_edge(const PairSplit& s, int32_t n, int per_vec, int lane) {
+template <class Split>
+__device__ __forceinline__ int32_t split_edge(const Split& s, int32_t n, int per_vec, int lane) {
   const int32_t e = lane < s.head ? lane : s.head + s.body * per_vec + (lane - s.head);
   return e < n ? e : -1;
 }
@@ -1342,7 +1391,7 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
 // logit differ only in token id).  Both follow from counts over an order-preserving key of the
 // logits: every copy of a key has the same mass, so counts give masses.
 //
-//  row_cuts_counted  bf16 rows of 16-byte length: the row pass has counted, per chunk, the 128 keys
+//  row_cuts_counted  bf16 rows: the row pass has counted, per chunk, the 128 keys
 //                    at and below the chunk maximum's (section 1); one wave per row sums them into
 //                    the row's top 128 keys and settles the cut when it lands there.  Other rows go
 //                    on a list for row_cuts.
@@ -1526,54 +1575,64 @@ __device__ __forceinline__ void select_bin(int nb, BinCount count_of, BinMass ma
 }
 
 // Every logit of a row, visited by the workgroup (f(z, bits, v); bits are the logit's raw 16 bits
-// for bf16 rows).  16-byte rows go by chunks, as the row pass reads them: wave w takes chunks w,
-// w + 8, ..., each loaded whole (16 vectors per lane, 16 KiB in flight per wave) before it is
-// visited; the partial last chunk goes through bounds-tested loads.
+// for bf16 rows).  The row goes by 16-byte vectors, as the row pass reads it: wave w takes chunks w,
+// w + 8, ... of the vectors, each loaded whole (16 vectors per lane, 16 KiB in flight per wave)
+// before it is visited; the partial last chunk goes through bounds-tested loads.  A row that is
+// only element-aligned (kVec false) starts its vectors at its first 16-byte boundary; the elements
+// before it and after the last whole vector are visited one per thread.
 template <class E, bool kVec, class F>
 __device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-  auto visit = [&](const u32x4& v, int32_t vi) {
+  auto visit = [&](const u32x4& v, int32_t v0) {  // v0: the row index of the vector's first element
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     if constexpr (E::kBytes == 2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        f(__uint_as_float(w[q] << 16), w[q] & 0xffffu, vi * 8 + 2 * q);
-        f(__uint_as_float(w[q] & 0xffff0000u), w[q] >> 16, vi * 8 + 2 * q + 1);
+        f(__uint_as_float(w[q] << 16), w[q] & 0xffffu, v0 + 2 * q);
+        f(__uint_as_float(w[q] & 0xffff0000u), w[q] >> 16, v0 + 2 * q + 1);
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) f(__uint_as_float(w[q]), 0u, vi * 4 + q);
+      for (int q = 0; q < 4; ++q) f(__uint_as_float(w[q]), 0u, v0 + q);
     }
   };
-  if constexpr (kVec) {
-    const u32x4* vp = reinterpret_cast<const u32x4*>(rp);
-    constexpr int32_t kVecPerChunk = E::kChunk / E::kPerVec;
-    const int32_t C_full = V / E::kChunk, nvec = V / E::kPerVec;  // 16-byte rows: no partial vector
-    for (int32_t c = wave; c < C_full; c += kCutWaves) {
-      const u32x4* cp = vp + (int64_t)c * kVecPerChunk;
-      u32x4 buf[kVecPerLane];
+  auto visit_one = [&](int32_t v) {
+    if constexpr (E::kBytes == 2) {
+      const uint32_t h = reinterpret_cast<const uint16_t*>(rp)[v];
+      f(__uint_as_float(h << 16), h, v);
+    } else {
+      f(E::at(rp, v), 0u, v);
+    }
+  };
+  int32_t head = 0;  // elements before the first 16-byte boundary
+  if constexpr (!kVec) {
+    const uintptr_t r0 = (uintptr_t)rp;
+    head = min(V, (int32_t)((((r0 + 15) & ~(uintptr_t)15) - r0) / E::kBytes));
+  }
+  const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)head * E::kBytes);
+  constexpr int32_t kVecPerChunk = E::kChunk / E::kPerVec;
+  const int32_t nvec = (V - head) / E::kPerVec, C_full = nvec / kVecPerChunk;
+  for (int32_t c = wave; c < C_full; c += kCutWaves) {
+    const u32x4* cp = vp + (int64_t)c * kVecPerChunk;
+    u32x4 buf[kVecPerLane];
 #pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) buf[k] = cp[lane + kWave * k];
+    for (int k = 0; k < kVecPerLane; ++k) buf[k] = cp[lane + kWave * k];
 #pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) {
-        // one vector at a time: its keys are not all computed ahead of the atomics
-        asm volatile("" : "+v"(buf[k])::"memory");
-        visit(buf[k], c * kVecPerChunk + lane + kWave * k);
-      }
+    for (int k = 0; k < kVecPerLane; ++k) {
+      // one vector at a time: its keys are not all computed ahead of the atomics
+      asm volatile("" : "+v"(buf[k])::"memory");
+      visit(buf[k], head + (c * kVecPerChunk + lane + kWave * k) * E::kPerVec);
     }
-    if (C_full * kVecPerChunk < nvec && C_full % kCutWaves == wave) {  // the partial last chunk
-      for (int32_t vi = C_full * kVecPerChunk + lane; vi < nvec; vi += kWave) visit(vp[vi], vi);
-    }
-  } else {
-    for (int32_t v = threadIdx.x; v < V; v += kCutThreads) {
-      if constexpr (E::kBytes == 2) {
-        const uint32_t h = reinterpret_cast<const uint16_t*>(rp)[v];
-        f(__uint_as_float(h << 16), h, v);
-      } else {
-        f(E::at(rp, v), 0u, v);
-      }
-    }
+  }
+  if (C_full * kVecPerChunk < nvec && C_full % kCutWaves == wave) {  // the partial last chunk
+    for (int32_t vi = C_full * kVecPerChunk + lane; vi < nvec; vi += kWave) visit(vp[vi], head + vi * E::kPerVec);
+  }
+  if constexpr (!kVec) {  // the head, then the tail after the last whole vector
+    const int32_t tail0 = head + nvec * E::kPerVec;
+    const int t = threadIdx.x;
+    if (t < head) visit_one(t);
+    else if (t - head < V - tail0) visit_one(tail0 + (t - head));
   }
 }
 
@@ -1825,6 +1884,19 @@ __device__ __forceinline__ void chunk_pass(const char* rp, int32_t V, int32_t C,
 #pragma unroll
         for (int e = 0; e < E::kPerVec; ++e) take(z[e]);
       }
+    } else if (!kVec) {  // split at 16-byte boundaries; the -inf padding past the body is not taken
+      u32x4 buf[kVecPerLane];
+      const SplitEdge se = load_split_chunk<E>(rp, c0, n, lane, buf);
+#pragma unroll
+      for (int k = 0; k < kVecPerLane; ++k) {
+        float z[E::kPerVec];
+        E::unpack(buf[k], z);
+        if (lane + kWave * k < se.body) {
+#pragma unroll
+          for (int e = 0; e < E::kPerVec; ++e) take(z[e]);
+        }
+      }
+      if (se.ok) take(se.z);
     } else {
       for (int32_t v = c0 + lane; v < c0 + n; v += kWave) take(E::at(rp, v));
     }
@@ -1862,7 +1934,8 @@ __device__ __forceinline__ RowProfile row_profile(const Params& P, int32_t slot)
 // The last steps of a row's cut, by one wave: the kept copies of the cut value per chunk in token
 // order, each chunk record's mass rewritten to the mass of the chunk's kept tokens, and the token id
 // of the last kept copy (unless every copy is kept: chunk cstar is loaded whole and searched in
-// registers, its vectors in token order, vector k * 64 + lane).  chunks(cb, st, cp), called by
+// registers, its vectors in token order, vector k * 64 + lane; a chunk off the 16-byte grid is
+// split, its head elements searched before the vectors and its tail after).  chunks(cb, st, cp), called by
 // every lane, gives chunk cb + lane's mass of kept tokens strictly above kappa (in its record's
 // frame) and its copies of kappa (0 past the last chunk).  Writes cuts[slot] and kept_tokens[slot].
 template <class E, bool kVec, class ChunkFn>
@@ -1897,53 +1970,61 @@ __device__ __forceinline__ void finish_cut(const Params& P, int32_t slot, const 
   if (n_eq < ties && cstar >= 0) {
     const int32_t c0 = cstar * E::kChunk, end = min(c0 + E::kChunk, P.V);
     uint32_t need = rstar;
+    u32x4 buf[kVecPerLane];
+    int32_t b0 = c0, nb = (end - c0) / E::kPerVec;  // the first vector element; vectors
+    SplitEdge se{};
     if constexpr (kVec) {
-      const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)c0 * E::kBytes);
-      const int32_t nvec = (end - c0) / E::kPerVec;
-      u32x4 buf[kVecPerLane];
+      load_chunk<E>(rp, c0, end - c0, lane, buf);
+    } else {  // split at 16-byte boundaries: the head's elements, the vectors, the tail's elements
+      se = load_split_chunk<E>(rp, c0, end - c0, lane, buf);
+      b0 = c0 + se.head;
+      nb = se.body;
+    }
+    // the need-th copy among the lanes flagged by hit (in lane order), if there are that many
+    auto among = [&](bool hit, int32_t v) {
+      const uint64_t m = __ballot(hit);
+      const uint32_t total = (uint32_t)__popcll((unsigned long long)m);
+      if (need > total) {
+        need -= total;
+        return false;
+      }
+      uint64_t mm = m;
+      for (uint32_t q = 1; q < need; ++q) mm &= mm - 1;  // drop the first need - 1 hits
+      vcut = lane_value(v, __ffsll((unsigned long long)mm) - 1);
+      return true;
+    };
+    bool found = !kVec && among(se.ok && lane < se.head && se.z == kappa, se.v);
+    // no break: a loop left early is not unrolled, and its indexing would put buf in scratch memory
 #pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) buf[k] = load_vec<E>(vp, lane + kWave * k, nvec);
+    for (int k = 0; k < kVecPerLane; ++k) {
+      if (found) continue;
+      float z[E::kPerVec];
+      E::unpack(buf[k], z);
+      uint32_t mask = 0u;
 #pragma unroll
-      for (int k = 0; k < kVecPerLane; ++k) {
-        float z[E::kPerVec];
-        E::unpack(buf[k], z);
-        uint32_t mask = 0u;
+      for (int e = 0; e < E::kPerVec; ++e)
+        if (lane + kWave * k < nb && z[e] == kappa) mask |= 1u << e;
+      const uint32_t mine = (uint32_t)__popc(mask);
+      const uint32_t incl = wave_inclusive_scan(mine);
+      const uint32_t total = lane_value(incl, kWave - 1);
+      if (need <= total) {
+        const uint64_t at = __ballot(incl - mine < need && need <= incl);
+        const int g = __ffsll((unsigned long long)at) - 1;
+        int32_t v = -1;
+        uint32_t left = need - (incl - mine);
 #pragma unroll
         for (int e = 0; e < E::kPerVec; ++e)
-          if (lane + kWave * k < nvec && z[e] == kappa) mask |= 1u << e;
-        const uint32_t mine = (uint32_t)__popc(mask);
-        const uint32_t incl = wave_inclusive_scan(mine);
-        const uint32_t total = lane_value(incl, kWave - 1);
-        if (need <= total) {
-          const uint64_t at = __ballot(incl - mine < need && need <= incl);
-          const int g = __ffsll((unsigned long long)at) - 1;
-          int32_t v = -1;
-          uint32_t left = need - (incl - mine);
-#pragma unroll
-          for (int e = 0; e < E::kPerVec; ++e)
-            if ((mask >> e) & 1u) {
-              if (left == 1u && v < 0) v = c0 + (lane + kWave * k) * E::kPerVec + e;
-              --left;
-            }
-          vcut = lane_value(v, g);
-          break;
-        }
-        need -= total;
-      }
-    } else {
-      for (int32_t b = c0; b < end; b += kWave) {  // 64 consecutive tokens per step
-        const bool hit = b + lane < end && E::at(rp, b + lane) == kappa;
-        const uint64_t m = __ballot(hit);
-        const uint32_t total = (uint32_t)__popcll((unsigned long long)m);
-        if (need <= total) {
-          uint64_t mm = m;
-          for (uint32_t q = 1; q < need; ++q) mm &= mm - 1;  // drop the first need - 1 hits
-          vcut = b + __ffsll((unsigned long long)mm) - 1;
-          break;
-        }
+          if ((mask >> e) & 1u) {
+            if (left == 1u && v < 0) v = b0 + (lane + kWave * k) * E::kPerVec + e;
+            --left;
+          }
+        vcut = lane_value(v, g);
+        found = true;
+      } else {
         need -= total;
       }
     }
+    if (!kVec && !found) among(se.ok && lane >= se.head && se.z == kappa, se.v);
   }
   if (lane == 0) {
     P.cuts[slot] = Cut{kappa, vcut};
@@ -2068,6 +2149,7 @@ __global__ __launch_bounds__(kCutThreads) void row_cuts(Params P) {
 // the row is read only where ties of the cut value leave a token id to find.  Otherwise (the cut
 // lies deeper, or a chunk that could not be counted reaches the window) the row is left pending
 // for row_cuts.  Lane l holds the keys top - 2l and top - 2l - 1.
+template <bool kVec>
 __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   // per wave: the lanes' contributions to 16 chunks, transposed (rows padded to 65 words), and
   // the 64 chunk sums of a batch
@@ -2200,7 +2282,7 @@ __global__ __launch_bounds__(256) void row_cuts_counted(Params P) {
   // per chunk: the kept mass above kappa (in the chunk record's frame) and the copies of kappa,
   // from the chunk's counts of the lanes' keys (a second pass over counts that are still cached)
   const float z0 = key_logit(key16_to_key(key0)), z1 = key_logit(key16_to_key(key1));
-  finish_cut<Bf16, true>(P, slot, rp, rec, kappa, f.k2, s.ties, n_eq, kept,
+  finish_cut<Bf16, kVec>(P, slot, rp, rec, kappa, f.k2, s.ties, n_eq, kept,
                          [&](int32_t cb, float& st, uint32_t& cp) {
                            const int nc = min(kWave, P.C - cb);
                            const uint32_t mine = cb + lane < P.C ? htop[cb + lane] : kNoCounts;
@@ -2851,8 +2933,42 @@ __device__ __forceinline__ float chain_weight(const ChainFrame& f, const char* t
 constexpr int kTreeWaves = 16;  // waves of a tree verdict workgroup (the passes are VALU-bound per CU)
 constexpr int kTreeGroup = 4;  // vectors per lane in flight per row in a residual pass
 
+// A chunk of a node's target row split on its 16-byte grid for the tree passes, whose draft rows
+// each sit at their own offset: while the first vector lies within 16 bytes of the row start it
+// joins the head, and while the last ends within 16 bytes of the row end it joins the tail, so the
+// two aligned pieces under any vector of any draft row stay inside that row.
+struct TreeSplit {
+  int32_t head, body;  // elements before the first vector; vectors
+  const u32x4* tv;     // target vector j
+};
+template <class E>
+__device__ __forceinline__ TreeSplit tree_split(const char* tp, int32_t V, int32_t c0, int32_t n) {
+  TreeSplit s;
+  const uintptr_t t0 = (uintptr_t)(tp + (int64_t)c0 * E::kBytes);
+  s.head = min(n, (int32_t)((((t0 + 15) & ~(uintptr_t)15) - t0) / E::kBytes));
+  s.body = (n - s.head) / E::kPerVec;
+  if (s.body > 0 && (int64_t)(c0 + s.head) * E::kBytes < 16) {
+    s.head += E::kPerVec;
+    s.body -= 1;
+  }
+  if (s.body > 0 && (int64_t)(c0 + s.head + s.body * E::kPerVec) * E::kBytes + 16 > (int64_t)V * E::kBytes)
+    s.body -= 1;
+  s.tv = reinterpret_cast<const u32x4*>(tp + (int64_t)(c0 + s.head) * E::kBytes);
+  return s;
+}
+
+// The bytes of draft row dp under body vector jc of a tree split (0 <= jc < body).
+template <class E>
+__device__ __forceinline__ u32x4 tree_draft_vec(const char* dp, int32_t c0, const TreeSplit& s, int jc) {
+  const uintptr_t x = (uintptr_t)(dp + (int64_t)(c0 + s.head) * E::kBytes);
+  const uint32_t shift = (uint32_t)(x & 15);
+  const u32x4* dv = reinterpret_cast<const u32x4*>(x - shift);
+  return funnel16(dv[jc], dv[shift != 0 ? jc + 1 : jc], shift);
+}
+
 // Chunk masses of R_l into lds_mass[0 .. C) by the whole workgroup (wave w takes chunks w,
-// w + n_waves, ...): 16-byte vectors, four in flight per lane, fp32 per vector, fp64 across vectors.
+// w + n_waves, ...): 16-byte vectors, four in flight per lane, fp32 per vector, fp64 across vectors
+// (rows off the 16-byte grid: split as tree_split says, the edge elements one per lane).
 template <class E, bool kVec>
 __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* trow, const void* draft, int32_t V,
                                              int32_t C, double* lds_mass, int lane, int wave, int n_waves) {
@@ -2863,12 +2979,17 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
       const int32_t nvec = n / E::kPerVec;
       const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
       constexpr int kGroup = kTreeGroup;
-      for (int g0 = 0; g0 < kVecPerLane; g0 += kGroup) {
+      // indices clamped into the chunk keep every load unconditional (a vector past the end has a
+      // target of -inf, so R is 0 there whatever the draft row holds)
+      for (int g0 = 0; g0 < kVecPerLane && g0 * kWave < nvec; g0 += kGroup) {
         float R[kGroup][E::kPerVec];
+        auto jc = [&](int k) { return min(lane + kWave * (g0 + k), nvec - 1); };
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) {
+          const int j = lane + kWave * (g0 + k);
+          const u32x4 t = tv[jc(k)];
           float z[E::kPerVec];
-          E::unpack(load_vec<E>(tv, lane + kWave * (g0 + k), nvec), z);
+          E::unpack(j < nvec ? t : neg_inf_vec<E>(), z);
 #pragma unroll
           for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_p(f, z[e]);
         }
@@ -2877,7 +2998,7 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
           const u32x4* dv = reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
           u32x4 b[kGroup];
 #pragma unroll
-          for (int k = 0; k < kGroup; ++k) b[k] = load_vec<E>(dv, lane + kWave * (g0 + k), nvec);
+          for (int k = 0; k < kGroup; ++k) b[k] = dv[jc(k)];
           const float d_hi = f.d_hi[j], d_lo = f.d_lo[j];
           float q[kGroup][E::kPerVec];
 #pragma unroll
@@ -2898,38 +3019,96 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
       }
-    } else {
-      for (int32_t v = c0 + lane; v < c0 + n; v += kWave) acc += (double)chain_weight<E>(f, trow, draft, V, v);
+    } else {  // split on the target row's 16-byte grid: body vectors, then the lane's edge element
+      const TreeSplit s = tree_split<E>(trow, V, c0, n);
+      const int32_t e = split_edge(s, n, E::kPerVec, lane);
+      constexpr int kGroup = kTreeGroup;
+      for (int g0 = 0; g0 < kVecPerLane && g0 * kWave < s.body; g0 += kGroup) {
+        float R[kGroup][E::kPerVec];
+        int jc[kGroup];
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+          const int j = lane + kWave * (g0 + k);
+          jc[k] = min(j, s.body - 1);
+          float z[E::kPerVec];
+          const u32x4 t = s.tv[jc[k]];
+          E::unpack(j < s.body ? t : neg_inf_vec<E>(), z);
+#pragma unroll
+          for (int q = 0; q < E::kPerVec; ++q) R[k][q] = chain_p(f, z[q]);
+        }
+        for (int j = 0; j < f.l;) {
+          const int j1 = chain_run_end(f, j);
+          const char* dp = row_ptr<E>(draft, f.drow[j], V);
+          u32x4 b[kGroup];
+#pragma unroll
+          for (int k = 0; k < kGroup; ++k) b[k] = tree_draft_vec<E>(dp, c0, s, jc[k]);
+          const float d_hi = f.d_hi[j], d_lo = f.d_lo[j];
+          float q[kGroup][E::kPerVec];
+#pragma unroll
+          for (int k = 0; k < kGroup; ++k) {
+            float z[E::kPerVec];
+            E::unpack(b[k], z);
+#pragma unroll
+            for (int e2 = 0; e2 < E::kPerVec; ++e2) q[k][e2] = fast_exp2(fmaf(z[e2], f.k2, -d_hi) - d_lo);
+          }
+          for (; j < j1; ++j) {
+            const float m = f.m[j];
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k)
+#pragma unroll
+              for (int e2 = 0; e2 < E::kPerVec; ++e2) R[k][e2] = fmaxf(fmaf(-m, q[k][e2], R[k][e2]), 0.0f);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
+      }
+      if (e >= 0) acc += (double)chain_weight<E>(f, trow, draft, V, c0 + e);
     }
     acc = wave_sum(acc);
     if (lane == 0) lds_mass[c] = acc;
   }
 }
 
-// Inverse CDF inside one chunk (16-byte aligned rows) by the whole workgroup: the chunk's vectors form
-// 16 rows of 64 (vector r*64 + l for lane l); wave w sums rows w, w + n_waves, ..., every wave scans
-// the row sums, and the wave owning the crossing row recomputes its vectors, scans their sums across
-// the lanes and walks the chosen vector.  kChain: the weights are R_l(v) of the frame f; else the
-// node's own p in the frame 2^(z k - ref).  If rounding leaves the target unreached, the last element
-// of positive weight is taken.  row_sums holds 16 doubles; the token is returned in every wave.
-template <class E, bool kChain>
+// Inverse CDF inside one chunk by the whole workgroup: the chunk's vectors form 16 rows of 64
+// (vector r*64 + l for lane l); wave w sums rows w, w + n_waves, ..., every wave scans the row sums,
+// and the wave owning the crossing row recomputes its vectors, scans their sums across the lanes and
+// walks the chosen vector.  A row off the 16-byte grid (kVec false) is split as tree_split says: two
+// more segments, the head's elements before the rows and the tail's after them, weighed by wave 0
+// and walked by it lane by lane.  kChain: the weights are R_l(v) of the frame f; else the node's own
+// p in the frame 2^(z k - ref).  If rounding leaves the target unreached, the last element of
+// positive weight is taken.  row_sums holds 18 doubles; the token is returned in every wave.
+template <class E, bool kChain, bool kVec>
 __device__ __forceinline__ int32_t tree_search_block(const ChainFrame& f, const char* trow, const void* draft,
                                                      int32_t V, int32_t c0, int32_t n, double target, float ref,
                                                      double* row_sums, int32_t* token, int lane, int wave,
                                                      int n_waves) {
+  constexpr int kOff = kVec ? 0 : 1;            // off the grid the head's segment comes first
+  constexpr int kSeg = kVecPerLane + 2 * kOff;  // the 16 rows (and the head and the tail)
   const int32_t nvec = n / E::kPerVec;
-  const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
+  TreeSplit s{0, nvec, reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes)};
+  if constexpr (!kVec) s = tree_split<E>(trow, V, c0, n);
+  const int32_t b0 = c0 + s.head;  // the first body element
   auto weights = [&](int vi, float (&w)[E::kPerVec]) {
     float z[E::kPerVec];
-    E::unpack(load_vec<E>(tv, vi, nvec), z);
+    int jc = 0;
+    if constexpr (kVec) {
+      E::unpack(load_vec<E>(s.tv, vi, nvec), z);
+    } else {
+      jc = min(vi, s.body - 1);
+      const u32x4 t = s.body > 0 ? s.tv[jc] : neg_inf_vec<E>();
+      E::unpack(vi < s.body ? t : neg_inf_vec<E>(), z);
+    }
     if constexpr (kChain) {
 #pragma unroll
       for (int e = 0; e < E::kPerVec; ++e) w[e] = chain_p(f, z[e]);
       for (int j = 0; j < f.l;) {
         const int j1 = chain_run_end(f, j);
-        const u32x4* dv = reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
+        const char* dp = row_ptr<E>(draft, f.drow[j], V);
         float zd[E::kPerVec];
-        E::unpack(load_vec<E>(dv, vi, nvec), zd);
+        if constexpr (kVec)
+          E::unpack(load_vec<E>(reinterpret_cast<const u32x4*>(dp + (int64_t)c0 * E::kBytes), vi, nvec), zd);
+        else
+          E::unpack(s.body > 0 ? tree_draft_vec<E>(dp, c0, s, jc) : neg_inf_vec<E>(), zd);
 #pragma unroll
         for (int e = 0; e < E::kPerVec; ++e) w[e] = chain_run(f, j, j1, w[e], zd[e]);
         j = j1;
@@ -2943,27 +3122,54 @@ __device__ __forceinline__ int32_t tree_search_block(const ChainFrame& f, const 
     float w[E::kPerVec];
     weights(r * kWave + lane, w);
     const double rs = wave_sum((double)tree_sum(w));
-    if (lane == 0) row_sums[r] = rs;
+    if (lane == 0) row_sums[kOff + r] = rs;
+  }
+  int32_t e = -1;
+  float ew = 0.0f;
+  if constexpr (!kVec) {
+    e = split_edge(s, n, E::kPerVec, lane);
+    if (wave == 0) {
+      if (e >= 0)
+        ew = kChain ? chain_weight<E>(f, trow, draft, V, c0 + e) : fast_exp2(fmaf(E::at(trow, c0 + e), f.k2, -ref));
+      const double hs = wave_sum(lane < s.head ? (double)ew : 0.0);
+      const double ts = wave_sum(lane < s.head ? 0.0 : (double)ew);
+      if (lane == 0) {
+        row_sums[0] = hs;
+        row_sums[kSeg - 1] = ts;
+      }
+    }
   }
   __syncthreads();
-  const double rsum = lane < kVecPerLane ? row_sums[lane] : 0.0;
+  const double rsum = lane < kSeg ? row_sums[lane] : 0.0;
   const double rex = wave_exclusive_scan(rsum, lane);
-  const uint64_t rhit = __ballot(lane < kVecPerLane && rex + rsum > target);
-  const uint64_t rpos = __ballot(lane < kVecPerLane && rsum > 0.0);
+  const uint64_t rhit = __ballot(lane < kSeg && rex + rsum > target);
+  const uint64_t rpos = __ballot(lane < kSeg && rsum > 0.0);
   if (!rhit && !rpos) {
     if (wave == 0 && lane == 0) *token = c0 + n - 1;
   } else {
     const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
-    if (wave == kr % n_waves) {
-      const double rest = target - lane_value(rex, kr);
+    const double rest = target - lane_value(rex, kr);
+    if (!kVec && (kr == 0 || kr == kSeg - 1)) {  // an edge segment (positive sum): wave 0 walks its lanes
+      if (wave == 0) {
+        const bool mine = e >= 0 && (kr == 0) == (lane < s.head);
+        const double w = mine ? (double)ew : 0.0;
+        const double ex = wave_exclusive_scan(w, lane);
+        const uint64_t hit = __ballot(rhit && mine && ex + w > rest);
+        const uint64_t pos = __ballot(mine && w > 0.0);
+        const int l = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)pos);
+        const int32_t y = lane_value(c0 + e, l);
+        if (lane == 0) *token = y;
+      }
+    } else if (wave == (kr - kOff) % n_waves) {
+      const int r = kr - kOff;
       float w[E::kPerVec];
-      weights(kr * kWave + lane, w);  // the same weights as the row sum's
+      weights(r * kWave + lane, w);  // the same weights as the row sum's
       const float v = tree_sum(w);
       const double vex = wave_exclusive_scan((double)v, lane);
       const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
       const uint64_t vpos = __ballot(v > 0.0f);
       const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
-      const int32_t base = c0 + (kr * kWave + lane) * E::kPerVec;
+      const int32_t base = b0 + (r * kWave + lane) * E::kPerVec;
       int32_t yl = base + E::kPerVec - 1, last_pos = -1;
       double upto = vex;
       bool found = false;
@@ -3200,13 +3406,12 @@ __global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
   }
   if (step.action != kTreeDraw) return;  // uniform: every wave read the same shared value
 
-  // 3. the extra token (every wave picks the chunk; 16-byte aligned rows are searched by the whole
-  // workgroup, others by wave 0 alone) and the outputs (wave 0)
+  // 3. the extra token (every wave picks the chunk, the whole workgroup searches it) and the outputs
+  // (wave 0)
   const int32_t row = step.row;
   int32_t y = step.token;
   double S = 1.0;
   if constexpr (!kGreedy) {
-    if (!kVec && wave != 0) return;
     const char* tp = row_ptr<E>(P.target, trow0 + row, P.V);
     const bool chain = step.kind == SDV_TERM_RESIDUAL;  // R_l by the chunk masses of the last pass
     const float2* rec = rec_t + (int64_t)row * P.C;     // else the node's own p, by its records
@@ -3218,16 +3423,10 @@ __global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
                            &tgt, &S, lane);
     const int32_t s0 = cs * E::kChunk, n = min(E::kChunk, P.V - s0);
     __shared__ int32_t drawn;
-    if constexpr (kVec) {
-      y = chain ? tree_search_block<E, true>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn, lane,
-                                             wave, n_waves)
-                : tree_search_block<E, false>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn, lane,
-                                              wave, n_waves);
-    } else {
-      y = chain ? search_chunk<E>(s0, n, tgt, [&](int32_t v) { return chain_weight<E>(frame, tp, P.draft, P.V, v); },
-                                  lane)
-                : search_chunk<E>(s0, n, tgt, [&](int32_t v) { return fast_exp2(fmaf(E::at(tp, v), k2, -ref)); }, lane);
-    }
+    y = chain ? tree_search_block<E, true, kVec>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn,
+                                                 lane, wave, n_waves)
+              : tree_search_block<E, false, kVec>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn,
+                                                  lane, wave, n_waves);
     if (!chain) S *= exp2((double)ref - rows[row].l2);  // probability units
   }
   if (wave != 0) return;
@@ -3418,7 +3617,7 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   // verdict workgroups per request (the row pass zeroes their counters)
   P.split = kMode == kModeGreedy ? 1 : (P.split > 0 ? std::min(P.split, P.C) : verdict_split(P.B, P.C));
   record(0);
-  if constexpr (E::kBytes == 2 && kVec && kMode != kModeGreedy) {
+  if constexpr (E::kBytes == 2 && kMode != kModeGreedy) {
     if (!cut) P.hist = nullptr;
     if (P.hist) {
       hipLaunchKernelGGL((row_records<E, kMode, kVec, true>), row_grid(P.n_units, kRowWaves), dim3(kWave * kRowWaves),
@@ -3435,10 +3634,10 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   if (cut) {
     const int64_t rows = P.qrows ? P.n_t : (int64_t)P.n_t + P.n_d;
     if (P.hist) {  // rows the counts settle; the rest are left pending for row_cuts
-      hipLaunchKernelGGL(row_cuts_counted, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, P);
+      hipLaunchKernelGGL((row_cuts_counted<kVec>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, P);
       if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
     }
-    if constexpr (E::kBytes == 2 && kVec) {
+    if constexpr (E::kBytes == 2) {
       if (P.hist) {  // the rows the count kernel left pending
         hipLaunchKernelGGL((row_cuts<E, kVec, true>), dim3((unsigned)rows), dim3(kCutThreads), 0, stream, P);
       } else {

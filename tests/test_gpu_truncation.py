@@ -123,7 +123,8 @@ def _profiles(B, V, rng):
     return top_k, milli
 
 
-@pytest.mark.parametrize("dtype,V", [("bf16", 32000), ("fp32", 4099), ("bf16", 1000), ("bf16", 1001)])
+@pytest.mark.parametrize("dtype,V", [("bf16", 32000), ("fp32", 4099), ("bf16", 1000), ("bf16", 1001),
+                                     ("bf16", 20011)])
 def test_mixed_profiles_match_oracle(dtype, V):
     rng = np.random.default_rng(V)
     base = W.make_random(f"trunc_{dtype}_{V}", rng.integers(0, 9, size=64), V, dtype, 1.0, 3.0,
@@ -135,11 +136,13 @@ def test_mixed_profiles_match_oracle(dtype, V):
     check(b, top_k, milli)
 
 
-def test_ties_everywhere():
+@pytest.mark.parametrize("V", [20000, 20001])
+def test_ties_everywhere(V):
     """Logits rounded to a few values: every cut lands inside a group of equal logits, so the kept
-    copies are decided by token id (and the kernel's search for the last kept id is exercised)."""
+    copies are decided by token id (and the kernel's search for the last kept id is exercised), on
+    16-byte rows and on rows split at 16-byte boundaries."""
     rng = np.random.default_rng(41)
-    B, V = 48, 20000
+    B = 48
     depths = rng.integers(0, 6, size=B)
     cu = W.offsets_from_depths(depths)
     n_d = int(cu[-1])
