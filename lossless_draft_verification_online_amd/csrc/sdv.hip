@@ -517,69 +517,6 @@ __device__ __forceinline__ float p_weight(const M& m, float zt, int32_t v, float
   return fast_exp2(fmaf(m.t(zt, v) ? zt : -INFINITY, k2, -ref_t));
 }
 
-// Inverse CDF inside one chunk, element by element (rows that are not 16-byte aligned): the
-// smallest v in [c0, c0 + n) whose running mass exceeds target; weight(v) gives the weight of
-// element v.  Step 1: lane l sums the weights of its contiguous run [c0 + l*run, c0 + (l+1)*run); a
-// wave scan of the run totals (fp64) picks the run that crosses the target.  Step 2: each lane takes
-// run/64 consecutive elements of that run, and a second scan picks the element.  If rounding leaves
-// the target unreached, the last element of positive weight is taken.
-template <class E, class Weight>
-__device__ __forceinline__ int32_t search_chunk(int32_t c0, int32_t n, double target, Weight weight, int lane) {
-  constexpr int run = kVecPerLane * E::kPerVec;  // 128 bf16 or 64 fp32 elements
-  constexpr int per_lane = run / kWave;          // 2 or 1 elements per lane in step 2
-  const int32_t end = c0 + n;
-  // step 1: run totals
-  const int32_t b = c0 + lane * run;
-  double tot = 0.0;
-  for (int32_t v = b; v < min(b + run, end); ++v) tot += (double)weight(v);
-  const double before = wave_exclusive_scan(tot, lane);
-  const uint64_t hit = __ballot(b < end && before + tot > target);
-  const uint64_t pos = __ballot(b < end && tot > 0.0);
-  if (!hit && !pos) return end - 1;
-  // the run to open: the crossing run, or else the last run with positive mass
-  const int f = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)pos);
-  const double rest = target - lane_value(before, f);
-  // step 2: per_lane consecutive elements per lane inside run f
-  const int32_t bf = c0 + f * run;
-  float w[per_lane];
-  double sub = 0.0;
-#pragma unroll
-  for (int q = 0; q < per_lane; ++q) {
-    const int32_t v = bf + lane * per_lane + q;
-    w[q] = v < end ? weight(v) : 0.0f;
-    sub += (double)w[q];
-  }
-  const double sub_before = wave_exclusive_scan(sub, lane);
-  const uint64_t hit2 = __ballot(hit && sub_before + sub > rest);
-  const uint64_t pos2 = __ballot(sub > 0.0);
-  int32_t y = end - 1;
-  if (hit2) {
-    const int g = __ffsll((unsigned long long)hit2) - 1;
-    // the first element of lane g whose running mass exceeds rest (its last element if rounding
-    // leaves every partial sum short)
-    int32_t yl = bf + lane * per_lane + per_lane - 1;
-    double upto = sub_before;
-    bool found = false;
-#pragma unroll
-    for (int q = 0; q < per_lane; ++q) {
-      upto += (double)w[q];
-      if (!found && upto > rest) {
-        yl = bf + lane * per_lane + q;
-        found = true;
-      }
-    }
-    y = lane_value(yl, g);
-  } else if (pos2) {
-    const int h = 63 - __clzll((long long)pos2);
-    int32_t yl = -1;
-#pragma unroll
-    for (int q = 0; q < per_lane; ++q)
-      if (w[q] > 0.0f) yl = bf + lane * per_lane + q;
-    y = lane_value(yl, h);
-  }
-  return y;
-}
-
 // Masses m_c (fp64) of the chunks of one row; returns the chunk holding u * S and the target inside it.
 // mass(c) is evaluated by every lane for its chunks; chunks are visited in ascending order.
 template <class MassFn>
@@ -1377,6 +1314,242 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
     if (w[e] > 0.0f) last_pos = base + e;
     if (!found && upto > rest) {
       yl = base + e;
+      found = true;
+    }
+  }
+  if (!vhit) yl = last_pos >= 0 ? last_pos : yl;
+  return lane_value(yl, l);
+}
+
+// ---------------------------------------------------------------------------- q rows off the grid
+// A chunk [c0, c0 + n) of a (target row, q row) pair that is not on the 16-byte grid, split on the
+// q row's grid: q vector j (4 binary32 values) is aligned, and the 4 target logits under it (8
+// bytes of bf16, 16 of fp32) are cut from two aligned pieces of that size by one shift, the same
+// for the whole pair.  A quad whose target pieces would reach outside the target row joins the
+// head or the tail elements, which go one per lane (at most 7 on each side), so every load stays
+// inside its row.
+template <class E>
+struct QSplit {
+  typedef typename Quad<E>::T TQ;
+  int32_t head, body;  // elements before the first quad; quads
+  uint32_t shift;      // bytes from an aligned target piece to the logits under a quad
+  const f32x4* qv;     // q vector j
+  const TQ* tv;        // target pieces of quad j: tv[j] and (shift > 0) tv[j + 1]
+};
+template <class E>
+__device__ __forceinline__ QSplit<E> q_split(const char* tp, const float* qp, int32_t V, int32_t c0, int32_t n) {
+  typedef typename Quad<E>::T TQ;
+  constexpr uintptr_t kPiece = sizeof(TQ);  // the bytes of 4 target logits
+  QSplit<E> s;
+  const uintptr_t q0 = (uintptr_t)(qp + c0);
+  s.head = min(n, (int32_t)((((q0 + 15) & ~(uintptr_t)15) - q0) / 4));
+  s.body = (n - s.head) / 4;
+  const uintptr_t x = (uintptr_t)(tp + (int64_t)(c0 + s.head) * E::kBytes);
+  s.shift = (uint32_t)(x & (kPiece - 1));
+  uintptr_t al = x - s.shift;
+  if (s.body > 0 && al < (uintptr_t)tp) {  // the first low piece would start before the target row
+    s.head += 4;
+    s.body -= 1;
+    al += kPiece;
+  }
+  const uintptr_t t_end = (uintptr_t)(tp + (int64_t)V * E::kBytes);
+  if (s.body > 0 && s.shift != 0 && al + kPiece * (uintptr_t)s.body + kPiece > t_end) s.body -= 1;  // the last high piece
+  s.qv = reinterpret_cast<const f32x4*>(qp + c0 + s.head);
+  s.tv = reinterpret_cast<const TQ*>(al);
+  return s;
+}
+
+// The 4 target logits `shift` bytes into (lo, hi): 8-byte pieces of bf16 (shift 0, 2, 4 or 6) or
+// 16-byte pieces of fp32 (funnel16).
+__device__ __forceinline__ Quad<Bf16>::T funnel_quad(const Quad<Bf16>::T lo, const Quad<Bf16>::T hi, uint32_t shift) {
+  const bool one = (shift & 4) != 0;
+  const uint32_t bits = (shift & 3) * 8;
+  const uint32_t c0 = one ? lo.y : lo.x, c1 = one ? hi.x : lo.y, c2 = one ? hi.y : hi.x;
+  return Quad<Bf16>::T{__builtin_amdgcn_alignbit(c1, c0, bits), __builtin_amdgcn_alignbit(c2, c1, bits)};
+}
+__device__ __forceinline__ u32x4 funnel_quad(const u32x4 lo, const u32x4 hi, uint32_t shift) {
+  return funnel16(lo, hi, shift);
+}
+template <class E>
+__device__ __forceinline__ typename Quad<E>::T neg_inf_quad() {
+  typename Quad<E>::T t;
+#pragma unroll
+  for (int w = 0; w < (int)(sizeof(t) / 4); ++w) t[w] = E::kNegInfWord;
+  return t;
+}
+
+// Quad j of a split q pair (body >= 1): the target logits (-inf from j = body on, so the weight
+// is 0) and the q vector; indices are clamped into the body so that every load is unconditional.
+template <class E>
+__device__ __forceinline__ void load_q_quad(const QSplit<E>& s, int j, typename Quad<E>::T& t, f32x4& q) {
+  const int jc = min(j, s.body - 1);
+  q = s.qv[jc];
+  const typename Quad<E>::T lo = s.tv[jc];
+  const typename Quad<E>::T hi = s.tv[s.shift != 0 ? jc + 1 : jc];
+  t = funnel_quad(lo, hi, s.shift);
+  if (j >= s.body) t = neg_inf_quad<E>();
+}
+
+// Residual mass of one chunk of a (target row, q row) pair off the 16-byte grid, by one wave: the
+// edge elements load first, then the quads in stages of 4 per lane, the loads of the next stage
+// issued before the current one is reduced.
+template <class E, class M>
+__device__ __forceinline__ double resid_chunk_mass_q_split(const M& m, const char* tp, const float* qp, int32_t V,
+                                                           int32_t c0, int32_t n, float k2, float ref_t, float q_scale,
+                                                           int lane) {
+  typedef typename Quad<E>::T TQ;
+  const QSplit<E> s = q_split<E>(tp, qp, V, c0, n);
+  const int32_t e = split_edge(s, n, 4, lane);
+  float zt = -INFINITY, qe = 0.0f;
+  if (e >= 0) {
+    zt = E::at(tp, c0 + e);
+    qe = qp[c0 + e];
+  }
+  double acc = 0.0;
+  if (s.body > 0) {
+    constexpr int kQuadsPerLane = E::kChunk / 4 / kWave;  // 32 (bf16) or 16 (fp32)
+    constexpr int kPart = 4, kParts = kQuadsPerLane / kPart;
+    struct Stage {
+      TQ lo[kPart], hi[kPart];
+      f32x4 q[kPart];
+    };
+    auto load = [&](int h, Stage& st) {
+#pragma unroll
+      for (int k = 0; k < kPart; ++k) {
+        const int jc = min(lane + kWave * (h * kPart + k), s.body - 1);
+        st.q[k] = s.qv[jc];
+        st.lo[k] = s.tv[jc];
+        st.hi[k] = s.tv[s.shift != 0 ? jc + 1 : jc];
+      }
+    };
+    auto pin = [&](Stage& st) {  // the reduction of this stage stays below the loads just issued
+#pragma unroll
+      for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.lo[k]), "+v"(st.hi[k]), "+v"(st.q[k])::"memory");
+    };
+    auto reduce = [&](const Stage& st, int h) {
+      float w[4 * kPart];
+#pragma unroll
+      for (int k = 0; k < kPart; ++k) {
+        const int j = lane + kWave * (h * kPart + k);
+        float ft[4];
+        Quad<E>::unpack(j < s.body ? funnel_quad(st.lo[k], st.hi[k], s.shift) : neg_inf_quad<E>(), ft);
+        const int32_t v0 = c0 + s.head + 4 * j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[4 * k + q] = resid_weight_q(m, ft[q], st.q[k][q], v0 + q, k2, ref_t, q_scale);
+      }
+      return (double)tree_sum(w);
+    };
+    Stage A, B;
+    load(0, A);
+#pragma unroll
+    for (int h = 0; h < kParts; h += 2) {
+      load(h + 1, B);
+      pin(A);
+      acc += reduce(A, h);
+      if (h + 2 < kParts) load(h + 2, A);
+      pin(B);
+      acc += reduce(B, h + 1);
+    }
+  }
+  if (e >= 0) acc += (double)resid_weight_q(m, zt, qe, c0 + e, k2, ref_t, q_scale);
+  return wave_sum(acc);
+}
+
+// Inverse CDF inside one chunk of a (target row, q row) pair off the 16-byte grid by a whole
+// workgroup: the quads form rows of 64 (quad r*64 + l for lane l), wave w sums rows w,
+// w + n_waves, ..., and the head's and tail's elements are two more segments before and after
+// them, weighed and walked by wave 0 as in search_chunk_split.  Returns the token in the wave that
+// resolves it, -1 in the others.  row_sums holds at least 34 doubles.
+template <class E, class M>
+__device__ __forceinline__ int32_t search_chunk_q_split(const M& m, const char* trow, const float* qrow, int32_t V,
+                                                        int32_t c0, int32_t n, double target, float k2, float ref_t,
+                                                        float q_scale, double* row_sums, int lane, int wave,
+                                                        int n_waves) {
+  typedef typename Quad<E>::T TQ;
+  constexpr int kRows = E::kChunk / 4 / kWave;  // rows of 64 quads: 32 (bf16) or 16 (fp32)
+  constexpr int kPer = kRows / kVerdictWaves;
+  constexpr int kSeg = kRows + 2;  // the head, the rows, the tail
+  static_assert(kRows % kVerdictWaves == 0 && kSeg <= kWave, "whole rows per wave, one scan of the segments");
+  const QSplit<E> s = q_split<E>(trow, qrow, V, c0, n);
+  const int32_t b0 = c0 + s.head;
+  auto weights = [&](const TQ& t, const f32x4& q, int32_t v0, float (&w)[4]) {
+    float ft[4];
+    Quad<E>::unpack(t, ft);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = resid_weight_q(m, ft[e], q[e], v0 + e, k2, ref_t, q_scale);
+  };
+  TQ t[kPer];
+  f32x4 q[kPer];
+  float vs[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    t[j] = neg_inf_quad<E>();
+    q[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (s.body > 0) load_q_quad<E>(s, (wave + j * n_waves) * kWave + lane, t[j], q[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    float w[4];
+    weights(t[j], q[j], b0 + 4 * ((wave + j * n_waves) * kWave + lane), w);
+    vs[j] = (w[0] + w[1]) + (w[2] + w[3]);
+    const double rs = wave_sum((double)vs[j]);
+    if (lane == 0) row_sums[1 + wave + j * n_waves] = rs;
+  }
+  const int32_t e = split_edge(s, n, 4, lane);
+  float ew = 0.0f;
+  if (wave == 0) {
+    if (e >= 0) ew = resid_weight_q(m, E::at(trow, c0 + e), qrow[c0 + e], c0 + e, k2, ref_t, q_scale);
+    const double hs = wave_sum(lane < s.head ? (double)ew : 0.0);
+    const double ts = wave_sum(lane < s.head ? 0.0 : (double)ew);
+    if (lane == 0) {
+      row_sums[0] = hs;
+      row_sums[kSeg - 1] = ts;
+    }
+  }
+  __syncthreads();
+  const double rsum = lane < kSeg ? row_sums[lane] : 0.0;
+  const double rex = wave_exclusive_scan(rsum, lane);
+  const uint64_t rhit = __ballot(lane < kSeg && rex + rsum > target);
+  const uint64_t rpos = __ballot(lane < kSeg && rsum > 0.0);
+  if (!rhit && !rpos) return wave == 0 ? c0 + n - 1 : -1;
+  const int kr = rhit ? __ffsll((unsigned long long)rhit) - 1 : 63 - __clzll((long long)rpos);
+  const double rest = target - lane_value(rex, kr);
+  if (kr == 0 || kr == kSeg - 1) {  // an edge segment (positive sum): wave 0 walks its lanes in order
+    if (wave != 0) return -1;
+    const bool mine = e >= 0 && (kr == 0) == (lane < s.head);
+    const double w = mine ? (double)ew : 0.0;
+    const double ex = wave_exclusive_scan(w, lane);
+    const uint64_t hit = __ballot(rhit && mine && ex + w > rest);
+    const uint64_t pos = __ballot(mine && w > 0.0);
+    const int l = hit ? __ffsll((unsigned long long)hit) - 1 : 63 - __clzll((long long)pos);
+    return lane_value(c0 + e, l);
+  }
+  const int row = kr - 1;
+  if (wave != row % n_waves) return -1;
+  const int j = row / n_waves;
+  float v = vs[0];  // j is uniform: selects, not an indexed register array
+#pragma unroll
+  for (int jj = 1; jj < kPer; ++jj)
+    if (jj == j) v = vs[jj];
+  const double vex = wave_exclusive_scan((double)v, lane);
+  const uint64_t vhit = __ballot(rhit && vex + (double)v > rest);
+  const uint64_t vpos = __ballot(v > 0.0f);
+  const int l = vhit ? __ffsll((unsigned long long)vhit) - 1 : (vpos ? 63 - __clzll((long long)vpos) : 63);
+  const int32_t base = b0 + 4 * (row * kWave + lane);
+  float w[4];
+#pragma unroll
+  for (int jj = 0; jj < kPer; ++jj)
+    if (jj == j) weights(t[jj], q[jj], base, w);
+  int32_t yl = base + 3;
+  int32_t last_pos = -1;
+  double upto = vex;
+  bool found = false;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    upto += (double)w[e2];
+    if (w[e2] > 0.0f) last_pos = base + e2;
+    if (!found && upto > rest) {
+      yl = base + e2;
       found = true;
     }
   }
@@ -2738,11 +2911,9 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
                         lds_mass + c_lo, lane, wave, n_waves);
     } else {
       for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
-        const int32_t c0 = c * E::kChunk, c1 = min(c0 + E::kChunk, P.V);
-        double cm = 0.0;
-        for (int32_t v = c0 + lane; v < c1; v += kWave)
-          cm += (double)resid_weight_q(m, E::at(tp, v), qp[v], v, k2, d.ref_t, d.q_scale);
-        cm = wave_sum(cm);
+        const int32_t c0 = c * E::kChunk;
+        const double cm = resid_chunk_mass_q_split<E>(m, tp, qp, P.V, c0, min(E::kChunk, P.V - c0), k2, d.ref_t,
+                                                      d.q_scale, lane);
         if (lane == 0) lds_mass[c] = cm;
       }
     }
@@ -2856,10 +3027,8 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
                                        wave, n_waves);
   } else {
     if (residual && kQ) {
-      if (wave != 0) return;
-      const float ref_t = d.ref_t, q_scale = d.q_scale;
-      y = search_chunk<E>(
-          s0, n, tgt, [&](int32_t v) { return resid_weight_q(m, E::at(tp, v), qp[v], v, k2, ref_t, q_scale); }, lane);
+      y = search_chunk_q_split<E>(m, tp, qp, P.V, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave,
+                                  n_waves);
     } else if (residual) {
       y = search_chunk_split<E, true>(m, tp, dp, P.V, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
                                       wave, n_waves);

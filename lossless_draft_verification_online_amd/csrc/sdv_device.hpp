@@ -247,10 +247,14 @@ __device__ __forceinline__ double lane_value(double v, int src) {
   return __longlong_as_double((long long)lane_value((uint64_t)__double_as_longlong(v), src));
 }
 
-// Sum of the eight (or four) elements of one vector as a balanced tree.
+// Sum of 4, 8 or 16 values as a balanced tree.
 template <int N>
 __device__ __forceinline__ float tree_sum(const float (&f)[N]) {
-  if constexpr (N == 8) {
+  static_assert(N == 4 || N == 8 || N == 16, "pairwise sums of 4, 8 or 16 values");
+  if constexpr (N == 16) {
+    return (((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]))) +
+           (((f[8] + f[9]) + (f[10] + f[11])) + ((f[12] + f[13]) + (f[14] + f[15])));
+  } else if constexpr (N == 8) {
     return ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
   } else {
     return (f[0] + f[1]) + (f[2] + f[3]);
