@@ -24,6 +24,11 @@
 //                request walks its tree in wave 0, and the whole workgroup computes the residual
 //                masses after each rejected child.
 //
+// Rows that are not 16-byte aligned (an odd vocabulary, a base on an element boundary) take the
+// same 16-byte loads: each chunk is split at 16-byte boundaries, the few elements before the first
+// vector and after the last go one per lane, and a second row of a pair is realigned to the first
+// by one shift (section "rows off the 16-byte grid").
+//
 // The kernel boundary orders the stream before the verdicts.  Inside a kernel only the verdict
 // workgroups of one request hand anything over: a correction's chunk masses, through the
 // workspace, behind a device-scope fence and a counter; no workgroup ever waits for another.  No
