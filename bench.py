@@ -41,7 +41,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B=256, V=128256"
 KERNEL_SOURCES = ["lossless_draft_verification_online_amd/csrc/sdv.hip",
-                  "lossless_draft_verification_online_amd/csrc/sdv_device.hpp"]
+                  "lossless_draft_verification_online_amd/csrc/sdv_device.hpp",
+                  "lossless_draft_verification_online_amd/csrc/split.hpp"]
 KERNELS = ["row_records", "verdicts"]
 TRUNCATION_KERNELS = ["row_records", "cuts", "verdicts"]  # "cuts": row_cuts_counted, then row_cuts
 TRACE_KERNELS = ["row_records", "row_cuts_counted", "row_cuts", "tree_verdicts", "verdicts", "read_reg_kernel", "read_lds_kernel",

@@ -8,7 +8,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", "sdv.hip"), os.path.join(PKG, "csrc", "commit.hip"),
            os.path.join(PKG, "csrc", "sdcp_uniforms.cpp")]
-DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "sdv_device.hpp"), os.path.join(ROOT, "include", "sdv.h")]
+DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "sdv_device.hpp"), os.path.join(PKG, "csrc", "split.hpp"),
+                     os.path.join(ROOT, "include", "sdv.h")]
 LIBRARY = os.path.join(PKG, "libsdv.so")
 
 HIPCC_FLAGS = [

@@ -44,6 +44,7 @@
 
 #include "../../include/sdv.h"
 #include "sdv_device.hpp"
+#include "split.hpp"
 
 namespace sdv {
 
@@ -367,16 +368,14 @@ struct SplitEdge {
 template <class E>
 __device__ __forceinline__ SplitEdge load_split_chunk(const char* rp, int32_t c0, int32_t n, int lane,
                                                       u32x4 (&buf)[kVecPerLane]) {
-  const uintptr_t b0 = (uintptr_t)(rp + (int64_t)c0 * E::kBytes);
-  const int32_t head = min(n, (int32_t)((((b0 + 15) & ~(uintptr_t)15) - b0) / E::kBytes));
-  const int32_t body = (n - head) / E::kPerVec * E::kPerVec;
-  load_chunk<E>(rp, c0 + head, body, lane, buf);
-  const int32_t e = lane < head ? lane : head + body + (lane - head);
+  const split::Plan p = split::row((uintptr_t)rp, E::kBytes, c0, n);
+  load_chunk<E>(rp, c0 + p.head, p.body * E::kPerVec, lane, buf);
+  const int32_t e = split::edge(p.head, p.body * E::kPerVec, n, lane);
   SplitEdge s;
-  s.head = head;
-  s.body = body / E::kPerVec;
-  s.ok = e < n;
-  s.v = c0 + e;
+  s.head = p.head;
+  s.body = p.body;
+  s.ok = e >= 0;
+  s.v = c0 + (s.ok ? e : 0);
   s.z = s.ok ? E::at(rp, s.v) : -INFINITY;
   return s;
 }
@@ -856,6 +855,12 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
 }
 
 // ---------------------------------------------------------------------------- rows off the 16-byte grid
+// A plan's address as an offset from the row pointer it came from, so that the compiler still
+// knows the loads through it read global memory.
+__device__ __forceinline__ const char* at_address(const char* base, uintptr_t a) {
+  return base + (intptr_t)(a - (uintptr_t)base);
+}
+
 // A chunk [c0, c0 + n) of a row pair whose rows are only element-aligned, split on the target row's
 // 16-byte grid: `body` vectors from element c0 + head on are aligned in the target row, and the
 // draft bytes under vector j are the 16 bytes `shift` past the aligned draft vector dv[j] (one shift
@@ -872,23 +877,9 @@ struct PairSplit {
 };
 template <class E>
 __device__ __forceinline__ PairSplit pair_split(const char* tp, const char* dp, int32_t V, int32_t c0, int32_t n) {
-  PairSplit s;
-  const uintptr_t t0 = (uintptr_t)(tp + (int64_t)c0 * E::kBytes);
-  s.head = min(n, (int32_t)((((t0 + 15) & ~(uintptr_t)15) - t0) / E::kBytes));
-  s.body = (n - s.head) / E::kPerVec;
-  const uintptr_t x = (uintptr_t)(dp + (int64_t)(c0 + s.head) * E::kBytes);
-  s.shift = (uint32_t)(x & 15);
-  uintptr_t dal = x - s.shift;
-  if (s.body > 0 && dal < (uintptr_t)dp) {  // the first low piece would start before the draft row
-    s.head += E::kPerVec;
-    s.body -= 1;
-    dal += 16;
-  }
-  const uintptr_t d_end = (uintptr_t)(dp + (int64_t)V * E::kBytes);
-  if (s.body > 0 && s.shift != 0 && dal + 16 * (uintptr_t)s.body + 16 > d_end) s.body -= 1;  // the last high piece
-  s.tv = reinterpret_cast<const u32x4*>(tp + (int64_t)(c0 + s.head) * E::kBytes);
-  s.dv = reinterpret_cast<const u32x4*>(dal);
-  return s;
+  const split::Plan p = split::pair((uintptr_t)tp, (uintptr_t)dp, E::kBytes, V, c0, n);
+  return PairSplit{p.head, p.body, p.shift, reinterpret_cast<const u32x4*>(at_address(tp, p.first)),
+                   reinterpret_cast<const u32x4*>(p.pieces)};
 }
 
 // The 16 bytes `shift` bytes into (lo, hi); shift is a multiple of 2 and the same in every lane, so
@@ -923,8 +914,7 @@ __device__ __forceinline__ void load_split_pair(const PairSplit& s, int j, u32x4
 // tail), or -1.
 template <class Split>
 __device__ __forceinline__ int32_t split_edge(const Split& s, int32_t n, int per_vec, int lane) {
-  const int32_t e = lane < s.head ? lane : s.head + s.body * per_vec + (lane - s.head);
-  return e < n ? e : -1;
+  return split::edge(s.head, s.body * per_vec, n, lane);
 }
 
 // Residual mass of one chunk of a rejected row pair off the 16-byte grid, by one wave.  The edge
@@ -1343,25 +1333,9 @@ struct QSplit {
 };
 template <class E>
 __device__ __forceinline__ QSplit<E> q_split(const char* tp, const float* qp, int32_t V, int32_t c0, int32_t n) {
-  typedef typename Quad<E>::T TQ;
-  constexpr uintptr_t kPiece = sizeof(TQ);  // the bytes of 4 target logits
-  QSplit<E> s;
-  const uintptr_t q0 = (uintptr_t)(qp + c0);
-  s.head = min(n, (int32_t)((((q0 + 15) & ~(uintptr_t)15) - q0) / 4));
-  s.body = (n - s.head) / 4;
-  const uintptr_t x = (uintptr_t)(tp + (int64_t)(c0 + s.head) * E::kBytes);
-  s.shift = (uint32_t)(x & (kPiece - 1));
-  uintptr_t al = x - s.shift;
-  if (s.body > 0 && al < (uintptr_t)tp) {  // the first low piece would start before the target row
-    s.head += 4;
-    s.body -= 1;
-    al += kPiece;
-  }
-  const uintptr_t t_end = (uintptr_t)(tp + (int64_t)V * E::kBytes);
-  if (s.body > 0 && s.shift != 0 && al + kPiece * (uintptr_t)s.body + kPiece > t_end) s.body -= 1;  // the last high piece
-  s.qv = reinterpret_cast<const f32x4*>(qp + c0 + s.head);
-  s.tv = reinterpret_cast<const TQ*>(al);
-  return s;
+  const split::Plan p = split::q((uintptr_t)tp, (uintptr_t)qp, E::kBytes, V, c0, n);
+  return QSplit<E>{p.head, p.body, p.shift, reinterpret_cast<const f32x4*>(qp + c0 + p.head),
+                   reinterpret_cast<const typename Quad<E>::T*>(p.pieces)};
 }
 
 // The 4 target logits `shift` bytes into (lo, hi): 8-byte pieces of bf16 (shift 0, 2, 4 or 6) or
@@ -1431,18 +1405,19 @@ __device__ __forceinline__ double resid_chunk_mass_q_split(const M& m, const cha
 #pragma unroll
       for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.lo[k]), "+v"(st.hi[k]), "+v"(st.q[k])::"memory");
     };
-    auto reduce = [&](const Stage& st, int h) {
-      float w[4 * kPart];
+    auto reduce = [&](const Stage& st, int h) {  // quad by quad: few weights live at once
+      float part = 0.0f;
 #pragma unroll
       for (int k = 0; k < kPart; ++k) {
         const int j = lane + kWave * (h * kPart + k);
-        float ft[4];
+        float ft[4], w[4];
         Quad<E>::unpack(j < s.body ? funnel_quad(st.lo[k], st.hi[k], s.shift) : neg_inf_quad<E>(), ft);
         const int32_t v0 = c0 + s.head + 4 * j;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[4 * k + q] = resid_weight_q(m, ft[q], st.q[k][q], v0 + q, k2, ref_t, q_scale);
+        for (int q = 0; q < 4; ++q) w[q] = resid_weight_q(m, ft[q], st.q[k][q], v0 + q, k2, ref_t, q_scale);
+        part += tree_sum(w);
       }
-      return (double)tree_sum(w);
+      return (double)part;
     };
     Stage A, B;
     load(0, A);
@@ -1784,10 +1759,7 @@ __device__ __forceinline__ void for_each_logit(const char* rp, int32_t V, F f) {
     }
   };
   int32_t head = 0;  // elements before the first 16-byte boundary
-  if constexpr (!kVec) {
-    const uintptr_t r0 = (uintptr_t)rp;
-    head = min(V, (int32_t)((((r0 + 15) & ~(uintptr_t)15) - r0) / E::kBytes));
-  }
+  if constexpr (!kVec) head = split::to_boundary((uintptr_t)rp, E::kBytes, V);
   const u32x4* vp = reinterpret_cast<const u32x4*>(rp + (int64_t)head * E::kBytes);
   constexpr int32_t kVecPerChunk = E::kChunk / E::kPerVec;
   const int32_t nvec = (V - head) / E::kPerVec, C_full = nvec / kVecPerChunk;
@@ -3117,26 +3089,17 @@ struct TreeSplit {
 };
 template <class E>
 __device__ __forceinline__ TreeSplit tree_split(const char* tp, int32_t V, int32_t c0, int32_t n) {
-  TreeSplit s;
-  const uintptr_t t0 = (uintptr_t)(tp + (int64_t)c0 * E::kBytes);
-  s.head = min(n, (int32_t)((((t0 + 15) & ~(uintptr_t)15) - t0) / E::kBytes));
-  s.body = (n - s.head) / E::kPerVec;
-  if (s.body > 0 && (int64_t)(c0 + s.head) * E::kBytes < 16) {
-    s.head += E::kPerVec;
-    s.body -= 1;
-  }
-  if (s.body > 0 && (int64_t)(c0 + s.head + s.body * E::kPerVec) * E::kBytes + 16 > (int64_t)V * E::kBytes)
-    s.body -= 1;
-  s.tv = reinterpret_cast<const u32x4*>(tp + (int64_t)(c0 + s.head) * E::kBytes);
-  return s;
+  const split::Plan p = split::tree((uintptr_t)tp, E::kBytes, V, c0, n);
+  return TreeSplit{p.head, p.body, reinterpret_cast<const u32x4*>(at_address(tp, p.first))};
 }
 
 // The bytes of draft row dp under body vector jc of a tree split (0 <= jc < body).
 template <class E>
 __device__ __forceinline__ u32x4 tree_draft_vec(const char* dp, int32_t c0, const TreeSplit& s, int jc) {
-  const uintptr_t x = (uintptr_t)(dp + (int64_t)(c0 + s.head) * E::kBytes);
-  const uint32_t shift = (uint32_t)(x & 15);
-  const u32x4* dv = reinterpret_cast<const u32x4*>(x - shift);
+  uintptr_t pieces;
+  uint32_t shift;
+  split::tree_pieces(split::Plan{s.head, s.body, 0u, 0, 0}, (uintptr_t)dp, E::kBytes, c0, &pieces, &shift);
+  const u32x4* dv = reinterpret_cast<const u32x4*>(at_address(dp, pieces));
   return funnel16(dv[jc], dv[shift != 0 ? jc + 1 : jc], shift);
 }
 
