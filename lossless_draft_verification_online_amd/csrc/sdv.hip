@@ -1128,109 +1128,6 @@ struct Quad<F32> {
   }
 };
 
-// Residual chunk masses of a (target row, q row) pair by the waves of one workgroup (16-byte
-// aligned rows).  Wave w takes full chunks w, w + n_waves, ... in quarters of 4-element quads
-// (quad l + 64 k for lane l): the loads of the next quarter are issued before the current one is
-// reduced.  The partial last chunk, if any, is summed element by element by the wave that owns it.
-// q loads are non-temporal; target loads are plain, since non-temporal ones here slow the row pass
-// of the next call.
-template <class E, class M>
-__device__ __forceinline__ void resid_masses_q(const M& m, const char* tp, const float* qp, int32_t V, int32_t C,
-                                               float k2, float ref_t, float q_scale, double* lds_mass, int lane,
-                                               int wave, int n_waves) {
-  typedef typename Quad<E>::T TQ;
-  constexpr int kParts = 4;                               // stages per chunk
-  constexpr int kQuadsPerLane = E::kChunk / 4 / kWave;    // 32 (bf16) or 16 (fp32)
-  constexpr int kPart = kQuadsPerLane / kParts;           // quads per lane in one stage
-  struct Stage {
-    TQ t[kPart];
-    f32x4 q[kPart];
-  };
-  const int32_t C_full = V / E::kChunk;
-  auto chunk_of = [&](int32_t s) { return wave + (s / kParts) * n_waves; };
-  auto load = [&](int32_t s, Stage& st) {
-    const int32_t c0 = chunk_of(s) * E::kChunk;
-    const int h = s % kParts;
-    const TQ* tv = reinterpret_cast<const TQ*>(tp + (int64_t)c0 * E::kBytes);
-    const f32x4* qv = reinterpret_cast<const f32x4*>(qp + c0);
-#pragma unroll
-    for (int k = 0; k < kPart; ++k) {
-      const int u = lane + kWave * (h * kPart + k);
-      st.t[k] = tv[u];
-      st.q[k] = __builtin_nontemporal_load(qv + u);  // q rows never enter the row pass
-    }
-  };
-  auto reduce = [&](const Stage& st, int32_t s) {
-    const int32_t c0 = chunk_of(s) * E::kChunk;
-    const int h = s % kParts;
-    double acc = 0.0;
-#pragma unroll
-    for (int k = 0; k < kPart; k += 2) {
-      float ft[8], w[8];
-      Quad<E>::unpack(st.t[k], reinterpret_cast<float(&)[4]>(ft[0]));
-      Quad<E>::unpack(st.t[k + 1], reinterpret_cast<float(&)[4]>(ft[4]));
-      const int32_t v0 = c0 + 4 * (lane + kWave * (h * kPart + k)), v1 = v0 + 4 * kWave;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[e] = resid_weight_q(m, ft[e], st.q[k][e], v0 + e, k2, ref_t, q_scale);
-        w[4 + e] = resid_weight_q(m, ft[4 + e], st.q[k + 1][e], v1 + e, k2, ref_t, q_scale);
-      }
-      acc += (double)tree_sum(w);
-    }
-    return acc;
-  };
-  const int32_t n_mine = C_full > wave ? (C_full - wave + n_waves - 1) / n_waves : 0;
-  const int32_t steps = kParts * n_mine;  // even: steps come in pairs
-  Stage A, Bs;
-  double acc = 0.0;
-  // the loads just issued come before the reduction of the stage held: its registers pass through
-  // an empty asm placed after them, so the reduction cannot be scheduled above those loads
-  auto pin = [&](Stage& st) {
-#pragma unroll
-    for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.t[k]), "+v"(st.q[k])::"memory");
-  };
-  auto finish_chunk = [&](int32_t s) {  // after stage s: the chunk is complete when s ends a chunk
-    if ((s + 1) % kParts == 0) {
-      acc = wave_sum(acc);
-      if (lane == 0) lds_mass[chunk_of(s)] = acc;
-      acc = 0.0;
-    }
-  };
-  if (steps > 0) {
-    load(0, A);
-    // steady state: every load is unconditional (a load under a branch would leave the load counter
-    // unknown at the join and force a wait for every load in flight); the last pair is peeled off
-    int32_t s = 0;
-    for (; s + 2 < steps; s += 2) {
-      load(s + 1, Bs);
-      pin(A);  // the next stage is in flight while this one is reduced
-      acc += reduce(A, s);
-      asm volatile("" : "+v"(acc)::"memory");
-      finish_chunk(s);
-      load(s + 2, A);
-      pin(Bs);
-      acc += reduce(Bs, s + 1);
-      asm volatile("" : "+v"(acc)::"memory");
-      finish_chunk(s + 1);
-    }
-    load(s + 1, Bs);
-    pin(A);
-    acc += reduce(A, s);
-    asm volatile("" : "+v"(acc)::"memory");
-    finish_chunk(s);
-    acc += reduce(Bs, s + 1);
-    asm volatile("" : "+v"(acc)::"memory");
-    finish_chunk(s + 1);
-  }
-  if (C_full < C && C_full % n_waves == wave) {  // the partial last chunk
-    const int32_t c0 = C_full * E::kChunk;
-    double cm = 0.0;
-    for (int32_t v = c0 + lane; v < V; v += kWave) cm += (double)resid_weight_q(m, E::at(tp, v), qp[v], v, k2, ref_t, q_scale);
-    cm = wave_sum(cm);
-    if (lane == 0) lds_mass[C_full] = cm;
-  }
-}
-
 // Inverse CDF inside one chunk of a (target row, q row) pair by a whole workgroup (16-byte aligned
 // rows), laid out as the logit version: rows of 64 vectors, wave w sums rows w and w + n_waves, a
 // scan of the row sums picks the row, the owning wave scans its vector sums and walks the vector.
@@ -1369,10 +1266,10 @@ __device__ __forceinline__ void load_q_quad(const QSplit<E>& s, int j, typename 
   if (j >= s.body) t = neg_inf_quad<E>();
 }
 
-// Residual mass of one chunk of a (target row, q row) pair off the 16-byte grid, by one wave: the
-// edge elements load first, then the quads in stages of 4 per lane, the loads of the next stage
-// issued before the current one is reduced.
-template <class E, class M>
+// Residual mass of one chunk of a (target row, q row) pair, by one wave: the edge elements load
+// first, then the quads in stages of 4 per lane, the loads of the next stage issued before the
+// current one is reduced.  kVec: 16-byte aligned rows (no edges, no shift: one target piece per quad).
+template <class E, bool kVec, class M>
 __device__ __forceinline__ double resid_chunk_mass_q_split(const M& m, const char* tp, const float* qp, int32_t V,
                                                            int32_t c0, int32_t n, float k2, float ref_t, float q_scale,
                                                            int lane) {
@@ -1398,12 +1295,15 @@ __device__ __forceinline__ double resid_chunk_mass_q_split(const M& m, const cha
         const int jc = min(lane + kWave * (h * kPart + k), s.body - 1);
         st.q[k] = s.qv[jc];
         st.lo[k] = s.tv[jc];
-        st.hi[k] = s.tv[s.shift != 0 ? jc + 1 : jc];
+        if constexpr (!kVec) st.hi[k] = s.tv[s.shift != 0 ? jc + 1 : jc];
       }
     };
     auto pin = [&](Stage& st) {  // the reduction of this stage stays below the loads just issued
 #pragma unroll
-      for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.lo[k]), "+v"(st.hi[k]), "+v"(st.q[k])::"memory");
+      for (int k = 0; k < kPart; ++k) {
+        if constexpr (kVec) asm volatile("" : "+v"(st.lo[k]), "+v"(st.q[k])::"memory");
+        else asm volatile("" : "+v"(st.lo[k]), "+v"(st.hi[k]), "+v"(st.q[k])::"memory");
+      }
     };
     auto reduce = [&](const Stage& st, int h) {  // quad by quad: few weights live at once
       float part = 0.0f;
@@ -1411,7 +1311,8 @@ __device__ __forceinline__ double resid_chunk_mass_q_split(const M& m, const cha
       for (int k = 0; k < kPart; ++k) {
         const int j = lane + kWave * (h * kPart + k);
         float ft[4], w[4];
-        Quad<E>::unpack(j < s.body ? funnel_quad(st.lo[k], st.hi[k], s.shift) : neg_inf_quad<E>(), ft);
+        const TQ t = kVec ? st.lo[k] : funnel_quad(st.lo[k], st.hi[k], s.shift);
+        Quad<E>::unpack(j < s.body ? t : neg_inf_quad<E>(), ft);
         const int32_t v0 = c0 + s.head + 4 * j;
 #pragma unroll
         for (int q = 0; q < 4; ++q) w[q] = resid_weight_q(m, ft[q], st.q[k][q], v0 + q, k2, ref_t, q_scale);
@@ -2883,16 +2784,11 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     m_r.cd.vcut -= v_lo;
   }
   if (residual && kQ) {
-    if constexpr (kVec) {
-      resid_masses_q<E>(m_r, tp + (int64_t)v_lo * E::kBytes, qp + v_lo, V_r, c_hi - c_lo, k2, d.ref_t, d.q_scale,
-                        lds_mass + c_lo, lane, wave, n_waves);
-    } else {
-      for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
-        const int32_t c0 = c * E::kChunk;
-        const double cm = resid_chunk_mass_q_split<E>(m, tp, qp, P.V, c0, min(E::kChunk, P.V - c0), k2, d.ref_t,
-                                                      d.q_scale, lane);
-        if (lane == 0) lds_mass[c] = cm;
-      }
+    for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
+      const int32_t c0 = c * E::kChunk;
+      const double cm = resid_chunk_mass_q_split<E, kVec>(m, tp, qp, P.V, c0, min(E::kChunk, P.V - c0), k2, d.ref_t,
+                                                          d.q_scale, lane);
+      if (lane == 0) lds_mass[c] = cm;
     }
     __syncthreads();
   } else if (residual && !one_chunk && !few_chunks) {
