@@ -27,6 +27,21 @@ def to_device(a: np.ndarray | None, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def to_device_off_grid(a: np.ndarray | None, dtype: str, shift: int):
+    """a on the device, `shift` elements into a fresh buffer (shift > 0: its base sits on an element
+    boundary only, off the 16-byte grid)."""
+    if a is None:
+        return None
+    t = to_device(a, dtype)
+    if shift == 0:
+        return t
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
+    view = flat[shift:shift + t.numel()].view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 != 0
+    return view
+
+
 def upload(b):
     return (to_device(b.target, b.dtype), to_device(b.draft, b.dtype),
             torch.from_numpy(b.tokens).to(DEV), torch.from_numpy(b.cu).to(DEV))

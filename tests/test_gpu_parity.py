@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import DEV, check_parity, log, run_gpu, run_oracle, to_device
+from gpu_helpers import DEV, check_parity, log, run_gpu, run_oracle, to_device, to_device_off_grid
 
 pytestmark = pytest.mark.gpu
 
@@ -83,18 +83,6 @@ def test_row_argmax_exact_with_ties(V):
     np.testing.assert_array_equal(dg["target_argmax"], np.argmax(W.bf16_to_f32(b.target), axis=1))
 
 
-def _off_grid(a, dtype, shift):
-    """a on the device, `shift` elements into a fresh buffer: its rows sit on element boundaries only."""
-    if a is None:
-        return None
-    t = to_device(a, dtype)
-    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=DEV)
-    view = flat[shift:shift + t.numel()].view(t.shape)
-    view.copy_(t)
-    assert view.data_ptr() % 16 != 0
-    return view
-
-
 @pytest.mark.parametrize("V,dtype,T,shift", [(8192, "bf16", 1.0, 3), (8192, "bf16", 0.0, 5), (4096, "fp32", 0.8, 1),
                                              (20011, "bf16", 1.0, 7), (20011, "bf16", 0.0, 1), (4099, "fp32", 0.0, 2),
                                              (9, "bf16", 0.0, 3)])
@@ -121,7 +109,7 @@ def test_rows_off_the_16_byte_grid(V, dtype, T, shift):
         else:
             tv[r, [V // 2, V - 1]] = top        # a vector element tied with a tail element
     b.target = back(tv)
-    dev = (_off_grid(b.target, dtype, shift), _off_grid(b.draft, dtype, shift), torch.from_numpy(b.tokens).to(DEV),
+    dev = (to_device_off_grid(b.target, dtype, shift), to_device_off_grid(b.draft, dtype, shift), torch.from_numpy(b.tokens).to(DEV),
            torch.from_numpy(b.cu).to(DEV))
     diag = ("target_argmax",) if T == 0.0 else ("target_lse", "draft_lse", "terminal_kind")
     _, _, ref, _, dg = check_parity(b, dev_inputs=dev, diag=diag)

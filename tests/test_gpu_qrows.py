@@ -6,7 +6,9 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_helpers import check_parity, log, run_gpu, run_oracle
+import lossless_draft_verification_online_amd as sdv
+from gpu_helpers import DEV, check_parity, log, run_gpu, run_oracle, to_device_off_grid
+from oracle.compare import compare_verdicts
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +29,27 @@ def test_qrows_match_oracle(V, dtype, T):
     np.testing.assert_allclose(dg["ratio"], ref["ratio"], rtol=1e-5)
     np.testing.assert_allclose(np.exp(dg["target_lse"] - ref["target_lse"]), 1.0, rtol=1e-5)
     log(f"  {cmp['n_excused']} near-tie excuses, {(ref['terminal_kind'] == 2).sum()} corrections")
+
+
+@pytest.mark.parametrize("V,dtype,tshift,qshift", [(4096, "fp32", 0, 1), (8192, "bf16", 0, 3), (8192, "bf16", 5, 2),
+                                                   (20011, "bf16", 3, 1), (1003, "fp32", 2, 0)])
+def test_qrows_off_the_16_byte_grid(V, dtype, tshift, qshift):
+    """Target logits and q rows at bases off the 16-byte grid (shifted by whole elements): the pass
+    splits each pair on the q row's grid and cuts the target logits under every q vector from two
+    aligned pieces; verdicts against the oracle on the same rows."""
+    rng = np.random.default_rng(V + 10 * tshift + qshift)
+    b = W.with_qrows(W.make_random(f"q_off_v{V}_{tshift}_{qshift}", rng.integers(0, 9, size=32), V, dtype, 1.0, 3.0,
+                                   1.5, data_seed=V + 7, verify_seed=9))
+    log(f"  q rows off the grid: V={V} {dtype} target shift {tshift}, q shift {qshift}")
+    t = to_device_off_grid(b.target, dtype, tshift)
+    q = to_device_off_grid(b.qrows, "fp32", qshift)
+    acc, out, dg = sdv.verify_ex(t, None, torch.from_numpy(b.tokens).to(DEV), torch.from_numpy(b.cu).to(DEV),
+                                 b.temperature, b.seed, draft_probs=q, diag=("terminal_kind",))
+    torch.cuda.synchronize()
+    ref = run_oracle(b)
+    cmp = compare_verdicts(acc.cpu().numpy(), out.cpu().numpy(), ref, b.cu, b.temperature)
+    assert cmp["n_hard"] == 0, cmp["hard"][:10]
+    assert (dg["terminal_kind"].cpu().numpy() == 2).any()  # corrections ran through the split pass
 
 
 def test_full_size_ragged_b256_qrows():

@@ -12,7 +12,7 @@ import torch
 
 import lossless_draft_verification_online_amd as sdv
 import workloads as W
-from gpu_helpers import DEV, log, to_device
+from gpu_helpers import DEV, log, to_device, to_device_off_grid
 from oracle import oracle
 from oracle.compare import compare_tree_verdicts
 
@@ -30,8 +30,9 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
 
 
-def run_tree(b, diag=(), seed=None):
-    acc, out, nodes, dg = sdv.verify_tree(to_device(b.target, b.dtype), to_device(b.draft, b.dtype), _i32(b.tokens),
+def run_tree(b, diag=(), seed=None, shifts=(0, 0)):
+    acc, out, nodes, dg = sdv.verify_tree(to_device_off_grid(b.target, b.dtype, shifts[0]),
+                                          to_device_off_grid(b.draft, b.dtype, shifts[1]), _i32(b.tokens),
                                           _i32(b.parents), _i32(b.cu), b.temperature,
                                           b.seed if seed is None else seed, diag=diag,
                                           draft_row=None if b.draft_row is None else _i32(b.draft_row))
@@ -39,10 +40,11 @@ def run_tree(b, diag=(), seed=None):
     return acc.cpu().numpy(), out.cpu().numpy(), nodes.cpu().numpy(), {k: v.cpu().numpy() for k, v in dg.items()}
 
 
-def check_tree(b, seed=None, diag=()):
+def check_tree(b, seed=None, diag=(), shifts=(0, 0)):
     seed = b.seed if seed is None else seed
-    log(f"tree parity: {b.name} B={b.B} nodes={b.n_draft_rows} V={b.V} {b.dtype} T={b.temperature} seed={seed}")
-    acc, out, nodes, dg = run_tree(b, diag=diag, seed=seed)
+    log(f"tree parity: {b.name} B={b.B} nodes={b.n_draft_rows} V={b.V} {b.dtype} T={b.temperature} seed={seed}"
+        f" base shifts={shifts}")
+    acc, out, nodes, dg = run_tree(b, diag=diag, seed=seed, shifts=shifts)
     ref = oracle.verify_tree(b.target, b.draft, b.tokens, b.parents, b.cu, b.temperature, seed, diag=True,
                              draft_row=b.draft_row)
     res = compare_tree_verdicts(acc, out, nodes, ref, b.cu, b.parents, b.temperature)
@@ -51,12 +53,24 @@ def check_tree(b, seed=None, diag=()):
     return acc, out, nodes, dg, ref
 
 
+@pytest.mark.parametrize("V,dtype,shifts,shared", [(8192, "bf16", (3, 0), True), (8192, "bf16", (0, 5), False),
+                                                   (4096, "fp32", (1, 2), True), (20011, "bf16", (7, 1), True)])
+def test_tree_rows_off_the_16_byte_grid(V, dtype, shifts, shared):
+    """Target and draft bases shifted by whole elements, so every row sits off the 16-byte grid at
+    its own offset: the passes and searches split the target rows and cut each draft row's bytes
+    by its own shift."""
+    rng = np.random.default_rng(V + shifts[0])
+    b = W.make_tree(f"tree_off_v{V}", rng.integers(0, 25, size=24), "random", V, dtype, 1.0, 3.0, 1.5,
+                    data_seed=V + 11, verify_seed=13, shared=shared)
+    check_tree(b, shifts=shifts)
+
+
 @pytest.mark.parametrize("kind", ["random", "kary", "star"])
 @pytest.mark.parametrize("V,dtype,T", [(1000, "fp32", 1.0), (1001, "fp32", 0.7), (32000, "bf16", 0.8),
                                        (32003, "bf16", 1.0), (16384, "bf16", 0.3), (128256, "bf16", 1.0)])
 def test_tree_parity(kind, V, dtype, T):
-    """Random, binary and star trees of 0 to 24 nodes; 16-byte aligned rows and an odd vocabulary
-    (element loads); several chunks per row and a ragged last chunk."""
+    """Random, binary and star trees of 0 to 24 nodes; 16-byte aligned rows and odd vocabularies
+    (rows split at 16-byte boundaries); several chunks per row and a ragged last chunk."""
     rng = np.random.default_rng(V + len(kind))
     B = 48 if V < 100000 else 24
     sizes = rng.integers(0, 25, size=B)
