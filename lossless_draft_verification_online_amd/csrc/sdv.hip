@@ -2946,17 +2946,23 @@ __device__ __forceinline__ float chain_p(const ChainFrame& f, float zt) {
   return fast_exp2(fmaf(zt, f.k2, -f.t_hi) - f.t_lo);
 }
 
-// Rejected children j0 .. j1 - 1 share one draft row: its q is loaded and exponentiated once and
-// every step of the run applied to it.
+// Rejected children j0 .. j1 - 1 share one draft row: its q is loaded and exponentiated once, and
+// the run's steps collapse into one, since for q >= 0 and a, b >= 0
+// max(max(x - a q, 0) - b q, 0) = max(x - (a + b) q, 0): R = max(R - c q, 0) with c the sum of the
+// run's masses M_j (run_mass).
 __device__ __forceinline__ int chain_run_end(const ChainFrame& f, int j0) {
   int j1 = j0 + 1;
   while (j1 < f.l && f.drow[j1] == f.drow[j0]) ++j1;
   return j1;
 }
+__device__ __forceinline__ float run_mass(const ChainFrame& f, int j0, int j1) {
+  float c = 0.0f;
+  for (int j = j0; j < j1; ++j) c += f.m[j];
+  return c;
+}
 __device__ __forceinline__ float chain_run(const ChainFrame& f, int j0, int j1, float R, float zd) {
   const float q = fast_exp2(fmaf(zd, f.k2, -f.d_hi[j0]) - f.d_lo[j0]);
-  for (int j = j0; j < j1; ++j) R = fmaxf(fmaf(-f.m[j], q, R), 0.0f);
-  return R;
+  return fmaxf(fmaf(-run_mass(f, j0, j1), q, R), 0.0f);
 }
 
 // R_l(v) for one element (rows given as byte pointers of the logits).
@@ -3041,13 +3047,12 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
 #pragma unroll
             for (int e = 0; e < E::kPerVec; ++e) q[k][e] = fast_exp2(fmaf(z[e], f.k2, -d_hi) - d_lo);
           }
-          for (; j < j1; ++j) {
-            const float m = f.m[j];
+          const float c = run_mass(f, j, j1);
 #pragma unroll
-            for (int k = 0; k < kGroup; ++k)
+          for (int k = 0; k < kGroup; ++k)
 #pragma unroll
-              for (int e = 0; e < E::kPerVec; ++e) R[k][e] = fmaxf(fmaf(-m, q[k][e], R[k][e]), 0.0f);
-          }
+            for (int e = 0; e < E::kPerVec; ++e) R[k][e] = fmaxf(fmaf(-c, q[k][e], R[k][e]), 0.0f);
+          j = j1;
         }
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
@@ -3084,13 +3089,12 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
 #pragma unroll
             for (int e2 = 0; e2 < E::kPerVec; ++e2) q[k][e2] = fast_exp2(fmaf(z[e2], f.k2, -d_hi) - d_lo);
           }
-          for (; j < j1; ++j) {
-            const float m = f.m[j];
+          const float c = run_mass(f, j, j1);
 #pragma unroll
-            for (int k = 0; k < kGroup; ++k)
+          for (int k = 0; k < kGroup; ++k)
 #pragma unroll
-              for (int e2 = 0; e2 < E::kPerVec; ++e2) R[k][e2] = fmaxf(fmaf(-m, q[k][e2], R[k][e2]), 0.0f);
-          }
+            for (int e2 = 0; e2 < E::kPerVec; ++e2) R[k][e2] = fmaxf(fmaf(-c, q[k][e2], R[k][e2]), 0.0f);
+          j = j1;
         }
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
