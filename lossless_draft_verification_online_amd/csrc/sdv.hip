@@ -65,6 +65,7 @@ struct DiagPtrs {
 
 constexpr int32_t kMaxChunks = 4096;  // chunks per row: the verdict and cut kernels keep one value per chunk in LDS
 constexpr int kVerdictWaves = 8;      // waves of a verdict workgroup
+constexpr int kWideVerdictWaves = 16; // waves of a verdict workgroup for small batches of short rows
 
 // Truncating bf16 calls: the row pass also counts, per chunk, the logits of each of the kHistKeys
 // 16-bit order keys at and below the chunk maximum's (one binade of positive logits), so that a cut
@@ -765,13 +766,13 @@ __device__ __forceinline__ void resid_masses_pipelined(const M& m, const char* t
 // weight (the row sums of the first step), which every wave also stores into *total; a residual
 // range without positive weight returns -2 in every wave.  With kFraction over a whole row of up to
 // four chunks this one pass replaces the mass pass, the pick of a chunk and the search in it.
-template <class E, bool kResid, bool kFraction = false, int kChunks = 1, class M>
+template <class E, bool kResid, bool kFraction = false, int kChunks = 1, int kWaves = kVerdictWaves, class M>
 __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* trow, const char* drow, int32_t c0,
                                                       int32_t n, double target, float k2, float ref_t, float e_hi,
                                                       float q_scale, double* row_sums, int lane, int wave,
                                                       int n_waves, double* total = nullptr) {
   constexpr int kRows = kVecPerLane * kChunks;  // 16 rows of 64 vectors per chunk
-  static_assert(kRows % kVerdictWaves == 0 && kRows <= kWave, "whole rows per wave, one scan of the row sums");
+  static_assert(kRows % kWaves == 0 && kRows <= kWave, "whole rows per wave, one scan of the row sums");
   const int32_t nvec = n / E::kPerVec;
   const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
   const u32x4* dv = reinterpret_cast<const u32x4*>((kResid ? drow : trow) + (int64_t)c0 * E::kBytes);
@@ -784,8 +785,8 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
       w[q] = kResid ? resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale)
                     : p_weight(m, ft[q], v0 + q, k2, ref_t);
   };
-  // rows owned by this wave: wave + j n_waves, j < kPer (n_waves == kVerdictWaves)
-  constexpr int kPer = kRows / kVerdictWaves;
+  // rows owned by this wave: wave + j n_waves, j < kPer (n_waves == kWaves)
+  constexpr int kPer = kRows / kWaves;
   u32x4 t[kPer], dd[kPer];
   float vs[kPer];
 #pragma unroll
@@ -917,11 +918,13 @@ __device__ __forceinline__ int32_t split_edge(const Split& s, int32_t n, int per
   return split::edge(s.head, s.body * per_vec, n, lane);
 }
 
-// Residual mass of one chunk of a rejected row pair off the 16-byte grid, by one wave.  The edge
-// elements load first; the body goes in quarters of 4 vectors per lane, the loads of the next
-// quarter issued before the current one is reduced.  Every quarter loads (indices clamped into the
-// body), so no load sits under a branch and the waits count only the loads ahead of the data used.
-template <class E, class M>
+// Residual mass of one chunk of a rejected row pair, by one wave.  The edge elements load first;
+// the body goes in quarters of 4 vectors per lane, the loads of the next quarter issued before the
+// current one is reduced.  Every quarter loads (indices clamped into the body), so no load sits
+// under a branch and the waits count only the loads ahead of the data used.  kVec: 16-byte aligned
+// rows (no edges, no shift: one draft vector under each target vector); this form needs fewer
+// registers than resid_masses_pipelined and serves the 16-wave verdict workgroups.
+template <class E, bool kVec, class M>
 __device__ __forceinline__ double resid_chunk_mass_split(const M& m, const char* tp, const char* dp, int32_t V,
                                                          int32_t c0, int32_t n, float k2, float ref_t, float e_hi,
                                                          float q_scale, int lane) {
@@ -944,12 +947,15 @@ __device__ __forceinline__ double resid_chunk_mass_split(const M& m, const char*
         const int jc = min(lane + kWave * (h * kPart + k), s.body - 1);
         st.t[k] = s.tv[jc];
         st.lo[k] = s.dv[jc];
-        st.hi[k] = s.dv[s.shift != 0 ? jc + 1 : jc];
+        if constexpr (!kVec) st.hi[k] = s.dv[s.shift != 0 ? jc + 1 : jc];
       }
     };
     auto pin = [&](Stage& st) {  // the reduction of this stage stays below the loads just issued
 #pragma unroll
-      for (int k = 0; k < kPart; ++k) asm volatile("" : "+v"(st.t[k]), "+v"(st.lo[k]), "+v"(st.hi[k])::"memory");
+      for (int k = 0; k < kPart; ++k) {
+        if constexpr (kVec) asm volatile("" : "+v"(st.t[k]), "+v"(st.lo[k])::"memory");
+        else asm volatile("" : "+v"(st.t[k]), "+v"(st.lo[k]), "+v"(st.hi[k])::"memory");
+      }
     };
     auto reduce = [&](const Stage& st, int h) {
       double part = 0.0;
@@ -958,7 +964,7 @@ __device__ __forceinline__ double resid_chunk_mass_split(const M& m, const char*
         const int j = lane + kWave * (h * kPart + k);
         float ft[E::kPerVec], fd[E::kPerVec];
         E::unpack(j < s.body ? st.t[k] : neg_inf_vec<E>(), ft);
-        E::unpack(funnel16(st.lo[k], st.hi[k], s.shift), fd);
+        E::unpack(kVec ? st.lo[k] : funnel16(st.lo[k], st.hi[k], s.shift), fd);
         const int32_t v0 = c0 + s.head + j * E::kPerVec;
 #pragma unroll
         for (int q = 0; q < E::kPerVec; ++q) ft[q] = resid_weight(m, ft[q], fd[q], v0 + q, k2, ref_t, e_hi, q_scale);
@@ -989,13 +995,13 @@ __device__ __forceinline__ double resid_chunk_mass_split(const M& m, const char*
 // after them (wave 0 weighs both).  The scan runs over the 18 segment sums; an edge segment is
 // walked by wave 0 lane by lane.  Returns the token in the wave that resolves it, -1 in the
 // others.  row_sums holds at least 18 doubles.
-template <class E, bool kResid, class M>
+template <class E, bool kResid, int kWaves = kVerdictWaves, class M>
 __device__ __forceinline__ int32_t search_chunk_split(const M& m, const char* trow, const char* drow, int32_t V,
                                                       int32_t c0, int32_t n, double target, float k2, float ref_t,
                                                       float e_hi, float q_scale, double* row_sums, int lane, int wave,
                                                       int n_waves) {
   constexpr int kRows = kVecPerLane;  // 16 rows of 64 vectors
-  constexpr int kPer = kRows / kVerdictWaves;
+  constexpr int kPer = kRows / kWaves;
   constexpr int kSeg = kRows + 2;  // the head, the rows, the tail
   const PairSplit s = pair_split<E>(trow, kResid ? drow : trow, V, c0, n);
   auto weights = [&](const u32x4& t, const u32x4& dd, int32_t v0, float (&w)[E::kPerVec]) {
@@ -1132,7 +1138,7 @@ struct Quad<F32> {
 // rows), laid out as the logit version: rows of 64 vectors, wave w sums rows w and w + n_waves, a
 // scan of the row sums picks the row, the owning wave scans its vector sums and walks the vector.
 // Returns the token in the owning wave and -1 in the others.  row_sums holds at least 16 doubles.
-template <class E, class M>
+template <class E, int kWaves = kVerdictWaves, class M>
 __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* trow, const float* qrow, int32_t c0,
                                                         int32_t n, double target, float k2, float ref_t,
                                                         float q_scale, double* row_sums, int lane, int wave,
@@ -1151,7 +1157,7 @@ __device__ __forceinline__ int32_t search_chunk_q_block(const M& m, const char* 
       for (int e = 0; e < 4; ++e)
         w[4 * g + e] = resid_weight_q(m, ft[4 * g + e], q[g][e], v0 + 4 * g + e, k2, ref_t, q_scale);
   };
-  constexpr int kPer = kRows / kVerdictWaves;  // rows of 64 vectors per wave
+  constexpr int kPer = kRows / kWaves;  // rows of 64 vectors per wave
   u32x4 t[kPer];
   f32x4 q[kPer][kQV];
   float vs[kPer];
@@ -1341,16 +1347,16 @@ __device__ __forceinline__ double resid_chunk_mass_q_split(const M& m, const cha
 // w + n_waves, ..., and the head's and tail's elements are two more segments before and after
 // them, weighed and walked by wave 0 as in search_chunk_split.  Returns the token in the wave that
 // resolves it, -1 in the others.  row_sums holds at least 34 doubles.
-template <class E, class M>
+template <class E, int kWaves = kVerdictWaves, class M>
 __device__ __forceinline__ int32_t search_chunk_q_split(const M& m, const char* trow, const float* qrow, int32_t V,
                                                         int32_t c0, int32_t n, double target, float k2, float ref_t,
                                                         float q_scale, double* row_sums, int lane, int wave,
                                                         int n_waves) {
   typedef typename Quad<E>::T TQ;
   constexpr int kRows = E::kChunk / 4 / kWave;  // rows of 64 quads: 32 (bf16) or 16 (fp32)
-  constexpr int kPer = kRows / kVerdictWaves;
+  constexpr int kPer = kRows / kWaves;
   constexpr int kSeg = kRows + 2;  // the head, the rows, the tail
-  static_assert(kRows % kVerdictWaves == 0 && kSeg <= kWave, "whole rows per wave, one scan of the segments");
+  static_assert(kRows % kWaves == 0 && kSeg <= kWave, "whole rows per wave, one scan of the segments");
   const QSplit<E> s = q_split<E>(trow, qrow, V, c0, n);
   const int32_t b0 = c0 + s.head;
   auto weights = [&](const TQ& t, const f32x4& q, int32_t v0, float (&w)[4]) {
@@ -2491,12 +2497,12 @@ struct Decision {
   Cut ct, cd;  // cuts of the drawn position's target and draft rows (truncating profiles)
 };
 
-template <class E, bool kVec, bool kQ, bool kCut>
+template <class E, bool kVec, bool kQ, bool kCut, int kWaves>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves);
 
-static_assert(kVecPerLane % kVerdictWaves == 0, "the in-chunk search gives each wave whole rows of 64 vectors");
+static_assert(kVecPerLane % 16 == 0, "the in-chunk search gives each wave (8 or 16) whole rows of 64 vectors");
 constexpr int kMaxRows = 2 * SDV_MAX_DEPTH + 1;
 
 // Folds a request's rows: rows r <= K_t are its target rows r (records at rec_t), rows r > K_t its
@@ -2553,7 +2559,7 @@ __device__ __forceinline__ void stage_and_fold(const Params& P, const float2* re
 // hold the kept masses.  With P.split workgroups per request (blockIdx.y = 0 .. split - 1) every
 // one reaches the same decision from the same loads; the first writes it, and a correction's
 // residual pass is shared among them (draw_terminal).
-template <class E, bool kGreedy, bool kVec, bool kQ, bool kCut>
+template <class E, bool kGreedy, bool kVec, bool kQ, bool kCut, int kWaves>
 __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k2, uint64_t seed, bool bad_profile,
                                              double* lds_mass, RowFold* rows, Decision& dec) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -2717,15 +2723,15 @@ __device__ __forceinline__ void verdict_body(const Params& P, int32_t i, float k
   }
   __syncthreads();
   if constexpr (!kGreedy)
-    draw_terminal<E, kVec, kQ, kCut>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
+    draw_terminal<E, kVec, kQ, kCut, kWaves>(P, dec, k2, i, trow0, drow0, rec_t, lds_mass, lane, wave, n_waves);
 }
 
 // Workgroups (blockIdx.x, s), s < P.split, verify request blockIdx.x.  With a profile per request,
 // the request's temperature selects the rule at run time (uniformly over the workgroup).  A top-k
 // below 0 or a top-p outside [0, 1000] thousandths describes no profile: the request is rejected
 // under either rule.
-template <class E, int kMode, bool kVec, bool kQ, bool kCut>
-__global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
+template <class E, int kMode, bool kVec, bool kQ, bool kCut, int kWaves = kVerdictWaves>
+__global__ __launch_bounds__(kWave * kWaves) void verdicts(Params P) {
   extern __shared__ double lds_mass[];  // [C]
   __shared__ RowFold rows[kMaxRows];
   __shared__ Decision dec;
@@ -2735,10 +2741,12 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
   if constexpr (kMode == kModeProfiled) {
     const float k2 = k2_of(temperature_of(P.temp_each, i));
     const uint64_t seed = P.seed_each[i];
-    if (k2 > 0.0f) verdict_body<E, false, kVec, kQ, kCut>(P, i, k2, seed, bad_truncation, lds_mass, rows, dec);
-    else verdict_body<E, true, kVec, false, false>(P, i, 0.0f, seed, !(k2 == 0.0f) || bad_truncation, lds_mass, rows, dec);
+    if (k2 > 0.0f) verdict_body<E, false, kVec, kQ, kCut, kWaves>(P, i, k2, seed, bad_truncation, lds_mass, rows, dec);
+    else
+      verdict_body<E, true, kVec, false, false, kWaves>(P, i, 0.0f, seed, !(k2 == 0.0f) || bad_truncation, lds_mass,
+                                                        rows, dec);
   } else {
-    verdict_body<E, kMode == kModeGreedy, kVec, kQ && kMode != kModeGreedy, kCut && kMode != kModeGreedy>(
+    verdict_body<E, kMode == kModeGreedy, kVec, kQ && kMode != kModeGreedy, kCut && kMode != kModeGreedy, kWaves>(
         P, i, P.k2, P.seed, bad_truncation, lds_mass, rows, dec);
   }
 }
@@ -2747,7 +2755,7 @@ __global__ __launch_bounds__(kWave * kVerdictWaves) void verdicts(Params P) {
 // workgroups per request, workgroup s computes the residual masses of chunks [s C / split,
 // (s + 1) C / split) and publishes them; the last one to finish (a counter per request) reads the
 // others' and draws.  A bonus draw needs no residual pass: the first workgroup draws it alone.
-template <class E, bool kVec, bool kQ, bool kCut>
+template <class E, bool kVec, bool kQ, bool kCut, int kWaves>
 __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d, float k2, int32_t i, int32_t trow0,
                                               int32_t drow0, const float2* rec_t, double* lds_mass, int lane,
                                               int wave, int n_waves) {
@@ -2792,14 +2800,14 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
     }
     __syncthreads();
   } else if (residual && !one_chunk && !few_chunks) {
-    if constexpr (kVec) {
+    if constexpr (kVec && kWaves == kVerdictWaves) {
       resid_masses_pipelined<E>(m_r, tp + (int64_t)v_lo * E::kBytes, dp + (int64_t)v_lo * E::kBytes, V_r,
                                 c_hi - c_lo, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + c_lo, lane, wave, n_waves);
     } else {
       for (int32_t c = c_lo + wave; c < c_hi; c += n_waves) {
         const int32_t c0 = c * E::kChunk;
-        const double cm = resid_chunk_mass_split<E>(m, tp, dp, P.V, c0, min(E::kChunk, P.V - c0), k2, d.ref_t,
-                                                    d.e_hi, d.q_scale, lane);
+        const double cm = resid_chunk_mass_split<E, kVec>(m, tp, dp, P.V, c0, min(E::kChunk, P.V - c0), k2, d.ref_t,
+                                                          d.e_hi, d.q_scale, lane);
         if (lane == 0) lds_mass[c] = cm;
       }
     }
@@ -2845,7 +2853,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
       bool empty = false;
       double S = 0.0;
       if (residual) {
-        y = search_chunk_block<E, true, true, kC>(m, tp, dp, 0, P.V, (double)d.u, k2, d.ref_t, d.e_hi, d.q_scale,
+        y = search_chunk_block<E, true, true, kC, kWaves>(m, tp, dp, 0, P.V, (double)d.u, k2, d.ref_t, d.e_hi, d.q_scale,
                                                   lds_mass + P.C, lane, wave, n_waves, &S);
         empty = y == -2;  // no positive residual weight in floating point: draw from p_t
         // the fallback search rewrites the row sums every wave has just read: all reads come first
@@ -2853,7 +2861,7 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
         if (empty) __syncthreads();
       }
       if (!residual || empty)
-        y = search_chunk_block<E, false, true, kC>(m, tp, nullptr, 0, P.V, (double)d.u, k2, d.ref_t, 0.0f, 0.0f,
+        y = search_chunk_block<E, false, true, kC, kWaves>(m, tp, nullptr, 0, P.V, (double)d.u, k2, d.ref_t, 0.0f, 0.0f,
                                                    lds_mass + P.C, lane, wave, n_waves, &S);
       write_token(y, empty, S);
     };
@@ -2890,23 +2898,23 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
   int32_t y = -1;
   if constexpr (kVec) {
     if (residual && kQ)
-      y = search_chunk_q_block<E>(m, tp, qp, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave,
+      y = search_chunk_q_block<E, kWaves>(m, tp, qp, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave,
                                   n_waves);
     else if (residual)
-      y = search_chunk_block<E, true>(m, tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
+      y = search_chunk_block<E, true, false, 1, kWaves>(m, tp, dp, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
                                       wave, n_waves);
     else
-      y = search_chunk_block<E, false>(m, tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C, lane,
+      y = search_chunk_block<E, false, false, 1, kWaves>(m, tp, nullptr, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C, lane,
                                        wave, n_waves);
   } else {
     if (residual && kQ) {
-      y = search_chunk_q_split<E>(m, tp, qp, P.V, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave,
+      y = search_chunk_q_split<E, kWaves>(m, tp, qp, P.V, s0, n, tgt, k2, d.ref_t, d.q_scale, lds_mass + P.C, lane, wave,
                                   n_waves);
     } else if (residual) {
-      y = search_chunk_split<E, true>(m, tp, dp, P.V, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
+      y = search_chunk_split<E, true, kWaves>(m, tp, dp, P.V, s0, n, tgt, k2, d.ref_t, d.e_hi, d.q_scale, lds_mass + P.C, lane,
                                       wave, n_waves);
     } else {
-      y = search_chunk_split<E, false>(m, tp, nullptr, P.V, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
+      y = search_chunk_split<E, false, kWaves>(m, tp, nullptr, P.V, s0, n, tgt, k2, d.ref_t, 0.0f, 0.0f, lds_mass + P.C,
                                        lane, wave, n_waves);
     }
   }
@@ -3697,9 +3705,23 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
     if (P.qrows) {
       if (cut) hipLaunchKernelGGL((verdicts<E, kMode, kVec, true, true>), grid, block, lds, stream, P);
       else hipLaunchKernelGGL((verdicts<E, kMode, kVec, true, false>), grid, block, lds, stream, P);
+    } else if (cut) {
+      hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, true>), grid, block, lds, stream, P);
     } else {
-      if (cut) hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, true>), grid, block, lds, stream, P);
-      else hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, false>), grid, block, lds, stream, P);
+      // a small batch of 16-byte rows of two to four chunks (the single pass over the whole pair):
+      // 16 waves per request hide more of each correction's latency (64 x 32000 bf16: 11.8 against
+      // 12.7 us of verdicts by rocprofv3); rows of one chunk (1 x 1000 fp32: 6.4 against 6.3 us),
+      // long rows and full batches keep 8
+      bool wide = false;
+      if constexpr (kVec && kMode == kModeSampling)
+        wide = P.split == 1 && P.C >= 2 && P.C <= 4 && 2 * (int64_t)P.B <= kComputeUnits;
+      if (wide) {
+        if constexpr (kVec && kMode == kModeSampling)
+          hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, false, kWideVerdictWaves>), grid,
+                             dim3(kWave * kWideVerdictWaves), lds, stream, P);
+      } else {
+        hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, false>), grid, block, lds, stream, P);
+      }
     }
   } else {
     hipLaunchKernelGGL((verdicts<E, kMode, kVec, false, false>), grid, block, lds, stream, P);

@@ -260,6 +260,19 @@ def test_large_and_odd_vocabularies(V, dtype):
     check_parity(b, diag=("terminal_kind", "target_lse"))
 
 
+@pytest.mark.parametrize("V,dtype,B", [(12288, "fp32", 32), (24576, "bf16", 128), (16384, "bf16", 7)])
+def test_small_batches_of_short_rows(V, dtype, B):
+    """Batches of at most 128 requests on 16-byte rows of two to four chunks take the verdict kernel
+    with 16 waves per request (the single pass over the rejected pair, the quarter-stage mass pass
+    form); verdicts and normalisers against the oracle."""
+    rng = np.random.default_rng(V + B)
+    b = W.make_random(f"short_rows_v{V}_b{B}", rng.integers(0, 9, size=B), V, dtype, 0.9, 3.0,
+                      rng.uniform(0.5, 3, B), data_seed=V + B, verify_seed=21)
+    _, _, ref, cmp, dg = check_parity(b, diag=("terminal_kind", "target_lse"))
+    np.testing.assert_allclose(dg["target_lse"], ref["target_lse"], rtol=0, atol=RTOL_PROB)
+    assert (ref["terminal_kind"] == 2).any()
+
+
 def test_one_request_at_full_depth_and_width():
     b = W.make_random("b1_k64_v128256", [64], 128256, "bf16", 1.0, 3.0, 0.3, data_seed=64, verify_seed=64)
     acc, out, ref, cmp, _ = check_parity(b)
