@@ -857,7 +857,8 @@ __device__ __forceinline__ int32_t search_chunk_block(const M& m, const char* tr
 
 // ---------------------------------------------------------------------------- rows off the 16-byte grid
 // A plan's address as an offset from the row pointer it came from, so that the compiler still
-// knows the loads through it read global memory.
+// knows the loads through it read global memory (cast from an integer it would be a flat address:
+// flat loads, which also count against the shared-memory wait counter).
 __device__ __forceinline__ const char* at_address(const char* base, uintptr_t a) {
   return base + (intptr_t)(a - (uintptr_t)base);
 }
@@ -880,7 +881,7 @@ template <class E>
 __device__ __forceinline__ PairSplit pair_split(const char* tp, const char* dp, int32_t V, int32_t c0, int32_t n) {
   const split::Plan p = split::pair((uintptr_t)tp, (uintptr_t)dp, E::kBytes, V, c0, n);
   return PairSplit{p.head, p.body, p.shift, reinterpret_cast<const u32x4*>(at_address(tp, p.first)),
-                   reinterpret_cast<const u32x4*>(p.pieces)};
+                   reinterpret_cast<const u32x4*>(at_address(dp, p.pieces))};
 }
 
 // The 16 bytes `shift` bytes into (lo, hi); shift is a multiple of 2 and the same in every lane, so
@@ -1238,7 +1239,7 @@ template <class E>
 __device__ __forceinline__ QSplit<E> q_split(const char* tp, const float* qp, int32_t V, int32_t c0, int32_t n) {
   const split::Plan p = split::q((uintptr_t)tp, (uintptr_t)qp, E::kBytes, V, c0, n);
   return QSplit<E>{p.head, p.body, p.shift, reinterpret_cast<const f32x4*>(qp + c0 + p.head),
-                   reinterpret_cast<const typename Quad<E>::T*>(p.pieces)};
+                   reinterpret_cast<const typename Quad<E>::T*>(at_address(tp, p.pieces))};
 }
 
 // The 4 target logits `shift` bytes into (lo, hi): 8-byte pieces of bf16 (shift 0, 2, 4 or 6) or
