@@ -2946,13 +2946,17 @@ __device__ __forceinline__ void draw_terminal(const Params& P, const Decision d,
 struct ChainFrame {
   int32_t l;                       // rejected children so far
   float k2, t_hi, t_lo;            // the node's target row: log2 p(v) = zt k2 - (t_hi + t_lo)
-  float d_hi[SDV_MAX_DEPTH], d_lo[SDV_MAX_DEPTH];  // rejected child j's draft row, the same form
+  float d_hi[SDV_MAX_DEPTH];       // rejected child j's draft row: log2 q(v) = zd k2 - (d_hi + d_lo)
+  float d_scale[SDV_MAX_DEPTH];    // 2^(t_lo - d_lo) for child j
   float m[SDV_MAX_DEPTH];          // M_j, the mass before rejection j + 1 (m[0] = 1)
   int32_t drow[SDV_MAX_DEPTH];     // rejected child j's draft row (batch index)
 };
 
+// The passes work in units of 2^-t_lo: R'(v) = R(v) 2^t_lo, which starts from 2^(zt k2 - t_hi) and
+// takes each draft row's q as 2^(zd k2 - d_hi) with its coefficient scaled by d_scale, so that no
+// element pays for the low parts.  Masses summed in these units are scaled back by 2^-t_lo.
 __device__ __forceinline__ float chain_p(const ChainFrame& f, float zt) {
-  return fast_exp2(fmaf(zt, f.k2, -f.t_hi) - f.t_lo);
+  return fast_exp2(fmaf(zt, f.k2, -f.t_hi));
 }
 
 // Rejected children j0 .. j1 - 1 share one draft row: its q is loaded and exponentiated once, and
@@ -2967,10 +2971,10 @@ __device__ __forceinline__ int chain_run_end(const ChainFrame& f, int j0) {
 __device__ __forceinline__ float run_mass(const ChainFrame& f, int j0, int j1) {
   float c = 0.0f;
   for (int j = j0; j < j1; ++j) c += f.m[j];
-  return c;
+  return c * f.d_scale[j0];  // one row: one d_lo for the whole run
 }
 __device__ __forceinline__ float chain_run(const ChainFrame& f, int j0, int j1, float R, float zd) {
-  const float q = fast_exp2(fmaf(zd, f.k2, -f.d_hi[j0]) - f.d_lo[j0]);
+  const float q = fast_exp2(fmaf(zd, f.k2, -f.d_hi[j0]));
   return fmaxf(fmaf(-run_mass(f, j0, j1), q, R), 0.0f);
 }
 
@@ -3027,44 +3031,55 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
       const int32_t nvec = n / E::kPerVec;
       const u32x4* tv = reinterpret_cast<const u32x4*>(trow + (int64_t)c0 * E::kBytes);
       constexpr int kGroup = kTreeGroup;
-      // indices clamped into the chunk keep every load unconditional (a vector past the end has a
-      // target of -inf, so R is 0 there whatever the draft row holds)
-      for (int g0 = 0; g0 < kVecPerLane && g0 * kWave < nvec; g0 += kGroup) {
-        float R[kGroup][E::kPerVec];
-        auto jc = [&](int k) { return min(lane + kWave * (g0 + k), nvec - 1); };
-#pragma unroll
-        for (int k = 0; k < kGroup; ++k) {
-          const int j = lane + kWave * (g0 + k);
-          const u32x4 t = tv[jc(k)];
-          float z[E::kPerVec];
-          E::unpack(j < nvec ? t : neg_inf_vec<E>(), z);
-#pragma unroll
-          for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_p(f, z[e]);
-        }
-        for (int j = 0; j < f.l;) {  // one load and one exponential per run of rejections on one row
-          const int j1 = chain_run_end(f, j);
-          const u32x4* dv = reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
-          u32x4 b[kGroup];
-#pragma unroll
-          for (int k = 0; k < kGroup; ++k) b[k] = dv[jc(k)];
-          const float d_hi = f.d_hi[j], d_lo = f.d_lo[j];
-          float q[kGroup][E::kPerVec];
+      // a full chunk indexes its vectors directly; the partial last one clamps indices into the
+      // chunk, which keeps every load unconditional (a vector past the end has a target of -inf, so
+      // R is 0 there whatever the draft row holds)
+      auto pass = [&](auto full_chunk) {
+        constexpr bool kFull = decltype(full_chunk)::value;
+        for (int g0 = 0; g0 < kVecPerLane && (kFull || g0 * kWave < nvec); g0 += kGroup) {
+          float R[kGroup][E::kPerVec];
+          auto jc = [&](int k) { return kFull ? lane + kWave * (g0 + k) : min(lane + kWave * (g0 + k), nvec - 1); };
 #pragma unroll
           for (int k = 0; k < kGroup; ++k) {
+            const u32x4 t = tv[jc(k)];
             float z[E::kPerVec];
-            E::unpack(b[k], z);
+            E::unpack(kFull || lane + kWave * (g0 + k) < nvec ? t : neg_inf_vec<E>(), z);
 #pragma unroll
-            for (int e = 0; e < E::kPerVec; ++e) q[k][e] = fast_exp2(fmaf(z[e], f.k2, -d_hi) - d_lo);
+            for (int e = 0; e < E::kPerVec; ++e) R[k][e] = chain_p(f, z[e]);
           }
-          const float c = run_mass(f, j, j1);
+          for (int j = 0; j < f.l;) {  // one load and one exponential per run of rejections on one row
+            const int j1 = chain_run_end(f, j);
+            const u32x4* dv =
+                reinterpret_cast<const u32x4*>(row_ptr<E>(draft, f.drow[j], V) + (int64_t)c0 * E::kBytes);
+            u32x4 b[kGroup];
 #pragma unroll
-          for (int k = 0; k < kGroup; ++k)
+            for (int k = 0; k < kGroup; ++k) b[k] = dv[jc(k)];
+            const float d_hi = f.d_hi[j];
+            float q[kGroup][E::kPerVec];
 #pragma unroll
-            for (int e = 0; e < E::kPerVec; ++e) R[k][e] = fmaxf(fmaf(-c, q[k][e], R[k][e]), 0.0f);
-          j = j1;
+            for (int k = 0; k < kGroup; ++k) {
+              float z[E::kPerVec];
+              E::unpack(b[k], z);
+#pragma unroll
+              for (int e = 0; e < E::kPerVec; ++e) q[k][e] = fast_exp2(fmaf(z[e], f.k2, -d_hi));
+            }
+            const float cm = run_mass(f, j, j1);
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k)
+#pragma unroll
+              for (int e = 0; e < E::kPerVec; ++e) R[k][e] = fmaxf(fmaf(-cm, q[k][e], R[k][e]), 0.0f);
+            j = j1;
+          }
+#pragma unroll
+          for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
         }
-#pragma unroll
-        for (int k = 0; k < kGroup; ++k) acc += (double)tree_sum(R[k]);
+      };
+      bool full = false;  // (binary32 rows keep one form: with both, the pass spills registers)
+      if constexpr (E::kBytes == 2) full = nvec == kVecPerLane * kWave;
+      if (full) {
+        if constexpr (E::kBytes == 2) pass(std::true_type{});
+      } else {
+        pass(std::false_type{});
       }
     } else {  // split on the target row's 16-byte grid: body vectors, then the lane's edge element
       const TreeSplit s = tree_split<E>(trow, V, c0, n);
@@ -3089,14 +3104,14 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
           u32x4 b[kGroup];
 #pragma unroll
           for (int k = 0; k < kGroup; ++k) b[k] = tree_draft_vec<E>(dp, c0, s, jc[k]);
-          const float d_hi = f.d_hi[j], d_lo = f.d_lo[j];
+          const float d_hi = f.d_hi[j];
           float q[kGroup][E::kPerVec];
 #pragma unroll
           for (int k = 0; k < kGroup; ++k) {
             float z[E::kPerVec];
             E::unpack(b[k], z);
 #pragma unroll
-            for (int e2 = 0; e2 < E::kPerVec; ++e2) q[k][e2] = fast_exp2(fmaf(z[e2], f.k2, -d_hi) - d_lo);
+            for (int e2 = 0; e2 < E::kPerVec; ++e2) q[k][e2] = fast_exp2(fmaf(z[e2], f.k2, -d_hi));
           }
           const float c = run_mass(f, j, j1);
 #pragma unroll
@@ -3425,9 +3440,11 @@ __global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
             frame.t_lo = (float)(l2 - (double)(float)l2);
           }
           if (lane < l) {
+            const double t_lo = (double)(float)(l2 - (double)(float)l2);
+            const double d_lo = (double)(float)(rej_l2 - (double)(float)rej_l2);
             frame.drow[lane] = rej_drow;
             frame.d_hi[lane] = (float)rej_l2;
-            frame.d_lo[lane] = (float)(rej_l2 - (double)(float)rej_l2);
+            frame.d_scale[lane] = (float)exp2(t_lo - d_lo);
             frame.m[lane] = (float)rej_m;
           }
         }
@@ -3441,7 +3458,7 @@ __global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
     if (wave == 0) {  // M_l; a residual without positive mass restarts from the node's own p
       double S = 0.0;
       for (int32_t c = lane; c < P.C; c += kWave) S += lds_mass[c];
-      S = wave_sum(S);
+      S = wave_sum(S) * exp2(-(double)frame.t_lo);  // from units of 2^-t_lo
       if (S > 0.0) {
         M_l = S;
       } else {
@@ -3473,7 +3490,7 @@ __global__ __launch_bounds__(kWave * kTreeWaves) void tree_verdicts(Params P) {
                                                  lane, wave, n_waves)
               : tree_search_block<E, false, kVec>(frame, tp, P.draft, P.V, s0, n, tgt, ref, lds_mass + P.C, &drawn,
                                                   lane, wave, n_waves);
-    if (!chain) S *= exp2((double)ref - rows[row].l2);  // probability units
+    S *= chain ? exp2(-(double)frame.t_lo) : exp2((double)ref - rows[row].l2);  // probability units
   }
   if (wave != 0) return;
   const int32_t path_tok = __shfl(x, path_node < 0 ? 0 : path_node, kWave);
