@@ -67,10 +67,12 @@ def test_tree_rows_off_the_16_byte_grid(V, dtype, shifts, shared):
 
 @pytest.mark.parametrize("kind", ["random", "kary", "star"])
 @pytest.mark.parametrize("V,dtype,T", [(1000, "fp32", 1.0), (1001, "fp32", 0.7), (32000, "bf16", 0.8),
-                                       (32003, "bf16", 1.0), (16384, "bf16", 0.3), (128256, "bf16", 1.0)])
+                                       (32003, "bf16", 1.0), (16384, "bf16", 0.3), (128256, "bf16", 1.0),
+                                       (12288, "fp32", 1.0), (12290, "fp32", 0.9)])
 def test_tree_parity(kind, V, dtype, T):
     """Random, binary and star trees of 0 to 24 nodes; 16-byte aligned rows and odd vocabularies
-    (rows split at 16-byte boundaries); several chunks per row and a ragged last chunk."""
+    (rows split at 16-byte boundaries); several chunks per row and a ragged last chunk, in bf16
+    and in binary32 (whose passes keep one form for full and partial chunks)."""
     rng = np.random.default_rng(V + len(kind))
     B = 48 if V < 100000 else 24
     sizes = rng.integers(0, 25, size=B)
