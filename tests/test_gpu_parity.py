@@ -185,6 +185,30 @@ def test_vocab_sizes_and_ragged_tails(V, dtype):
         check_parity(b)
 
 
+@pytest.mark.parametrize("V,dtype,t_from,d_from", [(20000, "bf16", 12000, 15000), (5000, "fp32", 4096, 4500),
+                                                   (20003, "bf16", 16384, 16000)])
+def test_masked_vocabulary(V, dtype, t_from, d_from):
+    """Padded vocabularies: every target logit from t_from on and every draft logit from d_from on
+    is -inf (whole chunks among them), so p and q vanish there, and the draft tokens are drawn from
+    the masked draft rows.  Sampling (logit and probability draft rows) and greedy."""
+    rng = np.random.default_rng(V + t_from)
+    depths = rng.integers(0, 9, size=24)
+    neg = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    for T in (1.0, 0.0):
+        b = W.make_random(f"masked_v{V}", depths, V, dtype, T, 3.0, 1.5, V + 5, 19, keep_draft=True)
+        b.target = b.target.copy()
+        b.target[:, t_from:] = neg
+        b.draft = b.draft.copy()
+        b.draft[:, d_from:] = neg
+        tok_rng = np.random.Generator(np.random.Philox(V + 23))
+        b.tokens = W._gumbel_tokens(tok_rng, b.draft, dtype, T) if T > 0 else W._argmax_tokens(b.draft, dtype)
+        assert (b.tokens < d_from).all()
+        acc, *_ = check_parity(b)
+        assert (acc >= 0).all()
+        if T > 0:
+            check_parity(W.with_qrows(b))
+
+
 def test_bad_requests_are_isolated():
     rng = np.random.default_rng(21)
     depths = [3, 2, 4, 0, 5]
