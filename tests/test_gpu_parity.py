@@ -209,6 +209,18 @@ def test_masked_vocabulary(V, dtype, t_from, d_from):
             check_parity(W.with_qrows(b))
 
 
+@pytest.mark.parametrize("T", [0.02, 0.1, 8.0, 50.0])
+def test_extreme_temperatures(T):
+    """Temperatures far from 1: nearly one-hot p and q (most exponentials underflow to 0, and the
+    residual lives on a handful of tokens), and nearly flat ones (the ratio near 1 everywhere)."""
+    rng = np.random.default_rng(int(T * 100) + 7)
+    depths = rng.integers(0, 9, size=32)
+    for V, dtype in ((32000, "bf16"), (3001, "fp32")):
+        b = W.make_random(f"temp{T}_v{V}", depths, V, dtype, T, 3.0, rng.uniform(0.2, 2.0, 32), V + 9, 29)
+        acc, *_ = check_parity(b)
+        assert (acc >= 0).all()
+
+
 def test_bad_requests_are_isolated():
     rng = np.random.default_rng(21)
     depths = [3, 2, 4, 0, 5]
