@@ -6,6 +6,7 @@ kernels behind ``sdv_verify``.  Work goes on torch's current HIP stream.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 
 import torch
@@ -35,6 +36,19 @@ def workspace_bytes(B: int, n_draft_rows: int, V: int, dtype: torch.dtype) -> in
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _launch_on(dev: torch.device):
+    """(context, stream) for a launch on dev: the device guard (none when dev is already current)
+    and the handle of dev's current stream.  The per-call entry points use it to keep their host
+    cost small next to the kernels of a small batch."""
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    ctx = contextlib.nullcontext() if torch.cuda.current_device() == idx else torch.cuda.device(idx)
+    stream = _RAW_STREAM(idx) if _RAW_STREAM is not None else torch.cuda.current_stream(idx).cuda_stream
+    return ctx, stream
 
 
 def _workspace(nbytes: int, device: torch.device) -> torch.Tensor:
@@ -144,18 +158,18 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
         out_tokens = torch.empty(n_d + B, dtype=torch.int32, device=dev)
     else:
         accepted_len, out_tokens = out
-    need = int(_native.lib().sdv_workspace_bytes(B, n_d, V, dt))
-    ws = _workspace(need, dev) if workspace is None else workspace
-    shapes = {"target_lse": (n_d + B, torch.float64), "draft_lse": (n_d, torch.float64),
-              "target_argmax": (n_d + B, torch.int32), "ratio": (n_d, torch.float64),
-              "accept_uniform": (n_d, torch.float32), "draw_uniform": (B, torch.float32),
-              "terminal_kind": (B, torch.int32), "target_logit": (n_d, torch.float32),
-              "draft_logit": (n_d, torch.float32), "terminal_mass": (B, torch.float64)}
+    # a caller's workspace is checked against the shape's need by the library itself
+    ws = _workspace(int(_native.lib().sdv_workspace_bytes(B, n_d, V, dt)), dev) if workspace is None else workspace
     dvals = {}
     dg = None
     want_kept = "kept_tokens" in diag
     diag = tuple(name for name in diag if name != "kept_tokens")
     if diag or events:
+        shapes = {"target_lse": (n_d + B, torch.float64), "draft_lse": (n_d, torch.float64),
+                  "target_argmax": (n_d + B, torch.int32), "ratio": (n_d, torch.float64),
+                  "accept_uniform": (n_d, torch.float32), "draw_uniform": (B, torch.float32),
+                  "terminal_kind": (B, torch.int32), "target_logit": (n_d, torch.float32),
+                  "draft_logit": (n_d, torch.float32), "terminal_mass": (B, torch.float64)}
         dg = _native.SdvDiag()
         for name in diag:
             n, t = shapes[name]
@@ -165,9 +179,9 @@ def verify_ex(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: to
         for k, ev in enumerate(events or []):
             if ev is not None:
                 dg.events[k] = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    ctx, stream = _launch_on(dev)
     dg_ref = ctypes.byref(dg) if dg is not None else None
-    with torch.cuda.device(dev):
+    with ctx:
         if use_opts:
             opt = _native.SdvOptions()
             if profile is not None:
@@ -256,11 +270,12 @@ def verify_tree(target: torch.Tensor, draft: torch.Tensor | None, draft_tokens: 
         for k, ev in enumerate(events or []):
             if ev is not None:
                 dg.events[k] = ev.cuda_event if hasattr(ev, "cuda_event") else int(ev)
-    with torch.cuda.device(dev):
+    ctx, stream = _launch_on(dev)
+    with ctx:
         rc = _native.lib().sdv_verify_tree(
             _ptr(target), _ptr(draft), _ptr(draft_tokens), _ptr(parents), _ptr(draft_row), _ptr(offsets), B, n, n_dr, V, dt,
             float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(accepted_len), _ptr(accepted_nodes),
-            _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(), torch.cuda.current_stream(dev).cuda_stream,
+            _ptr(out_tokens), _ptr(ws), ws.numel() * ws.element_size(), stream,
             ctypes.byref(dg) if dg is not None else None)
     if rc != 0:
         raise SdvError(rc, "sdv_verify_tree")
