@@ -77,7 +77,10 @@ typedef enum {
  *                  first kernel, events[1] after the row pass (one record per 16 KiB chunk of
  *                  every row read), events[3] after the truncation kernel (top-k / top-p through
  *                  sdv_verify_opts; not recorded when it does not run), events[2] after the verdict
- *                  kernel (per request: fold, accept scan, terminal draw).
+ *                  kernel (per request: fold, accept scan, terminal draw).  A batch of one request
+ *                  with 16-byte aligned rows of at most 15 chunks in all, one profile and no
+ *                  truncation or probability rows, runs both passes in one launch: events[1] and
+ *                  events[2] are then both recorded after it.
  *   target_logit   [n_draft_rows]      z_target[x_j], the stored target logit at each draft token,
  *                                      widened to binary32 (T > 0)
  *   draft_logit    [n_draft_rows]      z_draft[x_j], the same on the draft row (T > 0, draft logits;

@@ -2752,6 +2752,39 @@ __global__ __launch_bounds__(kWave * kWaves) void verdicts(Params P) {
   }
 }
 
+// A batch of one request whose 16-byte aligned rows hold at most kOneLaunchUnits chunks in all runs
+// in one launch of kOneLaunchWaves waves.  Wave w computes the record of chunk w (the row pass's
+// work, every chunk at once), the last wave screens the offsets, and the workgroup then verifies
+// the request as the verdict kernel does, from the records it has just written (the workgroup
+// barrier orders those stores before the loads).  That saves the second launch and the records'
+// trip between two kernels.
+constexpr int kOneLaunchWaves = 16;
+constexpr int64_t kOneLaunchUnits = kOneLaunchWaves - 1;
+
+template <class E, int kMode>
+__global__ __launch_bounds__(kWave * kOneLaunchWaves) void one_launch(Params P) {
+  static_assert(kMode != kModeProfiled, "one profile per call");
+  constexpr bool kVec = true;
+  extern __shared__ double lds_mass[];
+  __shared__ RowFold rows[kMaxRows];
+  __shared__ Decision dec;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (wave == kOneLaunchWaves - 1) screen_offsets(P, lane);
+  const int64_t u = wave;
+  if (u < P.n_units) {
+    const int32_t slot = (int32_t)(u / P.C);
+    const int32_t c = (int32_t)(u - (int64_t)slot * P.C);
+    const char* rp = slot < P.n_t ? row_ptr<E>(P.target, slot, P.V) : row_ptr<E>(P.draft, slot - P.n_t, P.V);
+    const int32_t c0 = c * E::kChunk;
+    const float2 rec = chunk_record<E, kMode == kModeGreedy, kVec>(rp, c0, min(E::kChunk, P.V - c0), P.k2, lane);
+    if (lane == 0) P.part[u] = rec;
+  }
+  __syncthreads();  // the records and the screening, seen by every wave
+  verdict_body<E, kMode == kModeGreedy, kVec, false, false, kOneLaunchWaves>(P, 0, P.k2, P.seed, false, lds_mass, rows,
+                                                                            dec);
+}
+
 // The correction or bonus draw of a request (T > 0), by the verdict workgroup.  With P.split
 // workgroups per request, workgroup s computes the residual masses of chunks [s C / split,
 // (s + 1) C / split) and publishes them; the last one to finish (a counter per request) reads the
@@ -3679,7 +3712,23 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
   const bool cut = kMode != kModeGreedy && (P.top_k || P.top_p_milli);
   // verdict workgroups per request (the row pass zeroes their counters)
   P.split = kMode == kModeGreedy ? 1 : (P.split > 0 ? std::min(P.split, P.C) : verdict_split(P.B, P.C));
+  // shared memory of the verdict workgroups: C residual masses, then as many chunk records as the
+  // deepest request can need, up to the budget; deeper requests fold straight from the workspace
+  const int64_t want = (int64_t)(2 * SDV_MAX_DEPTH + 1) * P.C;
+  const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
+  P.lds_records = want < room ? want : room;
+  const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
   record(0);
+  if constexpr (kMode != kModeProfiled && kVec) {  // (the split loads of rows off the 16-byte grid spill here)
+    if (P.B == 1 && P.n_units <= kOneLaunchUnits && P.split == 1 && !cut && !P.qrows) {
+      P.hist = nullptr;
+      hipLaunchKernelGGL((one_launch<E, kMode>), dim3(1), dim3(kWave * kOneLaunchWaves), lds, stream, P);
+      if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
+      record(1);  // both passes ran in the one launch
+      record(2);
+      return SDV_OK;
+    }
+  }
   if constexpr (E::kBytes == 2 && kMode != kModeGreedy) {
     if (!cut) P.hist = nullptr;
     if (P.hist) {
@@ -3712,12 +3761,6 @@ int launch(Params& P, hipStream_t stream, const sdv_diag* diag) {
     if (hipGetLastError() != hipSuccess) return SDV_ERR_HIP;
     record(3);
   }
-  // shared memory: C residual masses, then as many chunk records as the deepest request can need,
-  // up to the budget; deeper requests fold straight from the workspace
-  const int64_t want = (int64_t)(2 * SDV_MAX_DEPTH + 1) * P.C;
-  const int64_t room = (int64_t)(kVerdictLdsBytes - (size_t)P.C * sizeof(double)) / (int64_t)sizeof(float2);
-  P.lds_records = want < room ? want : room;
-  const size_t lds = (size_t)P.C * sizeof(double) + (size_t)P.lds_records * sizeof(float2);
   const dim3 grid((unsigned)P.B, (unsigned)P.split), block(kWave * kVerdictWaves);
   if constexpr (kMode != kModeGreedy) {  // the greedy rule never reads the draft side
     if (P.qrows) {

@@ -221,6 +221,34 @@ def test_extreme_temperatures(T):
         assert (acc >= 0).all()
 
 
+@pytest.mark.parametrize("V,dtype,depths", [(1000, "fp32", [0, 1, 4, 7, 8]), (8192, "bf16", [0, 3, 7]),
+                                            (16384, "bf16", [0, 1, 3, 4]), (24, "fp32", [5, 64])])
+def test_one_request_batches(V, dtype, depths):
+    """A batch of one request whose rows hold at most 16 chunks runs in a single launch (records,
+    screening and verdict in one workgroup); deeper ones (K = 8 at one chunk per row, K = 4 at two,
+    K = 64) take the two kernels.  Parity with the oracle at T > 0 and T = 0, one call per depth."""
+    for K in depths:
+        for T in (1.0, 0.0):
+            b = W.make_random(f"one_v{V}_k{K}", [K], V, dtype, T, 3.0, 1.0, V + K, 41 + K)
+            acc, *_ = check_parity(b)
+            assert 0 <= acc[0] <= K
+
+
+def test_one_request_with_bad_offsets_writes_nothing():
+    """The single-launch path screens the offsets itself: cu[0] != 0 rejects the batch without
+    writing a slot."""
+    import lossless_draft_verification_online_amd as sdv
+    b = W.make_random("one_bad", [3], 1000, "fp32", 1.0, 2.0, 1.0, 5, 6)
+    t, d, x = to_device(b.target, "fp32"), to_device(b.draft, "fp32"), torch.from_numpy(b.tokens).to(DEV)
+    cu = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
+    out = torch.full((b.n_draft_rows + 1,), -7, dtype=torch.int32, device=DEV)
+    acc = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+    sdv.verify(t, d, x, cu, 1.0, 6, out=(acc, out))
+    torch.cuda.synchronize()
+    assert acc.cpu().tolist() == [-1]
+    assert (out.cpu().numpy() == -7).all()
+
+
 def test_bad_requests_are_isolated():
     rng = np.random.default_rng(21)
     depths = [3, 2, 4, 0, 5]
