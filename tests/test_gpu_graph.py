@@ -62,6 +62,22 @@ def test_linear_verification_replays(V, dtype, truncate):
     _replays_match(lambda o: sdv.verify_ex(t, d, x, cu, 1.0, 3, out=tuple(o), workspace=ws, **kw), outs, other)
 
 
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_one_request_replays(T):
+    """A batch of one small request (the single-launch path) captured and replayed."""
+    b = W.make_random("graph_one", [4], 1000, "fp32", T, 2.0, 1.0, data_seed=11, verify_seed=12, keep_draft=True)
+    t, d, x, cu = to_device(b.target, "fp32"), to_device(b.draft, "fp32"), _i32(b.tokens), _i32(b.cu)
+    ws = torch.empty(sdv.workspace_bytes(b.B, b.n_draft_rows, b.V, t.dtype), dtype=torch.uint8, device=DEV)
+    outs = [torch.empty(1, dtype=torch.int32, device=DEV), torch.empty(b.n_draft_rows + 1, dtype=torch.int32,
+                                                                       device=DEV)]
+    other_t = torch.randn_like(t)
+
+    def other():
+        sdv.verify_ex(other_t, d, x, cu, 0.7, 99, workspace=ws)
+
+    _replays_match(lambda o: sdv.verify_ex(t, d, x, cu, T, 3, out=tuple(o), workspace=ws), outs, other)
+
+
 def test_tree_verification_replays():
     rng = np.random.default_rng(5)
     b = W.make_tree("graph_tree", rng.integers(0, 20, size=24), "random", 32000, "bf16", 1.0, 2.5, 1.5, data_seed=6,
