@@ -3134,9 +3134,18 @@ __device__ __forceinline__ void chain_masses(const ChainFrame& f, const char* tr
         for (int j = 0; j < f.l;) {
           const int j1 = chain_run_end(f, j);
           const char* dp = row_ptr<E>(draft, f.drow[j], V);
+          uintptr_t pieces;
+          uint32_t shift;
+          split::tree_pieces(split::Plan{s.head, s.body, 0u, 0, 0}, (uintptr_t)dp, E::kBytes, c0, &pieces, &shift);
+          const u32x4* dv = reinterpret_cast<const u32x4*>(at_address(dp, pieces));
           u32x4 b[kGroup];
+          if (__builtin_amdgcn_readfirstlane(shift) == 0) {  // the draft row on the target's grid: one piece
 #pragma unroll
-          for (int k = 0; k < kGroup; ++k) b[k] = tree_draft_vec<E>(dp, c0, s, jc[k]);
+            for (int k = 0; k < kGroup; ++k) b[k] = dv[jc[k]];
+          } else {
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k) b[k] = funnel16(dv[jc[k]], dv[jc[k] + 1], shift);
+          }
           const float d_hi = f.d_hi[j];
           float q[kGroup][E::kPerVec];
 #pragma unroll

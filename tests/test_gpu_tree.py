@@ -54,11 +54,12 @@ def check_tree(b, seed=None, diag=(), shifts=(0, 0)):
 
 
 @pytest.mark.parametrize("V,dtype,shifts,shared", [(8192, "bf16", (3, 0), True), (8192, "bf16", (0, 5), False),
-                                                   (4096, "fp32", (1, 2), True), (20011, "bf16", (7, 1), True)])
+                                                   (4096, "fp32", (1, 2), True), (20011, "bf16", (7, 1), True),
+                                                   (8192, "bf16", (3, 3), True), (4096, "fp32", (2, 2), False)])
 def test_tree_rows_off_the_16_byte_grid(V, dtype, shifts, shared):
     """Target and draft bases shifted by whole elements, so every row sits off the 16-byte grid at
     its own offset: the passes and searches split the target rows and cut each draft row's bytes
-    by its own shift."""
+    by its own shift (none where both bases move alike and the rows are whole 16-byte lines)."""
     rng = np.random.default_rng(V + shifts[0])
     b = W.make_tree(f"tree_off_v{V}", rng.integers(0, 25, size=24), "random", V, dtype, 1.0, 3.0, 1.5,
                     data_seed=V + 11, verify_seed=13, shared=shared)
